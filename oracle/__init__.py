@@ -1,0 +1,49 @@
+"""CPU oracle for the Psi-Spec decode-step hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library and its
+Python binding) imports, calls or links this package; only the tests, the
+`smoke()` check and the CPU-baseline leg of the benchmark do.
+
+Every function here is a plain, slow, float64 restatement of what the method
+computes, written from the pages:
+
+* Uno: diffusion-augmented LLM (hyper.ai summary of arXiv 2609.04010),
+  section "方法" (method) -- gated LoRA over concatenated clean + noisy rows,
+  the Psi-Spec sampler with its linear and tree candidate strategies.
+* The same paper's abstract (chatpaper.ai, English part) -- lossless
+  acceleration.
+* ainews.surl.tw article on Uno -- "lossless" means the samples follow the
+  base AR distribution, not bit-identical text.
+
+Each module states the passage it follows and every reading taken where the
+pages are silent.  Pins that tie these functions to something other than
+themselves live in `tests/test_oracle_*.py`.
+"""
+
+from .gated_lora import gated_lora_linear
+from .verify_linear import (
+    softmax_rows,
+    row_log_stats,
+    accept_draft,
+    residual_weights,
+    inverse_cdf,
+    verify_linear,
+)
+from .tree_attention import ancestors_or_self, tree_attention, tree_attention_dense_mask
+from .verify_tree import node_depths, children_lists, verify_tree
+
+__all__ = [
+    "gated_lora_linear",
+    "softmax_rows",
+    "row_log_stats",
+    "accept_draft",
+    "residual_weights",
+    "inverse_cdf",
+    "verify_linear",
+    "ancestors_or_self",
+    "tree_attention",
+    "tree_attention_dense_mask",
+    "node_depths",
+    "children_lists",
+    "verify_tree",
+]

@@ -1,0 +1,27 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+TESTS = os.path.dirname(os.path.abspath(__file__))
+if TESTS not in sys.path:
+    sys.path.insert(0, TESTS)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: long CPU test")
+
+
+@pytest.fixture(scope="session")
+def gpu_lib():
+    """The HIP-backed binding; skips cleanly only when no GPU is present."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import diffusion_augmented_decoding_amd as dad
+    dad.load()          # raises if the built library is missing
+    return dad
