@@ -1,0 +1,106 @@
+// Host-side internals of libunospec: launcher declarations, error reporting,
+// kernel timing hooks.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/uno.h"
+
+namespace uno {
+
+// Thread-local error message set by the entry points.
+uno_status fail(uno_status s, const char* fmt, ...);
+uno_status check_hip(hipError_t e, const char* what);
+
+// Kernel timing: bracket a launch with events when profiling is on.
+struct ProfileScope {
+  ProfileScope(const char* name, hipStream_t stream);
+  ~ProfileScope();
+  const char* name;
+  hipStream_t stream;
+  int slot;
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- sampler
+struct RowStat {   // per logit row, log2 domain: y = logit * log2(e) / T
+  float m;         // max_v y_v
+  float s;         // sum_v 2^(y_v - m)
+  float yd;        // y at the draft token (p rows 0..k-1, q rows); unused otherwise
+  float pad;
+};
+
+struct VerifyLinearArgs {
+  uno_dtype dtype;
+  int batch, k, vocab;
+  const void* p; int64_t p_seq, p_row;
+  const void* q; int64_t q_seq, q_row;
+  const int32_t* drafts;
+  const float* u_acc;
+  const float* u_s;
+  float scale_log2;   // log2(e) / T
+  int32_t* out_len;
+  int32_t* out_tok;
+  float* out_pd;
+  float* out_qd;
+  float* out_mass;
+  RowStat* stats;     // workspace, batch * (2k + 1)
+};
+size_t verify_linear_workspace_bytes(int batch, int k);
+hipError_t launch_verify_linear(const VerifyLinearArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- gated LoRA
+struct GatedLoraArgs {
+  uno_dtype dtype;
+  int64_t M, N, K, r;
+  const void* x; int64_t ldx;
+  const void* w; int64_t ldw;
+  const void* a; int64_t lda;
+  const void* b; int64_t ldb;
+  const uint8_t* gate;
+  float lora_scale;
+  void* y; int64_t ldy;
+  void* ws; size_t ws_bytes;
+};
+size_t gated_lora_workspace_bytes(uno_dtype dtype, int64_t M, int64_t N, int64_t K, int64_t r);
+hipError_t launch_gated_lora(const GatedLoraArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- tree attention
+struct TreeAttnArgs {
+  int batch, n_tree, ctx, n_heads, n_kv, head_dim;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const void* k_tree;
+  const void* v_tree;
+  const int32_t* parent;
+  float scale;
+  void* out;
+  float* out_lse;
+  void* ws; size_t ws_bytes;
+};
+size_t tree_attention_workspace_bytes(int batch, int n_tree, int ctx, int n_heads, int n_kv, int head_dim);
+hipError_t launch_tree_attention(const TreeAttnArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- tree verify
+struct TreeVerifyArgs {
+  uno_dtype dtype;
+  int batch, n_tree, max_depth, vocab;
+  const int32_t* parent;
+  const int32_t* tokens;
+  const void* p;
+  const void* q;
+  const float* u_acc;
+  const float* u_s;
+  float scale_log2;
+  int32_t* out_len;
+  int32_t* out_path;
+  int32_t* out_tok;
+  void* ws; size_t ws_bytes;
+};
+size_t tree_verify_workspace_bytes(int batch, int n_tree, int max_depth, int vocab);
+hipError_t launch_tree_verify(const TreeVerifyArgs& a, hipStream_t stream);
+
+}  // namespace uno

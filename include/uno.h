@@ -1,0 +1,218 @@
+/*
+ * libunospec -- the data-parallel hot path of one Psi-Spec decode step of Uno,
+ * a diffusion-augmented LLM, for AMD Instinct MI355X (gfx950).
+ *
+ * Method source: "Uno" (arXiv 2609.04010) as summarised on hyper.ai, section
+ * "方法" (method): LoRA adapters on every AR weight matrix, a per-position
+ * gate over one concatenated clean + noisy forward, and the Psi-Spec sampler
+ * (rejection sampling against the AR distribution that keeps the longest
+ * valid prefix, with a linear and a tree candidate strategy).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Memory: every data pointer is device memory of the current HIP device,
+ *   owned by the caller.  The library never allocates or frees device memory
+ *   in a call; scratch space is the caller's `workspace`, sized by the
+ *   matching *_workspace query (a size of 0 allows workspace == NULL).
+ * - Layout: row-major (C order).  "ld"/"stride" arguments are in elements.
+ * - Ordering: work is enqueued on `stream` (NULL = the null stream) and the
+ *   call returns without synchronising.  Device-side faults surface at the
+ *   caller's next synchronisation.
+ * - Errors: arguments are validated on the host before anything is enqueued;
+ *   an invalid call enqueues nothing and returns a non-zero uno_status.
+ *   uno_last_error() returns a message for the calling thread's last error.
+ *   No C++ exception crosses this interface.
+ * - Threads: calls are reentrant; concurrent calls must not share a workspace.
+ * - Aliasing: outputs must not alias inputs or each other.
+ * - Data contract: token ids in [0, vocab), finite logits, uniforms in [0, 1).
+ *   These are not checked on the device.
+ */
+#ifndef UNO_H
+#define UNO_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  UNO_OK = 0,
+  UNO_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, bad stride, bad tree */
+  UNO_ERR_UNSUPPORTED = 2,      /* valid but outside what the kernels implement */
+  UNO_ERR_WORKSPACE = 3,        /* workspace smaller than the query returned */
+  UNO_ERR_HIP = 4,              /* a HIP runtime call or a launch failed */
+  UNO_ERR_INTERNAL = 5
+} uno_status;
+
+typedef enum { UNO_F32 = 0, UNO_BF16 = 1 } uno_dtype;
+
+#define UNO_ABI_VERSION 1
+
+int uno_abi_version(void);
+const char* uno_status_string(uno_status s);
+/* Message describing the calling thread's most recent error ("" if none). */
+const char* uno_last_error(void);
+
+/* --------------------------------------------------------------------------
+ * Gated-LoRA linear layer.
+ * Source: Uno summary (hyper.ai), section "方法": the diffusion weights are
+ * low-rank adapters on every AR weight matrix; drafting uses AR + adapter
+ * weights, verification the AR weights only; one forward over concatenated
+ * clean and noisy sequences, with a mask that disables the adapter on clean
+ * positions and enables it on noisy ones.
+ *
+ *   y[m, :] = x[m, :] W^T + lora_scale * gate[m] * (x[m, :] A^T) B^T
+ *
+ * dtype   UNO_BF16: x, W, A, B, y are bf16; products accumulate in fp32 on
+ *         matrix cores; the low-rank intermediate x A^T is held as bf16.
+ *         UNO_F32: everything fp32 (vector ALU).
+ * x [M, K] (row stride ldx >= K), W [N, K] (ldw >= K), A [r, K] (lda >= K),
+ * B [N, r] (ldb >= r), y [M, N] (ldy >= N).
+ * gate    uint8 [M]; 0 = clean/verify row (AR weights only), non-zero = noisy/
+ *         draft row (adapter on).  NULL = all rows 0.  r = 0 is allowed (A, B
+ *         unused, may be NULL): a plain GEMM.
+ * Requirements: M, N, K >= 1, r >= 0.  UNO_BF16 also needs K and r multiples
+ * of 8, all leading dimensions multiples of 8 and 16-byte aligned base
+ * pointers (else UNO_ERR_UNSUPPORTED).
+ * Rows whose gate is 0 give results bit-identical to the same call with r = 0.
+ * ------------------------------------------------------------------------ */
+uno_status uno_gated_lora_linear_workspace(uno_dtype dtype, int64_t M, int64_t N, int64_t K,
+                                           int64_t r, size_t* bytes);
+uno_status uno_gated_lora_linear(hipStream_t stream, uno_dtype dtype,
+                                 int64_t M, int64_t N, int64_t K, int64_t r,
+                                 const void* x, int64_t ldx, const void* W, int64_t ldw,
+                                 const void* A, int64_t lda, const void* B, int64_t ldb,
+                                 const uint8_t* gate, float lora_scale,
+                                 void* y, int64_t ldy,
+                                 void* workspace, size_t workspace_bytes);
+
+/* --------------------------------------------------------------------------
+ * Psi-Spec linear verify sampler.
+ * Source: Uno summary (hyper.ai), section "方法", last paragraph: a block
+ * proposed by the diffusion path is rejection-sampled against the base AR
+ * distribution and the longest valid prefix is accepted; the linear sampler
+ * draws one candidate sequence from the marginals; the block's first token
+ * comes from the AR weights.  The acceptance rule and residual are standard
+ * speculative sampling (Leviathan et al. 2023; Chen et al. 2023):
+ *
+ *   p_i = softmax(p_logits[b, i] / T), i = 0..k      (row k = bonus row)
+ *   q_i = softmax(q_logits[b, i] / T), i = 0..k-1
+ *   accept draft i  iff  u_accept[b, i] * q_i[d_i] < p_i[d_i]
+ *   L = first rejected i (k if none)
+ *   L < k: w = max(0, p_L - q_L) (falls back to p_L if sum(w) == 0); L = k: w = p_k
+ *   y = smallest v (token-id order) with cumsum(w)[v] > u_sample[b] * sum(w)
+ *
+ * p_logits [batch][k+1][vocab] with strides (p_seq_stride, p_row_stride),
+ *   row i = AR distribution of the position of draft i (the logit row of the
+ *   preceding token), row k = the position after the last draft.
+ * q_logits [batch][k][vocab] with strides (q_seq_stride, q_row_stride).
+ * draft_tokens int32 [batch][k]; u_accept f32 [batch][k]; u_sample f32 [batch].
+ * Outputs: out_accept_len int32 [batch] (L in 0..k), out_token int32 [batch]
+ *   (the correction or bonus token y; the step emits d[0:L] then y).
+ *   Optional (may be NULL): out_p_draft f32 [batch][k] = p_i[d_i],
+ *   out_q_draft f32 [batch][k] = q_i[d_i], out_residual_mass f32 [batch] =
+ *   sum(w) of the row y was drawn from (1 for a bonus draw).
+ * Requirements: batch >= 1, 0 <= k <= 64, 1 <= vocab <= 2^20, temperature > 0,
+ *   row strides >= vocab, sequence strides >= the rows they hold.
+ * ------------------------------------------------------------------------ */
+uno_status uno_psi_spec_verify_linear_workspace(int32_t batch, int32_t k, int32_t vocab, size_t* bytes);
+uno_status uno_psi_spec_verify_linear(hipStream_t stream, uno_dtype logit_dtype,
+                                      int32_t batch, int32_t k, int32_t vocab,
+                                      const void* p_logits, int64_t p_seq_stride, int64_t p_row_stride,
+                                      const void* q_logits, int64_t q_seq_stride, int64_t q_row_stride,
+                                      const int32_t* draft_tokens,
+                                      const float* u_accept, const float* u_sample,
+                                      float temperature,
+                                      int32_t* out_accept_len, int32_t* out_token,
+                                      float* out_p_draft, float* out_q_draft, float* out_residual_mass,
+                                      void* workspace, size_t workspace_bytes);
+
+/* --------------------------------------------------------------------------
+ * Tree-masked grouped-query attention for tree verification.
+ * Source: Uno summary (hyper.ai), section "方法", last paragraph: the tree
+ * sampler verifies several candidates concurrently as a prefix tree with tree
+ * attention.  Node i of the tree attends to every cached position and to the
+ * tree nodes that are its ancestors or itself:
+ *
+ *   O[b,i,h] = sum_j softmax_j(scale * <Q[b,i,h], K_j>) V_j,
+ *   j over cache rows 0..ctx_len-1 and tree nodes {ancestors of i} + {i},
+ *   K_j, V_j taken from KV head h / (n_heads / n_kv_heads).
+ *
+ * q       bf16 [batch][n_tree][n_heads][head_dim]   (RoPE already applied)
+ * k_cache, v_cache bf16 [batch][ctx_len][n_kv_heads][head_dim]
+ * k_tree,  v_tree  bf16 [batch][n_tree][n_kv_heads][head_dim]
+ * parent  int32 [batch][n_tree]: parent[b][0] = -1, 0 <= parent[b][i] < i.
+ *         Checked on the device; a bad tree makes the call's outputs NaN.
+ * out     bf16 [batch][n_tree][n_heads][head_dim]
+ * out_lse optional f32 [batch][n_tree][n_heads]: natural-log log-sum-exp of
+ *         the scaled scores.
+ * Requirements: head_dim == 128, n_heads a multiple of n_kv_heads,
+ *   n_heads / n_kv_heads <= 8, 1 <= n_tree <= 256, ctx_len >= 0, batch >= 1.
+ * ------------------------------------------------------------------------ */
+uno_status uno_tree_verify_attention_workspace(int32_t batch, int32_t n_tree, int32_t ctx_len,
+                                               int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                                               size_t* bytes);
+uno_status uno_tree_verify_attention(hipStream_t stream,
+                                     int32_t batch, int32_t n_tree, int32_t ctx_len,
+                                     int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                                     const void* q, const void* k_cache, const void* v_cache,
+                                     const void* k_tree, const void* v_tree,
+                                     const int32_t* parent, float softmax_scale,
+                                     void* out, float* out_lse,
+                                     void* workspace, size_t workspace_bytes);
+
+/* --------------------------------------------------------------------------
+ * Psi-Spec tree verify: per-node rejection over a prefix tree.
+ * Source: Uno summary (hyper.ai), section "方法", last paragraph (tree
+ * sampler; lossless in both the linear and the tree case).  Read as
+ * multi-candidate speculative sampling (SpecInfer, Miao et al. 2023):
+ *   cur = root, r = p_root;
+ *   children c of cur in ascending node id, token t, depth d:
+ *     accept iff u_accept[b][c] * q_d[t] < r[t] -> cur = c, r = p_c, repeat;
+ *     reject -> r = max(0, r - q_d) / sum (unchanged if the sum is 0);
+ *   no child accepted (or no child): y = smallest v with cumsum(r)[v] > u_sample * sum(r).
+ *   L = depth of cur; the path is the accepted node ids.
+ * Siblings are read as i.i.d. draws from the per-depth marginal q_d.
+ *
+ * parent, tokens int32 [batch][n_tree] (parent[b][0] = -1, parent[b][i] < i;
+ *   tokens[b][0] unused).
+ * p_logits [batch][n_tree][vocab]: AR row of each node (scores its children).
+ * q_logits [batch][max_depth][vocab]: draft marginal of depth 1..max_depth.
+ * u_accept f32 [batch][n_tree] (entry 0 unused), u_sample f32 [batch].
+ * Outputs: out_accept_len int32 [batch]; out_path int32 [batch][max_depth]
+ *   (accepted node ids, -1 padded); out_token int32 [batch].
+ * Requirements: 1 <= n_tree <= 1024, 1 <= max_depth <= 64 and >= the tree's
+ *   depth, 1 <= vocab <= 2^20, temperature > 0.  The tree structure is
+ *   checked on the device; a malformed tree yields out_accept_len = -1.
+ * ------------------------------------------------------------------------ */
+uno_status uno_psi_spec_verify_tree_workspace(int32_t batch, int32_t n_tree, int32_t max_depth,
+                                              int32_t vocab, size_t* bytes);
+uno_status uno_psi_spec_verify_tree(hipStream_t stream, uno_dtype logit_dtype,
+                                    int32_t batch, int32_t n_tree, int32_t max_depth, int32_t vocab,
+                                    const int32_t* parent, const int32_t* tokens,
+                                    const void* p_logits, const void* q_logits,
+                                    const float* u_accept, const float* u_sample,
+                                    float temperature,
+                                    int32_t* out_accept_len, int32_t* out_path, int32_t* out_token,
+                                    void* workspace, size_t workspace_bytes);
+
+/* --------------------------------------------------------------------------
+ * Kernel timing (measurement support, not part of the method).
+ * When enabled, every kernel the library launches whose name contains
+ * `name_filter` (NULL or "" = every kernel) is bracketed by HIP events
+ * recorded on its launch stream; uno_profile_query returns the summed
+ * duration in milliseconds and the launch count of recorded kernels whose
+ * name contains `name`, over launches since the last reset.  Querying
+ * synchronises on the recorded events.  Not thread-safe; for benchmarks.
+ * ------------------------------------------------------------------------ */
+void uno_profile_enable(int on, const char* name_filter);
+void uno_profile_reset(void);
+uno_status uno_profile_query(const char* name, double* total_ms, int64_t* count);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* UNO_H */

@@ -1,0 +1,181 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/uno.h declares, and rejects invalid calls on the host (before any HIP
+call) with the documented status codes."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import diffusion_augmented_decoding_amd as dad
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "uno.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+F32, BF16 = 0, 1
+P = ctypes.c_void_p
+FAKE = ctypes.c_void_p(0x1000)          # never dereferenced: validation fails first
+FAKE16 = ctypes.c_void_p(0x10000)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return dad.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(uno_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert set(declared_functions()) == set(dad.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 14
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strings(lib):
+    assert lib.uno_abi_version() == 1
+    for s in range(6):
+        assert lib.uno_status_string(s)
+    assert lib.uno_status_string(99) == b"unknown status"
+
+
+def _ws_gl(lib, dtype, m, n, k, r):
+    out = ctypes.c_size_t(0)
+    st = lib.uno_gated_lora_linear_workspace(dtype, m, n, k, r, ctypes.byref(out))
+    return st, out.value
+
+
+def test_gated_lora_workspace_queries(lib):
+    assert _ws_gl(lib, BF16, 1024, 12288, 4096, 128)[0] == OK
+    assert _ws_gl(lib, BF16, 1024, 12288, 4096, 0) == (OK, 0)
+    assert _ws_gl(lib, F32, 8, 256, 256, 8)[1] >= 8 * 8 * 4
+    assert _ws_gl(lib, BF16, 0, 1, 8, 8)[0] == INVALID
+    assert _ws_gl(lib, BF16, 4, 4, 12, 8)[0] == UNSUPPORTED      # K not multiple of 8
+    assert _ws_gl(lib, BF16, 4, 4, 16, 4)[0] == UNSUPPORTED      # r not multiple of 8
+    assert _ws_gl(lib, 7, 4, 4, 16, 8)[0] == INVALID             # dtype
+    assert lib.uno_gated_lora_linear_workspace(BF16, 4, 4, 16, 8, None) == INVALID
+
+
+def _gl(lib, **kw):
+    a = dict(stream=None, dtype=BF16, M=16, N=16, K=16, r=8, x=FAKE16, ldx=16, W=FAKE16, ldw=16,
+             A=FAKE16, lda=16, B=FAKE16, ldb=8, gate=FAKE16, scale=1.0, y=FAKE16, ldy=16, ws=FAKE16,
+             wsb=1 << 20)
+    a.update(kw)
+    return lib.uno_gated_lora_linear(a["stream"], a["dtype"], a["M"], a["N"], a["K"], a["r"], a["x"], a["ldx"],
+                                     a["W"], a["ldw"], a["A"], a["lda"], a["B"], a["ldb"], a["gate"], a["scale"],
+                                     a["y"], a["ldy"], a["ws"], a["wsb"])
+
+
+def test_gated_lora_rejects_bad_calls(lib):
+    assert _gl(lib, x=None) == INVALID
+    assert _gl(lib, y=None) == INVALID
+    assert _gl(lib, A=None) == INVALID                           # r > 0 with a gate needs A, B
+    assert _gl(lib, M=0) == INVALID
+    assert _gl(lib, ldx=8) == INVALID                            # ldx < K
+    assert _gl(lib, ldy=12) == INVALID
+    assert _gl(lib, ldx=20) == UNSUPPORTED                       # bf16 ld not multiple of 8
+    assert _gl(lib, x=FAKE16.value + 2) == UNSUPPORTED            # misaligned
+    assert _gl(lib, wsb=0) == WORKSPACE
+    assert _gl(lib, ws=None) == WORKSPACE
+    assert _gl(lib, scale=float("nan")) == INVALID
+    assert b"workspace" in lib.uno_last_error() or b"lora_scale" in lib.uno_last_error()
+
+
+def _vl(lib, **kw):
+    a = dict(dtype=BF16, batch=2, k=3, vocab=64, p=FAKE16, ps=256, pr=64, q=FAKE16, qs=192, qr=64,
+             d=FAKE16, ua=FAKE16, us=FAKE16, T=1.0, L=FAKE16, y=FAKE16, ws=FAKE16, wsb=1 << 20)
+    a.update(kw)
+    return lib.uno_psi_spec_verify_linear(None, a["dtype"], a["batch"], a["k"], a["vocab"], a["p"], a["ps"], a["pr"],
+                                          a["q"], a["qs"], a["qr"], a["d"], a["ua"], a["us"], a["T"], a["L"],
+                                          a["y"], None, None, None, a["ws"], a["wsb"])
+
+
+def test_verify_linear_rejects_bad_calls(lib):
+    assert _vl(lib, k=65) == INVALID
+    assert _vl(lib, k=-1) == INVALID
+    assert _vl(lib, batch=0) == INVALID
+    assert _vl(lib, vocab=0) == INVALID
+    assert _vl(lib, vocab=(1 << 20) + 1, pr=(1 << 20) + 1, ps=4 * ((1 << 20) + 1),
+               qr=(1 << 20) + 1, qs=3 * ((1 << 20) + 1)) == UNSUPPORTED
+    assert _vl(lib, p=None) == INVALID
+    assert _vl(lib, q=None) == INVALID
+    assert _vl(lib, T=0.0) == INVALID
+    assert _vl(lib, T=float("inf")) == INVALID
+    assert _vl(lib, pr=63) == INVALID
+    assert _vl(lib, ps=100) == INVALID
+    assert _vl(lib, qs=100) == INVALID
+    assert _vl(lib, wsb=8) == WORKSPACE
+    assert _vl(lib, dtype=5) == INVALID
+    ws = ctypes.c_size_t(0)
+    assert lib.uno_psi_spec_verify_linear_workspace(256, 15, 151936, ctypes.byref(ws)) == OK
+    assert ws.value >= 256 * 31 * 16
+    assert lib.uno_psi_spec_verify_linear_workspace(256, 65, 151936, ctypes.byref(ws)) == INVALID
+
+
+def _ta(lib, **kw):
+    a = dict(batch=1, n=65, ctx=1024, H=32, Hkv=8, D=128, q=FAKE16, kc=FAKE16, vc=FAKE16, kt=FAKE16, vt=FAKE16,
+             par=FAKE16, scale=0.088, out=FAKE16, lse=None, ws=None, wsb=0)
+    a.update(kw)
+    return lib.uno_tree_verify_attention(None, a["batch"], a["n"], a["ctx"], a["H"], a["Hkv"], a["D"], a["q"],
+                                         a["kc"], a["vc"], a["kt"], a["vt"], a["par"], a["scale"], a["out"],
+                                         a["lse"], a["ws"], a["wsb"])
+
+
+def test_tree_attention_rejects_bad_calls(lib):
+    assert _ta(lib, D=64) == UNSUPPORTED
+    assert _ta(lib, H=30) == INVALID
+    assert _ta(lib, H=80, Hkv=8) == UNSUPPORTED     # 10 heads per KV head
+    assert _ta(lib, n=257) == UNSUPPORTED
+    assert _ta(lib, n=0) == INVALID
+    assert _ta(lib, q=None) == INVALID
+    assert _ta(lib, kc=None) == INVALID
+    assert _ta(lib, par=None) == INVALID
+    assert _ta(lib, out=ctypes.c_void_p(0x10008)) == UNSUPPORTED
+    assert _ta(lib, scale=-1.0) == INVALID
+
+
+def _tv(lib, **kw):
+    a = dict(dtype=BF16, batch=1, n=65, D=3, V=1000, par=FAKE16, tok=FAKE16, p=FAKE16, q=FAKE16, ua=FAKE16,
+             us=FAKE16, T=1.0, L=FAKE16, path=FAKE16, y=FAKE16, ws=FAKE16, wsb=1 << 20)
+    a.update(kw)
+    return lib.uno_psi_spec_verify_tree(None, a["dtype"], a["batch"], a["n"], a["D"], a["V"], a["par"], a["tok"],
+                                        a["p"], a["q"], a["ua"], a["us"], a["T"], a["L"], a["path"], a["y"],
+                                        a["ws"], a["wsb"])
+
+
+def test_tree_verify_rejects_bad_calls(lib):
+    assert _tv(lib, n=1025) == UNSUPPORTED
+    assert _tv(lib, D=65) == UNSUPPORTED
+    assert _tv(lib, D=0) == INVALID
+    assert _tv(lib, par=None) == INVALID
+    assert _tv(lib, path=None) == INVALID
+    assert _tv(lib, T=-1.0) == INVALID
+    assert _tv(lib, wsb=16) == WORKSPACE
+    assert _tv(lib, dtype=3) == INVALID
+
+
+def test_profile_query_without_records(lib):
+    ms = ctypes.c_double(1.0)
+    cnt = ctypes.c_int64(5)
+    assert lib.uno_profile_query(b"uno_", ctypes.byref(ms), ctypes.byref(cnt)) == OK
+    assert cnt.value == 0 and ms.value == 0.0
+    assert lib.uno_profile_query(None, ctypes.byref(ms), ctypes.byref(cnt)) == INVALID
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    import importlib
+    mod = importlib.reload(dad)
+    mod._lib = None
+    with pytest.raises(RuntimeError):
+        mod.load(str(tmp_path / "missing.so"))
+    importlib.reload(dad)
