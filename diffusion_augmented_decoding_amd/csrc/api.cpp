@@ -95,10 +95,11 @@ uno_status uno_gated_lora_linear(hipStream_t stream, uno_dtype dtype, int64_t M,
     return fail(UNO_ERR_INVALID_ARGUMENT, "leading dimension smaller than the row width");
   if (!std::isfinite(lora_scale)) return fail(UNO_ERR_INVALID_ARGUMENT, "lora_scale must be finite");
   if (dtype == UNO_BF16) {
-    if (ldx % 8 || ldw % 8 || ldy % 8 || (lora && (lda % 8 || ldb % 8)))
-      return fail(UNO_ERR_UNSUPPORTED, "bf16 path needs leading dimensions that are multiples of 8");
-    if (!aligned16(x) || !aligned16(W) || !aligned16(y) || (lora && (!aligned16(A) || !aligned16(B))))
-      return fail(UNO_ERR_UNSUPPORTED, "bf16 path needs 16-byte aligned matrices");
+    if (ldx % 8 || ldw % 8 || (lora && (lda % 8 || ldb % 8)))
+      return fail(UNO_ERR_UNSUPPORTED, "bf16 path needs input leading dimensions that are multiples of 8");
+    if (!aligned16(x) || !aligned16(W) || (lora && (!aligned16(A) || !aligned16(B))))
+      return fail(UNO_ERR_UNSUPPORTED, "bf16 path needs 16-byte aligned input matrices");
+    if ((reinterpret_cast<uintptr_t>(y) & 1u) != 0) return fail(UNO_ERR_INVALID_ARGUMENT, "y is not 2-byte aligned");
   }
   const size_t need = gated_lora_workspace_bytes(dtype, M, N, K, lora ? r : 0);
   if (workspace_bytes < need || (need > 0 && !workspace))

@@ -8,24 +8,35 @@
 //   y = x W^T + s * diag(g) (x A^T) B^T  =  [x | t] [W | B]^T,
 //   t = s * diag(g) (x A^T)   (M x r, held as bf16)
 //
-// bf16 path, three launches on the caller's stream:
+// bf16 path, launches on the caller's stream:
 //  1. lora_down: split-K MFMA GEMM x A^T -> fp32 partials [splits][M][r];
 //  2. lora_gate: t = bf16(s * g[m] * sum of partials); rows with g = 0 are
 //     written as exact zeros, so they add exact zeros in step 3 (bit-identical
 //     to the call without adapter);
-//  3. gemm: one MFMA K-loop over the concatenated K + r columns, bf16 out.
+//  3. gemm: one MFMA K-loop over the concatenated K + r columns; bf16 out, or
+//     fp32 split-K partials followed by 4. gemm_reduce (fixed summation order).
 // The gate is therefore folded into the producer of t; y is written once.
 //
 // GEMM kernel: BM x BN x 64 tiles, WM x WN waves, v_mfma_f32_32x32x16_bf16.
 // The MFMA "A" operand is the weight tile (N side) and "B" the activation
 // tile (M side), so each lane ends up owning 4 consecutive output columns per
 // register group (8-byte bf16 / 16-byte fp32 stores).  Global -> register ->
-// LDS double buffering with one barrier per K-tile; LDS rows are 128 B with
-// the 16-byte chunk index XOR-swizzled by (row & 7), which makes the
-// fragment reads (32 rows, same chunk) bank-conflict free.  Tiles are mapped
-// to block ids so that the blocks one XCD runs (ids congruent mod 8) cover a
-// contiguous band of N-tiles across all M-tiles: each weight tile is then
-// fetched into one XCD's L2 and reused by every M-tile there.
+// LDS double buffering with one barrier per K-tile; the LDS stores of the
+// next tile are spread over the four 16-deep k-steps of the current one so
+// they overlap the MFMAs.  Global loads are branch-free (always from a valid
+// address, then masked), so all of a thread's loads issue back to back.  LDS
+// rows are 128 B with the 16-byte chunk index XOR-swizzled by (row & 7),
+// which makes the fragment reads (32 rows, same chunk) bank-conflict free.
+// Tiles are mapped to block ids so that the blocks one XCD runs (ids
+// congruent mod 8) cover a contiguous band of N-tiles across all M-tiles:
+// each weight tile is then fetched into one XCD's L2 and reused by every
+// M-tile there.
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -38,54 +49,53 @@ constexpr int kChunksPerRow = kBK / 8;   // 16-byte chunks per row
 
 struct GemmParams {
   int M, N, K1, K2;                    // K1 columns from (x, w), then K2 from (t, b)
-  const uint16_t* x; int64_t ldx;
-  const uint16_t* w; int64_t ldw;
+  const uint16_t* x; int64_t ldx;      // activation rows (M side)
+  const uint16_t* w; int64_t ldw;      // weight rows (N side)
   const uint16_t* t; int64_t ldt;
   const uint16_t* b; int64_t ldb;
   int ktiles_per_split;                // K-tiles per split (blockIdx.y)
   int tiles_m, tiles_n;
-  // output: bf16 y (mode 0) or fp32 partials [split][M][N] (mode 1)
-  uint16_t* y; int64_t ldy;
-  float* part;
+  int xcd_remap;                       // map block ids so one XCD runs a contiguous tile band
+  uint16_t* y; int64_t ldy;            // MODE 0 output
+  int y_vec;                           // 8-byte stores allowed (ldy % 4 == 0, y 8-byte aligned)
+  float* part;                         // MODE 1 output: fp32 [split][M][N]
 };
 
-__device__ __forceinline__ u32x4 load_chunk(const uint16_t* base, int64_t ld, int row, int nrows,
-                                            int kc, const uint16_t* base2, int64_t ld2, int K1,
-                                            int Ktot) {
-  u32x4 z = {0u, 0u, 0u, 0u};
-  if (row >= nrows || kc >= Ktot) return z;
-  const uint16_t* p = (kc < K1) ? base + int64_t(row) * ld + kc : base2 + int64_t(row) * ld2 + (kc - K1);
+// 16-byte chunk (8 bf16 along K) at K index kc of a row: from (base, ld) for
+// kc < K1, from (base2, ld2) at kc - K1 below Ktot.  Out-of-range chunks read
+// `base` instead (always valid) and are zeroed later, when written to LDS:
+// masking here would consume the value and force a wait on the load.
+__device__ __forceinline__ u32x4 load_chunk_raw(const uint16_t* base, int64_t ld, const uint16_t* base2,
+                                                int64_t ld2, int row, bool ok, int kc, int K1) {
+  const bool first = kc < K1;
+  const uint16_t* p = first ? base + int64_t(row) * ld + kc : base2 + int64_t(row) * ld2 + (kc - K1);
+  p = ok ? p : base;
   return *reinterpret_cast<const u32x4*>(p);
 }
 
-template <int BM, int BN, int WM, int WN, int MODE>
+// BM x BN block tile, WM x WN waves, P K-tiles of register prefetch, DBF:
+// double-buffer the MFMA fragments across k-steps, MODE: 0 = bf16 out,
+// 1 = fp32 split-K partials.
+template <int BM, int BN, int WM, int WN, int P, int DBF, int MODE>
 __global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p) {
   constexpr int NT = WM * WN * kWave;
   constexpr int TM = BM / WM, TN = BN / WN;        // wave tile
   constexpr int FM = TM / 32, FN = TN / 32;        // 32x32 fragments per wave
   constexpr int CH_A = BN * kChunksPerRow;         // weight-tile chunks
   constexpr int CH_B = BM * kChunksPerRow;         // activation-tile chunks
-  constexpr int LA = (CH_A + NT - 1) / NT;
-  constexpr int LB = (CH_B + NT - 1) / NT;
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(CH_A % NT == 0 && CH_B % NT == 0, "tile chunks must divide among threads");
+  constexpr int LA = CH_A / NT, LB = CH_B / NT, LT = LA + LB;
+  constexpr int STAGE = (BN + BM) * kBK * 2;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  // stage s: [BN rows of weights][BM rows of activations], 128 B per row
-  constexpr int STAGE = (BN + BM) * kBK * 2;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid / kWave;
   const int wm = wave % WM, wn = wave / WM;
 
-  // XCD-aware tile order: block id b runs on XCD b % 8; give each XCD a
-  // contiguous range of (n-major, m-minor) tiles.
   const int ntiles = p.tiles_m * p.tiles_n;
   const int bid = blockIdx.x;
-  int tile;
-  if ((ntiles & 7) == 0) {
-    tile = (bid & 7) * (ntiles >> 3) + (bid >> 3);
-  } else {
-    tile = bid;
-  }
+  const int tile = (p.xcd_remap && (ntiles & 7) == 0) ? (bid & 7) * (ntiles >> 3) + (bid >> 3) : bid;
   const int tm = tile % p.tiles_m, tn = tile / p.tiles_m;
   const int m0 = tm * BM, n0 = tn * BN;
 
@@ -103,79 +113,127 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  u32x4 ra[LA], rb[LB];
+  // Chunk i of this thread (A chunks first, then B): tile row and 16-byte
+  // column.  reg[s] is one of P register sets holding a K-tile in flight:
+  // K-tile j is loaded P iterations before it is stored to LDS, so each
+  // global load has P compute phases to land.
+  u32x4 reg[P][LT];
+  auto chunk_row = [&](int i) { return ((i < LA ? i : i - LA) * NT + tid) / kChunksPerRow; };
+  auto chunk_col = [&](int i) { return ((i < LA ? i : i - LA) * NT + tid) % kChunksPerRow; };
 
-  auto gload = [&](int kt) {
-    const int k0 = kt * kBK;
-#pragma unroll
-    for (int i = 0; i < LA; ++i) {
-      const int cid = tid + i * NT;
-      const int row = cid / kChunksPerRow, c = cid % kChunksPerRow;
-      ra[i] = (cid < CH_A) ? load_chunk(p.w, p.ldw, n0 + row, p.N, k0 + 8 * c, p.b, p.ldb, p.K1, Ktot)
-                           : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < LB; ++i) {
-      const int cid = tid + i * NT;
-      const int row = cid / kChunksPerRow, c = cid % kChunksPerRow;
-      rb[i] = (cid < CH_B) ? load_chunk(p.x, p.ldx, m0 + row, p.M, k0 + 8 * c, p.t, p.ldt, p.K1, Ktot)
-                           : u32x4{0u, 0u, 0u, 0u};
-    }
+  // K-tiles outside [kt_begin, kt_end) are never stored; their loads read the
+  // (cached) matrix base so every iteration issues the same loads, which lets
+  // the compiler count outstanding loads exactly instead of draining them.
+  auto chunk_ok = [&](int i, int kt) {
+    const int row = chunk_row(i), kc = kt * kBK + 8 * chunk_col(i);
+    return (i < LA ? (n0 + row < p.N) : (m0 + row < p.M)) && kc < Ktot && kt < kt_end;
   };
-  auto sstore = [&](int stage) {
-    unsigned char* base = smem + stage * STAGE;
-#pragma unroll
-    for (int i = 0; i < LA; ++i) {
-      const int cid = tid + i * NT;
-      if (cid < CH_A) {
-        const int row = cid / kChunksPerRow, c = cid % kChunksPerRow;
-        *reinterpret_cast<u32x4*>(base + row * (kBK * 2) + ((c ^ (row & 7)) * 16)) = ra[i];
-      }
-    }
-    unsigned char* bb = base + BN * kBK * 2;
-#pragma unroll
-    for (int i = 0; i < LB; ++i) {
-      const int cid = tid + i * NT;
-      if (cid < CH_B) {
-        const int row = cid / kChunksPerRow, c = cid % kChunksPerRow;
-        *reinterpret_cast<u32x4*>(bb + row * (kBK * 2) + ((c ^ (row & 7)) * 16)) = rb[i];
-      }
-    }
+  auto gload1 = [&](u32x4 (&dst)[LT], int i, int kt) {
+    const int row = chunk_row(i), c = chunk_col(i);
+    const bool ok = chunk_ok(i, kt);
+    if (i < LA)
+      dst[i] = load_chunk_raw(p.w, p.ldw, p.b, p.ldb, n0 + row, ok, kt * kBK + 8 * c, p.K1);
+    else
+      dst[i] = load_chunk_raw(p.x, p.ldx, p.t, p.ldt, m0 + row, ok, kt * kBK + 8 * c, p.K1);
+  };
+  // LDS byte offset of 16-byte chunk c of tile row `row`: the chunk index is
+  // XOR-swizzled by row so that the 8 (or 16) rows one ds_read_b128 phase
+  // touches land in distinct banks under a 32- or a 64-bank LDS
+  auto lds_off = [](int row, int c) { return row * (kBK * 2) + ((c ^ (row & 7) ^ ((row >> 3) & 1)) * 16); };
+  // write chunk i of a register set holding K-tile kt, zeroing invalid chunks
+  auto sstore = [&](const u32x4 (&src)[LT], int stage, int i, int kt) {
+    const int row = chunk_row(i), c = chunk_col(i);
+    unsigned char* base = smem + stage * STAGE + (i < LA ? 0 : BN * kBK * 2);
+    const u32x4 v = chunk_ok(i, kt) ? src[i] : u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(base + lds_off(row, c)) = v;
   };
 
   const int lrow = lane & 31, lhalf = lane >> 5;
-  if (kt_begin < kt_end) {
-    gload(kt_begin);
-    sstore(0);
-    __syncthreads();
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
-      const int cur = (kt - kt_begin) & 1;
-      const bool more = kt + 1 < kt_end;
-      if (more) gload(kt + 1);
-      const unsigned char* As = smem + cur * STAGE;
-      const unsigned char* Bs = As + BN * kBK * 2;
+  auto read_frags = [&](const unsigned char* As, const unsigned char* Bs, int kk, bf16x8 (&fa)[FN],
+                        bf16x8 (&fb)[FM]) {
+    const int c = 2 * kk + lhalf;
 #pragma unroll
-      for (int kk = 0; kk < kBK / 16; ++kk) {
-        const int c = 2 * kk + lhalf;
-        bf16x8 fa[FN], fb[FM];
+    for (int i = 0; i < FN; ++i)
+      fa[i] = *reinterpret_cast<const bf16x8*>(As + lds_off(wn * TN + i * 32 + lrow, c));
 #pragma unroll
-        for (int i = 0; i < FN; ++i) {
-          const int row = wn * TN + i * 32 + lrow;
-          fa[i] = *reinterpret_cast<const bf16x8*>(As + row * (kBK * 2) + ((c ^ (row & 7)) * 16));
-        }
+    for (int j = 0; j < FM; ++j)
+      fb[j] = *reinterpret_cast<const bf16x8*>(Bs + lds_off(wm * TM + j * 32 + lrow, c));
+  };
+  // Compute one K-tile from LDS stage `cur`.  Interleaved with its MFMAs:
+  // the fragments of the next k-step (double-buffered), and chunk by chunk
+  // the LDS store of register set `set` (K-tile kt_next, into the other
+  // stage) followed, when RELOAD, by the load of K-tile kt_reload into the
+  // chunk just freed.  Stores past the last K-tile write zeros into the
+  // stage nobody reads again, which keeps each k-step one basic block.
+  auto compute = [&](auto reload_tag, int cur, u32x4 (&set)[LT], int kt_next, int kt_reload) {
+    constexpr bool RELOAD = decltype(reload_tag)::value;
+    const unsigned char* As = smem + cur * STAGE;
+    const unsigned char* Bs = As + BN * kBK * 2;
+    constexpr int NB = DBF ? 2 : 1;
+    bf16x8 fa[NB][FN], fb[NB][FM];
+    if constexpr (DBF) read_frags(As, Bs, 0, fa[0], fb[0]);
 #pragma unroll
-        for (int j = 0; j < FM; ++j) {
-          const int row = wm * TM + j * 32 + lrow;
-          fb[j] = *reinterpret_cast<const bf16x8*>(Bs + row * (kBK * 2) + ((c ^ (row & 7)) * 16));
-        }
-#pragma unroll
-        for (int i = 0; i < FN; ++i)
-#pragma unroll
-          for (int j = 0; j < FM; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int fb_cur = DBF ? (kk & 1) : 0;
+      if constexpr (DBF) {
+        if (kk + 1 < kBK / 16) read_frags(As, Bs, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+      } else {
+        read_frags(As, Bs, kk, fa[0], fb[0]);
       }
-      if (more) sstore(cur ^ 1);
-      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fb_cur][i], fb[fb_cur][j], acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int i = kk * LT / 4; i < (kk + 1) * LT / 4; ++i) {
+        sstore(set, cur ^ 1, i, kt_next);
+        if constexpr (RELOAD) gload1(set, i, kt_reload);
+      }
+      // one MFMA, then one of each pending memory op, repeated
+      const int nr = DBF ? ((kk + 1 < kBK / 16) ? FN + FM : 0) : 0;
+      const int nw = (kk + 1) * LT / 4 - kk * LT / 4;
+#pragma unroll
+      for (int q = 0; q < FN * FM; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (q < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (q < nw) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        if (RELOAD && q < nw) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+    }
+  };
+
+  if (kt_begin < kt_end) {
+    // prologue: K-tiles kt_begin .. kt_begin+P-1 into sets 0..P-1; tile 0 to LDS
+#pragma unroll
+    for (int s = 0; s < P; ++s)
+#pragma unroll
+      for (int i = 0; i < LT; ++i) gload1(reg[s], i, kt_begin + s);
+#pragma unroll
+    for (int i = 0; i < LT; ++i) {
+      sstore(reg[0], 0, i, kt_begin);
+      gload1(reg[0], i, kt_begin + P);
+    }
+    __syncthreads();
+    // invariant at iteration t (K-tile kt = kt_begin + t): LDS stage t & 1 holds
+    // tile kt; set (t + 1 + j) % P holds tile kt + 1 + j, j = 0..P-1
+    int kt0 = kt_begin;
+    for (; kt0 + P <= kt_end; kt0 += P) {
+#pragma unroll
+      for (int u = 0; u < P; ++u) {
+        const int kt = kt0 + u;
+        compute(std::true_type{}, (kt - kt_begin) & 1, reg[(u + 1) % P], kt + 1, kt + 1 + P);
+        __syncthreads();
+      }
+    }
+    // tail: fewer than P K-tiles left, all already in registers
+#pragma unroll
+    for (int u = 0; u + 1 < P; ++u) {
+      const int kt = kt0 + u;
+      if (kt < kt_end) {
+        compute(std::false_type{}, (kt - kt_begin) & 1, reg[(u + 1) % P], kt + 1, 0);
+        __syncthreads();
+      }
     }
   }
 
@@ -193,9 +251,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p
         const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
         if constexpr (MODE == 0) {
           uint16_t* dst = p.y + int64_t(m) * p.ldy + n;
-          if (n + 3 < p.N) {
-            uint32_t lo = pack_bf16x2(v0, v1), hi = pack_bf16x2(v2, v3);
-            *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+          if (p.y_vec && n + 3 < p.N) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
           } else {
             const float vv[4] = {v0, v1, v2, v3};
             for (int e = 0; e < 4; ++e)
@@ -216,10 +273,43 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p
   }
 }
 
+// y = bf16(sum_s part[s]) in split order; 4 consecutive outputs per thread.
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restrict__ part, int splits, int M, int N,
+                                                          uint16_t* __restrict__ y, int64_t ldy, int y_vec) {
+  const int64_t q = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t per_row = (N + 3) / 4;
+  if (q >= int64_t(M) * per_row) return;
+  const int m = int(q / per_row);
+  const int n = int(q - int64_t(m) * per_row) * 4;
+  const int64_t plane = int64_t(M) * N;
+  const float* src = part + int64_t(m) * N + n;
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+  if (n + 3 < N && (N & 3) == 0) {
+    for (int sp = 0; sp < splits; ++sp) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(src + sp * plane);
+      s[0] += v[0];
+      s[1] += v[1];
+      s[2] += v[2];
+      s[3] += v[3];
+    }
+  } else {
+    for (int sp = 0; sp < splits; ++sp)
+      for (int e = 0; e < 4; ++e)
+        if (n + e < N) s[e] += src[sp * plane + e];
+  }
+  uint16_t* dst = y + int64_t(m) * ldy + n;
+  if (y_vec && n + 3 < N) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]));
+  } else {
+    for (int e = 0; e < 4; ++e)
+      if (n + e < N) dst[e] = f32_to_bf16(s[e]);
+  }
+}
+
 // t[m, j] = bf16(scale * g[m] * sum_s part[s][m][j]); exact 0 for g = 0.
-__global__ __launch_bounds__(256) void lora_gate_kernel(const float* __restrict__ part, int splits, int M,
-                                                        int r, const uint8_t* __restrict__ gate,
-                                                        float scale, uint16_t* __restrict__ t) {
+__global__ __launch_bounds__(256) void lora_gate_kernel(const float* __restrict__ part, int splits, int M, int r,
+                                                        const uint8_t* __restrict__ gate, float scale,
+                                                        uint16_t* __restrict__ t) {
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (i >= int64_t(M) * r) return;
   const int m = int(i / r);
@@ -254,9 +344,8 @@ __global__ __launch_bounds__(256) void lora_down_f32_kernel(const float* __restr
 
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ x, int64_t ldx,
                                                        const float* __restrict__ w, int64_t ldw,
-                                                       const float* __restrict__ t,
-                                                       const float* __restrict__ b, int64_t ldb,
-                                                       int M, int N, int K, int r,
+                                                       const float* __restrict__ t, const float* __restrict__ b,
+                                                       int64_t ldb, int M, int N, int K, int r,
                                                        float* __restrict__ y, int64_t ldy) {
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (i >= int64_t(M) * N) return;
@@ -275,9 +364,30 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
   y[int64_t(m) * ldy + n] = acc;
 }
 
-template <int BM, int BN, int WM, int WN, int MODE>
-hipError_t run_gemm(GemmParams p, int splits, hipStream_t stream, const char* name) {
-  auto kern = gemm_bf16_kernel<BM, BN, WM, WN, MODE>;
+// ------------------------------------------------------------------ dispatch
+// Kernel configurations: block tile, wave grid, register prefetch depth
+// (K-tiles in flight, sized so loads have about 1 us to land) and fragment
+// double-buffering (off where it would push the tile past 512 registers).
+struct TileShape {
+  const char* name;
+  int bm, bn, waves;
+};
+constexpr TileShape kShapes[] = {
+    {"64x64w4", 64, 64, 4},          {"128x128w4", 128, 128, 4},      {"256x192w4", 256, 192, 4},
+    {"256x192w8", 256, 192, 8},      {"256x192w8p1", 256, 192, 8},    {"256x192w8p2d0", 256, 192, 8},
+    {"256x128w8", 256, 128, 8},      {"256x128w8p2d0", 256, 128, 8},  {"256x256w4", 256, 256, 4},
+    {"256x256w8p1", 256, 256, 8},
+};
+constexpr int kNumShapes = int(sizeof(kShapes) / sizeof(kShapes[0]));
+
+struct TileCfg {
+  int shape;   // index into kShapes
+  int splits;
+};
+
+template <int BM, int BN, int WM, int WN, int P, int DBF, int MODE>
+hipError_t launch_tile(GemmParams p, int splits, hipStream_t stream, const char* name) {
+  auto kern = gemm_bf16_kernel<BM, BN, WM, WN, P, DBF, MODE>;
   const size_t lds = 2 * size_t(BN + BM) * kBK * 2;
   static bool configured = false;
   if (!configured) {
@@ -288,12 +398,71 @@ hipError_t run_gemm(GemmParams p, int splits, hipStream_t stream, const char* na
   }
   p.tiles_m = (p.M + BM - 1) / BM;
   p.tiles_n = (p.N + BN - 1) / BN;
+  {
+    const char* env = getenv("UNO_GEMM_XCD");   // tuning override: 0 disables the remap
+    p.xcd_remap = env ? atoi(env) : 1;
+  }
   const int kt_total = (p.K1 + p.K2 + kBK - 1) / kBK;
   p.ktiles_per_split = (kt_total + splits - 1) / splits;
   dim3 grid(p.tiles_m * p.tiles_n, splits);
   ProfileScope ps(name, stream);
   hipLaunchKernelGGL(kern, grid, dim3(WM * WN * kWave), lds, stream, p);
   return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_cfg(const TileCfg& c, const GemmParams& p, hipStream_t stream, const char* name) {
+  switch (c.shape) {
+    case 0: return launch_tile<64, 64, 2, 2, 4, 1, MODE>(p, c.splits, stream, name);
+    case 1: return launch_tile<128, 128, 2, 2, 4, 1, MODE>(p, c.splits, stream, name);
+    case 2: return launch_tile<256, 192, 2, 2, 2, 0, MODE>(p, c.splits, stream, name);
+    case 3: return launch_tile<256, 192, 4, 2, 2, 1, MODE>(p, c.splits, stream, name);
+    case 4: return launch_tile<256, 192, 4, 2, 1, 1, MODE>(p, c.splits, stream, name);
+    case 5: return launch_tile<256, 192, 4, 2, 2, 0, MODE>(p, c.splits, stream, name);
+    case 6: return launch_tile<256, 128, 4, 2, 3, 1, MODE>(p, c.splits, stream, name);
+    case 7: return launch_tile<256, 128, 4, 2, 2, 0, MODE>(p, c.splits, stream, name);
+    case 8: return launch_tile<256, 256, 2, 2, 1, 0, MODE>(p, c.splits, stream, name);
+    case 9: return launch_tile<256, 256, 4, 2, 1, 0, MODE>(p, c.splits, stream, name);
+  }
+  return hipErrorInvalidValue;
+}
+
+int shape_index(const char* name) {
+  for (int i = 0; i < kNumShapes; ++i)
+    if (strcmp(kShapes[i].name, name) == 0) return i;
+  return -1;
+}
+
+// Main-GEMM configuration.  UNO_GEMM_TILE="<shape name>[/splits]" overrides
+// the choice (tuning sweeps).
+TileCfg choose_main_tile(int64_t M, int64_t N, int64_t Ktot) {
+  const char* env = getenv("UNO_GEMM_TILE");
+  if (env) {
+    char nm[32] = {0};
+    int s = 1;
+    const char* slash = strchr(env, '/');
+    const size_t len = slash ? size_t(slash - env) : strlen(env);
+    if (len < sizeof(nm)) {
+      memcpy(nm, env, len);
+      if (slash) s = atoi(slash + 1);
+      const int id = shape_index(nm);
+      if (id >= 0 && s >= 1 && s <= 16) return {id, s};
+    }
+  }
+  // Measured on MI355X at M = 1024: 256x256 tiles with 8 waves are fastest
+  // when they alone give >= 160 tiles (the 4096 -> 12288 projections); below
+  // that, 256x128 (8 waves) or 128x128 tiles with split-K up to 4 to reach
+  // ~200 work units, keeping >= 16 K-tiles per split.
+  auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  const int64_t kt = (Ktot + kBK - 1) / kBK;
+  auto splits_for = [&](int64_t t) {
+    int s = 1;
+    while (t * s < 200 && s < 4 && kt / (2 * s) >= 16) s *= 2;
+    return s;
+  };
+  if (M >= 512 && N % 256 == 0 && tiles(256, 256) >= 160) return {9, 1};
+  if (M >= 512 && N % 128 == 0) return {7, splits_for(tiles(256, 128))};
+  return {1, splits_for(tiles(128, 128))};
 }
 
 int lora_down_splits(int64_t M, int64_t r, int64_t K) {
@@ -309,11 +478,15 @@ int lora_down_splits(int64_t M, int64_t r, int64_t K) {
 }  // namespace
 
 size_t gated_lora_workspace_bytes(uno_dtype dtype, int64_t M, int64_t N, int64_t K, int64_t r) {
-  (void)N;
-  if (r == 0) return 0;
-  if (dtype == UNO_F32) return align_up(size_t(M) * size_t(r) * 4, 256);
-  const int s = lora_down_splits(M, r, K);
-  return align_up(size_t(M) * size_t(r) * 2, 256) + align_up(size_t(s) * size_t(M) * size_t(r) * 4, 256);
+  if (dtype == UNO_F32) return r == 0 ? 0 : align_up(size_t(M) * size_t(r) * 4, 256);
+  size_t bytes = 0;
+  if (r > 0) {
+    const int s = lora_down_splits(M, r, K);
+    bytes += align_up(size_t(M) * size_t(r) * 2, 256) + align_up(size_t(s) * size_t(M) * size_t(r) * 4, 256);
+  }
+  const TileCfg c = choose_main_tile(M, N, K + r);
+  if (c.splits > 1) bytes += align_up(size_t(c.splits) * size_t(M) * size_t(N) * 4, 256);
+  return bytes;
 }
 
 hipError_t launch_gated_lora(const GatedLoraArgs& a, hipStream_t stream) {
@@ -325,8 +498,8 @@ hipError_t launch_gated_lora(const GatedLoraArgs& a, hipStream_t stream) {
       const int64_t n = a.M * a.r;
       ProfileScope ps("uno_lora_down_f32", stream);
       hipLaunchKernelGGL(lora_down_f32_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream,
-                         static_cast<const float*>(a.x), a.ldx, static_cast<const float*>(a.a), a.lda,
-                         a.gate, a.lora_scale, int(a.M), int(a.K), int(a.r), t);
+                         static_cast<const float*>(a.x), a.ldx, static_cast<const float*>(a.a), a.lda, a.gate,
+                         a.lora_scale, int(a.M), int(a.K), int(a.r), t);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -334,16 +507,19 @@ hipError_t launch_gated_lora(const GatedLoraArgs& a, hipStream_t stream) {
     ProfileScope ps("uno_gemm_f32", stream);
     hipLaunchKernelGGL(gemm_f32_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream,
                        static_cast<const float*>(a.x), a.ldx, static_cast<const float*>(a.w), a.ldw, t,
-                       static_cast<const float*>(a.b), a.ldb, int(a.M), int(a.N), int(a.K),
-                       lora ? int(a.r) : 0, static_cast<float*>(a.y), a.ldy);
+                       static_cast<const float*>(a.b), a.ldb, int(a.M), int(a.N), int(a.K), lora ? int(a.r) : 0,
+                       static_cast<float*>(a.y), a.ldy);
     return hipGetLastError();
   }
 
+  char* ws = static_cast<char*>(a.ws);
   uint16_t* t = nullptr;
   if (lora) {
     const int splits = lora_down_splits(a.M, a.r, a.K);
-    t = static_cast<uint16_t*>(a.ws);
-    float* part = reinterpret_cast<float*>(static_cast<char*>(a.ws) + align_up(size_t(a.M) * a.r * 2, 256));
+    t = reinterpret_cast<uint16_t*>(ws);
+    ws += align_up(size_t(a.M) * a.r * 2, 256);
+    float* part = reinterpret_cast<float*>(ws);
+    ws += align_up(size_t(splits) * size_t(a.M) * size_t(a.r) * 4, 256);
     GemmParams d{};
     d.M = int(a.M);
     d.N = int(a.r);
@@ -354,13 +530,13 @@ hipError_t launch_gated_lora(const GatedLoraArgs& a, hipStream_t stream) {
     d.w = static_cast<const uint16_t*>(a.a);
     d.ldw = a.lda;
     d.part = part;
-    hipError_t e = run_gemm<64, 64, 2, 2, 1>(d, splits, stream, "uno_lora_down_bf16");
+    hipError_t e = launch_cfg<1>(TileCfg{0, splits}, d, stream, "uno_lora_down_bf16");
     if (e != hipSuccess) return e;
     const int64_t n = a.M * a.r;
     {
       ProfileScope ps("uno_lora_gate", stream);
-      hipLaunchKernelGGL(lora_gate_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream, part,
-                         splits, int(a.M), int(a.r), a.gate, a.lora_scale, t);
+      hipLaunchKernelGGL(lora_gate_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream, part, splits,
+                         int(a.M), int(a.r), a.gate, a.lora_scale, t);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -374,13 +550,23 @@ hipError_t launch_gated_lora(const GatedLoraArgs& a, hipStream_t stream) {
   g.ldx = a.ldx;
   g.w = static_cast<const uint16_t*>(a.w);
   g.ldw = a.ldw;
-  g.t = t;
-  g.ldt = a.r;
-  g.b = static_cast<const uint16_t*>(a.b);
-  g.ldb = a.ldb;
+  g.t = lora ? t : g.x;
+  g.ldt = lora ? a.r : a.ldx;
+  g.b = lora ? static_cast<const uint16_t*>(a.b) : g.w;
+  g.ldb = lora ? a.ldb : a.ldw;
   g.y = static_cast<uint16_t*>(a.y);
   g.ldy = a.ldy;
-  return run_gemm<128, 128, 2, 2, 0>(g, 1, stream, "uno_gemm_bf16");
+  g.y_vec = (a.ldy % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.y) & 7u) == 0);
+  const TileCfg c = choose_main_tile(a.M, a.N, a.K + g.K2);
+  if (c.splits == 1) return launch_cfg<0>(c, g, stream, "uno_gemm_bf16");
+  g.part = reinterpret_cast<float*>(ws);
+  hipError_t e = launch_cfg<1>(c, g, stream, "uno_gemm_bf16_splitk");
+  if (e != hipSuccess) return e;
+  const int64_t quads = a.M * ((a.N + 3) / 4);
+  ProfileScope ps("uno_gemm_reduce", stream);
+  hipLaunchKernelGGL(gemm_reduce_kernel, dim3(unsigned((quads + 255) / 256)), dim3(256), 0, stream, g.part, c.splits,
+                     int(a.M), int(a.N), g.y, g.ldy, g.y_vec);
+  return hipGetLastError();
 }
 
 }  // namespace uno

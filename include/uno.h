@@ -75,8 +75,8 @@ const char* uno_last_error(void);
  *         draft row (adapter on).  NULL = all rows 0.  r = 0 is allowed (A, B
  *         unused, may be NULL): a plain GEMM.
  * Requirements: M, N, K >= 1, r >= 0.  UNO_BF16 also needs K and r multiples
- * of 8, all leading dimensions multiples of 8 and 16-byte aligned base
- * pointers (else UNO_ERR_UNSUPPORTED).
+ * of 8, ldx, ldw, lda, ldb multiples of 8 and 16-byte aligned x, W, A, B
+ * (else UNO_ERR_UNSUPPORTED); y and ldy are unconstrained.
  * Rows whose gate is 0 give results bit-identical to the same call with r = 0.
  * ------------------------------------------------------------------------ */
 uno_status uno_gated_lora_linear_workspace(uno_dtype dtype, int64_t M, int64_t N, int64_t K,

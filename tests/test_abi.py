@@ -84,6 +84,7 @@ def test_gated_lora_rejects_bad_calls(lib):
     assert _gl(lib, ldx=8) == INVALID                            # ldx < K
     assert _gl(lib, ldy=12) == INVALID
     assert _gl(lib, ldx=20) == UNSUPPORTED                       # bf16 ld not multiple of 8
+    assert _gl(lib, y=ctypes.c_void_p(0x10001)) == INVALID         # y must be 2-byte aligned
     assert _gl(lib, x=FAKE16.value + 2) == UNSUPPORTED            # misaligned
     assert _gl(lib, wsb=0) == WORKSPACE
     assert _gl(lib, ws=None) == WORKSPACE

@@ -1,7 +1,9 @@
 """GPU parity: uno_tree_verify_attention and uno_psi_spec_verify_tree.
 
 Attention bar: per (node, head) row, ||o - o_ref||_inf / ||o_ref||_inf <= 2e-2
-(bf16 output); LSE within 1e-5 relative (fp32).  Tree verify bar: accepted
+(bf16 output); LSE (fp32) within 1e-5 * max(1, |lse|): the log-sum-exp carries
+the absolute rounding of the fp32 scores (~|s| 2^-24 sqrt(head_dim)), so the
+fp32 relative bound is taken with a floor of 1 for values near zero.  Tree verify bar: accepted
 length, path and token bit-exact unless the oracle reaches the GPU's outcome
 with one visited uniform moved by at most 1e-5 (a near-tie, counted).
 """
@@ -25,6 +27,11 @@ def _attn(dad, c):
     return to_host(out), to_host(lse)
 
 
+def _check_lse(lse, ref):
+    err = np.abs(lse - ref) / np.maximum(1.0, np.abs(ref))
+    assert np.max(err) <= 1e-5, f"lse err {np.max(err):.3g}"
+
+
 def _attn_ref(c):
     return oracle.tree_attention(c["q_f32"], c["k_cache_f32"], c["v_cache_f32"], c["k_tree_f32"],
                                  c["v_tree_f32"], c["parent"], c["scale"])
@@ -40,7 +47,7 @@ def test_attention_tree_workload(gpu_lib):
     err = row_relerr(o, ro)
     say(f"  row rel err {err:.3g}")
     assert err <= 2e-2
-    np.testing.assert_allclose(lse, rl, rtol=1e-5)
+    _check_lse(lse, rl)
 
 
 @pytest.mark.parametrize("name,n,ctx,nh,nkv,batch", [
@@ -67,7 +74,7 @@ def test_attention_shapes(gpu_lib, name, n, ctx, nh, nkv, batch):
     o, lse = _attn(gpu_lib, c)
     ro, rl = _attn_ref(c)
     assert row_relerr(o, ro) <= 2e-2
-    np.testing.assert_allclose(lse, rl, rtol=1e-5)
+    _check_lse(lse, rl)
 
 
 def test_attention_malformed_tree_gives_nan(gpu_lib):
