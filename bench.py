@@ -102,8 +102,9 @@ def main():
     tv_out = {"accept_len": torch.empty(1, dtype=torch.int32, device=dev),
               "path": torch.empty((1, tv["max_depth"]), dtype=torch.int32, device=dev),
               "token": torch.empty(1, dtype=torch.int32, device=dev)}
-    tv_ws = torch.empty(dad.psi_spec_verify_tree_workspace(1, tv["n"], tv["max_depth"], VOCAB), dtype=torch.uint8,
-                        device=dev)
+    tv_maxc = workloads.max_children(parent)
+    tv_ws = torch.empty(dad.psi_spec_verify_tree_workspace(1, tv["n"], tv["max_depth"], tv_maxc, VOCAB),
+                        dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     log(f"all inputs resident ({time.time() - t0:.1f}s)")
 
@@ -115,7 +116,7 @@ def main():
         dad.tree_verify_attention(ta_dev["q"], ta_dev["k_cache"], ta_dev["v_cache"], ta_dev["k_tree"],
                                   ta_dev["v_tree"], ta_dev["parent"], ta["scale"], out=ta_out, lse=ta_lse)
         dad.psi_spec_verify_tree(tv_dev["parent"], tv_dev["tokens"], tv_dev["p"], tv_dev["q"], tv_dev["u_acc"],
-                                 tv_dev["u_s"], outputs=tv_out, workspace=tv_ws)
+                                 tv_dev["u_s"], max_children=tv_maxc, outputs=tv_out, workspace=tv_ws)
 
     # ------------------------------------------------------------ warmup + per-kernel breakdown
     for _ in range(args.warmup):
@@ -129,8 +130,8 @@ def main():
         step()
     torch.cuda.synchronize()
     kernels = ["uno_gemm_bf16", "uno_gemm_reduce", "uno_lora_down_bf16", "uno_lora_gate", "uno_row_stats",
-               "uno_accept_residual", "uno_tree_attention", "uno_tree_stats", "uno_tree_residual",
-               "uno_tree_walk_draw"]
+               "uno_accept", "uno_draw_seg", "uno_draw_resolve", "uno_tree_attention", "uno_tree_setup",
+               "uno_tree_stats", "uno_tree_round", "uno_tree_walk", "uno_tree_draw"]
     breakdown = {}
     for kname in kernels:
         ms, cnt = dad.profile_query(kname)
@@ -189,7 +190,8 @@ def main():
 
     gemm_ms = (breakdown["uno_gemm_bf16"] + breakdown["uno_gemm_reduce"] + breakdown["uno_lora_down_bf16"]
                + breakdown["uno_lora_gate"])
-    sampler_ms = breakdown["uno_row_stats"] + breakdown["uno_accept_residual"]
+    sampler_ms = (breakdown["uno_row_stats"] + breakdown["uno_accept"] + breakdown["uno_draw_seg"]
+                  + breakdown["uno_draw_resolve"])
     components = {
         "gated_lora_layer": {"us": gemm_ms * 1e3, "tflops": gemm_flops_step / (gemm_ms * 1e-3) / 1e12,
                              "mfma_frac": gemm_flops_step / (gemm_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
@@ -199,8 +201,8 @@ def main():
                           "row_stats_hbm_frac": sampler_bytes / (breakdown["uno_row_stats"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                           "mean_accept_len": float(np.mean(L)), "tokens": int(np.sum(L + 1))},
         "tree": {"attention_us": breakdown["uno_tree_attention"] * 1e3,
-                 "verify_us": (breakdown["uno_tree_stats"] + breakdown["uno_tree_residual"]
-                               + breakdown["uno_tree_walk_draw"]) * 1e3, "accept_len": tl},
+                 "verify_us": (breakdown["uno_tree_setup"] + breakdown["uno_tree_stats"] + breakdown["uno_tree_round"]
+                               + breakdown["uno_tree_walk"] + breakdown["uno_tree_draw"]) * 1e3, "accept_len": tl},
         "kernel_ms_per_step": breakdown,
     }
 

@@ -58,8 +58,8 @@ def _declare(lib):
                                                                ctypes.POINTER(_sz)]),
         "uno_tree_verify_attention": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _i32, _i32,
                                                      _p, _p, _p, _p, _p, _p, _f32, _p, _p, _p, _sz]),
-        "uno_psi_spec_verify_tree_workspace": (ctypes.c_int, [_i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
-        "uno_psi_spec_verify_tree": (ctypes.c_int, [_p, ctypes.c_int, _i32, _i32, _i32, _i32,
+        "uno_psi_spec_verify_tree_workspace": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
+        "uno_psi_spec_verify_tree": (ctypes.c_int, [_p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32,
                                                     _p, _p, _p, _p, _p, _p, _f32, _p, _p, _p, _p, _sz]),
         "uno_profile_enable": (None, [ctypes.c_int, ctypes.c_char_p]),
         "uno_profile_reset": (None, []),
@@ -235,19 +235,21 @@ def tree_verify_attention(q, k_cache, v_cache, k_tree, v_tree, parent, softmax_s
 
 
 # ------------------------------------------------------------------ tree verify
-def psi_spec_verify_tree_workspace(batch, n_tree, max_depth, vocab):
+def psi_spec_verify_tree_workspace(batch, n_tree, max_depth, max_children, vocab):
     load()
     out = _sz(0)
-    _check(_lib.uno_psi_spec_verify_tree_workspace(batch, n_tree, max_depth, vocab, ctypes.byref(out)))
+    _check(_lib.uno_psi_spec_verify_tree_workspace(batch, n_tree, max_depth, max_children, vocab,
+                                                   ctypes.byref(out)))
     return out.value
 
 
 def psi_spec_verify_tree(parent, tokens, p_logits, q_logits, u_accept, u_sample, temperature=1.0,
-                         outputs=None, workspace=None, stream=None):
+                         max_children=None, outputs=None, workspace=None, stream=None):
     """Tree Psi-Spec verify (uno_psi_spec_verify_tree).
 
     parent, tokens int32 [B, n]; p_logits [B, n, V]; q_logits [B, D, V]
-    (contiguous); u_accept f32 [B, n]; u_sample f32 [B].
+    (contiguous); u_accept f32 [B, n]; u_sample f32 [B].  max_children: bound
+    on the children of any node (None: n - 1).
     Returns dict: accept_len [B], path [B, D], token [B] (int32 device tensors).
     """
     import torch
@@ -255,15 +257,17 @@ def psi_spec_verify_tree(parent, tokens, p_logits, q_logits, u_accept, u_sample,
     bsz, n, vocab = p_logits.shape
     dmax = q_logits.shape[1]
     dev = p_logits.device
+    if max_children is None:
+        max_children = max(n - 1, 0)
     if outputs is None:
         outputs = {
             "accept_len": torch.empty(bsz, dtype=torch.int32, device=dev),
             "path": torch.empty((bsz, dmax), dtype=torch.int32, device=dev),
             "token": torch.empty(bsz, dtype=torch.int32, device=dev),
         }
-    ws = _workspace(psi_spec_verify_tree_workspace(bsz, n, dmax, vocab), dev, workspace)
+    ws = _workspace(psi_spec_verify_tree_workspace(bsz, n, dmax, max_children, vocab), dev, workspace)
     _check(_lib.uno_psi_spec_verify_tree(
-        _stream(stream), _dtype_code(p_logits), bsz, n, dmax, vocab,
+        _stream(stream), _dtype_code(p_logits), bsz, n, dmax, max_children, vocab,
         _ptr(parent), _ptr(tokens), _ptr(p_logits), _ptr(q_logits), _ptr(u_accept), _ptr(u_sample),
         float(temperature), _ptr(outputs["accept_len"]), _ptr(outputs["path"]), _ptr(outputs["token"]),
         _ptr(ws), _nbytes(ws)))

@@ -143,7 +143,7 @@ uno_status uno_psi_spec_verify_linear_workspace(int32_t batch, int32_t k, int32_
   if (!bytes) return fail(UNO_ERR_INVALID_ARGUMENT, "bytes is NULL");
   uno_status s = check_verify_linear_shape(batch, k, vocab);
   if (s != UNO_OK) return s;
-  *bytes = verify_linear_workspace_bytes(batch, k);
+  *bytes = verify_linear_workspace_bytes(batch, k, vocab);
   return UNO_OK;
   UNO_GUARD_END
 }
@@ -170,7 +170,7 @@ uno_status uno_psi_spec_verify_linear(hipStream_t stream, uno_dtype logit_dtype,
     return fail(UNO_ERR_INVALID_ARGUMENT, "p strides must cover [k+1][vocab]");
   if (k > 0 && (q_row_stride < vocab || q_seq_stride < int64_t(k) * q_row_stride))
     return fail(UNO_ERR_INVALID_ARGUMENT, "q strides must cover [k][vocab]");
-  const size_t need = verify_linear_workspace_bytes(batch, k);
+  const size_t need = verify_linear_workspace_bytes(batch, k, vocab);
   if (workspace_bytes < need || !workspace)
     return fail(UNO_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
   VerifyLinearArgs a{};
@@ -193,7 +193,7 @@ uno_status uno_psi_spec_verify_linear(hipStream_t stream, uno_dtype logit_dtype,
   a.out_pd = out_p_draft;
   a.out_qd = out_q_draft;
   a.out_mass = out_residual_mass;
-  a.stats = static_cast<RowStat*>(workspace);
+  a.ws = workspace;
   return check_hip(launch_verify_linear(a, stream), "uno_psi_spec_verify_linear launch");
   UNO_GUARD_END
 }
@@ -264,9 +264,13 @@ uno_status uno_tree_verify_attention(hipStream_t stream, int32_t batch, int32_t 
 }
 
 // ------------------------------------------------------------------ tree verify
-static uno_status check_tree_verify_shape(int32_t batch, int32_t n_tree, int32_t max_depth, int32_t vocab) {
+static uno_status check_tree_verify_shape(int32_t batch, int32_t n_tree, int32_t max_depth, int32_t max_children,
+                                          int32_t vocab) {
   if (batch < 1 || n_tree < 1 || max_depth < 1 || vocab < 1)
     return fail(UNO_ERR_INVALID_ARGUMENT, "batch, n_tree, max_depth and vocab must be >= 1");
+  if (max_children < 0 || max_children > 1023)
+    return fail(UNO_ERR_INVALID_ARGUMENT, "max_children must be in 0..1023 (got %d)", max_children);
+  if (batch > 65535) return fail(UNO_ERR_UNSUPPORTED, "batch above 65535");
   if (n_tree > 1024) return fail(UNO_ERR_UNSUPPORTED, "n_tree above 1024 (got %d)", n_tree);
   if (max_depth > 64) return fail(UNO_ERR_UNSUPPORTED, "max_depth above 64 (got %d)", max_depth);
   if (vocab > (1 << 20)) return fail(UNO_ERR_UNSUPPORTED, "vocab above 2^20 (got %d)", vocab);
@@ -274,33 +278,34 @@ static uno_status check_tree_verify_shape(int32_t batch, int32_t n_tree, int32_t
   return UNO_OK;
 }
 
-uno_status uno_psi_spec_verify_tree_workspace(int32_t batch, int32_t n_tree, int32_t max_depth, int32_t vocab,
-                                              size_t* bytes) {
+uno_status uno_psi_spec_verify_tree_workspace(int32_t batch, int32_t n_tree, int32_t max_depth, int32_t max_children,
+                                              int32_t vocab, size_t* bytes) {
   UNO_GUARD_BEGIN
   if (!bytes) return fail(UNO_ERR_INVALID_ARGUMENT, "bytes is NULL");
-  uno_status s = check_tree_verify_shape(batch, n_tree, max_depth, vocab);
+  uno_status s = check_tree_verify_shape(batch, n_tree, max_depth, max_children, vocab);
   if (s != UNO_OK) return s;
-  *bytes = tree_verify_workspace_bytes(batch, n_tree, max_depth, vocab);
+  *bytes = tree_verify_workspace_bytes(batch, n_tree, max_depth, max_children, vocab);
   return UNO_OK;
   UNO_GUARD_END
 }
 
 uno_status uno_psi_spec_verify_tree(hipStream_t stream, uno_dtype logit_dtype, int32_t batch, int32_t n_tree,
-                                    int32_t max_depth, int32_t vocab, const int32_t* parent, const int32_t* tokens,
-                                    const void* p_logits, const void* q_logits, const float* u_accept,
-                                    const float* u_sample, float temperature, int32_t* out_accept_len,
-                                    int32_t* out_path, int32_t* out_token, void* workspace, size_t workspace_bytes) {
+                                    int32_t max_depth, int32_t max_children, int32_t vocab, const int32_t* parent,
+                                    const int32_t* tokens, const void* p_logits, const void* q_logits,
+                                    const float* u_accept, const float* u_sample, float temperature,
+                                    int32_t* out_accept_len, int32_t* out_path, int32_t* out_token, void* workspace,
+                                    size_t workspace_bytes) {
   UNO_GUARD_BEGIN
   if (logit_dtype != UNO_F32 && logit_dtype != UNO_BF16)
     return fail(UNO_ERR_INVALID_ARGUMENT, "unknown dtype %d", int(logit_dtype));
-  uno_status s = check_tree_verify_shape(batch, n_tree, max_depth, vocab);
+  uno_status s = check_tree_verify_shape(batch, n_tree, max_depth, max_children, vocab);
   if (s != UNO_OK) return s;
   if (!parent || !tokens || !p_logits || !q_logits || !u_accept || !u_sample || !out_accept_len || !out_path ||
       !out_token)
     return fail(UNO_ERR_INVALID_ARGUMENT, "required pointer is NULL");
   if (!(temperature > 0.f) || !std::isfinite(temperature))
     return fail(UNO_ERR_INVALID_ARGUMENT, "temperature must be finite and > 0");
-  const size_t need = tree_verify_workspace_bytes(batch, n_tree, max_depth, vocab);
+  const size_t need = tree_verify_workspace_bytes(batch, n_tree, max_depth, max_children, vocab);
   if (workspace_bytes < need || !workspace)
     return fail(UNO_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
   TreeVerifyArgs a{};
@@ -308,6 +313,7 @@ uno_status uno_psi_spec_verify_tree(hipStream_t stream, uno_dtype logit_dtype, i
   a.batch = batch;
   a.n_tree = n_tree;
   a.max_depth = max_depth;
+  a.max_children = max_children;
   a.vocab = vocab;
   a.parent = parent;
   a.tokens = tokens;

@@ -84,6 +84,21 @@ __device__ __forceinline__ void wave_lse2(float& m, float& s) {
   lse2_merge(m, s, m2, s2);
 }
 
+// Butterfly within aligned groups of `width` lanes (a power of two <= 64,
+// uniform across the wave); every lane of a group ends with the same bits.
+__device__ __forceinline__ void group_lse2(float& m, float& s, int width) {
+  if (width > 1) lse2_step_swz<1>(m, s);
+  if (width > 2) lse2_step_swz<2>(m, s);
+  if (width > 4) lse2_step_swz<4>(m, s);
+  if (width > 8) lse2_step_swz<8>(m, s);
+  if (width > 16) lse2_step_swz<16>(m, s);
+  if (width > 32) {
+    float m2 = __shfl_xor(m, 32);
+    float s2 = __shfl_xor(s, 32);
+    lse2_merge(m, s, m2, s2);
+  }
+}
+
 // Inclusive prefix sum over the 64 lanes in lane order (Hillis-Steele; fixed order).
 __device__ __forceinline__ float wave_inclusive_scan(float v) {
   const int lane = threadIdx.x & 63;

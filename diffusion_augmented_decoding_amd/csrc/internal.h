@@ -46,9 +46,9 @@ struct VerifyLinearArgs {
   float* out_pd;
   float* out_qd;
   float* out_mass;
-  RowStat* stats;     // workspace, batch * (2k + 1)
+  void* ws;           // workspace (verify_linear_workspace_bytes)
 };
-size_t verify_linear_workspace_bytes(int batch, int k);
+size_t verify_linear_workspace_bytes(int batch, int k, int vocab);
 hipError_t launch_verify_linear(const VerifyLinearArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- gated LoRA
@@ -87,7 +87,7 @@ hipError_t launch_tree_attention(const TreeAttnArgs& a, hipStream_t stream);
 // ---------------------------------------------------------------- tree verify
 struct TreeVerifyArgs {
   uno_dtype dtype;
-  int batch, n_tree, max_depth, vocab;
+  int batch, n_tree, max_depth, max_children, vocab;
   const int32_t* parent;
   const int32_t* tokens;
   const void* p;
@@ -100,7 +100,7 @@ struct TreeVerifyArgs {
   int32_t* out_tok;
   void* ws; size_t ws_bytes;
 };
-size_t tree_verify_workspace_bytes(int batch, int n_tree, int max_depth, int vocab);
+size_t tree_verify_workspace_bytes(int batch, int n_tree, int max_depth, int max_children, int vocab);
 hipError_t launch_tree_verify(const TreeVerifyArgs& a, hipStream_t stream);
 
 }  // namespace uno

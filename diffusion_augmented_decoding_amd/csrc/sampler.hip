@@ -5,124 +5,184 @@
 // distribution, longest accepted prefix, correction drawn from the residual
 // (standard speculative sampling, Leviathan et al. 2023).
 //
-// Two launches on the caller's stream:
-//  1. row_stats: one workgroup per logit row (batch * (2k+1) rows).  A single
-//     streaming pass computes the row's softmax statistics in the log2 domain
-//     (max m, sum s of 2^(y-m), y = logit * log2(e)/T) and gathers the draft
-//     token's logit.  This pass moves ~94% of the sampler's bytes and is
-//     HBM-bound: 16-byte non-temporal loads, 4 loads in flight per thread,
-//     one rescale per 4 vectors.
-//  2. accept_residual: one workgroup per sequence.  Wave 0 evaluates the k
-//     accept tests u*q(d) < p(d) and finds the first rejection with a ballot;
-//     then the workgroup streams the one or two rows the correction is drawn
-//     from and resolves the inverse CDF in token order (block_draw).
+// Four launches on the caller's stream:
+//  1. stats: one workgroup per (logit row, 8192-element chunk): softmax
+//     partials (max, sum of 2^(y - max), y = logit * log2(e) / T) in a single
+//     streaming pass with 16-byte non-temporal loads, plus the draft token's
+//     logit from the chunk that holds it.  This pass moves ~94% of the
+//     sampler's bytes and is HBM-bound.
+//  2. accept: one wave per sequence merges each row's chunk partials in a
+//     fixed order, evaluates the k accept tests u * q(d) < p(d), finds the
+//     first rejection with a ballot, and describes the row pair the
+//     correction (or bonus) is drawn from.
+//  3. draw_seg: one workgroup per (sequence, chunk): masses of the residual
+//     w = max(0, p_L - q_L) (or of p for a bonus) over 512-element segments.
+//  4. draw_resolve: one wave per sequence: inverse CDF in token order over the
+//     segment masses, then within one re-read segment.
 #include "sampler_common.h"
 
 namespace uno {
 
 namespace {
 
+struct LinWs {
+  float2* part;     // [rows][nchunk]
+  float* xd;        // [rows] draft logit (p rows 0..k-1, q rows)
+  DrawDesc* desc;   // [batch]
+  float* seg;       // [batch][nchunk][32]
+};
+
+LinWs lin_ws(void* base, int batch, int k, int vocab) {
+  const int rows = batch * (2 * k + 1);
+  const int nc = stats_splits(rows, vocab);
+  char* p = static_cast<char*>(base);
+  LinWs w;
+  w.part = reinterpret_cast<float2*>(p);
+  p += align_up(size_t(rows) * nc * sizeof(float2), 256);
+  w.xd = reinterpret_cast<float*>(p);
+  p += align_up(size_t(rows) * sizeof(float), 256);
+  w.desc = reinterpret_cast<DrawDesc*>(p);
+  p += align_up(size_t(batch) * sizeof(DrawDesc), 256);
+  w.seg = reinterpret_cast<float*>(p);
+  return w;
+}
+
+// row r of sequence b: j <= k -> p row j, else q row j - k - 1
 template <typename T>
-__global__ __launch_bounds__(kStatThreads) void row_stats_kernel(VerifyLinearArgs a) {
-  const int rps = 2 * a.k + 1;
-  const int row = blockIdx.x;
-  const int b = row / rps;
-  const int j = row - b * rps;
-  const T* base;
-  int draft = -1;
+__device__ __forceinline__ const T* lin_row(const VerifyLinearArgs& a, int b, int j, int* draft) {
   if (j <= a.k) {
-    base = static_cast<const T*>(a.p) + int64_t(b) * a.p_seq + int64_t(j) * a.p_row;
-    if (j < a.k) draft = a.drafts[int64_t(b) * a.k + j];
-  } else {
-    const int i = j - a.k - 1;
-    base = static_cast<const T*>(a.q) + int64_t(b) * a.q_seq + int64_t(i) * a.q_row;
-    draft = a.drafts[int64_t(b) * a.k + i];
+    *draft = (j < a.k) ? a.drafts[int64_t(b) * a.k + j] : -1;
+    return static_cast<const T*>(a.p) + int64_t(b) * a.p_seq + int64_t(j) * a.p_row;
   }
-  row_stats_body<T>(base, a.vocab, a.scale_log2, draft, a.stats + row);
+  const int i = j - a.k - 1;
+  *draft = a.drafts[int64_t(b) * a.k + i];
+  return static_cast<const T*>(a.q) + int64_t(b) * a.q_seq + int64_t(i) * a.q_row;
 }
 
 template <typename T>
-__global__ __launch_bounds__(kDrawThreads) void accept_residual_kernel(VerifyLinearArgs a) {
-  __shared__ DrawShared sh;
-  __shared__ int sh_L;
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int k = a.k;
-  const float sl2 = a.scale_log2;
-  const RowStat* st = a.stats + int64_t(b) * (2 * k + 1);
-
-  if (wave == 0) {
-    bool rej = false;
-    if (lane < k) {
-      const RowStat sp = st[lane];
-      const RowStat sq = st[k + 1 + lane];
-      const float pd = fast_exp2(fmaf(sp.yd, sl2, -sp.m)) / sp.s;
-      const float qd = fast_exp2(fmaf(sq.yd, sl2, -sq.m)) / sq.s;
-      const float u = a.u_acc[int64_t(b) * k + lane];
-      rej = !(u * qd < pd);
-      if (a.out_pd) a.out_pd[int64_t(b) * k + lane] = pd;
-      if (a.out_qd) a.out_qd[int64_t(b) * k + lane] = qd;
+__global__ __launch_bounds__(kChunkThreads) void lin_stats_kernel(VerifyLinearArgs a, LinWs w) {
+  const int row = blockIdx.x, c = blockIdx.y;
+  const int nc = gridDim.y;
+  const int rps = 2 * a.k + 1;
+  const int b = row / rps, j = row - b * rps;
+  int draft;
+  const T* base = lin_row<T>(a, b, j, &draft);
+  const int span = split_span(a.vocab, nc);
+  const int lo = c * span, hi = min(a.vocab, lo + span);
+  const float2 r = range_stats<T>(base, lo, hi, a.scale_log2);
+  if (threadIdx.x == 0) {
+    w.part[int64_t(row) * nc + c] = r;
+    if (j != a.k) {   // rows that score a draft
+      const bool in_range = draft >= 0 && draft < a.vocab;
+      if (in_range && draft >= lo && draft < hi) w.xd[row] = load_logit<T>(base, draft);
+      if (!in_range && c == 0) w.xd[row] = -INFINITY;   // out-of-range id: probability 0, rejected
     }
-    const uint64_t mask = wave_ballot(rej);
-    if (lane == 0) sh_L = mask ? int(__builtin_ctzll(mask)) : k;
+  }
+}
+
+constexpr int kAcceptWaves = 4;
+constexpr int kMaxRows = 2 * 64 + 1;
+
+template <typename T>
+__global__ __launch_bounds__(kAcceptWaves * kWave) void lin_accept_kernel(VerifyLinearArgs a, LinWs w) {
+  __shared__ float sm[kMaxRows], ss[kMaxRows];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int k = a.k, rps = 2 * k + 1;
+  const int nc = stats_splits(a.batch * rps, a.vocab);
+  const float sl2 = a.scale_log2;
+  const int64_t r0 = int64_t(b) * rps;
+  // per-draft inputs, loaded before the merge so their latency overlaps it
+  float xp = 0.f, xq = 0.f, u = 0.f;
+  if (wave == 0 && lane < k) {
+    xp = w.xd[r0 + lane];
+    xq = w.xd[r0 + k + 1 + lane];
+    u = a.u_acc[int64_t(b) * k + lane];
+  }
+  // merge every row's split partials: a group of `gw` lanes per row (all rows
+  // at once), each lane folding splits sub, sub + gw, ... then a butterfly
+  int gw = 1;
+  while (gw < kWave && 2 * gw * rps <= kAcceptWaves * kWave) gw *= 2;
+  const int r = tid / gw, sub = tid % gw;
+  float m = -INFINITY, s = 0.f;
+  if (r < rps) {
+    const float2* part = w.part + (r0 + r) * nc;
+    for (int c = sub; c < nc; c += gw) {
+      const float2 v = part[c];
+      lse2_merge(m, s, v.x, v.y);
+    }
+  }
+  group_lse2(m, s, gw);
+  if (r < rps && sub == 0) {
+    sm[r] = m;
+    ss[r] = s;
   }
   __syncthreads();
-  const int L = sh_L;
-
-  DrawRows<T> d;
-  d.prow = static_cast<const T*>(a.p) + int64_t(b) * a.p_seq + int64_t(L) * a.p_row;
-  const RowStat sp = st[L];
-  d.mp = sp.m;
-  d.inv_sp = 1.f / sp.s;
-  if (L < k) {
-    d.qrow = static_cast<const T*>(a.q) + int64_t(b) * a.q_seq + int64_t(L) * a.q_row;
-    const RowStat sq = st[k + 1 + L];
-    d.mq = sq.m;
-    d.inv_sq = 1.f / sq.s;
-    d.c = 1.f;
-  } else {
-    d.qrow = d.prow;
-    d.mq = 0.f;
-    d.inv_sq = 0.f;
-    d.c = 0.f;
+  if (wave != 0) return;
+  // lane i < k: accept test of draft i
+  bool rej = false;
+  if (lane < k) {
+    const float pd = fast_exp2(fmaf(xp, sl2, -sm[lane])) / ss[lane];
+    const float qd = fast_exp2(fmaf(xq, sl2, -sm[k + 1 + lane])) / ss[k + 1 + lane];
+    rej = !(u * qd < pd);
+    if (a.out_pd) a.out_pd[int64_t(b) * k + lane] = pd;
+    if (a.out_qd) a.out_qd[int64_t(b) * k + lane] = qd;
   }
-  d.vec_p = (reinterpret_cast<uintptr_t>(d.prow) & 15u) == 0;
-  d.vec_q = (reinterpret_cast<uintptr_t>(d.qrow) & 15u) == 0;
-  int y;
-  float mass;
-  block_draw<T>(d, a.vocab, sl2, a.u_s[b], sh, y, mass);
-  if (tid == 0) {
+  const uint64_t mask = wave_ballot(rej);
+  const int L = mask ? int(__builtin_ctzll(mask)) : k;
+  if (lane == 0) {
     a.out_len[b] = L;
-    a.out_tok[b] = y;
-    if (a.out_mass) a.out_mass[b] = mass;
+    DrawDesc d;
+    d.prow = static_cast<const T*>(a.p) + int64_t(b) * a.p_seq + int64_t(L) * a.p_row;
+    d.mp = sm[L];
+    d.inv_sp = 1.f / ss[L];
+    if (L < k) {
+      d.qrow = static_cast<const T*>(a.q) + int64_t(b) * a.q_seq + int64_t(L) * a.q_row;
+      d.mq = sm[k + 1 + L];
+      d.inv_sq = 1.f / ss[k + 1 + L];
+      d.c = 1.f;
+    } else {
+      d.qrow = d.prow;
+      d.mq = 0.f;
+      d.inv_sq = 0.f;
+      d.c = 0.f;
+    }
+    d.active = 1;
+    w.desc[b] = d;
   }
 }
 
-}  // namespace
-
-size_t verify_linear_workspace_bytes(int batch, int k) {
-  return align_up(size_t(batch) * size_t(2 * k + 1) * sizeof(RowStat), 256);
-}
-
-hipError_t launch_verify_linear(const VerifyLinearArgs& a, hipStream_t stream) {
+template <typename T>
+hipError_t launch_lin(const VerifyLinearArgs& a, hipStream_t stream) {
   const int rows = a.batch * (2 * a.k + 1);
+  const int nc = stats_splits(rows, a.vocab);
+  LinWs w = lin_ws(a.ws, a.batch, a.k, a.vocab);
   {
     ProfileScope ps("uno_row_stats", stream);
-    if (a.dtype == UNO_BF16)
-      hipLaunchKernelGGL(row_stats_kernel<uint16_t>, dim3(rows), dim3(kStatThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL(row_stats_kernel<float>, dim3(rows), dim3(kStatThreads), 0, stream, a);
+    hipLaunchKernelGGL(lin_stats_kernel<T>, dim3(rows, nc), dim3(kChunkThreads), 0, stream, a, w);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
-    ProfileScope ps("uno_accept_residual", stream);
-    if (a.dtype == UNO_BF16)
-      hipLaunchKernelGGL(accept_residual_kernel<uint16_t>, dim3(a.batch), dim3(kDrawThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL(accept_residual_kernel<float>, dim3(a.batch), dim3(kDrawThreads), 0, stream, a);
+    ProfileScope ps("uno_accept", stream);
+    hipLaunchKernelGGL(lin_accept_kernel<T>, dim3(a.batch), dim3(kAcceptWaves * kWave), 0, stream, a, w);
   }
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_draw<T>(w.desc, a.batch, a.vocab, a.scale_log2, w.seg, a.u_s, a.out_tok, a.out_mass, stream,
+                        "uno_draw_seg", "uno_draw_resolve");
+}
+
+}  // namespace
+
+size_t verify_linear_workspace_bytes(int batch, int k, int vocab) {
+  const int rows = batch * (2 * k + 1);
+  const int nc = stats_splits(rows, vocab);
+  return align_up(size_t(rows) * nc * sizeof(float2), 256) + align_up(size_t(rows) * sizeof(float), 256) +
+         align_up(size_t(batch) * sizeof(DrawDesc), 256) + draw_seg_bytes(batch, vocab);
+}
+
+hipError_t launch_verify_linear(const VerifyLinearArgs& a, hipStream_t stream) {
+  return a.dtype == UNO_BF16 ? launch_lin<uint16_t>(a, stream) : launch_lin<float>(a, stream);
 }
 
 }  // namespace uno

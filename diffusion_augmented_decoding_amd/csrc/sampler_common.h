@@ -1,22 +1,25 @@
-// Device building blocks of the Psi-Spec verify samplers (linear and tree):
-// streaming softmax statistics of one logit row, and a block-wide inverse-CDF
-// draw over w_v = max(0, p_v - c q_v) in token-id order.
+// Device building blocks shared by the Psi-Spec verify samplers (linear and
+// tree): chunked softmax statistics of logit rows, and a two-launch,
+// chunk-parallel inverse-CDF draw over w_v = max(0, p_v - c q_v) (c > 0) or
+// w_v = p_v (c == 0), in token-id order.
+//
+// Every row pass is split into 8192-element chunks so that a handful of rows
+// still spreads over the whole chip; consumers merge the per-chunk partials
+// in a fixed order (deterministic results).
 #pragma once
 #include "device_common.h"
 #include "internal.h"
 
 namespace uno {
 
-constexpr int kStatThreads = 256;
-constexpr int kStatUnroll = 4;
-constexpr int kDrawThreads = 1024;
-constexpr int kDrawWaves = kDrawThreads / kWave;
-constexpr int kEPT = 8;                          // elements per thread per tile
-constexpr int kDrawTile = kDrawThreads * kEPT;   // 8192 elements
-constexpr int kSeg = kWave * kEPT;               // 512 elements per (tile, wave) segment
+constexpr int kChunk = 8192;                        // elements per chunk
+constexpr int kChunkThreads = 256;                  // threads per chunk workgroup
+constexpr int kSegPerChunk = 16;                    // 512-element segments
+constexpr int kSegLen = kChunk / kSegPerChunk;
 constexpr int kMaxVocab = 1 << 20;
-constexpr int kMaxTiles = kMaxVocab / kDrawTile; // 128
-constexpr int kSegSlots = kMaxTiles * kDrawWaves;
+constexpr int kMaxChunks = kMaxVocab / kChunk;      // 128
+
+__host__ __device__ inline int num_chunks(int vocab) { return (vocab + kChunk - 1) / kChunk; }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -26,29 +29,39 @@ template <> __device__ __forceinline__ float load_logit<uint16_t>(const uint16_t
 }
 template <> __device__ __forceinline__ float load_logit<float>(const float* p, int64_t i) { return p[i]; }
 
-// 16-byte vector of logits, unpacked to fp32.
-template <typename T> struct Vec16;
-template <> struct Vec16<uint16_t> {
-  static constexpr int N = 8;
-  u32x4 raw;
-  __device__ __forceinline__ void load(const uint16_t* p) {
-    raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+// Loads 8 consecutive logits starting at e0 (bounds- and alignment-safe;
+// elements past `vocab` come back as 0 and must be masked by the caller).
+template <typename T>
+__device__ __forceinline__ void load8(const T* row, int e0, int vocab, bool vec_ok, float (&x)[8]) {
+  if (vec_ok && e0 + 8 <= vocab) {
+    if constexpr (sizeof(T) == 2) {
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + e0));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[2 * j] = bf16_lo(v[j]);
+        x[2 * j + 1] = bf16_hi(v[j]);
+      }
+    } else {
+      const f32x4 v0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + e0));
+      const f32x4 v1 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + e0 + 4));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] = v0[j];
+        x[4 + j] = v1[j];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = (e0 + j < vocab) ? load_logit<T>(row, e0 + j) : 0.f;
   }
-  __device__ __forceinline__ float get(int j) const {
-    uint32_t w = raw[j >> 1];
-    return (j & 1) ? bf16_hi(w) : bf16_lo(w);
-  }
-};
-template <> struct Vec16<float> {
-  static constexpr int N = 4;
-  f32x4 raw;
-  __device__ __forceinline__ void load(const float* p) {
-    raw = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-  }
-  __device__ __forceinline__ float get(int j) const { return raw[j]; }
-};
+}
 
-// Online update of (m, s) with a group of raw logits x (y = x * sl2).
+template <typename T>
+__device__ __forceinline__ bool row_vec_ok(const T* row) {
+  return (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+}
+
+// Online merge of a group of raw logits x (y = x * sl2) into (m, s).
 template <int G>
 __device__ __forceinline__ void online_update(float& m, float& s, const float (&x)[G], float sl2) {
   float cmax = x[0];
@@ -62,244 +75,335 @@ __device__ __forceinline__ void online_update(float& m, float& s, const float (&
   s = acc;
 }
 
-// Softmax statistics of one row, by a kStatThreads-thread block:
-// out = {max y, sum 2^(y - max), logit at `draft` (if >= 0)}.
+// Number of pieces each row's statistics pass is split into: whole rows when
+// there are enough rows to fill the chip, else enough pieces for ~2048
+// workgroups (each piece a multiple of 8 elements).
+__host__ __device__ inline int stats_splits(int rows, int vocab) {
+  int s = (2048 + rows - 1) / rows;
+  const int maxs = (vocab + 2047) / 2048;
+  if (s > maxs) s = maxs;
+  return s < 1 ? 1 : s;
+}
+__host__ __device__ inline int split_span(int vocab, int nsplit) { return ((vocab + nsplit - 1) / nsplit + 7) / 8 * 8; }
+
+// Softmax partial (max y, sum 2^(y - max)) of elements [lo, hi) of one row by
+// a kChunkThreads block, returned in thread 0.  Lanes read consecutive
+// 16-byte vectors (coalesced); 4 vectors in flight per thread; one rescale
+// per 4 vectors.  `lo` is a multiple of 8.
 template <typename T>
-__device__ void row_stats_body(const T* __restrict__ row, int vocab, float sl2, int draft,
-                               RowStat* __restrict__ out) {
-  using V = Vec16<T>;
-  constexpr int VN = V::N;
+__device__ float2 range_stats(const T* row, int lo, int hi, float sl2) {
+  constexpr int VN = 16 / sizeof(T);
+  constexpr int U = 4;
   const int tid = threadIdx.x;
   float m = -INFINITY, s = 0.f;
-
-  const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
-  int head = int(((16u - (addr & 15u)) & 15u) / sizeof(T));
-  if (head > vocab) head = vocab;
-  if (tid < head) {
-    float x[1] = {load_logit<T>(row, tid)};
-    online_update<1>(m, s, x, sl2);
-  }
-  const T* vrow = row + head;
-  const int nvec = (vocab - head) / VN;
-  int i = tid;
-  for (; i + (kStatUnroll - 1) * kStatThreads < nvec; i += kStatUnroll * kStatThreads) {
-    V v[kStatUnroll];
+  if (row_vec_ok(row)) {
+    const int nvec = (hi - lo) / VN;
+    const T* base = row + lo;
+    int i = tid;
+    for (; i + (U - 1) * kChunkThreads < nvec; i += U * kChunkThreads) {
+      float x[U * VN];
 #pragma unroll
-    for (int u = 0; u < kStatUnroll; ++u) v[u].load(vrow + int64_t(i + u * kStatThreads) * VN);
-    float x[kStatUnroll * VN];
+      for (int u = 0; u < U; ++u) {
+        const T* ptr = base + int64_t(i + u * kChunkThreads) * VN;
+        if constexpr (sizeof(T) == 2) {
+          const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
 #pragma unroll
-    for (int u = 0; u < kStatUnroll; ++u)
+          for (int j = 0; j < 4; ++j) {
+            x[u * VN + 2 * j] = bf16_lo(v[j]);
+            x[u * VN + 2 * j + 1] = bf16_hi(v[j]);
+          }
+        } else {
+          const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ptr));
 #pragma unroll
-      for (int j = 0; j < VN; ++j) x[u * VN + j] = v[u].get(j);
-    online_update<kStatUnroll * VN>(m, s, x, sl2);
-  }
-  for (; i < nvec; i += kStatThreads) {
-    V v;
-    v.load(vrow + int64_t(i) * VN);
-    float x[VN];
+          for (int j = 0; j < 4; ++j) x[u * VN + j] = v[j];
+        }
+      }
+      online_update<U * VN>(m, s, x, sl2);
+    }
+    for (; i < nvec; i += kChunkThreads) {
+      float x[VN];
+      const T* ptr = base + int64_t(i) * VN;
+      if constexpr (sizeof(T) == 2) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
 #pragma unroll
-    for (int j = 0; j < VN; ++j) x[j] = v.get(j);
-    online_update<VN>(m, s, x, sl2);
+        for (int j = 0; j < 4; ++j) {
+          x[2 * j] = bf16_lo(v[j]);
+          x[2 * j + 1] = bf16_hi(v[j]);
+        }
+      } else {
+        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ptr));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = v[j];
+      }
+      online_update<VN>(m, s, x, sl2);
+    }
+    const int t = lo + nvec * VN + tid;
+    if (t < hi) {
+      float x[1] = {load_logit<T>(row, t)};
+      online_update<1>(m, s, x, sl2);
+    }
+  } else {
+    for (int t = lo + tid; t < hi; t += kChunkThreads) {
+      float x[1] = {load_logit<T>(row, t)};
+      online_update<1>(m, s, x, sl2);
+    }
   }
-  const int t = head + nvec * VN + tid;
-  if (t < vocab) {
-    float x[1] = {load_logit<T>(row, t)};
-    online_update<1>(m, s, x, sl2);
-  }
-
   wave_lse2(m, s);
-  __shared__ float sm[kStatThreads / kWave], ss[kStatThreads / kWave];
+  __shared__ float sm[kChunkThreads / kWave], ss[kChunkThreads / kWave];
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   if (lane == 0) {
     sm[wave] = m;
     ss[wave] = s;
   }
   __syncthreads();
+  float2 r = make_float2(-INFINITY, 0.f);
   if (tid == 0) {
     float M = sm[0], S = ss[0];
 #pragma unroll
-    for (int w = 1; w < kStatThreads / kWave; ++w) lse2_merge(M, S, sm[w], ss[w]);
-    RowStat r;
-    r.m = M;
-    r.s = S;
-    // an out-of-range draft id reads nothing and gets probability 0 (rejected)
-    r.yd = (draft >= 0 && draft < vocab) ? load_logit<T>(row, draft) : -INFINITY;
-    r.pad = 0.f;
-    *out = r;
+    for (int w = 1; w < kChunkThreads / kWave; ++w) lse2_merge(M, S, sm[w], ss[w]);
+    r = make_float2(M, S);
   }
+  return r;
 }
 
-// Loads 8 consecutive logits starting at e0 (bounds- and alignment-safe).
-template <typename T>
-__device__ __forceinline__ void load8(const T* row, int e0, int vocab, bool vec_ok, float (&x)[8]) {
-  if (vec_ok && e0 + 8 <= vocab) {
-    if constexpr (sizeof(T) == 2) {
-      Vec16<T> v;
-      v.load(row + e0);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = v.get(j);
-    } else {
-      Vec16<T> v0, v1;
-      v0.load(row + e0);
-      v1.load(row + e0 + 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[j] = v0.get(j);
-        x[4 + j] = v1.get(j);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = (e0 + j < vocab) ? load_logit<T>(row, e0 + j) : 0.f;
+// Merge of a row's split partials by one whole wave: lane l loads partials
+// l, l+64, ... (independent loads, one memory latency), then a butterfly.
+// The pairwise merge is symmetric, so every lane ends with the same bits.
+__device__ __forceinline__ RowStat wave_merge_chunks(const float2* part, int nchunk) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float m = -INFINITY, s = 0.f;
+  for (int c = lane; c < nchunk; c += kWave) {
+    const float2 v = part[c];
+    lse2_merge(m, s, v.x, v.y);
   }
+  wave_lse2(m, s);
+  RowStat r;
+  r.m = m;
+  r.s = s;
+  r.yd = 0.f;
+  r.pad = 0.f;
+  return r;
 }
 
-// The distribution a draw is taken from: w_v = max(0, p_v - c q_v) (c > 0) or
-// w_v = p_v (c == 0); p_v = 2^(x_v sl2 - mp) / sp, likewise q.
-template <typename T>
-struct DrawRows {
-  const T* prow;
-  const T* qrow;
+// Sum of n values by one whole wave (same bits in every lane).
+__device__ __forceinline__ float wave_sum_range(const float* v, int n) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float s = 0.f;
+  for (int c = lane; c < n; c += kWave) s += v[c];
+  return wave_sum(s);
+}
+
+// What a draw is taken from (filled by the accept / walk kernels).
+struct DrawDesc {
+  const void* prow;
+  const void* qrow;
   float mp, inv_sp, mq, inv_sq;
-  float c;
-  bool vec_p, vec_q;
+  float c;          // 0: w = p; > 0: w = max(0, p - c q)
+  int active;       // 0: no draw (token written as -1)
 };
 
+// w of 8 elements (and p alone, for the fallback when w has no mass).
 template <typename T>
-__device__ __forceinline__ void weights8(const DrawRows<T>& d, int e0, int vocab, float sl2, float (&w)[8]) {
+__device__ __forceinline__ void weights8(const DrawDesc& d, int e0, int vocab, float sl2, bool vp, bool vq,
+                                         float (&w)[8], float (&pw)[8]) {
   float xp[8];
-  load8<T>(d.prow, e0, vocab, d.vec_p, xp);
-  if (d.c != 0.f) {
-    float xq[8];
-    load8<T>(d.qrow, e0, vocab, d.vec_q, xq);
+  load8<T>(static_cast<const T*>(d.prow), e0, vocab, vp, xp);
+  float xq[8];
+  if (d.c != 0.f) load8<T>(static_cast<const T*>(d.qrow), e0, vocab, vq, xq);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const bool in = e0 + j < vocab;
+    const float p = fast_exp2(fmaf(xp[j], sl2, -d.mp)) * d.inv_sp;
+    pw[j] = in ? p : 0.f;
+    if (d.c != 0.f) {
+      const float q = fast_exp2(fmaf(xq[j], sl2, -d.mq)) * d.inv_sq;
+      w[j] = in ? fmaxf(fmaf(-d.c, q, p), 0.f) : 0.f;
+    } else {
+      w[j] = pw[j];
+    }
+  }
+}
+
+// Segment masses of one chunk: seg[(b * nchunk + c) * 2*kSegPerChunk + k] for
+// the 16 segments of w, then the 16 of p.  Grid (nchunk, batch), 256 threads.
+template <typename T>
+__global__ __launch_bounds__(kChunkThreads) void draw_seg_kernel(const DrawDesc* __restrict__ desc, int vocab,
+                                                                 float sl2, float* __restrict__ seg) {
+  const int b = blockIdx.x, c = blockIdx.y;
+  const int nchunk = gridDim.y;
+  const DrawDesc d = desc[b];
+  if (!d.active) return;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const bool vp = row_vec_ok(static_cast<const T*>(d.prow));
+  const bool vq = row_vec_ok(static_cast<const T*>(d.qrow));
+  constexpr int kSegPerWave = kSegPerChunk / (kChunkThreads / kWave);   // 4
+  float sw[kSegPerWave], sp[kSegPerWave];
+  // wave w owns segments 4w..4w+3; lane l reads elements [8l, 8l+8) of each
+#pragma unroll
+  for (int q = 0; q < kSegPerWave; ++q) {
+    const int e0 = c * kChunk + (wave * kSegPerWave + q) * kSegLen + lane * 8;
+    float w[8], pw[8];
+    weights8<T>(d, e0, vocab, sl2, vp, vq, w, pw);
+    sw[q] = 0.f;
+    sp[q] = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float p = fast_exp2(fmaf(xp[j], sl2, -d.mp)) * d.inv_sp;
-      const float q = fast_exp2(fmaf(xq[j], sl2, -d.mq)) * d.inv_sq;
-      w[j] = (e0 + j < vocab) ? fmaxf(fmaf(-d.c, q, p), 0.f) : 0.f;
+      sw[q] += w[j];
+      sp[q] += pw[j];
     }
-  } else {
+  }
+  float* dst = seg + (int64_t(b) * nchunk + c) * (2 * kSegPerChunk);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      w[j] = (e0 + j < vocab) ? fast_exp2(fmaf(xp[j], sl2, -d.mp)) * d.inv_sp : 0.f;
+  for (int q = 0; q < kSegPerWave; ++q) {
+    const float a = wave_sum(sw[q]), bsum = wave_sum(sp[q]);
+    if (lane == 0) {
+      dst[wave * kSegPerWave + q] = a;
+      dst[kSegPerChunk + wave * kSegPerWave + q] = bsum;
+    }
   }
 }
 
-struct DrawShared {
-  float seg[kSegSlots];     // per-(tile, wave) masses, then their inclusive prefix
-  int seg_hit;
-  float carry, target, total;
-};
-
-// Inverse-CDF draw by a kDrawThreads-thread block: y = smallest v with
-// cumsum(w)[v] > u * sum(w); if rounding leaves none, the last v with w_v > 0.
-// If sum(w) == 0 for c > 0, draws from p instead.  Returns y and sum(w) in
-// every thread.  Every thread of the block must call it.
+// Resolve the inverse CDF for one batch element (one wave): S = sum of the
+// segment masses in token order, target = u * S, the segment holding it, then
+// the element within the segment (re-reads 512 elements).  Falls back to p
+// when w has no mass.  y = -1 when the descriptor is inactive.
 template <typename T>
-__device__ void block_draw(DrawRows<T> d, int vocab, float sl2, float u, DrawShared& sh, int& y_out,
-                           float& mass_out) {
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int ntiles = (vocab + kDrawTile - 1) / kDrawTile;
-  const int nseg = ntiles * kDrawWaves;
-  for (int attempt = 0; attempt < 2; ++attempt) {
-    for (int t = 0; t < ntiles; t += 2) {
-      float w0[8], w1[8];
-      const int e0 = t * kDrawTile + tid * kEPT;
-      weights8<T>(d, e0, vocab, sl2, w0);
-      const bool has1 = (t + 1) < ntiles;
-      if (has1) weights8<T>(d, e0 + kDrawTile, vocab, sl2, w1);
-      float s0 = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) s0 += w0[j];
-      s0 = wave_sum(s0);
-      if (lane == 0) sh.seg[t * kDrawWaves + wave] = s0;
-      if (has1) {
-        float s1 = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) s1 += w1[j];
-        s1 = wave_sum(s1);
-        if (lane == 0) sh.seg[(t + 1) * kDrawWaves + wave] = s1;
-      }
+__global__ __launch_bounds__(kWave) void draw_resolve_kernel(const DrawDesc* __restrict__ desc, int vocab,
+                                                             float sl2, const float* __restrict__ seg,
+                                                             const float* __restrict__ u_s,
+                                                             int32_t* __restrict__ out_tok,
+                                                             float* __restrict__ out_mass) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  DrawDesc d = desc[b];
+  if (!d.active) {
+    if (lane == 0) {
+      out_tok[b] = -1;
+      if (out_mass) out_mass[b] = 0.f;
     }
-    __syncthreads();
-    if (wave == 0) {
-      float carry = 0.f;
-      for (int c = 0; c < nseg; c += kWave) {
-        const float v = (c + lane < nseg) ? sh.seg[c + lane] : 0.f;
-        const float incl = wave_inclusive_scan(v);
-        if (c + lane < nseg) sh.seg[c + lane] = carry + incl;     // inclusive prefix
-        carry += __shfl(incl, kWave - 1);
-      }
-      const float S = carry;
-      const float target = u * S;
-      int seg = -1, last_pos = -1;
-      for (int c = 0; c < nseg && seg < 0; c += kWave) {
-        const int i = c + lane;
-        const float pre = (i < nseg) ? sh.seg[i] : 0.f;
-        const float prev = (i == 0) ? 0.f : ((i < nseg) ? sh.seg[i - 1] : 0.f);
-        const uint64_t hit = wave_ballot(i < nseg && pre > target);
-        const uint64_t pos = wave_ballot(i < nseg && pre > prev);
-        if (hit) seg = c + int(__builtin_ctzll(hit));
-        if (pos) last_pos = c + 63 - int(__builtin_clzll(pos));
-      }
-      if (seg < 0) seg = last_pos;
-      if (lane == 0) {
-        sh.total = S;
-        sh.target = target;
-        sh.seg_hit = seg;
-        sh.carry = (seg > 0) ? sh.seg[seg - 1] : 0.f;
-      }
-    }
-    __syncthreads();
-    if (sh.total > 0.f || d.c == 0.f) break;
-    d.c = 0.f;            // residual without mass: fall back to p
-    __syncthreads();
+    return;
   }
-
-  __shared__ int sh_y;
-  if (wave == 0) {
-    const int seg = sh.seg_hit;
-    int y = 0;
-    if (seg >= 0) {
-      const int t = seg / kDrawWaves, wv = seg - t * kDrawWaves;
-      const int e0 = t * kDrawTile + wv * kSeg + lane * kEPT;
-      float w[8];
-      weights8<T>(d, e0, vocab, sl2, w);
-      float ls = 0.f;
+  const int nchunk = num_chunks(vocab);
+  const int nseg = nchunk * kSegPerChunk;
+  const float* base = seg + int64_t(b) * nchunk * (2 * kSegPerChunk);
+  auto segval = [&](int i, int which) {   // which: 0 = w, 1 = p
+    return base[(i / kSegPerChunk) * (2 * kSegPerChunk) + which * kSegPerChunk + (i % kSegPerChunk)];
+  };
+  // lane l owns segments l + 64 t; all loads issued before any use.  The
+  // unrolled groups are guarded by a wave-uniform bound (static register
+  // indices, no work past the last segment).
+  constexpr int kPerLane = kMaxChunks * kSegPerChunk / kWave;
+  const int ngroup = (nseg + kWave - 1) / kWave;
+  const float u = u_s[b];
+  float v[kPerLane], incl[kPerLane];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) ls += w[j];
-      const float incl = wave_inclusive_scan(ls);
-      const float carry = sh.carry, target = sh.target;
-      const uint64_t hit = wave_ballot(carry + incl > target);
-      const uint64_t pos = wave_ballot(ls > 0.f);
-      int sel;
-      bool by_target;
+  for (int t = 0; t < kPerLane; ++t) v[t] = (t * kWave + lane < nseg) ? segval(t * kWave + lane, 0) : 0.f;
+  // inclusive prefix of the segment masses in token order; S is its last value
+  auto prefix = [&]() {
+    float carry = 0.f;
+#pragma unroll
+    for (int t = 0; t < kPerLane; ++t) {
+      if (t < ngroup) {
+        incl[t] = wave_inclusive_scan(v[t]) + carry;
+        carry = __shfl(incl[t], kWave - 1);
+      }
+    }
+    return carry;
+  };
+  float S = prefix();
+  if (!(S > 0.f)) {   // residual without mass: draw from p instead
+    d.c = 0.f;
+#pragma unroll
+    for (int t = 0; t < kPerLane; ++t) v[t] = (t * kWave + lane < nseg) ? segval(t * kWave + lane, 1) : 0.f;
+    S = prefix();
+  }
+  const float target = u * S;
+  // first segment whose inclusive prefix exceeds the target, else the last
+  // segment with mass
+  int hit_seg = -1, last_pos = -1;
+  float carry_before = 0.f;
+#pragma unroll
+  for (int t = 0; t < kPerLane; ++t) {
+    if (t < ngroup && hit_seg < 0) {
+      const int c0 = t * kWave;
+      const bool valid = c0 + lane < nseg;
+      const uint64_t hit = wave_ballot(valid && incl[t] > target);
+      const uint64_t pos = wave_ballot(valid && v[t] > 0.f);
       if (hit) {
-        sel = int(__builtin_ctzll(hit));
-        by_target = true;
-      } else {
-        sel = pos ? 63 - int(__builtin_clzll(pos)) : 0;
-        by_target = false;
+        const int l = int(__builtin_ctzll(hit));
+        hit_seg = c0 + l;
+        carry_before = __shfl(incl[t] - v[t], l);
+      } else if (pos) {
+        const int l = 63 - int(__builtin_clzll(pos));
+        last_pos = c0 + l;
+        carry_before = __shfl(incl[t] - v[t], l);
       }
-      if (lane == sel) {
-        float cum = carry + incl - ls;
-        int pick = -1, lastp = -1;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          cum += w[j];
-          if (w[j] > 0.f) lastp = j;
-          if (by_target && pick < 0 && cum > target) pick = j;
-        }
-        if (pick < 0) pick = (lastp >= 0) ? lastp : 0;
-        y = e0 + pick;
-      }
-      y = __shfl(y, sel);
     }
-    if (lane == 0) sh_y = y;
   }
-  __syncthreads();
-  y_out = sh_y;
-  mass_out = sh.total;
+  bool by_target = hit_seg >= 0;
+  const int sidx = by_target ? hit_seg : last_pos;
+  int y = 0;
+  if (sidx >= 0) {
+    const int e0 = (sidx / kSegPerChunk) * kChunk + (sidx % kSegPerChunk) * kSegLen + lane * 8;
+    float w[8], pw[8];
+    weights8<T>(d, e0, vocab, sl2, row_vec_ok(static_cast<const T*>(d.prow)),
+                row_vec_ok(static_cast<const T*>(d.qrow)), w, pw);
+    float ls = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ls += w[j];
+    const float incl = wave_inclusive_scan(ls);
+    const uint64_t hit = wave_ballot(by_target && carry_before + incl > target);
+    const uint64_t pos = wave_ballot(ls > 0.f);
+    int sel;
+    bool tgt;
+    if (hit) {
+      sel = int(__builtin_ctzll(hit));
+      tgt = true;
+    } else {
+      sel = pos ? 63 - int(__builtin_clzll(pos)) : 0;
+      tgt = false;
+    }
+    if (lane == sel) {
+      float cum = carry_before + incl - ls;
+      int pick = -1, lastp = -1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        cum += w[j];
+        if (w[j] > 0.f) lastp = j;
+        if (tgt && pick < 0 && cum > target) pick = j;
+      }
+      if (pick < 0) pick = (lastp >= 0) ? lastp : 0;
+      y = e0 + pick;
+    }
+    y = __shfl(y, sel);
+  }
+  if (lane == 0) {
+    out_tok[b] = y;
+    if (out_mass) out_mass[b] = S;
+  }
+}
+
+// Launch the two draw kernels for `batch` descriptors.
+template <typename T>
+hipError_t launch_draw(const DrawDesc* desc, int batch, int vocab, float sl2, float* seg, const float* u_s,
+                       int32_t* out_tok, float* out_mass, hipStream_t stream, const char* seg_name,
+                       const char* resolve_name) {
+  {
+    ProfileScope ps(seg_name, stream);
+    hipLaunchKernelGGL(draw_seg_kernel<T>, dim3(batch, num_chunks(vocab)), dim3(kChunkThreads), 0, stream, desc,
+                       vocab, sl2, seg);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    ProfileScope ps(resolve_name, stream);
+    hipLaunchKernelGGL(draw_resolve_kernel<T>, dim3(batch), dim3(kWave), 0, stream, desc, vocab, sl2, seg, u_s,
+                       out_tok, out_mass);
+  }
+  return hipGetLastError();
+}
+
+inline size_t draw_seg_bytes(int batch, int vocab) {
+  return align_up(size_t(batch) * num_chunks(vocab) * 2 * kSegPerChunk * sizeof(float), 256);
 }
 
 }  // namespace uno

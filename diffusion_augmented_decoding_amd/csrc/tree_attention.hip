@@ -5,11 +5,16 @@
 // prefix tree using tree attention.  Node i attends to every cached position
 // and to the tree nodes that are its ancestors or itself.
 //
-// One workgroup per (32 query rows of one KV head's group, KV head, batch).
-// Query row r of the group is (node r / G, head g*G + r % G), G = H / H_kv, so
-// the G heads sharing a KV head share every K/V fetch.  Keys are the ctx cache
-// rows followed by the n tree nodes, in blocks of 32; the 4 waves take every
-// 4th block and merge their online-softmax states in LDS at the end.
+// Work unit: 32 query rows of one KV head's group.  Query row r of the group
+// is (node r / G, head g*G + r % G), G = H / H_kv, so the G heads sharing a KV
+// head share every K/V fetch.  Keys are the ctx cache rows followed by the n
+// tree nodes, in blocks of 32.  The key blocks of a unit are split over KS
+// workgroups (KS chosen so a decode-sized call still spreads over the chip)
+// and, inside a workgroup, over its 4 waves; each wave keeps the next block's
+// K and V in flight in registers while it computes the current one.  Waves
+// merge their online-softmax states in LDS; with KS > 1 each workgroup writes
+// its merged (max, sum, unnormalised O) to the workspace and a combine kernel
+// merges the KS partials of every row in a fixed order.
 //
 // Per key block, per wave (all on v_mfma_f32_32x32x16_bf16):
 //   S^T[key][row] = K_blk . Q^T : the K rows are head_dim-contiguous, so each
@@ -22,7 +27,12 @@
 //                   so its operand is two 8-byte LDS reads.  Keeping O
 //                   transposed leaves the rescale by exp2(m_old - m_new) local
 //                   to the lane that owns the row.
-// The tree mask is an ancestor-or-self bitset per node (<= 256 nodes) in LDS.
+// The tree mask is an ancestor-or-self bitset per node (<= 256 nodes) in LDS,
+// built from the parent array staged in LDS.
+//
+// Workgroups are numbered so that the tiles sharing one (batch, KV head, key
+// split) land on one XCD (hardware deals workgroups to the 8 XCDs round
+// robin): their common K/V blocks are fetched into that XCD's L2 once.
 #include "device_common.h"
 #include "internal.h"
 
@@ -36,6 +46,8 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kMaxNodes = 256;
 constexpr int kVtStride = 36;           // bf16 per transposed-V row (32 keys + pad)
+constexpr int kXcd = 8;
+constexpr int kTargetWgs = 640;         // ~2.5 workgroups per CU
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -46,22 +58,111 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_wave_barrier();
 }
 
-__global__ __launch_bounds__(kThreads) void tree_attn_kernel(TreeAttnArgs a) {
+struct AttnPlan {
+  int tiles;    // 32-row tiles per (batch, KV head)
+  int ks;       // key splits
+  int groups;   // batch * n_kv * ks
+  int nblk;     // key blocks
+};
+
+AttnPlan make_plan(int batch, int n, int ctx, int H, int Hkv) {
+  AttnPlan p;
+  const int G = H / Hkv;
+  p.tiles = (n * G + 31) / 32;
+  p.nblk = (ctx + n + kKB - 1) / kKB;
+  const int64_t base = int64_t(p.tiles) * Hkv * batch;
+  int ks = 1;
+  if (base < kTargetWgs) {
+    ks = int((kTargetWgs + base - 1) / base);
+    const int most = (p.nblk + kWaves - 1) / kWaves;   // at least one block per wave
+    if (ks > most) ks = most;
+    if (ks < 1) ks = 1;
+  }
+  p.ks = ks;
+  p.groups = batch * Hkv * ks;
+  return p;
+}
+
+// Partial results of one split: [group][tile][32 rows] x (m, s) and
+// x O[128] (fp32, unnormalised).
+struct AttnPart {
+  float* o;
+  float2* ms;
+};
+
+AttnPart part_ws(void* base, const AttnPlan& p) {
+  const size_t rows = size_t(p.groups) * p.tiles * 32;
+  AttnPart w;
+  w.o = static_cast<float*>(base);
+  w.ms = reinterpret_cast<float2*>(static_cast<char*>(base) + align_up(rows * kHD * sizeof(float), 256));
+  return w;
+}
+
+size_t part_bytes(const AttnPlan& p) {
+  if (p.ks == 1) return 0;
+  const size_t rows = size_t(p.groups) * p.tiles * 32;
+  return align_up(rows * kHD * sizeof(float), 256) + align_up(rows * sizeof(float2), 256);
+}
+
+__global__ __launch_bounds__(kThreads) void tree_attn_kernel(TreeAttnArgs a, AttnPlan pl, AttnPart part) {
   __shared__ uint64_t anc[kMaxNodes][4];
+  __shared__ int sh_par[kMaxNodes];
   __shared__ int sh_bad;
   __shared__ __align__(16) uint16_t vt[kWaves][kHD * kVtStride];   // 36 KB, reused for the merge
   __shared__ float mrg_m[kWaves][32], mrg_s[kWaves][32];
 
+  // ---- work unit (XCD-grouped numbering; the grid is padded to a multiple of 8 groups)
+  const int L = blockIdx.x;
+  const int slot = L / kXcd;
+  const int tile = slot % pl.tiles;
+  const int grp = (slot / pl.tiles) * kXcd + L % kXcd;
+  if (grp >= pl.groups) return;
+  const int ksi = grp % pl.ks;
+  const int g = (grp / pl.ks) % a.n_kv;
+  const int b = grp / (pl.ks * a.n_kv);
+
   const int n = a.n_tree, ctx = a.ctx, H = a.n_heads, Hkv = a.n_kv;
   const int G = H / Hkv;
   const int nrows = n * G;
-  const int row0 = blockIdx.x * 32;
-  const int g = blockIdx.y, b = blockIdx.z;
+  const int row0 = tile * 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid / kWave;
   const int lrow = lane & 31, lh = lane >> 5;
+  const int nkeys = ctx + n;
 
-  // ---- ancestor-or-self bitsets, one thread per node (walks its chain)
+  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
+  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
+  const uint16_t* kt = static_cast<const uint16_t*>(a.k_tree);
+  const uint16_t* vtr = static_cast<const uint16_t*>(a.v_tree);
+
+  // this wave's key blocks: j = ksi*4 + wave + i*(ks*4)
+  const int stride = pl.ks * kWaves;
+  const int j0 = ksi * kWaves + wave;
+  const int nb = j0 < pl.nblk ? (pl.nblk - 1 - j0) / stride + 1 : 0;
+
+  // K fragment rows of a block (key kb + lrow, dims 16 st + 8 lh) and the V
+  // chunks (chunk lane + 64 t -> key (lane & 31), dims 8 ((lane >> 5) + 2 t));
+  // keys past the end read the last key (finite values, masked scores).
+  auto key_row = [&](const uint16_t* cache, const uint16_t* tree, int key) {
+    key = min(key, nkeys - 1);
+    return key < ctx ? cache + ((int64_t(b) * ctx + key) * Hkv + g) * kHD
+                     : tree + ((int64_t(b) * n + (key - ctx)) * Hkv + g) * kHD;
+  };
+  auto load_block = [&](int j, u32x4 (&kr)[8], u32x4 (&vr)[8]) {
+    const int kb = j * kKB;
+    const uint16_t* krow = key_row(kc, kt, kb + lrow);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) kr[st] = *reinterpret_cast<const u32x4*>(krow + 16 * st + 8 * lh);
+    const uint16_t* vrow = key_row(vc, vtr, kb + lrow);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) vr[t] = *reinterpret_cast<const u32x4*>(vrow + 8 * (lh + 2 * t));
+  };
+
+  u32x4 kr[8], vr[8];
+  if (nb > 0) load_block(j0, kr, vr);   // first block in flight during the set-up below
+
+  // ---- parent array to LDS, then ancestor-or-self bitsets (one thread per node)
   if (tid == 0) sh_bad = 0;
+  for (int i = tid; i < n; i += kThreads) sh_par[i] = a.parent[int64_t(b) * n + i];
   __syncthreads();
   for (int i = tid; i < n; i += kThreads) {
     uint64_t w[4] = {0, 0, 0, 0};
@@ -69,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void tree_attn_kernel(TreeAttnArgs a) {
     bool bad = false;
     while (true) {
       w[j >> 6] |= uint64_t(1) << (j & 63);
-      const int pj = a.parent[int64_t(b) * n + j];
+      const int pj = sh_par[j];
       if (j == 0) {
         bad = (pj != -1);
         break;
@@ -113,46 +214,27 @@ __global__ __launch_bounds__(kThreads) void tree_attn_kernel(TreeAttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
 
-  const int nkeys = ctx + n;
-  const int nblk = (nkeys + kKB - 1) / kKB;
-  const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
-  const uint16_t* vc = static_cast<const uint16_t*>(a.v_cache);
-  const uint16_t* kt = static_cast<const uint16_t*>(a.k_tree);
-  const uint16_t* vtr = static_cast<const uint16_t*>(a.v_tree);
   uint16_t* myvt = vt[wave];
+  for (int i = 0, j = j0; i < nb; ++i, j += stride) {
+    if (i > 0) load_block(j, kr, vr);
+    const u32x4(&kcur)[8] = kr;
+    const u32x4(&vcur)[8] = vr;
+    const int kb = j * kKB;
 
-  for (int blk = wave; blk < nblk; blk += kWaves) {
-    const int kb = blk * kKB;
-    // ---- K fragments (A operand): key kb + lrow, dims 16s + 8lh .. +8
-    const int kj = kb + lrow;
-    const uint16_t* krow = nullptr;
-    if (kj < ctx)
-      krow = kc + ((int64_t(b) * ctx + kj) * Hkv + g) * kHD;
-    else if (kj < nkeys)
-      krow = kt + ((int64_t(b) * n + (kj - ctx)) * Hkv + g) * kHD;
     f32x16 s;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.f;
 #pragma unroll
-    for (int st = 0; st < kHD / 16; ++st) {
-      u32x4 v = krow ? *reinterpret_cast<const u32x4*>(krow + 16 * st + 8 * lh) : u32x4{0u, 0u, 0u, 0u};
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), qf[st], s, 0, 0, 0);
-    }
-    // ---- stage V block transposed: chunk id c = lane + 64 t -> key c % 32, dims 8 (c / 32) ..
+    for (int st = 0; st < kHD / 16; ++st)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kcur[st]), qf[st], s, 0, 0, 0);
+    // ---- stage V transposed: chunk t holds key lrow, dims 8 (lh + 2t) .. +8
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const int cid = lane + kWave * t;
-      const int key = cid & 31, dc = cid >> 5;
-      const int vj = kb + key;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (vj < ctx)
-        v = *reinterpret_cast<const u32x4*>(vc + ((int64_t(b) * ctx + vj) * Hkv + g) * kHD + 8 * dc);
-      else if (vj < nkeys)
-        v = *reinterpret_cast<const u32x4*>(vtr + ((int64_t(b) * n + (vj - ctx)) * Hkv + g) * kHD + 8 * dc);
+      const int dc = lh + 2 * t;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        myvt[(8 * dc + 2 * e) * kVtStride + key] = uint16_t(v[e] & 0xffffu);
-        myvt[(8 * dc + 2 * e + 1) * kVtStride + key] = uint16_t(v[e] >> 16);
+        myvt[(8 * dc + 2 * e) * kVtStride + lrow] = uint16_t(vcur[t][e] & 0xffffu);
+        myvt[(8 * dc + 2 * e + 1) * kVtStride + lrow] = uint16_t(vcur[t][e] >> 16);
       }
     }
     // ---- scores: lane holds row lrow, keys 8(e/4) + 4lh + e%4
@@ -252,8 +334,24 @@ __global__ __launch_bounds__(kThreads) void tree_attn_kernel(TreeAttnArgs a) {
     }
     __syncthreads();
   }
+  if (wave != 0) return;
 
-  if (wave == 0 && row_ok) {
+  if (pl.ks > 1) {
+    // partial of this split; a bad tree is passed on as a NaN max
+    const int64_t prow = (int64_t(grp) * pl.tiles + tile) * 32 + lrow;
+    float* dst = part.o + prow * kHD;
+#pragma unroll
+    for (int db = 0; db < kHD / 32; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const f32x4 v = {o[db][4 * gq], o[db][4 * gq + 1], o[db][4 * gq + 2], o[db][4 * gq + 3]};
+        *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * gq + 4 * lh) = v;
+      }
+    if (lh == 0) part.ms[prow] = make_float2(bad_tree ? __builtin_nanf("") : m, ssum);
+    return;
+  }
+
+  if (row_ok) {
     const float inv = bad_tree ? __builtin_nanf("") : 1.f / ssum;
     uint16_t* orow = static_cast<uint16_t*>(a.out) + ((int64_t(b) * n + node) * H + head) * kHD;
 #pragma unroll
@@ -270,16 +368,75 @@ __global__ __launch_bounds__(kThreads) void tree_attn_kernel(TreeAttnArgs a) {
   }
 }
 
+// Merge of the KS split partials of 8 rows per workgroup, ks ascending:
+// M = max m_k, S = sum s_k 2^(m_k - M), O = sum O_k 2^(m_k - M) / S.
+// Thread t: row 8 * (blockIdx.x % 4) + t / 32 of the tile, dims 4 (t % 32) .. +4.
+constexpr int kCombineThreads = 256;
+
+__global__ __launch_bounds__(kCombineThreads) void tree_attn_combine_kernel(TreeAttnArgs a, AttnPlan pl,
+                                                                            AttnPart part) {
+  const int tile = blockIdx.x / 4, quarter = blockIdx.x % 4;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int G = a.n_heads / a.n_kv;
+  const int rin = quarter * 8 + threadIdx.x / 32;
+  const int r = tile * 32 + rin;
+  if (r >= a.n_tree * G) return;
+  const int d0 = 4 * (threadIdx.x % 32);
+  const int node = r / G, head = g * G + r % G;
+  const int64_t grp0 = (int64_t(b) * a.n_kv + g) * pl.ks;
+  auto prow = [&](int k) { return ((grp0 + k) * pl.tiles + tile) * 32 + rin; };
+
+  float M = -INFINITY;
+  bool bad = false;
+#pragma unroll 4
+  for (int k = 0; k < pl.ks; ++k) {
+    const float mk = part.ms[prow(k)].x;
+    bad |= __builtin_isnan(mk);
+    M = fmaxf(M, mk);
+  }
+  float S = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int k = 0; k < pl.ks; ++k) {
+    const int64_t pr = prow(k);
+    const float2 ms = part.ms[pr];
+    const f32x4 v = *reinterpret_cast<const f32x4*>(part.o + pr * kHD + d0);
+    const float w = (ms.x == -INFINITY) ? 0.f : fexp2(ms.x - M);
+    S += ms.y * w;
+    acc += v * w;
+  }
+  const float inv = bad ? __builtin_nanf("") : 1.f / S;
+  uint16_t* orow = static_cast<uint16_t*>(a.out) + ((int64_t(b) * a.n_tree + node) * a.n_heads + head) * kHD;
+  *reinterpret_cast<uint2*>(orow + d0) =
+      make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv));
+  if (a.out_lse && d0 == 0)
+    a.out_lse[(int64_t(b) * a.n_tree + node) * a.n_heads + head] =
+        bad ? __builtin_nanf("") : (M + __log2f(S)) * kLn2;
+}
+
 }  // namespace
 
-size_t tree_attention_workspace_bytes(int, int, int, int, int, int) { return 0; }
+size_t tree_attention_workspace_bytes(int batch, int n_tree, int ctx, int n_heads, int n_kv, int) {
+  return part_bytes(make_plan(batch, n_tree, ctx, n_heads, n_kv));
+}
 
 hipError_t launch_tree_attention(const TreeAttnArgs& a, hipStream_t stream) {
-  const int G = a.n_heads / a.n_kv;
-  const int rows = a.n_tree * G;
-  dim3 grid((rows + 31) / 32, a.n_kv, a.batch);
-  ProfileScope ps("uno_tree_attention", stream);
-  hipLaunchKernelGGL(tree_attn_kernel, grid, dim3(kThreads), 0, stream, a);
+  const AttnPlan pl = make_plan(a.batch, a.n_tree, a.ctx, a.n_heads, a.n_kv);
+  const AttnPart part = pl.ks > 1 ? part_ws(a.ws, pl) : AttnPart{nullptr, nullptr};
+  const int64_t padded_groups = (int64_t(pl.groups) + kXcd - 1) / kXcd * kXcd;
+  const int64_t nwg = padded_groups * pl.tiles;
+  if (nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
+  {
+    ProfileScope ps("uno_tree_attention", stream);
+    hipLaunchKernelGGL(tree_attn_kernel, dim3(unsigned(nwg)), dim3(kThreads), 0, stream, a, pl, part);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pl.ks == 1) return e;
+  {
+    ProfileScope ps("uno_tree_attention_combine", stream);
+    hipLaunchKernelGGL(tree_attn_combine_kernel, dim3(pl.tiles * 4, a.n_kv, a.batch), dim3(kCombineThreads), 0,
+                       stream, a, pl, part);
+  }
   return hipGetLastError();
 }
 

@@ -145,10 +145,15 @@ uno_status uno_psi_spec_verify_linear(hipStream_t stream, uno_dtype logit_dtype,
  * k_cache, v_cache bf16 [batch][ctx_len][n_kv_heads][head_dim]
  * k_tree,  v_tree  bf16 [batch][n_tree][n_kv_heads][head_dim]
  * parent  int32 [batch][n_tree]: parent[b][0] = -1, 0 <= parent[b][i] < i.
- *         Checked on the device; a bad tree makes the call's outputs NaN.
+ *         Checked on the device; a bad tree makes that batch element's
+ *         outputs NaN.
  * out     bf16 [batch][n_tree][n_heads][head_dim]
  * out_lse optional f32 [batch][n_tree][n_heads]: natural-log log-sum-exp of
  *         the scaled scores.
+ * workspace: device memory of at least the size the _workspace query gives
+ *   (0 when the call has enough query tiles to fill the device on its own;
+ *   otherwise per-split partial results, fp32).  K and V must be finite: a
+ *   masked key still enters the products with weight 0.
  * Requirements: head_dim == 128, n_heads a multiple of n_kv_heads,
  *   n_heads / n_kv_heads <= 8, 1 <= n_tree <= 256, ctx_len >= 0, batch >= 1.
  * ------------------------------------------------------------------------ */
@@ -182,16 +187,22 @@ uno_status uno_tree_verify_attention(hipStream_t stream,
  * p_logits [batch][n_tree][vocab]: AR row of each node (scores its children).
  * q_logits [batch][max_depth][vocab]: draft marginal of depth 1..max_depth.
  * u_accept f32 [batch][n_tree] (entry 0 unused), u_sample f32 [batch].
+ * max_children: upper bound on the children of any node (the caller builds
+ *   the tree and knows its branching); the residual masses are computed in
+ *   max_children chunk-parallel rounds.
  * Outputs: out_accept_len int32 [batch]; out_path int32 [batch][max_depth]
  *   (accepted node ids, -1 padded); out_token int32 [batch].
- * Requirements: 1 <= n_tree <= 1024, 1 <= max_depth <= 64 and >= the tree's
- *   depth, 1 <= vocab <= 2^20, temperature > 0.  The tree structure is
- *   checked on the device; a malformed tree yields out_accept_len = -1.
+ * Requirements: 1 <= batch <= 65535, 1 <= n_tree <= 1024, 1 <= max_depth <= 64,
+ *   0 <= max_children <= 1023, 1 <= vocab <= 2^20, temperature > 0.  The tree
+ *   is checked on the device: parent[0] = -1, 0 <= parent[i] < i, depth at
+ *   most max_depth, at most max_children children per node; a tree that
+ *   fails yields out_accept_len = -1, out_token = -1 and an all -1 path.
  * ------------------------------------------------------------------------ */
 uno_status uno_psi_spec_verify_tree_workspace(int32_t batch, int32_t n_tree, int32_t max_depth,
-                                              int32_t vocab, size_t* bytes);
+                                              int32_t max_children, int32_t vocab, size_t* bytes);
 uno_status uno_psi_spec_verify_tree(hipStream_t stream, uno_dtype logit_dtype,
-                                    int32_t batch, int32_t n_tree, int32_t max_depth, int32_t vocab,
+                                    int32_t batch, int32_t n_tree, int32_t max_depth, int32_t max_children,
+                                    int32_t vocab,
                                     const int32_t* parent, const int32_t* tokens,
                                     const void* p_logits, const void* q_logits,
                                     const float* u_accept, const float* u_sample,

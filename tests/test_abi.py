@@ -143,21 +143,39 @@ def test_tree_attention_rejects_bad_calls(lib):
     assert _ta(lib, par=None) == INVALID
     assert _ta(lib, out=ctypes.c_void_p(0x10008)) == UNSUPPORTED
     assert _ta(lib, scale=-1.0) == INVALID
+    assert _ta(lib) == WORKSPACE                     # decode size: key splits need partials
+
+
+def test_tree_attention_workspace_queries(lib):
+    ws = ctypes.c_size_t(1)
+    # 65 nodes x 4 heads per KV head = 9 query tiles x 8 KV heads: split keys, fp32 partials
+    assert lib.uno_tree_verify_attention_workspace(1, 65, 1024, 32, 8, 128, ctypes.byref(ws)) == OK
+    assert ws.value >= 72 * 2 * 32 * 128 * 4
+    # 64 tiles x 4 KV heads x batch 3 fill the device without splitting
+    assert lib.uno_tree_verify_attention_workspace(3, 256, 40, 32, 4, 128, ctypes.byref(ws)) == OK
+    assert ws.value == 0
+    assert lib.uno_tree_verify_attention_workspace(1, 65, 1024, 32, 8, 128, None) == INVALID
 
 
 def _tv(lib, **kw):
-    a = dict(dtype=BF16, batch=1, n=65, D=3, V=1000, par=FAKE16, tok=FAKE16, p=FAKE16, q=FAKE16, ua=FAKE16,
+    a = dict(dtype=BF16, batch=1, n=65, D=3, C=4, V=1000, par=FAKE16, tok=FAKE16, p=FAKE16, q=FAKE16, ua=FAKE16,
              us=FAKE16, T=1.0, L=FAKE16, path=FAKE16, y=FAKE16, ws=FAKE16, wsb=1 << 20)
     a.update(kw)
-    return lib.uno_psi_spec_verify_tree(None, a["dtype"], a["batch"], a["n"], a["D"], a["V"], a["par"], a["tok"],
-                                        a["p"], a["q"], a["ua"], a["us"], a["T"], a["L"], a["path"], a["y"],
-                                        a["ws"], a["wsb"])
+    return lib.uno_psi_spec_verify_tree(None, a["dtype"], a["batch"], a["n"], a["D"], a["C"], a["V"], a["par"],
+                                        a["tok"], a["p"], a["q"], a["ua"], a["us"], a["T"], a["L"], a["path"],
+                                        a["y"], a["ws"], a["wsb"])
 
 
 def test_tree_verify_rejects_bad_calls(lib):
     assert _tv(lib, n=1025) == UNSUPPORTED
     assert _tv(lib, D=65) == UNSUPPORTED
     assert _tv(lib, D=0) == INVALID
+    assert _tv(lib, C=-1) == INVALID
+    assert _tv(lib, C=1024) == INVALID
+    assert _tv(lib, batch=65536) == UNSUPPORTED
+    ws = ctypes.c_size_t(0)
+    assert lib.uno_psi_spec_verify_tree_workspace(1, 65, 3, 4, 151936, ctypes.byref(ws)) == OK
+    assert ws.value > 0
     assert _tv(lib, par=None) == INVALID
     assert _tv(lib, path=None) == INVALID
     assert _tv(lib, T=-1.0) == INVALID

@@ -57,6 +57,8 @@ def test_attention_tree_workload(gpu_lib):
     ("cfg", 65, 0, 32, 8, 1),           # no cache at all
     ("single", 1, 200, 32, 8, 3),       # plain decode attention
     ("random", 256, 96, 8, 8, 1),       # largest tree
+    ("random", 256, 40, 32, 4, 3),      # enough query tiles for one key split per tile
+    ("single", 1, 3000, 8, 1, 1),       # long cache, many key splits
 ])
 def test_attention_shapes(gpu_lib, name, n, ctx, nh, nkv, batch):
     say(f"tree attention {name} n={n} ctx={ctx} H={nh}/{nkv} B={batch}")
@@ -86,10 +88,13 @@ def test_attention_malformed_tree_gives_nan(gpu_lib):
     assert np.all(np.isnan(o)) and np.all(np.isnan(lse))
 
 
-def _verify(dad, c):
+def _verify(dad, c, max_children=None):
     import torch
+    if max_children is None:
+        max_children = workloads.max_children(c["parent"])
     out = dad.psi_spec_verify_tree(to_dev(c["parent"].astype(np.int32)), to_dev(c["tokens"]), to_dev(c["p"]),
-                                   to_dev(c["q"]), to_dev(c["u_acc"]), to_dev(c["u_s"]), c["temperature"])
+                                   to_dev(c["q"]), to_dev(c["u_acc"]), to_dev(c["u_s"]), c["temperature"],
+                                   max_children=max_children)
     torch.cuda.synchronize()
     return {k: to_host(v) for k, v in out.items()}
 
@@ -144,5 +149,31 @@ def test_verify_tree_malformed(gpu_lib):
     parent = workloads.chain_parent(5)
     c = workloads.tree_verify_case(parent, 100, dtype="f32", seed=1)
     c["parent"][0, 2] = 3
-    g = _verify(gpu_lib, c)
+    g = _verify(gpu_lib, c, max_children=1)
     assert g["accept_len"][0] == -1 and g["token"][0] == -1 and np.all(g["path"][0] == -1)
+
+
+def test_verify_tree_more_children_than_declared(gpu_lib):
+    say("tree verify max_children below the tree's branching")
+    c = workloads.tree_verify_case(workloads.star_parent(6), 300, dtype="f32", seed=2, batch=2)
+    g = _verify(gpu_lib, c, max_children=3)
+    assert np.all(g["accept_len"] == -1) and np.all(g["token"] == -1)
+    g = _verify(gpu_lib, c, max_children=5)
+    assert _check_verify(c, g) <= 1
+
+
+def test_verify_tree_batch_of_different_trees(gpu_lib):
+    say("tree verify batch of different trees, one malformed")
+    parents = np.stack([workloads.random_parent(30, s) for s in range(4)])
+    cs = [workloads.tree_verify_case(parents[b], 2000, dtype="bf16", seed=10 + b) for b in range(4)]
+    c = {k: np.concatenate([x[k] for x in cs]) for k in ("parent", "tokens", "p", "p_f32", "u_acc", "u_s")}
+    dmax = max(x["max_depth"] for x in cs)
+    for k in ("q", "q_f32"):      # pad the per-depth draft rows to a common depth
+        c[k] = np.concatenate([np.pad(x[k], ((0, 0), (0, dmax - x["max_depth"]), (0, 0))) for x in cs])
+    c.update(batch=4, temperature=1.0)
+    c["parent"][3, 5] = 7         # malformed third tree
+    g = _verify(gpu_lib, c, max_children=workloads.max_children(parents))
+    assert g["accept_len"][3] == -1
+    good = {k: (v[:3] if isinstance(v, np.ndarray) else v) for k, v in c.items()}
+    good["batch"] = 3
+    assert _check_verify(good, {k: v[:3] for k, v in g.items()}) <= 1

@@ -222,6 +222,16 @@ def random_parent(n, seed, max_children=None):
     return p
 
 
+def max_children(parent):
+    """Largest number of children of any node of a parent array (or batch of them)."""
+    parent = np.asarray(parent).reshape(-1, np.shape(parent)[-1])
+    best = 0
+    for row in parent:
+        counts = np.bincount(row[1:][row[1:] >= 0], minlength=1) if row.size > 1 else np.zeros(1, int)
+        best = max(best, int(counts.max()) if counts.size else 0)
+    return best
+
+
 def _depths(parent):
     d = np.zeros(len(parent), dtype=np.int64)
     for i in range(1, len(parent)):
