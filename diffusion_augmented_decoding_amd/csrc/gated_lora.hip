@@ -30,7 +30,9 @@
 // Tiles are mapped to block ids so that the blocks one XCD runs (ids
 // congruent mod 8) cover a contiguous band of N-tiles across all M-tiles:
 // each weight tile is then fetched into one XCD's L2 and reused by every
-// M-tile there.
+// M-tile there.  A second kernel, gemm_dl_kernel, loads K-tiles straight into
+// LDS (global_load_lds) through a deeper stage ring; the dispatcher picks
+// per shape whichever measured faster.
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -73,6 +75,17 @@ __device__ __forceinline__ u32x4 load_chunk_raw(const uint16_t* base, int64_t ld
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// K-tiles [kt_begin, kt_end) of split blockIdx.y: the splits divide the
+// tiles of the first K1 columns; the last split also takes the adapter
+// columns.  A row whose adapter input is zero therefore sums exactly the same
+// partial products, split by split, as the call without adapter.
+__device__ __forceinline__ void split_range(const GemmParams& p, int bk, int kt_total, int& kt_begin, int& kt_end) {
+  const int kt1 = (p.K1 + bk - 1) / bk;
+  const int y = blockIdx.y;
+  kt_begin = min(y * p.ktiles_per_split, kt1);
+  kt_end = (y + 1 == int(gridDim.y)) ? kt_total : min((y + 1) * p.ktiles_per_split, kt1);
+}
+
 // BM x BN block tile, WM x WN waves, P K-tiles of register prefetch, DBF:
 // double-buffer the MFMA fragments across k-steps, MODE: 0 = bf16 out,
 // 1 = fp32 split-K partials.
@@ -101,9 +114,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p
 
   const int Ktot = p.K1 + p.K2;
   const int kt_total = (Ktot + kBK - 1) / kBK;
-  const int kt_begin = blockIdx.y * p.ktiles_per_split;
-  int kt_end = kt_begin + p.ktiles_per_split;
-  if (kt_end > kt_total) kt_end = kt_total;
+  int kt_begin, kt_end;
+  split_range(p, kBK, kt_total, kt_begin, kt_end);
 
   f32x16 acc[FN][FM];
 #pragma unroll
@@ -273,6 +285,198 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p
   }
 }
 
+// ------------------------------------------------------------------
+// Direct-to-LDS variant: K-tiles of 32 (64-byte LDS rows) move from global
+// memory straight into LDS with global_load_lds_dwordx4 (no register staging,
+// no LDS store instructions), S stages deep, so S - 1 K-tiles are in flight
+// while one is computed.  One wave instruction fills 1 KB of LDS (lane l at
+// byte 16 l), i.e. 16 rows x 4 chunks; each lane therefore loads the global
+// chunk whose swizzled LDS slot it fills.  Chunks past K (or of K-tiles past
+// the split) read a zero block; rows past M / N read the last valid row (their
+// outputs are never stored).  The 64-byte-row swizzle, chunk c of row r at
+// c ^ ((r >> 1) & 3) ^ ((r >> 3) & 1), keeps the fragment reads conflict-free
+// for both 8- and 16-lane LDS phases.
+constexpr int kBKd = 32;                  // K elements per direct-load K-tile
+
+__device__ __align__(16) const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
+
+// s_waitcnt vmcnt(N) alone (expcnt and lgkmcnt at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int BM, int BN, int WM, int WN, int S, int MODE>
+__global__ __launch_bounds__(WM * WN * kWave) void gemm_dl_kernel(GemmParams p) {
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int ROWS = BN + BM;                         // LDS rows per stage (weights first)
+  constexpr int BLKS = (ROWS + 15) / 16;                // 1 KB wave-instruction blocks of real rows
+  constexpr int LPW = (BLKS + NW - 1) / NW;             // load instructions per wave per stage
+  constexpr int STAGE = LPW * NW * 1024;                // bytes (blocks past BLKS are padding)
+  static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(BN % 16 == 0 && BM % 16 == 0, "tile rows come in 16-row blocks");
+  static_assert(S >= 3, "the pipeline keeps two stages ahead of the one computed");
+
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  // the LDS base as an opaque value: the optimizer cannot tell which LDS bytes
+  // the direct loads write, so it keeps every LDS read
+  uint32_t lds_base = uint32_t(reinterpret_cast<uintptr_t>(smem_raw));
+  asm volatile("" : "+s"(lds_base));
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave % WM, wn = wave / WM;
+
+  const int ntiles = p.tiles_m * p.tiles_n;
+  const int bid = blockIdx.x;
+  const int tile = (p.xcd_remap && (ntiles & 7) == 0) ? (bid & 7) * (ntiles >> 3) + (bid >> 3) : bid;
+  const int tm = tile % p.tiles_m, tn = tile / p.tiles_m;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int Ktot = p.K1 + p.K2;
+  const int kt_total = (Ktot + kBKd - 1) / kBKd;
+  int kt_begin, kt_end;
+  split_range(p, kBKd, kt_total, kt_begin, kt_end);
+
+  // this lane's slot in each of its LPW blocks: stage row, logical chunk,
+  // first- and second-part row pointers (clamped to a valid row)
+  const uint16_t* src1[LPW];
+  const uint16_t* src2[LPW];
+  int lcol[LPW];
+  bool real[LPW];
+#pragma unroll
+  for (int q = 0; q < LPW; ++q) {
+    const int blk = q * NW + wave;
+    const int row = blk * 16 + lane / 4;
+    const int rr = row < BN ? row : row - BN;                // row within its region
+    lcol[q] = 8 * ((lane & 3) ^ ((rr >> 1) & 3) ^ ((rr >> 3) & 1));
+    real[q] = (LPW * NW == BLKS) || row < ROWS;   // padding blocks only when the rows do not fill them
+    if (row < BN) {
+      const int n = min(n0 + rr, p.N - 1);
+      src1[q] = p.w + int64_t(n) * p.ldw;
+      src2[q] = p.b + int64_t(n) * p.ldb;
+    } else {
+      const int m = min(m0 + rr, p.M - 1);
+      src1[q] = p.x + int64_t(m) * p.ldx;
+      src2[q] = p.t + int64_t(m) * p.ldt;
+    }
+  }
+  const uint16_t* zero = reinterpret_cast<const uint16_t*>(kZeroChunk);
+  auto issue = [&](int stage, int kt) {
+#pragma unroll
+    for (int q = 0; q < LPW; ++q) {
+      const int kc = kt * kBKd + lcol[q];
+      // branch-free (bitwise, no short-circuit): one basic block per stage
+      const bool ok = real[q] & (kt < kt_end) & (kc < Ktot);
+      const uint16_t* g = kc < p.K1 ? src1[q] + kc : src2[q] + (kc - p.K1);
+      g = ok ? g : zero;
+      const uint32_t dst = lds_base + uint32_t(stage * STAGE + (q * NW + wave) * 1024);
+      __builtin_amdgcn_global_load_lds(g, reinterpret_cast<__attribute__((address_space(3))) void*>(uintptr_t(dst)),
+                                       16, 0, 0);
+    }
+  };
+
+  f32x16 acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  auto frag = [&](int stage, int row, int c) {
+    const uint32_t off = uint32_t(stage * STAGE + row * 64 + ((c ^ ((row >> 1) & 3) ^ ((row >> 3) & 1)) * 16));
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(uintptr_t(lds_base + off));
+  };
+
+  // Software pipeline over stages: the fragments of a stage's first k-step
+  // are read right after the barrier that publishes the stage, while the
+  // previous stage's second k-step still runs on the matrix cores; the wait
+  // and barrier for the next stage sit between the two k-steps' MFMAs, whose
+  // execution covers them.
+  auto read = [&](int stage, int kk, bf16x8 (&fa)[FN], bf16x8 (&fb)[FM]) {
+#pragma unroll
+    for (int a = 0; a < FN; ++a) fa[a] = frag(stage, wn * TN + a * 32 + lrow, 2 * kk + lhalf);
+#pragma unroll
+    for (int b = 0; b < FM; ++b) fb[b] = frag(stage, BN + wm * TM + b * 32 + lrow, 2 * kk + lhalf);
+  };
+  auto mma = [&](const bf16x8 (&fa)[FN], const bf16x8 (&fb)[FM]) {
+#pragma unroll
+    for (int a = 0; a < FN; ++a)
+#pragma unroll
+      for (int b = 0; b < FM; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+  };
+  auto sync_stage = [&]() {
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  const int nk = kt_end - kt_begin;
+  if (nk > 0) {
+    bf16x8 f0a[FN], f0b[FM], f1a[FN], f1b[FM];
+#pragma unroll
+    for (int s = 0; s + 1 < S; ++s) issue(s, kt_begin + s);
+    wait_vm<(S - 2) * LPW>();   // stage 0 landed
+    sync_stage();
+    read(0, 0, f0a, f0b);
+    for (int i = 0; i < nk; ++i) {
+      read(i % S, 1, f1a, f1b);
+      mma(f0a, f0b);
+      __builtin_amdgcn_sched_group_barrier(0x100, FN + FM, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, FN * FM, 0);
+      wait_vm<(S - 3) * LPW>();   // stage i + 1 landed (past the end: zero loads)
+      sync_stage();
+      issue((i + S - 1) % S, kt_begin + i + S - 1);
+      read((i + 1) % S, 0, f0a, f0b);
+      mma(f1a, f1b);
+      __builtin_amdgcn_sched_group_barrier(0x020, LPW, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, FN + FM, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, FN * FM, 0);
+    }
+  }
+  // drain the trailing (unused) prefetches before the workgroup exits
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+
+  // epilogue: lane owns column m = lrow of each fragment, rows n = 8g + 4*lhalf + e
+#pragma unroll
+  for (int j = 0; j < FM; ++j) {
+    const int m = m0 + wm * TM + j * 32 + lrow;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * TN + i * 32 + 8 * g + 4 * lhalf;
+        const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
+        const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+        if constexpr (MODE == 0) {
+          uint16_t* dst = p.y + int64_t(m) * p.ldy + n;
+          if (p.y_vec && n + 3 < p.N) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+          } else {
+            const float vv[4] = {v0, v1, v2, v3};
+            for (int e = 0; e < 4; ++e)
+              if (n + e < p.N) dst[e] = f32_to_bf16(vv[e]);
+          }
+        } else {
+          float* dst = p.part + (int64_t(blockIdx.y) * p.M + m) * p.N + n;
+          if (n + 3 < p.N && (p.N & 3) == 0) {
+            *reinterpret_cast<f32x4*>(dst) = f32x4{v0, v1, v2, v3};
+          } else {
+            const float vv[4] = {v0, v1, v2, v3};
+            for (int e = 0; e < 4; ++e)
+              if (n + e < p.N) dst[e] = vv[e];
+          }
+        }
+      }
+    }
+  }
+}
+
 // y = bf16(sum_s part[s]) in split order; 4 consecutive outputs per thread.
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restrict__ part, int splits, int M, int N,
                                                           uint16_t* __restrict__ y, int64_t ldy, int y_vec) {
@@ -376,7 +580,9 @@ constexpr TileShape kShapes[] = {
     {"64x64w4", 64, 64, 4},          {"128x128w4", 128, 128, 4},      {"256x192w4", 256, 192, 4},
     {"256x192w8", 256, 192, 8},      {"256x192w8p1", 256, 192, 8},    {"256x192w8p2d0", 256, 192, 8},
     {"256x128w8", 256, 128, 8},      {"256x128w8p2d0", 256, 128, 8},  {"256x256w4", 256, 256, 4},
-    {"256x256w8p1", 256, 256, 8},
+    {"256x256w8p1", 256, 256, 8},    {"dl256x256s4", 256, 256, 8},    {"dl256x256s5", 256, 256, 8},
+    {"dl256x192s4", 256, 192, 8},    {"dl256x192s5", 256, 192, 8},    {"dl256x128s6", 256, 128, 8},
+    {"dl128x128s6", 128, 128, 4},    {"dl256x256w4s4", 256, 256, 4},  {"dl256x256w4s5", 256, 256, 4},
 };
 constexpr int kNumShapes = int(sizeof(kShapes) / sizeof(kShapes[0]));
 
@@ -402,11 +608,36 @@ hipError_t launch_tile(GemmParams p, int splits, hipStream_t stream, const char*
     const char* env = getenv("UNO_GEMM_XCD");   // tuning override: 0 disables the remap
     p.xcd_remap = env ? atoi(env) : 1;
   }
-  const int kt_total = (p.K1 + p.K2 + kBK - 1) / kBK;
-  p.ktiles_per_split = (kt_total + splits - 1) / splits;
+  p.ktiles_per_split = ((p.K1 + kBK - 1) / kBK + splits - 1) / splits;
   dim3 grid(p.tiles_m * p.tiles_n, splits);
   ProfileScope ps(name, stream);
   hipLaunchKernelGGL(kern, grid, dim3(WM * WN * kWave), lds, stream, p);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, int S, int MODE>
+hipError_t launch_tile_dl(GemmParams p, int splits, hipStream_t stream, const char* name) {
+  auto kern = gemm_dl_kernel<BM, BN, WM, WN, S, MODE>;
+  constexpr int NW = WM * WN;
+  constexpr int LPW = ((BN + BM + 15) / 16 + NW - 1) / NW;
+  const size_t lds = size_t(S) * LPW * NW * 1024;
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  p.tiles_m = (p.M + BM - 1) / BM;
+  p.tiles_n = (p.N + BN - 1) / BN;
+  {
+    const char* env = getenv("UNO_GEMM_XCD");
+    p.xcd_remap = env ? atoi(env) : 1;
+  }
+  p.ktiles_per_split = ((p.K1 + kBKd - 1) / kBKd + splits - 1) / splits;
+  dim3 grid(p.tiles_m * p.tiles_n, splits);
+  ProfileScope ps(name, stream);
+  hipLaunchKernelGGL(kern, grid, dim3(NW * kWave), lds, stream, p);
   return hipGetLastError();
 }
 
@@ -423,6 +654,14 @@ hipError_t launch_cfg(const TileCfg& c, const GemmParams& p, hipStream_t stream,
     case 7: return launch_tile<256, 128, 4, 2, 2, 0, MODE>(p, c.splits, stream, name);
     case 8: return launch_tile<256, 256, 2, 2, 1, 0, MODE>(p, c.splits, stream, name);
     case 9: return launch_tile<256, 256, 4, 2, 1, 0, MODE>(p, c.splits, stream, name);
+    case 10: return launch_tile_dl<256, 256, 4, 2, 4, MODE>(p, c.splits, stream, name);
+    case 11: return launch_tile_dl<256, 256, 4, 2, 5, MODE>(p, c.splits, stream, name);
+    case 12: return launch_tile_dl<256, 192, 4, 2, 4, MODE>(p, c.splits, stream, name);
+    case 13: return launch_tile_dl<256, 192, 4, 2, 5, MODE>(p, c.splits, stream, name);
+    case 14: return launch_tile_dl<256, 128, 4, 2, 6, MODE>(p, c.splits, stream, name);
+    case 15: return launch_tile_dl<128, 128, 2, 2, 6, MODE>(p, c.splits, stream, name);
+    case 16: return launch_tile_dl<256, 256, 2, 2, 4, MODE>(p, c.splits, stream, name);
+    case 17: return launch_tile_dl<256, 256, 2, 2, 5, MODE>(p, c.splits, stream, name);
   }
   return hipErrorInvalidValue;
 }
@@ -435,6 +674,8 @@ int shape_index(const char* name) {
 
 // Main-GEMM configuration.  UNO_GEMM_TILE="<shape name>[/splits]" overrides
 // the choice (tuning sweeps).
+// The choice depends on the base K only, so a call with and without adapter
+// columns runs the same kernel and split (bit-identical gate-0 rows).
 TileCfg choose_main_tile(int64_t M, int64_t N, int64_t Ktot) {
   const char* env = getenv("UNO_GEMM_TILE");
   if (env) {
@@ -449,20 +690,22 @@ TileCfg choose_main_tile(int64_t M, int64_t N, int64_t Ktot) {
       if (id >= 0 && s >= 1 && s <= 16) return {id, s};
     }
   }
-  // Measured on MI355X at M = 1024: 256x256 tiles with 8 waves are fastest
-  // when they alone give >= 160 tiles (the 4096 -> 12288 projections); below
-  // that, 256x128 (8 waves) or 128x128 tiles with split-K up to 4 to reach
-  // ~200 work units, keeping >= 16 K-tiles per split.
+  // Measured on MI355X at M = 1024 (event-timed sweeps):
+  //   4096 -> 12288: direct-load 256x192, 4 stages (256 tiles, one per CU);
+  //   12288 -> 4096: 256x256 (8 waves) with 4 K-splits;
+  //   4096 -> 4096: direct-load 128x128, no split (256 tiles);
+  //   4096 -> 1024: direct-load 128x128 with 4 K-splits.
   auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   const int64_t kt = (Ktot + kBK - 1) / kBK;
-  auto splits_for = [&](int64_t t) {
+  auto splits_for = [&](int64_t t, int smax, int min_kt) {
     int s = 1;
-    while (t * s < 200 && s < 4 && kt / (2 * s) >= 16) s *= 2;
+    while (t * s < 192 && s < smax && kt / (2 * s) >= min_kt) s *= 2;
     return s;
   };
-  if (M >= 512 && N % 256 == 0 && tiles(256, 256) >= 160) return {9, 1};
-  if (M >= 512 && N % 128 == 0) return {7, splits_for(tiles(256, 128))};
-  return {1, splits_for(tiles(128, 128))};
+  if (M >= 512 && N % 192 == 0 && tiles(256, 192) >= 192) return {12, 1};
+  if (M >= 512 && N % 256 == 0 && tiles(256, 256) >= 64 && kt >= 128) return {9, splits_for(tiles(256, 256), 4, 8)};
+  if (M >= 512 && N % 128 == 0) return {15, splits_for(tiles(128, 128), 4, 8)};
+  return {1, splits_for(tiles(128, 128), 4, 16)};
 }
 
 int lora_down_splits(int64_t M, int64_t r, int64_t K) {
@@ -484,7 +727,7 @@ size_t gated_lora_workspace_bytes(uno_dtype dtype, int64_t M, int64_t N, int64_t
     const int s = lora_down_splits(M, r, K);
     bytes += align_up(size_t(M) * size_t(r) * 2, 256) + align_up(size_t(s) * size_t(M) * size_t(r) * 4, 256);
   }
-  const TileCfg c = choose_main_tile(M, N, K + r);
+  const TileCfg c = choose_main_tile(M, N, K);
   if (c.splits > 1) bytes += align_up(size_t(c.splits) * size_t(M) * size_t(N) * 4, 256);
   return bytes;
 }
@@ -557,7 +800,7 @@ hipError_t launch_gated_lora(const GatedLoraArgs& a, hipStream_t stream) {
   g.y = static_cast<uint16_t*>(a.y);
   g.ldy = a.ldy;
   g.y_vec = (a.ldy % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.y) & 7u) == 0);
-  const TileCfg c = choose_main_tile(a.M, a.N, a.K + g.K2);
+  const TileCfg c = choose_main_tile(a.M, a.N, a.K);
   if (c.splits == 1) return launch_cfg<0>(c, g, stream, "uno_gemm_bf16");
   g.part = reinterpret_cast<float*>(ws);
   hipError_t e = launch_cfg<1>(c, g, stream, "uno_gemm_bf16_splitk");

@@ -9,9 +9,10 @@
 // is (node r / G, head g*G + r % G), G = H / H_kv, so the G heads sharing a KV
 // head share every K/V fetch.  Keys are the ctx cache rows followed by the n
 // tree nodes, in blocks of 32.  The key blocks of a unit are split over KS
-// workgroups (KS chosen so a decode-sized call still spreads over the chip)
-// and, inside a workgroup, over its 4 waves; each wave keeps the next block's
-// K and V in flight in registers while it computes the current one.  Waves
+// workgroups (KS chosen so a decode-sized call still spreads over the chip,
+// with every workgroup resident at once) and, inside a workgroup, over its 4
+// waves.  All global loads of the set-up (parent ids, query rows, the first
+// K/V block) are issued before any of them is used.  Waves
 // merge their online-softmax states in LDS; with KS > 1 each workgroup writes
 // its merged (max, sum, unnormalised O) to the workspace and a combine kernel
 // merges the KS partials of every row in a fixed order.
@@ -45,9 +46,11 @@ constexpr int kKB = 32;                 // keys per block
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kMaxNodes = 256;
+static_assert(kMaxNodes <= kThreads, "one thread per tree node in the set-up");
 constexpr int kVtStride = 36;           // bf16 per transposed-V row (32 keys + pad)
 constexpr int kXcd = 8;
-constexpr int kTargetWgs = 640;         // ~2.5 workgroups per CU
+constexpr int kTargetWgs = 512;         // 2 resident workgroups per CU (register-bound)
+constexpr int kMrgStride = kHD + 4;     // fp32 row stride of the merge buffer (bank spread)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -73,7 +76,7 @@ AttnPlan make_plan(int batch, int n, int ctx, int H, int Hkv) {
   const int64_t base = int64_t(p.tiles) * Hkv * batch;
   int ks = 1;
   if (base < kTargetWgs) {
-    ks = int((kTargetWgs + base - 1) / base);
+    ks = int(kTargetWgs / base);      // every workgroup resident at once
     const int most = (p.nblk + kWaves - 1) / kWaves;   // at least one block per wave
     if (ks > most) ks = most;
     if (ks < 1) ks = 1;
@@ -157,14 +160,28 @@ __global__ __launch_bounds__(kThreads) void tree_attn_kernel(TreeAttnArgs a, Att
     for (int t = 0; t < 8; ++t) vr[t] = *reinterpret_cast<const u32x4*>(vrow + 8 * (lh + 2 * t));
   };
 
+  // ---- every global load of the set-up is issued first: parent ids, this
+  // lane's query row, the first K/V block
+  const int par_i = tid < n ? a.parent[int64_t(b) * n + tid] : 0;   // n <= kThreads
+  const int r = row0 + lrow;
+  const bool row_ok = r < nrows;
+  const int node = row_ok ? r / G : 0;
+  const int head = g * G + (row_ok ? r % G : 0);
+  u32x4 qv[kHD / 16];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t(b) * n + node) * H + head) * kHD;
+#pragma unroll
+    for (int s = 0; s < kHD / 16; ++s) qv[s] = *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * lh);
+  }
   u32x4 kr[8], vr[8];
-  if (nb > 0) load_block(j0, kr, vr);   // first block in flight during the set-up below
+  if (nb > 0) load_block(j0, kr, vr);
 
   // ---- parent array to LDS, then ancestor-or-self bitsets (one thread per node)
   if (tid == 0) sh_bad = 0;
-  for (int i = tid; i < n; i += kThreads) sh_par[i] = a.parent[int64_t(b) * n + i];
+  if (tid < n) sh_par[tid] = par_i;
   __syncthreads();
-  for (int i = tid; i < n; i += kThreads) {
+  if (tid < n) {
+    const int i = tid;
     uint64_t w[4] = {0, 0, 0, 0};
     int j = i, steps = 0;
     bool bad = false;
@@ -190,20 +207,9 @@ __global__ __launch_bounds__(kThreads) void tree_attn_kernel(TreeAttnArgs a, Att
   __syncthreads();
   const bool bad_tree = sh_bad != 0;
 
-  // ---- this lane's query row
-  const int r = row0 + lrow;
-  const bool row_ok = r < nrows;
-  const int node = row_ok ? r / G : 0;
-  const int head = g * G + (row_ok ? r % G : 0);
   bf16x8 qf[kHD / 16];
-  {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t(b) * n + node) * H + head) * kHD;
 #pragma unroll
-    for (int s = 0; s < kHD / 16; ++s) {
-      u32x4 v = row_ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * lh) : u32x4{0u, 0u, 0u, 0u};
-      qf[s] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
+  for (int s = 0; s < kHD / 16; ++s) qf[s] = __builtin_bit_cast(bf16x8, row_ok ? qv[s] : u32x4{0u, 0u, 0u, 0u});
   const uint64_t my_anc0 = anc[node][0], my_anc1 = anc[node][1], my_anc2 = anc[node][2], my_anc3 = anc[node][3];
 
   const float sc = a.scale * kLog2e;
@@ -301,12 +307,13 @@ __global__ __launch_bounds__(kThreads) void tree_attn_kernel(TreeAttnArgs a, Att
 
   // ---- merge the 4 waves' states: (2,3) -> (0,1), then 1 -> 0; vt reused as fp32 [32 rows][128 d]
   __syncthreads();
-  float* ob = reinterpret_cast<float*>(&vt[0][0]);    // room for 2 x 32 x 128 floats
+  float* ob = reinterpret_cast<float*>(&vt[0][0]);    // room for 2 x 32 x kMrgStride floats
+  static_assert(2 * 32 * kMrgStride * sizeof(float) <= sizeof(vt), "merge buffer fits in the V tiles");
 #pragma unroll
   for (int round = 0; round < 2; ++round) {
     const int writers_lo = (round == 0) ? 2 : 1, writers_hi = (round == 0) ? 4 : 2;
     if (wave >= writers_lo && wave < writers_hi) {
-      float* dst = ob + (wave - writers_lo) * 32 * kHD;
+      float* dst = ob + (wave - writers_lo) * 32 * kMrgStride;
       if (lh == 0) {
         mrg_m[wave][lrow] = m;
         mrg_s[wave][lrow] = ssum;
@@ -314,12 +321,12 @@ __global__ __launch_bounds__(kThreads) void tree_attn_kernel(TreeAttnArgs a, Att
 #pragma unroll
       for (int db = 0; db < kHD / 32; ++db)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) dst[lrow * kHD + 32 * db + 8 * (e >> 2) + 4 * lh + (e & 3)] = o[db][e];
+        for (int e = 0; e < 16; ++e) dst[lrow * kMrgStride + 32 * db + 8 * (e >> 2) + 4 * lh + (e & 3)] = o[db][e];
     }
     __syncthreads();
     if (wave < writers_lo) {
       const int src_w = wave + writers_lo;
-      const float* src = ob + wave * 32 * kHD;
+      const float* src = ob + wave * 32 * kMrgStride;
       const float m2 = mrg_m[src_w][lrow], s2 = mrg_s[src_w][lrow];
       const float mn = fmaxf(m, m2);
       const float a1 = (mn == -INFINITY) ? 0.f : fexp2(m - mn);
@@ -330,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void tree_attn_kernel(TreeAttnArgs a, Att
       for (int db = 0; db < kHD / 32; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          o[db][e] = o[db][e] * a1 + src[lrow * kHD + 32 * db + 8 * (e >> 2) + 4 * lh + (e & 3)] * a2;
+          o[db][e] = o[db][e] * a1 + src[lrow * kMrgStride + 32 * db + 8 * (e >> 2) + 4 * lh + (e & 3)] * a2;
     }
     __syncthreads();
   }
@@ -368,8 +375,9 @@ __global__ __launch_bounds__(kThreads) void tree_attn_kernel(TreeAttnArgs a, Att
   }
 }
 
-// Merge of the KS split partials of 8 rows per workgroup, ks ascending:
-// M = max m_k, S = sum s_k 2^(m_k - M), O = sum O_k 2^(m_k - M) / S.
+// Merge of the KS split partials of 8 rows per workgroup, ks ascending
+// (the result is M = max m_k, S = sum s_k 2^(m_k - M),
+// O = sum O_k 2^(m_k - M) / S).
 // Thread t: row 8 * (blockIdx.x % 4) + t / 32 of the tile, dims 4 (t % 32) .. +4.
 constexpr int kCombineThreads = 256;
 
@@ -386,24 +394,37 @@ __global__ __launch_bounds__(kCombineThreads) void tree_attn_combine_kernel(Tree
   const int64_t grp0 = (int64_t(b) * a.n_kv + g) * pl.ks;
   auto prow = [&](int k) { return ((grp0 + k) * pl.tiles + tile) * 32 + rin; };
 
-  float M = -INFINITY;
-  bool bad = false;
-#pragma unroll 4
-  for (int k = 0; k < pl.ks; ++k) {
-    const float mk = part.ms[prow(k)].x;
-    bad |= __builtin_isnan(mk);
-    M = fmaxf(M, mk);
-  }
-  float S = 0.f;
+  // online merge, 8 partials per step with all 16 loads of a step in flight
+  float M = -INFINITY, S = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int k = 0; k < pl.ks; ++k) {
-    const int64_t pr = prow(k);
-    const float2 ms = part.ms[pr];
-    const f32x4 v = *reinterpret_cast<const f32x4*>(part.o + pr * kHD + d0);
-    const float w = (ms.x == -INFINITY) ? 0.f : fexp2(ms.x - M);
-    S += ms.y * w;
-    acc += v * w;
+  bool bad = false;
+  for (int k0 = 0; k0 < pl.ks; k0 += 8) {
+    float2 ms[8];
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t pr = prow(min(k0 + u, pl.ks - 1));   // past the end: unused
+      ms[u] = part.ms[pr];
+      v[u] = *reinterpret_cast<const f32x4*>(part.o + pr * kHD + d0);
+    }
+    float mb = M;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (k0 + u < pl.ks) {
+        bad |= __builtin_isnan(ms[u].x);
+        mb = fmaxf(mb, ms[u].x);
+      }
+    const float resc = (M == -INFINITY) ? 0.f : fexp2(M - mb);
+    S *= resc;
+    acc *= resc;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (k0 + u < pl.ks) {
+        const float w = (ms[u].x == -INFINITY) ? 0.f : fexp2(ms[u].x - mb);
+        S += ms[u].y * w;
+        acc += v[u] * w;
+      }
+    M = mb;
   }
   const float inv = bad ? __builtin_nanf("") : 1.f / S;
   uint16_t* orow = static_cast<uint16_t*>(a.out) + ((int64_t(b) * a.n_tree + node) * a.n_heads + head) * kHD;
