@@ -31,6 +31,16 @@ from .verify_linear import (
 )
 from .tree_attention import ancestors_or_self, tree_attention, tree_attention_dense_mask
 from .verify_tree import node_depths, children_lists, verify_tree
+from .decoder import (
+    round_bf16,
+    rms_norm,
+    rope,
+    block_mask,
+    block_attention,
+    silu_mul,
+    decoder_layer,
+    lm_head,
+)
 
 __all__ = [
     "gated_lora_linear",
@@ -46,4 +56,12 @@ __all__ = [
     "node_depths",
     "children_lists",
     "verify_tree",
+    "round_bf16",
+    "rms_norm",
+    "rope",
+    "block_mask",
+    "block_attention",
+    "silu_mul",
+    "decoder_layer",
+    "lm_head",
 ]
