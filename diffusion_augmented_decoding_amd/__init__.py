@@ -22,8 +22,23 @@ EXPORTS = (
     "uno_psi_spec_verify_linear_workspace", "uno_psi_spec_verify_linear",
     "uno_tree_verify_attention_workspace", "uno_tree_verify_attention",
     "uno_psi_spec_verify_tree_workspace", "uno_psi_spec_verify_tree",
+    "uno_rms_norm", "uno_rope", "uno_silu_mul",
+    "uno_block_verify_attention_workspace", "uno_block_verify_attention",
+    "uno_sample_rows_workspace", "uno_sample_rows",
+    "uno_decoder_layer_workspace", "uno_decoder_layer",
     "uno_profile_enable", "uno_profile_reset", "uno_profile_query",
 )
+
+
+NUM_PROJ = 7
+PROJ = ("q", "k", "v", "o", "g", "u", "d")    # q, k, v, o, gate, up, down (UNO_PROJ_* order)
+
+
+class LayerWeights(ctypes.Structure):
+    """uno_layer_weights: device pointers of one decoder layer."""
+    _fields_ = [("attn_norm", ctypes.c_void_p), ("mlp_norm", ctypes.c_void_p),
+                ("w", ctypes.c_void_p * NUM_PROJ), ("a", ctypes.c_void_p * NUM_PROJ),
+                ("b", ctypes.c_void_p * NUM_PROJ), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p)]
 
 
 class UnoError(RuntimeError):
@@ -61,6 +76,20 @@ def _declare(lib):
         "uno_psi_spec_verify_tree_workspace": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
         "uno_psi_spec_verify_tree": (ctypes.c_int, [_p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32,
                                                     _p, _p, _p, _p, _p, _p, _f32, _p, _p, _p, _p, _sz]),
+        "uno_rms_norm": (ctypes.c_int, [_p, _i64, _i32, _p, _i64, _p, _i64, _p, _i64, _p, _f32, _p, _i64]),
+        "uno_rope": (ctypes.c_int, [_p, _i64, _i32, _p, _i64, _p, _f32]),
+        "uno_silu_mul": (ctypes.c_int, [_p, _i64, _i32, _p, _i64, _p, _i64, _p, _i64]),
+        "uno_block_verify_attention_workspace": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _i32,
+                                                                ctypes.POINTER(_sz)]),
+        "uno_block_verify_attention": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                      _p, _p, _p, _p, _p, _f32, _p, _p, _p, _sz]),
+        "uno_sample_rows_workspace": (ctypes.c_int, [_i32, _i32, ctypes.POINTER(_sz)]),
+        "uno_sample_rows": (ctypes.c_int, [_p, ctypes.c_int, _i32, _i32, _p, _i64, _p, _f32, _p, _p, _sz]),
+        "uno_decoder_layer_workspace": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                       ctypes.POINTER(_sz)]),
+        "uno_decoder_layer": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                             ctypes.POINTER(LayerWeights), _p, _p, _f32, _f32, _f32,
+                                             _p, _p, _sz]),
         "uno_profile_enable": (None, [ctypes.c_int, ctypes.c_char_p]),
         "uno_profile_reset": (None, []),
         "uno_profile_query": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
@@ -272,6 +301,133 @@ def psi_spec_verify_tree(parent, tokens, p_logits, q_logits, u_accept, u_sample,
         float(temperature), _ptr(outputs["accept_len"]), _ptr(outputs["path"]), _ptr(outputs["token"]),
         _ptr(ws), _nbytes(ws)))
     return outputs
+
+
+# ------------------------------------------------------------------ layer ops
+def rms_norm(x, weight, eps=1e-6, res=None, sum_out=None, out=None, want_out=True, stream=None):
+    """RMSNorm of x [rows, dim] (uno_rms_norm); with res, x + res is formed
+    first and written to sum_out (default: x itself).  Returns out (or None)."""
+    import torch
+    load()
+    rows, dim = x.shape
+    if res is not None and sum_out is None:
+        sum_out = x
+    if out is None and want_out:
+        out = torch.empty((rows, dim), dtype=x.dtype, device=x.device)
+    _check(_lib.uno_rms_norm(
+        _stream(stream), rows, dim, _ptr(x), x.stride(0), _ptr(res), res.stride(0) if res is not None else dim,
+        _ptr(sum_out), sum_out.stride(0) if sum_out is not None else dim, _ptr(weight), float(eps),
+        _ptr(out), out.stride(0) if out is not None else dim))
+    return out
+
+
+def rope(x, positions, theta=1.0e6, stream=None):
+    """Rotary embedding in place on x [rows, n_heads * 128] (uno_rope)."""
+    load()
+    rows, width = x.shape
+    _check(_lib.uno_rope(_stream(stream), rows, width // 128, _ptr(x), x.stride(0), _ptr(positions), float(theta)))
+    return x
+
+
+def silu_mul(g, u, out=None, stream=None):
+    """out = silu(g) * u on [rows, dim] bf16 (uno_silu_mul)."""
+    import torch
+    load()
+    rows, dim = g.shape
+    if out is None:
+        out = torch.empty_like(g)
+    _check(_lib.uno_silu_mul(_stream(stream), rows, dim, _ptr(g), g.stride(0), _ptr(u), u.stride(0),
+                             _ptr(out), out.stride(0)))
+    return out
+
+
+def block_verify_attention_workspace(batch, block, ctx, n_heads, n_kv, head_dim):
+    load()
+    out = _sz(0)
+    _check(_lib.uno_block_verify_attention_workspace(batch, block, ctx, n_heads, n_kv, head_dim,
+                                                     ctypes.byref(out)))
+    return out.value
+
+
+def block_verify_attention(q, k_cache, v_cache, k_block, v_block, block, softmax_scale,
+                           out=None, lse=None, want_lse=True, workspace=None, stream=None):
+    """Block-masked GQA attention (uno_block_verify_attention).
+
+    q [B, 2*block, H, 128], k_cache/v_cache [B, ctx, Hkv, 128], k_block/v_block
+    [B, 2*block, Hkv, 128] (bf16, contiguous).  Returns (out, lse or None).
+    """
+    import torch
+    load()
+    bsz, n, nh, hd = q.shape
+    ctx = k_cache.shape[1]
+    nkv = k_block.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((bsz, n, nh), dtype=torch.float32, device=q.device)
+    ws = _workspace(block_verify_attention_workspace(bsz, block, ctx, nh, nkv, hd), q.device, workspace)
+    _check(_lib.uno_block_verify_attention(
+        _stream(stream), bsz, block, ctx, nh, nkv, hd, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_block), _ptr(v_block), float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws), _nbytes(ws)))
+    return out, lse
+
+
+def sample_rows_workspace(rows, vocab):
+    load()
+    out = _sz(0)
+    _check(_lib.uno_sample_rows_workspace(rows, vocab, ctypes.byref(out)))
+    return out.value
+
+
+def sample_rows(logits, u, temperature=1.0, out=None, workspace=None, stream=None):
+    """Inverse-CDF draw per row of softmax(logits / T) (uno_sample_rows).
+    logits [rows, V] (last dim contiguous), u f32 [rows].  Returns int32 [rows]."""
+    import torch
+    load()
+    rows, vocab = logits.shape
+    if out is None:
+        out = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    ws = _workspace(sample_rows_workspace(rows, vocab), logits.device, workspace)
+    _check(_lib.uno_sample_rows(_stream(stream), _dtype_code(logits), rows, vocab, _ptr(logits), logits.stride(0),
+                                _ptr(u), float(temperature), _ptr(out), _ptr(ws), _nbytes(ws)))
+    return out
+
+
+def decoder_layer_workspace(batch, block, ctx, hidden, inter, n_heads, n_kv, r):
+    load()
+    out = _sz(0)
+    _check(_lib.uno_decoder_layer_workspace(batch, block, ctx, hidden, inter, n_heads, n_kv, r,
+                                            ctypes.byref(out)))
+    return out.value
+
+
+def layer_weights(w, k_cache=None, v_cache=None):
+    """uno_layer_weights from a dict of device tensors: attn_norm, mlp_norm and
+    w/a/b + one of q k v o g u d (gate, up, down), e.g. "wq", "aq", "bq"."""
+    lw = LayerWeights()
+    lw.attn_norm = w["attn_norm"].data_ptr()
+    lw.mlp_norm = w["mlp_norm"].data_ptr()
+    for i, p in enumerate(PROJ):
+        lw.w[i] = w["w" + p].data_ptr()
+        lw.a[i] = w["a" + p].data_ptr() if ("a" + p) in w else None
+        lw.b[i] = w["b" + p].data_ptr() if ("b" + p) in w else None
+    lw.k_cache = k_cache.data_ptr() if k_cache is not None else None
+    lw.v_cache = v_cache.data_ptr() if v_cache is not None else None
+    return lw
+
+
+def decoder_layer(hidden_state, weights, gate, positions, batch, block, ctx, n_heads, n_kv, inter, r,
+                  rms_eps=1e-6, rope_theta=1.0e6, lora_scale=1.0, workspace=None, stream=None):
+    """One decoder layer in place on hidden_state [rows, hidden] (uno_decoder_layer).
+    weights: a LayerWeights (see layer_weights)."""
+    load()
+    hidden = hidden_state.shape[1]
+    ws = _workspace(decoder_layer_workspace(batch, block, ctx, hidden, inter, n_heads, n_kv, r),
+                    hidden_state.device, workspace)
+    _check(_lib.uno_decoder_layer(_stream(stream), batch, block, ctx, hidden, inter, n_heads, n_kv, r,
+                                  ctypes.byref(weights), _ptr(gate), _ptr(positions), float(rms_eps),
+                                  float(rope_theta), float(lora_scale), _ptr(hidden_state), _ptr(ws), _nbytes(ws)))
+    return hidden_state
 
 
 # ------------------------------------------------------------------ kernel timing

@@ -25,18 +25,9 @@ uno_status check_hip(hipError_t e, const char* what) {
   return fail(UNO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
 }  // namespace uno
 
 using namespace uno;
-
-#define UNO_GUARD_BEGIN try {
-#define UNO_GUARD_END                                                 \
-  }                                                                   \
-  catch (...) {                                                       \
-    return fail(UNO_ERR_INTERNAL, "internal error (exception caught)"); \
-  }
 
 extern "C" {
 

@@ -12,6 +12,15 @@ namespace uno {
 // Thread-local error message set by the entry points.
 uno_status fail(uno_status s, const char* fmt, ...);
 uno_status check_hip(hipError_t e, const char* what);
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// every exported function body sits in a try block: no exception crosses the ABI
+#define UNO_GUARD_BEGIN try {
+#define UNO_GUARD_END                                                            \
+  }                                                                              \
+  catch (...) {                                                                  \
+    return ::uno::fail(UNO_ERR_INTERNAL, "internal error (exception caught)");   \
+  }
 
 // Kernel timing: bracket a launch with events when profiling is on.
 struct ProfileScope {
@@ -70,6 +79,7 @@ hipError_t launch_gated_lora(const GatedLoraArgs& a, hipStream_t stream);
 // ---------------------------------------------------------------- tree attention
 struct TreeAttnArgs {
   int batch, n_tree, ctx, n_heads, n_kv, head_dim;
+  int block;                 // 0: prefix-tree mask from parent; > 0: clean/noisy block mask
   const void* q;
   const void* k_cache;
   const void* v_cache;
@@ -102,5 +112,50 @@ struct TreeVerifyArgs {
 };
 size_t tree_verify_workspace_bytes(int batch, int n_tree, int max_depth, int max_children, int vocab);
 hipError_t launch_tree_verify(const TreeVerifyArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- row sampler
+struct SampleRowsArgs {
+  uno_dtype dtype;
+  int rows, vocab;
+  const void* logits; int64_t row_stride;
+  const float* u;
+  float scale_log2;   // log2(e) / T
+  int32_t* out_tok;
+  void* ws;
+};
+size_t sample_rows_workspace_bytes(int rows, int vocab);
+hipError_t launch_sample_rows(const SampleRowsArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- layer ops
+struct RmsNormArgs {
+  int64_t rows;
+  int dim;
+  const void* x; int64_t ldx;
+  const void* res; int64_t ldr;      // optional: s = x + res first
+  void* sum_out; int64_t lds;        // bf16(s) (required with res; may alias x)
+  const void* weight;
+  float eps;
+  void* out; int64_t ldo;            // optional: bf16(s / rms(s) * weight)
+};
+int rms_norm_max_dim();
+hipError_t launch_rms_norm(const RmsNormArgs& a, hipStream_t stream);
+
+struct RopeArgs {
+  int64_t rows;
+  int n_heads;
+  void* x; int64_t ldx;              // [rows][n_heads * 128], rotated in place
+  const int32_t* positions;          // [rows]
+  float theta;
+};
+hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);
+
+struct SiluMulArgs {
+  int64_t rows;
+  int dim;
+  const void* g; int64_t ldg;
+  const void* u; int64_t ldu;
+  void* out; int64_t ldo;
+};
+hipError_t launch_silu_mul(const SiluMulArgs& a, hipStream_t stream);
 
 }  // namespace uno

@@ -1,0 +1,147 @@
+// Per-row and elementwise operations of a decoder layer, gfx950: RMSNorm with
+// an optional fused residual add, rotary position embedding, SwiGLU product.
+//
+// Method context: Uno summary (hyper.ai, arXiv 2609.04010), section "实验":
+// the adapters are attached to an open-weight Qwen3-8B model, so one decode
+// step runs that model's layers (pre-norm RMSNorm, rotary embeddings on q and
+// k, SwiGLU MLP, residual stream) over the concatenated clean + noisy rows.
+// All three are HBM-bound streams: one pass over their inputs, bf16 in and
+// out, fp32 arithmetic, 16-byte vector accesses.
+#include "device_common.h"
+#include "internal.h"
+
+namespace uno {
+
+namespace {
+
+constexpr int kNormThreads = 256;
+constexpr int kNormMaxVec = 8;            // 8-element vectors per thread: dim <= 256 * 8 * 8
+
+__device__ __forceinline__ void unpack8(const u32x4 v, float (&x)[8]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[2 * j] = bf16_lo(v[j]);
+    x[2 * j + 1] = bf16_hi(v[j]);
+  }
+}
+
+__device__ __forceinline__ u32x4 pack8(const float (&x)[8]) {
+  return u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+}
+
+// One workgroup per row.  RES: s = x + res is rounded to bf16 and stored to
+// sum_out (which may alias x), and the rounded s is what gets normalised.
+// out may be null (residual add only).
+template <bool RES>
+__global__ __launch_bounds__(kNormThreads) void rms_norm_kernel(RmsNormArgs a) {
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nvec = a.dim / 8;
+  const uint16_t* xr = static_cast<const uint16_t*>(a.x) + row * a.ldx;
+  float v[kNormMaxVec][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < kNormMaxVec; ++c) {
+    const int i = tid + c * kNormThreads;
+    if (i < nvec) {
+      unpack8(*reinterpret_cast<const u32x4*>(xr + 8 * i), v[c]);
+      if constexpr (RES) {
+        float y[8];
+        unpack8(*reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.res) + row * a.ldr + 8 * i), y);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[c][e] = bf16_to_f32(f32_to_bf16(v[c][e] + y[e]));
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.sum_out) + row * a.lds + 8 * i) = pack8(v[c]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = fmaf(v[c][e], v[c][e], ss);
+    }
+  }
+  if (a.out == nullptr) return;
+  ss = wave_sum(ss);
+  __shared__ float red[kNormThreads / kWave];
+  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kNormThreads / kWave; ++w) tot += red[w];
+  const float rs = 1.f / sqrtf(tot / float(a.dim) + a.eps);
+  const uint16_t* wr = static_cast<const uint16_t*>(a.weight);
+  uint16_t* orow = static_cast<uint16_t*>(a.out) + row * a.ldo;
+#pragma unroll
+  for (int c = 0; c < kNormMaxVec; ++c) {
+    const int i = tid + c * kNormThreads;
+    if (i < nvec) {
+      float w[8];
+      unpack8(*reinterpret_cast<const u32x4*>(wr + 8 * i), w);
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = v[c][e] * rs * w[e];
+      *reinterpret_cast<u32x4*>(orow + 8 * i) = pack8(o);
+    }
+  }
+}
+
+// In-place rotary embedding.  Thread (row, head, i < 64): the pair
+// (x_i, x_{i+64}) rotated by pos * theta^(-i/64); the angle is formed and
+// reduced in double precision, so positions far into a long context keep
+// their phase.
+__global__ __launch_bounds__(256) void rope_kernel(RopeArgs a) {
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t per_row = int64_t(a.n_heads) * 64;
+  if (t >= a.rows * per_row) return;
+  const int64_t row = t / per_row;
+  const int rem = int(t - row * per_row);
+  const int head = rem / 64, i = rem % 64;
+  uint16_t* p = static_cast<uint16_t*>(a.x) + row * a.ldx + head * 128;
+  const double inv_freq = exp(-double(i) / 64.0 * log(double(a.theta)));
+  double s, c;
+  sincos(double(a.positions[row]) * inv_freq, &s, &c);
+  const float cs = float(c), sn = float(s);
+  const float x1 = bf16_to_f32(p[i]), x2 = bf16_to_f32(p[i + 64]);
+  p[i] = f32_to_bf16(x1 * cs - x2 * sn);
+  p[i + 64] = f32_to_bf16(x2 * cs + x1 * sn);
+}
+
+// out = silu(g) * u = g / (1 + e^-g) * u, 8 elements per thread.
+__global__ __launch_bounds__(256) void silu_mul_kernel(SiluMulArgs a) {
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t per_row = a.dim / 8;
+  if (t >= a.rows * per_row) return;
+  const int64_t row = t / per_row;
+  const int c = int(t - row * per_row);
+  float g[8], u[8], o[8];
+  unpack8(*reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.g) + row * a.ldg + 8 * c), g);
+  unpack8(*reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.u) + row * a.ldu + 8 * c), u);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = g[e] / (1.f + expf(-g[e])) * u[e];
+  *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + row * a.ldo + 8 * c) = pack8(o);
+}
+
+}  // namespace
+
+int rms_norm_max_dim() { return kNormThreads * 8 * kNormMaxVec; }
+
+hipError_t launch_rms_norm(const RmsNormArgs& a, hipStream_t stream) {
+  ProfileScope ps(a.res ? "uno_add_rms_norm" : "uno_rms_norm", stream);
+  if (a.res)
+    hipLaunchKernelGGL(rms_norm_kernel<true>, dim3(unsigned(a.rows)), dim3(kNormThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(rms_norm_kernel<false>, dim3(unsigned(a.rows)), dim3(kNormThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope(const RopeArgs& a, hipStream_t stream) {
+  const int64_t n = a.rows * a.n_heads * 64;
+  ProfileScope ps("uno_rope", stream);
+  hipLaunchKernelGGL(rope_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_mul(const SiluMulArgs& a, hipStream_t stream) {
+  const int64_t n = a.rows * (a.dim / 8);
+  ProfileScope ps("uno_silu_mul", stream);
+  hipLaunchKernelGGL(silu_mul_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace uno

@@ -172,7 +172,88 @@ hipError_t launch_lin(const VerifyLinearArgs& a, hipStream_t stream) {
                         "uno_draw_seg", "uno_draw_resolve");
 }
 
+// ---------------------------------------------------------------- row sampler
+// y[row] = inverse CDF of softmax(logits[row] / T) at u[row], in token order:
+// the same statistics pass and two-launch draw as the verify sampler, with
+// the draw descriptor set to w = p.
+struct SrWs {
+  float2* part;     // [rows][splits]
+  DrawDesc* desc;   // [rows]
+  float* seg;
+};
+
+SrWs sr_ws(void* base, int rows, int vocab) {
+  const int ns = stats_splits(rows, vocab);
+  char* p = static_cast<char*>(base);
+  SrWs w;
+  w.part = reinterpret_cast<float2*>(p);
+  p += align_up(size_t(rows) * ns * sizeof(float2), 256);
+  w.desc = reinterpret_cast<DrawDesc*>(p);
+  p += align_up(size_t(rows) * sizeof(DrawDesc), 256);
+  w.seg = reinterpret_cast<float*>(p);
+  return w;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kChunkThreads) void sr_stats_kernel(SampleRowsArgs a, SrWs w) {
+  const int row = blockIdx.x, c = blockIdx.y, ns = gridDim.y;
+  const T* base = static_cast<const T*>(a.logits) + int64_t(row) * a.row_stride;
+  const int span = split_span(a.vocab, ns);
+  const int lo = c * span, hi = min(a.vocab, lo + span);
+  const float2 r = range_stats<T>(base, lo, hi, a.scale_log2);
+  if (threadIdx.x == 0) w.part[int64_t(row) * ns + c] = r;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kWave) void sr_desc_kernel(SampleRowsArgs a, SrWs w) {
+  const int row = blockIdx.x;
+  const int ns = stats_splits(a.rows, a.vocab);
+  const RowStat st = wave_merge_chunks(w.part + int64_t(row) * ns, ns);
+  if (threadIdx.x == 0) {
+    DrawDesc d;
+    d.prow = static_cast<const T*>(a.logits) + int64_t(row) * a.row_stride;
+    d.qrow = d.prow;
+    d.mp = st.m;
+    d.inv_sp = 1.f / st.s;
+    d.mq = 0.f;
+    d.inv_sq = 0.f;
+    d.c = 0.f;
+    d.active = 1;
+    w.desc[row] = d;
+  }
+}
+
+template <typename T>
+hipError_t launch_sr(const SampleRowsArgs& a, hipStream_t stream) {
+  const int ns = stats_splits(a.rows, a.vocab);
+  SrWs w = sr_ws(a.ws, a.rows, a.vocab);
+  {
+    ProfileScope ps("uno_sample_stats", stream);
+    hipLaunchKernelGGL(sr_stats_kernel<T>, dim3(a.rows, ns), dim3(kChunkThreads), 0, stream, a, w);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    ProfileScope ps("uno_sample_desc", stream);
+    hipLaunchKernelGGL(sr_desc_kernel<T>, dim3(a.rows), dim3(kWave), 0, stream, a, w);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_draw<T>(w.desc, a.rows, a.vocab, a.scale_log2, w.seg, a.u, a.out_tok, nullptr, stream,
+                        "uno_sample_seg", "uno_sample_resolve");
+}
+
 }  // namespace
+
+size_t sample_rows_workspace_bytes(int rows, int vocab) {
+  const int ns = stats_splits(rows, vocab);
+  return align_up(size_t(rows) * ns * sizeof(float2), 256) + align_up(size_t(rows) * sizeof(DrawDesc), 256) +
+         draw_seg_bytes(rows, vocab);
+}
+
+hipError_t launch_sample_rows(const SampleRowsArgs& a, hipStream_t stream) {
+  return a.dtype == UNO_BF16 ? launch_sr<uint16_t>(a, stream) : launch_sr<float>(a, stream);
+}
 
 size_t verify_linear_workspace_bytes(int batch, int k, int vocab) {
   const int rows = batch * (2 * k + 1);

@@ -210,6 +210,105 @@ uno_status uno_psi_spec_verify_tree(hipStream_t stream, uno_dtype logit_dtype,
                                     int32_t* out_accept_len, int32_t* out_path, int32_t* out_token,
                                     void* workspace, size_t workspace_bytes);
 
+/* ==========================================================================
+ * The composed decode step.  Source: Uno summary (hyper.ai), section 方法
+ * (one forward over the concatenated clean and noisy rows of a block, the
+ * adapter switched per row) and section 实验 (adapters on an open-weight
+ * Qwen3-8B model, rank 128, a KV cache shared by the draft and verify paths,
+ * full attention).  The pages give no layer internals; the functions below
+ * implement a Qwen3-shaped pre-norm layer: RMSNorm, rotary embeddings on q
+ * and k ("rotate half" pairing), grouped-query attention, SwiGLU MLP,
+ * residual stream.  Rows of one sequence are its `block` clean rows followed
+ * by its `block` noisy rows; sequences are consecutive.  All activations are
+ * bf16, row-major, 16-byte aligned with leading dimensions that are
+ * multiples of 8 elements.
+ * ======================================================================== */
+
+/* RMSNorm with an optional fused residual add.
+ *   res == NULL: out = bf16(x / sqrt(mean(x^2) + eps) * weight)
+ *   res != NULL: s = bf16(x + res) is written to sum_out (which may be x
+ *                itself), then out = bf16(s / sqrt(mean(s^2) + eps) * weight);
+ *                out may be NULL (residual add only).
+ * rows >= 1, 8 <= dim <= 16384, dim % 8 == 0; one pass over the inputs. */
+uno_status uno_rms_norm(hipStream_t stream, int64_t rows, int32_t dim,
+                        const void* x, int64_t ldx, const void* res, int64_t ldr,
+                        void* sum_out, int64_t ld_sum, const void* weight, float eps,
+                        void* out, int64_t ldo);
+
+/* Rotary position embedding, in place, on x [rows][n_heads][128]: element
+ * pair (i, i + 64) of every head is rotated by positions[row] * theta^(-i/64)
+ * (angle formed in double precision).  positions int32 [rows], >= 0. */
+uno_status uno_rope(hipStream_t stream, int64_t rows, int32_t n_heads, void* x, int64_t ldx,
+                    const int32_t* positions, float theta);
+
+/* SwiGLU product out = bf16(silu(g) * u), silu(g) = g / (1 + e^-g);
+ * [rows][dim], dim % 8 == 0; out may be g or u. */
+uno_status uno_silu_mul(hipStream_t stream, int64_t rows, int32_t dim, const void* g, int64_t ldg,
+                        const void* u, int64_t ldu, void* out, int64_t ldo);
+
+/* Block-masked GQA attention of the 2*block rows of every sequence over its
+ * KV cache and the block's own keys: clean row i (i < block) sees the whole
+ * cache and clean rows 0..i; a noisy row sees the whole cache and all 2*block
+ * rows of the block.  Layouts as uno_tree_verify_attention with
+ * n_tree = 2*block: q [batch][2*block][n_heads][128], k_block/v_block
+ * [batch][2*block][n_kv_heads][128], caches [batch][ctx_len][n_kv_heads][128].
+ * 1 <= block <= 128; workspace from the query (fp32 split partials). */
+uno_status uno_block_verify_attention_workspace(int32_t batch, int32_t block, int32_t ctx_len,
+                                                int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                                                size_t* bytes);
+uno_status uno_block_verify_attention(hipStream_t stream,
+                                      int32_t batch, int32_t block, int32_t ctx_len,
+                                      int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                                      const void* q, const void* k_cache, const void* v_cache,
+                                      const void* k_block, const void* v_block, float softmax_scale,
+                                      void* out, float* out_lse,
+                                      void* workspace, size_t workspace_bytes);
+
+/* Row sampler: out_token[i] = smallest v with cumsum(softmax(logits[i] / T))_v
+ * > u[i] (the last token with mass if rounding leaves none), in token order --
+ * the same inverse-CDF rule as the verify samplers' draws.  Used to draw the
+ * draft tokens from the noisy rows' distributions.  logits [rows] rows of
+ * `vocab` at row_stride elements (bf16 or fp32); u f32 [rows] in [0, 1). */
+uno_status uno_sample_rows_workspace(int32_t rows, int32_t vocab, size_t* bytes);
+uno_status uno_sample_rows(hipStream_t stream, uno_dtype logit_dtype, int32_t rows, int32_t vocab,
+                           const void* logits, int64_t row_stride, const float* u, float temperature,
+                           int32_t* out_token, void* workspace, size_t workspace_bytes);
+
+/* One decoder layer over the residual stream, in place.
+ * Weights (bf16, row-major): attn_norm and mlp_norm [hidden]; for each
+ * projection p in (q, k, v, o, gate, up, down), w[p] [out][in], a[p]
+ * [r][in], b[p] [out][r] with (out, in) = (n_heads*128, hidden),
+ * (n_kv_heads*128, hidden) twice, (hidden, n_heads*128), (inter, hidden)
+ * twice, (hidden, inter).  k_cache/v_cache [batch][ctx][n_kv_heads][128].
+ *   a = rmsnorm(h); q, k, v = gated_lora(a); rope(q), rope(k);
+ *   att = block_attention(q, cache + (k, v)); h += gated_lora(att, o);
+ *   a = rmsnorm(h); h += gated_lora(silu(gated_lora(a, gate)) * gated_lora(a, up), down)
+ * with every gated_lora as uno_gated_lora_linear under `gate` [rows] and
+ * lora_scale.  hidden_state [rows][hidden], rows = batch * 2 * block;
+ * positions int32 [rows].  The block's k and v are not written to the cache.
+ * hidden and inter multiples of 8, r a multiple of 8, n_heads / n_kv_heads
+ * <= 8, 1 <= block <= 128. */
+enum { UNO_PROJ_Q = 0, UNO_PROJ_K, UNO_PROJ_V, UNO_PROJ_O, UNO_PROJ_GATE, UNO_PROJ_UP, UNO_PROJ_DOWN,
+       UNO_NUM_PROJ };
+typedef struct {
+  const void* attn_norm;
+  const void* mlp_norm;
+  const void* w[UNO_NUM_PROJ];
+  const void* a[UNO_NUM_PROJ];
+  const void* b[UNO_NUM_PROJ];
+  const void* k_cache;
+  const void* v_cache;
+} uno_layer_weights;
+
+uno_status uno_decoder_layer_workspace(int32_t batch, int32_t block, int32_t ctx_len, int32_t hidden,
+                                       int32_t inter, int32_t n_heads, int32_t n_kv_heads, int32_t r,
+                                       size_t* bytes);
+uno_status uno_decoder_layer(hipStream_t stream, int32_t batch, int32_t block, int32_t ctx_len,
+                             int32_t hidden, int32_t inter, int32_t n_heads, int32_t n_kv_heads, int32_t r,
+                             const uno_layer_weights* weights, const uint8_t* gate, const int32_t* positions,
+                             float rms_eps, float rope_theta, float lora_scale,
+                             void* hidden_state, void* workspace, size_t workspace_bytes);
+
 /* --------------------------------------------------------------------------
  * Kernel timing (measurement support, not part of the method).
  * When enabled, every kernel the library launches whose name contains

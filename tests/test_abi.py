@@ -198,3 +198,94 @@ def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError):
         mod.load(str(tmp_path / "missing.so"))
     importlib.reload(dad)
+
+
+def test_layer_ops_reject_bad_calls(lib):
+    # uno_rms_norm(stream, rows, dim, x, ldx, res, ldr, sum_out, ld_sum, weight, eps, out, ldo)
+    assert lib.uno_rms_norm(None, 0, 64, FAKE16, 64, None, 64, None, 64, FAKE16, 1e-6, FAKE16, 64) == INVALID
+    assert lib.uno_rms_norm(None, 4, 12, FAKE16, 12, None, 12, None, 12, FAKE16, 1e-6, FAKE16, 12) == UNSUPPORTED
+    assert lib.uno_rms_norm(None, 4, 16392, FAKE16, 16392, None, 0, None, 0, FAKE16, 1e-6, FAKE16,
+                            16392) == UNSUPPORTED
+    assert lib.uno_rms_norm(None, 4, 64, FAKE16, 64, None, 64, None, 64, FAKE16, 1e-6, None, 64) == INVALID
+    assert lib.uno_rms_norm(None, 4, 64, FAKE16, 64, FAKE16, 64, None, 64, FAKE16, 1e-6, FAKE16, 64) == INVALID
+    assert lib.uno_rms_norm(None, 4, 64, FAKE16, 60, None, 64, None, 64, FAKE16, 1e-6, FAKE16, 64) == UNSUPPORTED
+    assert lib.uno_rms_norm(None, 4, 64, ctypes.c_void_p(0x10002), 64, None, 64, None, 64, FAKE16, 1e-6,
+                            FAKE16, 64) == UNSUPPORTED
+    assert lib.uno_rms_norm(None, 4, 64, FAKE16, 64, None, 64, None, 64, FAKE16, -1.0, FAKE16, 64) == INVALID
+    # uno_rope(stream, rows, n_heads, x, ldx, positions, theta)
+    assert lib.uno_rope(None, 0, 8, FAKE16, 1024, FAKE16, 1e6) == INVALID
+    assert lib.uno_rope(None, 4, 8, FAKE16, 1000, FAKE16, 1e6) == INVALID
+    assert lib.uno_rope(None, 4, 8, FAKE16, 1024, None, 1e6) == INVALID
+    assert lib.uno_rope(None, 4, 8, FAKE16, 1024, FAKE16, 1.0) == INVALID
+    # uno_silu_mul(stream, rows, dim, g, ldg, u, ldu, out, ldo)
+    assert lib.uno_silu_mul(None, 4, 12, FAKE16, 12, FAKE16, 12, FAKE16, 12) == INVALID
+    assert lib.uno_silu_mul(None, 4, 16, FAKE16, 16, None, 16, FAKE16, 16) == INVALID
+    assert lib.uno_silu_mul(None, 4, 16, FAKE16, 20, FAKE16, 16, FAKE16, 16) == UNSUPPORTED
+
+
+def test_block_attention_rejects_bad_calls(lib):
+    ws = ctypes.c_size_t(0)
+    assert lib.uno_block_verify_attention_workspace(128, 16, 8192, 32, 8, 128, ctypes.byref(ws)) == OK
+    assert ws.value == 0                          # 16 tiles x 8 KV heads x 128 sequences: no key splits
+    assert lib.uno_block_verify_attention_workspace(1, 16, 8192, 32, 8, 128, ctypes.byref(ws)) == OK
+    assert ws.value > 0
+    assert lib.uno_block_verify_attention_workspace(1, 129, 64, 32, 8, 128, ctypes.byref(ws)) == UNSUPPORTED
+    assert lib.uno_block_verify_attention_workspace(1, 16, 64, 32, 8, 64, ctypes.byref(ws)) == UNSUPPORTED
+    assert lib.uno_block_verify_attention_workspace(1, 16, 64, 30, 8, 128, ctypes.byref(ws)) == INVALID
+
+    def call(**kw):
+        a = dict(batch=2, block=4, ctx=2000, H=8, Hkv=2, D=128, q=FAKE16, kc=FAKE16, vc=FAKE16, kb=FAKE16,
+                 vb=FAKE16, scale=0.088, out=FAKE16, lse=None, ws=FAKE16, wsb=1 << 24)
+        a.update(kw)
+        return lib.uno_block_verify_attention(None, a["batch"], a["block"], a["ctx"], a["H"], a["Hkv"], a["D"],
+                                              a["q"], a["kc"], a["vc"], a["kb"], a["vb"], a["scale"], a["out"],
+                                              a["lse"], a["ws"], a["wsb"])
+    assert call(block=0) == INVALID
+    assert call(q=None) == INVALID
+    assert call(kc=None) == INVALID
+    assert call(kb=ctypes.c_void_p(0x10008)) == UNSUPPORTED
+    assert call(scale=0.0) == INVALID
+    assert call(ws=None, wsb=0) == WORKSPACE
+
+
+def test_sample_rows_rejects_bad_calls(lib):
+    ws = ctypes.c_size_t(0)
+    assert lib.uno_sample_rows_workspace(1920, 151936, ctypes.byref(ws)) == OK
+    assert ws.value > 0
+    assert lib.uno_sample_rows_workspace(0, 10, ctypes.byref(ws)) == INVALID
+
+    def call(**kw):
+        a = dict(dtype=BF16, rows=4, V=100, l=FAKE16, rs=100, u=FAKE16, T=1.0, y=FAKE16, ws=FAKE16, wsb=1 << 20)
+        a.update(kw)
+        return lib.uno_sample_rows(None, a["dtype"], a["rows"], a["V"], a["l"], a["rs"], a["u"], a["T"], a["y"],
+                                   a["ws"], a["wsb"])
+    assert call(dtype=4) == INVALID
+    assert call(rows=0) == INVALID
+    assert call(rows=65536) == UNSUPPORTED
+    assert call(rs=99) == INVALID
+    assert call(u=None) == INVALID
+    assert call(T=0.0) == INVALID
+    assert call(wsb=4) == WORKSPACE
+
+
+def test_decoder_layer_rejects_bad_calls(lib):
+    ws = ctypes.c_size_t(0)
+    assert lib.uno_decoder_layer_workspace(128, 16, 8192, 4096, 12288, 32, 8, 128, ctypes.byref(ws)) == OK
+    assert ws.value >= 4096 * 12288 * 2 * 2          # gate and up activations
+    assert lib.uno_decoder_layer_workspace(128, 16, 8192, 4100, 12288, 32, 8, 128,
+                                           ctypes.byref(ws)) == UNSUPPORTED
+    assert lib.uno_decoder_layer_workspace(128, 16, 8192, 4096, 12288, 32, 8, 12, ctypes.byref(ws)) == UNSUPPORTED
+    lw = lib.uno_decoder_layer.argtypes[9]._type_()      # the struct type the loaded library was declared with
+    assert lib.uno_decoder_layer(None, 2, 4, 8, 256, 512, 4, 2, 8, ctypes.byref(lw), FAKE16, FAKE16, 1e-6, 1e6,
+                                 1.0, FAKE16, FAKE16, 1 << 30) == INVALID      # null weights
+    lw.attn_norm = lw.mlp_norm = FAKE16.value
+    for i in range(dad.NUM_PROJ):
+        lw.w[i] = lw.a[i] = lw.b[i] = FAKE16.value
+    lw.k_cache = lw.v_cache = FAKE16.value
+    assert lib.uno_decoder_layer(None, 2, 4, 8, 256, 512, 4, 2, 8, ctypes.byref(lw), FAKE16, FAKE16, 1e-6, 1e6,
+                                 1.0, FAKE16, FAKE16, 16) == WORKSPACE
+    assert lib.uno_decoder_layer(None, 2, 4, 8, 256, 512, 4, 2, 8, ctypes.byref(lw), FAKE16, FAKE16, 1e-6, 0.5,
+                                 1.0, FAKE16, FAKE16, 1 << 30) == INVALID      # rope theta
+    lw.w[3] = None
+    assert lib.uno_decoder_layer(None, 2, 4, 8, 256, 512, 4, 2, 8, ctypes.byref(lw), FAKE16, FAKE16, 1e-6, 1e6,
+                                 1.0, FAKE16, FAKE16, 1 << 30) == INVALID

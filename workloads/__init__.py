@@ -316,3 +316,105 @@ def tiny_step(seed=0):
     lora = gated_lora_case(8, 256, 256, 8, dtype="f32", seed=seed, gate=gate)
     ver = verify_linear_case(2, 3, 1024, 0.5, dtype="f32", seed=seed, workers=1)
     return {"lora": lora, "verify": ver}
+
+
+# ------------------------------------------------------------ decoder layer
+_T_LAYER_H, _T_LAYER_W, _T_LAYER_A, _T_LAYER_B, _T_LAYER_NORM = 51, 52, 53, 54, 55
+_T_LAYER_KC, _T_LAYER_VC = 56, 57
+_T_ROWS_L, _T_ROWS_U = 61, 62
+
+LAYER_PROJ = ("q", "k", "v", "o", "g", "u", "d")     # q, k, v, o, gate, up, down
+
+
+def layer_shapes(hidden, inter, n_heads, n_kv_heads, head_dim=128):
+    """(out, in) of the seven projections of a Qwen3-style layer."""
+    qd, kvd = n_heads * head_dim, n_kv_heads * head_dim
+    return {"q": (qd, hidden), "k": (kvd, hidden), "v": (kvd, hidden), "o": (hidden, qd),
+            "g": (inter, hidden), "u": (inter, hidden), "d": (hidden, inter)}
+
+
+def layer_weights_case(hidden, inter, n_heads, n_kv_heads, r, seed=0, layer=0, weight_std=0.02,
+                       norm_std=0.1):
+    """bf16 weights of one layer: w{p} [out, in], a{p} [r, in], b{p} [out, r]
+    ~ N(0, weight_std^2); attn_norm, mlp_norm = 1 + N(0, norm_std^2).
+
+    Returns {name: uint16 bits} and {name + "_f32": exact values}."""
+    out = {}
+    for i, (p, (n_out, n_in)) in enumerate(layer_shapes(hidden, inter, n_heads, n_kv_heads).items()):
+        for name, tag, shp in (("w", _T_LAYER_W, (n_out, n_in)), ("a", _T_LAYER_A, (r, n_in)),
+                               ("b", _T_LAYER_B, (n_out, r))):
+            x = rng_for(seed, tag, layer, i).standard_normal(shp, dtype=np.float32) * np.float32(weight_std)
+            out[name + p], out[name + p + "_f32"] = _store(x, "bf16")
+    for j, name in enumerate(("attn_norm", "mlp_norm")):
+        x = 1.0 + rng_for(seed, _T_LAYER_NORM, layer, j).standard_normal(hidden, dtype=np.float32) * np.float32(norm_std)
+        out[name], out[name + "_f32"] = _store(x, "bf16")
+    return out
+
+
+def layer_seq_rows(seed, b, block, hidden, x_std=1.0):
+    """Residual-stream rows of sequence b: 2*block rows of N(0, x_std^2), bf16
+    bits (clean rows then noisy rows)."""
+    x = rng_for(seed, _T_LAYER_H, b).standard_normal((2 * block, hidden), dtype=np.float32) * np.float32(x_std)
+    return bf16_bits(x)
+
+
+def _kv_seq(args):
+    seed, layer, b, ctx, nkv, head_dim, std = args
+    k = rng_for(seed, _T_LAYER_KC, layer, b).standard_normal((ctx, nkv, head_dim), dtype=np.float32)
+    v = rng_for(seed, _T_LAYER_VC, layer, b).standard_normal((ctx, nkv, head_dim), dtype=np.float32)
+    return bf16_bits(k * np.float32(std)), bf16_bits(v * np.float32(std))
+
+
+def kv_cache_seq(seed, layer, b, ctx, n_kv_heads, head_dim=128, std=1.0):
+    """KV cache of sequence b in one layer: (k, v) bf16 bits [ctx, Hkv, D] ~ N(0, std^2)."""
+    return _kv_seq((seed, layer, b, ctx, n_kv_heads, head_dim, std))
+
+
+def kv_cache_case(batch, ctx, n_kv_heads, seed=0, layer=0, std=1.0, workers=None):
+    """KV cache of a batch, (k, v) bf16 bits [batch, ctx, Hkv, 128]; sequence b
+    equals kv_cache_seq(seed, layer, b, ...)."""
+    kc = np.empty((batch, ctx, n_kv_heads, 128), dtype=np.uint16)
+    vc = np.empty((batch, ctx, n_kv_heads, 128), dtype=np.uint16)
+    jobs = [(seed, layer, b, ctx, n_kv_heads, 128, std) for b in range(batch)]
+    if workers is None:
+        workers = min(16, len(os.sched_getaffinity(0)))
+    if workers > 1 and batch * ctx * n_kv_heads * 128 > (1 << 24):
+        with ProcessPoolExecutor(max_workers=workers) as ex:
+            for b, (k, v) in enumerate(ex.map(_kv_seq, jobs, chunksize=max(1, batch // (4 * workers)))):
+                kc[b], vc[b] = k, v
+    else:
+        for b, job in enumerate(jobs):
+            kc[b], vc[b] = _kv_seq(job)
+    return kc, vc
+
+
+def block_positions(batch, block, ctx):
+    """Clean row i and noisy row i of every sequence sit at position ctx + i."""
+    per = np.concatenate([np.arange(block), np.arange(block)]) + ctx
+    return np.tile(per, batch).astype(np.int32)
+
+
+def decoder_layer_case(batch, block, ctx, hidden, inter, n_heads, n_kv_heads, r, seed=0, layer=0,
+                       weight_std=0.02, norm_std=0.1, kv_std=1.0, workers=None):
+    """Inputs of one decoder layer over `batch` sequences of `block` clean +
+    `block` noisy rows: residual stream h [rows, hidden], gate (0 clean,
+    1 noisy), positions, KV cache [batch, ctx, Hkv, 128] and the weights (all
+    bf16 bits).  Sequence b's rows and cache can be regenerated alone with
+    layer_seq_rows / kv_cache_seq."""
+    rows = batch * 2 * block
+    h = np.concatenate([layer_seq_rows(seed, b, block, hidden) for b in range(batch)], axis=0)
+    kc, vc = kv_cache_case(batch, ctx, n_kv_heads, seed, layer, kv_std, workers)
+    return {"batch": batch, "block": block, "ctx": ctx, "hidden": hidden, "inter": inter,
+            "n_heads": n_heads, "n_kv_heads": n_kv_heads, "r": r, "seed": seed, "layer": layer,
+            "h": h, "gate": default_gate(rows, block), "positions": block_positions(batch, block, ctx),
+            "k_cache": kc, "v_cache": vc,
+            "weights": layer_weights_case(hidden, inter, n_heads, n_kv_heads, r, seed, layer, weight_std,
+                                          norm_std)}
+
+
+def rows_case(rows, vocab, dtype="bf16", seed=0, std=2.0):
+    """Logits [rows, vocab] ~ N(0, std^2) in `dtype` storage and uniforms [rows]."""
+    x = rng_for(seed, _T_ROWS_L).standard_normal((rows, vocab), dtype=np.float32) * np.float32(std)
+    st, val = _store(x, dtype)
+    u = rng_for(seed, _T_ROWS_U).random(rows, dtype=np.float32)
+    return {"logits": st, "logits_f32": val, "u": u}
