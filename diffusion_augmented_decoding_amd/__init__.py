@@ -26,6 +26,7 @@ EXPORTS = (
     "uno_block_verify_attention_workspace", "uno_block_verify_attention",
     "uno_sample_rows_workspace", "uno_sample_rows",
     "uno_decoder_layer_workspace", "uno_decoder_layer",
+    "uno_psi_spec_step_workspace", "uno_psi_spec_step",
     "uno_profile_enable", "uno_profile_reset", "uno_profile_query",
 )
 
@@ -39,6 +40,13 @@ class LayerWeights(ctypes.Structure):
     _fields_ = [("attn_norm", ctypes.c_void_p), ("mlp_norm", ctypes.c_void_p),
                 ("w", ctypes.c_void_p * NUM_PROJ), ("a", ctypes.c_void_p * NUM_PROJ),
                 ("b", ctypes.c_void_p * NUM_PROJ), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p)]
+
+
+class StepConfig(ctypes.Structure):
+    """uno_step_config: shapes and scalars of one decode step."""
+    _fields_ = [(n, ctypes.c_int32) for n in ("batch", "block", "ctx_len", "hidden", "inter", "n_heads",
+                                              "n_kv_heads", "r", "n_layers", "vocab")] + \
+               [(n, ctypes.c_float) for n in ("rms_eps", "rope_theta", "lora_scale", "temperature")]
 
 
 class UnoError(RuntimeError):
@@ -90,6 +98,9 @@ def _declare(lib):
         "uno_decoder_layer": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                              ctypes.POINTER(LayerWeights), _p, _p, _f32, _f32, _f32,
                                              _p, _p, _sz]),
+        "uno_psi_spec_step_workspace": (ctypes.c_int, [ctypes.POINTER(StepConfig), ctypes.POINTER(_sz)]),
+        "uno_psi_spec_step": (ctypes.c_int, [_p, ctypes.POINTER(StepConfig), ctypes.POINTER(LayerWeights),
+                                             _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz]),
         "uno_profile_enable": (None, [ctypes.c_int, ctypes.c_char_p]),
         "uno_profile_reset": (None, []),
         "uno_profile_query": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
@@ -428,6 +439,49 @@ def decoder_layer(hidden_state, weights, gate, positions, batch, block, ctx, n_h
                                   ctypes.byref(weights), _ptr(gate), _ptr(positions), float(rms_eps),
                                   float(rope_theta), float(lora_scale), _ptr(hidden_state), _ptr(ws), _nbytes(ws)))
     return hidden_state
+
+
+# ------------------------------------------------------------------ decode step
+def step_config(batch, block, ctx_len, hidden, inter, n_heads, n_kv_heads, r, n_layers, vocab,
+                rms_eps=1e-6, rope_theta=1.0e6, lora_scale=1.0, temperature=1.0):
+    return StepConfig(batch, block, ctx_len, hidden, inter, n_heads, n_kv_heads, r, n_layers, vocab,
+                      rms_eps, rope_theta, lora_scale, temperature)
+
+
+def psi_spec_step_workspace(cfg):
+    load()
+    out = _sz(0)
+    _check(_lib.uno_psi_spec_step_workspace(ctypes.byref(cfg), ctypes.byref(out)))
+    return out.value
+
+
+def psi_spec_step(cfg, layers, embed, final_norm, lm_head, tokens, u_draft, u_accept, u_sample,
+                  logits=None, workspace=None, stream=None):
+    """One decode step (uno_psi_spec_step).
+
+    cfg: StepConfig; layers: sequence of LayerWeights (one per layer);
+    embed, lm_head bf16 [vocab, hidden]; final_norm bf16 [hidden];
+    tokens int32 [batch, 2*block]; u_draft, u_accept f32 [batch, block-1];
+    u_sample f32 [batch].  Returns a dict of device tensors: logits
+    [batch*2*block, vocab] bf16, drafts [batch, block-1], accept_len and token [batch].
+    """
+    import torch
+    load()
+    dev = tokens.device
+    rows = cfg.batch * 2 * cfg.block
+    k = cfg.block - 1
+    if logits is None:
+        logits = torch.empty((rows, cfg.vocab), dtype=torch.bfloat16, device=dev)
+    drafts = torch.empty((cfg.batch, max(k, 0)), dtype=torch.int32, device=dev)
+    acc = torch.empty(cfg.batch, dtype=torch.int32, device=dev)
+    tok = torch.empty(cfg.batch, dtype=torch.int32, device=dev)
+    arr = (LayerWeights * max(len(layers), 1))(*layers)
+    ws = _workspace(psi_spec_step_workspace(cfg), dev, workspace)
+    _check(_lib.uno_psi_spec_step(_stream(stream), ctypes.byref(cfg), arr, _ptr(embed), _ptr(final_norm),
+                                  _ptr(lm_head), _ptr(tokens), _ptr(u_draft), _ptr(u_accept), _ptr(u_sample),
+                                  _ptr(logits), _ptr(drafts) if k > 0 else None, _ptr(acc), _ptr(tok),
+                                  _ptr(ws), _nbytes(ws)))
+    return {"logits": logits, "drafts": drafts, "accept_len": acc, "token": tok}
 
 
 # ------------------------------------------------------------------ kernel timing

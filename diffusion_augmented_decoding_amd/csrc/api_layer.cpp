@@ -26,14 +26,18 @@ uno_status check_block_attn(int32_t batch, int32_t block, int32_t ctx, int32_t n
   return UNO_OK;
 }
 
+}  // namespace
+
+namespace uno {
+
 // Workspace layout of one decoder layer.
 struct LayerWs {
   size_t a, q, k, v, att, o, g, u, lora, attn, total;
 };
 
-size_t up256(size_t b) { return align_up(b, 256); }
+static size_t up256(size_t b) { return align_up(b, 256); }
 
-LayerWs layer_ws(int batch, int block, int ctx, int hidden, int inter, int nh, int nkv, int r) {
+static LayerWs layer_ws(int batch, int block, int ctx, int hidden, int inter, int nh, int nkv, int r) {
   const size_t rows = size_t(batch) * 2 * block;
   const int qd = nh * kHeadDim, kvd = nkv * kHeadDim;
   LayerWs w{};
@@ -62,7 +66,128 @@ LayerWs layer_ws(int batch, int block, int ctx, int hidden, int inter, int nh, i
   return w;
 }
 
-}  // namespace
+size_t decoder_layer_workspace_bytes(int batch, int block, int ctx, int hidden, int inter, int nh, int nkv, int r) {
+  return layer_ws(batch, block, ctx, hidden, inter, nh, nkv, r).total;
+}
+
+// One pre-norm decoder layer on the residual stream d.h, in place:
+//   a = rmsnorm(h); q, k, v = gated_lora(a); rope(q), rope(k);
+//   att = block_attention(q, cache + (k, v)); h += gated_lora(att, o);
+//   a = rmsnorm(h); h += gated_lora(silu(gated_lora(a, gate)) * gated_lora(a, up), down)
+hipError_t launch_decoder_layer(const DecoderLayerArgs& d, hipStream_t stream) {
+  const LayerWs L = layer_ws(d.batch, d.block, d.ctx, d.hidden, d.inter, d.n_heads, d.n_kv, d.r);
+  char* ws = static_cast<char*>(d.ws);
+  const int64_t rows = int64_t(d.batch) * 2 * d.block;
+  const int qd = d.n_heads * kHeadDim, kvd = d.n_kv * kHeadDim;
+  void* a = ws + L.a;
+  void* q = ws + L.q;
+  void* k = ws + L.k;
+  void* v = ws + L.v;
+  void* att = ws + L.att;
+  void* o = ws + L.o;
+  void* g = ws + L.g;
+  void* u = ws + L.u;
+  void* h = d.h;
+
+  auto proj = [&](int p, const void* x, int64_t K, int64_t N, void* y) {
+    GatedLoraArgs ga{};
+    ga.dtype = UNO_BF16;
+    ga.M = rows;
+    ga.N = N;
+    ga.K = K;
+    ga.r = (d.gate && d.r > 0) ? d.r : 0;
+    ga.x = x;
+    ga.ldx = K;
+    ga.w = d.w->w[p];
+    ga.ldw = K;
+    ga.a = d.w->a[p];
+    ga.lda = K;
+    ga.b = d.w->b[p];
+    ga.ldb = d.r;
+    ga.gate = d.gate;
+    ga.lora_scale = d.lora_scale;
+    ga.y = y;
+    ga.ldy = N;
+    ga.ws = ws + L.lora;
+    ga.ws_bytes = d.ws_bytes - L.lora;
+    return launch_gated_lora(ga, stream);
+  };
+  auto norm = [&](const void* res, const void* weight, void* out) {
+    RmsNormArgs na{};
+    na.rows = rows;
+    na.dim = d.hidden;
+    na.x = h;
+    na.ldx = d.hidden;
+    na.res = res;
+    na.ldr = d.hidden;
+    na.sum_out = res ? h : nullptr;
+    na.lds = d.hidden;
+    na.weight = weight;
+    na.eps = d.rms_eps;
+    na.out = out;
+    na.ldo = d.hidden;
+    return launch_rms_norm(na, stream);
+  };
+  auto rope = [&](void* x, int heads) {
+    RopeArgs ra{};
+    ra.rows = rows;
+    ra.n_heads = heads;
+    ra.x = x;
+    ra.ldx = int64_t(heads) * kHeadDim;
+    ra.positions = d.positions;
+    ra.theta = d.rope_theta;
+    return launch_rope(ra, stream);
+  };
+
+  hipError_t e = norm(nullptr, d.w->attn_norm, a);
+  if (e == hipSuccess) e = proj(UNO_PROJ_Q, a, d.hidden, qd, q);
+  if (e == hipSuccess) e = proj(UNO_PROJ_K, a, d.hidden, kvd, k);
+  if (e == hipSuccess) e = proj(UNO_PROJ_V, a, d.hidden, kvd, v);
+  if (e == hipSuccess) e = rope(q, d.n_heads);
+  if (e == hipSuccess) e = rope(k, d.n_kv);
+  if (e == hipSuccess) {
+    TreeAttnArgs ta{};
+    ta.batch = d.batch;
+    ta.n_tree = 2 * d.block;
+    ta.block = d.block;
+    ta.ctx = d.ctx;
+    ta.n_heads = d.n_heads;
+    ta.n_kv = d.n_kv;
+    ta.head_dim = kHeadDim;
+    ta.q = q;
+    ta.k_cache = d.w->k_cache;
+    ta.v_cache = d.w->v_cache;
+    ta.k_tree = k;
+    ta.v_tree = v;
+    ta.scale = 1.f / std::sqrt(float(kHeadDim));
+    ta.out = att;
+    ta.out_lse = nullptr;
+    ta.ws = ws + L.attn;
+    ta.ws_bytes = d.ws_bytes - L.attn;
+    e = launch_tree_attention(ta, stream);
+  }
+  if (e == hipSuccess) e = proj(UNO_PROJ_O, att, qd, d.hidden, o);
+  if (e == hipSuccess) e = norm(o, d.w->mlp_norm, a);                 // h += o; a = rmsnorm(h)
+  if (e == hipSuccess) e = proj(UNO_PROJ_GATE, a, d.hidden, d.inter, g);
+  if (e == hipSuccess) e = proj(UNO_PROJ_UP, a, d.hidden, d.inter, u);
+  if (e == hipSuccess) {
+    SiluMulArgs sa{};
+    sa.rows = rows;
+    sa.dim = d.inter;
+    sa.g = g;
+    sa.ldg = d.inter;
+    sa.u = u;
+    sa.ldu = d.inter;
+    sa.out = g;
+    sa.ldo = d.inter;
+    e = launch_silu_mul(sa, stream);
+  }
+  if (e == hipSuccess) e = proj(UNO_PROJ_DOWN, g, d.inter, d.hidden, o);
+  if (e == hipSuccess) e = norm(o, d.w->attn_norm, nullptr);         // h += down
+  return e;
+}
+
+}  // namespace uno
 
 extern "C" {
 
@@ -230,6 +355,8 @@ uno_status uno_sample_rows(hipStream_t stream, uno_dtype logit_dtype, int32_t ro
   a.vocab = vocab;
   a.logits = logits;
   a.row_stride = row_stride;
+  a.per_seq = rows;
+  a.seq_stride = 0;
   a.u = u;
   a.scale_log2 = 1.4426950408889634f / temperature;
   a.out_tok = out_token;
@@ -257,7 +384,7 @@ uno_status uno_decoder_layer_workspace(int32_t batch, int32_t block, int32_t ctx
   if (!bytes) return fail(UNO_ERR_INVALID_ARGUMENT, "bytes is NULL");
   uno_status s = check_layer(batch, block, ctx_len, hidden, inter, n_heads, n_kv_heads, r);
   if (s != UNO_OK) return s;
-  *bytes = layer_ws(batch, block, ctx_len, hidden, inter, n_heads, n_kv_heads, r).total;
+  *bytes = decoder_layer_workspace_bytes(batch, block, ctx_len, hidden, inter, n_heads, n_kv_heads, r);
   return UNO_OK;
   UNO_GUARD_END
 }
@@ -284,118 +411,29 @@ uno_status uno_decoder_layer(hipStream_t stream, int32_t batch, int32_t block, i
   if (!(rms_eps >= 0.f) || !std::isfinite(rms_eps) || !(rope_theta > 1.f) || !std::isfinite(rope_theta) ||
       !std::isfinite(lora_scale))
     return fail(UNO_ERR_INVALID_ARGUMENT, "rms_eps >= 0, rope_theta > 1 and a finite lora_scale required");
-  const LayerWs L = layer_ws(batch, block, ctx_len, hidden, inter, n_heads, n_kv_heads, r);
-  if (workspace_bytes < L.total || !workspace)
-    return fail(UNO_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, L.total);
+  const size_t need = decoder_layer_workspace_bytes(batch, block, ctx_len, hidden, inter, n_heads, n_kv_heads, r);
+  if (workspace_bytes < need || !workspace)
+    return fail(UNO_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
 
-  char* ws = static_cast<char*>(workspace);
-  const int64_t rows = int64_t(batch) * 2 * block;
-  const int qd = n_heads * kHeadDim, kvd = n_kv_heads * kHeadDim;
-  void* a = ws + L.a;
-  void* q = ws + L.q;
-  void* k = ws + L.k;
-  void* v = ws + L.v;
-  void* att = ws + L.att;
-  void* o = ws + L.o;
-  void* g = ws + L.g;
-  void* u = ws + L.u;
-  void* h = hidden_state;
-
-  auto proj = [&](int p, const void* x, int64_t K, int64_t N, void* y) {
-    GatedLoraArgs ga{};
-    ga.dtype = UNO_BF16;
-    ga.M = rows;
-    ga.N = N;
-    ga.K = K;
-    ga.r = (gate && r > 0) ? r : 0;
-    ga.x = x;
-    ga.ldx = K;
-    ga.w = wt->w[p];
-    ga.ldw = K;
-    ga.a = wt->a[p];
-    ga.lda = K;
-    ga.b = wt->b[p];
-    ga.ldb = r;
-    ga.gate = gate;
-    ga.lora_scale = lora_scale;
-    ga.y = y;
-    ga.ldy = N;
-    ga.ws = ws + L.lora;
-    ga.ws_bytes = workspace_bytes - L.lora;
-    return launch_gated_lora(ga, stream);
-  };
-  auto norm = [&](const void* res, const void* weight, void* out) {
-    RmsNormArgs na{};
-    na.rows = rows;
-    na.dim = hidden;
-    na.x = h;
-    na.ldx = hidden;
-    na.res = res;
-    na.ldr = hidden;
-    na.sum_out = res ? h : nullptr;
-    na.lds = hidden;
-    na.weight = weight;
-    na.eps = rms_eps;
-    na.out = out;
-    na.ldo = hidden;
-    return launch_rms_norm(na, stream);
-  };
-  auto rope = [&](void* x, int heads) {
-    RopeArgs ra{};
-    ra.rows = rows;
-    ra.n_heads = heads;
-    ra.x = x;
-    ra.ldx = int64_t(heads) * kHeadDim;
-    ra.positions = positions;
-    ra.theta = rope_theta;
-    return launch_rope(ra, stream);
-  };
-
-  hipError_t e = norm(nullptr, wt->attn_norm, a);
-  if (e == hipSuccess) e = proj(UNO_PROJ_Q, a, hidden, qd, q);
-  if (e == hipSuccess) e = proj(UNO_PROJ_K, a, hidden, kvd, k);
-  if (e == hipSuccess) e = proj(UNO_PROJ_V, a, hidden, kvd, v);
-  if (e == hipSuccess) e = rope(q, n_heads);
-  if (e == hipSuccess) e = rope(k, n_kv_heads);
-  if (e == hipSuccess) {
-    TreeAttnArgs ta{};
-    ta.batch = batch;
-    ta.n_tree = 2 * block;
-    ta.block = block;
-    ta.ctx = ctx_len;
-    ta.n_heads = n_heads;
-    ta.n_kv = n_kv_heads;
-    ta.head_dim = kHeadDim;
-    ta.q = q;
-    ta.k_cache = wt->k_cache;
-    ta.v_cache = wt->v_cache;
-    ta.k_tree = k;
-    ta.v_tree = v;
-    ta.scale = 1.f / std::sqrt(float(kHeadDim));
-    ta.out = att;
-    ta.out_lse = nullptr;
-    ta.ws = ws + L.attn;
-    ta.ws_bytes = workspace_bytes - L.attn;
-    e = launch_tree_attention(ta, stream);
-  }
-  if (e == hipSuccess) e = proj(UNO_PROJ_O, att, qd, hidden, o);
-  if (e == hipSuccess) e = norm(o, wt->mlp_norm, a);                 // h += o; a = rmsnorm(h)
-  if (e == hipSuccess) e = proj(UNO_PROJ_GATE, a, hidden, inter, g);
-  if (e == hipSuccess) e = proj(UNO_PROJ_UP, a, hidden, inter, u);
-  if (e == hipSuccess) {
-    SiluMulArgs sa{};
-    sa.rows = rows;
-    sa.dim = inter;
-    sa.g = g;
-    sa.ldg = inter;
-    sa.u = u;
-    sa.ldu = inter;
-    sa.out = g;
-    sa.ldo = inter;
-    e = launch_silu_mul(sa, stream);
-  }
-  if (e == hipSuccess) e = proj(UNO_PROJ_DOWN, g, inter, hidden, o);
-  if (e == hipSuccess) e = norm(o, wt->attn_norm, nullptr);         // h += down
+  DecoderLayerArgs la{};
+  la.batch = batch;
+  la.block = block;
+  la.ctx = ctx_len;
+  la.hidden = hidden;
+  la.inter = inter;
+  la.n_heads = n_heads;
+  la.n_kv = n_kv_heads;
+  la.r = r;
+  la.w = wt;
+  la.gate = gate;
+  la.positions = positions;
+  la.rms_eps = rms_eps;
+  la.rope_theta = rope_theta;
+  la.lora_scale = lora_scale;
+  la.h = hidden_state;
+  la.ws = workspace;
+  la.ws_bytes = workspace_bytes;
+  const hipError_t e = launch_decoder_layer(la, stream);
   return check_hip(e, "uno_decoder_layer launch");
   UNO_GUARD_END
 }

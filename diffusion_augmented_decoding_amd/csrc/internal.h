@@ -118,6 +118,7 @@ struct SampleRowsArgs {
   uno_dtype dtype;
   int rows, vocab;
   const void* logits; int64_t row_stride;
+  int per_seq; int64_t seq_stride;   // row i at (i / per_seq) * seq_stride + (i % per_seq) * row_stride
   const float* u;
   float scale_log2;   // log2(e) / T
   int32_t* out_tok;
@@ -157,5 +158,33 @@ struct SiluMulArgs {
   void* out; int64_t ldo;
 };
 hipError_t launch_silu_mul(const SiluMulArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- decoder layer
+struct DecoderLayerArgs {
+  int batch, block, ctx, hidden, inter, n_heads, n_kv, r;
+  const uno_layer_weights* w;
+  const uint8_t* gate;               // [rows]; null: adapter off everywhere
+  const int32_t* positions;          // [rows]
+  float rms_eps, rope_theta, lora_scale;
+  void* h;                           // bf16 [rows][hidden], updated in place
+  void* ws; size_t ws_bytes;
+};
+size_t decoder_layer_workspace_bytes(int batch, int block, int ctx, int hidden, int inter, int nh, int nkv, int r);
+hipError_t launch_decoder_layer(const DecoderLayerArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- step set-up
+// Row j of sequence b (rows of a sequence: block clean, then block noisy):
+// h[row] = embed[tokens[row]] (a zero row for an id outside [0, vocab)),
+// gate[row] = (j >= block), positions[row] = ctx + j % block.
+struct StepSetupArgs {
+  int64_t rows;
+  int block, ctx, hidden, vocab;
+  const int32_t* tokens;
+  const void* embed;                 // bf16 [vocab][hidden]
+  void* h;                           // bf16 [rows][hidden]
+  uint8_t* gate;
+  int32_t* positions;
+};
+hipError_t launch_step_setup(const StepSetupArgs& a, hipStream_t stream);
 
 }  // namespace uno

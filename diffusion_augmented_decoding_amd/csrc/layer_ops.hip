@@ -145,3 +145,34 @@ hipError_t launch_silu_mul(const SiluMulArgs& a, hipStream_t stream) {
 }
 
 }  // namespace uno
+
+namespace uno {
+
+namespace {
+
+// One workgroup per row: the embedding row copied in 16-byte vectors, the
+// row's gate and position written by thread 0.
+__global__ __launch_bounds__(256) void step_setup_kernel(StepSetupArgs a) {
+  const int64_t row = blockIdx.x;
+  const int j = int(row % (2 * a.block));
+  const int tok = a.tokens[row];
+  const bool ok = tok >= 0 && tok < a.vocab;
+  const int nvec = a.hidden / 8;
+  const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.embed) + int64_t(ok ? tok : 0) * a.hidden);
+  u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.h) + row * a.hidden);
+  for (int i = threadIdx.x; i < nvec; i += 256) dst[i] = ok ? src[i] : u32x4{0u, 0u, 0u, 0u};
+  if (threadIdx.x == 0) {
+    a.gate[row] = j >= a.block ? 1 : 0;
+    a.positions[row] = a.ctx + j % a.block;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_step_setup(const StepSetupArgs& a, hipStream_t stream) {
+  ProfileScope ps("uno_step_setup", stream);
+  hipLaunchKernelGGL(step_setup_kernel, dim3(unsigned(a.rows)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace uno

@@ -194,10 +194,17 @@ SrWs sr_ws(void* base, int rows, int vocab) {
   return w;
 }
 
+// row i of the call: sequence i / per_seq, row i % per_seq of that sequence
+template <typename T>
+__device__ __forceinline__ const T* sr_row(const SampleRowsArgs& a, int row) {
+  const int s = row / a.per_seq, j = row - s * a.per_seq;
+  return static_cast<const T*>(a.logits) + int64_t(s) * a.seq_stride + int64_t(j) * a.row_stride;
+}
+
 template <typename T>
 __global__ __launch_bounds__(kChunkThreads) void sr_stats_kernel(SampleRowsArgs a, SrWs w) {
   const int row = blockIdx.x, c = blockIdx.y, ns = gridDim.y;
-  const T* base = static_cast<const T*>(a.logits) + int64_t(row) * a.row_stride;
+  const T* base = sr_row<T>(a, row);
   const int span = split_span(a.vocab, ns);
   const int lo = c * span, hi = min(a.vocab, lo + span);
   const float2 r = range_stats<T>(base, lo, hi, a.scale_log2);
@@ -211,7 +218,7 @@ __global__ __launch_bounds__(kWave) void sr_desc_kernel(SampleRowsArgs a, SrWs w
   const RowStat st = wave_merge_chunks(w.part + int64_t(row) * ns, ns);
   if (threadIdx.x == 0) {
     DrawDesc d;
-    d.prow = static_cast<const T*>(a.logits) + int64_t(row) * a.row_stride;
+    d.prow = sr_row<T>(a, row);
     d.qrow = d.prow;
     d.mp = st.m;
     d.inv_sp = 1.f / st.s;

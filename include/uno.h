@@ -309,6 +309,50 @@ uno_status uno_decoder_layer(hipStream_t stream, int32_t batch, int32_t block, i
                              float rms_eps, float rope_theta, float lora_scale,
                              void* hidden_state, void* workspace, size_t workspace_bytes);
 
+/* One whole Psi-Spec decode step.  Source: Uno summary (hyper.ai), section
+ * 方法 (the diffusion path proposes a block, the AR path verifies it by
+ * rejection sampling and keeps the longest valid prefix; the linear sampler
+ * draws one candidate from the marginals; one forward pass runs over the
+ * concatenated clean and noisy rows with the adapter gated per row) and
+ * section 实验 (Qwen3-8B base, rank-128 adapters, shared KV cache).
+ *
+ * Per sequence b the step takes 2*block token ids: `block` clean ids (the
+ * AR token, then k = block - 1 drafts) and `block` noisy ids.  It runs
+ *   h = embed[tokens]; gate = 0 on clean rows, 1 on noisy rows;
+ *   positions: clean row j and noisy row j at ctx_len + j;
+ *   n_layers x uno_decoder_layer (layer l uses layers[l], its KV cache holds
+ *     ctx_len positions per sequence; the block is not written to it);
+ *   logits = rmsnorm(h, final_norm) . lm_head^T     (bf16 [rows][vocab], no adapter);
+ *   drafts[b][i] = inverse-CDF draw from softmax(noisy row i / T) at u_draft[b][i], i < k
+ *     (the uno_sample_rows rule);
+ *   uno_psi_spec_verify_linear with p = the k + 1 clean rows and q = the first k
+ *     noisy rows of the same logits, on the drafts just drawn.
+ * Reading: the pages leave open which forward's q a draft is verified against;
+ * here the drafts a step verifies are drawn from that step's own noisy rows,
+ * which is the same work per step as carrying them over from the previous
+ * step (one draw of k rows, one verify of 2k + 1 rows per sequence).
+ *
+ * layers: host array of n_layers uno_layer_weights (device pointers); embed and
+ * lm_head bf16 [vocab][hidden]; final_norm bf16 [hidden]; tokens int32
+ * [batch][2*block]; u_draft, u_accept f32 [batch][k]; u_sample f32 [batch];
+ * logits (output, caller-owned) bf16 [batch*2*block][vocab]; out_drafts int32
+ * [batch][k]; out_accept_len, out_token int32 [batch].  1 <= block <= 65,
+ * head_dim 128, hidden and inter multiples of 8, r a multiple of 8 (0: no
+ * adapter).  A token id outside [0, vocab) embeds as a zero row. */
+typedef struct {
+  int32_t batch, block, ctx_len;
+  int32_t hidden, inter, n_heads, n_kv_heads, r, n_layers, vocab;
+  float rms_eps, rope_theta, lora_scale, temperature;
+} uno_step_config;
+
+uno_status uno_psi_spec_step_workspace(const uno_step_config* config, size_t* bytes);
+uno_status uno_psi_spec_step(hipStream_t stream, const uno_step_config* config, const uno_layer_weights* layers,
+                             const void* embed, const void* final_norm, const void* lm_head,
+                             const int32_t* tokens, const float* u_draft, const float* u_accept,
+                             const float* u_sample, void* logits, int32_t* out_drafts,
+                             int32_t* out_accept_len, int32_t* out_token,
+                             void* workspace, size_t workspace_bytes);
+
 /* --------------------------------------------------------------------------
  * Kernel timing (measurement support, not part of the method).
  * When enabled, every kernel the library launches whose name contains

@@ -41,6 +41,7 @@ from .decoder import (
     decoder_layer,
     lm_head,
 )
+from .step import step_rows, decode_step
 
 __all__ = [
     "gated_lora_linear",
@@ -64,4 +65,6 @@ __all__ = [
     "silu_mul",
     "decoder_layer",
     "lm_head",
+    "step_rows",
+    "decode_step",
 ]

@@ -289,3 +289,44 @@ def test_decoder_layer_rejects_bad_calls(lib):
     lw.w[3] = None
     assert lib.uno_decoder_layer(None, 2, 4, 8, 256, 512, 4, 2, 8, ctypes.byref(lw), FAKE16, FAKE16, 1e-6, 1e6,
                                  1.0, FAKE16, FAKE16, 1 << 30) == INVALID
+
+
+def test_step_rejects_bad_calls(lib):
+    cfg_t = lib.uno_psi_spec_step.argtypes[1]._type_
+    lw_t = lib.uno_psi_spec_step.argtypes[2]._type_
+
+    def cfg(**kw):
+        a = dict(batch=128, block=16, ctx_len=8192, hidden=4096, inter=12288, n_heads=32, n_kv_heads=8, r=128,
+                 n_layers=36, vocab=151936, rms_eps=1e-6, rope_theta=1e6, lora_scale=1.0, temperature=1.0)
+        a.update(kw)
+        return cfg_t(*a.values())
+    ws = ctypes.c_size_t(0)
+    assert lib.uno_psi_spec_step_workspace(ctypes.byref(cfg()), ctypes.byref(ws)) == OK
+    assert ws.value >= 2 * 4096 * 4096 * 2
+    for bad, code in ((dict(block=66), UNSUPPORTED), (dict(batch=0), INVALID), (dict(n_heads=30), INVALID),
+                      (dict(vocab=(1 << 20) + 1), UNSUPPORTED), (dict(r=4), UNSUPPORTED),
+                      (dict(temperature=0.0), INVALID), (dict(hidden=4100), UNSUPPORTED),
+                      (dict(batch=8192, block=9), UNSUPPORTED)):
+        assert lib.uno_psi_spec_step_workspace(ctypes.byref(cfg(**bad)), ctypes.byref(ws)) == code, bad
+    assert lib.uno_psi_spec_step_workspace(None, ctypes.byref(ws)) == INVALID
+    layers = (lw_t * 2)()
+
+    def call(c, lay=layers, ws_bytes=1 << 40, **kw):
+        a = dict(embed=FAKE16, fnorm=FAKE16, lm=FAKE16, tok=FAKE16, ud=FAKE16, ua=FAKE16, us=FAKE16, logits=FAKE16,
+                 drafts=FAKE16, L=FAKE16, y=FAKE16)
+        a.update(kw)
+        return lib.uno_psi_spec_step(None, ctypes.byref(c), lay, a["embed"], a["fnorm"], a["lm"], a["tok"], a["ud"],
+                                     a["ua"], a["us"], a["logits"], a["drafts"], a["L"], a["y"], FAKE16, ws_bytes)
+    small = cfg(batch=2, block=4, ctx_len=8, hidden=256, inter=512, n_heads=4, n_kv_heads=2, r=8, n_layers=2,
+                vocab=1000)
+    assert call(small) == INVALID                          # layer weights are NULL
+    for l in range(2):
+        layers[l].attn_norm = layers[l].mlp_norm = layers[l].k_cache = layers[l].v_cache = FAKE16.value
+        for i in range(7):
+            layers[l].w[i] = layers[l].a[i] = layers[l].b[i] = FAKE16.value
+    assert call(small, embed=None) == INVALID
+    assert call(small, ud=None) == INVALID
+    assert call(small, lm=ctypes.c_void_p(0x10008)) == UNSUPPORTED
+    assert call(small, ws_bytes=64) == WORKSPACE
+    layers[1].b[6] = None
+    assert call(small) == INVALID

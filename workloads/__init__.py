@@ -418,3 +418,35 @@ def rows_case(rows, vocab, dtype="bf16", seed=0, std=2.0):
     st, val = _store(x, dtype)
     u = rng_for(seed, _T_ROWS_U).random(rows, dtype=np.float32)
     return {"logits": st, "logits_f32": val, "u": u}
+
+
+# ------------------------------------------------------------ decode step
+_T_EMBED, _T_LMHEAD, _T_FNORM, _T_TOK, _T_UDRAFT, _T_UACC2, _T_US2 = 71, 72, 73, 74, 75, 76, 77
+
+
+def step_case(batch, block, ctx, hidden, inter, n_heads, n_kv_heads, r, n_layers, vocab, seed=0,
+              weight_std=0.02, embed_std=1.0, norm_std=0.1):
+    """Inputs of one decode step: embedding and LM-head tables [vocab, hidden]
+    (embedding ~ N(0, embed_std^2), LM head ~ N(0, weight_std^2)), final norm
+    weights, n_layers layers (layer_weights_case) with their KV caches
+    (kv_cache_case), token ids [batch, 2*block] uniform over the vocabulary,
+    and the uniforms u_draft, u_accept [batch, block-1], u_sample [batch].
+    All tables are bf16 bits; the values are the bf16 values."""
+    k = block - 1
+    emb = rng_for(seed, _T_EMBED).standard_normal((vocab, hidden), dtype=np.float32) * np.float32(embed_std)
+    lm = rng_for(seed, _T_LMHEAD).standard_normal((vocab, hidden), dtype=np.float32) * np.float32(weight_std)
+    fn = 1.0 + rng_for(seed, _T_FNORM).standard_normal(hidden, dtype=np.float32) * np.float32(norm_std)
+    layers, kcs, vcs = [], [], []
+    for l in range(n_layers):
+        layers.append(layer_weights_case(hidden, inter, n_heads, n_kv_heads, r, seed, l, weight_std, norm_std))
+        kc, vc = kv_cache_case(batch, ctx, n_kv_heads, seed, l)
+        kcs.append(kc)
+        vcs.append(vc)
+    return {"batch": batch, "block": block, "ctx": ctx, "hidden": hidden, "inter": inter, "n_heads": n_heads,
+            "n_kv_heads": n_kv_heads, "r": r, "n_layers": n_layers, "vocab": vocab,
+            "embed": bf16_bits(emb), "lm_head": bf16_bits(lm), "final_norm": bf16_bits(fn),
+            "layers": layers, "k_caches": kcs, "v_caches": vcs,
+            "tokens": rng_for(seed, _T_TOK).integers(0, vocab, size=(batch, 2 * block)).astype(np.int32),
+            "u_draft": rng_for(seed, _T_UDRAFT).random((batch, k), dtype=np.float32),
+            "u_accept": rng_for(seed, _T_UACC2).random((batch, k), dtype=np.float32),
+            "u_sample": rng_for(seed, _T_US2).random(batch, dtype=np.float32)}
