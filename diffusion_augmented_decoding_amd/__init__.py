@@ -456,14 +456,15 @@ def psi_spec_step_workspace(cfg):
 
 
 def psi_spec_step(cfg, layers, embed, final_norm, lm_head, tokens, u_draft, u_accept, u_sample,
-                  logits=None, workspace=None, stream=None):
+                  logits=None, outputs=None, workspace=None, stream=None):
     """One decode step (uno_psi_spec_step).
 
-    cfg: StepConfig; layers: sequence of LayerWeights (one per layer);
+    cfg: StepConfig; layers: sequence (or ctypes array) of LayerWeights, one per layer;
     embed, lm_head bf16 [vocab, hidden]; final_norm bf16 [hidden];
     tokens int32 [batch, 2*block]; u_draft, u_accept f32 [batch, block-1];
     u_sample f32 [batch].  Returns a dict of device tensors: logits
-    [batch*2*block, vocab] bf16, drafts [batch, block-1], accept_len and token [batch].
+    [batch*2*block, vocab] bf16, drafts [batch, block-1], accept_len and token
+    [batch] (`outputs`, if given, is such a dict to write into).
     """
     import torch
     load()
@@ -472,16 +473,23 @@ def psi_spec_step(cfg, layers, embed, final_norm, lm_head, tokens, u_draft, u_ac
     k = cfg.block - 1
     if logits is None:
         logits = torch.empty((rows, cfg.vocab), dtype=torch.bfloat16, device=dev)
-    drafts = torch.empty((cfg.batch, max(k, 0)), dtype=torch.int32, device=dev)
-    acc = torch.empty(cfg.batch, dtype=torch.int32, device=dev)
-    tok = torch.empty(cfg.batch, dtype=torch.int32, device=dev)
-    arr = (LayerWeights * max(len(layers), 1))(*layers)
+    if outputs is None:
+        outputs = {"drafts": torch.empty((cfg.batch, max(k, 0)), dtype=torch.int32, device=dev),
+                   "accept_len": torch.empty(cfg.batch, dtype=torch.int32, device=dev),
+                   "token": torch.empty(cfg.batch, dtype=torch.int32, device=dev)}
+    drafts, acc, tok = outputs["drafts"], outputs["accept_len"], outputs["token"]
+    arr = layers if isinstance(layers, ctypes.Array) else (LayerWeights * max(len(layers), 1))(*layers)
     ws = _workspace(psi_spec_step_workspace(cfg), dev, workspace)
     _check(_lib.uno_psi_spec_step(_stream(stream), ctypes.byref(cfg), arr, _ptr(embed), _ptr(final_norm),
                                   _ptr(lm_head), _ptr(tokens), _ptr(u_draft), _ptr(u_accept), _ptr(u_sample),
                                   _ptr(logits), _ptr(drafts) if k > 0 else None, _ptr(acc), _ptr(tok),
                                   _ptr(ws), _nbytes(ws)))
     return {"logits": logits, "drafts": drafts, "accept_len": acc, "token": tok}
+
+
+def layer_array(layers):
+    """A ctypes array of LayerWeights (reusable across psi_spec_step calls)."""
+    return (LayerWeights * max(len(layers), 1))(*layers)
 
 
 # ------------------------------------------------------------------ kernel timing

@@ -61,7 +61,7 @@ static LayerWs layer_ws(int batch, int block, int ctx, int hidden, int inter, in
   size_t lora = 0;
   for (const auto& s : shapes) lora = std::max(lora, gated_lora_workspace_bytes(UNO_BF16, M, s[0], s[1], r));
   w.lora = take(lora);
-  w.attn = take(tree_attention_workspace_bytes(batch, 2 * block, ctx, nh, nkv, kHeadDim));
+  w.attn = take(block_attention_workspace_bytes(batch, block, ctx, nh, nkv));
   w.total = off;
   return w;
 }
@@ -164,7 +164,7 @@ hipError_t launch_decoder_layer(const DecoderLayerArgs& d, hipStream_t stream) {
     ta.out_lse = nullptr;
     ta.ws = ws + L.attn;
     ta.ws_bytes = d.ws_bytes - L.attn;
-    e = launch_tree_attention(ta, stream);
+    e = launch_block_attention(ta, stream);
   }
   if (e == hipSuccess) e = proj(UNO_PROJ_O, att, qd, d.hidden, o);
   if (e == hipSuccess) e = norm(o, d.w->mlp_norm, a);                 // h += o; a = rmsnorm(h)
@@ -277,7 +277,7 @@ uno_status uno_block_verify_attention_workspace(int32_t batch, int32_t block, in
   if (!bytes) return fail(UNO_ERR_INVALID_ARGUMENT, "bytes is NULL");
   uno_status s = check_block_attn(batch, block, ctx_len, n_heads, n_kv_heads, head_dim);
   if (s != UNO_OK) return s;
-  *bytes = tree_attention_workspace_bytes(batch, 2 * block, ctx_len, n_heads, n_kv_heads, head_dim);
+  *bytes = block_attention_workspace_bytes(batch, block, ctx_len, n_heads, n_kv_heads);
   return UNO_OK;
   UNO_GUARD_END
 }
@@ -297,7 +297,7 @@ uno_status uno_block_verify_attention(hipStream_t stream, int32_t batch, int32_t
     return fail(UNO_ERR_UNSUPPORTED, "bf16 tensors must be 16-byte aligned");
   if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
     return fail(UNO_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
-  const size_t need = tree_attention_workspace_bytes(batch, 2 * block, ctx_len, n_heads, n_kv_heads, head_dim);
+  const size_t need = block_attention_workspace_bytes(batch, block, ctx_len, n_heads, n_kv_heads);
   if (workspace_bytes < need || (need > 0 && !workspace))
     return fail(UNO_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
   TreeAttnArgs a{};
@@ -319,7 +319,7 @@ uno_status uno_block_verify_attention(hipStream_t stream, int32_t batch, int32_t
   a.out_lse = out_lse;
   a.ws = workspace;
   a.ws_bytes = workspace_bytes;
-  return check_hip(launch_tree_attention(a, stream), "uno_block_verify_attention launch");
+  return check_hip(launch_block_attention(a, stream), "uno_block_verify_attention launch");
   UNO_GUARD_END
 }
 

@@ -94,6 +94,18 @@ struct TreeAttnArgs {
 size_t tree_attention_workspace_bytes(int batch, int n_tree, int ctx, int n_heads, int n_kv, int head_dim);
 hipError_t launch_tree_attention(const TreeAttnArgs& a, hipStream_t stream);
 
+// Split-key partials shared by the attention kernels: [batch * n_kv * ks
+// groups][tiles32 tiles][32 rows] x (unnormalised O[128] fp32), then the same
+// rows x (max in the log2 domain, sum); merged by launch_attn_combine.
+size_t attn_part_bytes(int batch, int n_kv, int tiles32, int ks);
+hipError_t launch_attn_combine(const TreeAttnArgs& a, int tiles32, int ks, void* ws, hipStream_t stream,
+                               const char* name);
+
+// Block-masked attention (a.block > 0, a.n_tree = 2 * a.block) over a long
+// cache: K/V blocks staged in LDS and shared by 128 query rows.
+size_t block_attention_workspace_bytes(int batch, int block, int ctx, int n_heads, int n_kv);
+hipError_t launch_block_attention(const TreeAttnArgs& a, hipStream_t stream);
+
 // ---------------------------------------------------------------- tree verify
 struct TreeVerifyArgs {
   uno_dtype dtype;

@@ -107,10 +107,6 @@ size_t part_bytes(const AttnPlan& p) {
   return align_up(rows * kHD * sizeof(float), 256) + align_up(rows * sizeof(float2), 256);
 }
 
-// MASK 0: prefix tree (ancestors-or-self from the parent array);
-// MASK 1: block of a.block clean rows then as many noisy rows (clean row i
-// sees clean rows 0..i, a noisy row sees every row of the block).
-template <int MASK>
 __global__ __launch_bounds__(kThreads) void tree_attn_kernel(TreeAttnArgs a, AttnPlan pl, AttnPart part) {
   __shared__ uint64_t anc[kMaxNodes][4];
   __shared__ int sh_par[kMaxNodes];
@@ -166,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void tree_attn_kernel(TreeAttnArgs a, Att
 
   // ---- every global load of the set-up is issued first: parent ids, this
   // lane's query row, the first K/V block
-  const int par_i = (MASK == 0 && tid < n) ? a.parent[int64_t(b) * n + tid] : 0;   // n <= kThreads
+  const int par_i = tid < n ? a.parent[int64_t(b) * n + tid] : 0;   // n <= kThreads
   const int r = row0 + lrow;
   const bool row_ok = r < nrows;
   const int node = row_ok ? r / G : 0;
@@ -184,16 +180,7 @@ __global__ __launch_bounds__(kThreads) void tree_attn_kernel(TreeAttnArgs a, Att
   if (tid == 0) sh_bad = 0;
   if (tid < n) sh_par[tid] = par_i;
   __syncthreads();
-  if (MASK == 1 && tid < n) {
-    // visible block rows [0, lim)
-    const int lim = tid < a.block ? tid + 1 : n;
-#pragma unroll
-    for (int wd = 0; wd < 4; ++wd) {
-      const int nb_w = min(max(lim - 64 * wd, 0), 64);
-      anc[tid][wd] = nb_w == 64 ? ~uint64_t(0) : ((uint64_t(1) << nb_w) - 1);
-    }
-  }
-  if (MASK == 0 && tid < n) {
+  if (tid < n) {
     const int i = tid;
     uint64_t w[4] = {0, 0, 0, 0};
     int j = i, steps = 0;
@@ -450,6 +437,27 @@ __global__ __launch_bounds__(kCombineThreads) void tree_attn_combine_kernel(Tree
 
 }  // namespace
 
+size_t attn_part_bytes(int batch, int n_kv, int tiles32, int ks) {
+  AttnPlan pl{};
+  pl.tiles = tiles32;
+  pl.ks = ks;
+  pl.groups = batch * n_kv * ks;
+  return part_bytes(pl);
+}
+
+hipError_t launch_attn_combine(const TreeAttnArgs& a, int tiles32, int ks, void* ws, hipStream_t stream,
+                               const char* name) {
+  AttnPlan pl{};
+  pl.tiles = tiles32;
+  pl.ks = ks;
+  pl.groups = a.batch * a.n_kv * ks;
+  const AttnPart part = part_ws(ws, pl);
+  ProfileScope ps(name, stream);
+  hipLaunchKernelGGL(tree_attn_combine_kernel, dim3(tiles32 * 4, a.n_kv, a.batch), dim3(kCombineThreads), 0, stream,
+                     a, pl, part);
+  return hipGetLastError();
+}
+
 size_t tree_attention_workspace_bytes(int batch, int n_tree, int ctx, int n_heads, int n_kv, int) {
   return part_bytes(make_plan(batch, n_tree, ctx, n_heads, n_kv));
 }
@@ -461,16 +469,13 @@ hipError_t launch_tree_attention(const TreeAttnArgs& a, hipStream_t stream) {
   const int64_t nwg = padded_groups * pl.tiles;
   if (nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
   {
-    ProfileScope ps(a.block > 0 ? "uno_block_attention" : "uno_tree_attention", stream);
-    if (a.block > 0)
-      hipLaunchKernelGGL(tree_attn_kernel<1>, dim3(unsigned(nwg)), dim3(kThreads), 0, stream, a, pl, part);
-    else
-      hipLaunchKernelGGL(tree_attn_kernel<0>, dim3(unsigned(nwg)), dim3(kThreads), 0, stream, a, pl, part);
+    ProfileScope ps("uno_tree_attention", stream);
+    hipLaunchKernelGGL(tree_attn_kernel, dim3(unsigned(nwg)), dim3(kThreads), 0, stream, a, pl, part);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.ks == 1) return e;
   {
-    ProfileScope ps(a.block > 0 ? "uno_block_attention_combine" : "uno_tree_attention_combine", stream);
+    ProfileScope ps("uno_tree_attention_combine", stream);
     hipLaunchKernelGGL(tree_attn_combine_kernel, dim3(pl.tiles * 4, a.n_kv, a.batch), dim3(kCombineThreads), 0,
                        stream, a, pl, part);
   }
