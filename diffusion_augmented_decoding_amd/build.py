@@ -34,6 +34,14 @@ COMMON_FLAGS = [
 ]
 
 
+# per-file flags: the attention kernel keeps its MFMA accumulators in VGPRs
+# (gfx950 MFMAs take C/D from either file), which avoids copying them through
+# AGPRs around the softmax rescale
+FILE_FLAGS = {
+    "block_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _hipcc():
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -63,7 +71,7 @@ def build(verbose=False, jobs=None):
     for s in srcs:
         o = os.path.join(BUILD, os.path.basename(s) + ".o")
         objs.append(o)
-        cmds.append([hipcc] + COMMON_FLAGS + ["-c", s, "-o", o])
+        cmds.append([hipcc] + COMMON_FLAGS + FILE_FLAGS.get(os.path.basename(s), []) + ["-c", s, "-o", o])
     jobs = jobs or min(8, len(cmds))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))

@@ -37,6 +37,8 @@
 //                   d = lane's column from a row-major LDS tile (each 16-lane
 //                   group addresses a 4-key x 16-d patch, lane j at key j / 4,
 //                   d 4 (j % 4)), so no transposition pass is needed.
+#include <stdlib.h>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -49,7 +51,7 @@ constexpr int kKB = 32;                           // keys per block
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kRows = kWaves * 32;                // query rows per workgroup
-constexpr int kStages = 4;
+constexpr int kStagesDefault = 4;
 constexpr int kKBytes = kKB * kHD * 2;            // 8 KB of K per block
 constexpr int kStageBytes = 2 * kKBytes;          // K + V
 constexpr int kLpw = kStageBytes / 1024 / kWaves; // 1 KB load instructions per wave per stage
@@ -58,6 +60,7 @@ constexpr int kTargetWgs = 512;                   // 2 resident workgroups per C
 constexpr int kMinBlocksPerSplit = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.f;                      // log2 headroom of the lazily updated max
 
 static_assert(kLpw * kWaves * 1024 == kStageBytes, "a stage is a whole number of wave loads");
 
@@ -70,6 +73,13 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// two floats to packed bf16, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{lo, hi}, bf16x2v));
 }
 
 __host__ __device__ __forceinline__ int swz_v(int k) { return ((k & 1) ? 6 : 0) ^ ((k & 2) ? 10 : 0); }
@@ -144,6 +154,7 @@ __device__ __forceinline__ void read_vt(s16x4 (&t)[2][4], const uint32_t (&va)[2
   }
 }
 
+template <int kStages>
 __global__ __launch_bounds__(kThreads) void block_attn_kernel(TreeAttnArgs a, BlkPlan pl, float* part_o,
                                                               float2* part_ms) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -210,13 +221,27 @@ __global__ __launch_bounds__(kThreads) void block_attn_kernel(TreeAttnArgs a, Bl
     cbase[q] = v ? cache_v : cache_k;
     tbase[q] = v ? tree_v : tree_k;
   }
+  // running address of this lane's chunk in the next block to issue (cache rows)
+  uint64_t run[kLpw];
+#pragma unroll
+  for (int q = 0; q < kLpw; ++q) run[q] = cbase[q] + uint64_t(blk0 * kKB + krow[q]) * row_bytes + colb[q];
+  const uint64_t run_step = uint64_t(kKB) * row_bytes;
+  // blocks are issued in order blk0, blk0 + 1, ...
   auto issue = [&](int stage, int j) {
+    // wave-uniform cases: past the split (zero chunks), all cache keys, or the tail
+    const int mode = j >= blk_end ? 0 : ((j + 1) * kKB <= ctx ? 1 : 2);
 #pragma unroll
     for (int q = 0; q < kLpw; ++q) {
       const int key = j * kKB + krow[q];
-      const bool ok = (j < blk_end) & (key < nkeys);
-      uint64_t addr = key < ctx ? cbase[q] + uint64_t(key) * row_bytes : tbase[q] + uint64_t(key - ctx) * row_bytes;
-      addr = ok ? addr + colb[q] : zaddr;
+      uint64_t addr = zaddr;
+      if (mode == 1) {
+        addr = run[q];
+      } else if (mode == 2) {
+        const uint64_t at = key < ctx ? cbase[q] + uint64_t(key) * row_bytes
+                                      : tbase[q] + uint64_t(key - ctx) * row_bytes;
+        addr = key < nkeys ? at + colb[q] : zaddr;
+      }
+      run[q] += run_step;
       const uint32_t dst = lds_base + uint32_t(stage * kStageBytes + (q * kWaves + wave) * 1024);
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(addr),
                                        reinterpret_cast<__attribute__((address_space(3))) void*>(uintptr_t(dst)),
@@ -267,46 +292,64 @@ __global__ __launch_bounds__(kThreads) void block_attn_kernel(TreeAttnArgs a, Bl
 
     // scores: lane holds row lrow, keys 8 (e / 4) + 4 lh + e % 4 of the block
     const int kb = j * kKB;
-    float y[16];
-    float bmax = -INFINITY;
+    const bool full = kb + kKB <= ctx;   // every key of the block is a cache key: nothing is masked
+    uint32_t okm = 0xffffu;              // bit e: score e visible
+    float bmax;
+    if (full) {
+      float r = s[0];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int key = kb + 8 * (e >> 2) + 4 * lh + (e & 3);
-      // branch-free: cache keys always, block keys by the clean/noisy rule
-      const bool ok = (key < nkeys) & ((key < ctx) | (node >= blk) | (key - ctx <= node));
-      y[e] = ok ? s[e] * sc : -INFINITY;
-      bmax = fmaxf(bmax, y[e]);
-    }
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-    const float mn = fmaxf(m, bmax);
-    float alpha = 1.f, psum = 0.f;
-    if (mn == -INFINITY) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) y[e] = 0.f;
+      for (int e = 1; e < 16; ++e) r = fmaxf(r, s[e]);
+      bmax = r * sc;                     // sc > 0
     } else {
-      alpha = fexp2(m - mn);
+      okm = 0;
+      bmax = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        y[e] = fexp2(y[e] - mn);
+        const int key = kb + 8 * (e >> 2) + 4 * lh + (e & 3);
+        // cache keys always, block keys by the clean/noisy rule
+        const bool ok = (key < nkeys) & ((key < ctx) | (node >= blk) | (key - ctx <= node));
+        okm |= uint32_t(ok) << e;
+        bmax = ok ? fmaxf(bmax, s[e] * sc) : bmax;
+      }
+    }
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+    // Lazy rescaling: the running max m moves only when a score exceeds it by
+    // more than kLazy (log2 units), so P = 2^(y - m) <= 2^kLazy, and the
+    // accumulator is rescaled only in the rare blocks where some row's max moved.
+    const bool grow = bmax > m + kLazy;
+    if (__ballot(grow) != 0) {
+      const float mn = grow ? bmax : m;
+      const float alpha = grow ? fexp2(m - mn) : 1.f;   // m = -inf: alpha = 0
+      ssum *= alpha;
+#pragma unroll
+      for (int db = 0; db < kHD / 32; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+      m = mn;
+    }
+    const float nm = m == -INFINITY ? 0.f : -m;   // a row with nothing visible yet: P = 0
+    float y[16];
+    float psum = 0.f;
+    if (full) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        y[e] = fexp2(fmaf(s[e], sc, nm));
+        psum += y[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        y[e] = ((okm >> e) & 1u) ? fexp2(fmaf(s[e], sc, nm)) : 0.f;
         psum += y[e];
       }
     }
     psum += __shfl_xor(psum, 32);
-    ssum = ssum * alpha + psum;
-    m = mn;
+    ssum += psum;
     bf16x8 pf[2];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const uint32_t w0 = pack_bf16x2(y[8 * st + 0], y[8 * st + 1]);
-      const uint32_t w1 = pack_bf16x2(y[8 * st + 2], y[8 * st + 3]);
-      const uint32_t w2 = pack_bf16x2(y[8 * st + 4], y[8 * st + 5]);
-      const uint32_t w3 = pack_bf16x2(y[8 * st + 6], y[8 * st + 7]);
-      pf[st] = __builtin_bit_cast(bf16x8, u32x4{w0, w1, w2, w3});
-    }
-#pragma unroll
-    for (int db = 0; db < kHD / 32; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+    for (int st = 0; st < 2; ++st)
+      pf[st] = __builtin_bit_cast(bf16x8, u32x4{pk_bf16(y[8 * st + 0], y[8 * st + 1]), pk_bf16(y[8 * st + 2], y[8 * st + 3]),
+                                                pk_bf16(y[8 * st + 4], y[8 * st + 5]), pk_bf16(y[8 * st + 6], y[8 * st + 7])});
 
     // O^T += V^T . P^T; the A fragment of (db, st) is keys 16 st + 4 lh + 0..3
     // (P elements 0..3) and 16 st + 8 + 4 lh + 0..3 (elements 4..7) at d = 32 db + lrow
@@ -377,6 +420,21 @@ __global__ __launch_bounds__(kThreads) void block_attn_kernel(TreeAttnArgs a, Bl
   }
 }
 
+template <int S>
+hipError_t launch_stages(const TreeAttnArgs& a, const BlkPlan& pl, int64_t nwg, float* part_o, float2* part_ms,
+                         hipStream_t stream) {
+  const size_t lds = size_t(S) * kStageBytes;
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(block_attn_kernel<S>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  hipLaunchKernelGGL(block_attn_kernel<S>, dim3(unsigned(nwg)), dim3(kThreads), lds, stream, a, pl, part_o, part_ms);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t block_attention_workspace_bytes(int batch, int block, int ctx, int n_heads, int n_kv) {
@@ -398,12 +456,20 @@ hipError_t launch_block_attention(const TreeAttnArgs& a, hipStream_t stream) {
     part_o = static_cast<float*>(a.ws);
     part_ms = reinterpret_cast<float2*>(static_cast<char*>(a.ws) + align_up(rows * kHD * sizeof(float), 256));
   }
+  int stages = kStagesDefault;
+  {
+    const char* env = getenv("UNO_ATTN_STAGES");   // tuning override: 3..5
+    if (env && atoi(env) >= 3 && atoi(env) <= 5) stages = atoi(env);
+  }
+  hipError_t e = hipSuccess;
   {
     ProfileScope ps("uno_block_attention", stream);
-    hipLaunchKernelGGL(block_attn_kernel, dim3(unsigned(nwg)), dim3(kThreads), kStages * kStageBytes, stream, a, pl,
-                       part_o, part_ms);
+    switch (stages) {
+      case 3: e = launch_stages<3>(a, pl, nwg, part_o, part_ms, stream); break;
+      case 5: e = launch_stages<5>(a, pl, nwg, part_o, part_ms, stream); break;
+      default: e = launch_stages<4>(a, pl, nwg, part_o, part_ms, stream); break;
+    }
   }
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.ks == 1) return e;
   return launch_attn_combine(a, tiles32, pl.ks, a.ws, stream, "uno_block_attention_combine");
 }
