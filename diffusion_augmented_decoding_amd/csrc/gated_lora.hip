@@ -690,7 +690,7 @@ TileCfg choose_main_tile(int64_t M, int64_t N, int64_t Ktot) {
       if (id >= 0 && s >= 1 && s <= 16) return {id, s};
     }
   }
-  // Measured on MI355X at M = 1024 (event-timed sweeps):
+  // Measured on MI355X at M = 1024 (event-timed sweeps), where M < 2048:
   //   4096 -> 12288: direct-load 256x192, 4 stages (256 tiles, one per CU);
   //   12288 -> 4096: 256x256 (8 waves) with 4 K-splits;
   //   4096 -> 4096: direct-load 128x128, no split (256 tiles);
@@ -702,6 +702,10 @@ TileCfg choose_main_tile(int64_t M, int64_t N, int64_t Ktot) {
     while (t * s < 192 && s < smax && kt / (2 * s) >= min_kt) s *= 2;
     return s;
   };
+  // Measured at M = 4096 (the decode step's rows): the register-prefetch
+  // 256x256 kernel (8 waves) leads for every projection with N >= 2048 and
+  // for the LM head (1.0-1.15 PFLOP/s against 0.6-1.0 for the others).
+  if (M >= 2048 && N >= 2048) return {9, 1};
   if (M >= 512 && N % 192 == 0 && tiles(256, 192) >= 192) return {12, 1};
   if (M >= 512 && N % 256 == 0 && tiles(256, 256) >= 64 && kt >= 128) return {9, splits_for(tiles(256, 256), 4, 8)};
   if (M >= 512 && N % 128 == 0) return {15, splits_for(tiles(128, 128), 4, 8)};
