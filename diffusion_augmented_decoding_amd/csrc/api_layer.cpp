@@ -128,14 +128,17 @@ hipError_t launch_decoder_layer(const DecoderLayerArgs& d, hipStream_t stream) {
     na.ldo = d.hidden;
     return launch_rms_norm(na, stream);
   };
-  auto rope = [&](void* x, int heads) {
+  auto rope_qk = [&]() {
     RopeArgs ra{};
     ra.rows = rows;
-    ra.n_heads = heads;
-    ra.x = x;
-    ra.ldx = int64_t(heads) * kHeadDim;
+    ra.n_heads = d.n_heads;
+    ra.x = q;
+    ra.ldx = int64_t(d.n_heads) * kHeadDim;
     ra.positions = d.positions;
     ra.theta = d.rope_theta;
+    ra.n_heads2 = d.n_kv;
+    ra.x2 = k;
+    ra.ldx2 = int64_t(d.n_kv) * kHeadDim;
     return launch_rope(ra, stream);
   };
 
@@ -143,8 +146,7 @@ hipError_t launch_decoder_layer(const DecoderLayerArgs& d, hipStream_t stream) {
   if (e == hipSuccess) e = proj(UNO_PROJ_Q, a, d.hidden, qd, q);
   if (e == hipSuccess) e = proj(UNO_PROJ_K, a, d.hidden, kvd, k);
   if (e == hipSuccess) e = proj(UNO_PROJ_V, a, d.hidden, kvd, v);
-  if (e == hipSuccess) e = rope(q, d.n_heads);
-  if (e == hipSuccess) e = rope(k, d.n_kv);
+  if (e == hipSuccess) e = rope_qk();
   if (e == hipSuccess) {
     TreeAttnArgs ta{};
     ta.batch = d.batch;
@@ -230,7 +232,7 @@ uno_status uno_rope(hipStream_t stream, int64_t rows, int32_t n_heads, void* x, 
                     const int32_t* positions, float theta) {
   UNO_GUARD_BEGIN
   if (rows < 1 || n_heads < 1) return fail(UNO_ERR_INVALID_ARGUMENT, "rows and n_heads must be >= 1");
-  if (rows * n_heads * 64 / 256 >= 0x7fffffff) return fail(UNO_ERR_UNSUPPORTED, "too many elements");
+  if (rows > 0x7fffffff) return fail(UNO_ERR_UNSUPPORTED, "rows above 2^31 - 1");
   if (!x || !positions) return fail(UNO_ERR_INVALID_ARGUMENT, "x and positions are required");
   if (ldx < int64_t(n_heads) * kHeadDim) return fail(UNO_ERR_INVALID_ARGUMENT, "ldx below n_heads * 128");
   if (!(theta > 1.f) || !std::isfinite(theta)) return fail(UNO_ERR_INVALID_ARGUMENT, "theta must be finite and > 1");

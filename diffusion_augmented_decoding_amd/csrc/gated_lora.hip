@@ -583,6 +583,7 @@ constexpr TileShape kShapes[] = {
     {"256x256w8p1", 256, 256, 8},    {"dl256x256s4", 256, 256, 8},    {"dl256x256s5", 256, 256, 8},
     {"dl256x192s4", 256, 192, 8},    {"dl256x192s5", 256, 192, 8},    {"dl256x128s6", 256, 128, 8},
     {"dl128x128s6", 128, 128, 4},    {"dl256x256w4s4", 256, 256, 4},  {"dl256x256w4s5", 256, 256, 4},
+    {"256x256w8p2", 256, 256, 8},    {"256x256w8p1d1", 256, 256, 8},  {"256x256w8p2d1", 256, 256, 8},
 };
 constexpr int kNumShapes = int(sizeof(kShapes) / sizeof(kShapes[0]));
 
@@ -662,6 +663,9 @@ hipError_t launch_cfg(const TileCfg& c, const GemmParams& p, hipStream_t stream,
     case 15: return launch_tile_dl<128, 128, 2, 2, 6, MODE>(p, c.splits, stream, name);
     case 16: return launch_tile_dl<256, 256, 2, 2, 4, MODE>(p, c.splits, stream, name);
     case 17: return launch_tile_dl<256, 256, 2, 2, 5, MODE>(p, c.splits, stream, name);
+    case 18: return launch_tile<256, 256, 4, 2, 2, 0, MODE>(p, c.splits, stream, name);
+    case 19: return launch_tile<256, 256, 4, 2, 1, 1, MODE>(p, c.splits, stream, name);
+    case 20: return launch_tile<256, 256, 4, 2, 2, 1, MODE>(p, c.splits, stream, name);
   }
   return hipErrorInvalidValue;
 }

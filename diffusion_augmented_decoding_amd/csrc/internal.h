@@ -159,6 +159,8 @@ struct RopeArgs {
   void* x; int64_t ldx;              // [rows][n_heads * 128], rotated in place
   const int32_t* positions;          // [rows]
   float theta;
+  int n_heads2;                      // optional second tensor at the same positions (0: none)
+  void* x2; int64_t ldx2;
 };
 hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);
 

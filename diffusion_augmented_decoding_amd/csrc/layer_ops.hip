@@ -81,25 +81,29 @@ __global__ __launch_bounds__(kNormThreads) void rms_norm_kernel(RmsNormArgs a) {
   }
 }
 
-// In-place rotary embedding.  Thread (row, head, i < 64): the pair
-// (x_i, x_{i+64}) rotated by pos * theta^(-i/64); the angle is formed and
-// reduced in double precision, so positions far into a long context keep
-// their phase.
+// In-place rotary embedding, one workgroup per row.  Thread t owns pair
+// index i = t % 64 and forms the angle pos * theta^(-i/64) once, in double
+// precision (positions far into a long context keep their phase), then
+// rotates the pair (x_i, x_{i+64}) of every 4th head from t / 64 on, in x
+// and then in the optional second tensor at the same positions (q and k).
 __global__ __launch_bounds__(256) void rope_kernel(RopeArgs a) {
-  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t per_row = int64_t(a.n_heads) * 64;
-  if (t >= a.rows * per_row) return;
-  const int64_t row = t / per_row;
-  const int rem = int(t - row * per_row);
-  const int head = rem / 64, i = rem % 64;
-  uint16_t* p = static_cast<uint16_t*>(a.x) + row * a.ldx + head * 128;
+  const int64_t row = blockIdx.x;
+  const int i = threadIdx.x & 63, h0 = threadIdx.x >> 6;
   const double inv_freq = exp(-double(i) / 64.0 * log(double(a.theta)));
   double s, c;
   sincos(double(a.positions[row]) * inv_freq, &s, &c);
   const float cs = float(c), sn = float(s);
-  const float x1 = bf16_to_f32(p[i]), x2 = bf16_to_f32(p[i + 64]);
-  p[i] = f32_to_bf16(x1 * cs - x2 * sn);
-  p[i + 64] = f32_to_bf16(x2 * cs + x1 * sn);
+  auto rotate = [&](uint16_t* p) {
+    const float x1 = bf16_to_f32(p[i]), x2 = bf16_to_f32(p[i + 64]);
+    p[i] = f32_to_bf16(x1 * cs - x2 * sn);
+    p[i + 64] = f32_to_bf16(x2 * cs + x1 * sn);
+  };
+  uint16_t* xr = static_cast<uint16_t*>(a.x) + row * a.ldx;
+  for (int h = h0; h < a.n_heads; h += 4) rotate(xr + h * 128);
+  if (a.x2) {
+    uint16_t* xr2 = static_cast<uint16_t*>(a.x2) + row * a.ldx2;
+    for (int h = h0; h < a.n_heads2; h += 4) rotate(xr2 + h * 128);
+  }
 }
 
 // out = silu(g) * u = g / (1 + e^-g) * u, 8 elements per thread.
@@ -131,9 +135,8 @@ hipError_t launch_rms_norm(const RmsNormArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_rope(const RopeArgs& a, hipStream_t stream) {
-  const int64_t n = a.rows * a.n_heads * 64;
   ProfileScope ps("uno_rope", stream);
-  hipLaunchKernelGGL(rope_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(rope_kernel, dim3(unsigned(a.rows)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
