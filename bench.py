@@ -301,7 +301,7 @@ def cpu_baseline_step(args, tokens_per_step):
     import workloads
     f = FULL
     blk, ctx, V, hid = f["block"], f["ctx"], f["vocab"], f["hidden"]
-    n_seq, n_apply = 2, 12
+    n_seq, n_apply = 2, 36
     gate, pos = oracle.step_rows(1, blk, ctx)
     w = workloads.layer_weights_case(hid, f["inter"], f["n_heads"], f["n_kv"], f["r"], args.seed, 0)
     w64 = {kk[:-4]: v.astype(np.float64) for kk, v in w.items() if kk.endswith("_f32")}

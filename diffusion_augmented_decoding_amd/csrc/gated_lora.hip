@@ -89,7 +89,13 @@ __device__ __forceinline__ void split_range(const GemmParams& p, int bk, int kt_
 // BM x BN block tile, WM x WN waves, P K-tiles of register prefetch, DBF:
 // double-buffer the MFMA fragments across k-steps, MODE: 0 = bf16 out,
 // 1 = fp32 split-K partials.
-template <int BM, int BN, int WM, int WN, int P, int DBF, int MODE>
+// FAST: every K-tile is whole (K1 and K2 multiples of 64) and every operand
+// spans < 2 GB, so tiles are read with buffer loads: a per-lane row offset
+// fixed for the whole K loop plus a scalar offset (chunk group, K-tile), with
+// rows past M / N and K-tiles past the split falling outside the buffer and
+// reading zeros.  No per-load address arithmetic or masking is left in the
+// loop, and the LDS slot of each chunk is a fixed offset.
+template <int BM, int BN, int WM, int WN, int P, int DBF, int MODE, int FAST>
 __global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p) {
   constexpr int NT = WM * WN * kWave;
   constexpr int TM = BM / WM, TN = BN / WN;        // wave tile
@@ -153,11 +159,75 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p
   // touches land in distinct banks under a 32- or a 64-bank LDS
   auto lds_off = [](int row, int c) { return row * (kBK * 2) + ((c ^ (row & 7) ^ ((row >> 3) & 1)) * 16); };
   // write chunk i of a register set holding K-tile kt, zeroing invalid chunks
-  auto sstore = [&](const u32x4 (&src)[LT], int stage, int i, int kt) {
+  auto sstore_slow = [&](const u32x4 (&src)[LT], int stage, int i, int kt) {
     const int row = chunk_row(i), c = chunk_col(i);
     unsigned char* base = smem + stage * STAGE + (i < LA ? 0 : BN * kBK * 2);
     const u32x4 v = chunk_ok(i, kt) ? src[i] : u32x4{0u, 0u, 0u, 0u};
     *reinterpret_cast<u32x4*>(base + lds_off(row, c)) = v;
+  };
+
+  // ---- FAST addressing (see above): chunk i covers tile rows
+  // (i mod side) * NT/8 + tid/8, 16-byte column tid % 8 of the K-tile
+  constexpr int RPG = NT / kChunksPerRow;          // tile rows per chunk group
+  static_assert(!FAST || (RPG % 16 == 0), "the LDS swizzle must not depend on the chunk group");
+  // (buffer descriptors are built unconditionally: the non-FAST path ignores them)
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.w), 0, int(int64_t(p.N) * p.ldw * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.b), 0, int(int64_t(p.N) * p.ldb * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.x), 0, int(int64_t(p.M) * p.ldx * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rt =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.t), 0, int(int64_t(p.M) * p.ldt * 2), 0x00020000);
+  uint32_t va1 = 0, va2 = 0, vb1 = 0, vb2 = 0, slot = 0;
+  int kt1 = 0;
+  if constexpr (FAST) {
+    const uint32_t col = uint32_t(tid % kChunksPerRow) * 16;
+    const int trow = tid / kChunksPerRow;
+    va1 = uint32_t((n0 + trow) * p.ldw * 2) + col;
+    va2 = uint32_t((n0 + trow) * p.ldb * 2) + col;
+    vb1 = uint32_t((m0 + trow) * p.ldx * 2) + col;
+    vb2 = uint32_t((m0 + trow) * p.ldt * 2) + col;
+    slot = uint32_t(lds_off(trow, tid % kChunksPerRow));
+    kt1 = p.K1 / kBK;
+  }
+  auto gload_fast = [&](u32x4 (&dst)[LT], int i, int kt) {
+    // every choice below is wave-uniform; the descriptors are never selected
+    // at run time (a selected descriptor would need a readfirstlane loop)
+    const bool live = kt < kt_end;
+    const bool first = kt < kt1;
+    const int q = i < LA ? i : i - LA;
+    const int ktl = first ? kt : kt - kt1;
+    if (i < LA) {
+      const int step = first ? RPG * int(p.ldw) * 2 : RPG * int(p.ldb) * 2;
+      uint32_t off = (first ? va1 : va2) + uint32_t(q * step + ktl * kBK * 2);
+      off = live ? off : 0x80000000u;   // past the split: out of range, reads 0
+      dst[i] = __builtin_bit_cast(u32x4, first ? __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0)
+                                               : __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
+    } else {
+      const int step = first ? RPG * int(p.ldx) * 2 : RPG * int(p.ldt) * 2;
+      uint32_t off = (first ? vb1 : vb2) + uint32_t(q * step + ktl * kBK * 2);
+      off = live ? off : 0x80000000u;
+      dst[i] = __builtin_bit_cast(u32x4, first ? __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0)
+                                               : __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, 0));
+    }
+  };
+  auto sstore_fast = [&](const u32x4 (&src)[LT], int stage, int i) {
+    const int q = i < LA ? i : i - LA;
+    unsigned char* base = smem + stage * STAGE + (i < LA ? 0 : BN * kBK * 2) + q * RPG * kBK * 2;
+    *reinterpret_cast<u32x4*>(base + slot) = src[i];
+  };
+  auto sstore = [&](const u32x4 (&src)[LT], int stage, int i, int kt) {
+    if constexpr (FAST)
+      sstore_fast(src, stage, i);
+    else
+      sstore_slow(src, stage, i, kt);
+  };
+  auto gload = [&](u32x4 (&dst)[LT], int i, int kt) {
+    if constexpr (FAST)
+      gload_fast(dst, i, kt);
+    else
+      gload1(dst, i, kt);
   };
 
   const int lrow = lane & 31, lhalf = lane >> 5;
@@ -200,7 +270,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p
 #pragma unroll
       for (int i = kk * LT / 4; i < (kk + 1) * LT / 4; ++i) {
         sstore(set, cur ^ 1, i, kt_next);
-        if constexpr (RELOAD) gload1(set, i, kt_reload);
+        if constexpr (RELOAD) gload(set, i, kt_reload);
       }
       // one MFMA, then one of each pending memory op, repeated
       const int nr = DBF ? ((kk + 1 < kBK / 16) ? FN + FM : 0) : 0;
@@ -220,11 +290,11 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p
 #pragma unroll
     for (int s = 0; s < P; ++s)
 #pragma unroll
-      for (int i = 0; i < LT; ++i) gload1(reg[s], i, kt_begin + s);
+      for (int i = 0; i < LT; ++i) gload(reg[s], i, kt_begin + s);
 #pragma unroll
     for (int i = 0; i < LT; ++i) {
       sstore(reg[0], 0, i, kt_begin);
-      gload1(reg[0], i, kt_begin + P);
+      gload(reg[0], i, kt_begin + P);
     }
     __syncthreads();
     // invariant at iteration t (K-tile kt = kt_begin + t): LDS stage t & 1 holds
@@ -583,7 +653,6 @@ constexpr TileShape kShapes[] = {
     {"256x256w8p1", 256, 256, 8},    {"dl256x256s4", 256, 256, 8},    {"dl256x256s5", 256, 256, 8},
     {"dl256x192s4", 256, 192, 8},    {"dl256x192s5", 256, 192, 8},    {"dl256x128s6", 256, 128, 8},
     {"dl128x128s6", 128, 128, 4},    {"dl256x256w4s4", 256, 256, 4},  {"dl256x256w4s5", 256, 256, 4},
-    {"256x256w8p2", 256, 256, 8},    {"256x256w8p1d1", 256, 256, 8},  {"256x256w8p2d1", 256, 256, 8},
 };
 constexpr int kNumShapes = int(sizeof(kShapes) / sizeof(kShapes[0]));
 
@@ -592,9 +661,18 @@ struct TileCfg {
   int splits;
 };
 
-template <int BM, int BN, int WM, int WN, int P, int DBF, int MODE>
-hipError_t launch_tile(GemmParams p, int splits, hipStream_t stream, const char* name) {
-  auto kern = gemm_bf16_kernel<BM, BN, WM, WN, P, DBF, MODE>;
+// The buffer-load path needs whole K-tiles and operands whose byte offsets
+// (including rows up to one tile past the end) stay below 2^31.
+bool fast_ok(const GemmParams& p, int bm, int bn) {
+  const int64_t lim = int64_t(1) << 31;
+  return p.K1 % kBK == 0 && p.K2 % kBK == 0 && int64_t(p.N + bn) * p.ldw * 2 < lim &&
+         int64_t(p.N + bn) * p.ldb * 2 < lim && int64_t(p.M + bm) * p.ldx * 2 < lim &&
+         int64_t(p.M + bm) * p.ldt * 2 < lim;
+}
+
+template <int BM, int BN, int WM, int WN, int P, int DBF, int MODE, int FAST>
+hipError_t launch_tile_k(GemmParams p, int splits, hipStream_t stream, const char* name) {
+  auto kern = gemm_bf16_kernel<BM, BN, WM, WN, P, DBF, MODE, FAST>;
   const size_t lds = 2 * size_t(BN + BM) * kBK * 2;
   static bool configured = false;
   if (!configured) {
@@ -614,6 +692,19 @@ hipError_t launch_tile(GemmParams p, int splits, hipStream_t stream, const char*
   ProfileScope ps(name, stream);
   hipLaunchKernelGGL(kern, grid, dim3(WM * WN * kWave), lds, stream, p);
   return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, int P, int DBF, int MODE>
+hipError_t launch_tile(GemmParams p, int splits, hipStream_t stream, const char* name) {
+  return launch_tile_k<BM, BN, WM, WN, P, DBF, MODE, 0>(p, splits, stream, name);
+}
+
+template <int BM, int BN, int WM, int WN, int P, int DBF, int MODE>
+hipError_t launch_tile_fast(GemmParams p, int splits, hipStream_t stream, const char* name) {
+  const char* env = getenv("UNO_GEMM_FAST");   // tuning override: 0 keeps the masked loads
+  if (fast_ok(p, BM, BN) && !(env && atoi(env) == 0))
+    return launch_tile_k<BM, BN, WM, WN, P, DBF, MODE, 1>(p, splits, stream, name);
+  return launch_tile_k<BM, BN, WM, WN, P, DBF, MODE, 0>(p, splits, stream, name);
 }
 
 template <int BM, int BN, int WM, int WN, int S, int MODE>
@@ -653,8 +744,8 @@ hipError_t launch_cfg(const TileCfg& c, const GemmParams& p, hipStream_t stream,
     case 5: return launch_tile<256, 192, 4, 2, 2, 0, MODE>(p, c.splits, stream, name);
     case 6: return launch_tile<256, 128, 4, 2, 3, 1, MODE>(p, c.splits, stream, name);
     case 7: return launch_tile<256, 128, 4, 2, 2, 0, MODE>(p, c.splits, stream, name);
-    case 8: return launch_tile<256, 256, 2, 2, 1, 0, MODE>(p, c.splits, stream, name);
-    case 9: return launch_tile<256, 256, 4, 2, 1, 0, MODE>(p, c.splits, stream, name);
+    case 8: return launch_tile_fast<256, 256, 2, 2, 1, 0, MODE>(p, c.splits, stream, name);
+    case 9: return launch_tile_fast<256, 256, 4, 2, 1, 0, MODE>(p, c.splits, stream, name);
     case 10: return launch_tile_dl<256, 256, 4, 2, 4, MODE>(p, c.splits, stream, name);
     case 11: return launch_tile_dl<256, 256, 4, 2, 5, MODE>(p, c.splits, stream, name);
     case 12: return launch_tile_dl<256, 192, 4, 2, 4, MODE>(p, c.splits, stream, name);
@@ -663,9 +754,7 @@ hipError_t launch_cfg(const TileCfg& c, const GemmParams& p, hipStream_t stream,
     case 15: return launch_tile_dl<128, 128, 2, 2, 6, MODE>(p, c.splits, stream, name);
     case 16: return launch_tile_dl<256, 256, 2, 2, 4, MODE>(p, c.splits, stream, name);
     case 17: return launch_tile_dl<256, 256, 2, 2, 5, MODE>(p, c.splits, stream, name);
-    case 18: return launch_tile<256, 256, 4, 2, 2, 0, MODE>(p, c.splits, stream, name);
-    case 19: return launch_tile<256, 256, 4, 2, 1, 1, MODE>(p, c.splits, stream, name);
-    case 20: return launch_tile<256, 256, 4, 2, 2, 1, MODE>(p, c.splits, stream, name);
+
   }
   return hipErrorInvalidValue;
 }
@@ -716,15 +805,32 @@ TileCfg choose_main_tile(int64_t M, int64_t N, int64_t Ktot) {
   return {1, splits_for(tiles(128, 128), 4, 16)};
 }
 
-int lora_down_splits(int64_t M, int64_t r, int64_t K) {
-  const int64_t tiles = ((M + 63) / 64) * ((r + 63) / 64);
-  int64_t s = (256 + tiles - 1) / tiles;
+// LoRA-down tile and split count.  Measured at M = 4096 (event-timed): the
+// direct-load 128x128 tile with 8 K-splits takes 18 us at K = 4096 and 30 us
+// at K = 12288, against 25 and 67 us for 64x64 tiles with 2 splits; below
+// 2048 rows the 64x64 tile spreads over enough workgroups.
+TileCfg lora_down_cfg(int64_t M, int64_t r, int64_t K) {
   const int64_t kt = (K + kBK - 1) / kBK;
+  int shape = 0;
+  int64_t s;
+  if (M >= 2048 && r % 128 == 0) {
+    shape = 15;
+    s = 8;
+  } else {
+    const int64_t tiles = ((M + 63) / 64) * ((r + 63) / 64);
+    s = (256 + tiles - 1) / tiles;
+  }
+  {
+    const char* env = getenv("UNO_LORA_SPLITS");   // tuning override (sweeps): partials for this many splits
+    if (env && atoi(env) >= 1 && atoi(env) <= 16) s = atoi(env);
+  }
   if (s > kt / 2) s = kt / 2;
   if (s < 1) s = 1;
   if (s > 16) s = 16;
-  return int(s);
+  return TileCfg{shape, int(s)};
 }
+
+int lora_down_splits(int64_t M, int64_t r, int64_t K) { return lora_down_cfg(M, r, K).splits; }
 
 }  // namespace
 
@@ -781,12 +887,29 @@ hipError_t launch_gated_lora(const GatedLoraArgs& a, hipStream_t stream) {
     d.w = static_cast<const uint16_t*>(a.a);
     d.ldw = a.lda;
     d.part = part;
-    hipError_t e = launch_cfg<1>(TileCfg{0, splits}, d, stream, "uno_lora_down_bf16");
+    TileCfg dc = lora_down_cfg(a.M, a.r, a.K);
+    {
+      // tuning override "<shape name>/<splits>" (sweeps only); the split count sizes the
+      // partials, so it may not exceed the one the workspace was sized for
+      const char* env = getenv("UNO_LORA_TILE");
+      if (env) {
+        char nm[32] = {0};
+        const char* slash = strchr(env, '/');
+        const size_t len = slash ? size_t(slash - env) : strlen(env);
+        if (len < sizeof(nm)) {
+          memcpy(nm, env, len);
+          const int id = shape_index(nm);
+          const int sp = slash ? atoi(slash + 1) : 1;
+          if (id >= 0 && sp >= 1 && sp <= splits) dc = TileCfg{id, sp};
+        }
+      }
+    }
+    hipError_t e = launch_cfg<1>(dc, d, stream, "uno_lora_down_bf16");
     if (e != hipSuccess) return e;
     const int64_t n = a.M * a.r;
     {
       ProfileScope ps("uno_lora_gate", stream);
-      hipLaunchKernelGGL(lora_gate_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream, part, splits,
+      hipLaunchKernelGGL(lora_gate_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream, part, dc.splits,
                          int(a.M), int(a.r), a.gate, a.lora_scale, t);
     }
     e = hipGetLastError();
