@@ -290,7 +290,7 @@ def bench_full_step(args, dad, torch):
 
 def cpu_baseline_step(args, tokens_per_step):
     """The float64 oracle on a bounded sample of the whole step: 2 of the 128
-    sequences (32 rows each) through 12 applications of one full-size layer
+    sequences (32 rows each) through 36 applications of one full-size layer
     over that sequence's 8K cache (the layer's values do not change its cost),
     the LM head over a 1/16 slice of the vocabulary, and the draft draw +
     verify of one sequence at the full vocabulary; scaled to 128 sequences,
