@@ -50,6 +50,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def measured_traffic(summary, source):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when the kernel source has changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(os.path.join(ROOT, "profiles", summary)).read()
+        src = open(os.path.join(ROOT, "diffusion_augmented_decoding_amd", "csrc", source), "rb").read()
+    except OSError:
+        return None
+    fields = dict(line.split(None, 1) for line in text.splitlines()
+                  if line.startswith(("traffic_bytes_per_launch", "source_sha256")))
+    if fields.get("source_sha256", "").strip() != hashlib.sha256(src).hexdigest():
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -68,6 +84,8 @@ def main():
     ap.add_argument("--workload", choices=("step", "hot_path"), default="step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-components", action="store_true", help="skip the per-layer/sampler/tree workloads")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="end with a plain 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -90,6 +108,16 @@ def main():
     else:
         out = bench_hot_path(args, dad, torch, steps=args.steps, warmup=args.warmup,
                              with_cpu=not args.no_cpu_baseline)
+    if args.copy_probe:
+        # a plain copy of known size: FETCH_SIZE / WRITE_SIZE of this kernel
+        # give the scale between the counters and bytes moved
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_probe_bytes"] = {"read": 1 << 30, "write": 1 << 30}
     print(json.dumps(out), flush=True)
 
 
@@ -227,7 +255,8 @@ def bench_full_step(args, dad, torch):
         roof = {"bound": "hbm", "achieved": algo / (per_launch_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = (measured_traffic("uno_gemm_bf16_full_step_traffic.txt", "gated_lora.hip")
+                       if dominant == "uno_gemm_bf16" else None)
     roof["kernel"] = dominant
     roof["avg_launch_us"] = per_launch_ms * 1e3
     roof["launches_per_step"] = launches_per_step

@@ -63,6 +63,24 @@ struct GemmParams {
   float* part;                         // MODE 1 output: fp32 [split][M][N]
 };
 
+// Output tile of linear index `tile`.  Mode 1: column-major (M-tiles
+// fastest), so the contiguous band of tiles one XCD runs spans few N-tiles
+// and every M-tile.  Mode 2: groups of 8 M-tiles, N-tiles across the group,
+// so an XCD's band (and the workgroups it runs at once) is a 2D block of
+// M- and N-tiles that share both operands in that XCD's L2.
+__device__ __forceinline__ void tile_coords(const GemmParams& p, int tile, int& tm, int& tn) {
+  if (p.xcd_remap == 2 && p.tiles_m >= 8) {
+    const int gsz = 8 * p.tiles_n;
+    const int g = tile / gsz, rem = tile - g * gsz;
+    const int gm = min(8, p.tiles_m - 8 * g);   // rows in this (possibly partial) group
+    tm = 8 * g + rem % gm;
+    tn = rem / gm;
+  } else {
+    tm = tile % p.tiles_m;
+    tn = tile / p.tiles_m;
+  }
+}
+
 // 16-byte chunk (8 bf16 along K) at K index kc of a row: from (base, ld) for
 // kc < K1, from (base2, ld2) at kc - K1 below Ktot.  Out-of-range chunks read
 // `base` instead (always valid) and are zeroed later, when written to LDS:
@@ -115,7 +133,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p
   const int ntiles = p.tiles_m * p.tiles_n;
   const int bid = blockIdx.x;
   const int tile = (p.xcd_remap && (ntiles & 7) == 0) ? (bid & 7) * (ntiles >> 3) + (bid >> 3) : bid;
-  const int tm = tile % p.tiles_m, tn = tile / p.tiles_m;
+  int tm, tn;
+  tile_coords(p, tile, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int Ktot = p.K1 + p.K2;
@@ -403,7 +422,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_dl_kernel(GemmParams p) 
   const int ntiles = p.tiles_m * p.tiles_n;
   const int bid = blockIdx.x;
   const int tile = (p.xcd_remap && (ntiles & 7) == 0) ? (bid & 7) * (ntiles >> 3) + (bid >> 3) : bid;
-  const int tm = tile % p.tiles_m, tn = tile / p.tiles_m;
+  int tm, tn;
+  tile_coords(p, tile, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int Ktot = p.K1 + p.K2;
@@ -684,8 +704,8 @@ hipError_t launch_tile_k(GemmParams p, int splits, hipStream_t stream, const cha
   p.tiles_m = (p.M + BM - 1) / BM;
   p.tiles_n = (p.N + BN - 1) / BN;
   {
-    const char* env = getenv("UNO_GEMM_XCD");   // tuning override: 0 disables the remap
-    p.xcd_remap = env ? atoi(env) : 1;
+    const char* env = getenv("UNO_GEMM_XCD");   // tuning override: 0 no remap, 1 column bands, 2 (default) 2D groups
+    p.xcd_remap = env ? atoi(env) : 2;
   }
   p.ktiles_per_split = ((p.K1 + kBK - 1) / kBK + splits - 1) / splits;
   dim3 grid(p.tiles_m * p.tiles_n, splits);
@@ -724,7 +744,7 @@ hipError_t launch_tile_dl(GemmParams p, int splits, hipStream_t stream, const ch
   p.tiles_n = (p.N + BN - 1) / BN;
   {
     const char* env = getenv("UNO_GEMM_XCD");
-    p.xcd_remap = env ? atoi(env) : 1;
+    p.xcd_remap = env ? atoi(env) : 2;
   }
   p.ktiles_per_split = ((p.K1 + kBKd - 1) / kBKd + splits - 1) / splits;
   dim3 grid(p.tiles_m * p.tiles_n, splits);
