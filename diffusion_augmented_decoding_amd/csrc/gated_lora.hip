@@ -716,11 +716,6 @@ hipError_t launch_tile_k(GemmParams p, int splits, hipStream_t stream, const cha
 
 template <int BM, int BN, int WM, int WN, int P, int DBF, int MODE>
 hipError_t launch_tile(GemmParams p, int splits, hipStream_t stream, const char* name) {
-  return launch_tile_k<BM, BN, WM, WN, P, DBF, MODE, 0>(p, splits, stream, name);
-}
-
-template <int BM, int BN, int WM, int WN, int P, int DBF, int MODE>
-hipError_t launch_tile_fast(GemmParams p, int splits, hipStream_t stream, const char* name) {
   const char* env = getenv("UNO_GEMM_FAST");   // tuning override: 0 keeps the masked loads
   if (fast_ok(p, BM, BN) && !(env && atoi(env) == 0))
     return launch_tile_k<BM, BN, WM, WN, P, DBF, MODE, 1>(p, splits, stream, name);
@@ -764,8 +759,8 @@ hipError_t launch_cfg(const TileCfg& c, const GemmParams& p, hipStream_t stream,
     case 5: return launch_tile<256, 192, 4, 2, 2, 0, MODE>(p, c.splits, stream, name);
     case 6: return launch_tile<256, 128, 4, 2, 3, 1, MODE>(p, c.splits, stream, name);
     case 7: return launch_tile<256, 128, 4, 2, 2, 0, MODE>(p, c.splits, stream, name);
-    case 8: return launch_tile_fast<256, 256, 2, 2, 1, 0, MODE>(p, c.splits, stream, name);
-    case 9: return launch_tile_fast<256, 256, 4, 2, 1, 0, MODE>(p, c.splits, stream, name);
+    case 8: return launch_tile<256, 256, 2, 2, 1, 0, MODE>(p, c.splits, stream, name);
+    case 9: return launch_tile<256, 256, 4, 2, 1, 0, MODE>(p, c.splits, stream, name);
     case 10: return launch_tile_dl<256, 256, 4, 2, 4, MODE>(p, c.splits, stream, name);
     case 11: return launch_tile_dl<256, 256, 4, 2, 5, MODE>(p, c.splits, stream, name);
     case 12: return launch_tile_dl<256, 192, 4, 2, 4, MODE>(p, c.splits, stream, name);
@@ -803,11 +798,11 @@ TileCfg choose_main_tile(int64_t M, int64_t N, int64_t Ktot) {
       if (id >= 0 && s >= 1 && s <= 16) return {id, s};
     }
   }
-  // Measured on MI355X at M = 1024 (event-timed sweeps), where M < 2048:
-  //   4096 -> 12288: direct-load 256x192, 4 stages (256 tiles, one per CU);
+  // Measured on MI355X at M = 1024 (event-timed sweeps, buffer-load path), where M < 2048:
+  //   4096 -> 12288: 256x192 (8 waves, 2-deep prefetch; 256 tiles, one per CU), 1.02 PFLOP/s;
   //   12288 -> 4096: 256x256 (8 waves) with 4 K-splits;
-  //   4096 -> 4096: direct-load 128x128, no split (256 tiles);
-  //   4096 -> 1024: direct-load 128x128 with 4 K-splits.
+  //   4096 -> 4096: 128x128 (4 waves), no split (256 tiles);
+  //   4096 -> 1024: 128x128 (4 waves) with 4 K-splits.
   auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   const int64_t kt = (Ktot + kBK - 1) / kBK;
   auto splits_for = [&](int64_t t, int smax, int min_kt) {
@@ -819,9 +814,9 @@ TileCfg choose_main_tile(int64_t M, int64_t N, int64_t Ktot) {
   // 256x256 kernel (8 waves) leads for every projection with N >= 2048 and
   // for the LM head (1.0-1.15 PFLOP/s against 0.6-1.0 for the others).
   if (M >= 2048 && N >= 2048) return {9, 1};
-  if (M >= 512 && N % 192 == 0 && tiles(256, 192) >= 192) return {12, 1};
+  if (M >= 512 && N % 192 == 0 && tiles(256, 192) >= 192) return {5, 1};
   if (M >= 512 && N % 256 == 0 && tiles(256, 256) >= 64 && kt >= 128) return {9, splits_for(tiles(256, 256), 4, 8)};
-  if (M >= 512 && N % 128 == 0) return {15, splits_for(tiles(128, 128), 4, 8)};
+  if (M >= 512 && N % 128 == 0) return {1, splits_for(tiles(128, 128), 4, 8)};
   return {1, splits_for(tiles(128, 128), 4, 16)};
 }
 
