@@ -168,9 +168,14 @@ def bench_full_step(args, dad, torch):
     layers, keep = [], []
     for li in range(nl):
         w = {"attn_norm": 1.0 + randn((hid,), 0.1), "mlp_norm": 1.0 + randn((hid,), 0.1)}
+        # the adapters of q/k/v and of gate/up are stored back to back, so each
+        # group's LoRA-down runs as one launch
+        a_qkv = randn((3 * r, hid), 0.02)
+        a_gu = randn((2 * r, hid), 0.02)
+        packed_a = {"q": a_qkv[:r], "k": a_qkv[r:2 * r], "v": a_qkv[2 * r:], "g": a_gu[:r], "u": a_gu[r:]}
         for p, (n_out, n_in) in shapes.items():
             w["w" + p] = randn((n_out, n_in), 0.02)
-            w["a" + p] = randn((r, n_in), 0.02)
+            w["a" + p] = packed_a[p] if p in packed_a else randn((r, n_in), 0.02)
             w["b" + p] = randn((n_out, r), 0.02)
         kc = randn((B, ctx, Hkv, 128), 1.0)
         vc = randn((B, ctx, Hkv, 128), 1.0)

@@ -32,7 +32,7 @@ namespace uno {
 
 // Workspace layout of one decoder layer.
 struct LayerWs {
-  size_t a, q, k, v, att, o, g, u, lora, attn, total;
+  size_t a, q, k, v, att, o, g, u, lora, attn, tqkv, tgu, lpart, total;
 };
 
 static size_t up256(size_t b) { return align_up(b, 256); }
@@ -62,6 +62,10 @@ static LayerWs layer_ws(int batch, int block, int ctx, int hidden, int inter, in
   for (const auto& s : shapes) lora = std::max(lora, gated_lora_workspace_bytes(UNO_BF16, M, s[0], s[1], r));
   w.lora = take(lora);
   w.attn = take(block_attention_workspace_bytes(batch, block, ctx, nh, nkv));
+  // grouped LoRA-down (adapters of q/k/v, and of gate/up, stored back to back)
+  w.tqkv = take(rows * 3 * size_t(r) * 2);
+  w.tgu = take(rows * 2 * size_t(r) * 2);
+  w.lpart = take(r > 0 ? std::max(lora_down_part_bytes(M, 3 * r, hidden), lora_down_part_bytes(M, 2 * r, hidden)) : 0);
   w.total = off;
   return w;
 }
@@ -89,7 +93,8 @@ hipError_t launch_decoder_layer(const DecoderLayerArgs& d, hipStream_t stream) {
   void* u = ws + L.u;
   void* h = d.h;
 
-  auto proj = [&](int p, const void* x, int64_t K, int64_t N, void* y) {
+  auto proj = [&](int p, const void* x, int64_t K, int64_t N, void* y, const uint16_t* t_pre = nullptr,
+                  int64_t ldt_pre = 0) {
     GatedLoraArgs ga{};
     ga.dtype = UNO_BF16;
     ga.M = rows;
@@ -108,6 +113,8 @@ hipError_t launch_decoder_layer(const DecoderLayerArgs& d, hipStream_t stream) {
     ga.lora_scale = d.lora_scale;
     ga.y = y;
     ga.ldy = N;
+    ga.t_pre = t_pre;
+    ga.ldt_pre = ldt_pre;
     ga.ws = ws + L.lora;
     ga.ws_bytes = d.ws_bytes - L.lora;
     return launch_gated_lora(ga, stream);
@@ -142,10 +149,43 @@ hipError_t launch_decoder_layer(const DecoderLayerArgs& d, hipStream_t stream) {
     return launch_rope(ra, stream);
   };
 
+  // Adapters stored back to back (q, k, v; gate, up) share one LoRA-down
+  // launch over the common input; each projection then reads its slice of T.
+  const bool lora = d.gate && d.r > 0;
+  const int64_t rK = int64_t(d.r) * d.hidden;
+  auto packed = [&](int p0, int n) {
+    if (!lora) return false;
+    const uint16_t* base = static_cast<const uint16_t*>(d.w->a[p0]);
+    for (int i = 1; i < n; ++i)
+      if (static_cast<const uint16_t*>(d.w->a[p0 + i]) != base + i * rK) return false;
+    return true;
+  };
+  auto group_down = [&](int p0, int n, const void* x, uint16_t* t) {
+    LoraDownArgs ld{};
+    ld.M = rows;
+    ld.K = d.hidden;
+    ld.n = int64_t(n) * d.r;
+    ld.x = x;
+    ld.ldx = d.hidden;
+    ld.a = d.w->a[p0];
+    ld.lda = d.hidden;
+    ld.gate = d.gate;
+    ld.lora_scale = d.lora_scale;
+    ld.t = t;
+    ld.part = ws + L.lpart;
+    return launch_lora_down(ld, stream);
+  };
+  uint16_t* tqkv = reinterpret_cast<uint16_t*>(ws + L.tqkv);
+  uint16_t* tgu = reinterpret_cast<uint16_t*>(ws + L.tgu);
+  const bool qkv_grouped = packed(UNO_PROJ_Q, 3);
+  const bool gu_grouped = packed(UNO_PROJ_GATE, 2);
+  const int64_t r3 = 3 * int64_t(d.r), r2 = 2 * int64_t(d.r);
+
   hipError_t e = norm(nullptr, d.w->attn_norm, a);
-  if (e == hipSuccess) e = proj(UNO_PROJ_Q, a, d.hidden, qd, q);
-  if (e == hipSuccess) e = proj(UNO_PROJ_K, a, d.hidden, kvd, k);
-  if (e == hipSuccess) e = proj(UNO_PROJ_V, a, d.hidden, kvd, v);
+  if (e == hipSuccess && qkv_grouped) e = group_down(UNO_PROJ_Q, 3, a, tqkv);
+  if (e == hipSuccess) e = proj(UNO_PROJ_Q, a, d.hidden, qd, q, qkv_grouped ? tqkv : nullptr, r3);
+  if (e == hipSuccess) e = proj(UNO_PROJ_K, a, d.hidden, kvd, k, qkv_grouped ? tqkv + d.r : nullptr, r3);
+  if (e == hipSuccess) e = proj(UNO_PROJ_V, a, d.hidden, kvd, v, qkv_grouped ? tqkv + 2 * d.r : nullptr, r3);
   if (e == hipSuccess) e = rope_qk();
   if (e == hipSuccess) {
     TreeAttnArgs ta{};
@@ -170,8 +210,9 @@ hipError_t launch_decoder_layer(const DecoderLayerArgs& d, hipStream_t stream) {
   }
   if (e == hipSuccess) e = proj(UNO_PROJ_O, att, qd, d.hidden, o);
   if (e == hipSuccess) e = norm(o, d.w->mlp_norm, a);                 // h += o; a = rmsnorm(h)
-  if (e == hipSuccess) e = proj(UNO_PROJ_GATE, a, d.hidden, d.inter, g);
-  if (e == hipSuccess) e = proj(UNO_PROJ_UP, a, d.hidden, d.inter, u);
+  if (e == hipSuccess && gu_grouped) e = group_down(UNO_PROJ_GATE, 2, a, tgu);
+  if (e == hipSuccess) e = proj(UNO_PROJ_GATE, a, d.hidden, d.inter, g, gu_grouped ? tgu : nullptr, r2);
+  if (e == hipSuccess) e = proj(UNO_PROJ_UP, a, d.hidden, d.inter, u, gu_grouped ? tgu + d.r : nullptr, r2);
   if (e == hipSuccess) {
     SiluMulArgs sa{};
     sa.rows = rows;

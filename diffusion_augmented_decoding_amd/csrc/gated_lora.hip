@@ -861,6 +861,55 @@ size_t gated_lora_workspace_bytes(uno_dtype dtype, int64_t M, int64_t N, int64_t
   return bytes;
 }
 
+size_t lora_down_part_bytes(int64_t M, int64_t n, int64_t K) {
+  return align_up(size_t(lora_down_splits(M, n, K)) * size_t(M) * size_t(n) * 4, 256);
+}
+
+// T[M][n] = bf16(s * g[m] * x A^T) for the n rows of A (one projection's r,
+// or several projections' adapters stored back to back): split-K MFMA GEMM
+// into fp32 partials, then lora_gate_kernel sums them in a fixed order.
+hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t stream) {
+  const int splits = lora_down_splits(a.M, a.n, a.K);
+  GemmParams d{};
+  d.M = int(a.M);
+  d.N = int(a.n);
+  d.K1 = int(a.K);
+  d.K2 = 0;
+  d.x = static_cast<const uint16_t*>(a.x);
+  d.ldx = a.ldx;
+  d.w = static_cast<const uint16_t*>(a.a);
+  d.ldw = a.lda;
+  d.t = d.x;
+  d.ldt = d.ldx;
+  d.b = d.w;
+  d.ldb = d.ldw;
+  d.part = static_cast<float*>(a.part);
+  TileCfg dc = lora_down_cfg(a.M, a.n, a.K);
+  {
+    // tuning override "<shape name>/<splits>" (sweeps only); the split count sizes the
+    // partials, so it may not exceed the one the workspace was sized for
+    const char* env = getenv("UNO_LORA_TILE");
+    if (env) {
+      char nm[32] = {0};
+      const char* slash = strchr(env, '/');
+      const size_t len = slash ? size_t(slash - env) : strlen(env);
+      if (len < sizeof(nm)) {
+        memcpy(nm, env, len);
+        const int id = shape_index(nm);
+        const int sp = slash ? atoi(slash + 1) : 1;
+        if (id >= 0 && sp >= 1 && sp <= splits) dc = TileCfg{id, sp};
+      }
+    }
+  }
+  hipError_t e = launch_cfg<1>(dc, d, stream, "uno_lora_down_bf16");
+  if (e != hipSuccess) return e;
+  const int64_t n = a.M * a.n;
+  ProfileScope ps("uno_lora_gate", stream);
+  hipLaunchKernelGGL(lora_gate_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const float*>(a.part), dc.splits, int(a.M), int(a.n), a.gate, a.lora_scale, a.t);
+  return hipGetLastError();
+}
+
 hipError_t launch_gated_lora(const GatedLoraArgs& a, hipStream_t stream) {
   const bool lora = a.r > 0 && a.gate != nullptr;
   if (a.dtype == UNO_F32) {
@@ -885,50 +934,31 @@ hipError_t launch_gated_lora(const GatedLoraArgs& a, hipStream_t stream) {
   }
 
   char* ws = static_cast<char*>(a.ws);
-  uint16_t* t = nullptr;
-  if (lora) {
-    const int splits = lora_down_splits(a.M, a.r, a.K);
-    t = reinterpret_cast<uint16_t*>(ws);
+  const uint16_t* t = nullptr;
+  int64_t ldt = a.r;
+  if (lora && a.t_pre) {
+    // T computed by the caller (a grouped LoRA-down over several projections)
+    t = static_cast<const uint16_t*>(a.t_pre);
+    ldt = a.ldt_pre;
+  } else if (lora) {
+    uint16_t* tw = reinterpret_cast<uint16_t*>(ws);
     ws += align_up(size_t(a.M) * a.r * 2, 256);
-    float* part = reinterpret_cast<float*>(ws);
-    ws += align_up(size_t(splits) * size_t(a.M) * size_t(a.r) * 4, 256);
-    GemmParams d{};
-    d.M = int(a.M);
-    d.N = int(a.r);
-    d.K1 = int(a.K);
-    d.K2 = 0;
-    d.x = static_cast<const uint16_t*>(a.x);
-    d.ldx = a.ldx;
-    d.w = static_cast<const uint16_t*>(a.a);
-    d.ldw = a.lda;
-    d.part = part;
-    TileCfg dc = lora_down_cfg(a.M, a.r, a.K);
-    {
-      // tuning override "<shape name>/<splits>" (sweeps only); the split count sizes the
-      // partials, so it may not exceed the one the workspace was sized for
-      const char* env = getenv("UNO_LORA_TILE");
-      if (env) {
-        char nm[32] = {0};
-        const char* slash = strchr(env, '/');
-        const size_t len = slash ? size_t(slash - env) : strlen(env);
-        if (len < sizeof(nm)) {
-          memcpy(nm, env, len);
-          const int id = shape_index(nm);
-          const int sp = slash ? atoi(slash + 1) : 1;
-          if (id >= 0 && sp >= 1 && sp <= splits) dc = TileCfg{id, sp};
-        }
-      }
-    }
-    hipError_t e = launch_cfg<1>(dc, d, stream, "uno_lora_down_bf16");
+    LoraDownArgs ld{};
+    ld.M = a.M;
+    ld.K = a.K;
+    ld.n = a.r;
+    ld.x = a.x;
+    ld.ldx = a.ldx;
+    ld.a = a.a;
+    ld.lda = a.lda;
+    ld.gate = a.gate;
+    ld.lora_scale = a.lora_scale;
+    ld.t = tw;
+    ld.part = ws;
+    ws += align_up(size_t(lora_down_splits(a.M, a.r, a.K)) * size_t(a.M) * size_t(a.r) * 4, 256);
+    hipError_t e = launch_lora_down(ld, stream);
     if (e != hipSuccess) return e;
-    const int64_t n = a.M * a.r;
-    {
-      ProfileScope ps("uno_lora_gate", stream);
-      hipLaunchKernelGGL(lora_gate_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream, part, dc.splits,
-                         int(a.M), int(a.r), a.gate, a.lora_scale, t);
-    }
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    t = tw;
   }
   GemmParams g{};
   g.M = int(a.M);
@@ -940,7 +970,7 @@ hipError_t launch_gated_lora(const GatedLoraArgs& a, hipStream_t stream) {
   g.w = static_cast<const uint16_t*>(a.w);
   g.ldw = a.ldw;
   g.t = lora ? t : g.x;
-  g.ldt = lora ? a.r : a.ldx;
+  g.ldt = lora ? ldt : a.ldx;
   g.b = lora ? static_cast<const uint16_t*>(a.b) : g.w;
   g.ldb = lora ? a.ldb : a.ldw;
   g.y = static_cast<uint16_t*>(a.y);

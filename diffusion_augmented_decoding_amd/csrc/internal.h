@@ -72,8 +72,22 @@ struct GatedLoraArgs {
   float lora_scale;
   void* y; int64_t ldy;
   void* ws; size_t ws_bytes;
+  const void* t_pre; int64_t ldt_pre;   // optional (bf16 path): T = s g (x A^T) computed by the caller
 };
 size_t gated_lora_workspace_bytes(uno_dtype dtype, int64_t M, int64_t N, int64_t K, int64_t r);
+
+// bf16 LoRA-down of n adapter rows: t [M][n] = bf16(s * g[m] * (x A^T)[m]), 0 where g = 0.
+struct LoraDownArgs {
+  int64_t M, K, n;
+  const void* x; int64_t ldx;
+  const void* a; int64_t lda;        // [n][K]
+  const uint8_t* gate;
+  float lora_scale;
+  uint16_t* t;                       // [M][n]
+  void* part;                        // fp32 partials, lora_down_part_bytes(M, n, K)
+};
+size_t lora_down_part_bytes(int64_t M, int64_t n, int64_t K);
+hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t stream);
 hipError_t launch_gated_lora(const GatedLoraArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- tree attention

@@ -284,7 +284,9 @@ uno_status uno_sample_rows(hipStream_t stream, uno_dtype logit_dtype, int32_t ro
  *   att = block_attention(q, cache + (k, v)); h += gated_lora(att, o);
  *   a = rmsnorm(h); h += gated_lora(silu(gated_lora(a, gate)) * gated_lora(a, up), down)
  * with every gated_lora as uno_gated_lora_linear under `gate` [rows] and
- * lora_scale.  hidden_state [rows][hidden], rows = batch * 2 * block;
+ * lora_scale.  When the adapters a[q], a[k], a[v] are stored back to back
+ * (one [3r][hidden] array), and likewise a[gate], a[up], each group's
+ * LoRA-down runs as one launch over the shared input.  hidden_state [rows][hidden], rows = batch * 2 * block;
  * positions int32 [rows].  The block's k and v are not written to the cache.
  * hidden and inter multiples of 8, r a multiple of 8, n_heads / n_kv_heads
  * <= 8, 1 <= block <= 128. */

@@ -197,9 +197,16 @@ def _layer_oracle_weights(wt):
     return {k[:-4]: v.astype(np.float64) for k, v in wt.items() if k.endswith("_f32")}
 
 
-def _run_layer(dad, c, gate=True):
+def _run_layer(dad, c, gate=True, packed=False):
     import torch
     wt = {k: _bits_dev(v) for k, v in c["weights"].items() if not k.endswith("_f32")}
+    if packed:
+        # adapters of q/k/v and of gate/up back to back: the grouped LoRA-down path
+        for group in (("q", "k", "v"), ("g", "u")):
+            cat = torch.cat([wt["a" + p] for p in group], dim=0).contiguous()
+            r = wt["a" + group[0]].shape[0]
+            for i, p in enumerate(group):
+                wt["a" + p] = cat[i * r:(i + 1) * r]
     kc, vc = _bits_dev(c["k_cache"]), _bits_dev(c["v_cache"])
     h = _bits_dev(c["h"])
     lw = dad.layer_weights(wt, kc, vc)
@@ -219,15 +226,18 @@ def _layer_ref(c, seqs):
     return rows, out
 
 
-@pytest.mark.parametrize("batch,block,ctx,hidden,inter,nh,nkv,r", [
-    (2, 4, 40, 256, 512, 4, 2, 16),
-    (3, 16, 300, 512, 1024, 8, 2, 32),
-    (1, 2, 0, 128, 384, 2, 1, 8),
+@pytest.mark.parametrize("batch,block,ctx,hidden,inter,nh,nkv,r,packed", [
+    (2, 4, 40, 256, 512, 4, 2, 16, False),
+    (2, 4, 40, 256, 512, 4, 2, 16, True),
+    (3, 16, 300, 512, 1024, 8, 2, 32, False),
+    (3, 16, 300, 512, 1024, 8, 2, 32, True),
+    (1, 2, 0, 128, 384, 2, 1, 8, False),
 ])
-def test_decoder_layer(gpu_lib, batch, block, ctx, hidden, inter, nh, nkv, r):
-    say(f"decoder layer B={batch} block={block} ctx={ctx} hidden={hidden} inter={inter} H={nh}/{nkv} r={r}")
+def test_decoder_layer(gpu_lib, batch, block, ctx, hidden, inter, nh, nkv, r, packed):
+    say(f"decoder layer B={batch} block={block} ctx={ctx} hidden={hidden} inter={inter} H={nh}/{nkv} r={r} "
+        f"packed adapters={packed}")
     c = workloads.decoder_layer_case(batch, block, ctx, hidden, inter, nh, nkv, r, seed=batch + ctx)
-    got = _run_layer(gpu_lib, c)
+    got = _run_layer(gpu_lib, c, packed=packed)
     rows, ref = _layer_ref(c, list(range(batch)))
     err = row_relerr(got[rows], ref)
     say(f"  row rel err {err:.3g}")
@@ -236,11 +246,12 @@ def test_decoder_layer(gpu_lib, batch, block, ctx, hidden, inter, nh, nkv, r):
 
 def test_decoder_layer_full_size_sampled_sequences(gpu_lib):
     """One Qwen3-8B-shaped layer at the decode-step shape: 128 sequences x
-    (16 clean + 16 noisy) rows, 8K cache, rank-128 adapters; the oracle
+    (16 clean + 16 noisy) rows, 8K cache, rank-128 adapters stored as the
+    bench stores them (q/k/v and gate/up adapters back to back); the oracle
     recomputes 2 sampled sequences (64 rows, both gate values)."""
     say("decoder layer B=128 block=16 ctx=8192 Qwen3-8B shapes (sampled)")
     c = workloads.decoder_layer_case(128, 16, 8192, seed=3, **QWEN)
-    got = _run_layer(gpu_lib, c)
+    got = _run_layer(gpu_lib, c, packed=True)
     assert np.all(np.isfinite(got))
     rows, ref = _layer_ref(c, [5, 120])
     err = row_relerr(got[rows], ref)
