@@ -28,11 +28,12 @@
 // rows are 128 B with the 16-byte chunk index XOR-swizzled by (row & 7),
 // which makes the fragment reads (32 rows, same chunk) bank-conflict free.
 // Tiles are mapped to block ids so that the blocks one XCD runs (ids
-// congruent mod 8) cover a contiguous band of N-tiles across all M-tiles:
-// each weight tile is then fetched into one XCD's L2 and reused by every
-// M-tile there.  A second kernel, gemm_dl_kernel, loads K-tiles straight into
-// LDS (global_load_lds) through a deeper stage ring; the dispatcher picks
-// per shape whichever measured faster.
+// congruent mod 8) form a contiguous band, and the band is ordered in groups
+// of 8 M-tiles by all N-tiles: the workgroups an XCD runs at once then share
+// both their weight and their activation tiles in that XCD's L2.  A second
+// kernel, gemm_dl_kernel, loads K-tiles straight into LDS (global_load_lds)
+// through a deeper stage ring; the dispatcher picks per shape whichever
+// measured faster (the LoRA-down at 4096 rows runs on it).
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
