@@ -211,9 +211,30 @@ hipError_t launch_decoder_layer(const DecoderLayerArgs& d, hipStream_t stream) {
   if (e == hipSuccess) e = proj(UNO_PROJ_O, att, qd, d.hidden, o);
   if (e == hipSuccess) e = norm(o, d.w->mlp_norm, a);                 // h += o; a = rmsnorm(h)
   if (e == hipSuccess && gu_grouped) e = group_down(UNO_PROJ_GATE, 2, a, tgu);
-  if (e == hipSuccess) e = proj(UNO_PROJ_GATE, a, d.hidden, d.inter, g, gu_grouped ? tgu : nullptr, r2);
-  if (e == hipSuccess) e = proj(UNO_PROJ_UP, a, d.hidden, d.inter, u, gu_grouped ? tgu + d.r : nullptr, r2);
-  if (e == hipSuccess) {
+  // gate, up and SwiGLU in one GEMM when T of both adapters sits side by side
+  // (or there is no adapter); else two projections and the SwiGLU kernel
+  SwigluArgs sw{};
+  sw.M = rows;
+  sw.N = d.inter;
+  sw.K = d.hidden;
+  sw.r = lora ? d.r : 0;
+  sw.x = a;
+  sw.ldx = d.hidden;
+  sw.wg = d.w->w[UNO_PROJ_GATE];
+  sw.wu = d.w->w[UNO_PROJ_UP];
+  sw.ldw = d.hidden;
+  sw.bg = d.w->b[UNO_PROJ_GATE];
+  sw.bu = d.w->b[UNO_PROJ_UP];
+  sw.ldb = d.r;
+  sw.t = tgu;
+  sw.ldt = r2;
+  sw.y = g;
+  sw.ldy = d.inter;
+  const bool fused = (!lora || gu_grouped) && swiglu_fused_ok(sw);
+  if (e == hipSuccess && fused) e = launch_gated_lora_swiglu(sw, stream);
+  if (e == hipSuccess && !fused) e = proj(UNO_PROJ_GATE, a, d.hidden, d.inter, g, gu_grouped ? tgu : nullptr, r2);
+  if (e == hipSuccess && !fused) e = proj(UNO_PROJ_UP, a, d.hidden, d.inter, u, gu_grouped ? tgu + d.r : nullptr, r2);
+  if (e == hipSuccess && !fused) {
     SiluMulArgs sa{};
     sa.rows = rows;
     sa.dim = d.inter;

@@ -62,6 +62,9 @@ struct GemmParams {
   uint16_t* y; int64_t ldy;            // MODE 0 output
   int y_vec;                           // 8-byte stores allowed (ldy % 4 == 0, y 8-byte aligned)
   float* part;                         // MODE 1 output: fp32 [split][M][N]
+  const uint16_t* w2;                  // MODE 2: up-projection weights (gate in w), ld ldw
+  const uint16_t* b2;                  // MODE 2: up-projection adapter B (gate in b), ld ldb
+  int kr;                              // MODE 2: K-tiles per adapter (r / 64); t = [t_gate | t_up]
 };
 
 // Output tile of linear index `tile`.  Mode 1: column-major (M-tiles
@@ -107,7 +110,17 @@ __device__ __forceinline__ void split_range(const GemmParams& p, int bk, int kt_
 
 // BM x BN block tile, WM x WN waves, P K-tiles of register prefetch, DBF:
 // double-buffer the MFMA fragments across k-steps, MODE: 0 = bf16 out,
-// 1 = fp32 split-K partials.
+// 1 = fp32 split-K partials, 2 = SwiGLU of a gate and an up projection
+// (below).
+// MODE 2 (FAST only, BN = 256 on 8 waves): a block tile covers BN / 2
+// features of both projections.  Its weight rows come in four bands of 64:
+// gate rows of features n0 .. n0 + 63, up rows of the same features, then the
+// same for n0 + 64 .. n0 + 127, so each wave's 128 rows hold 64 gate and the
+// 64 matching up rows, and fragment i + FN / 2 of a lane sits at the same
+// feature as fragment i.  The adapter columns run over t = [t_gate | t_up]
+// (2r of them): gate rows read B_gate against t_gate and zeros (buffer reads
+// past the end) against t_up, up rows the reverse.  The epilogue writes
+// bf16(silu(g) * u) from the fp32 accumulators.
 // FAST: every K-tile is whole (K1 and K2 multiples of 64) and every operand
 // spans < 2 GB, so tiles are read with buffer loads: a per-lane row offset
 // fixed for the whole K loop plus a scalar offset (chunk group, K-tile), with
@@ -136,7 +149,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p
   const int tile = (p.xcd_remap && (ntiles & 7) == 0) ? (bid & 7) * (ntiles >> 3) + (bid >> 3) : bid;
   int tm, tn;
   tile_coords(p, tile, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  static_assert(MODE != 2 || (FAST && BN == 256 && WM * WN == 8), "SwiGLU tiles: 256 weight rows, 8 waves");
+  const int m0 = tm * BM, n0 = tn * (MODE == 2 ? BN / 2 : BN);   // MODE 2: first feature of the tile
 
   const int Ktot = p.K1 + p.K2;
   const int kt_total = (Ktot + kBK - 1) / kBK;
@@ -199,6 +213,10 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.x), 0, int(int64_t(p.M) * p.ldx * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t rt =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.t), 0, int(int64_t(p.M) * p.ldt * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw2 =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.w2), 0, int(int64_t(p.N) * p.ldw * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb2 =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.b2), 0, int(int64_t(p.N) * p.ldb * 2), 0x00020000);
   uint32_t va1 = 0, va2 = 0, vb1 = 0, vb2 = 0, slot = 0;
   int kt1 = 0;
   if constexpr (FAST) {
@@ -218,7 +236,24 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p
     const bool first = kt < kt1;
     const int q = i < LA ? i : i - LA;
     const int ktl = first ? kt : kt - kt1;
-    if (i < LA) {
+    if (i < LA && MODE == 2) {
+      // chunk group i: band i / 2 (features n0 + 64 (i / 2) ..), gate rows for
+      // even i, up rows for odd i; an adapter K-tile belongs to the gate
+      // (ktl < kr) or to the up projection, the other rows read zeros
+      const bool up = (i & 1) != 0;
+      const bool half = ktl >= p.kr;
+      const bool valid = first || (half == up);
+      const int step = first ? RPG * int(p.ldw) * 2 : RPG * int(p.ldb) * 2;
+      const int kcol = (first || !half) ? ktl : ktl - p.kr;
+      uint32_t off = (first ? va1 : va2) + uint32_t((i >> 1) * step + kcol * kBK * 2);
+      off = (live && valid) ? off : 0x80000000u;
+      if (up)
+        dst[i] = __builtin_bit_cast(u32x4, first ? __builtin_amdgcn_raw_buffer_load_b128(rw2, off, 0, 0)
+                                                 : __builtin_amdgcn_raw_buffer_load_b128(rb2, off, 0, 0));
+      else
+        dst[i] = __builtin_bit_cast(u32x4, first ? __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0)
+                                                 : __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
+    } else if (i < LA) {
       const int step = first ? RPG * int(p.ldw) * 2 : RPG * int(p.ldb) * 2;
       uint32_t off = (first ? va1 : va2) + uint32_t(q * step + ktl * kBK * 2);
       off = live ? off : 0x80000000u;   // past the split: out of range, reads 0
@@ -339,6 +374,35 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p
     }
   }
 
+  if constexpr (MODE == 2) {
+    // fragment i (gate) and i + FN / 2 (up) of a lane hold the same features
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int m = m0 + wm * TM + j * 32 + lrow;
+      if (m >= p.M) continue;
+#pragma unroll
+      for (int i = 0; i < FN / 2; ++i) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * (TN / 2) + i * 32 + 8 * g + 4 * lhalf;
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float gv = acc[i][j][4 * g + e], uv = acc[i + FN / 2][j][4 * g + e];
+            o[e] = gv / (1.f + expf(-gv)) * uv;
+          }
+          uint16_t* dst = p.y + int64_t(m) * p.ldy + n;
+          if (p.y_vec && n + 3 < p.N) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+          } else {
+            for (int e = 0; e < 4; ++e)
+              if (n + e < p.N) dst[e] = f32_to_bf16(o[e]);
+          }
+        }
+      }
+    }
+    return;
+  }
   // epilogue: lane owns column m = lrow of each fragment, rows n = 8g + 4*lhalf + e
 #pragma unroll
   for (int j = 0; j < FM; ++j) {
@@ -532,6 +596,35 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_dl_kernel(GemmParams p) 
   // drain the trailing (unused) prefetches before the workgroup exits
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 
+  if constexpr (MODE == 2) {
+    // fragment i (gate) and i + FN / 2 (up) of a lane hold the same features
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int m = m0 + wm * TM + j * 32 + lrow;
+      if (m >= p.M) continue;
+#pragma unroll
+      for (int i = 0; i < FN / 2; ++i) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * (TN / 2) + i * 32 + 8 * g + 4 * lhalf;
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float gv = acc[i][j][4 * g + e], uv = acc[i + FN / 2][j][4 * g + e];
+            o[e] = gv / (1.f + expf(-gv)) * uv;
+          }
+          uint16_t* dst = p.y + int64_t(m) * p.ldy + n;
+          if (p.y_vec && n + 3 < p.N) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+          } else {
+            for (int e = 0; e < 4; ++e)
+              if (n + e < p.N) dst[e] = f32_to_bf16(o[e]);
+          }
+        }
+      }
+    }
+    return;
+  }
   // epilogue: lane owns column m = lrow of each fragment, rows n = 8g + 4*lhalf + e
 #pragma unroll
   for (int j = 0; j < FM; ++j) {
@@ -702,8 +795,9 @@ hipError_t launch_tile_k(GemmParams p, int splits, hipStream_t stream, const cha
     if (e != hipSuccess) return e;
     configured = true;
   }
+  constexpr int TILE_N = MODE == 2 ? BN / 2 : BN;   // MODE 2: features per tile
   p.tiles_m = (p.M + BM - 1) / BM;
-  p.tiles_n = (p.N + BN - 1) / BN;
+  p.tiles_n = (p.N + TILE_N - 1) / TILE_N;
   {
     const char* env = getenv("UNO_GEMM_XCD");   // tuning override: 0 no remap, 1 column bands, 2 (default) 2D groups
     p.xcd_remap = env ? atoi(env) : 2;
@@ -909,6 +1003,47 @@ hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(lora_gate_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream,
                      static_cast<const float*>(a.part), dc.splits, int(a.M), int(a.n), a.gate, a.lora_scale, a.t);
   return hipGetLastError();
+}
+
+namespace {
+
+GemmParams swiglu_params(const SwigluArgs& a) {
+  GemmParams g{};
+  const bool lora = a.r > 0;
+  g.M = int(a.M);
+  g.N = int(a.N);
+  g.K1 = int(a.K);
+  g.K2 = lora ? int(2 * a.r) : 0;
+  g.x = static_cast<const uint16_t*>(a.x);
+  g.ldx = a.ldx;
+  g.w = static_cast<const uint16_t*>(a.wg);
+  g.w2 = static_cast<const uint16_t*>(a.wu);
+  g.ldw = a.ldw;
+  g.t = lora ? static_cast<const uint16_t*>(a.t) : g.x;
+  g.ldt = lora ? a.ldt : a.ldx;
+  g.b = lora ? static_cast<const uint16_t*>(a.bg) : g.w;
+  g.b2 = lora ? static_cast<const uint16_t*>(a.bu) : g.w2;
+  g.ldb = lora ? a.ldb : a.ldw;
+  g.kr = lora ? int(a.r / kBK) : 0;
+  g.y = static_cast<uint16_t*>(a.y);
+  g.ldy = a.ldy;
+  g.y_vec = (a.ldy % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.y) & 7u) == 0);
+  return g;
+}
+
+}  // namespace
+
+bool swiglu_fused_ok(const SwigluArgs& a) {
+  if (a.K % kBK != 0 || a.r % kBK != 0) return false;
+  if (a.r > 0 && (!a.t || a.ldt < 2 * a.r || !a.bg || !a.bu)) return false;
+  return fast_ok(swiglu_params(a), 256, 256);
+}
+
+// gate and up projections in one launch (MODE 2 of gemm_bf16_kernel), y =
+// bf16(silu(g) * u); the 256 x 256 tile with 8 waves on the buffer-load path
+hipError_t launch_gated_lora_swiglu(const SwigluArgs& a, hipStream_t stream) {
+  if (!swiglu_fused_ok(a)) return hipErrorNotSupported;
+  return launch_tile_k<256, 256, 4, 2, 1, 0, 2, 1>(swiglu_params(a), 1, stream, "uno_gemm_bf16");
 }
 
 hipError_t launch_gated_lora(const GatedLoraArgs& a, hipStream_t stream) {

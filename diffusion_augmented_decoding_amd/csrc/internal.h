@@ -90,6 +90,23 @@ size_t lora_down_part_bytes(int64_t M, int64_t n, int64_t K);
 hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t stream);
 hipError_t launch_gated_lora(const GatedLoraArgs& a, hipStream_t stream);
 
+// bf16 gate and up projections with the SwiGLU product fused into the GEMM
+// epilogue: y[m][f] = bf16(silu(g) * u), g = x Wg^T + t_g Bg^T, u = x Wu^T +
+// t_u Bu^T in fp32, t = [t_g | t_u] (M x 2r, both adapters' T side by side,
+// as one grouped LoRA-down writes them).  N = features.  Needs K and r
+// multiples of 64 and operands within the buffer-load window
+// (swiglu_fused_ok); the caller falls back to two projections otherwise.
+struct SwigluArgs {
+  int64_t M, N, K, r;
+  const void* x; int64_t ldx;
+  const void* wg; const void* wu; int64_t ldw;     // [N][K] each
+  const void* bg; const void* bu; int64_t ldb;     // [N][r] each
+  const void* t; int64_t ldt;                      // [M][2r]; unused when r == 0
+  void* y; int64_t ldy;
+};
+bool swiglu_fused_ok(const SwigluArgs& a);
+hipError_t launch_gated_lora_swiglu(const SwigluArgs& a, hipStream_t stream);
+
 // ---------------------------------------------------------------- tree attention
 struct TreeAttnArgs {
   int batch, n_tree, ctx, n_heads, n_kv, head_dim;

@@ -232,6 +232,10 @@ def _layer_ref(c, seqs):
     (3, 16, 300, 512, 1024, 8, 2, 32, False),
     (3, 16, 300, 512, 1024, 8, 2, 32, True),
     (1, 2, 0, 128, 384, 2, 1, 8, False),
+    # rank a multiple of 64 with adapters back to back: gate, up and SwiGLU run
+    # as one GEMM (ragged feature tile: 1088 = 8.5 x 128)
+    (2, 8, 136, 512, 1088, 8, 2, 64, True),
+    (2, 8, 136, 512, 1088, 8, 2, 64, False),
 ])
 def test_decoder_layer(gpu_lib, batch, block, ctx, hidden, inter, nh, nkv, r, packed):
     say(f"decoder layer B={batch} block={block} ctx={ctx} hidden={hidden} inter={inter} H={nh}/{nkv} r={r} "
@@ -239,6 +243,19 @@ def test_decoder_layer(gpu_lib, batch, block, ctx, hidden, inter, nh, nkv, r, pa
     c = workloads.decoder_layer_case(batch, block, ctx, hidden, inter, nh, nkv, r, seed=batch + ctx)
     got = _run_layer(gpu_lib, c, packed=packed)
     rows, ref = _layer_ref(c, list(range(batch)))
+    err = row_relerr(got[rows], ref)
+    say(f"  row rel err {err:.3g}")
+    assert err <= 2e-2
+
+
+def test_decoder_layer_without_adapters(gpu_lib):
+    """No gate vector: every row takes the AR weights only (the fused
+    gate/up/SwiGLU GEMM without adapter columns); the oracle sees all gates 0."""
+    say("decoder layer without adapters B=2 block=8 ctx=136 hidden=512 inter=1088")
+    c = workloads.decoder_layer_case(2, 8, 136, 512, 1088, 8, 2, 64, seed=11)
+    got = _run_layer(gpu_lib, c, gate=False)
+    c0 = dict(c, gate=np.zeros_like(c["gate"]))
+    rows, ref = _layer_ref(c0, [0, 1])
     err = row_relerr(got[rows], ref)
     say(f"  row rel err {err:.3g}")
     assert err <= 2e-2
