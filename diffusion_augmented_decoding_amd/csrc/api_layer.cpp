@@ -93,8 +93,8 @@ hipError_t launch_decoder_layer(const DecoderLayerArgs& d, hipStream_t stream) {
   void* u = ws + L.u;
   void* h = d.h;
 
-  auto proj = [&](int p, const void* x, int64_t K, int64_t N, void* y, const uint16_t* t_pre = nullptr,
-                  int64_t ldt_pre = 0) {
+  auto proj_args = [&](int p, const void* x, int64_t K, int64_t N, void* y, const uint16_t* t_pre = nullptr,
+                       int64_t ldt_pre = 0) {
     GatedLoraArgs ga{};
     ga.dtype = UNO_BF16;
     ga.M = rows;
@@ -117,7 +117,11 @@ hipError_t launch_decoder_layer(const DecoderLayerArgs& d, hipStream_t stream) {
     ga.ldt_pre = ldt_pre;
     ga.ws = ws + L.lora;
     ga.ws_bytes = d.ws_bytes - L.lora;
-    return launch_gated_lora(ga, stream);
+    return ga;
+  };
+  auto proj = [&](int p, const void* x, int64_t K, int64_t N, void* y, const uint16_t* t_pre = nullptr,
+                  int64_t ldt_pre = 0) {
+    return launch_gated_lora(proj_args(p, x, K, N, y, t_pre, ldt_pre), stream);
   };
   auto norm = [&](const void* res, const void* weight, void* out) {
     RmsNormArgs na{};
@@ -184,8 +188,17 @@ hipError_t launch_decoder_layer(const DecoderLayerArgs& d, hipStream_t stream) {
   hipError_t e = norm(nullptr, d.w->attn_norm, a);
   if (e == hipSuccess && qkv_grouped) e = group_down(UNO_PROJ_Q, 3, a, tqkv);
   if (e == hipSuccess) e = proj(UNO_PROJ_Q, a, d.hidden, qd, q, qkv_grouped ? tqkv : nullptr, r3);
-  if (e == hipSuccess) e = proj(UNO_PROJ_K, a, d.hidden, kvd, k, qkv_grouped ? tqkv + d.r : nullptr, r3);
-  if (e == hipSuccess) e = proj(UNO_PROJ_V, a, d.hidden, kvd, v, qkv_grouped ? tqkv + 2 * d.r : nullptr, r3);
+  if (e == hipSuccess) {
+    // k and v: one launch over both outputs where the shapes allow
+    const GatedLoraArgs ak = proj_args(UNO_PROJ_K, a, d.hidden, kvd, k, qkv_grouped ? tqkv + d.r : nullptr, r3);
+    const GatedLoraArgs av = proj_args(UNO_PROJ_V, a, d.hidden, kvd, v, qkv_grouped ? tqkv + 2 * d.r : nullptr, r3);
+    if (gated_lora_pair_ok(ak, av)) {
+      e = launch_gated_lora_pair(ak, av, stream);
+    } else {
+      e = launch_gated_lora(ak, stream);
+      if (e == hipSuccess) e = launch_gated_lora(av, stream);
+    }
+  }
   if (e == hipSuccess) e = rope_qk();
   if (e == hipSuccess) {
     TreeAttnArgs ta{};

@@ -65,6 +65,11 @@ struct GemmParams {
   const uint16_t* w2;                  // MODE 2: up-projection weights (gate in w), ld ldw
   const uint16_t* b2;                  // MODE 2: up-projection adapter B (gate in b), ld ldb
   int kr;                              // MODE 2: K-tiles per adapter (r / 64); t = [t_gate | t_up]
+  // MODE 0, two segments: output columns from seg_n on come from (w2, b2, t +
+  // t2_off) and go to y2 (same ldy), column n - seg_n; 0 = one segment
+  int seg_n;
+  int64_t t2_off;
+  uint16_t* y2;
 };
 
 // Output tile of linear index `tile`.  Mode 1: column-major (M-tiles
@@ -128,7 +133,8 @@ __device__ __forceinline__ void split_range(const GemmParams& p, int bk, int kt_
 // reading zeros.  No per-load address arithmetic or masking is left in the
 // loop, and the LDS slot of each chunk is a fixed offset.
 template <int BM, int BN, int WM, int WN, int P, int DBF, int MODE, int FAST>
-__global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p) {
+__global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p_in) {
+  GemmParams p = p_in;
   constexpr int NT = WM * WN * kWave;
   constexpr int TM = BM / WM, TN = BN / WN;        // wave tile
   constexpr int FM = TM / 32, FN = TN / 32;        // 32x32 fragments per wave
@@ -150,7 +156,23 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p
   int tm, tn;
   tile_coords(p, tile, tm, tn);
   static_assert(MODE != 2 || (FAST && BN == 256 && WM * WN == 8), "SwiGLU tiles: 256 weight rows, 8 waves");
-  const int m0 = tm * BM, n0 = tn * (MODE == 2 ? BN / 2 : BN);   // MODE 2: first feature of the tile
+  const int m0 = tm * BM;
+  int n0 = tn * (MODE == 2 ? BN / 2 : BN);   // MODE 2: first feature of the tile
+  if constexpr (MODE == 0 && FAST) {
+    // two segments (tiles never straddle seg_n): rebase onto the second
+    if (p.seg_n > 0) {
+      if (n0 >= p.seg_n) {
+        p.w = p.w2;
+        p.b = p.b2;
+        p.t = p.t + p.t2_off;
+        p.y = p.y2;
+        n0 -= p.seg_n;
+        p.N -= p.seg_n;
+      } else {
+        p.N = p.seg_n;
+      }
+    }
+  }
 
   const int Ktot = p.K1 + p.K2;
   const int kt_total = (Ktot + kBK - 1) / kBK;
@@ -1044,6 +1066,62 @@ bool swiglu_fused_ok(const SwigluArgs& a) {
 hipError_t launch_gated_lora_swiglu(const SwigluArgs& a, hipStream_t stream) {
   if (!swiglu_fused_ok(a)) return hipErrorNotSupported;
   return launch_tile_k<256, 256, 4, 2, 1, 0, 2, 1>(swiglu_params(a), 1, stream, "uno_gemm_bf16");
+}
+
+namespace {
+
+GemmParams lora_params(const GatedLoraArgs& a, const uint16_t* t, int64_t ldt) {
+  const bool lora = a.r > 0 && a.gate != nullptr;
+  GemmParams g{};
+  g.M = int(a.M);
+  g.N = int(a.N);
+  g.K1 = int(a.K);
+  g.K2 = lora ? int(a.r) : 0;
+  g.x = static_cast<const uint16_t*>(a.x);
+  g.ldx = a.ldx;
+  g.w = static_cast<const uint16_t*>(a.w);
+  g.ldw = a.ldw;
+  g.t = lora ? t : g.x;
+  g.ldt = lora ? ldt : a.ldx;
+  g.b = lora ? static_cast<const uint16_t*>(a.b) : g.w;
+  g.ldb = lora ? a.ldb : a.ldw;
+  g.y = static_cast<uint16_t*>(a.y);
+  g.ldy = a.ldy;
+  g.y_vec = (a.ldy % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.y) & 7u) == 0);
+  return g;
+}
+
+}  // namespace
+
+// Two projections of one input with the same shapes (k and v), each with T
+// computed by the caller, as one launch over 2N output columns.
+bool gated_lora_pair_ok(const GatedLoraArgs& a, const GatedLoraArgs& b) {
+  const bool la = a.r > 0 && a.gate, lb = b.r > 0 && b.gate;
+  if (a.dtype != UNO_BF16 || b.dtype != UNO_BF16 || la != lb) return false;
+  if (a.M != b.M || a.N != b.N || a.K != b.K || a.r != b.r || a.x != b.x || a.ldx != b.ldx || a.ldw != b.ldw ||
+      a.ldb != b.ldb || a.ldy != b.ldy || a.ldt_pre != b.ldt_pre || a.gate != b.gate)
+    return false;
+  if (la && (!a.t_pre || !b.t_pre)) return false;
+  if (a.M < 2048 || a.N % 128 != 0 || a.N * 2 > 0x7fffffff) return false;
+  const GemmParams ga = lora_params(a, static_cast<const uint16_t*>(a.t_pre), a.ldt_pre);
+  const GemmParams gb = lora_params(b, static_cast<const uint16_t*>(b.t_pre), b.ldt_pre);
+  return fast_ok(ga, 256, 128) && fast_ok(gb, 256, 128) && ga.y_vec && gb.y_vec;
+}
+
+// Measured at 4096 rows, N = 1024 each (k and v): 256 x 128 tiles on 8 waves
+// (2-deep prefetch), 256 tiles over 2N, 76 us against 2 x 53 us for two
+// launches on 128 x 128 tiles.
+hipError_t launch_gated_lora_pair(const GatedLoraArgs& a, const GatedLoraArgs& b, hipStream_t stream) {
+  if (!gated_lora_pair_ok(a, b)) return hipErrorNotSupported;
+  const bool lora = a.r > 0 && a.gate;
+  GemmParams g = lora_params(a, static_cast<const uint16_t*>(a.t_pre), a.ldt_pre);
+  g.N = int(2 * a.N);
+  g.seg_n = int(a.N);
+  g.w2 = static_cast<const uint16_t*>(b.w);
+  g.b2 = lora ? static_cast<const uint16_t*>(b.b) : g.w2;
+  g.t2_off = lora ? static_cast<const uint16_t*>(b.t_pre) - static_cast<const uint16_t*>(a.t_pre) : 0;
+  g.y2 = static_cast<uint16_t*>(b.y);
+  return launch_tile_k<256, 128, 4, 2, 2, 0, 0, 1>(g, 1, stream, "uno_gemm_bf16");
 }
 
 hipError_t launch_gated_lora(const GatedLoraArgs& a, hipStream_t stream) {

@@ -89,6 +89,10 @@ struct LoraDownArgs {
 size_t lora_down_part_bytes(int64_t M, int64_t n, int64_t K);
 hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t stream);
 hipError_t launch_gated_lora(const GatedLoraArgs& a, hipStream_t stream);
+// Two bf16 projections of the same input and shapes (k and v), T of each
+// computed by the caller (t_pre), as one GEMM launch over both outputs.
+bool gated_lora_pair_ok(const GatedLoraArgs& a, const GatedLoraArgs& b);
+hipError_t launch_gated_lora_pair(const GatedLoraArgs& a, const GatedLoraArgs& b, hipStream_t stream);
 
 // bf16 gate and up projections with the SwiGLU product fused into the GEMM
 // epilogue: y[m][f] = bf16(silu(g) * u), g = x Wg^T + t_g Bg^T, u = x Wu^T +

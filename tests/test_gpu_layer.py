@@ -248,6 +248,20 @@ def test_decoder_layer(gpu_lib, batch, block, ctx, hidden, inter, nh, nkv, r, pa
     assert err <= 2e-2
 
 
+def test_decoder_layer_2048_rows_sampled(gpu_lib):
+    """2048 rows (64 sequences x 32) with adapters back to back: k and v run
+    as one two-segment GEMM and gate/up/SwiGLU as one GEMM; the oracle
+    recomputes 2 sampled sequences."""
+    say("decoder layer B=64 block=16 ctx=40 hidden=512 inter=1024 H=8/2 r=64 (sampled)")
+    c = workloads.decoder_layer_case(64, 16, 40, 512, 1024, 8, 2, 64, seed=21)
+    got = _run_layer(gpu_lib, c, packed=True)
+    assert np.all(np.isfinite(got))
+    rows, ref = _layer_ref(c, [3, 60])
+    err = row_relerr(got[rows], ref)
+    say(f"  row rel err {err:.3g}")
+    assert err <= 2e-2
+
+
 def test_decoder_layer_without_adapters(gpu_lib):
     """No gate vector: every row takes the AR weights only (the fused
     gate/up/SwiGLU GEMM without adapter columns); the oracle sees all gates 0."""
