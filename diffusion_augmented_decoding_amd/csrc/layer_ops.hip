@@ -29,25 +29,39 @@ __device__ __forceinline__ u32x4 pack8(const float (&x)[8]) {
   return u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
 }
 
-// One workgroup per row.  RES: s = x + res is rounded to bf16 and stored to
-// sum_out (which may alias x), and the rounded s is what gets normalised.
-// out may be null (residual add only).
-template <bool RES>
+// One workgroup per row, VPT 8-element vectors per thread (dim <= 256 * 8 *
+// VPT).  RES: s = x + res is rounded to bf16 and stored to sum_out (which may
+// alias x), and the rounded s is what gets normalised.  out may be null
+// (residual add only).  The weight vectors are loaded with the row, so the
+// only dependent step after the loads is the reduction.
+template <bool RES, int VPT>
 __global__ __launch_bounds__(kNormThreads) void rms_norm_kernel(RmsNormArgs a) {
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
   const int nvec = a.dim / 8;
   const uint16_t* xr = static_cast<const uint16_t*>(a.x) + row * a.ldx;
-  float v[kNormMaxVec][8];
-  float ss = 0.f;
+  const uint16_t* wr = static_cast<const uint16_t*>(a.weight);
+  const bool norm = a.out != nullptr;
+  u32x4 xv[VPT], rv[VPT], wv[VPT];
 #pragma unroll
-  for (int c = 0; c < kNormMaxVec; ++c) {
+  for (int c = 0; c < VPT; ++c) {
     const int i = tid + c * kNormThreads;
     if (i < nvec) {
-      unpack8(*reinterpret_cast<const u32x4*>(xr + 8 * i), v[c]);
+      xv[c] = *reinterpret_cast<const u32x4*>(xr + 8 * i);
+      if constexpr (RES) rv[c] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.res) + row * a.ldr + 8 * i);
+      if (norm) wv[c] = *reinterpret_cast<const u32x4*>(wr + 8 * i);
+    }
+  }
+  float v[VPT][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < VPT; ++c) {
+    const int i = tid + c * kNormThreads;
+    if (i < nvec) {
+      unpack8(xv[c], v[c]);
       if constexpr (RES) {
         float y[8];
-        unpack8(*reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.res) + row * a.ldr + 8 * i), y);
+        unpack8(rv[c], y);
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[c][e] = bf16_to_f32(f32_to_bf16(v[c][e] + y[e]));
         *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.sum_out) + row * a.lds + 8 * i) = pack8(v[c]);
@@ -56,7 +70,7 @@ __global__ __launch_bounds__(kNormThreads) void rms_norm_kernel(RmsNormArgs a) {
       for (int e = 0; e < 8; ++e) ss = fmaf(v[c][e], v[c][e], ss);
     }
   }
-  if (a.out == nullptr) return;
+  if (!norm) return;
   ss = wave_sum(ss);
   __shared__ float red[kNormThreads / kWave];
   if ((tid & (kWave - 1)) == 0) red[tid / kWave] = ss;
@@ -65,14 +79,13 @@ __global__ __launch_bounds__(kNormThreads) void rms_norm_kernel(RmsNormArgs a) {
 #pragma unroll
   for (int w = 0; w < kNormThreads / kWave; ++w) tot += red[w];
   const float rs = 1.f / sqrtf(tot / float(a.dim) + a.eps);
-  const uint16_t* wr = static_cast<const uint16_t*>(a.weight);
   uint16_t* orow = static_cast<uint16_t*>(a.out) + row * a.ldo;
 #pragma unroll
-  for (int c = 0; c < kNormMaxVec; ++c) {
+  for (int c = 0; c < VPT; ++c) {
     const int i = tid + c * kNormThreads;
     if (i < nvec) {
       float w[8];
-      unpack8(*reinterpret_cast<const u32x4*>(wr + 8 * i), w);
+      unpack8(wv[c], w);
       float o[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = v[c][e] * rs * w[e];
@@ -106,6 +119,51 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeArgs a) {
   }
 }
 
+// Vectorised rotary embedding (x, x2 8-byte aligned, leading dimensions
+// multiples of 4), one workgroup per row: the 64 angles of the row are formed
+// once, in double precision, by the first 64 threads and shared through LDS;
+// then thread t rotates pairs 4 (t % 16) .. + 3 of heads t / 16, t / 16 + 16,
+// ... with 8-byte loads and stores of x_i and x_{i+64}.
+__global__ __launch_bounds__(256) void rope_vec_kernel(RopeArgs a) {
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  __shared__ float cs_s[64], sn_s[64];
+  if (tid < 64) {
+    const double inv_freq = exp(-double(tid) / 64.0 * log(double(a.theta)));
+    double s, c;
+    sincos(double(a.positions[row]) * inv_freq, &s, &c);
+    cs_s[tid] = float(c);
+    sn_s[tid] = float(s);
+  }
+  __syncthreads();
+  const int i0 = 4 * (tid & 15), h0 = tid >> 4;
+  float cs[4], sn[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    cs[j] = cs_s[i0 + j];
+    sn[j] = sn_s[i0 + j];
+  }
+  auto rotate = [&](uint16_t* p) {
+    const uint2 lo = *reinterpret_cast<const uint2*>(p + i0), hi = *reinterpret_cast<const uint2*>(p + 64 + i0);
+    const float x1[4] = {bf16_lo(lo.x), bf16_hi(lo.x), bf16_lo(lo.y), bf16_hi(lo.y)};
+    const float x2[4] = {bf16_lo(hi.x), bf16_hi(hi.x), bf16_lo(hi.y), bf16_hi(hi.y)};
+    float o1[4], o2[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o1[j] = x1[j] * cs[j] - x2[j] * sn[j];
+      o2[j] = x2[j] * cs[j] + x1[j] * sn[j];
+    }
+    *reinterpret_cast<uint2*>(p + i0) = make_uint2(pack_bf16x2(o1[0], o1[1]), pack_bf16x2(o1[2], o1[3]));
+    *reinterpret_cast<uint2*>(p + 64 + i0) = make_uint2(pack_bf16x2(o2[0], o2[1]), pack_bf16x2(o2[2], o2[3]));
+  };
+  uint16_t* xr = static_cast<uint16_t*>(a.x) + row * a.ldx;
+  for (int h = h0; h < a.n_heads; h += 16) rotate(xr + h * 128);
+  if (a.x2) {
+    uint16_t* xr2 = static_cast<uint16_t*>(a.x2) + row * a.ldx2;
+    for (int h = h0; h < a.n_heads2; h += 16) rotate(xr2 + h * 128);
+  }
+}
+
 // out = silu(g) * u = g / (1 + e^-g) * u, 8 elements per thread.
 __global__ __launch_bounds__(256) void silu_mul_kernel(SiluMulArgs a) {
   const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
@@ -125,18 +183,34 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(SiluMulArgs a) {
 
 int rms_norm_max_dim() { return kNormThreads * 8 * kNormMaxVec; }
 
+template <bool RES>
+static hipError_t launch_norm_vpt(const RmsNormArgs& a, hipStream_t stream) {
+  const int vpt = (a.dim / 8 + kNormThreads - 1) / kNormThreads;
+  const dim3 grid(unsigned(a.rows)), block(kNormThreads);
+  if (vpt <= 1)
+    hipLaunchKernelGGL((rms_norm_kernel<RES, 1>), grid, block, 0, stream, a);
+  else if (vpt <= 2)
+    hipLaunchKernelGGL((rms_norm_kernel<RES, 2>), grid, block, 0, stream, a);
+  else if (vpt <= 4)
+    hipLaunchKernelGGL((rms_norm_kernel<RES, 4>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((rms_norm_kernel<RES, kNormMaxVec>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_rms_norm(const RmsNormArgs& a, hipStream_t stream) {
   ProfileScope ps(a.res ? "uno_add_rms_norm" : "uno_rms_norm", stream);
-  if (a.res)
-    hipLaunchKernelGGL(rms_norm_kernel<true>, dim3(unsigned(a.rows)), dim3(kNormThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(rms_norm_kernel<false>, dim3(unsigned(a.rows)), dim3(kNormThreads), 0, stream, a);
-  return hipGetLastError();
+  return a.res ? launch_norm_vpt<true>(a, stream) : launch_norm_vpt<false>(a, stream);
 }
 
 hipError_t launch_rope(const RopeArgs& a, hipStream_t stream) {
   ProfileScope ps("uno_rope", stream);
-  hipLaunchKernelGGL(rope_kernel, dim3(unsigned(a.rows)), dim3(256), 0, stream, a);
+  auto vec_ok = [](const void* p, int64_t ld) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0 && ld % 4 == 0; };
+  const bool vec = vec_ok(a.x, a.ldx) && (!a.x2 || vec_ok(a.x2, a.ldx2));
+  if (vec)
+    hipLaunchKernelGGL(rope_vec_kernel, dim3(unsigned(a.rows)), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(rope_kernel, dim3(unsigned(a.rows)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

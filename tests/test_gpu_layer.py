@@ -93,6 +93,25 @@ def test_rope(gpu_lib, rows, heads):
     assert np.array_equal(got[0], _f32(x)[0].reshape(heads, 128))
 
 
+def test_rope_unaligned_rows(gpu_lib):
+    """Rows 130 elements apart (not a multiple of 4): the element-wise kernel
+    instead of the 8-byte one; the bytes between rows stay untouched."""
+    say("rope rows=9 heads=1 ldx=130")
+    import torch
+    rng = workloads.rng_for(9, 1, 3)
+    x = workloads.bf16_bits(rng.standard_normal((9, 128), dtype=np.float32))
+    pos = rng.integers(0, 131072, 9).astype(np.int32)
+    buf = torch.zeros((9, 130), dtype=torch.bfloat16, device="cuda")
+    buf[:, :128] = _bits_dev(x)
+    buf[:, 128:] = 7.0
+    gpu_lib.rope(buf[:, :128], to_dev(pos), 1.0e6)
+    torch.cuda.synchronize()
+    ref = oracle.rope(_f32(x).reshape(9, 1, 128), pos, 1.0e6)
+    got = to_host(buf[:, :128]).reshape(9, 1, 128)
+    assert row_relerr(got, ref) <= 2e-2
+    assert torch.all(buf[:, 128:] == 7.0)
+
+
 # ---------------------------------------------------------------- silu * mul
 @pytest.mark.parametrize("rows,dim", [(3, 8), (100, 12288), (17, 1000)])
 def test_silu_mul(gpu_lib, rows, dim):
