@@ -732,6 +732,25 @@ __global__ __launch_bounds__(256) void lora_gate_kernel(const float* __restrict_
   t[i] = f32_to_bf16(scale * s);
 }
 
+// The same, four consecutive elements per thread (r % 4 == 0): 16-byte
+// partial loads and an 8-byte store; the splits are summed in the same order.
+__global__ __launch_bounds__(256) void lora_gate4_kernel(const float* __restrict__ part, int splits, int M, int r,
+                                                         const uint8_t* __restrict__ gate, float scale,
+                                                         uint16_t* __restrict__ t) {
+  const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i >= int64_t(M) * r) return;
+  const int m = int(i / r);
+  if (gate[m] == 0) {
+    *reinterpret_cast<uint2*>(t + i) = make_uint2(0u, 0u);
+    return;
+  }
+  const int64_t plane = int64_t(M) * r;
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < splits; ++sp) s += *reinterpret_cast<const f32x4*>(part + sp * plane + i);
+  *reinterpret_cast<uint2*>(t + i) =
+      make_uint2(pack_bf16x2(scale * s[0], scale * s[1]), pack_bf16x2(scale * s[2], scale * s[3]));
+}
+
 // ------------------------------------------------------------------ fp32 path
 __global__ __launch_bounds__(256) void lora_down_f32_kernel(const float* __restrict__ x, int64_t ldx,
                                                             const float* __restrict__ a, int64_t lda,
@@ -1022,8 +1041,13 @@ hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int64_t n = a.M * a.n;
   ProfileScope ps("uno_lora_gate", stream);
-  hipLaunchKernelGGL(lora_gate_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream,
-                     static_cast<const float*>(a.part), dc.splits, int(a.M), int(a.n), a.gate, a.lora_scale, a.t);
+  // the vector form needs 4-element rows and 16-byte aligned partials / 8-byte aligned T
+  if (a.n % 4 == 0 && (reinterpret_cast<uintptr_t>(a.part) & 15u) == 0 && (reinterpret_cast<uintptr_t>(a.t) & 7u) == 0)
+    hipLaunchKernelGGL(lora_gate4_kernel, dim3(unsigned((n / 4 + 255) / 256)), dim3(256), 0, stream,
+                       static_cast<const float*>(a.part), dc.splits, int(a.M), int(a.n), a.gate, a.lora_scale, a.t);
+  else
+    hipLaunchKernelGGL(lora_gate_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream,
+                       static_cast<const float*>(a.part), dc.splits, int(a.M), int(a.n), a.gate, a.lora_scale, a.t);
   return hipGetLastError();
 }
 
