@@ -110,3 +110,21 @@ def test_layer_projection_full_size_sampled_rows(gpu_lib, proj):
     say(f"  row rel err {err:.3g}")
     assert err <= 2e-2
     assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("r", [256, 384])
+def test_grouped_adapter_ranks_at_decode_rows(gpu_lib, r):
+    """4096 rows (128 sequences x (16 clean + 16 noisy)) with the adapter ranks
+    of the grouped LoRA-down launches (gate|up: 2 x 128, q|k|v: 3 x 128), which
+    take the one-tile-wide LoRA-down kernels; 48 sampled rows against the
+    oracle."""
+    say(f"gated_lora grouped rank {r}: 4096 x 1024 x 4096")
+    c = workloads.gated_lora_case(4096, 1024, 4096, r, dtype="bf16", seed=3, tag=r,
+                                  gate=workloads.default_gate(4096, 16))
+    y = to_host(_run(gpu_lib, c))
+    rows = np.sort(np.random.default_rng(5).choice(4096, 48, replace=False))
+    assert set(c["gate"][rows].tolist()) == {0, 1}
+    err = row_relerr(y[rows], _ref(c, rows))
+    say(f"  row rel err {err:.3g}")
+    assert err <= 2e-2
+    assert np.all(np.isfinite(y))
