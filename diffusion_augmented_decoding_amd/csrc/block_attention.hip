@@ -155,6 +155,43 @@ __device__ __forceinline__ void read_vt(s16x4 (&t)[2][4], const uint32_t (&va)[2
   }
 }
 
+// The eight K fragments of a block (one per 16-dim step), issued together and
+// waited for once: one LDS round trip instead of one per fragment.
+__device__ __forceinline__ void read_k(bf16x8 (&kf)[8], const uint32_t (&ka)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %9\n\t"
+      "ds_read_b128 %2, %10\n\t"
+      "ds_read_b128 %3, %11\n\t"
+      "ds_read_b128 %4, %12\n\t"
+      "ds_read_b128 %5, %13\n\t"
+      "ds_read_b128 %6, %14\n\t"
+      "ds_read_b128 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3]), "=&v"(kf[4]), "=&v"(kf[5]), "=&v"(kf[6]),
+        "=&v"(kf[7])
+      : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(ka[4]), "v"(ka[5]), "v"(ka[6]), "v"(ka[7])
+      : "memory");
+}
+
+// x combined with the value of lane l ^ 32: v_permlane32_swap exchanges the
+// upper half of one register with the lower half of another, so swapping two
+// copies of x leaves each lane with x and its partner in the two registers
+// (no LDS round trip, unlike a cross-half shuffle).
+__device__ __forceinline__ void swap_halves(float& a, float& b) {
+  asm volatile("s_nop 4\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 4" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  float a = x, b = x;
+  swap_halves(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  float a = x, b = x;
+  swap_halves(a, b);
+  return a + b;
+}
+
 template <int kStages>
 __global__ __launch_bounds__(kThreads) void block_attn_kernel(TreeAttnArgs a, BlkPlan pl, float* part_o,
                                                               float2* part_ms) {
@@ -277,15 +314,19 @@ __global__ __launch_bounds__(kThreads) void block_attn_kernel(TreeAttnArgs a, Bl
       voff[half][db] = uint32_t(kKBytes + vr * 256 + (((d >> 3) ^ swz_v(vr)) << 4) + ((d & 7) << 1));
     }
 
+  uint32_t kcol[kHD / 16];   // this lane's K fragment bytes of step st inside a stage
+#pragma unroll
+  for (int st = 0; st < kHD / 16; ++st) kcol[st] = koff_row + uint32_t(((2 * st + lh) ^ (lrow & 15)) << 4);
+
   auto compute = [&](int stage, int j) {
     const uint32_t sb = lds_base + uint32_t(stage * kStageBytes);
     // S^T = K . Q^T
     bf16x8 kf[kHD / 16];
+    {
+      uint32_t ka[kHD / 16];
 #pragma unroll
-    for (int st = 0; st < kHD / 16; ++st) {
-      const int c = 2 * st + lh;
-      kf[st] = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-          uintptr_t(sb + koff_row + uint32_t((c ^ (lrow & 15)) << 4)));
+      for (int st = 0; st < kHD / 16; ++st) ka[st] = sb + kcol[st];
+      read_k(kf, ka);
     }
     f32x16 s;
 #pragma unroll
@@ -315,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void block_attn_kernel(TreeAttnArgs a, Bl
         bmax = ok ? fmaxf(bmax, s[e] * sc) : bmax;
       }
     }
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+    bmax = max_xor32(bmax);
     // Lazy rescaling: the running max m moves only when a score exceeds it by
     // more than kLazy (log2 units), so P = 2^(y - m) <= 2^kLazy, and the
     // accumulator is rescaled only in the rare blocks where some row's max moved.
@@ -346,7 +387,7 @@ __global__ __launch_bounds__(kThreads) void block_attn_kernel(TreeAttnArgs a, Bl
         psum += y[e];
       }
     }
-    psum += __shfl_xor(psum, 32);
+    psum = sum_xor32(psum);
     ssum += psum;
     bf16x8 pf[2];
 #pragma unroll
