@@ -112,17 +112,19 @@ def test_layer_projection_full_size_sampled_rows(gpu_lib, proj):
     assert np.all(np.isfinite(y))
 
 
-@pytest.mark.parametrize("r", [256, 384])
-def test_grouped_adapter_ranks_at_decode_rows(gpu_lib, r):
+@pytest.mark.parametrize("m,k,r", [(4096, 4096, 256), (4096, 4096, 384), (2072, 1032, 384)])
+def test_grouped_adapter_ranks_at_decode_rows(gpu_lib, m, k, r):
     """4096 rows (128 sequences x (16 clean + 16 noisy)) with the adapter ranks
     of the grouped LoRA-down launches (gate|up: 2 x 128, q|k|v: 3 x 128), which
-    take the one-tile-wide LoRA-down kernels; 48 sampled rows against the
+    take the one-tile-wide LoRA-down kernels, plus a ragged case (a partial
+    last row tile and a partial last K-tile); 48 sampled rows against the
     oracle."""
-    say(f"gated_lora grouped rank {r}: 4096 x 1024 x 4096")
-    c = workloads.gated_lora_case(4096, 1024, 4096, r, dtype="bf16", seed=3, tag=r,
-                                  gate=workloads.default_gate(4096, 16))
+    say(f"gated_lora grouped rank {r}: {m} x 1024 x {k}")
+    c = workloads.gated_lora_case(m, 1024, k, r, dtype="bf16", seed=3, tag=r + k,
+                                  gate=workloads.default_gate(m, 4 if m % 32 else 16))
     y = to_host(_run(gpu_lib, c))
-    rows = np.sort(np.random.default_rng(5).choice(4096, 48, replace=False))
+    rows = np.sort(np.concatenate([np.random.default_rng(5).choice(m - 8, 40, replace=False),
+                                   np.arange(m - 8, m)]))
     assert set(c["gate"][rows].tolist()) == {0, 1}
     err = row_relerr(y[rows], _ref(c, rows))
     say(f"  row rel err {err:.3g}")
