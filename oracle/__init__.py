@@ -42,6 +42,7 @@ from .decoder import (
     lm_head,
 )
 from .step import step_rows, decode_step
+from .kv_commit import kv_commit
 
 __all__ = [
     "gated_lora_linear",
@@ -67,4 +68,5 @@ __all__ = [
     "lm_head",
     "step_rows",
     "decode_step",
+    "kv_commit",
 ]

@@ -79,11 +79,14 @@ def block_mask(block):
     return allow
 
 
-def block_attention(q, k_cache, v_cache, k_blk, v_blk, block, scale):
+def block_attention(q, k_cache, v_cache, k_blk, v_blk, block, scale, ctx_lens=None):
     """Attention of the block rows over cache + block under `block_mask`.
 
     q [B, n, H, D] with n = 2*block; k_cache/v_cache [B, C, Hkv, D];
-    k_blk/v_blk [B, n, Hkv, D].  Returns (out [B, n, H, D], lse [B, n, H]).
+    k_blk/v_blk [B, n, Hkv, D].  ctx_lens [B] (optional): sequence b's cache
+    holds ctx_lens[b] <= C valid rows; rows from ctx_lens[b] on are unused
+    capacity and are not attended.  None means every sequence has C rows.
+    Returns (out [B, n, H, D], lse [B, n, H]).
     """
     q = np.asarray(q, dtype=np.float64)
     kc = np.asarray(k_cache, dtype=np.float64)
@@ -95,15 +98,17 @@ def block_attention(q, k_cache, v_cache, k_blk, v_blk, block, scale):
     group = nh // nkv
     ctx = kc.shape[1]
     allow = block_mask(block)
+    lens = np.full(bsz, ctx) if ctx_lens is None else np.asarray(ctx_lens)
     out = np.zeros((bsz, n, nh, hd))
     lse = np.zeros((bsz, n, nh))
     for b in range(bsz):
+        c = int(lens[b])
         for h in range(nh):
             g = h // group
-            keys = np.concatenate([kc[b, :, g, :], kb[b, :, g, :]], axis=0)     # [C + n, D]
-            vals = np.concatenate([vc[b, :, g, :], vb[b, :, g, :]], axis=0)
-            s = scale * (q[b, :, h, :] @ keys.T)                               # [n, C + n]
-            ok = np.concatenate([np.ones((n, ctx), dtype=bool), allow], axis=1)
+            keys = np.concatenate([kc[b, :c, g, :], kb[b, :, g, :]], axis=0)     # [c + n, D]
+            vals = np.concatenate([vc[b, :c, g, :], vb[b, :, g, :]], axis=0)
+            s = scale * (q[b, :, h, :] @ keys.T)                               # [n, c + n]
+            ok = np.concatenate([np.ones((n, c), dtype=bool), allow], axis=1)
             s = np.where(ok, s, -np.inf)
             m = np.max(s, axis=1, keepdims=True)
             e = np.exp(s - m)
@@ -121,8 +126,9 @@ def silu_mul(g, u):
 
 
 def decoder_layer(h, w, gate, positions, k_cache, v_cache, block, n_heads, n_kv_heads,
-                  eps=1e-6, theta=1.0e6, lora_scale=1.0):
+                  eps=1e-6, theta=1.0e6, lora_scale=1.0, ctx_lens=None):
     """One layer on the residual stream h [rows, hidden], rows = B * 2 * block.
+    ctx_lens: per-sequence valid cache rows, as in `block_attention`.
 
     w: dict with attn_norm, mlp_norm [hidden] and, for p in q k v o g u d,
     w{p} [out, in], a{p} [r, in], b{p} [out, r].  Every stored intermediate
@@ -146,7 +152,7 @@ def decoder_layer(h, w, gate, positions, k_cache, v_cache, block, n_heads, n_kv_
     n = 2 * block
     att, _ = block_attention(q.reshape(bsz, n, n_heads, hd), k_cache, v_cache,
                              k.reshape(bsz, n, n_kv_heads, hd), v.reshape(bsz, n, n_kv_heads, hd),
-                             block, 1.0 / np.sqrt(hd))
+                             block, 1.0 / np.sqrt(hd), ctx_lens)
     att = bf(att.reshape(rows, n_heads * hd))
     o = proj(att, "o")
     h1 = bf(h + o)
