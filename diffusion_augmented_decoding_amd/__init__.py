@@ -27,6 +27,7 @@ EXPORTS = (
     "uno_sample_rows_workspace", "uno_sample_rows",
     "uno_decoder_layer_workspace", "uno_decoder_layer",
     "uno_psi_spec_step_workspace", "uno_psi_spec_step",
+    "uno_kv_commit",
     "uno_profile_enable", "uno_profile_reset", "uno_profile_query",
 )
 
@@ -90,17 +91,18 @@ def _declare(lib):
         "uno_block_verify_attention_workspace": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _i32,
                                                                 ctypes.POINTER(_sz)]),
         "uno_block_verify_attention": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _i32, _i32,
-                                                      _p, _p, _p, _p, _p, _f32, _p, _p, _p, _sz]),
+                                                      _p, _p, _p, _p, _p, _p, _f32, _p, _p, _p, _sz]),
         "uno_sample_rows_workspace": (ctypes.c_int, [_i32, _i32, ctypes.POINTER(_sz)]),
         "uno_sample_rows": (ctypes.c_int, [_p, ctypes.c_int, _i32, _i32, _p, _i64, _p, _f32, _p, _p, _sz]),
         "uno_decoder_layer_workspace": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                                        ctypes.POINTER(_sz)]),
         "uno_decoder_layer": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
-                                             ctypes.POINTER(LayerWeights), _p, _p, _f32, _f32, _f32,
+                                             ctypes.POINTER(LayerWeights), _p, _p, _p, _f32, _f32, _f32,
                                              _p, _p, _sz]),
         "uno_psi_spec_step_workspace": (ctypes.c_int, [ctypes.POINTER(StepConfig), ctypes.POINTER(_sz)]),
         "uno_psi_spec_step": (ctypes.c_int, [_p, ctypes.POINTER(StepConfig), ctypes.POINTER(LayerWeights),
-                                             _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz]),
+                                             _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz]),
+        "uno_kv_commit": (ctypes.c_int, [_p, _i32, _i32, _p, _p]),
         "uno_profile_enable": (None, [ctypes.c_int, ctypes.c_char_p]),
         "uno_profile_reset": (None, []),
         "uno_profile_query": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
@@ -361,11 +363,12 @@ def block_verify_attention_workspace(batch, block, ctx, n_heads, n_kv, head_dim)
 
 
 def block_verify_attention(q, k_cache, v_cache, k_block, v_block, block, softmax_scale,
-                           out=None, lse=None, want_lse=True, workspace=None, stream=None):
+                           out=None, lse=None, want_lse=True, workspace=None, stream=None, cache_len=None):
     """Block-masked GQA attention (uno_block_verify_attention).
 
     q [B, 2*block, H, 128], k_cache/v_cache [B, ctx, Hkv, 128], k_block/v_block
-    [B, 2*block, Hkv, 128] (bf16, contiguous).  Returns (out, lse or None).
+    [B, 2*block, Hkv, 128] (bf16, contiguous); cache_len int32 [B] (optional):
+    valid cache rows per sequence.  Returns (out, lse or None).
     """
     import torch
     load()
@@ -378,7 +381,7 @@ def block_verify_attention(q, k_cache, v_cache, k_block, v_block, block, softmax
         lse = torch.empty((bsz, n, nh), dtype=torch.float32, device=q.device)
     ws = _workspace(block_verify_attention_workspace(bsz, block, ctx, nh, nkv, hd), q.device, workspace)
     _check(_lib.uno_block_verify_attention(
-        _stream(stream), bsz, block, ctx, nh, nkv, hd, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+        _stream(stream), bsz, block, ctx, nh, nkv, hd, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len),
         _ptr(k_block), _ptr(v_block), float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws), _nbytes(ws)))
     return out, lse
 
@@ -428,15 +431,17 @@ def layer_weights(w, k_cache=None, v_cache=None):
 
 
 def decoder_layer(hidden_state, weights, gate, positions, batch, block, ctx, n_heads, n_kv, inter, r,
-                  rms_eps=1e-6, rope_theta=1.0e6, lora_scale=1.0, workspace=None, stream=None):
+                  rms_eps=1e-6, rope_theta=1.0e6, lora_scale=1.0, workspace=None, stream=None, cache_len=None):
     """One decoder layer in place on hidden_state [rows, hidden] (uno_decoder_layer).
-    weights: a LayerWeights (see layer_weights)."""
+    weights: a LayerWeights (see layer_weights); cache_len int32 [batch]
+    (optional): valid cache rows per sequence, ctx then being the capacity;
+    the clean rows' k and v are written after them."""
     load()
     hidden = hidden_state.shape[1]
     ws = _workspace(decoder_layer_workspace(batch, block, ctx, hidden, inter, n_heads, n_kv, r),
                     hidden_state.device, workspace)
     _check(_lib.uno_decoder_layer(_stream(stream), batch, block, ctx, hidden, inter, n_heads, n_kv, r,
-                                  ctypes.byref(weights), _ptr(gate), _ptr(positions), float(rms_eps),
+                                  ctypes.byref(weights), _ptr(gate), _ptr(positions), _ptr(cache_len), float(rms_eps),
                                   float(rope_theta), float(lora_scale), _ptr(hidden_state), _ptr(ws), _nbytes(ws)))
     return hidden_state
 
@@ -456,7 +461,7 @@ def psi_spec_step_workspace(cfg):
 
 
 def psi_spec_step(cfg, layers, embed, final_norm, lm_head, tokens, u_draft, u_accept, u_sample,
-                  logits=None, outputs=None, workspace=None, stream=None):
+                  logits=None, outputs=None, workspace=None, stream=None, cache_len=None):
     """One decode step (uno_psi_spec_step).
 
     cfg: StepConfig; layers: sequence (or ctypes array) of LayerWeights, one per layer;
@@ -465,6 +470,9 @@ def psi_spec_step(cfg, layers, embed, final_norm, lm_head, tokens, u_draft, u_ac
     u_sample f32 [batch].  Returns a dict of device tensors: logits
     [batch*2*block, vocab] bf16, drafts [batch, block-1], accept_len and token
     [batch] (`outputs`, if given, is such a dict to write into).
+    cache_len int32 [batch] (optional, updated in place): valid cache rows per
+    sequence out of cfg.ctx_len; the step appends the clean rows' k and v and
+    commits the kept ones (the decode loop's form).
     """
     import torch
     load()
@@ -481,10 +489,18 @@ def psi_spec_step(cfg, layers, embed, final_norm, lm_head, tokens, u_draft, u_ac
     arr = layers if isinstance(layers, ctypes.Array) else (LayerWeights * max(len(layers), 1))(*layers)
     ws = _workspace(psi_spec_step_workspace(cfg), dev, workspace)
     _check(_lib.uno_psi_spec_step(_stream(stream), ctypes.byref(cfg), arr, _ptr(embed), _ptr(final_norm),
-                                  _ptr(lm_head), _ptr(tokens), _ptr(u_draft), _ptr(u_accept), _ptr(u_sample),
+                                  _ptr(lm_head), _ptr(tokens), _ptr(cache_len), _ptr(u_draft), _ptr(u_accept), _ptr(u_sample),
                                   _ptr(logits), _ptr(drafts) if k > 0 else None, _ptr(acc), _ptr(tok),
                                   _ptr(ws), _nbytes(ws)))
     return {"logits": logits, "drafts": drafts, "accept_len": acc, "token": tok}
+
+
+def kv_commit(accept_len, cache_len, capacity, stream=None):
+    """cache_len[b] = min(capacity, cache_len[b] + accept_len[b] + 1) in place (uno_kv_commit)."""
+    load()
+    _check(_lib.uno_kv_commit(_stream(stream), int(cache_len.shape[0]), int(capacity), _ptr(accept_len),
+                              _ptr(cache_len)))
+    return cache_len
 
 
 def layer_array(layers):

@@ -150,6 +150,15 @@ hipError_t launch_decoder_layer(const DecoderLayerArgs& d, hipStream_t stream) {
     ra.n_heads2 = d.n_kv;
     ra.x2 = k;
     ra.ldx2 = int64_t(d.n_kv) * kHeadDim;
+    if (d.cache_len) {   // the clean rows' keys (rotated) and values join the cache's free slots
+      ra.cache_len = d.cache_len;
+      ra.block = d.block;
+      ra.cap = d.ctx;
+      ra.k_cache = const_cast<void*>(d.w->k_cache);
+      ra.v_cache = const_cast<void*>(d.w->v_cache);
+      ra.v = v;
+      ra.ldv = int64_t(d.n_kv) * kHeadDim;
+    }
     return launch_rope(ra, stream);
   };
 
@@ -206,6 +215,7 @@ hipError_t launch_decoder_layer(const DecoderLayerArgs& d, hipStream_t stream) {
     ta.n_tree = 2 * d.block;
     ta.block = d.block;
     ta.ctx = d.ctx;
+    ta.ctx_lens = d.cache_len;
     ta.n_heads = d.n_heads;
     ta.n_kv = d.n_kv;
     ta.head_dim = kHeadDim;
@@ -361,9 +371,9 @@ uno_status uno_block_verify_attention_workspace(int32_t batch, int32_t block, in
 
 uno_status uno_block_verify_attention(hipStream_t stream, int32_t batch, int32_t block, int32_t ctx_len,
                                       int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, const void* q,
-                                      const void* k_cache, const void* v_cache, const void* k_block,
-                                      const void* v_block, float softmax_scale, void* out, float* out_lse,
-                                      void* workspace, size_t workspace_bytes) {
+                                      const void* k_cache, const void* v_cache, const int32_t* cache_len,
+                                      const void* k_block, const void* v_block, float softmax_scale, void* out,
+                                      float* out_lse, void* workspace, size_t workspace_bytes) {
   UNO_GUARD_BEGIN
   uno_status s = check_block_attn(batch, block, ctx_len, n_heads, n_kv_heads, head_dim);
   if (s != UNO_OK) return s;
@@ -382,6 +392,7 @@ uno_status uno_block_verify_attention(hipStream_t stream, int32_t batch, int32_t
   a.n_tree = 2 * block;
   a.block = block;
   a.ctx = ctx_len;
+  a.ctx_lens = cache_len;
   a.n_heads = n_heads;
   a.n_kv = n_kv_heads;
   a.head_dim = head_dim;
@@ -469,8 +480,8 @@ uno_status uno_decoder_layer_workspace(int32_t batch, int32_t block, int32_t ctx
 uno_status uno_decoder_layer(hipStream_t stream, int32_t batch, int32_t block, int32_t ctx_len, int32_t hidden,
                              int32_t inter, int32_t n_heads, int32_t n_kv_heads, int32_t r,
                              const uno_layer_weights* wt, const uint8_t* gate, const int32_t* positions,
-                             float rms_eps, float rope_theta, float lora_scale, void* hidden_state,
-                             void* workspace, size_t workspace_bytes) {
+                             const int32_t* cache_len, float rms_eps, float rope_theta, float lora_scale,
+                             void* hidden_state, void* workspace, size_t workspace_bytes) {
   UNO_GUARD_BEGIN
   uno_status s = check_layer(batch, block, ctx_len, hidden, inter, n_heads, n_kv_heads, r);
   if (s != UNO_OK) return s;
@@ -504,6 +515,7 @@ uno_status uno_decoder_layer(hipStream_t stream, int32_t batch, int32_t block, i
   la.w = wt;
   la.gate = gate;
   la.positions = positions;
+  la.cache_len = cache_len;
   la.rms_eps = rms_eps;
   la.rope_theta = rope_theta;
   la.lora_scale = lora_scale;
@@ -512,6 +524,16 @@ uno_status uno_decoder_layer(hipStream_t stream, int32_t batch, int32_t block, i
   la.ws_bytes = workspace_bytes;
   const hipError_t e = launch_decoder_layer(la, stream);
   return check_hip(e, "uno_decoder_layer launch");
+  UNO_GUARD_END
+}
+
+// ------------------------------------------------------------------ KV commit
+uno_status uno_kv_commit(hipStream_t stream, int32_t batch, int32_t capacity, const int32_t* accept_len,
+                         int32_t* cache_len) {
+  UNO_GUARD_BEGIN
+  if (batch < 1 || capacity < 0) return fail(UNO_ERR_INVALID_ARGUMENT, "batch >= 1 and capacity >= 0 required");
+  if (!accept_len || !cache_len) return fail(UNO_ERR_INVALID_ARGUMENT, "accept_len and cache_len are required");
+  return check_hip(launch_kv_commit(batch, capacity, accept_len, cache_len, stream), "uno_kv_commit launch");
   UNO_GUARD_END
 }
 

@@ -84,7 +84,7 @@ uno_status uno_psi_spec_step_workspace(const uno_step_config* config, size_t* by
 
 uno_status uno_psi_spec_step(hipStream_t stream, const uno_step_config* config, const uno_layer_weights* layers,
                              const void* embed, const void* final_norm, const void* lm_head, const int32_t* tokens,
-                             const float* u_draft, const float* u_accept, const float* u_sample, void* logits,
+                             int32_t* cache_len, const float* u_draft, const float* u_accept, const float* u_sample, void* logits,
                              int32_t* out_drafts, int32_t* out_accept_len, int32_t* out_token, void* workspace,
                              size_t workspace_bytes) {
   UNO_GUARD_BEGIN
@@ -130,6 +130,7 @@ uno_status uno_psi_spec_step(hipStream_t stream, const uno_step_config* config, 
   sa.rows = rows;
   sa.block = c.block;
   sa.ctx = c.ctx_len;
+  sa.cache_len = cache_len;
   sa.hidden = c.hidden;
   sa.vocab = c.vocab;
   sa.tokens = tokens;
@@ -153,6 +154,7 @@ uno_status uno_psi_spec_step(hipStream_t stream, const uno_step_config* config, 
     la.w = &layers[l];
     la.gate = c.r > 0 ? gate : nullptr;
     la.positions = pos;
+    la.cache_len = cache_len;
     la.rms_eps = c.rms_eps;
     la.rope_theta = c.rope_theta;
     la.lora_scale = c.lora_scale;
@@ -234,6 +236,9 @@ uno_status uno_psi_spec_step(hipStream_t stream, const uno_step_config* config, 
     va.ws = scratch;
     e = launch_verify_linear(va, stream);
   }
+  // commit: the block's AR token and its accepted drafts, appended by every
+  // layer during the forward pass, join each sequence's valid cache prefix
+  if (e == hipSuccess && cache_len) e = launch_kv_commit(c.batch, c.ctx_len, out_accept_len, cache_len, stream);
   return check_hip(e, "uno_psi_spec_step launch");
   UNO_GUARD_END
 }

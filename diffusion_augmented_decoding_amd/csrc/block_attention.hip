@@ -6,7 +6,9 @@
 // "实验" -- the clean (verify) and noisy (draft) rows share one KV cache.
 // Mask (the pages give none; the reading used throughout): every row sees the
 // whole cache; clean row i also sees clean rows 0..i; a noisy row sees all
-// 2*block rows of its block.
+// 2*block rows of its block.  With per-sequence cache lengths (a cache whose
+// verified prefix grows by the kept rows of each step) sequence b sees its
+// first ctx_lens[b] cache rows; its rows sit `ctx` (the capacity) rows apart.
 //
 // Work unit: 128 query rows of one (sequence, KV head), i.e. 4 waves x 32
 // rows, where row r is (block row r / G, head g*G + r % G): the G query heads
@@ -209,7 +211,10 @@ __global__ __launch_bounds__(kThreads) void block_attn_kernel(TreeAttnArgs a, Bl
   const int g = (grp / pl.ks) % a.n_kv;
   const int b = grp / (pl.ks * a.n_kv);
 
-  const int n = a.n_tree, ctx = a.ctx, H = a.n_heads, Hkv = a.n_kv, blk = a.block;
+  const int n = a.n_tree, cap = a.ctx, H = a.n_heads, Hkv = a.n_kv, blk = a.block;
+  // valid cache rows of this sequence (rows cap apart in memory); the key
+  // blocks past its cache and block rows are not visited
+  const int ctx = a.ctx_lens ? __builtin_amdgcn_readfirstlane(min(max(a.ctx_lens[b], 0), cap)) : cap;
   const int G = H / Hkv;
   const int nrows = n * G;
   const int nkeys = ctx + n;
@@ -218,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void block_attn_kernel(TreeAttnArgs a, Bl
   const int lrow = lane & 31, lh = lane >> 5;
 
   const int blk0 = ksi * pl.per;
-  const int blk_end = min(pl.nblk, blk0 + pl.per);
+  const int blk_end = min((nkeys + kKB - 1) / kKB, blk0 + pl.per);
   const int nb = blk_end - blk0;
 
   const uint16_t* kc = static_cast<const uint16_t*>(a.k_cache);
@@ -243,8 +248,8 @@ __global__ __launch_bounds__(kThreads) void block_attn_kernel(TreeAttnArgs a, Bl
   // physical chunk l & 15.  Addresses are plain 64-bit integers and every choice is a
   // select, so a stage's loads form one basic block with no waits between them.
   const uint64_t row_bytes = uint64_t(Hkv) * kHD * 2;
-  const uint64_t cache_k = reinterpret_cast<uint64_t>(kc) + (uint64_t(b) * ctx * Hkv + g) * kHD * 2;
-  const uint64_t cache_v = reinterpret_cast<uint64_t>(vc) + (uint64_t(b) * ctx * Hkv + g) * kHD * 2;
+  const uint64_t cache_k = reinterpret_cast<uint64_t>(kc) + (uint64_t(b) * cap * Hkv + g) * kHD * 2;
+  const uint64_t cache_v = reinterpret_cast<uint64_t>(vc) + (uint64_t(b) * cap * Hkv + g) * kHD * 2;
   const uint64_t tree_k = reinterpret_cast<uint64_t>(kt) + (uint64_t(b) * n * Hkv + g) * kHD * 2;
   const uint64_t tree_v = reinterpret_cast<uint64_t>(vt) + (uint64_t(b) * n * Hkv + g) * kHD * 2;
   const uint64_t zaddr = reinterpret_cast<uint64_t>(&kZero16[0]);

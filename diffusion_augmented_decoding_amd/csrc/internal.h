@@ -115,6 +115,9 @@ hipError_t launch_gated_lora_swiglu(const SwigluArgs& a, hipStream_t stream);
 struct TreeAttnArgs {
   int batch, n_tree, ctx, n_heads, n_kv, head_dim;
   int block;                 // 0: prefix-tree mask from parent; > 0: clean/noisy block mask
+  const int32_t* ctx_lens;   // block mask only: valid cache rows per sequence, clamped to
+                             // [0, ctx]; ctx is then the rows of capacity per sequence
+                             // (nullptr: every sequence has ctx rows)
   const void* q;
   const void* k_cache;
   const void* v_cache;
@@ -196,6 +199,14 @@ struct RopeArgs {
   float theta;
   int n_heads2;                      // optional second tensor at the same positions (0: none)
   void* x2; int64_t ldx2;
+  // Optional append into a KV cache (cache_len != nullptr; needs x2): rows are
+  // sequences of 2*block (block clean, then block noisy); clean row j of
+  // sequence b writes its rotated x2 row to k_cache and its v row to v_cache
+  // at slot cache_len[b] + j when 0 <= slot < cap.  Caches [batch][cap][n_heads2][128].
+  const int32_t* cache_len;
+  int block, cap;
+  void* k_cache; void* v_cache;
+  const void* v; int64_t ldv;
 };
 hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);
 
@@ -214,6 +225,9 @@ struct DecoderLayerArgs {
   const uno_layer_weights* w;
   const uint8_t* gate;               // [rows]; null: adapter off everywhere
   const int32_t* positions;          // [rows]
+  const int32_t* cache_len;          // [batch] valid cache rows (nullptr: ctx rows each); when set,
+                                     // ctx is the capacity and the clean rows' k, v are appended
+                                     // at slots cache_len[b] + j (the length itself is not changed)
   float rms_eps, rope_theta, lora_scale;
   void* h;                           // bf16 [rows][hidden], updated in place
   void* ws; size_t ws_bytes;
@@ -224,10 +238,12 @@ hipError_t launch_decoder_layer(const DecoderLayerArgs& a, hipStream_t stream);
 // ---------------------------------------------------------------- step set-up
 // Row j of sequence b (rows of a sequence: block clean, then block noisy):
 // h[row] = embed[tokens[row]] (a zero row for an id outside [0, vocab)),
-// gate[row] = (j >= block), positions[row] = ctx + j % block.
+// gate[row] = (j >= block), positions[row] = ctx + j % block, with ctx
+// replaced by cache_len[b] when cache_len is given.
 struct StepSetupArgs {
   int64_t rows;
   int block, ctx, hidden, vocab;
+  const int32_t* cache_len;          // [batch] or nullptr
   const int32_t* tokens;
   const void* embed;                 // bf16 [vocab][hidden]
   void* h;                           // bf16 [rows][hidden]
@@ -235,5 +251,10 @@ struct StepSetupArgs {
   int32_t* positions;
 };
 hipError_t launch_step_setup(const StepSetupArgs& a, hipStream_t stream);
+
+// KV commit after verification: cache_len[b] = min(cap, cache_len[b] +
+// accept_len[b] + 1) for b < batch (the rows themselves were appended during
+// the forward pass; the rejected and noisy rows are dropped by not counting them).
+hipError_t launch_kv_commit(int batch, int cap, const int32_t* accept_len, int32_t* cache_len, hipStream_t stream);
 
 }  // namespace uno

@@ -94,6 +94,24 @@ __global__ __launch_bounds__(kNormThreads) void rms_norm_kernel(RmsNormArgs a) {
   }
 }
 
+// Cache slot of a clean row for the optional KV append: rows come in
+// sequences of 2*block (clean then noisy); clean row j of sequence b goes to
+// slot cache_len[b] + j of that sequence's cache when the slot is inside the
+// capacity.  Returns false for noisy rows, rows past the capacity and calls
+// without an append; else sets the row's key and value destinations.
+__device__ __forceinline__ bool append_slot(const RopeArgs& a, int64_t row, uint16_t*& kd, uint16_t*& vd) {
+  if (!a.cache_len) return false;
+  const int64_t b = row / (2 * a.block);
+  const int j = int(row % (2 * a.block));
+  if (j >= a.block) return false;
+  const int64_t slot = int64_t(a.cache_len[b]) + j;
+  if (slot < 0 || slot >= a.cap) return false;
+  const int64_t off = (b * a.cap + slot) * int64_t(a.n_heads2) * 128;
+  kd = static_cast<uint16_t*>(a.k_cache) + off;
+  vd = static_cast<uint16_t*>(a.v_cache) + off;
+  return true;
+}
+
 // In-place rotary embedding, one workgroup per row.  Thread t owns pair
 // index i = t % 64 and forms the angle pos * theta^(-i/64) once, in double
 // precision (positions far into a long context keep their phase), then
@@ -116,6 +134,15 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeArgs a) {
   if (a.x2) {
     uint16_t* xr2 = static_cast<uint16_t*>(a.x2) + row * a.ldx2;
     for (int h = h0; h < a.n_heads2; h += 4) rotate(xr2 + h * 128);
+    uint16_t *kd, *vd;
+    if (append_slot(a, row, kd, vd)) {
+      __syncthreads();   // the rotated row, written by this workgroup, is complete
+      const uint16_t* vr = static_cast<const uint16_t*>(a.v) + row * a.ldv;
+      for (int e = threadIdx.x; e < a.n_heads2 * 128; e += 256) {
+        kd[e] = xr2[e];
+        vd[e] = vr[e];
+      }
+    }
   }
 }
 
@@ -143,7 +170,8 @@ __global__ __launch_bounds__(256) void rope_vec_kernel(RopeArgs a) {
     cs[j] = cs_s[i0 + j];
     sn[j] = sn_s[i0 + j];
   }
-  auto rotate = [&](uint16_t* p) {
+  // rotates the head at p in place; dup (optional) receives a copy of the result
+  auto rotate = [&](uint16_t* p, uint16_t* dup) {
     const uint2 lo = *reinterpret_cast<const uint2*>(p + i0), hi = *reinterpret_cast<const uint2*>(p + 64 + i0);
     const float x1[4] = {bf16_lo(lo.x), bf16_hi(lo.x), bf16_lo(lo.y), bf16_hi(lo.y)};
     const float x2[4] = {bf16_lo(hi.x), bf16_hi(hi.x), bf16_lo(hi.y), bf16_hi(hi.y)};
@@ -153,14 +181,27 @@ __global__ __launch_bounds__(256) void rope_vec_kernel(RopeArgs a) {
       o1[j] = x1[j] * cs[j] - x2[j] * sn[j];
       o2[j] = x2[j] * cs[j] + x1[j] * sn[j];
     }
-    *reinterpret_cast<uint2*>(p + i0) = make_uint2(pack_bf16x2(o1[0], o1[1]), pack_bf16x2(o1[2], o1[3]));
-    *reinterpret_cast<uint2*>(p + 64 + i0) = make_uint2(pack_bf16x2(o2[0], o2[1]), pack_bf16x2(o2[2], o2[3]));
+    const uint2 r1 = make_uint2(pack_bf16x2(o1[0], o1[1]), pack_bf16x2(o1[2], o1[3]));
+    const uint2 r2 = make_uint2(pack_bf16x2(o2[0], o2[1]), pack_bf16x2(o2[2], o2[3]));
+    *reinterpret_cast<uint2*>(p + i0) = r1;
+    *reinterpret_cast<uint2*>(p + 64 + i0) = r2;
+    if (dup) {
+      *reinterpret_cast<uint2*>(dup + i0) = r1;
+      *reinterpret_cast<uint2*>(dup + 64 + i0) = r2;
+    }
   };
   uint16_t* xr = static_cast<uint16_t*>(a.x) + row * a.ldx;
-  for (int h = h0; h < a.n_heads; h += 16) rotate(xr + h * 128);
+  for (int h = h0; h < a.n_heads; h += 16) rotate(xr + h * 128, nullptr);
   if (a.x2) {
     uint16_t* xr2 = static_cast<uint16_t*>(a.x2) + row * a.ldx2;
-    for (int h = h0; h < a.n_heads2; h += 16) rotate(xr2 + h * 128);
+    uint16_t *kd = nullptr, *vd = nullptr;
+    const bool app = append_slot(a, row, kd, vd);
+    for (int h = h0; h < a.n_heads2; h += 16) rotate(xr2 + h * 128, app ? kd + h * 128 : nullptr);
+    if (app) {
+      // the value row goes to the cache unchanged, in 8-byte pieces
+      const uint2* vr = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.v) + row * a.ldv);
+      for (int e = threadIdx.x; e < a.n_heads2 * 32; e += 256) reinterpret_cast<uint2*>(vd)[e] = vr[e];
+    }
   }
 }
 
@@ -206,7 +247,8 @@ hipError_t launch_rms_norm(const RmsNormArgs& a, hipStream_t stream) {
 hipError_t launch_rope(const RopeArgs& a, hipStream_t stream) {
   ProfileScope ps("uno_rope", stream);
   auto vec_ok = [](const void* p, int64_t ld) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0 && ld % 4 == 0; };
-  const bool vec = vec_ok(a.x, a.ldx) && (!a.x2 || vec_ok(a.x2, a.ldx2));
+  const bool vec = vec_ok(a.x, a.ldx) && (!a.x2 || vec_ok(a.x2, a.ldx2)) &&
+                   (!a.cache_len || (vec_ok(a.v, a.ldv) && vec_ok(a.k_cache, 0) && vec_ok(a.v_cache, 0)));
   if (vec)
     hipLaunchKernelGGL(rope_vec_kernel, dim3(unsigned(a.rows)), dim3(256), 0, stream, a);
   else
@@ -240,11 +282,28 @@ __global__ __launch_bounds__(256) void step_setup_kernel(StepSetupArgs a) {
   for (int i = threadIdx.x; i < nvec; i += 256) dst[i] = ok ? src[i] : u32x4{0u, 0u, 0u, 0u};
   if (threadIdx.x == 0) {
     a.gate[row] = j >= a.block ? 1 : 0;
-    a.positions[row] = a.ctx + j % a.block;
+    a.positions[row] = (a.cache_len ? a.cache_len[row / (2 * a.block)] : a.ctx) + j % a.block;
   }
 }
 
 }  // namespace
+
+// One thread per sequence: the kept rows (the block's AR token and the L
+// accepted drafts, already written by the forward pass) join the valid prefix.
+__global__ __launch_bounds__(256) void kv_commit_kernel(int batch, int cap, const int32_t* accept_len,
+                                                        int32_t* cache_len) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= batch) return;
+  const int64_t len = int64_t(cache_len[b]) + accept_len[b] + 1;
+  cache_len[b] = int32_t(len < cap ? len : cap);
+}
+
+hipError_t launch_kv_commit(int batch, int cap, const int32_t* accept_len, int32_t* cache_len, hipStream_t stream) {
+  ProfileScope ps("uno_kv_commit", stream);
+  hipLaunchKernelGGL(kv_commit_kernel, dim3(unsigned((batch + 255) / 256)), dim3(256), 0, stream, batch, cap,
+                     accept_len, cache_len);
+  return hipGetLastError();
+}
 
 hipError_t launch_step_setup(const StepSetupArgs& a, hipStream_t stream) {
   ProfileScope ps("uno_step_setup", stream);

@@ -49,7 +49,7 @@ typedef enum {
 
 typedef enum { UNO_F32 = 0, UNO_BF16 = 1 } uno_dtype;
 
-#define UNO_ABI_VERSION 1
+#define UNO_ABI_VERSION 2
 
 int uno_abi_version(void);
 const char* uno_status_string(uno_status s);
@@ -252,7 +252,11 @@ uno_status uno_silu_mul(hipStream_t stream, int64_t rows, int32_t dim, const voi
  * rows of the block.  Layouts as uno_tree_verify_attention with
  * n_tree = 2*block: q [batch][2*block][n_heads][128], k_block/v_block
  * [batch][2*block][n_kv_heads][128], caches [batch][ctx_len][n_kv_heads][128].
- * 1 <= block <= 128; workspace from the query (fp32 split partials). */
+ * 1 <= block <= 128; workspace from the query (fp32 split partials).
+ * cache_len (optional, device int32 [batch]): sequence b's cache holds
+ * cache_len[b] valid rows (clamped to [0, ctx_len]) and only those are
+ * attended; ctx_len is then the capacity, the row distance between
+ * sequences.  NULL = every sequence has ctx_len rows. */
 uno_status uno_block_verify_attention_workspace(int32_t batch, int32_t block, int32_t ctx_len,
                                                 int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
                                                 size_t* bytes);
@@ -260,6 +264,7 @@ uno_status uno_block_verify_attention(hipStream_t stream,
                                       int32_t batch, int32_t block, int32_t ctx_len,
                                       int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
                                       const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* cache_len,
                                       const void* k_block, const void* v_block, float softmax_scale,
                                       void* out, float* out_lse,
                                       void* workspace, size_t workspace_bytes);
@@ -287,7 +292,15 @@ uno_status uno_sample_rows(hipStream_t stream, uno_dtype logit_dtype, int32_t ro
  * lora_scale.  When the adapters a[q], a[k], a[v] are stored back to back
  * (one [3r][hidden] array), and likewise a[gate], a[up], each group's
  * LoRA-down runs as one launch over the shared input.  hidden_state [rows][hidden], rows = batch * 2 * block;
- * positions int32 [rows].  The block's k and v are not written to the cache.
+ * positions int32 [rows].
+ * cache_len NULL: every sequence's cache holds ctx_len rows and the block's
+ * k and v are not written to it.  cache_len (device int32 [batch]) set:
+ * sequence b's cache holds cache_len[b] valid rows out of a capacity of
+ * ctx_len (attention sees those rows only), and clean row j of sequence b
+ * writes its k (after RoPE) and v into slot cache_len[b] + j of the cache
+ * when that slot is below ctx_len; cache_len itself is not changed (see
+ * uno_kv_commit).  The caches are then written: k_cache/v_cache must not be
+ * read by concurrent work.
  * hidden and inter multiples of 8, r a multiple of 8, n_heads / n_kv_heads
  * <= 8, 1 <= block <= 128. */
 enum { UNO_PROJ_Q = 0, UNO_PROJ_K, UNO_PROJ_V, UNO_PROJ_O, UNO_PROJ_GATE, UNO_PROJ_UP, UNO_PROJ_DOWN,
@@ -298,8 +311,8 @@ typedef struct {
   const void* w[UNO_NUM_PROJ];
   const void* a[UNO_NUM_PROJ];
   const void* b[UNO_NUM_PROJ];
-  const void* k_cache;
-  const void* v_cache;
+  void* k_cache;   /* read; written only by calls given a cache_len */
+  void* v_cache;
 } uno_layer_weights;
 
 uno_status uno_decoder_layer_workspace(int32_t batch, int32_t block, int32_t ctx_len, int32_t hidden,
@@ -308,8 +321,24 @@ uno_status uno_decoder_layer_workspace(int32_t batch, int32_t block, int32_t ctx
 uno_status uno_decoder_layer(hipStream_t stream, int32_t batch, int32_t block, int32_t ctx_len,
                              int32_t hidden, int32_t inter, int32_t n_heads, int32_t n_kv_heads, int32_t r,
                              const uno_layer_weights* weights, const uint8_t* gate, const int32_t* positions,
-                             float rms_eps, float rope_theta, float lora_scale,
+                             const int32_t* cache_len, float rms_eps, float rope_theta, float lora_scale,
                              void* hidden_state, void* workspace, size_t workspace_bytes);
+
+/* KV commit after verification.  Source: Uno summary (hyper.ai), section
+ * 方法 (the AR path keeps the longest valid prefix of the block; the block's
+ * first token comes from the AR weights alone) and section 实验 (drafting
+ * and verification share one KV cache).  The clean rows of a block carry
+ * the adapter gate 0 and see only the cache and earlier clean rows, so
+ * their keys and values are the AR model's; uno_decoder_layer with a
+ * cache_len has already written them after each sequence's valid rows.
+ * This call keeps clean rows 0..L (the block's AR token and the accepted
+ * drafts) and drops the rest by not counting them:
+ *   cache_len[b] = min(capacity, cache_len[b] + accept_len[b] + 1), b < batch.
+ * accept_len, cache_len: device int32 [batch]; cache_len updated in place.
+ * The correction token is not in the cache: it is the next block's first
+ * clean row.  batch >= 1, capacity >= 0. */
+uno_status uno_kv_commit(hipStream_t stream, int32_t batch, int32_t capacity, const int32_t* accept_len,
+                         int32_t* cache_len);
 
 /* One whole Psi-Spec decode step.  Source: Uno summary (hyper.ai), section
  * 方法 (the diffusion path proposes a block, the AR path verifies it by
@@ -340,7 +369,18 @@ uno_status uno_decoder_layer(hipStream_t stream, int32_t batch, int32_t block, i
  * logits (output, caller-owned) bf16 [batch*2*block][vocab]; out_drafts int32
  * [batch][k]; out_accept_len, out_token int32 [batch].  1 <= block <= 65,
  * head_dim 128, hidden and inter multiples of 8, r a multiple of 8 (0: no
- * adapter).  A token id outside [0, vocab) embeds as a zero row. */
+ * adapter).  A token id outside [0, vocab) embeds as a zero row.
+ *
+ * cache_len (optional, device int32 [batch], updated in place): the decode
+ * loop's form.  Sequence b's caches hold cache_len[b] valid rows out of a
+ * capacity of ctx_len per sequence; clean row j and noisy row j sit at
+ * position cache_len[b] + j; every layer writes the clean rows' k and v into
+ * its cache after the valid rows (uno_decoder_layer), and after verification
+ * the step commits the kept rows (uno_kv_commit), so the next step's
+ * cache_len[b] is the old one + out_accept_len[b] + 1.  A slot at or past
+ * ctx_len is not written and the length stops at ctx_len.  NULL: every
+ * cache holds ctx_len rows, the caches are only read and positions are
+ * ctx_len + j. */
 typedef struct {
   int32_t batch, block, ctx_len;
   int32_t hidden, inter, n_heads, n_kv_heads, r, n_layers, vocab;
@@ -350,7 +390,7 @@ typedef struct {
 uno_status uno_psi_spec_step_workspace(const uno_step_config* config, size_t* bytes);
 uno_status uno_psi_spec_step(hipStream_t stream, const uno_step_config* config, const uno_layer_weights* layers,
                              const void* embed, const void* final_norm, const void* lm_head,
-                             const int32_t* tokens, const float* u_draft, const float* u_accept,
+                             const int32_t* tokens, int32_t* cache_len, const float* u_draft, const float* u_accept,
                              const float* u_sample, void* logits, int32_t* out_drafts,
                              int32_t* out_accept_len, int32_t* out_token,
                              void* workspace, size_t workspace_bytes);

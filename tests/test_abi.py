@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.uno_abi_version() == 1
+    assert lib.uno_abi_version() == 2
     for s in range(6):
         assert lib.uno_status_string(s)
     assert lib.uno_status_string(99) == b"unknown status"
@@ -234,12 +234,12 @@ def test_block_attention_rejects_bad_calls(lib):
     assert lib.uno_block_verify_attention_workspace(1, 16, 64, 30, 8, 128, ctypes.byref(ws)) == INVALID
 
     def call(**kw):
-        a = dict(batch=2, block=4, ctx=2000, H=8, Hkv=2, D=128, q=FAKE16, kc=FAKE16, vc=FAKE16, kb=FAKE16,
-                 vb=FAKE16, scale=0.088, out=FAKE16, lse=None, ws=FAKE16, wsb=1 << 24)
+        a = dict(batch=2, block=4, ctx=2000, H=8, Hkv=2, D=128, q=FAKE16, kc=FAKE16, vc=FAKE16, cl=None,
+                 kb=FAKE16, vb=FAKE16, scale=0.088, out=FAKE16, lse=None, ws=FAKE16, wsb=1 << 24)
         a.update(kw)
         return lib.uno_block_verify_attention(None, a["batch"], a["block"], a["ctx"], a["H"], a["Hkv"], a["D"],
-                                              a["q"], a["kc"], a["vc"], a["kb"], a["vb"], a["scale"], a["out"],
-                                              a["lse"], a["ws"], a["wsb"])
+                                              a["q"], a["kc"], a["vc"], a["cl"], a["kb"], a["vb"], a["scale"],
+                                              a["out"], a["lse"], a["ws"], a["wsb"])
     assert call(block=0) == INVALID
     assert call(q=None) == INVALID
     assert call(kc=None) == INVALID
@@ -276,18 +276,18 @@ def test_decoder_layer_rejects_bad_calls(lib):
                                            ctypes.byref(ws)) == UNSUPPORTED
     assert lib.uno_decoder_layer_workspace(128, 16, 8192, 4096, 12288, 32, 8, 12, ctypes.byref(ws)) == UNSUPPORTED
     lw = lib.uno_decoder_layer.argtypes[9]._type_()      # the struct type the loaded library was declared with
-    assert lib.uno_decoder_layer(None, 2, 4, 8, 256, 512, 4, 2, 8, ctypes.byref(lw), FAKE16, FAKE16, 1e-6, 1e6,
+    assert lib.uno_decoder_layer(None, 2, 4, 8, 256, 512, 4, 2, 8, ctypes.byref(lw), FAKE16, FAKE16, None, 1e-6, 1e6,
                                  1.0, FAKE16, FAKE16, 1 << 30) == INVALID      # null weights
     lw.attn_norm = lw.mlp_norm = FAKE16.value
     for i in range(dad.NUM_PROJ):
         lw.w[i] = lw.a[i] = lw.b[i] = FAKE16.value
     lw.k_cache = lw.v_cache = FAKE16.value
-    assert lib.uno_decoder_layer(None, 2, 4, 8, 256, 512, 4, 2, 8, ctypes.byref(lw), FAKE16, FAKE16, 1e-6, 1e6,
+    assert lib.uno_decoder_layer(None, 2, 4, 8, 256, 512, 4, 2, 8, ctypes.byref(lw), FAKE16, FAKE16, None, 1e-6, 1e6,
                                  1.0, FAKE16, FAKE16, 16) == WORKSPACE
-    assert lib.uno_decoder_layer(None, 2, 4, 8, 256, 512, 4, 2, 8, ctypes.byref(lw), FAKE16, FAKE16, 1e-6, 0.5,
+    assert lib.uno_decoder_layer(None, 2, 4, 8, 256, 512, 4, 2, 8, ctypes.byref(lw), FAKE16, FAKE16, None, 1e-6, 0.5,
                                  1.0, FAKE16, FAKE16, 1 << 30) == INVALID      # rope theta
     lw.w[3] = None
-    assert lib.uno_decoder_layer(None, 2, 4, 8, 256, 512, 4, 2, 8, ctypes.byref(lw), FAKE16, FAKE16, 1e-6, 1e6,
+    assert lib.uno_decoder_layer(None, 2, 4, 8, 256, 512, 4, 2, 8, ctypes.byref(lw), FAKE16, FAKE16, None, 1e-6, 1e6,
                                  1.0, FAKE16, FAKE16, 1 << 30) == INVALID
 
 
@@ -315,8 +315,9 @@ def test_step_rejects_bad_calls(lib):
         a = dict(embed=FAKE16, fnorm=FAKE16, lm=FAKE16, tok=FAKE16, ud=FAKE16, ua=FAKE16, us=FAKE16, logits=FAKE16,
                  drafts=FAKE16, L=FAKE16, y=FAKE16)
         a.update(kw)
-        return lib.uno_psi_spec_step(None, ctypes.byref(c), lay, a["embed"], a["fnorm"], a["lm"], a["tok"], a["ud"],
-                                     a["ua"], a["us"], a["logits"], a["drafts"], a["L"], a["y"], FAKE16, ws_bytes)
+        return lib.uno_psi_spec_step(None, ctypes.byref(c), lay, a["embed"], a["fnorm"], a["lm"], a["tok"],
+                                     a.get("cl"), a["ud"], a["ua"], a["us"], a["logits"], a["drafts"], a["L"],
+                                     a["y"], FAKE16, ws_bytes)
     small = cfg(batch=2, block=4, ctx_len=8, hidden=256, inter=512, n_heads=4, n_kv_heads=2, r=8, n_layers=2,
                 vocab=1000)
     assert call(small) == INVALID                          # layer weights are NULL
@@ -330,3 +331,10 @@ def test_step_rejects_bad_calls(lib):
     assert call(small, ws_bytes=64) == WORKSPACE
     layers[1].b[6] = None
     assert call(small) == INVALID
+
+
+def test_kv_commit_rejects_bad_calls(lib):
+    assert lib.uno_kv_commit(None, 0, 16, FAKE16, FAKE16) == INVALID
+    assert lib.uno_kv_commit(None, 4, -1, FAKE16, FAKE16) == INVALID
+    assert lib.uno_kv_commit(None, 4, 16, None, FAKE16) == INVALID
+    assert lib.uno_kv_commit(None, 4, 16, FAKE16, None) == INVALID
