@@ -177,8 +177,9 @@ def bench_full_step(args, dad, torch):
             w["w" + p] = randn((n_out, n_in), 0.02)
             w["a" + p] = packed_a[p] if p in packed_a else randn((r, n_in), 0.02)
             w["b" + p] = randn((n_out, r), 0.02)
-        kc = randn((B, ctx, Hkv, 128), 1.0)
-        vc = randn((B, ctx, Hkv, 128), 1.0)
+        # ctx valid rows per sequence plus one block of free slots for the append
+        kc = randn((B, ctx + blk, Hkv, 128), 1.0)
+        vc = randn((B, ctx + blk, Hkv, 128), 1.0)
         keep.append((w, kc, vc))
         layers.append(dad.layer_weights(w, kc, vc))
     arr = dad.layer_array(layers)
@@ -189,7 +190,12 @@ def bench_full_step(args, dad, torch):
     u_draft = torch.rand((B, k), dtype=torch.float32, device=dev, generator=gen)
     u_accept = torch.rand((B, k), dtype=torch.float32, device=dev, generator=gen)
     u_sample = torch.rand((B,), dtype=torch.float32, device=dev, generator=gen)
-    cfg = dad.step_config(B, blk, ctx, hid, inter, H, Hkv, r, nl, V)
+    cfg = dad.step_config(B, blk, ctx + blk, hid, inter, H, Hkv, r, nl, V)
+    # the decode loop's form: every layer appends the block's clean keys and
+    # values after the ctx valid rows and the step commits the kept ones; the
+    # lengths go back to ctx before each step so every step does the same work
+    cache_len0 = torch.full((B,), ctx, dtype=torch.int32, device=dev)
+    cache_len = cache_len0.clone()
     logits = torch.empty((rows, V), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(dad.psi_spec_step_workspace(cfg), dtype=torch.uint8, device=dev)
     outs = {"drafts": torch.empty((B, k), dtype=torch.int32, device=dev),
@@ -200,8 +206,9 @@ def bench_full_step(args, dad, torch):
         f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated)")
 
     def step():
+        cache_len.copy_(cache_len0)
         dad.psi_spec_step(cfg, arr, embed, final_norm, lm_head, tokens, u_draft, u_accept, u_sample,
-                          logits=logits, outputs=outs, workspace=ws)
+                          logits=logits, outputs=outs, workspace=ws, cache_len=cache_len)
 
     for _ in range(args.warmup):
         step()
@@ -218,7 +225,7 @@ def bench_full_step(args, dad, torch):
     names = ["uno_step_setup", "uno_rms_norm", "uno_add_rms_norm", "uno_rope", "uno_silu_mul", "uno_lora_down_bf16",
              "uno_lora_gate", "uno_gemm_bf16", "uno_gemm_reduce", "uno_block_attention", "uno_sample_stats",
              "uno_sample_desc", "uno_sample_seg", "uno_sample_resolve", "uno_row_stats", "uno_accept",
-             "uno_draw_seg", "uno_draw_resolve"]
+             "uno_draw_seg", "uno_draw_resolve", "uno_kv_commit"]
     breakdown = {}
     for kn in names:
         ms, cnt = dad.profile_query(kn)
@@ -315,6 +322,8 @@ def bench_full_step(args, dad, torch):
                    "model": "36-layer Qwen3-8B-shaped stack, hidden 4096, MLP 12288, GQA 32/8, head_dim 128, "
                             "rank-128 gated LoRA on q/k/v/o/gate/up/down, vocab 151936",
                    "batch": B, "block": blk, "rows": rows, "ctx_len": ctx, "drafts_per_seq": k,
+                   "kv_cache": "decode loop: ctx_len valid rows per sequence; each layer appends the block's "
+                               "clean k/v and the step commits the kept rows (lengths reset before each step)",
                    "tokens_per_step": tokens_per_step, "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,
