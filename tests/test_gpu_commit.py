@@ -191,3 +191,57 @@ def test_step_decode_loop_two_steps(gpu_lib):
         say(f"  step {step}: committed k/v row rel err {worst:.3g}")
         assert worst <= 2e-2
         o_len = new_len
+
+
+def test_decoder_layer_full_size_decode_loop_sampled(gpu_lib):
+    """One Qwen3-8B-shaped layer in the launch configuration the bench times:
+    128 sequences x (16 clean + 16 noisy) rows, caches of 8192 + 16 rows with
+    8192 valid (two sequences shorter), adapters back to back; the oracle
+    recomputes 2 sampled sequences, their appended rows are checked, and every
+    sequence's rows outside its append are unchanged."""
+    import torch
+    batch, block, cap = 128, 16, 8192 + 16
+    hidden, inter, nh, nkv, r = 4096, 12288, 32, 8, 128
+    say(f"decoder layer decode loop B={batch} block={block} cap={cap} Qwen3-8B shapes (sampled)")
+    c = workloads.decoder_layer_case(batch, block, cap, hidden, inter, nh, nkv, r, seed=4)
+    lens = np.full(batch, 8192)
+    lens[5], lens[120] = 6001, 8191          # a ragged tail, and a sequence with room for 1 of its 16 rows
+    for name in ("k_cache", "v_cache"):
+        c[name] = _fill_slack(c[name], lens)
+    pos = _positions(lens, block)
+    wt = {k: to_dev(v) for k, v in c["weights"].items() if not k.endswith("_f32")}
+    for group in (("q", "k", "v"), ("g", "u")):   # adapters back to back, as the bench stores them
+        cat = torch.cat([wt["a" + p] for p in group], dim=0).contiguous()
+        for i, p in enumerate(group):
+            wt["a" + p] = cat[i * r:(i + 1) * r]
+    kc, vc, h = to_dev(c["k_cache"]), to_dev(c["v_cache"]), to_dev(c["h"])
+    lw = gpu_lib.layer_weights(wt, kc, vc)
+    gpu_lib.decoder_layer(h, lw, to_dev(c["gate"]), to_dev(pos), batch, block, cap, nh, nkv, inter, r,
+                          cache_len=to_dev(lens.astype(np.int32)))
+    torch.cuda.synchronize()
+    got = to_host(h)
+    assert np.all(np.isfinite(got))
+    w64 = {k[:-4]: v.astype(np.float64) for k, v in c["weights"].items() if k.endswith("_f32")}
+    # the caches come back as raw bf16 bits (2 GB each; no float copies of the whole cache)
+    kbits = kc.view(torch.int16).cpu().numpy().view(np.uint16)
+    vbits = vc.view(torch.int16).cpu().numpy().view(np.uint16)
+    n = 2 * block
+    for b in (5, 120, 77):
+        rows = np.arange(b * n, (b + 1) * n)
+        ref, st = oracle.decoder_layer(_f32(c["h"][rows]), w64, c["gate"][rows], pos[rows],
+                                       _f32(c["k_cache"][b:b + 1]), _f32(c["v_cache"][b:b + 1]), block, nh, nkv,
+                                       ctx_lens=lens[b:b + 1])
+        err = row_relerr(got[rows], ref)
+        m = min(block, cap - lens[b])
+        new = slice(lens[b], lens[b] + m)
+        kerr = row_relerr(_f32(kbits[b, new]), st["k"][:m])
+        verr = row_relerr(_f32(vbits[b, new]), st["v"][:m])
+        say(f"  seq {b} (len {lens[b]}): hidden row rel err {err:.3g}, appended k {kerr:.3g}, v {verr:.3g}")
+        assert err <= 2e-2 and kerr <= 2e-2 and verr <= 2e-2
+    # rows outside each sequence's append are untouched, for every sequence (bit for bit)
+    for b in range(batch):
+        m = min(block, cap - lens[b])
+        keep = np.ones(cap, bool)
+        keep[lens[b]:lens[b] + m] = False
+        assert np.array_equal(kbits[b, keep], c["k_cache"][b, keep]), f"seq {b}: k rows outside the append"
+        assert np.array_equal(vbits[b, keep], c["v_cache"][b, keep]), f"seq {b}: v rows outside the append"
