@@ -115,6 +115,7 @@ hipError_t launch_decoder_layer(const DecoderLayerArgs& d, hipStream_t stream) {
     ga.ldy = N;
     ga.t_pre = t_pre;
     ga.ldt_pre = ldt_pre;
+    ga.gate_block = d.gate_block;
     ga.ws = ws + L.lora;
     ga.ws_bytes = d.ws_bytes - L.lora;
     return ga;
@@ -186,6 +187,7 @@ hipError_t launch_decoder_layer(const DecoderLayerArgs& d, hipStream_t stream) {
     ld.lora_scale = d.lora_scale;
     ld.t = t;
     ld.part = ws + L.lpart;
+    ld.gather_blk = d.gate_block;
     return launch_lora_down(ld, stream);
   };
   uint16_t* tqkv = reinterpret_cast<uint16_t*>(ws + L.tqkv);

@@ -153,6 +153,7 @@ uno_status uno_psi_spec_step(hipStream_t stream, const uno_step_config* config, 
     la.r = c.r;
     la.w = &layers[l];
     la.gate = c.r > 0 ? gate : nullptr;
+    la.gate_block = c.block;   // the gates step_setup writes: 0 on each sequence's clean rows, 1 on its noisy rows
     la.positions = pos;
     la.cache_len = cache_len;
     la.rms_eps = c.rms_eps;

@@ -38,6 +38,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -70,6 +71,10 @@ struct GemmParams {
   int seg_n;
   int64_t t2_off;
   uint16_t* y2;
+  // LoRA-down (gemm_dl_kernel) only: > 0 gathers the x rows, logical row i
+  // reading physical row (i / g) * 2g + g + i % g (the noisy rows of
+  // sequences of g clean + g noisy rows); the partials stay in logical rows
+  int gather_blk;
 };
 
 // Output tile of linear index `tile`.  Mode 1: column-major (M-tiles
@@ -537,8 +542,10 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_dl_kernel(GemmParams p) 
       src2[q] = p.b + int64_t(n) * p.ldb;
     } else {
       const int m = min(m0 + rr, p.M - 1);
-      src1[q] = p.x + int64_t(m) * p.ldx;
-      src2[q] = p.t + int64_t(m) * p.ldt;
+      const int g = p.gather_blk;
+      const int pm = g > 0 ? (m / g) * 2 * g + g + m % g : m;
+      src1[q] = p.x + int64_t(pm) * p.ldx;
+      src2[q] = p.t + int64_t(pm) * p.ldt;
     }
   }
   const uint16_t* zero = reinterpret_cast<const uint16_t*>(kZeroChunk);
@@ -734,19 +741,33 @@ __global__ __launch_bounds__(256) void lora_gate_kernel(const float* __restrict_
 
 // The same, four consecutive elements per thread (r % 4 == 0): 16-byte
 // partial loads and an 8-byte store; the splits are summed in the same order.
+// gblk > 0: the structured gate (rows j < gblk of every 2 * gblk are 0, the
+// rest 1) with partials over the gated rows only ([splits][M / 2][r], row
+// (m / 2gblk) * gblk + j - gblk); `gate` is then not read.
 __global__ __launch_bounds__(256) void lora_gate4_kernel(const float* __restrict__ part, int splits, int M, int r,
                                                          const uint8_t* __restrict__ gate, float scale,
-                                                         uint16_t* __restrict__ t) {
+                                                         uint16_t* __restrict__ t, int gblk) {
   const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
   if (i >= int64_t(M) * r) return;
   const int m = int(i / r);
-  if (gate[m] == 0) {
+  int pm = m, prow = M;
+  if (gblk > 0) {
+    const int j = m % (2 * gblk);
+    pm = j < gblk ? -1 : (m / (2 * gblk)) * gblk + (j - gblk);
+    prow = M / 2;
+  } else if (gate[m] == 0) {
+    pm = -1;
+  }
+  if (pm < 0) {
     *reinterpret_cast<uint2*>(t + i) = make_uint2(0u, 0u);
     return;
   }
-  const int64_t plane = int64_t(M) * r;
+  const int64_t plane = int64_t(prow) * r;
+  const float* src = part + int64_t(pm) * r + (i - int64_t(m) * r);
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < splits; ++sp) s += *reinterpret_cast<const f32x4*>(part + sp * plane + i);
+  // unrolled so the loads of 8 splits are in flight together; the adds keep split order
+#pragma unroll 8
+  for (int sp = 0; sp < splits; ++sp) s += *reinterpret_cast<const f32x4*>(src + sp * plane);
   *reinterpret_cast<uint2*>(t + i) =
       make_uint2(pack_bf16x2(scale * s[0], scale * s[1]), pack_bf16x2(scale * s[2], scale * s[3]));
 }
@@ -976,7 +997,13 @@ TileCfg lora_down_cfg(int64_t M, int64_t r, int64_t K) {
     // at 4096 x 4096 the q|k|v group (r = 384) takes 28 us against 41 with
     // 128 x 128 tiles, gate|up (256) 22.5 against 30.6
     shape = r % 384 == 0 ? 18 : (r % 256 == 0 ? 21 : 15);
-    s = 8;
+    // at least 8 K-splits, more when the row tiles alone leave CUs idle:
+    // 2048 rows take 16 tiles x 12 splits.  More splits shorten this kernel
+    // but lengthen the split sum (every split is re-read): inside the decode
+    // step (noisy rows gathered) the two together take 4.57 ms per step at 8
+    // splits, 4.38 at 12 and 4.48 at 16
+    const int64_t tiles_m = (M + 127) / 128;
+    s = std::max<int64_t>(8, (192 + tiles_m - 1) / tiles_m);
   } else {
     const int64_t tiles = ((M + 63) / 64) * ((r + 63) / 64);
     s = (256 + tiles - 1) / tiles;
@@ -1011,13 +1038,33 @@ size_t lora_down_part_bytes(int64_t M, int64_t n, int64_t K) {
   return align_up(size_t(lora_down_splits(M, n, K)) * size_t(M) * size_t(n) * 4, 256);
 }
 
+namespace {
+
+bool is_dl_shape(int shape) { return shape == 15 || shape == 18 || shape == 21; }
+
+// The gathered LoRA-down (structured gate): over the M / 2 gated rows only,
+// when those rows take a direct-to-LDS tile, the gate kernel's vector form
+// applies and the partials fit the space sized for the full M rows.
+bool lora_gather_ok(const LoraDownArgs& a) {
+  if (a.gather_blk <= 0 || a.M % (2 * a.gather_blk) != 0) return false;
+  if (!is_dl_shape(lora_down_cfg(a.M / 2, a.n, a.K).shape)) return false;
+  if (a.n % 4 != 0 || (reinterpret_cast<uintptr_t>(a.part) & 15u) != 0 || (reinterpret_cast<uintptr_t>(a.t) & 7u) != 0)
+    return false;
+  return lora_down_part_bytes(a.M / 2, a.n, a.K) <= lora_down_part_bytes(a.M, a.n, a.K);
+}
+
+}  // namespace
+
 // T[M][n] = bf16(s * g[m] * x A^T) for the n rows of A (one projection's r,
 // or several projections' adapters stored back to back): split-K MFMA GEMM
 // into fp32 partials, then lora_gate_kernel sums them in a fixed order.
 hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t stream) {
-  const int splits = lora_down_splits(a.M, a.n, a.K);
+  // rows the GEMM reads: all M, or only the gated M / 2 under the structured gate
+  const bool gather = lora_gather_ok(a);
+  const int64_t Mg = gather ? a.M / 2 : a.M;
+  const int splits = lora_down_splits(Mg, a.n, a.K);
   GemmParams d{};
-  d.M = int(a.M);
+  d.M = int(Mg);
   d.N = int(a.n);
   d.K1 = int(a.K);
   d.K2 = 0;
@@ -1030,12 +1077,13 @@ hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t stream) {
   d.b = d.w;
   d.ldb = d.ldw;
   d.part = static_cast<float*>(a.part);
-  TileCfg dc = lora_down_cfg(a.M, a.n, a.K);
+  d.gather_blk = gather ? a.gather_blk : 0;
+  TileCfg dc = lora_down_cfg(Mg, a.n, a.K);
   {
     // tuning override "<shape name>/<splits>" (sweeps only); the split count sizes the
     // partials, so it may not exceed the one the workspace was sized for
     const char* env = getenv("UNO_LORA_TILE");
-    if (env) {
+    if (env && !gather) {
       char nm[32] = {0};
       const char* slash = strchr(env, '/');
       const size_t len = slash ? size_t(slash - env) : strlen(env);
@@ -1054,7 +1102,8 @@ hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t stream) {
   // the vector form needs 4-element rows and 16-byte aligned partials / 8-byte aligned T
   if (a.n % 4 == 0 && (reinterpret_cast<uintptr_t>(a.part) & 15u) == 0 && (reinterpret_cast<uintptr_t>(a.t) & 7u) == 0)
     hipLaunchKernelGGL(lora_gate4_kernel, dim3(unsigned((n / 4 + 255) / 256)), dim3(256), 0, stream,
-                       static_cast<const float*>(a.part), dc.splits, int(a.M), int(a.n), a.gate, a.lora_scale, a.t);
+                       static_cast<const float*>(a.part), dc.splits, int(a.M), int(a.n), a.gate, a.lora_scale, a.t,
+                       gather ? a.gather_blk : 0);
   else
     hipLaunchKernelGGL(lora_gate_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream,
                        static_cast<const float*>(a.part), dc.splits, int(a.M), int(a.n), a.gate, a.lora_scale, a.t);
@@ -1203,6 +1252,7 @@ hipError_t launch_gated_lora(const GatedLoraArgs& a, hipStream_t stream) {
     ld.lora_scale = a.lora_scale;
     ld.t = tw;
     ld.part = ws;
+    ld.gather_blk = a.gate_block;
     ws += align_up(size_t(lora_down_splits(a.M, a.r, a.K)) * size_t(a.M) * size_t(a.r) * 4, 256);
     hipError_t e = launch_lora_down(ld, stream);
     if (e != hipSuccess) return e;

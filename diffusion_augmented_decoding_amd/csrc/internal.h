@@ -73,6 +73,9 @@ struct GatedLoraArgs {
   void* y; int64_t ldy;
   void* ws; size_t ws_bytes;
   const void* t_pre; int64_t ldt_pre;   // optional (bf16 path): T = s g (x A^T) computed by the caller
+  int gate_block;                       // > 0: the gate is 0 on rows j < gate_block and 1 on the rest of
+                                        // every 2 * gate_block rows (as the decode step builds it); the
+                                        // LoRA-down then reads only the gated rows (`gate` is not read)
 };
 size_t gated_lora_workspace_bytes(uno_dtype dtype, int64_t M, int64_t N, int64_t K, int64_t r);
 
@@ -85,6 +88,7 @@ struct LoraDownArgs {
   float lora_scale;
   uint16_t* t;                       // [M][n]
   void* part;                        // fp32 partials, lora_down_part_bytes(M, n, K)
+  int gather_blk;                    // > 0: structured gate as GatedLoraArgs::gate_block
 };
 size_t lora_down_part_bytes(int64_t M, int64_t n, int64_t K);
 hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t stream);
@@ -228,6 +232,7 @@ struct DecoderLayerArgs {
   const int32_t* cache_len;          // [batch] valid cache rows (nullptr: ctx rows each); when set,
                                      // ctx is the capacity and the clean rows' k, v are appended
                                      // at slots cache_len[b] + j (the length itself is not changed)
+  int gate_block;                    // > 0: `gate` follows the step's clean/noisy pattern (GatedLoraArgs)
   float rms_eps, rope_theta, lora_scale;
   void* h;                           // bf16 [rows][hidden], updated in place
   void* ws; size_t ws_bytes;

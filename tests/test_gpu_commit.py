@@ -245,3 +245,51 @@ def test_decoder_layer_full_size_decode_loop_sampled(gpu_lib):
         keep[lens[b]:lens[b] + m] = False
         assert np.array_equal(kbits[b, keep], c["k_cache"][b, keep]), f"seq {b}: k rows outside the append"
         assert np.array_equal(vbits[b, keep], c["v_cache"][b, keep]), f"seq {b}: v rows outside the append"
+
+
+def test_step_full_size_decode_loop_packed_adapters(gpu_lib):
+    """The launch configuration the bench times, with one layer: 128 sequences
+    x (16 clean + 16 noisy) rows, caches of 8192 + 16 rows with 8192 valid
+    (one sequence shorter), rank-128 adapters of q/k/v and gate/up stored back
+    to back (grouped LoRA-down over the noisy rows only), V = 151,936.  The
+    oracle recomputes 2 sampled sequences: logits within the bar, committed
+    lengths exact, committed rows within the bar."""
+    import torch
+    batch, block, cap, hidden, inter, nh, nkv, r, vocab = 128, 16, 8192 + 16, 4096, 12288, 32, 8, 128, 151936
+    say(f"step decode loop full size, 1 layer, packed adapters: B={batch} block={block} cap={cap} V={vocab}")
+    c = workloads.step_case(batch, block, cap, hidden, inter, nh, nkv, r, 1, vocab, seed=17)
+    lens = np.full(batch, 8192)
+    lens[40] = 5000
+    c["k_caches"][0] = _fill_slack(c["k_caches"][0], lens)
+    c["v_caches"][0] = _fill_slack(c["v_caches"][0], lens)
+    wt = {k: to_dev(v) for k, v in c["layers"][0].items() if not k.endswith("_f32")}
+    for group in (("q", "k", "v"), ("g", "u")):
+        cat = torch.cat([wt["a" + p] for p in group], dim=0).contiguous()
+        for i, p in enumerate(group):
+            wt["a" + p] = cat[i * r:(i + 1) * r]
+    kc, vc = to_dev(c["k_caches"][0]), to_dev(c["v_caches"][0])
+    cfg = gpu_lib.step_config(batch, block, cap, hidden, inter, nh, nkv, r, 1, vocab)
+    cl = to_dev(lens.astype(np.int32))
+    out = gpu_lib.psi_spec_step(cfg, [gpu_lib.layer_weights(wt, kc, vc)], to_dev(c["embed"]), to_dev(c["final_norm"]),
+                                to_dev(c["lm_head"]), to_dev(c["tokens"]), to_dev(c["u_draft"]),
+                                to_dev(c["u_accept"]), to_dev(c["u_sample"]), cache_len=cl)
+    torch.cuda.synchronize()
+    lg = to_host(out["logits"])
+    acc = to_host(out["accept_len"])
+    assert np.all(np.isfinite(lg))
+    np.testing.assert_array_equal(to_host(cl), np.minimum(cap, lens + acc + 1))
+    w64 = [{k[:-4]: v.astype(np.float64) for k, v in c["layers"][0].items() if k.endswith("_f32")}]
+    n = 2 * block
+    for b in (40, 101):
+        sl = slice(b, b + 1)
+        ref = oracle.decode_step(c["tokens"][sl], _f32(c["embed"]), w64, [_f32(c["k_caches"][0][sl])],
+                                 [_f32(c["v_caches"][0][sl])], _f32(c["final_norm"]), _f32(c["lm_head"]),
+                                 c["u_draft"][sl], c["u_accept"][sl], c["u_sample"][sl], block, nh, nkv,
+                                 cache_len=lens[sl])
+        err = row_relerr(lg[b * n:(b + 1) * n], ref["logits"])
+        kept = slice(lens[b], lens[b] + acc[b] + 1)
+        kbits = kc[b, kept].view(torch.int16).cpu().numpy().view(np.uint16)
+        kerr = row_relerr(_f32(kbits), ref["k_clean"][0][0, :acc[b] + 1])
+        say(f"  seq {b} (len {lens[b]}): logits row rel err {err:.3g}, committed k row rel err {kerr:.3g}; "
+            f"L gpu {acc[b]} oracle {ref['accept_len'][0]}")
+        assert err <= 2e-2 and kerr <= 2e-2
