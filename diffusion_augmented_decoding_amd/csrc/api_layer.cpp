@@ -196,7 +196,7 @@ hipError_t launch_decoder_layer(const DecoderLayerArgs& d, hipStream_t stream) {
   const bool gu_grouped = packed(UNO_PROJ_GATE, 2);
   const int64_t r3 = 3 * int64_t(d.r), r2 = 2 * int64_t(d.r);
 
-  hipError_t e = norm(nullptr, d.w->attn_norm, a);
+  hipError_t e = d.norm_ready ? hipSuccess : norm(nullptr, d.w->attn_norm, a);
   if (e == hipSuccess && qkv_grouped) e = group_down(UNO_PROJ_Q, 3, a, tqkv);
   if (e == hipSuccess) e = proj(UNO_PROJ_Q, a, d.hidden, qd, q, qkv_grouped ? tqkv : nullptr, r3);
   if (e == hipSuccess) {
@@ -272,7 +272,10 @@ hipError_t launch_decoder_layer(const DecoderLayerArgs& d, hipStream_t stream) {
     e = launch_silu_mul(sa, stream);
   }
   if (e == hipSuccess) e = proj(UNO_PROJ_DOWN, g, d.inter, d.hidden, o);
-  if (e == hipSuccess) e = norm(o, d.w->attn_norm, nullptr);         // h += down
+  // h += down; with a next norm in the chain, the same pass writes its output
+  // (the gate/up GEMM has consumed `a` by now, so it may be overwritten)
+  if (e == hipSuccess) e = norm(o, d.next_norm ? d.next_norm : d.w->attn_norm,
+                                d.next_norm ? (d.next_out ? d.next_out : a) : nullptr);
   return e;
 }
 

@@ -154,6 +154,11 @@ uno_status uno_psi_spec_step(hipStream_t stream, const uno_step_config* config, 
     la.w = &layers[l];
     la.gate = c.r > 0 ? gate : nullptr;
     la.gate_block = c.block;   // the gates step_setup writes: 0 on each sequence's clean rows, 1 on its noisy rows
+    // each layer's closing residual add also normalises for what follows: the
+    // next layer's attention norm, or the final norm before the LM head
+    la.norm_ready = l > 0;
+    la.next_norm = l + 1 < c.n_layers ? layers[l + 1].attn_norm : final_norm;
+    la.next_out = l + 1 < c.n_layers ? nullptr : a;
     la.positions = pos;
     la.cache_len = cache_len;
     la.rms_eps = c.rms_eps;
@@ -165,8 +170,9 @@ uno_status uno_psi_spec_step(hipStream_t stream, const uno_step_config* config, 
     e = launch_decoder_layer(la, stream);
   }
 
-  // final norm and LM head (no adapter): logits [rows][vocab]
-  if (e == hipSuccess) {
+  // final norm (done by the last layer's closing pass when there are layers)
+  // and LM head (no adapter): logits [rows][vocab]
+  if (e == hipSuccess && c.n_layers == 0) {
     RmsNormArgs na{};
     na.rows = rows;
     na.dim = c.hidden;

@@ -233,6 +233,13 @@ struct DecoderLayerArgs {
                                      // ctx is the capacity and the clean rows' k, v are appended
                                      // at slots cache_len[b] + j (the length itself is not changed)
   int gate_block;                    // > 0: `gate` follows the step's clean/noisy pattern (GatedLoraArgs)
+  // Chaining layers (the decode step): norm_ready = the scratch buffer `a`
+  // already holds rmsnorm(h, attn_norm) (written by the previous layer), so the
+  // first norm is skipped; next_norm != nullptr = the closing residual add also
+  // writes rmsnorm(h, next_norm) to next_out (nullptr: this layer's `a`).
+  bool norm_ready;
+  const void* next_norm;
+  void* next_out;
   float rms_eps, rope_theta, lora_scale;
   void* h;                           // bf16 [rows][hidden], updated in place
   void* ws; size_t ws_bytes;
