@@ -15,6 +15,7 @@ import pytest
 
 import oracle
 import workloads
+from _layer_cases import APPEND_CASES, FULL_CASES, ids as layer_ids, make as make_layer_case
 from _parity import row_relerr, say, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
@@ -74,22 +75,20 @@ def test_kv_commit_lengths(gpu_lib):
     np.testing.assert_array_equal(to_host(cl), np.minimum(50, lens + acc + 1))
 
 
-def _positions(lens, block):
-    return np.concatenate([np.concatenate([np.arange(block), np.arange(block)]) + n for n in lens]).astype(np.int32)
-
-
-@pytest.mark.parametrize("batch,block,cap,lens", [
-    (3, 4, 40, [0, 17, 38]),        # the last sequence has room for 2 of its 4 clean rows
-    (2, 16, 300, [250, 5]),
-])
-def test_decoder_layer_appends_clean_rows(gpu_lib, batch, block, cap, lens):
-    say(f"decoder layer with cache lengths B={batch} block={block} cap={cap} lens={lens}")
+@pytest.mark.parametrize("lc", APPEND_CASES, ids=layer_ids(APPEND_CASES))
+def test_decoder_layer_appends_clean_rows(gpu_lib, lc):
+    """A layer over caches of per-sequence lengths (tests/_layer_cases.py): the
+    hidden state within the bar, the clean rows' rotated k and their v written
+    after each sequence's valid rows (only the rows that fit the capacity),
+    every other cache row bit-identical."""
+    batch, block, cap, lens = lc["batch"], lc["block"], lc["ctx"], lc["lens"]
+    nh, nkv, inter, r = lc["nh"], lc["nkv"], lc["inter"], lc["r"]
+    say(f"decoder layer with cache lengths {lc['name']}: B={batch} block={block} cap={cap} lens={lens}")
     import torch
-    hidden, inter, nh, nkv, r = 256, 512, 4, 2, 16
-    c = workloads.decoder_layer_case(batch, block, cap, hidden, inter, nh, nkv, r, seed=block + cap)
+    c = make_layer_case(lc)
     kc0 = _fill_slack(c["k_cache"], lens)
     vc0 = _fill_slack(c["v_cache"], lens)
-    pos = _positions(lens, block)
+    pos = c["positions"]
     wt = {k: to_dev(v) for k, v in c["weights"].items() if not k.endswith("_f32")}
     kc, vc, h = to_dev(kc0), to_dev(vc0), to_dev(c["h"])
     lw = gpu_lib.layer_weights(wt, kc, vc)
@@ -193,22 +192,21 @@ def test_step_decode_loop_two_steps(gpu_lib):
         o_len = new_len
 
 
-def test_decoder_layer_full_size_decode_loop_sampled(gpu_lib):
+@pytest.mark.parametrize("lc", FULL_CASES[1:], ids=layer_ids(FULL_CASES[1:]))
+def test_decoder_layer_full_size_decode_loop_sampled(gpu_lib, lc):
     """One Qwen3-8B-shaped layer in the launch configuration the bench times:
     128 sequences x (16 clean + 16 noisy) rows, caches of 8192 + 16 rows with
     8192 valid (two sequences shorter), adapters back to back; the oracle
-    recomputes 2 sampled sequences, their appended rows are checked, and every
+    recomputes 3 sampled sequences, their appended rows are checked, and every
     sequence's rows outside its append are unchanged."""
     import torch
-    batch, block, cap = 128, 16, 8192 + 16
-    hidden, inter, nh, nkv, r = 4096, 12288, 32, 8, 128
-    say(f"decoder layer decode loop B={batch} block={block} cap={cap} Qwen3-8B shapes (sampled)")
-    c = workloads.decoder_layer_case(batch, block, cap, hidden, inter, nh, nkv, r, seed=4)
-    lens = np.full(batch, 8192)
-    lens[5], lens[120] = 6001, 8191          # a ragged tail, and a sequence with room for 1 of its 16 rows
+    batch, block, cap, lens = lc["batch"], lc["block"], lc["ctx"], np.asarray(lc["lens"])
+    nh, nkv, inter, r = lc["nh"], lc["nkv"], lc["inter"], lc["r"]
+    say(f"decoder layer {lc['name']}: B={batch} block={block} cap={cap} Qwen3-8B shapes (sampled {lc['seqs']})")
+    c = make_layer_case(lc)
     for name in ("k_cache", "v_cache"):
         c[name] = _fill_slack(c[name], lens)
-    pos = _positions(lens, block)
+    pos = c["positions"]
     wt = {k: to_dev(v) for k, v in c["weights"].items() if not k.endswith("_f32")}
     for group in (("q", "k", "v"), ("g", "u")):   # adapters back to back, as the bench stores them
         cat = torch.cat([wt["a" + p] for p in group], dim=0).contiguous()
@@ -226,7 +224,7 @@ def test_decoder_layer_full_size_decode_loop_sampled(gpu_lib):
     kbits = kc.view(torch.int16).cpu().numpy().view(np.uint16)
     vbits = vc.view(torch.int16).cpu().numpy().view(np.uint16)
     n = 2 * block
-    for b in (5, 120, 77):
+    for b in lc["seqs"]:
         rows = np.arange(b * n, (b + 1) * n)
         ref, st = oracle.decoder_layer(_f32(c["h"][rows]), w64, c["gate"][rows], pos[rows],
                                        _f32(c["k_cache"][b:b + 1]), _f32(c["v_cache"][b:b + 1]), block, nh, nkv,

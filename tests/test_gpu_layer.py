@@ -14,12 +14,10 @@ import pytest
 
 import oracle
 import workloads
+from _layer_cases import FULL_CASES, LAYER_CASES, ids as layer_ids, make as make_layer_case, seq_rows as layer_seq_rows
 from _parity import TIE, draw_is_valid, row_relerr, say, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
-
-QWEN = dict(hidden=4096, inter=12288, n_heads=32, n_kv_heads=8, r=128)
-
 
 def _bits_dev(bits):
     return to_dev(bits)
@@ -245,65 +243,37 @@ def _layer_ref(c, seqs):
     return rows, out
 
 
-@pytest.mark.parametrize("batch,block,ctx,hidden,inter,nh,nkv,r,packed", [
-    (2, 4, 40, 256, 512, 4, 2, 16, False),
-    (2, 4, 40, 256, 512, 4, 2, 16, True),
-    (3, 16, 300, 512, 1024, 8, 2, 32, False),
-    (3, 16, 300, 512, 1024, 8, 2, 32, True),
-    (1, 2, 0, 128, 384, 2, 1, 8, False),
-    # rank a multiple of 64 with adapters back to back: gate, up and SwiGLU run
-    # as one GEMM (ragged feature tile: 1088 = 8.5 x 128)
-    (2, 8, 136, 512, 1088, 8, 2, 64, True),
-    (2, 8, 136, 512, 1088, 8, 2, 64, False),
-])
-def test_decoder_layer(gpu_lib, batch, block, ctx, hidden, inter, nh, nkv, r, packed):
-    say(f"decoder layer B={batch} block={block} ctx={ctx} hidden={hidden} inter={inter} H={nh}/{nkv} r={r} "
-        f"packed adapters={packed}")
-    c = workloads.decoder_layer_case(batch, block, ctx, hidden, inter, nh, nkv, r, seed=batch + ctx)
-    got = _run_layer(gpu_lib, c, packed=packed)
-    rows, ref = _layer_ref(c, list(range(batch)))
-    err = row_relerr(got[rows], ref)
-    say(f"  row rel err {err:.3g}")
-    assert err <= 2e-2
-
-
-def test_decoder_layer_2048_rows_sampled(gpu_lib):
-    """2048 rows (64 sequences x 32) with adapters back to back: k and v run
-    as one two-segment GEMM and gate/up/SwiGLU as one GEMM; the oracle
-    recomputes 2 sampled sequences."""
-    say("decoder layer B=64 block=16 ctx=40 hidden=512 inter=1024 H=8/2 r=64 (sampled)")
-    c = workloads.decoder_layer_case(64, 16, 40, 512, 1024, 8, 2, 64, seed=21)
-    got = _run_layer(gpu_lib, c, packed=True)
+@pytest.mark.parametrize("lc", LAYER_CASES, ids=layer_ids(LAYER_CASES))
+def test_decoder_layer(gpu_lib, lc):
+    """The layer cases of tests/_layer_cases.py: small shapes with the adapters
+    stored apart and back to back, no cache, the fused gate/up/SwiGLU GEMM
+    (rank 64 back to back, ragged 1088-feature tail), 2048 rows (k and v as one
+    two-segment GEMM) on 2 sampled sequences, and no adapters at all.  Each
+    planted wiring mistake moves these outputs by >= 3x the bar
+    (tests/test_layer_mutations.py)."""
+    say(f"decoder layer {lc['name']}: B={lc['batch']} block={lc['block']} ctx={lc['ctx']} hidden={lc['hidden']} "
+        f"inter={lc['inter']} H={lc['nh']}/{lc['nkv']} r={lc['r']} packed={lc['packed']} gate={lc['gate']}")
+    c = make_layer_case(lc)
+    got = _run_layer(gpu_lib, c, gate=lc["gate"], packed=lc["packed"])
     assert np.all(np.isfinite(got))
-    rows, ref = _layer_ref(c, [3, 60])
+    seqs, _ = layer_seq_rows(lc)
+    rows, ref = _layer_ref(c, list(seqs))
     err = row_relerr(got[rows], ref)
     say(f"  row rel err {err:.3g}")
     assert err <= 2e-2
 
 
-def test_decoder_layer_without_adapters(gpu_lib):
-    """No gate vector: every row takes the AR weights only (the fused
-    gate/up/SwiGLU GEMM without adapter columns); the oracle sees all gates 0."""
-    say("decoder layer without adapters B=2 block=8 ctx=136 hidden=512 inter=1088")
-    c = workloads.decoder_layer_case(2, 8, 136, 512, 1088, 8, 2, 64, seed=11)
-    got = _run_layer(gpu_lib, c, gate=False)
-    c0 = dict(c, gate=np.zeros_like(c["gate"]))
-    rows, ref = _layer_ref(c0, [0, 1])
-    err = row_relerr(got[rows], ref)
-    say(f"  row rel err {err:.3g}")
-    assert err <= 2e-2
-
-
-def test_decoder_layer_full_size_sampled_sequences(gpu_lib):
+@pytest.mark.parametrize("lc", FULL_CASES[:1], ids=layer_ids(FULL_CASES[:1]))
+def test_decoder_layer_full_size_sampled_sequences(gpu_lib, lc):
     """One Qwen3-8B-shaped layer at the decode-step shape: 128 sequences x
     (16 clean + 16 noisy) rows, 8K cache, rank-128 adapters stored as the
     bench stores them (q/k/v and gate/up adapters back to back); the oracle
     recomputes 2 sampled sequences (64 rows, both gate values)."""
-    say("decoder layer B=128 block=16 ctx=8192 Qwen3-8B shapes (sampled)")
-    c = workloads.decoder_layer_case(128, 16, 8192, seed=3, **QWEN)
+    say(f"decoder layer {lc['name']}: B=128 block=16 ctx=8192 Qwen3-8B shapes (sampled {lc['seqs']})")
+    c = make_layer_case(lc)
     got = _run_layer(gpu_lib, c, packed=True)
     assert np.all(np.isfinite(got))
-    rows, ref = _layer_ref(c, [5, 120])
+    rows, ref = _layer_ref(c, lc["seqs"])
     err = row_relerr(got[rows], ref)
     say(f"  row rel err {err:.3g}")
     assert err <= 2e-2

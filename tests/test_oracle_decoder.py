@@ -175,3 +175,85 @@ def test_lm_head_matches_torch_pipeline():
     a = a.to(torch.float32).to(torch.bfloat16).to(torch.float64)
     ref = (a @ torch.from_numpy(wl).T).numpy()
     np.testing.assert_allclose(oracle.lm_head(h, nw, wl), ref, rtol=1e-12, atol=1e-12)
+
+
+def _torch_layer(h, w, gate, pos, kc, vc, block, nh, nkv, ctx_lens=None, eps=1e-6, theta=1.0e6):
+    """The layer written independently of the oracle, from torch CPU float64
+    primitives: F.rms_norm, F.linear for W x and the gated B(A x), RoPE as a
+    complex rotation (torch.polar), F.scaled_dot_product_attention under an
+    explicit boolean block mask, F.silu(gate) * up, residual adds; storage
+    rounding fp32 -> bf16 at the same points as the GPU kernels."""
+    F = torch.nn.functional
+    T = torch.float64
+
+    def t(a):
+        return torch.as_tensor(np.asarray(a, dtype=np.float64))
+
+    def bf(x):
+        return x.to(torch.float32).to(torch.bfloat16).to(T)
+
+    H = t(h)
+    rows, hidden = H.shape
+    n = 2 * block
+    bsz = rows // n
+    g = torch.as_tensor(np.asarray(gate, dtype=np.float64))[:, None]
+
+    def lin(x, p):
+        return bf(F.linear(x, t(w["w" + p])) + g * F.linear(F.linear(x, t(w["a" + p])), t(w["b" + p])))
+
+    def rot(x):
+        z = torch.complex(x[..., :64], x[..., 64:])
+        freq = theta ** (-torch.arange(64, dtype=T) / 64.0)
+        ang = torch.as_tensor(np.asarray(pos, dtype=np.float64))[:, None] * freq[None, :]
+        z = z * torch.polar(torch.ones_like(ang), ang)[:, None, :]
+        return torch.cat([z.real, z.imag], dim=-1)
+
+    a = bf(F.rms_norm(H, (hidden,), t(w["attn_norm"]), eps))
+    q = bf(rot(lin(a, "q").view(rows, nh, 128)))
+    k = bf(rot(lin(a, "k").view(rows, nkv, 128)))
+    v = lin(a, "v").view(rows, nkv, 128)
+    blk = torch.zeros(n, n, dtype=torch.bool)
+    blk[:block, :block] = torch.ones(block, block, dtype=torch.bool).tril()   # clean: causal over clean rows
+    blk[block:, :] = True                                                     # noisy: the whole block
+    att = torch.empty(rows, nh, 128, dtype=T)
+    cap = np.asarray(kc).shape[1]
+    for b in range(bsz):
+        c = cap if ctx_lens is None else int(ctx_lens[b])
+        sl = slice(b * n, (b + 1) * n)
+        keys = torch.cat([t(kc[b, :c]), k[sl]], dim=0).transpose(0, 1).repeat_interleave(nh // nkv, dim=0)
+        vals = torch.cat([t(vc[b, :c]), v[sl]], dim=0).transpose(0, 1).repeat_interleave(nh // nkv, dim=0)
+        mask = torch.cat([torch.ones(n, c, dtype=torch.bool), blk], dim=1)
+        att[sl] = F.scaled_dot_product_attention(q[sl].transpose(0, 1), keys, vals, attn_mask=mask).transpose(0, 1)
+    att = bf(att.reshape(rows, nh * 128))
+    h1 = bf(H + lin(att, "o"))
+    a2 = bf(F.rms_norm(h1, (hidden,), t(w["mlp_norm"]), eps))
+    m = bf(F.silu(lin(a2, "g")) * lin(a2, "u"))
+    return bf(h1 + lin(m, "d")).numpy()
+
+
+@pytest.mark.parametrize("lens", [None, [9, 0, 4]])
+def test_decoder_layer_matches_torch_composition(lens):
+    """oracle.decoder_layer against the torch composition above, with the
+    whole cache valid and with per-sequence lengths (one empty).  Both sides
+    compute in float64 and round to bf16 at the same points; summation order
+    differs, so a value sitting on a bf16 rounding boundary may land one bf16
+    ulp apart, which can then move later values by a few ulps."""
+    hidden, inter, nh, nkv, r, block, ctx, bsz = 256, 384, 4, 2, 16, 3, 9, 3
+    w = _layer_weights(hidden, inter, nh, nkv, r, scale=0.05, seed=7)
+    g = np.random.default_rng(8)
+    h = oracle.round_bf16(0.1 * g.standard_normal((bsz * 2 * block, hidden)))
+    gate = np.tile(np.concatenate([np.zeros(block), np.ones(block)]).astype(np.uint8), bsz)
+    starts = [ctx] * bsz if lens is None else lens
+    pos = np.concatenate([np.arange(2 * block) + s for s in starts])
+    kc = oracle.round_bf16(g.standard_normal((bsz, ctx, nkv, 128)))
+    vc = oracle.round_bf16(g.standard_normal((bsz, ctx, nkv, 128)))
+    if lens is not None:
+        for b, n in enumerate(lens):      # unused capacity: large values a wrong mask would pick up
+            kc[b, n:] = 30.0
+            vc[b, n:] = -30.0
+    got, _ = oracle.decoder_layer(h, w, gate, pos, kc, vc, block, nh, nkv, ctx_lens=lens)
+    ref = _torch_layer(h, w, gate, pos, kc, vc, block, nh, nkv, ctx_lens=lens)
+    assert np.mean(got == ref) > 0.999
+    np.testing.assert_allclose(got, ref, rtol=4 * 2.0 ** -8, atol=1e-3)
+    # the layer moved the stream: the comparison is not of the identity
+    assert np.max(np.abs(got - h)) > 0.1 * np.max(np.abs(h))

@@ -389,20 +389,21 @@ def kv_cache_case(batch, ctx, n_kv_heads, seed=0, layer=0, std=1.0, workers=None
 
 
 def block_positions(batch, block, ctx):
-    """Clean row i and noisy row i of every sequence sit at position ctx + i."""
-    per = np.concatenate([np.arange(block), np.arange(block)]) + ctx
+    """Clean row i of every sequence sits at position ctx + i and noisy row i
+    at ctx + block + i (the noisy rows stand for the next block)."""
+    per = np.arange(2 * block) + ctx
     return np.tile(per, batch).astype(np.int32)
 
 
 def decoder_layer_case(batch, block, ctx, hidden, inter, n_heads, n_kv_heads, r, seed=0, layer=0,
-                       weight_std=0.02, norm_std=0.1, kv_std=1.0, workers=None):
+                       weight_std=0.02, norm_std=0.1, kv_std=1.0, workers=None, x_std=1.0):
     """Inputs of one decoder layer over `batch` sequences of `block` clean +
-    `block` noisy rows: residual stream h [rows, hidden], gate (0 clean,
-    1 noisy), positions, KV cache [batch, ctx, Hkv, 128] and the weights (all
-    bf16 bits).  Sequence b's rows and cache can be regenerated alone with
-    layer_seq_rows / kv_cache_seq."""
+    `block` noisy rows: residual stream h [rows, hidden] ~ N(0, x_std^2), gate
+    (0 clean, 1 noisy), positions, KV cache [batch, ctx, Hkv, 128] ~
+    N(0, kv_std^2) and the weights (all bf16 bits).  Sequence b's rows and
+    cache can be regenerated alone with layer_seq_rows / kv_cache_seq."""
     rows = batch * 2 * block
-    h = np.concatenate([layer_seq_rows(seed, b, block, hidden) for b in range(batch)], axis=0)
+    h = np.concatenate([layer_seq_rows(seed, b, block, hidden, x_std) for b in range(batch)], axis=0)
     kc, vc = kv_cache_case(batch, ctx, n_kv_heads, seed, layer, kv_std, workers)
     return {"batch": batch, "block": block, "ctx": ctx, "hidden": hidden, "inter": inter,
             "n_heads": n_heads, "n_kv_heads": n_kv_heads, "r": r, "seed": seed, "layer": layer,
