@@ -165,6 +165,13 @@ def bench_full_step(args, dad, torch):
     qd, kvd = H * 128, Hkv * 128
     shapes = {"q": (qd, hid), "k": (kvd, hid), "v": (kvd, hid), "o": (hid, qd), "g": (inter, hid),
               "u": (inter, hid), "d": (hid, inter)}
+    # the decode loop: every step may keep up to a block of rows, so the
+    # caches hold ctx valid rows plus a block of room for every step run
+    n_prof = 2
+    n_total = args.warmup + n_prof + args.steps
+    if n_total > 512:
+        raise SystemExit("at most 512 warmup + timed steps (the KV capacity grows with the step count)")
+    cap = ctx + blk * (n_total + 1)
     layers, keep = [], []
     for li in range(nl):
         w = {"attn_norm": 1.0 + randn((hid,), 0.1), "mlp_norm": 1.0 + randn((hid,), 0.1)}
@@ -177,9 +184,8 @@ def bench_full_step(args, dad, torch):
             w["w" + p] = randn((n_out, n_in), 0.02)
             w["a" + p] = packed_a[p] if p in packed_a else randn((r, n_in), 0.02)
             w["b" + p] = randn((n_out, r), 0.02)
-        # ctx valid rows per sequence plus one block of free slots for the append
-        kc = randn((B, ctx + blk, Hkv, 128), 1.0)
-        vc = randn((B, ctx + blk, Hkv, 128), 1.0)
+        kc = randn((B, cap, Hkv, 128), 1.0)
+        vc = randn((B, cap, Hkv, 128), 1.0)
         keep.append((w, kc, vc))
         layers.append(dad.layer_weights(w, kc, vc))
     arr = dad.layer_array(layers)
@@ -190,25 +196,30 @@ def bench_full_step(args, dad, torch):
     u_draft = torch.rand((B, k), dtype=torch.float32, device=dev, generator=gen)
     u_accept = torch.rand((B, k), dtype=torch.float32, device=dev, generator=gen)
     u_sample = torch.rand((B,), dtype=torch.float32, device=dev, generator=gen)
-    cfg = dad.step_config(B, blk, ctx + blk, hid, inter, H, Hkv, r, nl, V)
-    # the decode loop's form: every layer appends the block's clean keys and
-    # values after the ctx valid rows and the step commits the kept ones; the
-    # lengths go back to ctx before each step so every step does the same work
-    cache_len0 = torch.full((B,), ctx, dtype=torch.int32, device=dev)
-    cache_len = cache_len0.clone()
-    logits = torch.empty((rows, V), dtype=torch.bfloat16, device=dev)
+    cfg = dad.step_config(B, blk, cap, hid, inter, H, Hkv, r, nl, V)
+    # the decode loop's form: each step takes the previous step's next ids
+    # (written in place over `tokens`), verifies their drafts against the
+    # previous step's noisy-row logits (two logits buffers used in turn),
+    # appends its clean keys and values in every layer and commits the kept
+    # rows, so the caches grow from ctx rows by the emitted tokens
+    cache_len = torch.full((B,), ctx, dtype=torch.int32, device=dev)
+    bufs = [torch.empty((rows, V), dtype=torch.bfloat16, device=dev) for _ in range(2)]
     ws = torch.empty(dad.psi_spec_step_workspace(cfg), dtype=torch.uint8, device=dev)
     outs = {"drafts": torch.empty((B, k), dtype=torch.int32, device=dev),
             "accept_len": torch.empty(B, dtype=torch.int32, device=dev),
             "token": torch.empty(B, dtype=torch.int32, device=dev)}
     torch.cuda.synchronize()
     log(f"full step: inputs resident ({time.time() - t0:.1f}s, "
-        f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated)")
+        f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated, capacity {cap} rows per sequence)")
+    state = {"t": 0}
 
     def step():
-        cache_len.copy_(cache_len0)
+        t = state["t"]
+        prev = None if t == 0 else dad.noisy_rows(bufs[(t - 1) % 2], cfg)
         dad.psi_spec_step(cfg, arr, embed, final_norm, lm_head, tokens, u_draft, u_accept, u_sample,
-                          logits=logits, outputs=outs, workspace=ws, cache_len=cache_len)
+                          prev_q=prev, logits=bufs[t % 2], outputs=outs, workspace=ws, cache_len=cache_len,
+                          next_tokens=tokens)
+        state["t"] = t + 1
 
     for _ in range(args.warmup):
         step()
@@ -225,7 +236,7 @@ def bench_full_step(args, dad, torch):
     names = ["uno_step_setup", "uno_rms_norm", "uno_add_rms_norm", "uno_rope", "uno_silu_mul", "uno_lora_down_bf16",
              "uno_lora_gate", "uno_gemm_bf16", "uno_gemm_reduce", "uno_block_attention", "uno_sample_stats",
              "uno_sample_desc", "uno_sample_seg", "uno_sample_resolve", "uno_row_stats", "uno_accept",
-             "uno_draw_seg", "uno_draw_resolve", "uno_kv_commit"]
+             "uno_draw_seg", "uno_draw_resolve", "uno_step_finish"]
     breakdown = {}
     for kn in names:
         ms, cnt = dad.profile_query(kn)
@@ -237,6 +248,7 @@ def bench_full_step(args, dad, torch):
     log(f"full step: breakdown {json.dumps({k: round(v, 3) for k, v in breakdown.items()})}")
 
     # timed region; events around the dominant kernel's launches only
+    len_start = cache_len.cpu().numpy().astype(np.int64)
     dad.profile_enable(True, dominant)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
@@ -249,9 +261,15 @@ def bench_full_step(args, dad, torch):
     dad.profile_reset()
     ms_per_step = (t_end - t_start) * 1e3 / args.steps
 
+    # every step keeps L + 1 rows per sequence and emits L + 1 tokens (L
+    # accepted drafts and y), so the growth of the cache lengths over the
+    # timed steps counts the verified tokens
+    len_end = cache_len.cpu().numpy().astype(np.int64)
     L = outs["accept_len"].cpu().numpy()
-    tokens_per_step = int(np.sum(L + 1))
-    value = tokens_per_step / (ms_per_step * 1e-3)
+    assert np.all(L >= 0), "a sequence ran out of KV capacity"
+    tokens_timed = int(np.sum(len_end - len_start))
+    tokens_per_step = tokens_timed / args.steps
+    value = tokens_timed / (args.steps * ms_per_step * 1e-3)
 
     m_on = B * blk
     gemm_flops, down_flops = full_step_flops(m_on)
@@ -279,7 +297,7 @@ def bench_full_step(args, dad, torch):
     sampler_ms = sum(breakdown[n] for n in ("uno_sample_stats", "uno_sample_desc", "uno_sample_seg",
                                             "uno_sample_resolve", "uno_row_stats", "uno_accept", "uno_draw_seg",
                                             "uno_draw_resolve"))
-    sampler_bytes = float(B) * (3 * k + 1) * V * 2          # draft rows once, verify rows once
+    sampler_bytes = float(B) * (3 * k + 1) * V * 2          # draft rows, verify's p rows and carried q rows
     gemm_s, attn_s = gemm_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12), kv_bytes_step / (HBM_PEAK_GBS * 1e9)
     lower_bound_ms = (gemm_s + attn_s) * 1e3
     components = {
@@ -295,13 +313,13 @@ def bench_full_step(args, dad, torch):
         "norm_rope_silu_ms": sum(breakdown[n] for n in ("uno_rms_norm", "uno_add_rms_norm", "uno_rope",
                                                         "uno_silu_mul", "uno_step_setup")),
         "sampler": {"ms": sampler_ms, "gb": sampler_bytes / 1e9, "gbs": sampler_bytes / (sampler_ms * 1e-3) / 1e9},
-        "mean_accept_len": float(np.mean(L)),
+        "mean_accept_len": tokens_per_step / B - 1.0,
         "kernel_ms_per_step": breakdown,
     }
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_step(args, tokens_per_step)
-    del keep, layers, arr, embed, lm_head, logits, ws
+    del keep, layers, arr, embed, lm_head, bufs, ws
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return {
@@ -322,8 +340,12 @@ def bench_full_step(args, dad, torch):
                    "model": "36-layer Qwen3-8B-shaped stack, hidden 4096, MLP 12288, GQA 32/8, head_dim 128, "
                             "rank-128 gated LoRA on q/k/v/o/gate/up/down, vocab 151936",
                    "batch": B, "block": blk, "rows": rows, "ctx_len": ctx, "drafts_per_seq": k,
-                   "kv_cache": "decode loop: ctx_len valid rows per sequence; each layer appends the block's "
-                               "clean k/v and the step commits the kept rows (lengths reset before each step)",
+                   "kv_cache": "decode loop: ctx_len valid rows per sequence at the first step; each layer "
+                               "appends the block's clean k/v and the step commits the kept rows, so the cache "
+                               "grows by the emitted tokens",
+                   "decode_loop": "chained: each step takes the previous step's ids [y, drafts, noisy ids] and "
+                                  "verifies the drafts against the previous step's noisy-row logits",
+                   "ctx_len_timed_mean": float((len_start.mean() + len_end.mean()) / 2),
                    "tokens_per_step": tokens_per_step, "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -101,7 +101,8 @@ def _declare(lib):
                                              _p, _p, _sz]),
         "uno_psi_spec_step_workspace": (ctypes.c_int, [ctypes.POINTER(StepConfig), ctypes.POINTER(_sz)]),
         "uno_psi_spec_step": (ctypes.c_int, [_p, ctypes.POINTER(StepConfig), ctypes.POINTER(LayerWeights),
-                                             _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz]),
+                                             _p, _p, _p, _p, _p, _p, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p,
+                                             _p, _sz]),
         "uno_kv_commit": (ctypes.c_int, [_p, _i32, _i32, _p, _p]),
         "uno_profile_enable": (None, [ctypes.c_int, ctypes.c_char_p]),
         "uno_profile_reset": (None, []),
@@ -461,18 +462,27 @@ def psi_spec_step_workspace(cfg):
 
 
 def psi_spec_step(cfg, layers, embed, final_norm, lm_head, tokens, u_draft, u_accept, u_sample,
-                  logits=None, outputs=None, workspace=None, stream=None, cache_len=None):
-    """One decode step (uno_psi_spec_step).
+                  prev_q=None, logits=None, outputs=None, workspace=None, stream=None, cache_len=None,
+                  next_tokens=None):
+    """One decode step of the decode loop (uno_psi_spec_step).
 
     cfg: StepConfig; layers: sequence (or ctypes array) of LayerWeights, one per layer;
     embed, lm_head bf16 [vocab, hidden]; final_norm bf16 [hidden];
-    tokens int32 [batch, 2*block]; u_draft, u_accept f32 [batch, block-1];
-    u_sample f32 [batch].  Returns a dict of device tensors: logits
-    [batch*2*block, vocab] bf16, drafts [batch, block-1], accept_len and token
-    [batch] (`outputs`, if given, is such a dict to write into).
+    tokens int32 [batch, 2*block] (clean ids [y, drafts], then noisy ids);
+    u_draft, u_accept f32 [batch, block-1]; u_sample f32 [batch].
+    prev_q: bf16 [batch, block-1, vocab] view (any strides, last dim
+    contiguous) of the previous step's noisy-row logits the clean drafts were
+    drawn from (e.g. noisy_rows(previous logits, cfg)); None on the loop's
+    first step (no draft verified).
+    Returns a dict of device tensors: logits [batch*2*block, vocab] bf16,
+    drafts [batch, block-1], accept_len and token [batch] (`outputs`, if
+    given, is such a dict to write into), and next_tokens when asked for
+    (next_tokens: an int32 [batch, 2*block] tensor, or True for a new one;
+    it may be `tokens` itself).
     cache_len int32 [batch] (optional, updated in place): valid cache rows per
     sequence out of cfg.ctx_len; the step appends the clean rows' k and v and
-    commits the kept ones (the decode loop's form).
+    commits the kept ones (a sequence whose kept rows do not fit gets
+    accept_len = token = -1).
     """
     import torch
     load()
@@ -485,18 +495,33 @@ def psi_spec_step(cfg, layers, embed, final_norm, lm_head, tokens, u_draft, u_ac
         outputs = {"drafts": torch.empty((cfg.batch, max(k, 0)), dtype=torch.int32, device=dev),
                    "accept_len": torch.empty(cfg.batch, dtype=torch.int32, device=dev),
                    "token": torch.empty(cfg.batch, dtype=torch.int32, device=dev)}
+    if next_tokens is True:
+        next_tokens = torch.empty_like(tokens)
     drafts, acc, tok = outputs["drafts"], outputs["accept_len"], outputs["token"]
     arr = layers if isinstance(layers, ctypes.Array) else (LayerWeights * max(len(layers), 1))(*layers)
     ws = _workspace(psi_spec_step_workspace(cfg), dev, workspace)
+    qs = prev_q.stride() if prev_q is not None else (0, 0, 1)
     _check(_lib.uno_psi_spec_step(_stream(stream), ctypes.byref(cfg), arr, _ptr(embed), _ptr(final_norm),
-                                  _ptr(lm_head), _ptr(tokens), _ptr(cache_len), _ptr(u_draft), _ptr(u_accept), _ptr(u_sample),
-                                  _ptr(logits), _ptr(drafts) if k > 0 else None, _ptr(acc), _ptr(tok),
+                                  _ptr(lm_head), _ptr(tokens), _ptr(cache_len), _ptr(prev_q), qs[0], qs[1],
+                                  _ptr(u_draft), _ptr(u_accept), _ptr(u_sample), _ptr(logits),
+                                  _ptr(drafts) if k > 0 else None, _ptr(acc), _ptr(tok), _ptr(next_tokens),
                                   _ptr(ws), _nbytes(ws)))
-    return {"logits": logits, "drafts": drafts, "accept_len": acc, "token": tok}
+    out = {"logits": logits, "drafts": drafts, "accept_len": acc, "token": tok}
+    if next_tokens is not None:
+        out["next_tokens"] = next_tokens
+    return out
+
+
+def noisy_rows(logits, cfg):
+    """The [batch, block-1, vocab] view of a step's logits holding its noisy
+    rows 0..k-1: the q the next step verifies its drafts against."""
+    lg = logits.view(cfg.batch, 2 * cfg.block, cfg.vocab)
+    return lg[:, cfg.block:2 * cfg.block - 1]
 
 
 def kv_commit(accept_len, cache_len, capacity, stream=None):
-    """cache_len[b] = min(capacity, cache_len[b] + accept_len[b] + 1) in place (uno_kv_commit)."""
+    """cache_len[b] += accept_len[b] + 1 in place when the kept rows fit the
+    capacity, else accept_len[b] = -1 (uno_kv_commit)."""
     load()
     _check(_lib.uno_kv_commit(_stream(stream), int(cache_len.shape[0]), int(capacity), _ptr(accept_len),
                               _ptr(cache_len)))

@@ -176,6 +176,7 @@ uno_status uno_psi_spec_verify_linear(hipStream_t stream, uno_dtype logit_dtype,
   a.q_seq = q_seq_stride;
   a.q_row = q_row_stride;
   a.drafts = draft_tokens;
+  a.drafts_seq = k;
   a.u_acc = u_accept;
   a.u_s = u_sample;
   a.scale_log2 = float(1.4426950408889634 / double(temperature));

@@ -533,7 +533,7 @@ uno_status uno_decoder_layer(hipStream_t stream, int32_t batch, int32_t block, i
 }
 
 // ------------------------------------------------------------------ KV commit
-uno_status uno_kv_commit(hipStream_t stream, int32_t batch, int32_t capacity, const int32_t* accept_len,
+uno_status uno_kv_commit(hipStream_t stream, int32_t batch, int32_t capacity, int32_t* accept_len,
                          int32_t* cache_len) {
   UNO_GUARD_BEGIN
   if (batch < 1 || capacity < 0) return fail(UNO_ERR_INVALID_ARGUMENT, "batch >= 1 and capacity >= 0 required");

@@ -84,9 +84,10 @@ uno_status uno_psi_spec_step_workspace(const uno_step_config* config, size_t* by
 
 uno_status uno_psi_spec_step(hipStream_t stream, const uno_step_config* config, const uno_layer_weights* layers,
                              const void* embed, const void* final_norm, const void* lm_head, const int32_t* tokens,
-                             int32_t* cache_len, const float* u_draft, const float* u_accept, const float* u_sample, void* logits,
-                             int32_t* out_drafts, int32_t* out_accept_len, int32_t* out_token, void* workspace,
-                             size_t workspace_bytes) {
+                             int32_t* cache_len, const void* prev_q, int64_t prev_q_seq_stride,
+                             int64_t prev_q_row_stride, const float* u_draft, const float* u_accept,
+                             const float* u_sample, void* logits, int32_t* out_drafts, int32_t* out_accept_len,
+                             int32_t* out_token, int32_t* out_next_tokens, void* workspace, size_t workspace_bytes) {
   UNO_GUARD_BEGIN
   uno_status s = check_config(config);
   if (s != UNO_OK) return s;
@@ -95,8 +96,16 @@ uno_status uno_psi_spec_step(hipStream_t stream, const uno_step_config* config, 
   if (!embed || !final_norm || !lm_head || !tokens || !u_sample || !logits || !out_accept_len || !out_token ||
       (c.n_layers > 0 && !layers))
     return fail(UNO_ERR_INVALID_ARGUMENT, "required pointer is NULL");
-  if (k > 0 && (!u_draft || !u_accept || !out_drafts))
-    return fail(UNO_ERR_INVALID_ARGUMENT, "u_draft, u_accept and out_drafts are required when block > 1");
+  if (k > 0 && (!u_draft || !out_drafts))
+    return fail(UNO_ERR_INVALID_ARGUMENT, "u_draft and out_drafts are required when block > 1");
+  // the drafts verified this step are the clean ids 1..k, drawn by the previous step from prev_q
+  const int kv = (prev_q && k > 0) ? k : 0;
+  if (kv > 0) {
+    if (!u_accept) return fail(UNO_ERR_INVALID_ARGUMENT, "u_accept is required with prev_q");
+    if (prev_q_row_stride < c.vocab || prev_q_seq_stride < int64_t(k) * prev_q_row_stride)
+      return fail(UNO_ERR_INVALID_ARGUMENT, "prev_q strides must cover [k][vocab]");
+    if (reinterpret_cast<uintptr_t>(prev_q) & 1u) return fail(UNO_ERR_UNSUPPORTED, "prev_q must be 2-byte aligned");
+  }
   if (!aligned16(embed) || !aligned16(final_norm) || !aligned16(lm_head) || (reinterpret_cast<uintptr_t>(logits) & 7u))
     return fail(UNO_ERR_UNSUPPORTED, "embed, final_norm, lm_head 16-byte and logits 8-byte aligned required");
   for (int l = 0; l < c.n_layers; ++l) {
@@ -131,6 +140,7 @@ uno_status uno_psi_spec_step(hipStream_t stream, const uno_step_config* config, 
   sa.block = c.block;
   sa.ctx = c.ctx_len;
   sa.cache_len = cache_len;
+  sa.cap = c.ctx_len;
   sa.hidden = c.hidden;
   sa.vocab = c.vocab;
   sa.tokens = tokens;
@@ -221,20 +231,23 @@ uno_status uno_psi_spec_step(hipStream_t stream, const uno_step_config* config, 
     e = launch_sample_rows(ra, stream);
   }
 
-  // verify: p from the k + 1 clean rows, q from the first k noisy rows
+  // verify the clean drafts: p from the kv + 1 clean rows, q from the previous
+  // step's noisy rows (prev_q); without prev_q no draft is verified (L = 0, y
+  // drawn from clean row 0)
   if (e == hipSuccess) {
     VerifyLinearArgs va{};
     va.dtype = UNO_BF16;
     va.batch = c.batch;
-    va.k = k;
+    va.k = kv;
     va.vocab = c.vocab;
     va.p = lg;
     va.p_seq = seq_stride;
     va.p_row = c.vocab;
-    va.q = lg + int64_t(c.block) * c.vocab;
-    va.q_seq = seq_stride;
-    va.q_row = c.vocab;
-    va.drafts = out_drafts;
+    va.q = prev_q;
+    va.q_seq = prev_q_seq_stride;
+    va.q_row = prev_q_row_stride;
+    va.drafts = tokens + 1;
+    va.drafts_seq = 2 * int64_t(c.block);
     va.u_acc = u_accept;
     va.u_s = u_sample;
     va.scale_log2 = scale_log2;
@@ -243,9 +256,22 @@ uno_status uno_psi_spec_step(hipStream_t stream, const uno_step_config* config, 
     va.ws = scratch;
     e = launch_verify_linear(va, stream);
   }
-  // commit: the block's AR token and its accepted drafts, appended by every
-  // layer during the forward pass, join each sequence's valid cache prefix
-  if (e == hipSuccess && cache_len) e = launch_kv_commit(c.batch, c.ctx_len, out_accept_len, cache_len, stream);
+  // commit (the block's AR token and its accepted drafts, appended by every
+  // layer during the forward pass, join each sequence's valid cache prefix;
+  // a sequence whose kept rows do not fit is flagged) and the next step's ids
+  if (e == hipSuccess && (cache_len || out_next_tokens)) {
+    StepFinishArgs fa{};
+    fa.batch = c.batch;
+    fa.block = c.block;
+    fa.cap = c.ctx_len;
+    fa.accept_len = out_accept_len;
+    fa.token = out_token;
+    fa.cache_len = cache_len;
+    fa.drafts = out_drafts;
+    fa.tokens = tokens;
+    fa.next = out_next_tokens;
+    e = launch_step_finish(fa, stream);
+  }
   return check_hip(e, "uno_psi_spec_step launch");
   UNO_GUARD_END
 }

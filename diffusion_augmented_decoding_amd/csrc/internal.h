@@ -46,7 +46,7 @@ struct VerifyLinearArgs {
   int batch, k, vocab;
   const void* p; int64_t p_seq, p_row;
   const void* q; int64_t q_seq, q_row;
-  const int32_t* drafts;
+  const int32_t* drafts; int64_t drafts_seq;   // draft i of sequence b at drafts[b * drafts_seq + i]
   const float* u_acc;
   const float* u_s;
   float scale_log2;   // log2(e) / T
@@ -250,12 +250,14 @@ hipError_t launch_decoder_layer(const DecoderLayerArgs& a, hipStream_t stream);
 // ---------------------------------------------------------------- step set-up
 // Row j of sequence b (rows of a sequence: block clean, then block noisy):
 // h[row] = embed[tokens[row]] (a zero row for an id outside [0, vocab)),
-// gate[row] = (j >= block), positions[row] = ctx + j % block, with ctx
-// replaced by cache_len[b] when cache_len is given.
+// gate[row] = (j >= block), positions[row] = ctx + j (clean row j at ctx + j,
+// noisy row j at ctx + block + j), with ctx replaced by cache_len[b] clamped
+// to [0, cap] when cache_len is given.
 struct StepSetupArgs {
   int64_t rows;
   int block, ctx, hidden, vocab;
   const int32_t* cache_len;          // [batch] or nullptr
+  int cap;                           // rows of capacity per sequence (with cache_len)
   const int32_t* tokens;
   const void* embed;                 // bf16 [vocab][hidden]
   void* h;                           // bf16 [rows][hidden]
@@ -264,9 +266,26 @@ struct StepSetupArgs {
 };
 hipError_t launch_step_setup(const StepSetupArgs& a, hipStream_t stream);
 
-// KV commit after verification: cache_len[b] = min(cap, cache_len[b] +
-// accept_len[b] + 1) for b < batch (the rows themselves were appended during
-// the forward pass; the rejected and noisy rows are dropped by not counting them).
-hipError_t launch_kv_commit(int batch, int cap, const int32_t* accept_len, int32_t* cache_len, hipStream_t stream);
+// KV commit after verification, for b < batch: with len = cache_len[b]
+// (clamped to [0, cap]) and L = accept_len[b], cache_len[b] = len + L + 1 when
+// L >= 0 and len + L + 1 <= cap (the rows themselves were appended during the
+// forward pass; the rejected and noisy rows are dropped by not counting
+// them); otherwise the length is left as it is and accept_len[b] = -1.
+hipError_t launch_kv_commit(int batch, int cap, int32_t* accept_len, int32_t* cache_len, hipStream_t stream);
+
+// The end of a decode step, one sequence per 2*block threads: the commit
+// above (when cache_len is given; a flagged sequence also gets token -1),
+// then the next step's ids [y, d_0 .. d_{k-1}, noisy ids] (next may alias
+// tokens: each id is read and written by the same thread).
+struct StepFinishArgs {
+  int batch, block, cap;
+  int32_t* accept_len;               // [batch], set to -1 on overflow
+  int32_t* token;                    // [batch], set to -1 on overflow
+  int32_t* cache_len;                // [batch] or nullptr
+  const int32_t* drafts;             // [batch][block - 1]
+  const int32_t* tokens;             // [batch][2 * block]
+  int32_t* next;                     // [batch][2 * block] or nullptr
+};
+hipError_t launch_step_finish(const StepFinishArgs& a, hipStream_t stream);
 
 }  // namespace uno

@@ -270,7 +270,10 @@ namespace uno {
 namespace {
 
 // One workgroup per row: the embedding row copied in 16-byte vectors, the
-// row's gate and position written by thread 0.
+// row's gate and position written by thread 0.  Clean row j sits at
+// ctx + j and noisy row j at ctx + block + j (the noisy rows stand for the
+// next block); ctx is the sequence's valid cache rows, clamped to the
+// capacity as the attention kernel clamps it.
 __global__ __launch_bounds__(256) void step_setup_kernel(StepSetupArgs a) {
   const int64_t row = blockIdx.x;
   const int j = int(row % (2 * a.block));
@@ -281,27 +284,74 @@ __global__ __launch_bounds__(256) void step_setup_kernel(StepSetupArgs a) {
   u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.h) + row * a.hidden);
   for (int i = threadIdx.x; i < nvec; i += 256) dst[i] = ok ? src[i] : u32x4{0u, 0u, 0u, 0u};
   if (threadIdx.x == 0) {
+    int ctx = a.ctx;
+    if (a.cache_len) ctx = min(max(a.cache_len[row / (2 * a.block)], 0), a.cap);
     a.gate[row] = j >= a.block ? 1 : 0;
-    a.positions[row] = (a.cache_len ? a.cache_len[row / (2 * a.block)] : a.ctx) + j % a.block;
+    a.positions[row] = ctx + j;
   }
+}
+
+// The commit of one sequence (cache_len may be null: no cache to commit to).
+// Returns false when the sequence is flagged.
+__device__ __forceinline__ bool commit_one(int b, int cap, int32_t* accept_len, int32_t* cache_len) {
+  const int L = accept_len[b];
+  if (!cache_len) return L >= 0;
+  const int len = min(max(cache_len[b], 0), cap);
+  if (L < 0 || int64_t(len) + L + 1 > cap) {
+    accept_len[b] = -1;
+    return false;
+  }
+  cache_len[b] = len + L + 1;
+  return true;
 }
 
 }  // namespace
 
 // One thread per sequence: the kept rows (the block's AR token and the L
-// accepted drafts, already written by the forward pass) join the valid prefix.
-__global__ __launch_bounds__(256) void kv_commit_kernel(int batch, int cap, const int32_t* accept_len,
-                                                        int32_t* cache_len) {
+// accepted drafts, already written by the forward pass) join the valid
+// prefix when they all fit; otherwise the sequence is flagged.
+__global__ __launch_bounds__(256) void kv_commit_kernel(int batch, int cap, int32_t* accept_len, int32_t* cache_len) {
   const int b = blockIdx.x * 256 + threadIdx.x;
   if (b >= batch) return;
-  const int64_t len = int64_t(cache_len[b]) + accept_len[b] + 1;
-  cache_len[b] = int32_t(len < cap ? len : cap);
+  commit_one(b, cap, accept_len, cache_len);
 }
 
-hipError_t launch_kv_commit(int batch, int cap, const int32_t* accept_len, int32_t* cache_len, hipStream_t stream) {
+// One workgroup of 2*block threads per sequence: thread 0 commits (and on a
+// flag writes token -1 too); thread j then writes id j of the next step:
+// the token y (j = 0), draft j - 1 (j < block), or the noisy id (read and
+// written by the same thread, so next may alias tokens).
+__global__ __launch_bounds__(256) void step_finish_kernel(StepFinishArgs a) {
+  const int b = blockIdx.x, j = threadIdx.x;
+  __shared__ int32_t y;
+  if (j == 0) {
+    const bool ok = commit_one(b, a.cap, a.accept_len, a.cache_len);
+    if (!ok) a.token[b] = -1;
+    y = ok ? a.token[b] : -1;
+  }
+  __syncthreads();
+  if (!a.next || j >= 2 * a.block) return;
+  const int64_t at = int64_t(b) * 2 * a.block + j;
+  int32_t id;
+  if (j == 0)
+    id = y;
+  else if (j < a.block)
+    id = a.drafts[int64_t(b) * (a.block - 1) + (j - 1)];
+  else
+    id = a.tokens[at];
+  a.next[at] = id;
+}
+
+hipError_t launch_kv_commit(int batch, int cap, int32_t* accept_len, int32_t* cache_len, hipStream_t stream) {
   ProfileScope ps("uno_kv_commit", stream);
   hipLaunchKernelGGL(kv_commit_kernel, dim3(unsigned((batch + 255) / 256)), dim3(256), 0, stream, batch, cap,
                      accept_len, cache_len);
+  return hipGetLastError();
+}
+
+hipError_t launch_step_finish(const StepFinishArgs& a, hipStream_t stream) {
+  ProfileScope ps("uno_step_finish", stream);
+  const unsigned threads = unsigned((2 * a.block + 63) / 64 * 64);
+  hipLaunchKernelGGL(step_finish_kernel, dim3(unsigned(a.batch)), dim3(threads), 0, stream, a);
   return hipGetLastError();
 }
 

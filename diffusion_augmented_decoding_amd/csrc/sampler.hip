@@ -51,11 +51,11 @@ LinWs lin_ws(void* base, int batch, int k, int vocab) {
 template <typename T>
 __device__ __forceinline__ const T* lin_row(const VerifyLinearArgs& a, int b, int j, int* draft) {
   if (j <= a.k) {
-    *draft = (j < a.k) ? a.drafts[int64_t(b) * a.k + j] : -1;
+    *draft = (j < a.k) ? a.drafts[int64_t(b) * a.drafts_seq + j] : -1;
     return static_cast<const T*>(a.p) + int64_t(b) * a.p_seq + int64_t(j) * a.p_row;
   }
   const int i = j - a.k - 1;
-  *draft = a.drafts[int64_t(b) * a.k + i];
+  *draft = a.drafts[int64_t(b) * a.drafts_seq + i];
   return static_cast<const T*>(a.q) + int64_t(b) * a.q_seq + int64_t(i) * a.q_row;
 }
 

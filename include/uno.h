@@ -49,7 +49,7 @@ typedef enum {
 
 typedef enum { UNO_F32 = 0, UNO_BF16 = 1 } uno_dtype;
 
-#define UNO_ABI_VERSION 2
+#define UNO_ABI_VERSION 3
 
 int uno_abi_version(void);
 const char* uno_status_string(uno_status s);
@@ -332,55 +332,71 @@ uno_status uno_decoder_layer(hipStream_t stream, int32_t batch, int32_t block, i
  * their keys and values are the AR model's; uno_decoder_layer with a
  * cache_len has already written them after each sequence's valid rows.
  * This call keeps clean rows 0..L (the block's AR token and the accepted
- * drafts) and drops the rest by not counting them:
- *   cache_len[b] = min(capacity, cache_len[b] + accept_len[b] + 1), b < batch.
- * accept_len, cache_len: device int32 [batch]; cache_len updated in place.
+ * drafts) and drops the rest by not counting them.  For b < batch, with
+ * len = cache_len[b] clamped to [0, capacity] and L = accept_len[b]:
+ *   L >= 0 and len + L + 1 <= capacity:  cache_len[b] = len + L + 1;
+ *   otherwise (the kept rows do not all fit, or L is already -1): cache_len[b]
+ *   is left as it is and accept_len[b] = -1 (the sequence is flagged: its
+ *   emitted tokens would no longer match its cache).
+ * accept_len, cache_len: device int32 [batch], both updated in place.
  * The correction token is not in the cache: it is the next block's first
  * clean row.  batch >= 1, capacity >= 0. */
-uno_status uno_kv_commit(hipStream_t stream, int32_t batch, int32_t capacity, const int32_t* accept_len,
+uno_status uno_kv_commit(hipStream_t stream, int32_t batch, int32_t capacity, int32_t* accept_len,
                          int32_t* cache_len);
 
-/* One whole Psi-Spec decode step.  Source: Uno summary (hyper.ai), section
- * 方法 (the diffusion path proposes a block, the AR path verifies it by
- * rejection sampling and keeps the longest valid prefix; the linear sampler
- * draws one candidate from the marginals; one forward pass runs over the
- * concatenated clean and noisy rows with the adapter gated per row) and
- * section 实验 (Qwen3-8B base, rank-128 adapters, shared KV cache).
+/* One whole Psi-Spec decode step of the decode loop.  Source: Uno summary
+ * (hyper.ai), section 方法 (both weight sets draft, only the AR weights
+ * verify; the diffusion path keeps the next-token parametrisation and
+ * predicts the next clean token from a noisy sequence; a block proposed on
+ * the diffusion path is rejection-sampled against the AR distribution and
+ * the longest valid prefix is kept; the first token of a block comes from
+ * the AR weights; the linear sampler draws one candidate from the marginals;
+ * one forward pass runs over the concatenated clean and noisy rows with the
+ * adapter gated per row) and section 实验 (Qwen3-8B base, rank-128 adapters,
+ * one KV cache shared by drafting and verification).
  *
- * Per sequence b the step takes 2*block token ids: `block` clean ids (the
- * AR token, then k = block - 1 drafts) and `block` noisy ids.  It runs
+ * Per sequence b the step takes 2*block token ids: `block` clean ids -- the
+ * previous step's AR token y, then the k = block - 1 drafts d that step drew
+ * -- and `block` noisy ids (the caller's noise/mask ids for the next block).
+ * It runs
  *   h = embed[tokens]; gate = 0 on clean rows, 1 on noisy rows;
- *   positions: clean row j and noisy row j at ctx_len + j;
- *   n_layers x uno_decoder_layer (layer l uses layers[l], its KV cache holds
- *     ctx_len positions per sequence; the block is not written to it);
- *   logits = rmsnorm(h, final_norm) . lm_head^T     (bf16 [rows][vocab], no adapter);
- *   drafts[b][i] = inverse-CDF draw from softmax(noisy row i / T) at u_draft[b][i], i < k
- *     (the uno_sample_rows rule);
- *   uno_psi_spec_verify_linear with p = the k + 1 clean rows and q = the first k
- *     noisy rows of the same logits, on the drafts just drawn.
- * Reading: the pages leave open which forward's q a draft is verified against;
- * here the drafts a step verifies are drawn from that step's own noisy rows,
- * which is the same work per step as carrying them over from the previous
- * step (one draw of k rows, one verify of 2k + 1 rows per sequence).
+ *   positions: clean row j at ctx + j, noisy row j at ctx + block + j (the
+ *     noisy rows stand for the next block; ctx = cache_len[b] or ctx_len);
+ *   n_layers x uno_decoder_layer (layer l uses layers[l]);
+ *   logits = rmsnorm(h, final_norm) . lm_head^T  (bf16 [rows][vocab], no adapter);
+ *   out_drafts[b][i] = inverse-CDF draw from softmax(noisy row i / T) at
+ *     u_draft[b][i], i < k (the uno_sample_rows rule): the next step's drafts;
+ *   uno_psi_spec_verify_linear of the clean drafts d against p = the k + 1
+ *     clean rows and q = prev_q, the previous step's noisy-row logits the
+ *     drafts were drawn from (the caller keeps that step's logits buffer and
+ *     passes its noisy rows 0..k-1 with strides; nothing is copied).  With
+ *     prev_q NULL (the loop's first step) no draft is verified: L = 0 and y
+ *     is drawn from clean row 0.
+ *   out_next_tokens[b] (optional) = [y, out_drafts[b][0..k-1], the noisy ids
+ *     of tokens[b]]: the next step's ids, assembled on the device; may be
+ *     `tokens` itself.
  *
  * layers: host array of n_layers uno_layer_weights (device pointers); embed and
  * lm_head bf16 [vocab][hidden]; final_norm bf16 [hidden]; tokens int32
- * [batch][2*block]; u_draft, u_accept f32 [batch][k]; u_sample f32 [batch];
- * logits (output, caller-owned) bf16 [batch*2*block][vocab]; out_drafts int32
- * [batch][k]; out_accept_len, out_token int32 [batch].  1 <= block <= 65,
- * head_dim 128, hidden and inter multiples of 8, r a multiple of 8 (0: no
- * adapter).  A token id outside [0, vocab) embeds as a zero row.
+ * [batch][2*block]; prev_q bf16, row i of sequence b at prev_q +
+ * b * prev_q_seq_stride + i * prev_q_row_stride (elements; row stride >=
+ * vocab, sequence stride >= k row strides), must not alias logits; u_draft,
+ * u_accept f32 [batch][k]; u_sample f32 [batch]; logits (output,
+ * caller-owned) bf16 [batch*2*block][vocab]; out_drafts int32 [batch][k];
+ * out_accept_len, out_token int32 [batch].  1 <= block <= 65, head_dim 128,
+ * hidden and inter multiples of 8, r a multiple of 8 (0: no adapter).  A
+ * token id outside [0, vocab) embeds as a zero row.
  *
  * cache_len (optional, device int32 [batch], updated in place): the decode
- * loop's form.  Sequence b's caches hold cache_len[b] valid rows out of a
- * capacity of ctx_len per sequence; clean row j and noisy row j sit at
- * position cache_len[b] + j; every layer writes the clean rows' k and v into
- * its cache after the valid rows (uno_decoder_layer), and after verification
- * the step commits the kept rows (uno_kv_commit), so the next step's
- * cache_len[b] is the old one + out_accept_len[b] + 1.  A slot at or past
- * ctx_len is not written and the length stops at ctx_len.  NULL: every
- * cache holds ctx_len rows, the caches are only read and positions are
- * ctx_len + j. */
+ * loop's form.  Sequence b's caches hold cache_len[b] valid rows (clamped to
+ * [0, ctx_len]) out of a capacity of ctx_len per sequence; every layer writes
+ * the clean rows' k and v into its cache after the valid rows
+ * (uno_decoder_layer), and after verification the step commits the kept
+ * rows as uno_kv_commit does, so the next step's cache_len[b] is the old one
+ * + out_accept_len[b] + 1.  A sequence whose kept rows do not fit is
+ * flagged: out_accept_len[b] = out_token[b] = -1, its length unchanged.
+ * NULL: every cache holds ctx_len rows, the caches are only read and
+ * positions start at ctx_len. */
 typedef struct {
   int32_t batch, block, ctx_len;
   int32_t hidden, inter, n_heads, n_kv_heads, r, n_layers, vocab;
@@ -390,10 +406,11 @@ typedef struct {
 uno_status uno_psi_spec_step_workspace(const uno_step_config* config, size_t* bytes);
 uno_status uno_psi_spec_step(hipStream_t stream, const uno_step_config* config, const uno_layer_weights* layers,
                              const void* embed, const void* final_norm, const void* lm_head,
-                             const int32_t* tokens, int32_t* cache_len, const float* u_draft, const float* u_accept,
-                             const float* u_sample, void* logits, int32_t* out_drafts,
-                             int32_t* out_accept_len, int32_t* out_token,
-                             void* workspace, size_t workspace_bytes);
+                             const int32_t* tokens, int32_t* cache_len,
+                             const void* prev_q, int64_t prev_q_seq_stride, int64_t prev_q_row_stride,
+                             const float* u_draft, const float* u_accept, const float* u_sample,
+                             void* logits, int32_t* out_drafts, int32_t* out_accept_len, int32_t* out_token,
+                             int32_t* out_next_tokens, void* workspace, size_t workspace_bytes);
 
 /* --------------------------------------------------------------------------
  * Kernel timing (measurement support, not part of the method).

@@ -41,7 +41,7 @@ from .decoder import (
     decoder_layer,
     lm_head,
 )
-from .step import step_rows, decode_step
+from .step import step_rows, decode_step, decode_loop, emitted_tokens
 from .kv_commit import kv_commit
 
 __all__ = [
@@ -68,5 +68,7 @@ __all__ = [
     "lm_head",
     "step_rows",
     "decode_step",
+    "decode_loop",
+    "emitted_tokens",
     "kv_commit",
 ]

@@ -86,7 +86,8 @@ def verify_linear(p_logits, q_logits, drafts, u_accept, u_sample, temperature=1.
 
     p_logits [B, k+1, V]  AR rows; row i scores draft i, row k is the bonus row.
     q_logits [B, k, V]    draft marginals, row i for draft i.
-    drafts   [B, k]       int token ids in [0, V).
+    drafts   [B, k]       int token ids; an id outside [0, V) has probability 0
+                          under p and q and is rejected.
     u_accept [B, k], u_sample [B]: uniforms in [0, 1).
 
     Returns a dict of numpy arrays:
@@ -115,8 +116,9 @@ def verify_linear(p_logits, q_logits, drafts, u_accept, u_sample, temperature=1.
         length = k
         for i in range(k):
             d = int(drafts[b, i])
-            p_draft[b, i] = p[i, d]
-            q_draft[b, i] = q[i, d]
+            if 0 <= d < p.shape[1]:            # an id outside [0, V) has probability 0: rejected
+                p_draft[b, i] = p[i, d]
+                q_draft[b, i] = q[i, d]
         for i in range(k):
             if not accept_draft(u_accept[b, i], p_draft[b, i], q_draft[b, i]):
                 length = i

@@ -24,7 +24,17 @@ import workloads
 
 WEIGHT_STD = 0.05
 X_STD = 0.1
-BAR = 2e-2           # bf16 row-wise relative error bar of the GPU tests
+# Bar for the layer's output hidden state (row-wise max relative error).  The
+# single-operation bf16 bar is 2e-2 (each stage of the layer is held to it on
+# its own in tests/test_gpu_layer.py).  The hidden state chains ten bf16
+# storage points (the norm, q/k/v, the rotated q/k, the attention output, o and
+# its residual add, the MLP norm, gate/up, the SwiGLU product, down and its
+# residual add); at each, a value that fp32 and float64 accumulation place on
+# opposite sides of a bf16 rounding boundary rounds one ulp apart (2^-8 to
+# 2^-7 of the element) between two correct implementations, and later stages
+# carry the difference on.  Allowing ~4 such ulps at a row's largest element
+# gives 3e-2.
+BAR = 3e-2
 POWER = 3.0          # each planted mistake must move the output by POWER * BAR
 
 

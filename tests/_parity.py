@@ -124,3 +124,55 @@ def tree_outcome_near(parent, tokens, p, q, ua, us, temperature, gpu_out, tie=TI
         if same(r):
             return True
     return False
+
+
+def check_step_decisions(logits, block, tokens, prev_q, gpu, u_draft, u_accept, u_sample, temperature=1.0,
+                         seqs=None, tie=TIE):
+    """Every sampling decision of a decode step, checked against the oracle run
+    on the GPU's own logits (so both sides decide on the same bf16 values):
+    the drafts drawn from the noisy rows, the accepted length of the clean
+    drafts against prev_q, and the correction/bonus token -- bit-exact except
+    where a uniform lies within `tie` of its decision boundary (counted).
+
+    logits [B * 2*block, V] (host values); tokens [B, 2*block]; prev_q
+    [B, k, V] host values or None; gpu: dict of host arrays drafts [B, k],
+    accept_len [B], token [B] (flagged sequences, accept_len -1, are skipped).
+    Returns (draft near-ties: draft draws counted one by one, decision
+    near-ties: sequences whose accepted length or token differed at a
+    near-tie)."""
+    bsz = np.asarray(tokens).shape[0]
+    lg = np.asarray(logits).reshape(bsz, 2 * block, -1)     # converted to float64 a row at a time
+    k = block - 1
+    kv = k if prev_q is not None else 0
+    draft_ties = ties = 0
+    for b in (range(bsz) if seqs is None else seqs):
+        for i in range(k):
+            q = oracle.softmax_rows(lg[b, block + i], temperature)
+            ref = oracle.inverse_cdf(q, u_draft[b, i])
+            got = int(gpu["drafts"][b, i])
+            if got != ref:
+                assert draw_is_valid(q, float(u_draft[b, i]), got, tie), f"seq {b} draft {i}: gpu {got} oracle {ref}"
+                draft_ties += 1
+        if int(gpu["accept_len"][b]) < 0:
+            continue
+        pq = np.asarray(prev_q[b], dtype=np.float64)[None] if kv else np.zeros((1, 0, lg.shape[2]))
+        o = oracle.verify_linear(lg[b:b + 1, :kv + 1].astype(np.float64), pq, np.asarray(tokens)[b:b + 1, 1:kv + 1],
+                                 np.asarray(u_accept)[b:b + 1, :kv], np.asarray(u_sample)[b:b + 1], temperature)
+        Lo, Lg = int(o["accept_len"][0]), int(gpu["accept_len"][b])
+        if Lo != Lg:
+            i = min(Lo, Lg)
+            ratio = o["p_draft"][0, i] / o["q_draft"][0, i]
+            assert abs(float(u_accept[b, i]) - ratio) < tie, f"seq {b}: L gpu {Lg} oracle {Lo}"
+            ties += 1
+            continue
+        yo, yg = int(o["token"][0]), int(gpu["token"][b])
+        if yo != yg:
+            p = oracle.softmax_rows(lg[b, Lo], temperature)
+            if Lo < kv:
+                w, s = oracle.residual_weights(p, oracle.softmax_rows(pq[0, Lo], temperature))
+                w = p if s == 0.0 else w
+            else:
+                w = p
+            assert draw_is_valid(w, float(u_sample[b]), yg, tie), f"seq {b}: token gpu {yg} oracle {yo} (L={Lo})"
+            ties += 1
+    return draft_ties, ties

@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.uno_abi_version() == 2
+    assert lib.uno_abi_version() == 3
     for s in range(6):
         assert lib.uno_status_string(s)
     assert lib.uno_status_string(99) == b"unknown status"
@@ -312,12 +312,12 @@ def test_step_rejects_bad_calls(lib):
     layers = (lw_t * 2)()
 
     def call(c, lay=layers, ws_bytes=1 << 40, **kw):
-        a = dict(embed=FAKE16, fnorm=FAKE16, lm=FAKE16, tok=FAKE16, ud=FAKE16, ua=FAKE16, us=FAKE16, logits=FAKE16,
-                 drafts=FAKE16, L=FAKE16, y=FAKE16)
+        a = dict(embed=FAKE16, fnorm=FAKE16, lm=FAKE16, tok=FAKE16, pq=FAKE16, pq_seq=3 * 1000, pq_row=1000,
+                 ud=FAKE16, ua=FAKE16, us=FAKE16, logits=FAKE16, drafts=FAKE16, L=FAKE16, y=FAKE16, nxt=None)
         a.update(kw)
         return lib.uno_psi_spec_step(None, ctypes.byref(c), lay, a["embed"], a["fnorm"], a["lm"], a["tok"],
-                                     a.get("cl"), a["ud"], a["ua"], a["us"], a["logits"], a["drafts"], a["L"],
-                                     a["y"], FAKE16, ws_bytes)
+                                     a.get("cl"), a["pq"], a["pq_seq"], a["pq_row"], a["ud"], a["ua"], a["us"],
+                                     a["logits"], a["drafts"], a["L"], a["y"], a["nxt"], FAKE16, ws_bytes)
     small = cfg(batch=2, block=4, ctx_len=8, hidden=256, inter=512, n_heads=4, n_kv_heads=2, r=8, n_layers=2,
                 vocab=1000)
     assert call(small) == INVALID                          # layer weights are NULL
@@ -327,6 +327,11 @@ def test_step_rejects_bad_calls(lib):
             layers[l].w[i] = layers[l].a[i] = layers[l].b[i] = FAKE16.value
     assert call(small, embed=None) == INVALID
     assert call(small, ud=None) == INVALID
+    assert call(small, ua=None) == INVALID                 # a carried q needs the accept uniforms
+    assert call(small, pq_row=999) == INVALID              # row stride below the vocabulary
+    assert call(small, pq_seq=2 * 1000) == INVALID         # sequence stride below k rows
+    assert call(small, pq=ctypes.c_void_p(0x10001)) == UNSUPPORTED
+    assert call(small, pq=None, ua=None, ws_bytes=64) == WORKSPACE   # the first step needs no accept uniforms
     assert call(small, lm=ctypes.c_void_p(0x10008)) == UNSUPPORTED
     assert call(small, ws_bytes=64) == WORKSPACE
     layers[1].b[6] = None

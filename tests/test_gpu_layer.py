@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 import workloads
-from _layer_cases import FULL_CASES, LAYER_CASES, ids as layer_ids, make as make_layer_case, seq_rows as layer_seq_rows
+from _layer_cases import BAR as LAYER_BAR, FULL_CASES, LAYER_CASES, ids as layer_ids, make as make_layer_case, seq_rows as layer_seq_rows
 from _parity import TIE, draw_is_valid, row_relerr, say, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
@@ -260,7 +260,7 @@ def test_decoder_layer(gpu_lib, lc):
     rows, ref = _layer_ref(c, list(seqs))
     err = row_relerr(got[rows], ref)
     say(f"  row rel err {err:.3g}")
-    assert err <= 2e-2
+    assert err <= LAYER_BAR
 
 
 @pytest.mark.parametrize("lc", FULL_CASES[:1], ids=layer_ids(FULL_CASES[:1]))
@@ -276,4 +276,81 @@ def test_decoder_layer_full_size_sampled_sequences(gpu_lib, lc):
     rows, ref = _layer_ref(c, lc["seqs"])
     err = row_relerr(got[rows], ref)
     say(f"  row rel err {err:.3g}")
-    assert err <= 2e-2
+    assert err <= LAYER_BAR
+
+
+@pytest.mark.parametrize("name", ["small", "block16", "no_cache"])
+def test_decoder_layer_stages_within_single_op_bar(gpu_lib, name):
+    """Each stage of the layer, run through its own entry point on the GPU's
+    output of the stage before, against the oracle's stage on the same input:
+    every stage within the single-operation bf16 bar (2e-2), and the whole
+    layer (uno_decoder_layer, adapters stored apart so it takes the same
+    kernels) bit-identical to the chain of stages.  The layer's hidden state
+    is held to the composite bar (3e-2) because these per-stage differences,
+    one bf16 rounding each, add up along the chain."""
+    import torch
+    lc = [c for c in LAYER_CASES if c["name"] == name][0]
+    say(f"decoder layer stages {name}")
+    c = make_layer_case(lc)
+    nh, nkv, block, B = lc["nh"], lc["nkv"], lc["block"], lc["batch"]
+    n = 2 * block
+    w64 = _layer_oracle_weights(c["weights"])
+    Wd = {k: _bits_dev(v) for k, v in c["weights"].items() if not k.endswith("_f32")}
+    h = _f32(c["h"])
+    gate, pos = c["gate"], c["positions"]
+    rows = h.shape[0]
+    gt = to_dev(gate)
+    bf = oracle.round_bf16
+
+    def dev(x):
+        return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).cuda()
+
+    def back(t):
+        torch.cuda.synchronize()
+        return to_host(t).astype(np.float64)
+
+    def proj(x, p):
+        got = back(gpu_lib.gated_lora_linear(dev(x), Wd["w" + p], Wd["a" + p], Wd["b" + p], gt))
+        return got, bf(oracle.gated_lora_linear(x, w64["w" + p], w64["a" + p], w64["b" + p], gate))
+
+    err = {}
+    a = back(gpu_lib.rms_norm(dev(h), Wd["attn_norm"], 1e-6))
+    err["attn_norm"] = row_relerr(a, bf(oracle.rms_norm(h, w64["attn_norm"])))
+    qkv = {}
+    for p in "qkv":
+        qkv[p], ref = proj(a, p)
+        err[p] = row_relerr(qkv[p], ref)
+    qd, kd = dev(qkv["q"]), dev(qkv["k"])
+    gpu_lib.rope(qd, to_dev(pos), 1e6)
+    gpu_lib.rope(kd, to_dev(pos), 1e6)
+    qr, kr = back(qd), back(kd)
+    err["rope_q"] = row_relerr(qr, bf(oracle.rope(qkv["q"].reshape(rows, nh, 128), pos)).reshape(rows, -1))
+    err["rope_k"] = row_relerr(kr, bf(oracle.rope(qkv["k"].reshape(rows, nkv, 128), pos)).reshape(rows, -1))
+    att_d, _ = gpu_lib.block_verify_attention(dev(qr).view(B, n, nh, 128), _bits_dev(c["k_cache"]),
+                                              _bits_dev(c["v_cache"]), dev(kr).view(B, n, nkv, 128),
+                                              dev(qkv["v"]).view(B, n, nkv, 128), block, 1 / np.sqrt(128))
+    att = back(att_d).reshape(rows, -1)
+    ra, _ = oracle.block_attention(qr.reshape(B, n, nh, 128), _f32(c["k_cache"]), _f32(c["v_cache"]),
+                                   kr.reshape(B, n, nkv, 128), qkv["v"].reshape(B, n, nkv, 128), block,
+                                   1 / np.sqrt(128))
+    err["attention"] = row_relerr(att, bf(ra.reshape(rows, -1)))
+    o, ref = proj(att, "o")
+    err["o"] = row_relerr(o, ref)
+    h1 = bf(h + o)
+    a2 = back(gpu_lib.rms_norm(dev(h1), Wd["mlp_norm"], 1e-6))
+    err["mlp_norm"] = row_relerr(a2, bf(oracle.rms_norm(h1, w64["mlp_norm"])))
+    g, ref = proj(a2, "g")
+    err["gate"] = row_relerr(g, ref)
+    u, ref = proj(a2, "u")
+    err["up"] = row_relerr(u, ref)
+    m = back(gpu_lib.silu_mul(dev(g), dev(u)))
+    err["swiglu"] = row_relerr(m, bf(oracle.silu_mul(g, u)))
+    d, ref = proj(m, "d")
+    err["down"] = row_relerr(d, ref)
+    chain = bf(h1 + d)
+    say("  " + ", ".join(f"{k} {v:.3g}" for k, v in err.items()))
+    assert max(err.values()) <= 2e-2
+    whole = _run_layer(gpu_lib, c, gate=lc["gate"], packed=False)
+    assert np.array_equal(whole, chain), "the fused layer differs from the chain of its stages"
+    ref_layer, _ = oracle.decoder_layer(h, w64, gate, pos, _f32(c["k_cache"]), _f32(c["v_cache"]), block, nh, nkv)
+    say(f"  layer row rel err {row_relerr(whole, ref_layer):.3g} (composite bar {LAYER_BAR})")

@@ -334,16 +334,19 @@ def layer_shapes(hidden, inter, n_heads, n_kv_heads, head_dim=128):
 
 
 def layer_weights_case(hidden, inter, n_heads, n_kv_heads, r, seed=0, layer=0, weight_std=0.02,
-                       norm_std=0.1):
-    """bf16 weights of one layer: w{p} [out, in], a{p} [r, in], b{p} [out, r]
-    ~ N(0, weight_std^2); attn_norm, mlp_norm = 1 + N(0, norm_std^2).
+                       norm_std=0.1, lora_std=None):
+    """bf16 weights of one layer: w{p} [out, in] ~ N(0, weight_std^2), a{p}
+    [r, in] and b{p} [out, r] ~ N(0, lora_std^2) (default weight_std);
+    attn_norm, mlp_norm = 1 + N(0, norm_std^2).
 
     Returns {name: uint16 bits} and {name + "_f32": exact values}."""
     out = {}
+    lora_std = weight_std if lora_std is None else lora_std
     for i, (p, (n_out, n_in)) in enumerate(layer_shapes(hidden, inter, n_heads, n_kv_heads).items()):
         for name, tag, shp in (("w", _T_LAYER_W, (n_out, n_in)), ("a", _T_LAYER_A, (r, n_in)),
                                ("b", _T_LAYER_B, (n_out, r))):
-            x = rng_for(seed, tag, layer, i).standard_normal(shp, dtype=np.float32) * np.float32(weight_std)
+            std = weight_std if name == "w" else lora_std
+            x = rng_for(seed, tag, layer, i).standard_normal(shp, dtype=np.float32) * np.float32(std)
             out[name + p], out[name + p + "_f32"] = _store(x, "bf16")
     for j, name in enumerate(("attn_norm", "mlp_norm")):
         x = 1.0 + rng_for(seed, _T_LAYER_NORM, layer, j).standard_normal(hidden, dtype=np.float32) * np.float32(norm_std)
@@ -396,7 +399,7 @@ def block_positions(batch, block, ctx):
 
 
 def decoder_layer_case(batch, block, ctx, hidden, inter, n_heads, n_kv_heads, r, seed=0, layer=0,
-                       weight_std=0.02, norm_std=0.1, kv_std=1.0, workers=None, x_std=1.0):
+                       weight_std=0.02, norm_std=0.1, kv_std=1.0, workers=None, x_std=1.0, lora_std=None):
     """Inputs of one decoder layer over `batch` sequences of `block` clean +
     `block` noisy rows: residual stream h [rows, hidden] ~ N(0, x_std^2), gate
     (0 clean, 1 noisy), positions, KV cache [batch, ctx, Hkv, 128] ~
@@ -410,7 +413,7 @@ def decoder_layer_case(batch, block, ctx, hidden, inter, n_heads, n_kv_heads, r,
             "h": h, "gate": default_gate(rows, block), "positions": block_positions(batch, block, ctx),
             "k_cache": kc, "v_cache": vc,
             "weights": layer_weights_case(hidden, inter, n_heads, n_kv_heads, r, seed, layer, weight_std,
-                                          norm_std)}
+                                          norm_std, lora_std)}
 
 
 def rows_case(rows, vocab, dtype="bf16", seed=0, std=2.0):
