@@ -19,7 +19,7 @@ _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too s
 EXPORTS = (
     "uno_abi_version", "uno_status_string", "uno_last_error",
     "uno_gated_lora_linear_workspace", "uno_gated_lora_linear",
-    "uno_psi_spec_verify_linear_workspace", "uno_psi_spec_verify_linear",
+    "uno_psi_spec_verify_linear_workspace", "uno_psi_spec_verify_linear", "uno_psi_spec_verify_linear_noalloc",
     "uno_tree_verify_attention_workspace", "uno_tree_verify_attention",
     "uno_psi_spec_verify_tree_workspace", "uno_psi_spec_verify_tree",
     "uno_rms_norm", "uno_rope", "uno_silu_mul",
@@ -78,6 +78,9 @@ def _declare(lib):
         "uno_psi_spec_verify_linear": (ctypes.c_int, [_p, ctypes.c_int, _i32, _i32, _i32,
                                                       _p, _i64, _i64, _p, _i64, _i64,
                                                       _p, _p, _p, _f32, _p, _p, _p, _p, _p, _p, _sz]),
+        "uno_psi_spec_verify_linear_noalloc": (ctypes.c_int, [_p, ctypes.c_int, _i32, _i32, _i32,
+                                                              _p, _i64, _i64, _p, _i64, _i64,
+                                                              _p, _p, _p, _f32, _p, _p, _p, _p, _p]),
         "uno_tree_verify_attention_workspace": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _i32,
                                                                ctypes.POINTER(_sz)]),
         "uno_tree_verify_attention": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -240,6 +243,37 @@ def psi_spec_verify_linear(p_logits, q_logits, drafts, u_accept, u_sample, tempe
         _ptr(outputs["accept_len"]), _ptr(outputs["token"]),
         _ptr(outputs.get("p_draft")), _ptr(outputs.get("q_draft")), _ptr(outputs.get("residual_mass")),
         _ptr(ws), _nbytes(ws)))
+    return outputs
+
+
+def psi_spec_verify_linear_noalloc(p_logits, q_logits, drafts, u_accept, u_sample, temperature=1.0,
+                                   outputs=None, want_probs=True, stream=None):
+    """uno_psi_spec_verify_linear_noalloc: the linear verify with no workspace
+    (the library's own per-GPU scratch; see include/uno.h).  Arguments and the
+    returned dict as psi_spec_verify_linear; `outputs` may be passed so that
+    nothing at all is allocated here."""
+    import torch
+    load()
+    bsz, k1, vocab = p_logits.shape
+    k = k1 - 1
+    dev = p_logits.device
+    if outputs is None:
+        outputs = {
+            "accept_len": torch.empty(bsz, dtype=torch.int32, device=dev),
+            "token": torch.empty(bsz, dtype=torch.int32, device=dev),
+        }
+        if want_probs:
+            outputs["p_draft"] = torch.empty((bsz, k), dtype=torch.float32, device=dev)
+            outputs["q_draft"] = torch.empty((bsz, k), dtype=torch.float32, device=dev)
+            outputs["residual_mass"] = torch.empty(bsz, dtype=torch.float32, device=dev)
+    qs = q_logits.stride() if q_logits is not None else (0, 0, 1)
+    _check(_lib.uno_psi_spec_verify_linear_noalloc(
+        _stream(stream), _dtype_code(p_logits), bsz, k, vocab,
+        _ptr(p_logits), p_logits.stride(0), p_logits.stride(1),
+        _ptr(q_logits), qs[0], qs[1],
+        _ptr(drafts), _ptr(u_accept), _ptr(u_sample), float(temperature),
+        _ptr(outputs["accept_len"]), _ptr(outputs["token"]),
+        _ptr(outputs.get("p_draft")), _ptr(outputs.get("q_draft")), _ptr(outputs.get("residual_mass"))))
     return outputs
 
 

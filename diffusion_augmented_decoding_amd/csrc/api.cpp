@@ -129,24 +129,19 @@ static uno_status check_verify_linear_shape(int32_t batch, int32_t k, int32_t vo
   return UNO_OK;
 }
 
-uno_status uno_psi_spec_verify_linear_workspace(int32_t batch, int32_t k, int32_t vocab, size_t* bytes) {
-  UNO_GUARD_BEGIN
-  if (!bytes) return fail(UNO_ERR_INVALID_ARGUMENT, "bytes is NULL");
-  uno_status s = check_verify_linear_shape(batch, k, vocab);
-  if (s != UNO_OK) return s;
-  *bytes = verify_linear_workspace_bytes(batch, k, vocab);
-  return UNO_OK;
-  UNO_GUARD_END
-}
+}  // extern "C"
 
-uno_status uno_psi_spec_verify_linear(hipStream_t stream, uno_dtype logit_dtype, int32_t batch, int32_t k,
-                                      int32_t vocab, const void* p_logits, int64_t p_seq_stride,
-                                      int64_t p_row_stride, const void* q_logits, int64_t q_seq_stride,
-                                      int64_t q_row_stride, const int32_t* draft_tokens, const float* u_accept,
-                                      const float* u_sample, float temperature, int32_t* out_accept_len,
-                                      int32_t* out_token, float* out_p_draft, float* out_q_draft,
-                                      float* out_residual_mass, void* workspace, size_t workspace_bytes) {
-  UNO_GUARD_BEGIN
+namespace uno {
+
+// Host validation of a linear verify call (everything but the workspace) and
+// its kernel arguments; shared by the workspace and the allocation-free
+// entry points.
+uno_status verify_linear_args(uno_dtype logit_dtype, int32_t batch, int32_t k, int32_t vocab, const void* p_logits,
+                              int64_t p_seq_stride, int64_t p_row_stride, const void* q_logits,
+                              int64_t q_seq_stride, int64_t q_row_stride, const int32_t* draft_tokens,
+                              const float* u_accept, const float* u_sample, float temperature,
+                              int32_t* out_accept_len, int32_t* out_token, float* out_p_draft, float* out_q_draft,
+                              float* out_residual_mass, VerifyLinearArgs* out) {
   if (logit_dtype != UNO_F32 && logit_dtype != UNO_BF16)
     return fail(UNO_ERR_INVALID_ARGUMENT, "unknown dtype %d", int(logit_dtype));
   uno_status s = check_verify_linear_shape(batch, k, vocab);
@@ -161,9 +156,6 @@ uno_status uno_psi_spec_verify_linear(hipStream_t stream, uno_dtype logit_dtype,
     return fail(UNO_ERR_INVALID_ARGUMENT, "p strides must cover [k+1][vocab]");
   if (k > 0 && (q_row_stride < vocab || q_seq_stride < int64_t(k) * q_row_stride))
     return fail(UNO_ERR_INVALID_ARGUMENT, "q strides must cover [k][vocab]");
-  const size_t need = verify_linear_workspace_bytes(batch, k, vocab);
-  if (workspace_bytes < need || !workspace)
-    return fail(UNO_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
   VerifyLinearArgs a{};
   a.dtype = logit_dtype;
   a.batch = batch;
@@ -185,6 +177,40 @@ uno_status uno_psi_spec_verify_linear(hipStream_t stream, uno_dtype logit_dtype,
   a.out_pd = out_p_draft;
   a.out_qd = out_q_draft;
   a.out_mass = out_residual_mass;
+  *out = a;
+  return UNO_OK;
+}
+
+}  // namespace uno
+
+extern "C" {
+
+uno_status uno_psi_spec_verify_linear_workspace(int32_t batch, int32_t k, int32_t vocab, size_t* bytes) {
+  UNO_GUARD_BEGIN
+  if (!bytes) return fail(UNO_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  uno_status s = check_verify_linear_shape(batch, k, vocab);
+  if (s != UNO_OK) return s;
+  *bytes = verify_linear_workspace_bytes(batch, k, vocab);
+  return UNO_OK;
+  UNO_GUARD_END
+}
+
+uno_status uno_psi_spec_verify_linear(hipStream_t stream, uno_dtype logit_dtype, int32_t batch, int32_t k,
+                                      int32_t vocab, const void* p_logits, int64_t p_seq_stride,
+                                      int64_t p_row_stride, const void* q_logits, int64_t q_seq_stride,
+                                      int64_t q_row_stride, const int32_t* draft_tokens, const float* u_accept,
+                                      const float* u_sample, float temperature, int32_t* out_accept_len,
+                                      int32_t* out_token, float* out_p_draft, float* out_q_draft,
+                                      float* out_residual_mass, void* workspace, size_t workspace_bytes) {
+  UNO_GUARD_BEGIN
+  VerifyLinearArgs a{};
+  uno_status s = verify_linear_args(logit_dtype, batch, k, vocab, p_logits, p_seq_stride, p_row_stride, q_logits,
+                                    q_seq_stride, q_row_stride, draft_tokens, u_accept, u_sample, temperature,
+                                    out_accept_len, out_token, out_p_draft, out_q_draft, out_residual_mass, &a);
+  if (s != UNO_OK) return s;
+  const size_t need = verify_linear_workspace_bytes(batch, k, vocab);
+  if (workspace_bytes < need || !workspace)
+    return fail(UNO_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
   a.ws = workspace;
   return check_hip(launch_verify_linear(a, stream), "uno_psi_spec_verify_linear launch");
   UNO_GUARD_END

@@ -59,6 +59,14 @@ struct VerifyLinearArgs {
 };
 size_t verify_linear_workspace_bytes(int batch, int k, int vocab);
 hipError_t launch_verify_linear(const VerifyLinearArgs& a, hipStream_t stream);
+// Host validation of a linear verify call (all but the workspace); fills the
+// kernel arguments (ws left null).
+uno_status verify_linear_args(uno_dtype logit_dtype, int32_t batch, int32_t k, int32_t vocab, const void* p_logits,
+                              int64_t p_seq_stride, int64_t p_row_stride, const void* q_logits,
+                              int64_t q_seq_stride, int64_t q_row_stride, const int32_t* draft_tokens,
+                              const float* u_accept, const float* u_sample, float temperature,
+                              int32_t* out_accept_len, int32_t* out_token, float* out_p_draft, float* out_q_draft,
+                              float* out_residual_mass, VerifyLinearArgs* out);
 
 // ---------------------------------------------------------------- gated LoRA
 struct GatedLoraArgs {

@@ -130,6 +130,27 @@ uno_status uno_psi_spec_verify_linear(hipStream_t stream, uno_dtype logit_dtype,
                                       float* out_p_draft, float* out_q_draft, float* out_residual_mass,
                                       void* workspace, size_t workspace_bytes);
 
+/* Allocation-free variant of uno_psi_spec_verify_linear, for callers that
+ * cannot allocate device memory or hand over a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  Same
+ * arguments (minus the workspace), same kernels, same outputs bit for bit.
+ * Its scratch is a 16 MiB array of the library's own in device memory, one per
+ * GPU, held until the process ends: a call whose workspace query
+ * (uno_psi_spec_verify_linear_workspace) exceeds 16 MiB returns
+ * UNO_ERR_UNSUPPORTED (16 MiB covers batch 4096 x 64 drafts at vocab
+ * 151,936).  The call allocates nothing.  Every call on one GPU shares that
+ * GPU's array: calls that overlap on a GPU (other streams, other threads)
+ * race on it and must be serialised by the caller. */
+uno_status uno_psi_spec_verify_linear_noalloc(hipStream_t stream, uno_dtype logit_dtype,
+                                              int32_t batch, int32_t k, int32_t vocab,
+                                              const void* p_logits, int64_t p_seq_stride, int64_t p_row_stride,
+                                              const void* q_logits, int64_t q_seq_stride, int64_t q_row_stride,
+                                              const int32_t* draft_tokens,
+                                              const float* u_accept, const float* u_sample,
+                                              float temperature,
+                                              int32_t* out_accept_len, int32_t* out_token,
+                                              float* out_p_draft, float* out_q_draft, float* out_residual_mass);
+
 /* --------------------------------------------------------------------------
  * Tree-masked grouped-query attention for tree verification.
  * Source: Uno summary (hyper.ai), section "方法", last paragraph: the tree

@@ -343,3 +343,23 @@ def test_kv_commit_rejects_bad_calls(lib):
     assert lib.uno_kv_commit(None, 4, -1, FAKE16, FAKE16) == INVALID
     assert lib.uno_kv_commit(None, 4, 16, None, FAKE16) == INVALID
     assert lib.uno_kv_commit(None, 4, 16, FAKE16, None) == INVALID
+
+
+def test_verify_linear_noalloc_rejects_bad_calls(lib):
+    """Host validation of the allocation-free verify: the linear verify's
+    argument checks, and a call whose scratch would exceed the library's
+    16 MiB per-GPU array is refused before anything is enqueued."""
+    def call(**kw):
+        a = dict(dtype=BF16, batch=4, k=3, vocab=1000, p=FAKE16, ps=4000, pr=1000, q=FAKE16, qs=3000, qr=1000,
+                 d=FAKE16, ua=FAKE16, us=FAKE16, t=1.0, L=FAKE16, y=FAKE16)
+        a.update(kw)
+        return lib.uno_psi_spec_verify_linear_noalloc(None, a["dtype"], a["batch"], a["k"], a["vocab"], a["p"],
+                                                      a["ps"], a["pr"], a["q"], a["qs"], a["qr"], a["d"], a["ua"],
+                                                      a["us"], a["t"], a["L"], a["y"], None, None, None)
+    assert call(p=None) == INVALID
+    assert call(k=65) == INVALID
+    assert call(t=0.0) == INVALID
+    assert call(pr=999) == INVALID
+    big = dict(batch=8192, k=64, vocab=151936, ps=65 * 151936, pr=151936, qs=64 * 151936, qr=151936)
+    assert call(**big) == UNSUPPORTED
+    assert b"16777216" in lib.uno_last_error()
