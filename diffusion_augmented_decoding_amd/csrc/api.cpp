@@ -152,9 +152,10 @@ uno_status verify_linear_args(uno_dtype logit_dtype, int32_t batch, int32_t k, i
     return fail(UNO_ERR_INVALID_ARGUMENT, "q_logits, draft_tokens and u_accept must be non-NULL when k > 0");
   if (!(temperature > 0.f) || !std::isfinite(temperature))
     return fail(UNO_ERR_INVALID_ARGUMENT, "temperature must be finite and > 0");
-  if (p_row_stride < vocab || p_seq_stride < int64_t(k + 1) * p_row_stride)
+  // the sequence strides are never used with a single sequence
+  if (p_row_stride < vocab || (batch > 1 && p_seq_stride < int64_t(k + 1) * p_row_stride))
     return fail(UNO_ERR_INVALID_ARGUMENT, "p strides must cover [k+1][vocab]");
-  if (k > 0 && (q_row_stride < vocab || q_seq_stride < int64_t(k) * q_row_stride))
+  if (k > 0 && (q_row_stride < vocab || (batch > 1 && q_seq_stride < int64_t(k) * q_row_stride)))
     return fail(UNO_ERR_INVALID_ARGUMENT, "q strides must cover [k][vocab]");
   VerifyLinearArgs a{};
   a.dtype = logit_dtype;

@@ -102,7 +102,7 @@ uno_status uno_psi_spec_step(hipStream_t stream, const uno_step_config* config, 
   const int kv = (prev_q && k > 0) ? k : 0;
   if (kv > 0) {
     if (!u_accept) return fail(UNO_ERR_INVALID_ARGUMENT, "u_accept is required with prev_q");
-    if (prev_q_row_stride < c.vocab || prev_q_seq_stride < int64_t(k) * prev_q_row_stride)
+    if (prev_q_row_stride < c.vocab || (c.batch > 1 && prev_q_seq_stride < int64_t(k) * prev_q_row_stride))
       return fail(UNO_ERR_INVALID_ARGUMENT, "prev_q strides must cover [k][vocab]");
     if (reinterpret_cast<uintptr_t>(prev_q) & 1u) return fail(UNO_ERR_UNSUPPORTED, "prev_q must be 2-byte aligned");
   }

@@ -24,8 +24,10 @@
  *   No C++ exception crosses this interface.
  * - Threads: calls are reentrant; concurrent calls must not share a workspace.
  * - Aliasing: outputs must not alias inputs or each other.
- * - Data contract: token ids in [0, vocab), finite logits, uniforms in [0, 1).
- *   These are not checked on the device.
+ * - Data contract: token ids in [0, vocab), finite logits with |logit / T| <=
+ *   1e4 (the softmax kernels subtract a separately rounded row maximum inside
+ *   a fused multiply-add; exp(-1e4) is already 0 in fp32, so -1e4 stands for
+ *   probability 0), uniforms in [0, 1).  These are not checked on the device.
  */
 #ifndef UNO_H
 #define UNO_H
@@ -116,7 +118,8 @@ uno_status uno_gated_lora_linear(hipStream_t stream, uno_dtype dtype,
  *   out_q_draft f32 [batch][k] = q_i[d_i], out_residual_mass f32 [batch] =
  *   sum(w) of the row y was drawn from (1 for a bonus draw).
  * Requirements: batch >= 1, 0 <= k <= 64, 1 <= vocab <= 2^20, temperature > 0,
- *   row strides >= vocab, sequence strides >= the rows they hold.
+ *   row strides >= vocab, sequence strides >= the rows they hold (not
+ *   checked, and not used, when batch is 1).
  * ------------------------------------------------------------------------ */
 uno_status uno_psi_spec_verify_linear_workspace(int32_t batch, int32_t k, int32_t vocab, size_t* bytes);
 uno_status uno_psi_spec_verify_linear(hipStream_t stream, uno_dtype logit_dtype,

@@ -177,3 +177,31 @@ def test_verify_tree_batch_of_different_trees(gpu_lib):
     good = {k: (v[:3] if isinstance(v, np.ndarray) else v) for k, v in c.items()}
     good["batch"] = 3
     assert _check_verify(good, {k: v[:3] for k, v in g.items()}) <= 1
+
+
+def test_tree_handworked_golden_cases(gpu_lib):
+    """The hand-worked trees of tests/golden/verify_tree_handworked.json
+    (ascending sibling order, a duplicate sibling rejected by the residual,
+    every child rejected, the second depth's marginal) through the HIP
+    kernels with fp32 logits ln(p): accepted length, path and token exactly
+    as worked by hand."""
+    import json
+    import os
+    import torch
+    with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "verify_tree_handworked.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        say(f"tree golden {c['name']}")
+        parent = np.asarray([c["parent"]], np.int32)
+        pl = np.log(np.maximum(np.array(c["p"]), 1e-300)).astype(np.float32)[None]
+        ql = np.log(np.maximum(np.array(c["q"]), 1e-300)).astype(np.float32)[None]
+        out = gpu_lib.psi_spec_verify_tree(to_dev(parent), to_dev(np.asarray([c["tokens"]], np.int32)), to_dev(pl),
+                                           to_dev(ql), to_dev(np.asarray([c["u_accept"]], np.float32)),
+                                           to_dev(np.asarray([c["u_sample"]], np.float32)),
+                                           max_children=workloads.max_children(parent))
+        torch.cuda.synchronize()
+        e = c["expect"]
+        L = int(to_host(out["accept_len"])[0])
+        assert L == e["accept_len"], c["name"]
+        assert list(to_host(out["path"])[0, :L]) == e["path"], c["name"]
+        assert int(to_host(out["token"])[0]) == e["token"], c["name"]

@@ -6,11 +6,17 @@ the drafts within 1e-5 relative (fp32 outputs); residual mass within 1e-5
 absolute (a sum of at most 2^20 fp32 probability differences).
 """
 
+import json
+import os
+
 import numpy as np
 import pytest
 
+import oracle
 import workloads
-from _parity import check_linear, say, to_dev, to_host
+from _parity import TIE, check_linear, draw_is_valid, say, to_dev, to_host
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "verify_linear_handworked.json")
 
 pytestmark = pytest.mark.gpu
 
@@ -78,7 +84,7 @@ def test_identical_draft_accepts_all_and_determinism(gpu_lib):
 def test_parity_full_vocab_batch(gpu_lib, sigma):
     """The sampler workload at batch 256 x block 16 (k = 15), vocab 151,936,
     bf16, checked on sampled sequences (the oracle recomputes each one)."""
-    batch = 256 if sigma == 0.5 else 32
+    batch = 256
     say(f"verify_linear full V sigma={sigma} batch={batch}: generating")
     c = workloads.verify_linear_case(batch, 15, 151936, sigma, dtype="bf16", seed=0, keep_f32=False)
     say("  running on GPU")
@@ -97,3 +103,92 @@ def test_parity_full_vocab_batch(gpu_lib, sigma):
     ties = check_linear(rows, g, seqs, 15)
     say(f"  ties: {ties}; mean accepted length {g['accept_len'].mean():.3f}")
     assert ties <= 1
+
+
+def _logits(prob):
+    """ln(prob), with probability 0 as the logit -1e4 (exp(-1e4) is 0 in fp32
+    and in float64 alike; the data contract bounds |logit / T| by 1e4)."""
+    with np.errstate(divide="ignore"):
+        return np.maximum(np.log(np.asarray(prob, np.float64)), -1e4)
+
+
+def _f32_case(p, q, drafts, u_acc, u_s):
+    """Device tensors of one sequence given as probabilities (fp32 logits ln p)."""
+    pl = _logits(p).astype(np.float32)[None]
+    ql = _logits(q).astype(np.float32).reshape(1, -1, pl.shape[2])
+    return [to_dev(pl), to_dev(ql), to_dev(np.asarray([drafts], np.int32)),
+            to_dev(np.asarray([u_acc], np.float32).reshape(1, -1)), to_dev(np.asarray([u_s], np.float32))]
+
+
+def test_handworked_golden_cases(gpu_lib):
+    """The hand-worked cases of tests/golden/verify_linear_handworked.json
+    (residual point mass, accept then bonus, p/q = 1, all accepted, a bonus
+    draw exactly on a CDF boundary) through the HIP kernels with fp32 logits
+    ln(p): accepted length and token exactly as worked by hand, the draft
+    probabilities within 1e-5 relative, the residual mass within 1e-5."""
+    import torch
+    with open(GOLDEN) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        say(f"golden {c['name']}")
+        out = gpu_lib.psi_spec_verify_linear(*_f32_case(c["p"], c["q"], c["drafts"], c["u_accept"], c["u_sample"]))
+        torch.cuda.synchronize()
+        g = {kk: to_host(v) for kk, v in out.items()}
+        e = c["expect"]
+        assert int(g["accept_len"][0]) == e["accept_len"], c["name"]
+        assert int(g["token"][0]) == e["token"], c["name"]
+        np.testing.assert_allclose(g["p_draft"][0], e["p_draft"], rtol=1e-5)
+        np.testing.assert_allclose(g["q_draft"][0], e["q_draft"], rtol=1e-5)
+        assert abs(float(g["residual_mass"][0]) - e["residual_mass"]) <= 1e-5, c["name"]
+
+
+def test_edge_one_hot_and_zero_residual(gpu_lib):
+    """Edge cases of the accept rule and the residual draw, each against the
+    oracle and its closed form:
+    * p one-hot at v != d: every draft rejected, y = v;
+    * q one-hot at d: the draft is accepted iff u < p(d), and a rejection draws
+      from p without d;
+    * a rejected draft of probability 0 under p = q: the residual
+      max(0, p - q) has no mass, so y is drawn from p instead (S = 0 fallback,
+      residual mass reported as 1)."""
+    import torch
+    V = 300
+    rng = np.random.default_rng(3)
+    base = rng.dirichlet(np.ones(V))
+    # p one-hot at 17 (every other token probability exactly 0), drafts elsewhere
+    p = np.zeros((3, V))
+    p[:, 17] = 1.0
+    q = np.tile(base, (2, 1))
+    out = gpu_lib.psi_spec_verify_linear(*_f32_case(p, q, [3, 4], [0.0, 0.0], 0.9))
+    torch.cuda.synchronize()
+    assert int(to_host(out["accept_len"])[0]) == 0 and int(to_host(out["token"])[0]) == 17
+    # q one-hot at the draft d = 5: accept iff u < p(5)
+    p = np.tile(base, (2, 1))
+    q = np.zeros((1, V))
+    q[0, 5] = 1.0
+    for u in (0.5 * base[5], 1.5 * base[5]):
+        for us in (0.1, 0.6, 0.95):
+            out = gpu_lib.psi_spec_verify_linear(*_f32_case(p, q, [5], [u], us))
+            torch.cuda.synchronize()
+            L, y = int(to_host(out["accept_len"])[0]), int(to_host(out["token"])[0])
+            assert L == (1 if u < base[5] else 0)
+            w = base.copy() if L == 1 else np.where(np.arange(V) == 5, 0.0, base)
+            ref = oracle.inverse_cdf(w, us)
+            assert y == ref or draw_is_valid(w, us, y, TIE), (u, us, y, ref)
+    # S = 0: p = q, the draft has probability 0 under both, so it is rejected
+    # and the residual max(0, p - q) is empty: y is drawn from p
+    pz = base.copy()
+    pz[9] = 0.0
+    pz /= pz.sum()
+    p = np.tile(pz, (2, 1))
+    q = pz[None]
+    for us in (0.05, 0.5, 0.97):
+        out = gpu_lib.psi_spec_verify_linear(*_f32_case(p, q, [9], [0.3], us))
+        torch.cuda.synchronize()
+        g = {kk: to_host(v) for kk, v in out.items()}
+        o = oracle.verify_linear(_logits(p)[None], _logits(q)[None], np.array([[9]]), np.array([[0.3]]),
+                                 np.array([us]))
+        assert int(g["accept_len"][0]) == 0 == int(o["accept_len"][0])
+        assert abs(float(g["residual_mass"][0]) - 1.0) <= 1e-5          # the fallback row is p itself
+        assert int(g["token"][0]) == int(o["token"][0]) or draw_is_valid(pz, us, int(g["token"][0]), TIE)
+        assert int(g["token"][0]) != 9
