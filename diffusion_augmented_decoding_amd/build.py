@@ -1,9 +1,12 @@
 """Build libunospec.so in-tree with hipcc for gfx950.
 
-    python -m diffusion_augmented_decoding_amd.build [--verbose]
+    python -m diffusion_augmented_decoding_amd.build [--verbose] [--tuning]
 
 Compiles every csrc/*.hip and csrc/*.cpp to an object under _build/ (in
 parallel) and links them into diffusion_augmented_decoding_amd/libunospec.so.
+--tuning builds libunospec_tuning.so instead (objects under _build/tuning/),
+compiled with -DUNO_TUNING: that library reads the UNO_* tile and split
+overrides from the environment for sweeps; libunospec.so never does.
 """
 
 import glob
@@ -61,25 +64,29 @@ def _run(cmd, verbose):
         print(out, flush=True)
 
 
-def build(verbose=False, jobs=None):
-    """Compile and link libunospec.so; returns its path."""
+def build(verbose=False, jobs=None, tuning=False):
+    """Compile and link libunospec.so (libunospec_tuning.so with tuning=True);
+    returns its path."""
     hipcc = _hipcc()
-    os.makedirs(BUILD, exist_ok=True)
+    bdir = os.path.join(BUILD, "tuning") if tuning else BUILD
+    lib = os.path.join(PKG, "libunospec_tuning.so") if tuning else LIB
+    extra = ["-DUNO_TUNING"] if tuning else []
+    os.makedirs(bdir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     objs = []
     cmds = []
     for s in srcs:
-        o = os.path.join(BUILD, os.path.basename(s) + ".o")
+        o = os.path.join(bdir, os.path.basename(s) + ".o")
         objs.append(o)
-        cmds.append([hipcc] + COMMON_FLAGS + FILE_FLAGS.get(os.path.basename(s), []) + ["-c", s, "-o", o])
+        cmds.append([hipcc] + COMMON_FLAGS + extra + FILE_FLAGS.get(os.path.basename(s), []) + ["-c", s, "-o", o])
     jobs = jobs or min(8, len(cmds))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="--verbose" in sys.argv))
+    print(build(verbose="--verbose" in sys.argv, tuning="--tuning" in sys.argv))

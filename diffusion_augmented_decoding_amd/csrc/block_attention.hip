@@ -473,12 +473,10 @@ template <int S>
 hipError_t launch_stages(const TreeAttnArgs& a, const BlkPlan& pl, int64_t nwg, float* part_o, float2* part_ms,
                          hipStream_t stream) {
   const size_t lds = size_t(S) * kStageBytes;
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(block_attn_kernel<S>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  static std::atomic<uint64_t> configured{0};
+  {
+    hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(block_attn_kernel<S>), int(lds), configured);
     if (e != hipSuccess) return e;
-    configured = true;
   }
   hipLaunchKernelGGL(block_attn_kernel<S>, dim3(unsigned(nwg)), dim3(kThreads), lds, stream, a, pl, part_o, part_ms);
   return hipGetLastError();
@@ -507,7 +505,7 @@ hipError_t launch_block_attention(const TreeAttnArgs& a, hipStream_t stream) {
   }
   int stages = kStagesDefault;
   {
-    const char* env = getenv("UNO_ATTN_STAGES");   // tuning override: 3..5
+    const char* env = tuning_env("UNO_ATTN_STAGES");   // tuning override: 3..5
     if (env && atoi(env) >= 3 && atoi(env) <= 5) stages = atoi(env);
   }
   hipError_t e = hipSuccess;

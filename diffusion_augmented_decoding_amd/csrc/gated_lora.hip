@@ -161,6 +161,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p
   int tm, tn;
   tile_coords(p, tile, tm, tn);
   static_assert(MODE != 2 || (FAST && BN == 256 && WM * WN == 8), "SwiGLU tiles: 256 weight rows, 8 waves");
+  static_assert(MODE >= 0 && MODE <= 2, "modes of the main kernel: bf16 out, partials, SwiGLU");
   const int m0 = tm * BM;
   int n0 = tn * (MODE == 2 ? BN / 2 : BN);   // MODE 2: first feature of the tile
   if constexpr (MODE == 0 && FAST) {
@@ -500,6 +501,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_dl_kernel(GemmParams p) 
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(BN % 16 == 0 && BM % 16 == 0, "tile rows come in 16-row blocks");
   static_assert(S >= 3, "the pipeline keeps two stages ahead of the one computed");
+  static_assert(MODE >= 0 && MODE <= 2, "modes: bf16 out, partials, SwiGLU");
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
   // the LDS base as an opaque value: the optimizer cannot tell which LDS bytes
@@ -830,7 +832,8 @@ constexpr TileShape kShapes[] = {
     {"dl256x192s4", 256, 192, 8},    {"dl256x192s5", 256, 192, 8},    {"dl256x128s6", 256, 128, 8},
     {"dl128x128s6", 128, 128, 4},    {"dl256x256w4s4", 256, 256, 4},  {"dl256x256w4s5", 256, 256, 4},
     {"dl128x384s4", 128, 384, 8},    {"dl128x256s6", 128, 256, 8},    {"dl128x384s5", 128, 384, 8},
-    {"dl128x256s4", 128, 256, 8},
+    {"dl128x256s4", 128, 256, 8},    {"dl64x384s4", 64, 384, 4},      {"dl64x256s4", 64, 256, 4},
+    {"dl64x128s6", 64, 128, 2},
 };
 constexpr int kNumShapes = int(sizeof(kShapes) / sizeof(kShapes[0]));
 
@@ -852,18 +855,16 @@ template <int BM, int BN, int WM, int WN, int P, int DBF, int MODE, int FAST>
 hipError_t launch_tile_k(GemmParams p, int splits, hipStream_t stream, const char* name) {
   auto kern = gemm_bf16_kernel<BM, BN, WM, WN, P, DBF, MODE, FAST>;
   const size_t lds = 2 * size_t(BN + BM) * kBK * 2;
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  static std::atomic<uint64_t> configured{0};
+  {
+    hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), int(lds), configured);
     if (e != hipSuccess) return e;
-    configured = true;
   }
   constexpr int TILE_N = MODE == 2 ? BN / 2 : BN;   // MODE 2: features per tile
   p.tiles_m = (p.M + BM - 1) / BM;
   p.tiles_n = (p.N + TILE_N - 1) / TILE_N;
   {
-    const char* env = getenv("UNO_GEMM_XCD");   // tuning override: 0 no remap, 1 column bands, 2 (default) 2D groups
+    const char* env = tuning_env("UNO_GEMM_XCD");   // tuning override: 0 no remap, 1 column bands, 2 (default) 2D groups
     p.xcd_remap = env ? atoi(env) : 2;
   }
   p.ktiles_per_split = ((p.K1 + kBK - 1) / kBK + splits - 1) / splits;
@@ -875,7 +876,7 @@ hipError_t launch_tile_k(GemmParams p, int splits, hipStream_t stream, const cha
 
 template <int BM, int BN, int WM, int WN, int P, int DBF, int MODE>
 hipError_t launch_tile(GemmParams p, int splits, hipStream_t stream, const char* name) {
-  const char* env = getenv("UNO_GEMM_FAST");   // tuning override: 0 keeps the masked loads
+  const char* env = tuning_env("UNO_GEMM_FAST");   // tuning override: 0 keeps the masked loads
   if (fast_ok(p, BM, BN) && !(env && atoi(env) == 0))
     return launch_tile_k<BM, BN, WM, WN, P, DBF, MODE, 1>(p, splits, stream, name);
   return launch_tile_k<BM, BN, WM, WN, P, DBF, MODE, 0>(p, splits, stream, name);
@@ -887,17 +888,15 @@ hipError_t launch_tile_dl(GemmParams p, int splits, hipStream_t stream, const ch
   constexpr int NW = WM * WN;
   constexpr int LPW = ((BN + BM + 15) / 16 + NW - 1) / NW;
   const size_t lds = size_t(S) * LPW * NW * 1024;
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  static std::atomic<uint64_t> configured{0};
+  {
+    hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), int(lds), configured);
     if (e != hipSuccess) return e;
-    configured = true;
   }
   p.tiles_m = (p.M + BM - 1) / BM;
   p.tiles_n = (p.N + BN - 1) / BN;
   {
-    const char* env = getenv("UNO_GEMM_XCD");
+    const char* env = tuning_env("UNO_GEMM_XCD");
     p.xcd_remap = env ? atoi(env) : 2;
   }
   p.ktiles_per_split = ((p.K1 + kBKd - 1) / kBKd + splits - 1) / splits;
@@ -907,33 +906,52 @@ hipError_t launch_tile_dl(GemmParams p, int splits, hipStream_t stream, const ch
   return hipGetLastError();
 }
 
+// The shapes the dispatcher chooses are always built; the others only in a
+// tuning build (they are reachable through the tile overrides alone).
+// The LoRA-down shapes (direct-to-LDS kernel, MODE 1: partials for the gate kernel).
+template <int MODE>
+hipError_t launch_cfg_dl(const TileCfg& c, const GemmParams& p, hipStream_t stream, const char* name) {
+  switch (c.shape) {
+    case 15: return launch_tile_dl<128, 128, 2, 2, 6, MODE>(p, c.splits, stream, name);
+    case 18: return launch_tile_dl<128, 384, 2, 4, 4, MODE>(p, c.splits, stream, name);
+    case 21: return launch_tile_dl<128, 256, 2, 4, 4, MODE>(p, c.splits, stream, name);
+#ifdef UNO_TUNING
+    case 22: return launch_tile_dl<64, 384, 1, 4, 4, MODE>(p, c.splits, stream, name);
+    case 23: return launch_tile_dl<64, 256, 1, 4, 4, MODE>(p, c.splits, stream, name);
+    case 24: return launch_tile_dl<64, 128, 1, 2, 6, MODE>(p, c.splits, stream, name);
+    case 19: return launch_tile_dl<128, 256, 2, 4, 6, MODE>(p, c.splits, stream, name);
+    case 20: return launch_tile_dl<128, 384, 2, 4, 5, MODE>(p, c.splits, stream, name);
+#endif
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
 template <int MODE>
 hipError_t launch_cfg(const TileCfg& c, const GemmParams& p, hipStream_t stream, const char* name) {
   switch (c.shape) {
     case 0: return launch_tile<64, 64, 2, 2, 4, 1, MODE>(p, c.splits, stream, name);
     case 1: return launch_tile<128, 128, 2, 2, 4, 1, MODE>(p, c.splits, stream, name);
+    case 5: return launch_tile<256, 192, 4, 2, 2, 0, MODE>(p, c.splits, stream, name);
+    case 9: return launch_tile<256, 256, 4, 2, 1, 0, MODE>(p, c.splits, stream, name);
+#ifdef UNO_TUNING
     case 2: return launch_tile<256, 192, 2, 2, 2, 0, MODE>(p, c.splits, stream, name);
     case 3: return launch_tile<256, 192, 4, 2, 2, 1, MODE>(p, c.splits, stream, name);
     case 4: return launch_tile<256, 192, 4, 2, 1, 1, MODE>(p, c.splits, stream, name);
-    case 5: return launch_tile<256, 192, 4, 2, 2, 0, MODE>(p, c.splits, stream, name);
     case 6: return launch_tile<256, 128, 4, 2, 3, 1, MODE>(p, c.splits, stream, name);
     case 7: return launch_tile<256, 128, 4, 2, 2, 0, MODE>(p, c.splits, stream, name);
     case 8: return launch_tile<256, 256, 2, 2, 1, 0, MODE>(p, c.splits, stream, name);
-    case 9: return launch_tile<256, 256, 4, 2, 1, 0, MODE>(p, c.splits, stream, name);
     case 10: return launch_tile_dl<256, 256, 4, 2, 4, MODE>(p, c.splits, stream, name);
     case 11: return launch_tile_dl<256, 256, 4, 2, 5, MODE>(p, c.splits, stream, name);
     case 12: return launch_tile_dl<256, 192, 4, 2, 4, MODE>(p, c.splits, stream, name);
     case 13: return launch_tile_dl<256, 192, 4, 2, 5, MODE>(p, c.splits, stream, name);
     case 14: return launch_tile_dl<256, 128, 4, 2, 6, MODE>(p, c.splits, stream, name);
-    case 15: return launch_tile_dl<128, 128, 2, 2, 6, MODE>(p, c.splits, stream, name);
     case 16: return launch_tile_dl<256, 256, 2, 2, 4, MODE>(p, c.splits, stream, name);
     case 17: return launch_tile_dl<256, 256, 2, 2, 5, MODE>(p, c.splits, stream, name);
-    case 18: return launch_tile_dl<128, 384, 2, 4, 4, MODE>(p, c.splits, stream, name);
-    case 19: return launch_tile_dl<128, 256, 2, 4, 6, MODE>(p, c.splits, stream, name);
-    case 20: return launch_tile_dl<128, 384, 2, 4, 5, MODE>(p, c.splits, stream, name);
-    case 21: return launch_tile_dl<128, 256, 2, 4, 4, MODE>(p, c.splits, stream, name);
-
+#endif
+    default: break;
   }
+  if constexpr (MODE == 1) return launch_cfg_dl<MODE>(c, p, stream, name);
   return hipErrorInvalidValue;
 }
 
@@ -948,7 +966,7 @@ int shape_index(const char* name) {
 // The choice depends on the base K only, so a call with and without adapter
 // columns runs the same kernel and split (bit-identical gate-0 rows).
 TileCfg choose_main_tile(int64_t M, int64_t N, int64_t Ktot) {
-  const char* env = getenv("UNO_GEMM_TILE");
+  const char* env = tuning_env("UNO_GEMM_TILE");
   if (env) {
     char nm[32] = {0};
     int s = 1;
@@ -1009,7 +1027,7 @@ TileCfg lora_down_cfg(int64_t M, int64_t r, int64_t K) {
     s = (256 + tiles - 1) / tiles;
   }
   {
-    const char* env = getenv("UNO_LORA_SPLITS");   // tuning override (sweeps): partials for this many splits
+    const char* env = tuning_env("UNO_LORA_SPLITS");   // tuning override (sweeps): partials for this many splits
     if (env && atoi(env) >= 1 && atoi(env) <= 16) s = atoi(env);
   }
   if (s > kt / 2) s = kt / 2;
@@ -1040,7 +1058,7 @@ size_t lora_down_part_bytes(int64_t M, int64_t n, int64_t K) {
 
 namespace {
 
-bool is_dl_shape(int shape) { return shape == 15 || shape == 18 || shape == 21; }
+bool is_dl_shape(int shape) { return shape == 15 || (shape >= 18 && shape <= 24); }
 
 // The gathered LoRA-down (structured gate): over the M / 2 gated rows only,
 // when those rows take a direct-to-LDS tile, the gate kernel's vector form
@@ -1080,10 +1098,11 @@ hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t stream) {
   d.gather_blk = gather ? a.gather_blk : 0;
   TileCfg dc = lora_down_cfg(Mg, a.n, a.K);
   {
-    // tuning override "<shape name>/<splits>" (sweeps only); the split count sizes the
-    // partials, so it may not exceed the one the workspace was sized for
-    const char* env = getenv("UNO_LORA_TILE");
-    if (env && !gather) {
+    // tuning build: per-shape override UNO_LORA_TILE_<n>_<K>="<shape name>/<splits>"
+    char key[64];
+    snprintf(key, sizeof(key), "UNO_LORA_TILE_%lld_%lld", (long long)a.n, (long long)a.K);
+    const char* env = tuning_env(key);
+    if (env) {
       char nm[32] = {0};
       const char* slash = strchr(env, '/');
       const size_t len = slash ? size_t(slash - env) : strlen(env);
@@ -1091,16 +1110,40 @@ hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t stream) {
         memcpy(nm, env, len);
         const int id = shape_index(nm);
         const int sp = slash ? atoi(slash + 1) : 1;
-        if (id >= 0 && sp >= 1 && sp <= splits) dc = TileCfg{id, sp};
+        if (id >= 0 && sp >= 1 && sp <= splits && (!gather || is_dl_shape(id))) dc = TileCfg{id, sp};
       }
     }
   }
-  hipError_t e = launch_cfg<1>(dc, d, stream, "uno_lora_down_bf16");
+  {
+    // tuning override "<shape name>/<splits>" (sweeps only); the split count sizes the
+    // partials, so it may not exceed the one the workspace was sized for
+    const char* env = tuning_env("UNO_LORA_TILE");
+    if (env) {
+      char nm[32] = {0};
+      const char* slash = strchr(env, '/');
+      const size_t len = slash ? size_t(slash - env) : strlen(env);
+      if (len < sizeof(nm)) {
+        memcpy(nm, env, len);
+        const int id = shape_index(nm);
+        const int sp = slash ? atoi(slash + 1) : 1;
+        if (id >= 0 && sp >= 1 && sp <= splits && (!gather || is_dl_shape(id))) dc = TileCfg{id, sp};
+      }
+    }
+  }
+  // the vector form needs 4-element rows and 16-byte aligned partials / 8-byte aligned T
+  const bool vec = a.n % 4 == 0 && (reinterpret_cast<uintptr_t>(a.part) & 15u) == 0 &&
+                   (reinterpret_cast<uintptr_t>(a.t) & 7u) == 0;
+  char pname[64] = "uno_lora_down_bf16", gname[64] = "uno_lora_gate";
+#ifdef UNO_TUNING
+  // tuning build: kernel timings named per shape
+  snprintf(pname, sizeof(pname), "uno_lora_down_bf16_%lld_%lld", (long long)a.n, (long long)a.K);
+  snprintf(gname, sizeof(gname), "uno_lora_gate_%lld_%lld", (long long)a.n, (long long)a.K);
+#endif
+  hipError_t e = launch_cfg<1>(dc, d, stream, pname);
   if (e != hipSuccess) return e;
   const int64_t n = a.M * a.n;
-  ProfileScope ps("uno_lora_gate", stream);
-  // the vector form needs 4-element rows and 16-byte aligned partials / 8-byte aligned T
-  if (a.n % 4 == 0 && (reinterpret_cast<uintptr_t>(a.part) & 15u) == 0 && (reinterpret_cast<uintptr_t>(a.t) & 7u) == 0)
+  ProfileScope ps(gname, stream);
+  if (vec)
     hipLaunchKernelGGL(lora_gate4_kernel, dim3(unsigned((n / 4 + 255) / 256)), dim3(256), 0, stream,
                        static_cast<const float*>(a.part), dc.splits, int(a.M), int(a.n), a.gate, a.lora_scale, a.t,
                        gather ? a.gather_blk : 0);

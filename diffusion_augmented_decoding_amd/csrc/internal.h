@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
+
+#include <atomic>
 
 #include "../../include/uno.h"
 
@@ -32,6 +35,30 @@ struct ProfileScope {
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Tuning overrides for sweeps: a build compiled with -DUNO_TUNING reads them
+// from the environment; the library as built for use ignores the environment.
+inline const char* tuning_env(const char* name) {
+#ifdef UNO_TUNING
+  return getenv(name);
+#else
+  (void)name;
+  return nullptr;
+#endif
+}
+
+// Raise a kernel's dynamic-LDS limit to `bytes` once per device: `done` holds
+// one bit per device id (ids >= 64 set the attribute on every launch).
+inline hipError_t ensure_dynamic_lds(const void* kern, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t(1) << dev) : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
 
 // ---------------------------------------------------------------- sampler
 struct RowStat {   // per logit row, log2 domain: y = logit * log2(e) / T
@@ -273,6 +300,7 @@ struct StepSetupArgs {
   int32_t* positions;
 };
 hipError_t launch_step_setup(const StepSetupArgs& a, hipStream_t stream);
+
 
 // KV commit after verification, for b < batch: with len = cache_len[b]
 // (clamped to [0, cap]) and L = accept_len[b], cache_len[b] = len + L + 1 when
