@@ -84,6 +84,8 @@ def main():
     ap.add_argument("--workload", choices=("step", "hot_path"), default="step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-components", action="store_true", help="skip the per-layer/sampler/tree workloads")
+    ap.add_argument("--unmerged", action="store_true",
+                    help="full step without gate-merged weights: every projection runs the LoRA-down path")
     ap.add_argument("--copy-probe", action="store_true",
                     help="end with a plain 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -105,6 +107,7 @@ def main():
             out["components"]["layer_1024_rows"] = comp["components"]["gated_lora_layer"]
             out["components"]["linear_verify_256x16"] = comp["components"]["linear_verify"]
             out["components"]["tree_batch1"] = comp["components"]["tree"]
+            out["components"]["linear_verify_sigma_sweep"] = bench_linear_sigma_sweep(args, dad, torch)
     else:
         out = bench_hot_path(args, dad, torch, steps=args.steps, warmup=args.warmup,
                              with_cpu=not args.no_cpu_baseline)
@@ -122,16 +125,20 @@ def main():
 
 
 # ====================================================================== full step
-def full_step_flops(m_on):
-    """Algorithmic GEMM work of one step: base projections + on-row LoRA-up (main
-    GEMM kernel), on-row LoRA-down (its own kernel), LM head."""
+def full_step_flops(m_on, merged=False):
+    """GEMM work of one step: base projections + on-row LoRA-up (main GEMM
+    kernel), on-row LoRA-down (its own kernel), LM head.  merged: the gated
+    rows read W + B A, so the main GEMM does 2 M N K per projection and there
+    is no LoRA-down (the work executed; the adapter's own flops are not
+    credited)."""
     f = FULL
     rows = f["batch"] * 2 * f["block"]
     qd, kvd = f["n_heads"] * 128, f["n_kv"] * 128
     shapes = [(qd, f["hidden"]), (kvd, f["hidden"]), (kvd, f["hidden"]), (f["hidden"], qd),
               (f["inter"], f["hidden"]), (f["inter"], f["hidden"]), (f["hidden"], f["inter"])]
-    main = sum(2.0 * rows * n * k + 2.0 * m_on * f["r"] * n for n, k in shapes) * f["n_layers"]
-    down = sum(2.0 * m_on * f["r"] * k for n, k in shapes) * f["n_layers"]
+    up = 0.0 if merged else 1.0
+    main = sum(2.0 * rows * n * k + up * 2.0 * m_on * f["r"] * n for n, k in shapes) * f["n_layers"]
+    down = up * sum(2.0 * m_on * f["r"] * k for n, k in shapes) * f["n_layers"]
     head = 2.0 * rows * f["vocab"] * f["hidden"]
     return main + head, down
 
@@ -184,6 +191,9 @@ def bench_full_step(args, dad, torch):
             w["w" + p] = randn((n_out, n_in), 0.02)
             w["a" + p] = packed_a[p] if p in packed_a else randn((r, n_in), 0.02)
             w["b" + p] = randn((n_out, r), 0.02)
+        if not args.unmerged:
+            # load-time set-up: the gated (noisy) rows read W + B A
+            dad.merge_layer(w)
         kc = randn((B, cap, Hkv, 128), 1.0)
         vc = randn((B, cap, Hkv, 128), 1.0)
         keep.append((w, kc, vc))
@@ -272,7 +282,7 @@ def bench_full_step(args, dad, torch):
     value = tokens_timed / (args.steps * ms_per_step * 1e-3)
 
     m_on = B * blk
-    gemm_flops, down_flops = full_step_flops(m_on)
+    gemm_flops, down_flops = full_step_flops(m_on, merged=not args.unmerged)
     attn_bytes = full_step_attention_bytes()
     launches_per_step = dom_cnt / args.steps
     per_launch_ms = dom_ms / max(1, dom_cnt)
@@ -346,6 +356,9 @@ def bench_full_step(args, dad, torch):
                    "decode_loop": "chained: each step takes the previous step's ids [y, drafts, noisy ids] and "
                                   "verifies the drafts against the previous step's noisy-row logits",
                    "ctx_len_timed_mean": float((len_start.mean() + len_end.mean()) / 2),
+                   "lora": ("LoRA-down over the noisy rows + [x|T][W|B]^T" if args.unmerged else
+                            "gate-merged weights set up at load (uno_lora_merge): clean rows x W^T, noisy rows "
+                            "x (W + B A)^T, no LoRA-down in the step"),
                    "tokens_per_step": tokens_per_step, "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,
@@ -578,6 +591,67 @@ def bench_hot_path(args, dad, torch, steps, warmup, with_cpu):
         "cpu_baseline": cpu,
         "components": components,
     }
+
+
+def bench_linear_sigma_sweep(args, dad, torch, sigmas=(0.1, 0.5, 2.0), reps=20):
+    """The linear verify at batch 256 x block 16 (k = 15), V = 151,936, bf16, for
+    several draft/target distances sigma: AR logits ~ N(0, 2^2), draft logits =
+    AR logits + N(0, sigma^2), drafts by Gumbel-max from the draft rows (the
+    distribution of workloads.verify_linear_case, generated on the device).
+    Reports the verify's time (HIP events around its launches), its HBM rate
+    over the rows it reads, the mean accepted length, and two lower bounds at
+    the 8 TB/s peak: reading every row once (what this design reads), and
+    reading only the rows an early exit at the first rejection would need
+    (p and q rows 0..L, plus the residual or bonus rows of the draw)."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    B, k, V = LIN_BATCH, LIN_K, VOCAB
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed + 1)
+    ws = torch.empty(dad.psi_spec_verify_linear_workspace(B, k, V), dtype=torch.uint8, device=dev)
+    out = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+           "token": torch.empty(B, dtype=torch.int32, device=dev)}
+    names = ("uno_row_stats", "uno_accept", "uno_draw_seg", "uno_draw_resolve")
+    res = []
+    for sigma in sigmas:
+        lp = torch.randn((B, k + 1, V), device=dev, generator=gen) * 2.0
+        lq = lp[:, :k] + torch.randn((B, k, V), device=dev, generator=gen) * sigma
+        p = lp.to(torch.bfloat16)
+        q = lq.to(torch.bfloat16)
+        del lp, lq
+        g = -torch.log(-torch.log(torch.rand((B, k, V), device=dev, generator=gen).clamp_(1e-30, 1.0)))
+        drafts = torch.argmax(q.float() + g, dim=-1).to(torch.int32)
+        del g
+        ua = torch.rand((B, k), device=dev, generator=gen)
+        us = torch.rand((B,), device=dev, generator=gen)
+        for _ in range(3):
+            dad.psi_spec_verify_linear(p, q, drafts, ua, us, outputs=out, workspace=ws)
+        torch.cuda.synchronize()
+        dad.profile_reset()
+        dad.profile_enable(True)
+        for _ in range(reps):
+            dad.psi_spec_verify_linear(p, q, drafts, ua, us, outputs=out, workspace=ws)
+        torch.cuda.synchronize()
+        ms = sum(dad.profile_query(n)[0] for n in names) / reps
+        stats_ms = dad.profile_query("uno_row_stats")[0] / reps
+        dad.profile_enable(False)
+        dad.profile_reset()
+        L = out["accept_len"].cpu().numpy().astype(np.int64)
+        row = V * 2.0
+        full_bytes = B * (2 * k + 1) * row
+        draw_rows = np.where(L < k, 2, 1)               # residual: p_L and q_L; bonus: p_k
+        needed = (L + 1) + np.minimum(L + 1, k) + draw_rows
+        early_bytes = float(needed.sum()) * row
+        res.append({"sigma": sigma, "us": ms * 1e3, "row_stats_us": stats_ms * 1e3,
+                    "row_stats_gbs": full_bytes / (stats_ms * 1e-3) / 1e9,
+                    "row_stats_hbm_frac": full_bytes / (stats_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "mean_accept_len": float(L.mean()),
+                    "full_read_lower_bound_us": full_bytes / (HBM_PEAK_GBS * 1e9) * 1e6,
+                    "early_exit_lower_bound_us": early_bytes / (HBM_PEAK_GBS * 1e9) * 1e6})
+        log(f"linear verify sigma {sigma}: {ms * 1e3:.1f} us, mean L {L.mean():.2f}")
+        del p, q, drafts
+        torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline_hot_path(args, lin, ta, tv, tokens_per_step):

@@ -18,7 +18,7 @@ _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too s
 
 EXPORTS = (
     "uno_abi_version", "uno_status_string", "uno_last_error",
-    "uno_gated_lora_linear_workspace", "uno_gated_lora_linear",
+    "uno_gated_lora_linear_workspace", "uno_gated_lora_linear", "uno_lora_merge",
     "uno_psi_spec_verify_linear_workspace", "uno_psi_spec_verify_linear", "uno_psi_spec_verify_linear_noalloc",
     "uno_tree_verify_attention_workspace", "uno_tree_verify_attention",
     "uno_psi_spec_verify_tree_workspace", "uno_psi_spec_verify_tree",
@@ -40,7 +40,8 @@ class LayerWeights(ctypes.Structure):
     """uno_layer_weights: device pointers of one decoder layer."""
     _fields_ = [("attn_norm", ctypes.c_void_p), ("mlp_norm", ctypes.c_void_p),
                 ("w", ctypes.c_void_p * NUM_PROJ), ("a", ctypes.c_void_p * NUM_PROJ),
-                ("b", ctypes.c_void_p * NUM_PROJ), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p)]
+                ("b", ctypes.c_void_p * NUM_PROJ), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+                ("w_merged", ctypes.c_void_p * NUM_PROJ)]
 
 
 class StepConfig(ctypes.Structure):
@@ -107,6 +108,7 @@ def _declare(lib):
                                              _p, _p, _p, _p, _p, _p, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p,
                                              _p, _sz]),
         "uno_kv_commit": (ctypes.c_int, [_p, _i32, _i32, _p, _p]),
+        "uno_lora_merge": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _f32, _p, _i64]),
         "uno_profile_enable": (None, [ctypes.c_int, ctypes.c_char_p]),
         "uno_profile_reset": (None, []),
         "uno_profile_query": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
@@ -450,9 +452,34 @@ def decoder_layer_workspace(batch, block, ctx, hidden, inter, n_heads, n_kv, r):
     return out.value
 
 
+def lora_merge(w, a, b, lora_scale=1.0, out=None, stream=None):
+    """uno_lora_merge: bf16(w + lora_scale * b @ a) for bf16 w [N][K], a [r][K],
+    b [N][r] (rows may be strided; the last dimension contiguous)."""
+    import torch
+    N, K = w.shape
+    r = a.shape[0]
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.bfloat16, device=w.device)
+    for t in (w, a, b, out):
+        if t.dtype != torch.bfloat16 or t.stride(1) != 1:
+            raise ValueError("bf16 matrices with contiguous rows expected")
+    _check(_lib.uno_lora_merge(_stream(stream), N, K, r, _ptr(w), w.stride(0), _ptr(a), a.stride(0), _ptr(b),
+                               b.stride(0), float(lora_scale), _ptr(out), out.stride(0)))
+    return out
+
+
+def merge_layer(w, lora_scale=1.0, stream=None):
+    """The gate-merged weights of one layer's dict (see layer_weights): adds
+    "m" + p = bf16(w_p + lora_scale * b_p a_p) for every projection p."""
+    for p in PROJ:
+        w["m" + p] = lora_merge(w["w" + p], w["a" + p], w["b" + p], lora_scale, stream=stream)
+    return w
+
+
 def layer_weights(w, k_cache=None, v_cache=None):
     """uno_layer_weights from a dict of device tensors: attn_norm, mlp_norm and
-    w/a/b + one of q k v o g u d (gate, up, down), e.g. "wq", "aq", "bq"."""
+    w/a/b + one of q k v o g u d (gate, up, down), e.g. "wq", "aq", "bq", and
+    optionally the gate-merged "mq", ... (all seven; see merge_layer)."""
     lw = LayerWeights()
     lw.attn_norm = w["attn_norm"].data_ptr()
     lw.mlp_norm = w["mlp_norm"].data_ptr()
@@ -462,6 +489,9 @@ def layer_weights(w, k_cache=None, v_cache=None):
         lw.b[i] = w["b" + p].data_ptr() if ("b" + p) in w else None
     lw.k_cache = k_cache.data_ptr() if k_cache is not None else None
     lw.v_cache = v_cache.data_ptr() if v_cache is not None else None
+    if all(("m" + p) in w for p in PROJ):
+        for i, p in enumerate(PROJ):
+            lw.w_merged[i] = w["m" + p].data_ptr()
     return lw
 
 

@@ -119,6 +119,26 @@ uno_status uno_gated_lora_linear(hipStream_t stream, uno_dtype dtype, int64_t M,
   UNO_GUARD_END
 }
 
+// ------------------------------------------------------------------ LoRA merge
+uno_status uno_lora_merge(hipStream_t stream, int64_t N, int64_t K, int64_t r, const void* W, int64_t ldw,
+                          const void* A, int64_t lda, const void* B, int64_t ldb, float lora_scale, void* out,
+                          int64_t ldo) {
+  UNO_GUARD_BEGIN
+  if (N < 1 || K < 1 || r < 1) return fail(UNO_ERR_INVALID_ARGUMENT, "N, K and r must be >= 1");
+  if (N > 65535) return fail(UNO_ERR_UNSUPPORTED, "N above 65535 (got %lld)", (long long)N);
+  if (K > (int64_t(1) << 30) || r > (int64_t(1) << 20)) return fail(UNO_ERR_UNSUPPORTED, "K or r too large");
+  if (!W || !A || !B || !out) return fail(UNO_ERR_INVALID_ARGUMENT, "W, A, B and out must be non-NULL");
+  if (ldw < K || lda < K || ldb < r || ldo < K)
+    return fail(UNO_ERR_INVALID_ARGUMENT, "leading dimension smaller than the row width");
+  if (!std::isfinite(lora_scale)) return fail(UNO_ERR_INVALID_ARGUMENT, "lora_scale must be finite");
+  if (((reinterpret_cast<uintptr_t>(W) | reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B) |
+        reinterpret_cast<uintptr_t>(out)) & 1u) != 0)
+    return fail(UNO_ERR_INVALID_ARGUMENT, "bf16 matrices must be 2-byte aligned");
+  LoraMergeArgs m{N, K, r, W, ldw, A, lda, B, ldb, lora_scale, out, ldo};
+  return check_hip(launch_lora_merge(m, stream), "uno_lora_merge launch");
+  UNO_GUARD_END
+}
+
 // ------------------------------------------------------------------ linear verify
 static uno_status check_verify_linear_shape(int32_t batch, int32_t k, int32_t vocab) {
   if (batch < 1) return fail(UNO_ERR_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", batch);

@@ -92,6 +92,10 @@ hipError_t launch_decoder_layer(const DecoderLayerArgs& d, hipStream_t stream) {
   void* g = ws + L.g;
   void* u = ws + L.u;
   void* h = d.h;
+  // gate-merged weights (all seven projections) under the structured gate:
+  // the gated rows read w + s b a and no LoRA-down runs
+  bool merged = d.gate && d.r > 0 && d.gate_block > 0;
+  for (int p = 0; p < UNO_NUM_PROJ && merged; ++p) merged = d.w->w_merged[p] != nullptr;
 
   auto proj_args = [&](int p, const void* x, int64_t K, int64_t N, void* y, const uint16_t* t_pre = nullptr,
                        int64_t ldt_pre = 0) {
@@ -116,6 +120,7 @@ hipError_t launch_decoder_layer(const DecoderLayerArgs& d, hipStream_t stream) {
     ga.t_pre = t_pre;
     ga.ldt_pre = ldt_pre;
     ga.gate_block = d.gate_block;
+    ga.w_merged = merged ? d.w->w_merged[p] : nullptr;
     ga.ws = ws + L.lora;
     ga.ws_bytes = d.ws_bytes - L.lora;
     return ga;
@@ -192,8 +197,8 @@ hipError_t launch_decoder_layer(const DecoderLayerArgs& d, hipStream_t stream) {
   };
   uint16_t* tqkv = reinterpret_cast<uint16_t*>(ws + L.tqkv);
   uint16_t* tgu = reinterpret_cast<uint16_t*>(ws + L.tgu);
-  const bool qkv_grouped = packed(UNO_PROJ_Q, 3);
-  const bool gu_grouped = packed(UNO_PROJ_GATE, 2);
+  const bool qkv_grouped = !merged && packed(UNO_PROJ_Q, 3);
+  const bool gu_grouped = !merged && packed(UNO_PROJ_GATE, 2);
   const int64_t r3 = 3 * int64_t(d.r), r2 = 2 * int64_t(d.r);
 
   hipError_t e = d.norm_ready ? hipSuccess : norm(nullptr, d.w->attn_norm, a);
@@ -255,7 +260,12 @@ hipError_t launch_decoder_layer(const DecoderLayerArgs& d, hipStream_t stream) {
   sw.ldt = r2;
   sw.y = g;
   sw.ldy = d.inter;
-  const bool fused = (!lora || gu_grouped) && swiglu_fused_ok(sw);
+  if (merged) {
+    sw.wg_merged = d.w->w_merged[UNO_PROJ_GATE];
+    sw.wu_merged = d.w->w_merged[UNO_PROJ_UP];
+    sw.gate_block = d.gate_block;
+  }
+  const bool fused = (!lora || gu_grouped || merged) && swiglu_fused_ok(sw);
   if (e == hipSuccess && fused) e = launch_gated_lora_swiglu(sw, stream);
   if (e == hipSuccess && !fused) e = proj(UNO_PROJ_GATE, a, d.hidden, d.inter, g, gu_grouped ? tgu : nullptr, r2);
   if (e == hipSuccess && !fused) e = proj(UNO_PROJ_UP, a, d.hidden, d.inter, u, gu_grouped ? tgu + d.r : nullptr, r2);

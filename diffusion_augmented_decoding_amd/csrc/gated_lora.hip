@@ -71,11 +71,31 @@ struct GemmParams {
   int seg_n;
   int64_t t2_off;
   uint16_t* y2;
+  // Gate-merged weights (MODE 0 and 2, FAST, no adapter columns): logical
+  // rows m >= merge_m (the gated rows) read wm / wm2, the copies of w / w2 with
+  // the adapter merged in (W + s B A); rows below merge_m read w / w2.  With
+  // row_blk > 0 the logical rows are gathered: row m < merge_m is physical
+  // row (m / row_blk) * 2 row_blk + m % row_blk (the first row_blk rows of
+  // every 2 row_blk, the clean rows), row merge_m + i is physical row
+  // (i / row_blk) * 2 row_blk + row_blk + i % row_blk (the noisy rows), for
+  // the activations and the output alike.  0: off.
+  int merge_m;
+  int row_blk;
+  const uint16_t* wm;
+  const uint16_t* wm2;
   // LoRA-down (gemm_dl_kernel) only: > 0 gathers the x rows, logical row i
   // reading physical row (i / g) * 2g + g + i % g (the noisy rows of
   // sequences of g clean + g noisy rows); the partials stay in logical rows
   int gather_blk;
 };
+
+// Physical row of logical row m under the gate-merged row order.
+__device__ __forceinline__ int phys_row(const GemmParams& p, int m) {
+  if (p.row_blk <= 0) return m;
+  const bool gated = m >= p.merge_m;
+  const int i = gated ? m - p.merge_m : m;
+  return (i / p.row_blk) * 2 * p.row_blk + (gated ? p.row_blk : 0) + i % p.row_blk;
+}
 
 // Output tile of linear index `tile`.  Mode 1: column-major (M-tiles
 // fastest), so the contiguous band of tiles one XCD runs spans few N-tiles
@@ -164,6 +184,13 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p
   static_assert(MODE >= 0 && MODE <= 2, "modes of the main kernel: bf16 out, partials, SwiGLU");
   const int m0 = tm * BM;
   int n0 = tn * (MODE == 2 ? BN / 2 : BN);   // MODE 2: first feature of the tile
+  if constexpr (FAST && MODE != 1) {
+    // gated rows (tiles never straddle merge_m): the merged weights
+    if (p.merge_m > 0 && m0 >= p.merge_m) {
+      p.w = p.wm;
+      p.w2 = p.wm2;
+    }
+  }
   if constexpr (MODE == 0 && FAST) {
     // two segments (tiles never straddle seg_n): rebase onto the second
     if (p.seg_n > 0) {
@@ -252,7 +279,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p
     const int trow = tid / kChunksPerRow;
     va1 = uint32_t((n0 + trow) * p.ldw * 2) + col;
     va2 = uint32_t((n0 + trow) * p.ldb * 2) + col;
-    vb1 = uint32_t((m0 + trow) * p.ldx * 2) + col;
+    vb1 = uint32_t(phys_row(p, m0 + trow) * p.ldx * 2) + col;
     vb2 = uint32_t((m0 + trow) * p.ldt * 2) + col;
     slot = uint32_t(lds_off(trow, tid % kChunksPerRow));
     kt1 = p.K1 / kBK;
@@ -288,7 +315,9 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p
       dst[i] = __builtin_bit_cast(u32x4, first ? __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0)
                                                : __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
     } else {
-      const int step = first ? RPG * int(p.ldx) * 2 : RPG * int(p.ldt) * 2;
+      // gathered rows: RPG is a multiple of row_blk, so RPG logical rows
+      // further on are 2 RPG physical rows further on
+      const int step = first ? RPG * int(p.ldx) * (p.row_blk > 0 ? 4 : 2) : RPG * int(p.ldt) * 2;
       uint32_t off = (first ? vb1 : vb2) + uint32_t(q * step + ktl * kBK * 2);
       off = live ? off : 0x80000000u;
       dst[i] = __builtin_bit_cast(u32x4, first ? __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0)
@@ -419,7 +448,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p
             const float gv = acc[i][j][4 * g + e], uv = acc[i + FN / 2][j][4 * g + e];
             o[e] = gv / (1.f + expf(-gv)) * uv;
           }
-          uint16_t* dst = p.y + int64_t(m) * p.ldy + n;
+          uint16_t* dst = p.y + int64_t(phys_row(p, m)) * p.ldy + n;
           if (p.y_vec && n + 3 < p.N) {
             *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
           } else {
@@ -444,7 +473,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p
         const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
         const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
         if constexpr (MODE == 0) {
-          uint16_t* dst = p.y + int64_t(m) * p.ldy + n;
+          uint16_t* dst = p.y + int64_t(phys_row(p, m)) * p.ldy + n;
           if (p.y_vec && n + 3 < p.N) {
             *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
           } else {
@@ -774,6 +803,50 @@ __global__ __launch_bounds__(256) void lora_gate4_kernel(const float* __restrict
       make_uint2(pack_bf16x2(scale * s[0], scale * s[1]), pack_bf16x2(scale * s[2], scale * s[3]));
 }
 
+// ------------------------------------------------------------------ merge
+// out[n][k] = bf16(w[n][k] + scale * sum_j b[n][j] a[j][k]): the sum over
+// j = 0 .. r-1 in order with fp32 fused multiply-adds, one rounding at the end.
+// One thread per 8 consecutive k of a row n (grid.y = n); vec: 16-byte loads
+// and stores (every leading dimension a multiple of 8, 16-byte aligned bases).
+__global__ __launch_bounds__(256) void lora_merge_kernel(const uint16_t* __restrict__ w, int64_t ldw,
+                                                         const uint16_t* __restrict__ a, int64_t lda,
+                                                         const uint16_t* __restrict__ b, int64_t ldb, float scale,
+                                                         int K, int r, uint16_t* __restrict__ out, int64_t ldo,
+                                                         int vec) {
+  const int n = blockIdx.y;
+  const int k0 = (blockIdx.x * 256 + threadIdx.x) * 8;
+  if (k0 >= K) return;
+  const int cnt = min(8, K - k0);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const uint16_t* brow = b + int64_t(n) * ldb;
+  for (int j = 0; j < r; ++j) {
+    const float bj = bf16_to_f32(brow[j]);
+    const uint16_t* arow = a + int64_t(j) * lda + k0;
+    if (vec && cnt == 8) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(arow);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = fmaf(bj, bf16_lo(v[e]), acc[2 * e]);
+        acc[2 * e + 1] = fmaf(bj, bf16_hi(v[e]), acc[2 * e + 1]);
+      }
+    } else {
+      for (int e = 0; e < cnt; ++e) acc[e] = fmaf(bj, bf16_to_f32(arow[e]), acc[e]);
+    }
+  }
+  const uint16_t* wrow = w + int64_t(n) * ldw + k0;
+  uint16_t* orow = out + int64_t(n) * ldo + k0;
+  if (vec && cnt == 8) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(wrow);
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = pack_bf16x2(bf16_lo(v[e]) + scale * acc[2 * e], bf16_hi(v[e]) + scale * acc[2 * e + 1]);
+    *reinterpret_cast<u32x4*>(orow) = o;
+  } else {
+    for (int e = 0; e < cnt; ++e) orow[e] = f32_to_bf16(bf16_to_f32(wrow[e]) + scale * acc[e]);
+  }
+}
+
 // ------------------------------------------------------------------ fp32 path
 __global__ __launch_bounds__(256) void lora_down_f32_kernel(const float* __restrict__ x, int64_t ldx,
                                                             const float* __restrict__ a, int64_t lda,
@@ -876,6 +949,10 @@ hipError_t launch_tile_k(GemmParams p, int splits, hipStream_t stream, const cha
 
 template <int BM, int BN, int WM, int WN, int P, int DBF, int MODE>
 hipError_t launch_tile(GemmParams p, int splits, hipStream_t stream, const char* name) {
+  // the gate-merged row order exists on the buffer-load path only
+  if (p.merge_m > 0)
+    return fast_ok(p, BM, BN) ? launch_tile_k<BM, BN, WM, WN, P, DBF, MODE, 1>(p, splits, stream, name)
+                              : hipErrorNotSupported;
   const char* env = tuning_env("UNO_GEMM_FAST");   // tuning override: 0 keeps the masked loads
   if (fast_ok(p, BM, BN) && !(env && atoi(env) == 0))
     return launch_tile_k<BM, BN, WM, WN, P, DBF, MODE, 1>(p, splits, stream, name);
@@ -1155,9 +1232,27 @@ hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t stream) {
 
 namespace {
 
+void set_merged(GemmParams& g, int64_t M, int gate_block, const void* wm, const void* wm2) {
+  g.K2 = 0;
+  g.kr = 0;
+  g.t = g.x;
+  g.ldt = g.ldx;
+  g.b = g.w;
+  g.b2 = g.w2;
+  g.ldb = g.ldw;
+  g.merge_m = int(M / 2);
+  g.row_blk = gate_block;
+  g.wm = static_cast<const uint16_t*>(wm);
+  g.wm2 = static_cast<const uint16_t*>(wm2);
+}
+
+bool swiglu_merged(const SwigluArgs& a) {
+  return a.r > 0 && a.wg_merged && a.wu_merged && merged_rows_ok(a.M, a.gate_block, 256, 512);
+}
+
 GemmParams swiglu_params(const SwigluArgs& a) {
   GemmParams g{};
-  const bool lora = a.r > 0;
+  const bool lora = a.r > 0 && !swiglu_merged(a);
   g.M = int(a.M);
   g.N = int(a.N);
   g.K1 = int(a.K);
@@ -1176,14 +1271,20 @@ GemmParams swiglu_params(const SwigluArgs& a) {
   g.y = static_cast<uint16_t*>(a.y);
   g.ldy = a.ldy;
   g.y_vec = (a.ldy % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.y) & 7u) == 0);
+  if (swiglu_merged(a)) set_merged(g, a.M, a.gate_block, a.wg_merged, a.wu_merged);
   return g;
 }
 
 }  // namespace
 
+bool merged_rows_ok(int64_t M, int gate_block, int bm, int threads) {
+  if (gate_block <= 0 || M % (2 * gate_block) != 0 || (M / 2) % bm != 0) return false;
+  return (threads / kChunksPerRow) % gate_block == 0;
+}
+
 bool swiglu_fused_ok(const SwigluArgs& a) {
   if (a.K % kBK != 0 || a.r % kBK != 0) return false;
-  if (a.r > 0 && (!a.t || a.ldt < 2 * a.r || !a.bg || !a.bu)) return false;
+  if (a.r > 0 && !swiglu_merged(a) && (!a.t || a.ldt < 2 * a.r || !a.bg || !a.bu)) return false;
   return fast_ok(swiglu_params(a), 256, 256);
 }
 
@@ -1195,6 +1296,11 @@ hipError_t launch_gated_lora_swiglu(const SwigluArgs& a, hipStream_t stream) {
 }
 
 namespace {
+
+// Gate-merged launch of one projection (pair: bm = 256 on 8 waves).
+bool lora_merged(const GatedLoraArgs& a, int bm, int threads) {
+  return a.dtype == UNO_BF16 && a.r > 0 && a.gate && a.w_merged && merged_rows_ok(a.M, a.gate_block, bm, threads);
+}
 
 GemmParams lora_params(const GatedLoraArgs& a, const uint16_t* t, int64_t ldt) {
   const bool lora = a.r > 0 && a.gate != nullptr;
@@ -1227,10 +1333,15 @@ bool gated_lora_pair_ok(const GatedLoraArgs& a, const GatedLoraArgs& b) {
   if (a.M != b.M || a.N != b.N || a.K != b.K || a.r != b.r || a.x != b.x || a.ldx != b.ldx || a.ldw != b.ldw ||
       a.ldb != b.ldb || a.ldy != b.ldy || a.ldt_pre != b.ldt_pre || a.gate != b.gate)
     return false;
-  if (la && (!a.t_pre || !b.t_pre)) return false;
+  const bool merged = lora_merged(a, 256, 512) && lora_merged(b, 256, 512) && a.gate_block == b.gate_block;
+  if (la && !merged && (!a.t_pre || !b.t_pre)) return false;
   if (a.M < 2048 || a.N % 128 != 0 || a.N * 2 > 0x7fffffff) return false;
-  const GemmParams ga = lora_params(a, static_cast<const uint16_t*>(a.t_pre), a.ldt_pre);
-  const GemmParams gb = lora_params(b, static_cast<const uint16_t*>(b.t_pre), b.ldt_pre);
+  GemmParams ga = lora_params(a, static_cast<const uint16_t*>(a.t_pre), a.ldt_pre);
+  GemmParams gb = lora_params(b, static_cast<const uint16_t*>(b.t_pre), b.ldt_pre);
+  if (merged) {
+    set_merged(ga, a.M, a.gate_block, a.w_merged, b.w_merged);
+    set_merged(gb, b.M, b.gate_block, b.w_merged, a.w_merged);
+  }
   return fast_ok(ga, 256, 128) && fast_ok(gb, 256, 128) && ga.y_vec && gb.y_vec;
 }
 
@@ -1239,7 +1350,8 @@ bool gated_lora_pair_ok(const GatedLoraArgs& a, const GatedLoraArgs& b) {
 // launches on 128 x 128 tiles.
 hipError_t launch_gated_lora_pair(const GatedLoraArgs& a, const GatedLoraArgs& b, hipStream_t stream) {
   if (!gated_lora_pair_ok(a, b)) return hipErrorNotSupported;
-  const bool lora = a.r > 0 && a.gate;
+  const bool merged = lora_merged(a, 256, 512) && lora_merged(b, 256, 512) && a.gate_block == b.gate_block;
+  const bool lora = a.r > 0 && a.gate && !merged;
   GemmParams g = lora_params(a, static_cast<const uint16_t*>(a.t_pre), a.ldt_pre);
   g.N = int(2 * a.N);
   g.seg_n = int(a.N);
@@ -1247,6 +1359,8 @@ hipError_t launch_gated_lora_pair(const GatedLoraArgs& a, const GatedLoraArgs& b
   g.b2 = lora ? static_cast<const uint16_t*>(b.b) : g.w2;
   g.t2_off = lora ? static_cast<const uint16_t*>(b.t_pre) - static_cast<const uint16_t*>(a.t_pre) : 0;
   g.y2 = static_cast<uint16_t*>(b.y);
+  // merged: k rows read (w, w_merged of k), v rows (after the segment swap) those of v
+  if (merged) set_merged(g, a.M, a.gate_block, a.w_merged, b.w_merged);
   return launch_tile_k<256, 128, 4, 2, 2, 0, 0, 1>(g, 1, stream, "uno_gemm_bf16");
 }
 
@@ -1273,6 +1387,16 @@ hipError_t launch_gated_lora(const GatedLoraArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
 
+  if (lora && a.w_merged && a.gate_block > 0) {
+    // the gated rows against the merged weights: no LoRA-down, no adapter columns
+    const TileCfg c = choose_main_tile(a.M, a.N, a.K);
+    const int threads = kShapes[c.shape].waves * kWave;
+    if (c.splits == 1 && lora_merged(a, kShapes[c.shape].bm, threads)) {
+      GemmParams g = lora_params(a, nullptr, 0);
+      set_merged(g, a.M, a.gate_block, a.w_merged, a.w_merged);
+      if (fast_ok(g, kShapes[c.shape].bm, kShapes[c.shape].bn)) return launch_cfg<0>(c, g, stream, "uno_gemm_bf16");
+    }
+  }
   char* ws = static_cast<char*>(a.ws);
   const uint16_t* t = nullptr;
   int64_t ldt = a.r;
@@ -1326,6 +1450,18 @@ hipError_t launch_gated_lora(const GatedLoraArgs& a, hipStream_t stream) {
   ProfileScope ps("uno_gemm_reduce", stream);
   hipLaunchKernelGGL(gemm_reduce_kernel, dim3(unsigned((quads + 255) / 256)), dim3(256), 0, stream, g.part, c.splits,
                      int(a.M), int(a.N), g.y, g.ldy, g.y_vec);
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_merge(const LoraMergeArgs& m, hipStream_t stream) {
+  const bool vec = m.ldw % 8 == 0 && m.lda % 8 == 0 && m.ldo % 8 == 0 &&
+                   ((reinterpret_cast<uintptr_t>(m.w) | reinterpret_cast<uintptr_t>(m.a) |
+                     reinterpret_cast<uintptr_t>(m.out)) & 15u) == 0;
+  const dim3 grid(unsigned((m.K + 2047) / 2048), unsigned(m.N));
+  ProfileScope ps("uno_lora_merge", stream);
+  hipLaunchKernelGGL(lora_merge_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(m.w), m.ldw,
+                     static_cast<const uint16_t*>(m.a), m.lda, static_cast<const uint16_t*>(m.b), m.ldb, m.scale,
+                     int(m.K), int(m.r), static_cast<uint16_t*>(m.out), m.ldo, vec ? 1 : 0);
   return hipGetLastError();
 }
 

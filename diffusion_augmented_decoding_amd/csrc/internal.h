@@ -111,7 +111,24 @@ struct GatedLoraArgs {
   int gate_block;                       // > 0: the gate is 0 on rows j < gate_block and 1 on the rest of
                                         // every 2 * gate_block rows (as the decode step builds it); the
                                         // LoRA-down then reads only the gated rows (`gate` is not read)
+  const void* w_merged;                 // optional (bf16, with gate_block > 0): w + lora_scale * b a, ld ldw;
+                                        // the gated rows then read it and no LoRA-down runs
 };
+// Gate-merged GEMM rows: M rows of the structured gate (gate_block) split into
+// clean and gated halves of whole bm-row tiles, gathered by load groups of
+// threads / 8 rows.
+bool merged_rows_ok(int64_t M, int gate_block, int bm, int threads);
+
+// out[n][k] = bf16(w[n][k] + scale * sum_j b[n][j] a[j][k]) (bf16 operands)
+struct LoraMergeArgs {
+  int64_t N, K, r;
+  const void* w; int64_t ldw;
+  const void* a; int64_t lda;
+  const void* b; int64_t ldb;
+  float scale;
+  void* out; int64_t ldo;
+};
+hipError_t launch_lora_merge(const LoraMergeArgs& m, hipStream_t stream);
 size_t gated_lora_workspace_bytes(uno_dtype dtype, int64_t M, int64_t N, int64_t K, int64_t r);
 
 // bf16 LoRA-down of n adapter rows: t [M][n] = bf16(s * g[m] * (x A^T)[m]), 0 where g = 0.
@@ -144,8 +161,12 @@ struct SwigluArgs {
   const void* x; int64_t ldx;
   const void* wg; const void* wu; int64_t ldw;     // [N][K] each
   const void* bg; const void* bu; int64_t ldb;     // [N][r] each
-  const void* t; int64_t ldt;                      // [M][2r]; unused when r == 0
+  const void* t; int64_t ldt;                      // [M][2r]; unused when r == 0 or merged
   void* y; int64_t ldy;
+  // optional: gate-merged weights (both), with the structured gate of
+  // gate_block; the gated rows read them and t, bg, bu are not used
+  const void* wg_merged; const void* wu_merged;
+  int gate_block;
 };
 bool swiglu_fused_ok(const SwigluArgs& a);
 hipError_t launch_gated_lora_swiglu(const SwigluArgs& a, hipStream_t stream);

@@ -51,7 +51,7 @@ typedef enum {
 
 typedef enum { UNO_F32 = 0, UNO_BF16 = 1 } uno_dtype;
 
-#define UNO_ABI_VERSION 3
+#define UNO_ABI_VERSION 4
 
 int uno_abi_version(void);
 const char* uno_status_string(uno_status s);
@@ -337,7 +337,29 @@ typedef struct {
   const void* b[UNO_NUM_PROJ];
   void* k_cache;   /* read; written only by calls given a cache_len */
   void* v_cache;
+  /* Optional gate-merged weights, all seven or none: w_merged[p] =
+   * bf16(w[p] + lora_scale * b[p] a[p]) as uno_lora_merge writes it, with the
+   * lora_scale of the call.  Used by uno_psi_spec_step, whose gate is 0 on
+   * every clean row and 1 on every noisy row: there the noisy rows read
+   * w_merged and the clean rows w, and no LoRA-down runs.  Ignored by
+   * uno_decoder_layer (its gate is arbitrary). */
+  const void* w_merged[UNO_NUM_PROJ];
 } uno_layer_weights;
+
+/* Gate-merged weights for uno_layer_weights.w_merged.  Source: Uno summary
+ * (hyper.ai), section 方法 (the gated LoRA: a row with gate 1 adds the
+ * low-rank update to the AR weights, a row with gate 0 keeps them); with a
+ * 0/1 gate, a gated row computes x (W + s B A)^T, the LoRA merge identity.
+ * out[n][k] = bf16(W[n][k] + lora_scale * sum_j B[n][j] A[j][k]), the sum
+ * over j = 0..r-1 in order with fp32 fused multiply-adds and one rounding at
+ * the end.  bf16 only: W [N][K] (ld ldw), A [r][K] (ld lda), B [N][r] (ld
+ * ldb), out [N][K] (ld ldo), device memory, out aliasing none of the inputs.
+ * 1 <= N <= 65535, K >= 1, r >= 1.  A one-time set-up call (weights load);
+ * every leading dimension a multiple of 8 with 16-byte aligned W, A and out
+ * takes the vector path. */
+uno_status uno_lora_merge(hipStream_t stream, int64_t N, int64_t K, int64_t r, const void* W, int64_t ldw,
+                          const void* A, int64_t lda, const void* B, int64_t ldb, float lora_scale, void* out,
+                          int64_t ldo);
 
 uno_status uno_decoder_layer_workspace(int32_t batch, int32_t block, int32_t ctx_len, int32_t hidden,
                                        int32_t inter, int32_t n_heads, int32_t n_kv_heads, int32_t r,

@@ -20,7 +20,7 @@ pages are silent.  Pins that tie these functions to something other than
 themselves live in `tests/test_oracle_*.py`.
 """
 
-from .gated_lora import gated_lora_linear
+from .gated_lora import gated_lora_linear, merged_weight
 from .verify_linear import (
     softmax_rows,
     row_log_stats,
@@ -46,6 +46,7 @@ from .kv_commit import kv_commit
 
 __all__ = [
     "gated_lora_linear",
+    "merged_weight",
     "softmax_rows",
     "row_log_stats",
     "accept_draft",

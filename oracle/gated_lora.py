@@ -11,6 +11,10 @@ Computed here (float64, no intermediate rounding):
 
     Y = X W^T + s * diag(g) (X A^T) B^T
 
+With a 0/1 gate, a row with g = 1 computes X (W + s B A)^T, the LoRA merge
+identity; merged_weight() writes that matrix out, the weight the GPU reads
+for the gated rows when it is given gate-merged weights.
+
 Readings where the pages are silent:
 * no bias term;
 * the LoRA scale alpha/r is folded into B, so s = 1 by default;
@@ -40,3 +44,11 @@ def gated_lora_linear(x, w, a, b, gate=None, lora_scale=1.0):
     down = x @ a.T                      # LoRA down-projection, [M, r]
     gated = down * g[:, None]           # adapter on only where g = 1
     return base + lora_scale * (gated @ b.T)
+
+
+def merged_weight(w, a, b, lora_scale=1.0):
+    """W + s * B A in float64 ([N, K]): the weight a gated (g = 1) row sees."""
+    w = np.asarray(w, dtype=np.float64)
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return w + lora_scale * (b @ a)

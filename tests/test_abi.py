@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.uno_abi_version() == 3
+    assert lib.uno_abi_version() == 4
     for s in range(6):
         assert lib.uno_status_string(s)
     assert lib.uno_status_string(99) == b"unknown status"
@@ -363,3 +363,23 @@ def test_verify_linear_noalloc_rejects_bad_calls(lib):
     big = dict(batch=8192, k=64, vocab=151936, ps=65 * 151936, pr=151936, qs=64 * 151936, qr=151936)
     assert call(**big) == UNSUPPORTED
     assert b"16777216" in lib.uno_last_error()
+
+
+def _merge(lib, **kw):
+    a = dict(stream=None, N=16, K=16, r=8, W=FAKE16, ldw=16, A=FAKE16, lda=16, B=FAKE16, ldb=8, scale=1.0,
+             out=FAKE16, ldo=16)
+    a.update(kw)
+    return lib.uno_lora_merge(a["stream"], a["N"], a["K"], a["r"], a["W"], a["ldw"], a["A"], a["lda"], a["B"],
+                              a["ldb"], a["scale"], a["out"], a["ldo"])
+
+
+def test_lora_merge_rejects_bad_calls(lib):
+    assert _merge(lib, N=0) == INVALID
+    assert _merge(lib, r=0) == INVALID
+    assert _merge(lib, W=None) == INVALID
+    assert _merge(lib, out=None) == INVALID
+    assert _merge(lib, ldw=8) == INVALID                 # leading dimension below K
+    assert _merge(lib, ldb=4) == INVALID                 # below r
+    assert _merge(lib, scale=float("inf")) == INVALID
+    assert _merge(lib, N=70000) == UNSUPPORTED
+    assert _merge(lib, out=ctypes.c_void_p(0x10001)) == INVALID   # not 2-byte aligned

@@ -283,8 +283,10 @@ def test_decoder_layer_full_size_decode_loop_sampled(gpu_lib, lc):
         assert np.array_equal(vbits[b, keep], c["v_cache"][b, keep]), f"seq {b}: v rows outside the append"
 
 
-def test_step_full_size_decode_loop_packed_adapters(gpu_lib):
-    """The launch configuration the bench times, with one layer: 128 sequences
+@pytest.mark.parametrize("merged", [False, True])
+def test_step_full_size_decode_loop_packed_adapters(gpu_lib, merged):
+    """The launch configuration the bench times (merged: with gate-merged
+    weights, as the bench runs it), with one layer: 128 sequences
     x (16 clean + 16 noisy) rows, caches of 8192 + 16 rows with 8192 valid
     (one sequence shorter), rank-128 adapters of q/k/v and gate/up stored back
     to back (grouped LoRA-down over the noisy rows only), V = 151,936, a
@@ -293,7 +295,8 @@ def test_step_full_size_decode_loop_packed_adapters(gpu_lib):
     the bar, committed lengths exact, committed rows within the bar."""
     import torch
     batch, block, cap, hidden, inter, nh, nkv, r, vocab = 128, 16, 8192 + 16, 4096, 12288, 32, 8, 128, 151936
-    say(f"step decode loop full size, 1 layer, packed adapters: B={batch} block={block} cap={cap} V={vocab}")
+    say(f"step decode loop full size, 1 layer, packed adapters: B={batch} block={block} cap={cap} V={vocab} "
+        f"merged={merged}")
     c = workloads.step_case(batch, block, cap, hidden, inter, nh, nkv, r, 1, vocab, seed=17)
     lens = np.full(batch, 8192)
     lens[40] = 5000
@@ -304,6 +307,8 @@ def test_step_full_size_decode_loop_packed_adapters(gpu_lib):
         cat = torch.cat([wt["a" + p] for p in group], dim=0).contiguous()
         for i, p in enumerate(group):
             wt["a" + p] = cat[i * r:(i + 1) * r]
+    if merged:
+        gpu_lib.merge_layer(wt)
     kc, vc = to_dev(c["k_caches"][0]), to_dev(c["v_caches"][0])
     cfg = gpu_lib.step_config(batch, block, cap, hidden, inter, nh, nkv, r, 1, vocab)
     cl = to_dev(lens.astype(np.int32))

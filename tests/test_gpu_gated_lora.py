@@ -130,3 +130,34 @@ def test_grouped_adapter_ranks_at_decode_rows(gpu_lib, m, k, r):
     say(f"  row rel err {err:.3g}")
     assert err <= 2e-2
     assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("n,k,r,scale", [
+    (300, 1001, 8, 0.5),      # odd K: the element-wise path
+    (256, 4096, 128, 1.0),    # a projection's shape class: 16-byte path
+    (64, 12288, 128, 1.0),    # the down projection's K
+])
+def test_lora_merge_matches_oracle(gpu_lib, n, k, r, scale):
+    """uno_lora_merge against oracle.merged_weight (W + s B A in float64) on the
+    same bf16 operands: the bf16 result equals the round-to-nearest-even of the
+    exact value except where the fp32 sum lands on the other side of a rounding
+    tie, and is within one bf16 step of it everywhere."""
+    import torch
+    say(f"lora merge N={n} K={k} r={r} s={scale}")
+    c = workloads.gated_lora_case(4, n, k, r, dtype="bf16", seed=n + k, weight_std=0.05)
+    out = gpu_lib.lora_merge(to_dev(c["w"]), to_dev(c["a"]), to_dev(c["b"]), scale)
+    torch.cuda.synchronize()
+    got = to_host(out).astype(np.float64)          # bf16 values, widened exactly
+    ref = oracle.merged_weight(c["w_f32"], c["a_f32"], c["b_f32"], scale)
+    exact = workloads.bf16_to_f32(workloads.bf16_bits(ref)).astype(np.float64)
+    # one bf16 step of the result, plus the fp32 rounding of the r products,
+    # their sum and the final add (bounded through the operand magnitudes; it
+    # dominates only where W and s B A nearly cancel)
+    mag = np.abs(c["w_f32"]).astype(np.float64) + abs(scale) * (np.abs(c["b_f32"]) @ np.abs(c["a_f32"]))
+    bound = np.abs(exact) * 2.0 ** -7 + mag * (r + 2) * 2.0 ** -24
+    excess = np.abs(got - exact) - bound
+    say(f"  worst excess over the bound {excess.max():.3g}")
+    assert np.all(excess <= 0)
+    frac = np.mean(got == exact)
+    say(f"  equal to the rounded exact value: {frac:.6f}")
+    assert frac >= 0.999

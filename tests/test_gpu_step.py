@@ -14,6 +14,9 @@ oracle.decode_step.
 * The full-size step (two Qwen3-8B-shaped layers, 128 sequences, V =
   151,936) is run twice on the same inputs and must give bitwise identical
   results.
+* "merged": the layers also carry gate-merged weights (uno_lora_merge), so
+  the noisy rows read W + B A and no LoRA-down runs; the same bars hold
+  against the same (unmerged) oracle.
 """
 
 import numpy as np
@@ -30,21 +33,23 @@ def _f64(bits):
     return workloads.bf16_to_f32(bits).astype(np.float64)
 
 
-def _layers(dad, c):
+def _layers(dad, c, merged=False):
     keep, layers = [], []
     for l in range(c["n_layers"]):
         wt = {k: to_dev(v) for k, v in c["layers"][l].items() if not k.endswith("_f32")}
+        if merged:
+            dad.merge_layer(wt)
         kc, vc = to_dev(c["k_caches"][l]), to_dev(c["v_caches"][l])
         keep += [wt, kc, vc]
         layers.append(dad.layer_weights(wt, kc, vc))
     return keep, layers
 
 
-def _run_step(dad, c, prev_q=None, temperature=1.0, cache_len=None):
+def _run_step(dad, c, prev_q=None, temperature=1.0, cache_len=None, merged=False):
     import torch
     cfg = dad.step_config(c["batch"], c["block"], c["ctx"], c["hidden"], c["inter"], c["n_heads"],
                           c["n_kv_heads"], c["r"], c["n_layers"], c["vocab"], temperature=temperature)
-    keep, layers = _layers(dad, c)
+    keep, layers = _layers(dad, c, merged)
     pq = None if prev_q is None else to_dev(prev_q)
     out = dad.psi_spec_step(cfg, layers, to_dev(c["embed"]), to_dev(c["final_norm"]), to_dev(c["lm_head"]),
                             to_dev(c["tokens"]), to_dev(c["u_draft"]), to_dev(c["u_accept"]), to_dev(c["u_sample"]),
@@ -157,16 +162,20 @@ def test_step_zero_layers_capacity_flags(gpu_lib):
     say(f"  L {g['accept_len'].tolist()}, lengths {lens.tolist()} -> {new.tolist()}")
 
 
-@pytest.mark.parametrize("batch,block,ctx,hidden,inter,nh,nkv,r,n_layers,vocab", [
-    (2, 4, 40, 256, 512, 4, 2, 16, 2, 1000),
-    (3, 16, 130, 512, 1024, 8, 2, 32, 3, 4096),
+@pytest.mark.parametrize("batch,block,ctx,hidden,inter,nh,nkv,r,n_layers,vocab,merged", [
+    (2, 4, 40, 256, 512, 4, 2, 16, 2, 1000, False),
+    (3, 16, 130, 512, 1024, 8, 2, 32, 3, 4096, False),
+    # 512 rows: 256 clean + 256 noisy, whole tiles on both sides of the split,
+    # so q, k, v, o and the fused gate/up run gate-merged (down splits K and
+    # takes the LoRA-down path)
+    (16, 16, 70, 512, 1024, 4, 2, 64, 2, 2048, True),
 ])
-def test_step_with_layers(gpu_lib, batch, block, ctx, hidden, inter, nh, nkv, r, n_layers, vocab):
-    say(f"step: B={batch} block={block} ctx={ctx} hidden={hidden} layers={n_layers} V={vocab}")
+def test_step_with_layers(gpu_lib, batch, block, ctx, hidden, inter, nh, nkv, r, n_layers, vocab, merged):
+    say(f"step: B={batch} block={block} ctx={ctx} hidden={hidden} layers={n_layers} V={vocab} merged={merged}")
     c = workloads.step_case(batch, block, ctx, hidden, inter, nh, nkv, r, n_layers, vocab, seed=ctx,
                             weight_std=0.05)
     prev_q = _random_prev_q(c, ctx)
-    g = _run_step(gpu_lib, c, prev_q)
+    g = _run_step(gpu_lib, c, prev_q, merged=merged)
     o = _oracle(c, list(range(batch)), prev_q)
     err = row_relerr(g["logits"], o["logits"])
     dties, ties = check_step_decisions(g["logits"], block, c["tokens"], _f64(prev_q), g, c["u_draft"],
@@ -177,7 +186,8 @@ def test_step_with_layers(gpu_lib, batch, block, ctx, hidden, inter, nh, nkv, r,
     assert ties <= 1 and dties <= 1
 
 
-def test_step_full_size_two_layers_decisions_and_determinism(gpu_lib):
+@pytest.mark.parametrize("merged", [False, True])
+def test_step_full_size_two_layers_decisions_and_determinism(gpu_lib, merged):
     """The decode-step shape with two Qwen3-8B-shaped layers: 128 sequences x
     (16 clean + 16 noisy) rows, 8K cache, rank-128 adapters, vocab 151,936.
     Every launch has the configuration of the 36-layer step.  The oracle
@@ -186,11 +196,11 @@ def test_step_full_size_two_layers_decisions_and_determinism(gpu_lib):
     on the GPU's own logits; a second run on the same inputs is bitwise
     identical (fixed-order split reductions everywhere)."""
     import torch
-    say("step full size, 2 layers: B=128 block=16 ctx=8192 V=151936")
+    say(f"step full size, 2 layers: B=128 block=16 ctx=8192 V=151936 merged={merged}")
     c = workloads.step_case(128, 16, 8192, 4096, 12288, 32, 8, 128, 2, 151936, seed=11)
     prev_q = _random_prev_q(c, 11)
     cfg = gpu_lib.step_config(128, 16, 8192, 4096, 12288, 32, 8, 128, 2, 151936)
-    keep, layers = _layers(gpu_lib, c)
+    keep, layers = _layers(gpu_lib, c, merged)
     args = [to_dev(c[k]) for k in ("embed", "final_norm", "lm_head", "tokens", "u_draft", "u_accept", "u_sample")]
     pq = to_dev(prev_q)
     runs = []

@@ -63,6 +63,24 @@ def test_gate_on_is_merged_weight():
     np.testing.assert_allclose(y1, ref, rtol=1e-11, atol=1e-12)
 
 
+def test_merged_weight_bruteforce_and_gate_on_rows():
+    """merged_weight against an element-by-element fsum of W + s sum_j B A, and
+    a gated row of gated_lora_linear equals that row times the merged weight."""
+    c = workloads.gated_lora_case(5, 9, 11, 4, dtype="f32", seed=8)
+    x, w, a, b = (c[k].astype(np.float64) for k in ("x_f32", "w_f32", "a_f32", "b_f32"))
+    s = 0.75
+    m = oracle.merged_weight(w, a, b, s)
+    brute = np.array([[math.fsum([w[n, k]] + [s * b[n, j] * a[j, k] for j in range(4)]) for k in range(11)]
+                      for n in range(9)])
+    np.testing.assert_allclose(m, brute, rtol=1e-13, atol=1e-14)
+    g = np.array([1, 0, 1, 1, 0], np.uint8)
+    y = oracle.gated_lora_linear(x, w, a, b, g, lora_scale=s)
+    on = np.array([[math.fsum(x[i] * m[o]) for o in range(9)] for i in range(5)])
+    off = np.array([[math.fsum(x[i] * w[o]) for o in range(9)] for i in range(5)])
+    np.testing.assert_allclose(y[g == 1], on[g == 1], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(y[g == 0], off[g == 0], rtol=1e-11, atol=1e-12)
+
+
 def test_rows_gated_independently_and_low_rank():
     c = workloads.gated_lora_case(32, 64, 48, 4, dtype="f32", seed=9)
     x, w, a, b = c["x_f32"], c["w_f32"], c["a_f32"], c["b_f32"]
