@@ -108,6 +108,7 @@ def main():
             out["components"]["linear_verify_256x16"] = comp["components"]["linear_verify"]
             out["components"]["tree_batch1"] = comp["components"]["tree"]
             out["components"]["linear_verify_sigma_sweep"] = bench_linear_sigma_sweep(args, dad, torch)
+            out["components"]["tree_batch1_graph"] = bench_tree_graph(args, dad, torch)
     else:
         out = bench_hot_path(args, dad, torch, steps=args.steps, warmup=args.warmup,
                              with_cpu=not args.no_cpu_baseline)
@@ -652,6 +653,114 @@ def bench_linear_sigma_sweep(args, dad, torch, sigmas=(0.1, 0.5, 2.0), reps=20):
         del p, q, drafts
         torch.cuda.empty_cache()
     return res
+
+
+def bench_tree_graph(args, dad, torch, copies=64, distinct=4, replays=5):
+    """The batch-1 tree path (tree attention over a 1024-row cache + tree
+    verify of a 65-node tree, V = 151,936), `copies` trees per replay, each on
+    its own copy of the inputs (so no replay finds a tree's rows in cache),
+    captured once as a HIP graph and replayed: per-tree time without host
+    launch gaps.  `distinct` seeded trees fill the copies in turn.  Bytes per
+    tree: the cache's K and V, the tree's q, k, v and output, and every logit
+    row of the verify read once."""
+    import numpy as np
+    import workloads
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16 else torch.from_numpy(a)
+        return t.to(dev)
+
+    parent = workloads.tree_parent_cfg(args.seed)
+    maxc = workloads.max_children(parent)
+    cases = []
+    for s in range(distinct):
+        ta = workloads.tree_attention_case(1, parent, 1024, 32, 8, 128, seed=args.seed + 100 + s)
+        tv = workloads.tree_verify_case(parent, VOCAB, dtype="bf16", seed=args.seed + 100 + s)
+        cases.append((ta, tv))
+    n, dmax = cases[0][1]["n"], cases[0][1]["max_depth"]
+    ws_a = torch.empty(max(1, dad.tree_verify_attention_workspace(1, n, 1024, 32, 8, 128)), dtype=torch.uint8,
+                       device=dev)
+    ws_v = torch.empty(dad.psi_spec_verify_tree_workspace(1, n, dmax, maxc, VOCAB), dtype=torch.uint8, device=dev)
+    inst = []
+    for i in range(copies):
+        ta, tv = cases[i % distinct]
+        e = {k: up(ta[k]) for k in ("q", "k_cache", "v_cache", "k_tree", "v_tree")}
+        e["parent"] = up(ta["parent"].astype(np.int32))
+        e.update({"v_" + k: up(tv[k]) for k in ("parent", "tokens", "p", "q", "u_acc", "u_s")})
+        e["scale"] = ta["scale"]
+        e["out"] = torch.empty_like(e["q"])
+        e["lse"] = torch.empty((1, n, 32), dtype=torch.float32, device=dev)
+        e["res"] = {"accept_len": torch.empty(1, dtype=torch.int32, device=dev),
+                    "path": torch.empty((1, dmax), dtype=torch.int32, device=dev),
+                    "token": torch.empty(1, dtype=torch.int32, device=dev)}
+        inst.append(e)
+
+    def run_all():
+        for e in inst:
+            dad.tree_verify_attention(e["q"], e["k_cache"], e["v_cache"], e["k_tree"], e["v_tree"], e["parent"],
+                                      e["scale"], out=e["out"], lse=e["lse"], workspace=ws_a)
+            dad.psi_spec_verify_tree(e["v_parent"], e["v_tokens"], e["v_p"], e["v_q"], e["v_u_acc"], e["v_u_s"],
+                                     max_children=maxc, outputs=e["res"], workspace=ws_v)
+
+    run_all()
+    torch.cuda.synchronize()
+    # launches of one tree (every library launch is bracketed when profiling is on)
+    dad.profile_reset()
+    dad.profile_enable(True)
+    e0 = inst[0]
+    dad.tree_verify_attention(e0["q"], e0["k_cache"], e0["v_cache"], e0["k_tree"], e0["v_tree"], e0["parent"],
+                              e0["scale"], out=e0["out"], lse=e0["lse"], workspace=ws_a)
+    dad.psi_spec_verify_tree(e0["v_parent"], e0["v_tokens"], e0["v_p"], e0["v_q"], e0["v_u_acc"], e0["v_u_s"],
+                             max_children=maxc, outputs=e0["res"], workspace=ws_v)
+    torch.cuda.synchronize()
+    launches = int(dad.profile_query("uno_")[1])
+    dad.profile_enable(False)
+    dad.profile_reset()
+    eager = [(int(e["res"]["accept_len"][0]), int(e["res"]["token"][0])) for e in inst[:distinct]]
+    eager_out = inst[0]["out"].clone()
+    timing = "hip_graph"
+    g = None
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run_all()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run_all()
+        torch.cuda.synchronize()
+    except Exception as exc:   # the runtime cannot capture one of the launches
+        log(f"tree path: graph capture unavailable ({exc}); timing stream launches")
+        g = None
+        timing = "stream"
+        torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    checks_ok = True
+    times = []
+    for r in range(replays):
+        for e in inst[:distinct]:
+            e["res"]["accept_len"].fill_(-7)
+        torch.cuda.synchronize()
+        start.record()
+        if g is not None:
+            g.replay()
+        else:
+            run_all()
+        stop.record()
+        torch.cuda.synchronize()
+        times.append(start.elapsed_time(stop))
+        got = [(int(e["res"]["accept_len"][0]), int(e["res"]["token"][0])) for e in inst[:distinct]]
+        checks_ok &= got == eager and bool(torch.equal(inst[0]["out"].view(torch.int16), eager_out.view(torch.int16)))
+    per_tree_us = float(np.median(times)) * 1e3 / copies
+    attn_bytes = 2.0 * 1024 * 8 * 128 * 2 + n * (32 + 2 * 8 + 32) * 128 * 2
+    verify_bytes = float(n + dmax) * VOCAB * 2
+    return {"timing": timing, "copies": copies, "replays": replays, "us_per_tree": per_tree_us,
+            "gbs": (attn_bytes + verify_bytes) / (per_tree_us * 1e-6) / 1e9, "bytes_per_tree": attn_bytes + verify_bytes,
+            "replays_match_eager": bool(checks_ok), "launches_per_tree": launches}
 
 
 def cpu_baseline_hot_path(args, lin, ta, tv, tokens_per_step):

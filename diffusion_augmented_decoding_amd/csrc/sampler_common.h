@@ -29,21 +29,31 @@ template <> __device__ __forceinline__ float load_logit<uint16_t>(const uint16_t
 }
 template <> __device__ __forceinline__ float load_logit<float>(const float* p, int64_t i) { return p[i]; }
 
+// 16-byte row load: non-temporal (a row streamed once) or cached (a row the
+// caller reads again soon, e.g. the tree verify's rounds).
+template <bool NT, typename V>
+__device__ __forceinline__ V row_load(const V* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
+}
+
 // Loads 8 consecutive logits starting at e0 (bounds- and alignment-safe;
 // elements past `vocab` come back as 0 and must be masked by the caller).
-template <typename T>
+template <typename T, bool NT = true>
 __device__ __forceinline__ void load8(const T* row, int e0, int vocab, bool vec_ok, float (&x)[8]) {
   if (vec_ok && e0 + 8 <= vocab) {
     if constexpr (sizeof(T) == 2) {
-      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + e0));
+      const u32x4 v = row_load<NT>(reinterpret_cast<const u32x4*>(row + e0));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         x[2 * j] = bf16_lo(v[j]);
         x[2 * j + 1] = bf16_hi(v[j]);
       }
     } else {
-      const f32x4 v0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + e0));
-      const f32x4 v1 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + e0 + 4));
+      const f32x4 v0 = row_load<NT>(reinterpret_cast<const f32x4*>(row + e0));
+      const f32x4 v1 = row_load<NT>(reinterpret_cast<const f32x4*>(row + e0 + 4));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         x[j] = v0[j];
@@ -90,7 +100,7 @@ __host__ __device__ inline int split_span(int vocab, int nsplit) { return ((voca
 // a kChunkThreads block, returned in thread 0.  Lanes read consecutive
 // 16-byte vectors (coalesced); 4 vectors in flight per thread; one rescale
 // per 4 vectors.  `lo` is a multiple of 8.
-template <typename T>
+template <typename T, bool NT = true>
 __device__ float2 range_stats(const T* row, int lo, int hi, float sl2) {
   constexpr int VN = 16 / sizeof(T);
   constexpr int U = 4;
@@ -106,14 +116,14 @@ __device__ float2 range_stats(const T* row, int lo, int hi, float sl2) {
       for (int u = 0; u < U; ++u) {
         const T* ptr = base + int64_t(i + u * kChunkThreads) * VN;
         if constexpr (sizeof(T) == 2) {
-          const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
+          const u32x4 v = row_load<NT>(reinterpret_cast<const u32x4*>(ptr));
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             x[u * VN + 2 * j] = bf16_lo(v[j]);
             x[u * VN + 2 * j + 1] = bf16_hi(v[j]);
           }
         } else {
-          const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ptr));
+          const f32x4 v = row_load<NT>(reinterpret_cast<const f32x4*>(ptr));
 #pragma unroll
           for (int j = 0; j < 4; ++j) x[u * VN + j] = v[j];
         }
@@ -124,14 +134,14 @@ __device__ float2 range_stats(const T* row, int lo, int hi, float sl2) {
       float x[VN];
       const T* ptr = base + int64_t(i) * VN;
       if constexpr (sizeof(T) == 2) {
-        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
+        const u32x4 v = row_load<NT>(reinterpret_cast<const u32x4*>(ptr));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           x[2 * j] = bf16_lo(v[j]);
           x[2 * j + 1] = bf16_hi(v[j]);
         }
       } else {
-        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ptr));
+        const f32x4 v = row_load<NT>(reinterpret_cast<const f32x4*>(ptr));
 #pragma unroll
         for (int j = 0; j < 4; ++j) x[j] = v[j];
       }
@@ -185,6 +195,29 @@ __device__ __forceinline__ RowStat wave_merge_chunks(const float2* part, int nch
   return r;
 }
 
+// Two rows' merges at once (all loads in flight together); each result is
+// that of wave_merge_chunks on its row.
+__device__ __forceinline__ void wave_merge_two(const float2* part_a, const float2* part_b, int nchunk,
+                                               RowStat (&out)[2]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float ma = -INFINITY, sa = 0.f, mb = -INFINITY, sb = 0.f;
+  for (int c = lane; c < nchunk; c += kWave) {
+    const float2 va = part_a[c], vb = part_b[c];
+    lse2_merge(ma, sa, va.x, va.y);
+    lse2_merge(mb, sb, vb.x, vb.y);
+  }
+  wave_lse2(ma, sa);
+  wave_lse2(mb, sb);
+  out[0].m = ma;
+  out[0].s = sa;
+  out[0].yd = 0.f;
+  out[0].pad = 0.f;
+  out[1].m = mb;
+  out[1].s = sb;
+  out[1].yd = 0.f;
+  out[1].pad = 0.f;
+}
+
 // Sum of n values by one whole wave (same bits in every lane).
 __device__ __forceinline__ float wave_sum_range(const float* v, int n) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -203,13 +236,13 @@ struct DrawDesc {
 };
 
 // w of 8 elements (and p alone, for the fallback when w has no mass).
-template <typename T>
+template <typename T, bool NT = true>
 __device__ __forceinline__ void weights8(const DrawDesc& d, int e0, int vocab, float sl2, bool vp, bool vq,
                                          float (&w)[8], float (&pw)[8]) {
   float xp[8];
-  load8<T>(static_cast<const T*>(d.prow), e0, vocab, vp, xp);
+  load8<T, NT>(static_cast<const T*>(d.prow), e0, vocab, vp, xp);
   float xq[8];
-  if (d.c != 0.f) load8<T>(static_cast<const T*>(d.qrow), e0, vocab, vq, xq);
+  if (d.c != 0.f) load8<T, NT>(static_cast<const T*>(d.qrow), e0, vocab, vq, xq);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const bool in = e0 + j < vocab;
@@ -224,13 +257,11 @@ __device__ __forceinline__ void weights8(const DrawDesc& d, int e0, int vocab, f
   }
 }
 
-// Segment masses of one chunk: seg[(b * nchunk + c) * 2*kSegPerChunk + k] for
-// the 16 segments of w, then the 16 of p.  Grid (nchunk, batch), 256 threads.
+// Segment masses of chunk c of draw b: seg[(b * nchunk + c) * 2*kSegPerChunk + k]
+// for the 16 segments of w, then the 16 of p.  A block of kChunkThreads threads.
 template <typename T>
-__global__ __launch_bounds__(kChunkThreads) void draw_seg_kernel(const DrawDesc* __restrict__ desc, int vocab,
-                                                                 float sl2, float* __restrict__ seg) {
-  const int b = blockIdx.x, c = blockIdx.y;
-  const int nchunk = gridDim.y;
+__device__ __forceinline__ void draw_seg_body(const DrawDesc* __restrict__ desc, int vocab, float sl2,
+                                              float* __restrict__ seg, int b, int c, int nchunk) {
   const DrawDesc d = desc[b];
   if (!d.active) return;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
@@ -263,17 +294,24 @@ __global__ __launch_bounds__(kChunkThreads) void draw_seg_kernel(const DrawDesc*
   }
 }
 
+// Grid (batch, nchunk), 256 threads.
+template <typename T>
+__global__ __launch_bounds__(kChunkThreads) void draw_seg_kernel(const DrawDesc* __restrict__ desc, int vocab,
+                                                                 float sl2, float* __restrict__ seg) {
+  draw_seg_body<T>(desc, vocab, sl2, seg, blockIdx.x, blockIdx.y, gridDim.y);
+}
+
 // Resolve the inverse CDF for one batch element (one wave): S = sum of the
 // segment masses in token order, target = u * S, the segment holding it, then
 // the element within the segment (re-reads 512 elements).  Falls back to p
-// when w has no mass.  y = -1 when the descriptor is inactive.
+// when w has no mass.  y = -1 when the descriptor is inactive.  Called by
+// one whole wave (the first of its block).
 template <typename T>
-__global__ __launch_bounds__(kWave) void draw_resolve_kernel(const DrawDesc* __restrict__ desc, int vocab,
-                                                             float sl2, const float* __restrict__ seg,
-                                                             const float* __restrict__ u_s,
-                                                             int32_t* __restrict__ out_tok,
-                                                             float* __restrict__ out_mass) {
-  const int b = blockIdx.x, lane = threadIdx.x;
+__device__ __forceinline__ void draw_resolve_body(const DrawDesc* __restrict__ desc, int vocab, float sl2,
+                                                  const float* __restrict__ seg, const float* __restrict__ u_s,
+                                                  int32_t* __restrict__ out_tok, float* __restrict__ out_mass,
+                                                  int b) {
+  const int lane = threadIdx.x & (kWave - 1);
   DrawDesc d = desc[b];
   if (!d.active) {
     if (lane == 0) {
@@ -380,6 +418,15 @@ __global__ __launch_bounds__(kWave) void draw_resolve_kernel(const DrawDesc* __r
     out_tok[b] = y;
     if (out_mass) out_mass[b] = S;
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kWave) void draw_resolve_kernel(const DrawDesc* __restrict__ desc, int vocab,
+                                                             float sl2, const float* __restrict__ seg,
+                                                             const float* __restrict__ u_s,
+                                                             int32_t* __restrict__ out_tok,
+                                                             float* __restrict__ out_mass) {
+  draw_resolve_body<T>(desc, vocab, sl2, seg, u_s, out_tok, out_mass, blockIdx.x);
 }
 
 // Launch the two draw kernels for `batch` descriptors.
