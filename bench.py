@@ -493,8 +493,8 @@ def bench_hot_path(args, dad, torch, steps, warmup, with_cpu):
         step()
     torch.cuda.synchronize()
     kernels = ["uno_gemm_bf16", "uno_gemm_reduce", "uno_lora_down_bf16", "uno_lora_gate", "uno_row_stats",
-               "uno_accept", "uno_draw_seg", "uno_draw_resolve", "uno_tree_attention", "uno_tree_setup",
-               "uno_tree_stats", "uno_tree_round", "uno_tree_walk", "uno_tree_draw"]
+               "uno_accept", "uno_draw_seg", "uno_draw_resolve", "uno_tree_attention", "uno_tree_stats",
+               "uno_tree_flow"]
     breakdown = {}
     for kname in kernels:
         ms, cnt = dad.profile_query(kname)
@@ -562,8 +562,7 @@ def bench_hot_path(args, dad, torch, steps, warmup, with_cpu):
                           "mean_accept_len": float(np.mean(L)), "tokens": int(np.sum(L + 1)),
                           "verified_tokens_per_s": int(np.sum(L + 1)) / (sampler_ms * 1e-3)},
         "tree": {"attention_us": breakdown["uno_tree_attention"] * 1e3,
-                 "verify_us": (breakdown["uno_tree_setup"] + breakdown["uno_tree_stats"] + breakdown["uno_tree_round"]
-                               + breakdown["uno_tree_walk"] + breakdown["uno_tree_draw"]) * 1e3, "accept_len": tl},
+                 "verify_us": (breakdown["uno_tree_stats"] + breakdown["uno_tree_flow"]) * 1e3, "accept_len": tl},
         "kernel_ms_per_step": breakdown,
     }
     cpu = cpu_baseline_hot_path(args, lin, ta, tv, tokens_per_step) if with_cpu else None

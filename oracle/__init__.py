@@ -29,6 +29,7 @@ from .verify_linear import (
     inverse_cdf,
     verify_linear,
 )
+from .sampling import kth_largest, top_k_mask, top_p_mask, transform_probs
 from .tree_attention import ancestors_or_self, tree_attention, tree_attention_dense_mask
 from .verify_tree import node_depths, children_lists, verify_tree
 from .decoder import (
@@ -53,6 +54,10 @@ __all__ = [
     "residual_weights",
     "inverse_cdf",
     "verify_linear",
+    "kth_largest",
+    "top_k_mask",
+    "top_p_mask",
+    "transform_probs",
     "ancestors_or_self",
     "tree_attention",
     "tree_attention_dense_mask",

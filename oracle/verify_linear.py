@@ -31,6 +31,10 @@ reading that makes the procedure lossless is standard speculative sampling
 5. y = the smallest token id v with cumsum(w)[v] > u_s * sum(w); if rounding
    leaves no such v, y = the last v with w[v] > 0.
 Emitted tokens for the step: d[0:L] followed by y.
+
+With a sampling transform (top-k, top-p, greedy; oracle/sampling.py) every p
+and q row is replaced by its transformed distribution before step 2 and the
+same rules run on those (drafts are then drawn from the transformed q).
 """
 
 import numpy as np
@@ -81,7 +85,8 @@ def inverse_cdf(w, u):
     return int(pos[-1])
 
 
-def verify_linear(p_logits, q_logits, drafts, u_accept, u_sample, temperature=1.0):
+def verify_linear(p_logits, q_logits, drafts, u_accept, u_sample, temperature=1.0, top_k=0, top_p=1.0,
+                  greedy=False):
     """Verify a batch of linear draft blocks.
 
     p_logits [B, k+1, V]  AR rows; row i scores draft i, row k is the bonus row.
@@ -89,6 +94,8 @@ def verify_linear(p_logits, q_logits, drafts, u_accept, u_sample, temperature=1.
     drafts   [B, k]       int token ids; an id outside [0, V) has probability 0
                           under p and q and is rejected.
     u_accept [B, k], u_sample [B]: uniforms in [0, 1).
+    top_k, top_p, greedy: the sampling transform of every p and q row
+    (oracle.sampling.transform_probs); the defaults leave the rows unchanged.
 
     Returns a dict of numpy arrays:
       accept_len [B] int, token [B] int (correction or bonus y),
@@ -110,9 +117,17 @@ def verify_linear(p_logits, q_logits, drafts, u_accept, u_sample, temperature=1.
     q_draft = np.zeros((bsz, k), dtype=np.float64)
     res_mass = np.zeros(bsz, dtype=np.float64)
 
+    from .sampling import transform_probs
+    plain = top_k <= 0 and top_p >= 1.0 and not greedy
+
+    def rows(lg):
+        if plain:
+            return softmax_rows(lg, temperature)
+        return np.stack([transform_probs(r, temperature, top_k, top_p, greedy) for r in lg])
+
     for b in range(bsz):
-        p = softmax_rows(p_logits[b], temperature)          # [k+1, V]
-        q = softmax_rows(q_logits[b], temperature) if k else np.zeros((0, p.shape[1]))
+        p = rows(p_logits[b])                                # [k+1, V]
+        q = rows(q_logits[b]) if k else np.zeros((0, p.shape[1]))
         length = k
         for i in range(k):
             d = int(drafts[b, i])
