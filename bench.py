@@ -649,6 +649,31 @@ def bench_linear_sigma_sweep(args, dad, torch, sigmas=(0.1, 0.5, 2.0), reps=20):
                     "full_read_lower_bound_us": full_bytes / (HBM_PEAK_GBS * 1e9) * 1e6,
                     "early_exit_lower_bound_us": early_bytes / (HBM_PEAK_GBS * 1e9) * 1e6})
         log(f"linear verify sigma {sigma}: {ms * 1e3:.1f} us, mean L {L.mean():.2f}")
+        if sigma == 0.5:
+            # the same rows under sampling transforms (uno_psi_spec_verify_linear_sampled;
+            # the drafts here come from the untransformed rows, which changes no work)
+            ws_s = torch.empty(dad.psi_spec_verify_linear_sampled_workspace(B, k, V), dtype=torch.uint8, device=dev)
+            sampled = {}
+            for name, kw in (("top_k_50", dict(top_k=50)), ("top_p_0.9", dict(top_p=0.9)),
+                             ("top_k_50_top_p_0.9", dict(top_k=50, top_p=0.9)), ("greedy", dict(greedy=True))):
+                for _ in range(2):
+                    dad.psi_spec_verify_linear_sampled(p, q, drafts, ua, us, outputs=out, workspace=ws_s, **kw)
+                torch.cuda.synchronize()
+                dad.profile_reset()
+                dad.profile_enable(True)
+                for _ in range(reps // 2):
+                    dad.psi_spec_verify_linear_sampled(p, q, drafts, ua, us, outputs=out, workspace=ws_s, **kw)
+                torch.cuda.synchronize()
+                sm = sum(dad.profile_query(n)[0] for n in ("uno_row_cut", "uno_accept", "uno_draw_seg",
+                                                          "uno_draw_resolve")) / (reps // 2)
+                cut_ms = dad.profile_query("uno_row_cut")[0] / (reps // 2)
+                dad.profile_enable(False)
+                dad.profile_reset()
+                sampled[name] = {"us": sm * 1e3, "row_cut_us": cut_ms * 1e3,
+                                 "mean_accept_len": float(out["accept_len"].float().mean())}
+                log(f"  sampled verify {name}: {sm * 1e3:.1f} us")
+            res[-1]["sampled"] = sampled
+            del ws_s
         del p, q, drafts
         torch.cuda.empty_cache()
     return res

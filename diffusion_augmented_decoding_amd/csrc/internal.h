@@ -86,6 +86,10 @@ struct VerifyLinearArgs {
 };
 size_t verify_linear_workspace_bytes(int batch, int k, int vocab);
 hipError_t launch_verify_linear(const VerifyLinearArgs& a, hipStream_t stream);
+// The same verify on rows transformed by top-k (0: off), top-p (1: off) or greedy.
+size_t verify_linear_sampled_workspace_bytes(int batch, int k, int vocab);
+hipError_t launch_verify_linear_sampled(const VerifyLinearArgs& a, int top_k, float top_p, int greedy,
+                                        hipStream_t stream);
 // Host validation of a linear verify call (all but the workspace); fills the
 // kernel arguments (ws left null).
 uno_status verify_linear_args(uno_dtype logit_dtype, int32_t batch, int32_t k, int32_t vocab, const void* p_logits,

@@ -172,6 +172,351 @@ hipError_t launch_lin(const VerifyLinearArgs& a, hipStream_t stream) {
                         "uno_draw_seg", "uno_draw_resolve");
 }
 
+// ---------------------------------------------------------------- sampling transforms
+// The verify under a sampling transform (top-k, top-p, greedy): every p and q
+// row is replaced by its transformed distribution, then the same accept,
+// residual and draw rules run on those.  Four launches:
+//  1. lin_cut: one 1024-thread block per row finds, exactly, the smallest
+//     logit key the transform keeps (radix select from the top, 8 key bits
+//     per level: integer counts for top-k, fixed-point masses for top-p, both
+//     through LDS integer atomics, so the result does not depend on the
+//     order of the additions), then the kept mass in a fixed order, the
+//     row's maximum and its first argmax (greedy) and the draft's logit;
+//  2. lin_accept_cut: the accept tests on the transformed probabilities;
+//  3-4. the draw kernels with the transform applied to both rows.
+struct RowCut {
+  float m;          // max_v y_v (y = logit log2(e) / T)
+  float s;          // sum over kept v of 2^(y_v - m); 1 for greedy
+  uint32_t tau;     // smallest kept logit key
+  int argmax;       // greedy: the row's first argmax; -1 otherwise
+};
+
+struct CutWs {
+  RowCut* cut;      // [rows]
+  float* xd;        // [rows]
+  DrawDesc* desc;   // [batch]
+  float* seg;
+};
+
+CutWs cut_ws(void* base, int batch, int k, int vocab) {
+  const int rows = batch * (2 * k + 1);
+  char* p = static_cast<char*>(base);
+  CutWs w;
+  w.cut = reinterpret_cast<RowCut*>(p);
+  p += align_up(size_t(rows) * sizeof(RowCut), 256);
+  w.xd = reinterpret_cast<float*>(p);
+  p += align_up(size_t(rows) * sizeof(float), 256);
+  w.desc = reinterpret_cast<DrawDesc*>(p);
+  p += align_up(size_t(batch) * sizeof(DrawDesc), 256);
+  w.seg = reinterpret_cast<float*>(p);
+  (void)vocab;
+  return w;
+}
+
+struct CutParams {
+  int top_k;        // 0: off
+  float top_p;      // 1: off
+  int greedy;
+};
+
+constexpr int kCutThreads = 1024;
+constexpr int kCutWaves = kCutThreads / kWave;
+constexpr double kMassScale = 1099511627776.0;   // 2^40: fixed-point masses (2^20 tokens of mass <= 1 fit)
+
+// One pass over row elements [0, vocab) by the block: f(index, logit) for
+// each, 8 consecutive elements per thread per step (16-byte loads).
+template <typename T, typename F>
+__device__ __forceinline__ void cut_pass(const T* row, int vocab, F f) {
+  const bool vec = row_vec_ok(row);
+  for (int e0 = threadIdx.x * 8; e0 < vocab; e0 += kCutThreads * 8) {
+    float x[8];
+    load8<T, false>(row, e0, vocab, vec, x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (e0 + j < vocab) f(e0 + j, x[j]);
+  }
+}
+
+// Radix descent: the first bin, from the top, at which the running total
+// (starting from `before`) reaches `target`; returns the bin, and in
+// `before` the total of the bins above it.  Wave 0 runs it (256 bins, 4 per
+// lane, lane l holding bins 255 - 4l .. 252 - 4l); every lane gets the result.
+template <typename U>
+__device__ __forceinline__ int find_from_top(const U* hist, double target, double& before) {
+  const int lane = threadIdx.x & (kWave - 1);
+  double c[4], mine = 0.0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    c[q] = double(hist[255 - (4 * lane + q)]);
+    mine += c[q];
+  }
+  // inclusive scan of the lanes' sums (exact: integers below 2^53)
+  double incl = mine;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const double o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  const double excl = incl - mine;
+  const uint64_t hit = wave_ballot(before + incl >= target);
+  int bin = 0;
+  double bef = 0.0;
+  if (hit) {
+    const int l = int(__builtin_ctzll(hit));
+    double run = before + __shfl(excl, l);
+    int found = 3;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const double cq = __shfl(c[q], l);
+      if (found == 3 && q < 3 && run + cq >= target) {
+        found = q;
+      } else if (found == 3 && q < 3) {
+        run += cq;
+      }
+    }
+    bin = 255 - (4 * l + found);
+    bef = run;
+  } else {   // never reached (target within the total): keep everything
+    bin = 0;
+    bef = before + __shfl(incl, kWave - 1);
+  }
+  before = bef;
+  return bin;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kCutThreads) void lin_cut_kernel(VerifyLinearArgs a, CutWs w, CutParams cp) {
+  __shared__ uint32_t hcnt[256];
+  __shared__ unsigned long long hmass[256];
+  __shared__ uint32_t red_k[kCutWaves];
+  __shared__ int red_i[kCutWaves];
+  __shared__ float red_f[kCutWaves];
+  __shared__ uint32_t sh_key;
+  __shared__ int sh_idx;
+  __shared__ double sh_before;
+  __shared__ unsigned long long sh_total;
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int rps = 2 * a.k + 1;
+  const int b = row / rps, j = row - b * rps;
+  int draft;
+  const T* base = lin_row<T>(a, b, j, &draft);
+  const int V = a.vocab;
+  const float sl2 = a.scale_log2;
+  // key bits that vary: 16 for bf16 rows (the low half of a bf16 key is set by its sign)
+  constexpr int kLevels = sizeof(T) == 2 ? 2 : 4;
+
+  // pass A: the largest key and its first index
+  uint32_t bk = 0;
+  int bi = 0x7fffffff;
+  cut_pass<T>(base, V, [&](int v, float x) {
+    const uint32_t kk = logit_key(x);
+    if (kk > bk || (kk == bk && v < bi)) {
+      bk = kk;
+      bi = v;
+    }
+  });
+  // block argmax: largest key, then smallest index
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const uint32_t ok = __shfl_xor(bk, off);
+    const int oi = __shfl_xor(bi, off);
+    if (ok > bk || (ok == bk && oi < bi)) {
+      bk = ok;
+      bi = oi;
+    }
+  }
+  if (lane == 0) {
+    red_k[wave] = bk;
+    red_i[wave] = bi;
+  }
+  for (int i = tid; i < 256; i += kCutThreads) {
+    hcnt[i] = 0;
+    hmass[i] = 0ull;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t k0 = red_k[0];
+    int i0 = red_i[0];
+    for (int q = 1; q < kCutWaves; ++q)
+      if (red_k[q] > k0 || (red_k[q] == k0 && red_i[q] < i0)) {
+        k0 = red_k[q];
+        i0 = red_i[q];
+      }
+    sh_key = k0;
+    sh_idx = i0;
+  }
+  __syncthreads();
+  const uint32_t maxkey = sh_key;
+  const int amax = sh_idx;
+  const float m = key_logit(maxkey) * sl2;
+  if (tid == 0 && j != a.k)   // rows that score a draft: its logit (-inf for an id outside [0, V))
+    w.xd[row] = (draft >= 0 && draft < V) ? load_logit<T>(base, draft) : -INFINITY;
+  if (cp.greedy) {
+    if (tid == 0) w.cut[row] = RowCut{m, 1.f, maxkey, amax};
+    return;
+  }
+  // the key prefix fixed so far and its width; below it every element counts
+  uint32_t prefix = 0;
+  int fixed_bits = 0;
+  auto in_prefix = [&](uint32_t kk) { return fixed_bits == 0 || (kk >> (32 - fixed_bits)) == (prefix >> (32 - fixed_bits)); };
+  uint32_t tau = 0;   // keep all
+  // ---- top-k: the k-th largest key, by counts
+  if (cp.top_k > 0 && cp.top_k < V) {
+    double before = 0.0;
+    for (int lev = 0; lev < kLevels; ++lev) {
+      const int shift = 24 - 8 * lev;
+      cut_pass<T>(base, V, [&](int, float x) {
+        const uint32_t kk = logit_key(x);
+        if (in_prefix(kk)) atomicAdd(&hcnt[(kk >> shift) & 255u], 1u);
+      });
+      __syncthreads();
+      if (wave == 0) {
+        double bef = before;
+        const int bin = find_from_top(hcnt, double(cp.top_k), bef);
+        if (lane == 0) {
+          sh_key = uint32_t(bin);
+          sh_before = bef;
+        }
+      }
+      __syncthreads();
+      prefix |= sh_key << shift;
+      fixed_bits += 8;
+      before = sh_before;
+      for (int i = tid; i < 256; i += kCutThreads) hcnt[i] = 0;
+      __syncthreads();
+    }
+    if (kLevels == 2) prefix |= (prefix & 0x80000000u) ? 0u : 0xffffu;
+    tau = prefix;
+    prefix = 0;
+    fixed_bits = 0;
+  }
+  // ---- top-p on the kept distribution: the smallest key group whose mass
+  // above is below top_p of the kept mass, by fixed-point masses
+  if (cp.top_p < 1.f) {
+    const uint32_t base_tau = tau;
+    auto mass_fx = [&](float x) {
+      return (unsigned long long)(double(fast_exp2(fmaf(x, sl2, -m))) * kMassScale);
+    };
+    double before = 0.0, target = 0.0;
+    for (int lev = 0; lev < kLevels; ++lev) {
+      const int shift = 24 - 8 * lev;
+      cut_pass<T>(base, V, [&](int, float x) {
+        const uint32_t kk = logit_key(x);
+        if (kk >= base_tau && in_prefix(kk)) atomicAdd(&hmass[(kk >> shift) & 255u], mass_fx(x));
+      });
+      __syncthreads();
+      if (lev == 0) {
+        if (tid == 0) {
+          unsigned long long t = 0;
+          for (int i = 0; i < 256; ++i) t += hmass[i];
+          sh_total = t;
+        }
+        __syncthreads();
+        target = double(cp.top_p) * double(sh_total);
+      }
+      if (wave == 0) {
+        double bef = before;
+        const int bin = find_from_top(hmass, target, bef);
+        if (lane == 0) {
+          sh_key = uint32_t(bin);
+          sh_before = bef;
+        }
+      }
+      __syncthreads();
+      prefix |= sh_key << shift;
+      fixed_bits += 8;
+      before = sh_before;
+      for (int i = tid; i < 256; i += kCutThreads) hmass[i] = 0ull;
+      __syncthreads();
+    }
+    if (kLevels == 2) prefix |= (prefix & 0x80000000u) ? 0u : 0xffffu;
+    tau = prefix > base_tau ? prefix : base_tau;
+  }
+  // kept mass, each thread in index order, then waves in order
+  float acc = 0.f;
+  cut_pass<T>(base, V, [&](int, float x) {
+    if (logit_key(x) >= tau) acc += fast_exp2(fmaf(x, sl2, -m));
+  });
+  acc = wave_sum(acc);
+  if (lane == 0) red_f[wave] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    float t = 0.f;
+    for (int q = 0; q < kCutWaves; ++q) t += red_f[q];
+    w.cut[row] = RowCut{m, t, tau, -1};
+  }
+}
+
+// One wave per sequence: the accept tests on the transformed probabilities.
+template <typename T>
+__global__ __launch_bounds__(kWave) void lin_accept_cut_kernel(VerifyLinearArgs a, CutWs w) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int k = a.k, rps = 2 * k + 1;
+  const int64_t r0 = int64_t(b) * rps;
+  const float sl2 = a.scale_log2;
+  bool rej = false;
+  if (lane < k) {
+    const int d = a.drafts[int64_t(b) * a.drafts_seq + lane];
+    const RowCut cpp = w.cut[r0 + lane], cq = w.cut[r0 + k + 1 + lane];
+    const float xp = w.xd[r0 + lane], xq = w.xd[r0 + k + 1 + lane];
+    const float pd = row_prob<true>(xp, d, sl2, cpp.m, 1.f / cpp.s, cpp.tau, cpp.argmax);
+    const float qd = row_prob<true>(xq, d, sl2, cq.m, 1.f / cq.s, cq.tau, cq.argmax);
+    rej = !(a.u_acc[int64_t(b) * k + lane] * qd < pd);
+    if (a.out_pd) a.out_pd[int64_t(b) * k + lane] = pd;
+    if (a.out_qd) a.out_qd[int64_t(b) * k + lane] = qd;
+  }
+  const uint64_t mask = wave_ballot(rej);
+  const int L = mask ? int(__builtin_ctzll(mask)) : k;
+  if (lane == 0) {
+    a.out_len[b] = L;
+    const RowCut cpp = w.cut[r0 + L];
+    DrawDesc d;
+    d.prow = static_cast<const T*>(a.p) + int64_t(b) * a.p_seq + int64_t(L) * a.p_row;
+    d.mp = cpp.m;
+    d.inv_sp = 1.f / cpp.s;
+    d.tp = cpp.tau;
+    d.gp = cpp.argmax;
+    if (L < k) {
+      const RowCut cq = w.cut[r0 + k + 1 + L];
+      d.qrow = static_cast<const T*>(a.q) + int64_t(b) * a.q_seq + int64_t(L) * a.q_row;
+      d.mq = cq.m;
+      d.inv_sq = 1.f / cq.s;
+      d.tq = cq.tau;
+      d.gq = cq.argmax;
+      d.c = 1.f;
+    } else {
+      d.qrow = d.prow;
+      d.mq = 0.f;
+      d.inv_sq = 0.f;
+      d.tq = 0u;
+      d.gq = -1;
+      d.c = 0.f;
+    }
+    d.active = 1;
+    w.desc[b] = d;
+  }
+}
+
+template <typename T>
+hipError_t launch_lin_cut(const VerifyLinearArgs& a, const CutParams& cp, hipStream_t stream) {
+  const int rows = a.batch * (2 * a.k + 1);
+  CutWs w = cut_ws(a.ws, a.batch, a.k, a.vocab);
+  {
+    ProfileScope ps("uno_row_cut", stream);
+    hipLaunchKernelGGL(lin_cut_kernel<T>, dim3(rows), dim3(kCutThreads), 0, stream, a, w, cp);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    ProfileScope ps("uno_accept", stream);
+    hipLaunchKernelGGL(lin_accept_cut_kernel<T>, dim3(a.batch), dim3(kWave), 0, stream, a, w);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_draw<T, true>(w.desc, a.batch, a.vocab, a.scale_log2, w.seg, a.u_s, a.out_tok, a.out_mass, stream,
+                              "uno_draw_seg", "uno_draw_resolve");
+}
+
 // ---------------------------------------------------------------- row sampler
 // y[row] = inverse CDF of softmax(logits[row] / T) at u[row], in token order:
 // the same statistics pass and two-launch draw as the verify sampler, with
@@ -271,6 +616,18 @@ size_t verify_linear_workspace_bytes(int batch, int k, int vocab) {
 
 hipError_t launch_verify_linear(const VerifyLinearArgs& a, hipStream_t stream) {
   return a.dtype == UNO_BF16 ? launch_lin<uint16_t>(a, stream) : launch_lin<float>(a, stream);
+}
+
+size_t verify_linear_sampled_workspace_bytes(int batch, int k, int vocab) {
+  const int rows = batch * (2 * k + 1);
+  return align_up(size_t(rows) * sizeof(RowCut), 256) + align_up(size_t(rows) * sizeof(float), 256) +
+         align_up(size_t(batch) * sizeof(DrawDesc), 256) + draw_seg_bytes(batch, vocab);
+}
+
+hipError_t launch_verify_linear_sampled(const VerifyLinearArgs& a, int top_k, float top_p, int greedy,
+                                        hipStream_t stream) {
+  const CutParams cp{top_k, top_p, greedy};
+  return a.dtype == UNO_BF16 ? launch_lin_cut<uint16_t>(a, cp, stream) : launch_lin_cut<float>(a, cp, stream);
 }
 
 }  // namespace uno

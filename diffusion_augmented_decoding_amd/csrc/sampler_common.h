@@ -233,10 +233,38 @@ struct DrawDesc {
   float mp, inv_sp, mq, inv_sq;
   float c;          // 0: w = p; > 0: w = max(0, p - c q)
   int active;       // 0: no draw (token written as -1)
+  // sampling transform (read by the CUT draw kernels only): tokens whose
+  // logit key is below tp (tq) have probability 0 under p (q); gp (gq) >= 0:
+  // the row is one-hot at that token (greedy)
+  uint32_t tp, tq;
+  int gp, gq;
 };
 
+// Order-preserving key of a logit: a < b as floats iff key(a) < key(b) as
+// unsigned integers (finite values and -inf).  A bf16 value's key has its
+// low 16 bits all 0 (positive) or all 1 (negative).
+__device__ __forceinline__ uint32_t logit_key(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_logit(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Probability of token v with logit x under a row (m, 1/s) and its
+// transform (keys below `cut` out; one-hot at g >= 0).
+template <bool CUT>
+__device__ __forceinline__ float row_prob(float x, int v, float sl2, float m, float inv_s, uint32_t cut, int g) {
+  if constexpr (CUT) {
+    if (g >= 0) return v == g ? 1.f : 0.f;
+    return logit_key(x) >= cut ? fast_exp2(fmaf(x, sl2, -m)) * inv_s : 0.f;
+  } else {
+    return fast_exp2(fmaf(x, sl2, -m)) * inv_s;
+  }
+}
+
 // w of 8 elements (and p alone, for the fallback when w has no mass).
-template <typename T, bool NT = true>
+template <typename T, bool NT = true, bool CUT = false>
 __device__ __forceinline__ void weights8(const DrawDesc& d, int e0, int vocab, float sl2, bool vp, bool vq,
                                          float (&w)[8], float (&pw)[8]) {
   float xp[8];
@@ -246,10 +274,10 @@ __device__ __forceinline__ void weights8(const DrawDesc& d, int e0, int vocab, f
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const bool in = e0 + j < vocab;
-    const float p = fast_exp2(fmaf(xp[j], sl2, -d.mp)) * d.inv_sp;
+    const float p = row_prob<CUT>(xp[j], e0 + j, sl2, d.mp, d.inv_sp, d.tp, d.gp);
     pw[j] = in ? p : 0.f;
     if (d.c != 0.f) {
-      const float q = fast_exp2(fmaf(xq[j], sl2, -d.mq)) * d.inv_sq;
+      const float q = row_prob<CUT>(xq[j], e0 + j, sl2, d.mq, d.inv_sq, d.tq, d.gq);
       w[j] = in ? fmaxf(fmaf(-d.c, q, p), 0.f) : 0.f;
     } else {
       w[j] = pw[j];
@@ -259,7 +287,7 @@ __device__ __forceinline__ void weights8(const DrawDesc& d, int e0, int vocab, f
 
 // Segment masses of chunk c of draw b: seg[(b * nchunk + c) * 2*kSegPerChunk + k]
 // for the 16 segments of w, then the 16 of p.  A block of kChunkThreads threads.
-template <typename T>
+template <typename T, bool CUT = false>
 __device__ __forceinline__ void draw_seg_body(const DrawDesc* __restrict__ desc, int vocab, float sl2,
                                               float* __restrict__ seg, int b, int c, int nchunk) {
   const DrawDesc d = desc[b];
@@ -274,7 +302,7 @@ __device__ __forceinline__ void draw_seg_body(const DrawDesc* __restrict__ desc,
   for (int q = 0; q < kSegPerWave; ++q) {
     const int e0 = c * kChunk + (wave * kSegPerWave + q) * kSegLen + lane * 8;
     float w[8], pw[8];
-    weights8<T>(d, e0, vocab, sl2, vp, vq, w, pw);
+    weights8<T, true, CUT>(d, e0, vocab, sl2, vp, vq, w, pw);
     sw[q] = 0.f;
     sp[q] = 0.f;
 #pragma unroll
@@ -295,10 +323,10 @@ __device__ __forceinline__ void draw_seg_body(const DrawDesc* __restrict__ desc,
 }
 
 // Grid (batch, nchunk), 256 threads.
-template <typename T>
+template <typename T, bool CUT = false>
 __global__ __launch_bounds__(kChunkThreads) void draw_seg_kernel(const DrawDesc* __restrict__ desc, int vocab,
                                                                  float sl2, float* __restrict__ seg) {
-  draw_seg_body<T>(desc, vocab, sl2, seg, blockIdx.x, blockIdx.y, gridDim.y);
+  draw_seg_body<T, CUT>(desc, vocab, sl2, seg, blockIdx.x, blockIdx.y, gridDim.y);
 }
 
 // Resolve the inverse CDF for one batch element (one wave): S = sum of the
@@ -306,7 +334,7 @@ __global__ __launch_bounds__(kChunkThreads) void draw_seg_kernel(const DrawDesc*
 // the element within the segment (re-reads 512 elements).  Falls back to p
 // when w has no mass.  y = -1 when the descriptor is inactive.  Called by
 // one whole wave (the first of its block).
-template <typename T>
+template <typename T, bool CUT = false>
 __device__ __forceinline__ void draw_resolve_body(const DrawDesc* __restrict__ desc, int vocab, float sl2,
                                                   const float* __restrict__ seg, const float* __restrict__ u_s,
                                                   int32_t* __restrict__ out_tok, float* __restrict__ out_mass,
@@ -383,8 +411,8 @@ __device__ __forceinline__ void draw_resolve_body(const DrawDesc* __restrict__ d
   if (sidx >= 0) {
     const int e0 = (sidx / kSegPerChunk) * kChunk + (sidx % kSegPerChunk) * kSegLen + lane * 8;
     float w[8], pw[8];
-    weights8<T>(d, e0, vocab, sl2, row_vec_ok(static_cast<const T*>(d.prow)),
-                row_vec_ok(static_cast<const T*>(d.qrow)), w, pw);
+    weights8<T, true, CUT>(d, e0, vocab, sl2, row_vec_ok(static_cast<const T*>(d.prow)),
+                           row_vec_ok(static_cast<const T*>(d.qrow)), w, pw);
     float ls = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) ls += w[j];
@@ -420,31 +448,32 @@ __device__ __forceinline__ void draw_resolve_body(const DrawDesc* __restrict__ d
   }
 }
 
-template <typename T>
+template <typename T, bool CUT = false>
 __global__ __launch_bounds__(kWave) void draw_resolve_kernel(const DrawDesc* __restrict__ desc, int vocab,
                                                              float sl2, const float* __restrict__ seg,
                                                              const float* __restrict__ u_s,
                                                              int32_t* __restrict__ out_tok,
                                                              float* __restrict__ out_mass) {
-  draw_resolve_body<T>(desc, vocab, sl2, seg, u_s, out_tok, out_mass, blockIdx.x);
+  draw_resolve_body<T, CUT>(desc, vocab, sl2, seg, u_s, out_tok, out_mass, blockIdx.x);
 }
 
-// Launch the two draw kernels for `batch` descriptors.
-template <typename T>
+// Launch the two draw kernels for `batch` descriptors (CUT: the rows carry a
+// sampling transform).
+template <typename T, bool CUT = false>
 hipError_t launch_draw(const DrawDesc* desc, int batch, int vocab, float sl2, float* seg, const float* u_s,
                        int32_t* out_tok, float* out_mass, hipStream_t stream, const char* seg_name,
                        const char* resolve_name) {
   {
     ProfileScope ps(seg_name, stream);
-    hipLaunchKernelGGL(draw_seg_kernel<T>, dim3(batch, num_chunks(vocab)), dim3(kChunkThreads), 0, stream, desc,
-                       vocab, sl2, seg);
+    hipLaunchKernelGGL((draw_seg_kernel<T, CUT>), dim3(batch, num_chunks(vocab)), dim3(kChunkThreads), 0, stream,
+                       desc, vocab, sl2, seg);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     ProfileScope ps(resolve_name, stream);
-    hipLaunchKernelGGL(draw_resolve_kernel<T>, dim3(batch), dim3(kWave), 0, stream, desc, vocab, sl2, seg, u_s,
-                       out_tok, out_mass);
+    hipLaunchKernelGGL((draw_resolve_kernel<T, CUT>), dim3(batch), dim3(kWave), 0, stream, desc, vocab, sl2, seg,
+                       u_s, out_tok, out_mass);
   }
   return hipGetLastError();
 }

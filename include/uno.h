@@ -51,7 +51,7 @@ typedef enum {
 
 typedef enum { UNO_F32 = 0, UNO_BF16 = 1 } uno_dtype;
 
-#define UNO_ABI_VERSION 4
+#define UNO_ABI_VERSION 5
 
 int uno_abi_version(void);
 const char* uno_status_string(uno_status s);
@@ -153,6 +153,39 @@ uno_status uno_psi_spec_verify_linear_noalloc(hipStream_t stream, uno_dtype logi
                                               float temperature,
                                               int32_t* out_accept_len, int32_t* out_token,
                                               float* out_p_draft, float* out_q_draft, float* out_residual_mass);
+
+/* Linear verify under a sampling transform.  Source: 4sapi.net blog on Uno,
+ * its checklist (a changed temperature or top_p changes the distribution the
+ * AR model samples from); Uno summary (hyper.ai), section "方法" (the verify
+ * is lossless with respect to the AR sampling distribution).  Every p and q
+ * row is replaced by its transformed distribution, then the rules of
+ * uno_psi_spec_verify_linear run unchanged (drafts must come from the
+ * transformed q rows):
+ *   top_k >= 1: keep the tokens whose logit is at least the top_k-th largest
+ *     logit of the row (ties at the boundary all kept); 0 = off;
+ *   0 < top_p < 1: after top-k, keep the tokens whose strictly larger logits
+ *     carry less than top_p of the kept mass (whole tie groups, largest
+ *     first, until the mass reaches top_p); 1 = off;
+ *   greedy = 1: the row is one-hot at its first largest logit (temperature,
+ *     top_k and top_p ignored).
+ * Kept rows are renormalised.  out_p_draft / out_q_draft are the transformed
+ * probabilities and out_residual_mass the transformed residual's mass.  The
+ * kept set is found exactly per row (radix selection on the logit order with
+ * integer and 2^-40 fixed-point counts); a top-p boundary whose mass above
+ * lies within 2^-40 * 2^20 of top_p times the kept mass may resolve either
+ * way.  Arguments and requirements as uno_psi_spec_verify_linear, plus top_k
+ * >= 0, 0 < top_p <= 1, greedy in {0, 1}. */
+uno_status uno_psi_spec_verify_linear_sampled_workspace(int32_t batch, int32_t k, int32_t vocab, size_t* bytes);
+uno_status uno_psi_spec_verify_linear_sampled(hipStream_t stream, uno_dtype logit_dtype,
+                                              int32_t batch, int32_t k, int32_t vocab,
+                                              const void* p_logits, int64_t p_seq_stride, int64_t p_row_stride,
+                                              const void* q_logits, int64_t q_seq_stride, int64_t q_row_stride,
+                                              const int32_t* draft_tokens,
+                                              const float* u_accept, const float* u_sample,
+                                              float temperature, int32_t top_k, float top_p, int32_t greedy,
+                                              int32_t* out_accept_len, int32_t* out_token,
+                                              float* out_p_draft, float* out_q_draft, float* out_residual_mass,
+                                              void* workspace, size_t workspace_bytes);
 
 /* --------------------------------------------------------------------------
  * Tree-masked grouped-query attention for tree verification.

@@ -176,3 +176,64 @@ def check_step_decisions(logits, block, tokens, prev_q, gpu, u_draft, u_accept, 
             assert draw_is_valid(w, float(u_sample[b]), yg, tie), f"seq {b}: token gpu {yg} oracle {yo} (L={Lo})"
             ties += 1
     return draft_ties, ties
+
+
+def top_p_margin(row, temperature, top_k, top_p):
+    """Distance of a row's top-p boundary from deciding the other way: the
+    smallest |mass strictly above a tie group - top_p| over the groups of the
+    top-k renormalised distribution (inf when top-p is off)."""
+    if top_p >= 1.0:
+        return np.inf
+    x = np.asarray(row, np.float64)
+    p = oracle.softmax_rows(x, temperature)
+    p = np.where(oracle.top_k_mask(x, top_k), p, 0.0)
+    p = p / p.sum()
+    vals, inv = np.unique(-x, return_inverse=True)
+    gm = np.bincount(inv, weights=p, minlength=vals.size)
+    above = np.concatenate(([0.0], np.cumsum(gm)[:-1]))
+    live = gm > 0
+    return float(np.min(np.abs(above[live] - top_p)))
+
+
+def check_linear_sampled(case_rows, gpu, seqs, k, temperature, top_k, top_p, greedy, tie=TIE, prob_rtol=1e-5,
+                         mass_atol=1e-5, cut_tie=1e-6):
+    """check_linear under a sampling transform.  A sequence one of whose rows
+    has its top-p boundary within cut_tie of flipping is counted as a tie
+    (its kept set may resolve either way), as are the usual near-ties."""
+    ties = 0
+    kw = dict(top_k=top_k, top_p=top_p, greedy=greedy)
+    for b in seqs:
+        p, q, d, ua, us = case_rows(b)
+        if not greedy and min(top_p_margin(r, temperature, top_k, top_p) for r in list(p) + list(q)) < cut_tie:
+            ties += 1
+            continue
+        o = oracle.verify_linear(p[None], q[None], d[None], ua[None], np.array([us]), temperature, **kw)
+        Lo, yo = int(o["accept_len"][0]), int(o["token"][0])
+        Lg, yg = int(gpu["accept_len"][b]), int(gpu["token"][b])
+        if k > 0 and "p_draft" in gpu:
+            for name in ("p_draft", "q_draft"):
+                ref = o[name][0]
+                got = gpu[name][b]
+                err = np.max(np.abs(got - ref) / np.maximum(ref, 1e-300))
+                assert err <= prob_rtol, f"seq {b} {name} rel err {err:.3g}"
+        if Lo != Lg:
+            i = min(Lo, Lg)
+            qd = o["q_draft"][0, i]
+            ratio = o["p_draft"][0, i] / qd if qd > 0 else np.inf
+            assert abs(float(ua[i]) - ratio) < tie, f"seq {b}: L gpu {Lg} oracle {Lo}, |u - p/q| = {abs(ua[i] - ratio):.3g}"
+            ties += 1
+            continue
+        if "residual_mass" in gpu:
+            err = abs(gpu["residual_mass"][b] - o["residual_mass"][0])
+            assert err <= mass_atol, f"seq {b} residual mass err {err:.3g}"
+        if yg != yo:
+            pr = oracle.transform_probs(p[Lo], temperature, **kw)
+            if Lo < k:
+                w, s = oracle.residual_weights(pr, oracle.transform_probs(q[Lo], temperature, **kw))
+                if s == 0.0:
+                    w = pr
+            else:
+                w = pr
+            assert draw_is_valid(w, us, yg, tie), f"seq {b}: token gpu {yg} oracle {yo} (L={Lo})"
+            ties += 1
+    return ties

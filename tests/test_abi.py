@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.uno_abi_version() == 4
+    assert lib.uno_abi_version() == 5
     for s in range(6):
         assert lib.uno_status_string(s)
     assert lib.uno_status_string(99) == b"unknown status"
@@ -383,3 +383,29 @@ def test_lora_merge_rejects_bad_calls(lib):
     assert _merge(lib, scale=float("inf")) == INVALID
     assert _merge(lib, N=70000) == UNSUPPORTED
     assert _merge(lib, out=ctypes.c_void_p(0x10001)) == INVALID   # not 2-byte aligned
+
+
+def _vls(lib, **kw):
+    a = dict(stream=None, dtype=BF16, batch=2, k=3, vocab=100, p=FAKE16, ps=400, pr=100, q=FAKE16, qs=300, qr=100,
+             d=FAKE16, ua=FAKE16, us=FAKE16, t=1.0, top_k=5, top_p=0.9, greedy=0, L=FAKE16, y=FAKE16, pd=None,
+             qd=None, mass=None, ws=FAKE16, wsb=1 << 30)
+    a.update(kw)
+    return lib.uno_psi_spec_verify_linear_sampled(a["stream"], a["dtype"], a["batch"], a["k"], a["vocab"], a["p"],
+                                                  a["ps"], a["pr"], a["q"], a["qs"], a["qr"], a["d"], a["ua"],
+                                                  a["us"], a["t"], a["top_k"], a["top_p"], a["greedy"], a["L"],
+                                                  a["y"], a["pd"], a["qd"], a["mass"], a["ws"], a["wsb"])
+
+
+def test_verify_linear_sampled_rejects_bad_calls(lib):
+    assert _vls(lib, top_k=-1) == INVALID
+    assert _vls(lib, top_p=0.0) == INVALID
+    assert _vls(lib, top_p=1.5) == INVALID
+    assert _vls(lib, top_p=float("nan")) == INVALID
+    assert _vls(lib, greedy=2) == INVALID
+    assert _vls(lib, t=0.0) == INVALID
+    assert _vls(lib, p=None) == INVALID
+    assert _vls(lib, ws=None) == WORKSPACE
+    assert _vls(lib, wsb=16) == WORKSPACE
+    out = ctypes.c_size_t(0)
+    assert lib.uno_psi_spec_verify_linear_sampled_workspace(256, 15, 151936, ctypes.byref(out)) == OK
+    assert out.value > 0
