@@ -30,6 +30,7 @@ EXPORTS = (
     "uno_psi_spec_step_workspace", "uno_psi_spec_step",
     "uno_kv_commit",
     "uno_profile_enable", "uno_profile_reset", "uno_profile_query",
+    "uno_debug_checks", "uno_debug_checks_enabled",
 )
 
 
@@ -114,6 +115,8 @@ def _declare(lib):
                                              _p, _p, _p, _p, _p, _p, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p,
                                              _p, _sz]),
         "uno_kv_commit": (ctypes.c_int, [_p, _i32, _i32, _p, _p]),
+        "uno_debug_checks": (None, [_i32]),
+        "uno_debug_checks_enabled": (ctypes.c_int32, []),
         "uno_lora_merge": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _f32, _p, _i64]),
         "uno_profile_enable": (None, [ctypes.c_int, ctypes.c_char_p]),
         "uno_profile_reset": (None, []),
@@ -645,6 +648,15 @@ def layer_array(layers):
 
 
 # ------------------------------------------------------------------ kernel timing
+def debug_checks(on=None):
+    """Data-contract checks of token ids and uniforms (uno_debug_checks): set
+    them on or off, or (on=None) return whether they are on."""
+    load()
+    if on is not None:
+        _lib.uno_debug_checks(1 if on else 0)
+    return bool(_lib.uno_debug_checks_enabled())
+
+
 def profile_enable(on=True, name_filter=None):
     """Record HIP events around kernels whose name contains name_filter (None = all)."""
     load()

@@ -233,6 +233,8 @@ uno_status uno_psi_spec_verify_linear(hipStream_t stream, uno_dtype logit_dtype,
   if (workspace_bytes < need || !workspace)
     return fail(UNO_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
   a.ws = workspace;
+  s = debug_check_verify_linear(stream, a);
+  if (s != UNO_OK) return s;
   return check_hip(launch_verify_linear(a, stream), "uno_psi_spec_verify_linear launch");
   UNO_GUARD_END
 }
@@ -276,6 +278,8 @@ uno_status uno_psi_spec_verify_linear_sampled(hipStream_t stream, uno_dtype logi
   if (workspace_bytes < need || !workspace)
     return fail(UNO_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
   a.ws = workspace;
+  s = debug_check_verify_linear(stream, a);
+  if (s != UNO_OK) return s;
   return check_hip(launch_verify_linear_sampled(a, top_k, top_p, greedy, stream),
                    "uno_psi_spec_verify_linear_sampled launch");
   UNO_GUARD_END
@@ -410,6 +414,12 @@ uno_status uno_psi_spec_verify_tree(hipStream_t stream, uno_dtype logit_dtype, i
   a.out_tok = out_token;
   a.ws = workspace;
   a.ws_bytes = workspace_bytes;
+  if (debug_checks()) {   // node tokens (the root's is unused) and the uniforms
+    uno_status d = debug_check_ids(stream, tokens, batch, n_tree, n_tree, 1, 0, vocab, "tokens");
+    if (d == UNO_OK) d = debug_check_unit(stream, u_accept, int64_t(batch) * n_tree, "u_accept");
+    if (d == UNO_OK) d = debug_check_unit(stream, u_sample, batch, "u_sample");
+    if (d != UNO_OK) return d;
+  }
   return check_hip(launch_tree_verify(a, stream), "uno_psi_spec_verify_tree launch");
   UNO_GUARD_END
 }

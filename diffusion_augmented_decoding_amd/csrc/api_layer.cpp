@@ -464,6 +464,10 @@ uno_status uno_sample_rows(hipStream_t stream, uno_dtype logit_dtype, int32_t ro
   a.scale_log2 = 1.4426950408889634f / temperature;
   a.out_tok = out_token;
   a.ws = workspace;
+  if (debug_checks()) {
+    const uno_status d = debug_check_unit(stream, u, rows, "u");
+    if (d != UNO_OK) return d;
+  }
   return check_hip(launch_sample_rows(a, stream), "uno_sample_rows launch");
   UNO_GUARD_END
 }

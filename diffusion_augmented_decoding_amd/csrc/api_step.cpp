@@ -124,6 +124,13 @@ uno_status uno_psi_spec_step(hipStream_t stream, const uno_step_config* config, 
   if (workspace_bytes < W.total || !workspace)
     return fail(UNO_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, W.total);
 
+  if (debug_checks()) {   // ids of every row and the uniforms the step uses
+    uno_status d = debug_check_ids(stream, tokens, c.batch, 2 * c.block, 2 * c.block, 0, 0, c.vocab, "tokens");
+    if (d == UNO_OK && k > 0) d = debug_check_unit(stream, u_draft, int64_t(c.batch) * k, "u_draft");
+    if (d == UNO_OK && kv > 0) d = debug_check_unit(stream, u_accept, int64_t(c.batch) * kv, "u_accept");
+    if (d == UNO_OK) d = debug_check_unit(stream, u_sample, c.batch, "u_sample");
+    if (d != UNO_OK) return d;
+  }
   char* ws = static_cast<char*>(workspace);
   const int64_t rows = int64_t(c.batch) * 2 * c.block;
   void* h = ws + W.h;

@@ -47,6 +47,16 @@ inline const char* tuning_env(const char* name) {
 #endif
 }
 
+// Data-contract checks (UNO_DEBUG / uno_debug_checks): on when enabled; each
+// check waits for the device and returns UNO_ERR_INVALID_ARGUMENT on a
+// violation.  ids[r * stride + c], r < rows, first_col <= c < cols, in [lo, hi).
+bool debug_checks();
+uno_status debug_check_ids(hipStream_t stream, const int32_t* ids, int64_t rows, int64_t cols, int64_t stride,
+                           int64_t first_col, int32_t lo, int32_t hi, const char* what);
+uno_status debug_check_unit(hipStream_t stream, const float* u, int64_t n, const char* what);
+// The checks of a linear verify call (draft ids, both uniforms), when enabled.
+inline uno_status debug_check_verify_linear(hipStream_t stream, const struct VerifyLinearArgs& a);
+
 // Raise a kernel's dynamic-LDS limit to `bytes` once per device: `done` holds
 // one bit per device id (ids >= 64 set the attribute on every launch).
 inline hipError_t ensure_dynamic_lds(const void* kern, int bytes, std::atomic<uint64_t>& done) {
@@ -84,6 +94,13 @@ struct VerifyLinearArgs {
   float* out_mass;
   void* ws;           // workspace (verify_linear_workspace_bytes)
 };
+inline uno_status debug_check_verify_linear(hipStream_t stream, const VerifyLinearArgs& a) {
+  if (!debug_checks()) return UNO_OK;
+  uno_status s = debug_check_ids(stream, a.drafts, a.batch, a.k, a.drafts_seq, 0, 0, a.vocab, "draft_tokens");
+  if (s == UNO_OK) s = debug_check_unit(stream, a.u_acc, int64_t(a.batch) * a.k, "u_accept");
+  if (s == UNO_OK) s = debug_check_unit(stream, a.u_s, a.batch, "u_sample");
+  return s;
+}
 size_t verify_linear_workspace_bytes(int batch, int k, int vocab);
 hipError_t launch_verify_linear(const VerifyLinearArgs& a, hipStream_t stream);
 // The same verify on rows transformed by top-k (0: off), top-p (1: off) or greedy.

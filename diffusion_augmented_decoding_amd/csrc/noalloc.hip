@@ -64,6 +64,8 @@ extern "C" uno_status uno_psi_spec_verify_linear_noalloc(
                                     q_seq_stride, q_row_stride, draft_tokens, u_accept, u_sample, temperature,
                                     out_accept_len, out_token, out_p_draft, out_q_draft, out_residual_mass, &a);
   if (s != UNO_OK) return s;
+  s = debug_check_verify_linear(stream, a);
+  if (s != UNO_OK) return s;
   const size_t need = verify_linear_workspace_bytes(batch, k, vocab);
   if (need > kScratchBytes)
     return fail(UNO_ERR_UNSUPPORTED, "scratch of %zu bytes needed, the allocation-free call has %zu (use "

@@ -27,7 +27,12 @@
  * - Data contract: token ids in [0, vocab), finite logits with |logit / T| <=
  *   1e4 (the softmax kernels subtract a separately rounded row maximum inside
  *   a fused multiply-add; exp(-1e4) is already 0 in fp32, so -1e4 stands for
- *   probability 0), uniforms in [0, 1).  These are not checked on the device.
+ *   probability 0), uniforms in [0, 1).  These are not checked on the device,
+ *   unless the data-contract checks are on (UNO_DEBUG set to anything but "0"
+ *   in the environment, or uno_debug_checks(1)): the verify, sampler and step
+ *   calls then check their token ids and uniforms on the device first, wait
+ *   for the result, and return UNO_ERR_INVALID_ARGUMENT on a violation.  (A
+ *   debugging aid: the calls then synchronise their stream.)
  */
 #ifndef UNO_H
 #define UNO_H
@@ -90,6 +95,11 @@ uno_status uno_gated_lora_linear(hipStream_t stream, uno_dtype dtype,
                                  const uint8_t* gate, float lora_scale,
                                  void* y, int64_t ldy,
                                  void* workspace, size_t workspace_bytes);
+
+/* The data-contract checks (see the conventions above): on = 1 / off = 0; the
+ * default comes from the UNO_DEBUG environment variable. */
+void uno_debug_checks(int32_t on);
+int32_t uno_debug_checks_enabled(void);
 
 /* --------------------------------------------------------------------------
  * Psi-Spec linear verify sampler.

@@ -409,3 +409,12 @@ def test_verify_linear_sampled_rejects_bad_calls(lib):
     out = ctypes.c_size_t(0)
     assert lib.uno_psi_spec_verify_linear_sampled_workspace(256, 15, 151936, ctypes.byref(out)) == OK
     assert out.value > 0
+
+
+def test_debug_checks_switch(lib):
+    was = lib.uno_debug_checks_enabled()
+    lib.uno_debug_checks(1)
+    assert lib.uno_debug_checks_enabled() == 1
+    lib.uno_debug_checks(0)
+    assert lib.uno_debug_checks_enabled() == 0
+    lib.uno_debug_checks(was)
