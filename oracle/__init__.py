@@ -32,6 +32,7 @@ from .verify_linear import (
 from .sampling import kth_largest, top_k_mask, top_p_mask, transform_probs
 from .tree_attention import ancestors_or_self, tree_attention, tree_attention_dense_mask
 from .verify_tree import node_depths, children_lists, verify_tree
+from .tree_build import tree_layout, draw_without, build_tree
 from .decoder import (
     round_bf16,
     rms_norm,
@@ -64,6 +65,9 @@ __all__ = [
     "node_depths",
     "children_lists",
     "verify_tree",
+    "tree_layout",
+    "draw_without",
+    "build_tree",
     "round_bf16",
     "rms_norm",
     "rope",

@@ -29,6 +29,13 @@ Readings:
 * q is one row per depth (delta = 1..max_depth -> q row delta-1), shared by
   siblings; p is one AR row per node, scoring that node's children;
 * accept comparison and inverse-CDF follow the linear sampler's conventions.
+
+Without replacement (siblings drawn with the earlier siblings' tokens removed,
+oracle/tree_build.py): sibling j is tested against q_j, the per-depth
+marginal with the tokens of the siblings tried before it removed and the rest
+renormalised, and a rejection subtracts q_j: r <- max(0, r - q_j) / sum
+(recursive rejection sampling without replacement, Jeon et al. 2024).  A
+residual with zero mass stays as it is for the node's remaining siblings.
 """
 
 import numpy as np
@@ -52,7 +59,7 @@ def children_lists(parent):
     return ch
 
 
-def _verify_one(parent, tokens, p_logits, q_logits, u_accept, u_s, temperature):
+def _verify_one(parent, tokens, p_logits, q_logits, u_accept, u_s, temperature, without_replacement=False):
     depth = node_depths(parent)
     kids = children_lists(parent)
     max_depth = q_logits.shape[0]
@@ -62,10 +69,18 @@ def _verify_one(parent, tokens, p_logits, q_logits, u_accept, u_s, temperature):
     visited = []            # (node, accepted) in visiting order; diagnostic
     while True:
         moved = False
+        removed = []             # tokens of the siblings rejected so far (without replacement)
+        frozen = False
         for c in kids[cur]:
             dl = depth[c]
             assert 1 <= dl <= max_depth
             qd = softmax_rows(q_logits[dl - 1], temperature)
+            if without_replacement:
+                qd = qd.copy()
+                for t_old in removed:
+                    qd[t_old] = 0.0
+                z = float(np.sum(qd))
+                qd = qd / z if z > 0.0 else qd
             t = int(tokens[c])
             ok = u_accept[c] * qd[t] < r[t]
             visited.append((c, bool(ok)))
@@ -75,10 +90,15 @@ def _verify_one(parent, tokens, p_logits, q_logits, u_accept, u_s, temperature):
                 r = softmax_rows(p_logits[c], temperature)
                 moved = True
                 break
+            removed.append(t)
+            if frozen:
+                continue
             w = np.maximum(0.0, r - qd)
             s = float(np.sum(w))
             if s > 0.0:
                 r = w / s
+            elif without_replacement:
+                frozen = True
         if not moved:
             break
     y = inverse_cdf(r, u_s)
@@ -86,7 +106,7 @@ def _verify_one(parent, tokens, p_logits, q_logits, u_accept, u_s, temperature):
 
 
 def verify_tree(parent, tokens, p_logits, q_logits, u_accept, u_sample, temperature=1.0,
-                return_visited=False):
+                return_visited=False, without_replacement=False):
     """Verify a batch of candidate trees.
 
     parent   [B, n]  parent[b, 0] = -1, 0 <= parent[b, i] < i
@@ -97,6 +117,7 @@ def verify_tree(parent, tokens, p_logits, q_logits, u_accept, u_sample, temperat
 
     Returns dict: accept_len [B], path [B, D] (node ids, -1 padded), token [B];
     with return_visited, also the per-batch list of (node, accepted) decisions.
+    without_replacement: siblings were drawn without replacement (module doc).
     """
     parent = np.asarray(parent)
     tokens = np.asarray(tokens)
@@ -112,7 +133,7 @@ def verify_tree(parent, tokens, p_logits, q_logits, u_accept, u_sample, temperat
     visits = []
     for b in range(bsz):
         length, path, y, visited = _verify_one(parent[b], tokens[b], p_logits[b], q_logits[b],
-                                               u_accept[b], u_sample[b], temperature)
+                                               u_accept[b], u_sample[b], temperature, without_replacement)
         acc[b] = length
         paths[b, :length] = path
         ys[b] = y
