@@ -23,6 +23,7 @@ EXPORTS = (
     "uno_psi_spec_verify_linear_sampled_workspace", "uno_psi_spec_verify_linear_sampled",
     "uno_tree_verify_attention_workspace", "uno_tree_verify_attention",
     "uno_psi_spec_verify_tree_workspace", "uno_psi_spec_verify_tree",
+    "uno_psi_spec_build_tree_workspace", "uno_psi_spec_build_tree",
     "uno_rms_norm", "uno_rope", "uno_silu_mul",
     "uno_block_verify_attention_workspace", "uno_block_verify_attention",
     "uno_sample_rows_workspace", "uno_sample_rows",
@@ -96,6 +97,9 @@ def _declare(lib):
         "uno_psi_spec_verify_tree_workspace": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
         "uno_psi_spec_verify_tree": (ctypes.c_int, [_p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32,
                                                     _p, _p, _p, _p, _p, _p, _f32, _p, _p, _p, _p, _sz]),
+        "uno_psi_spec_build_tree_workspace": (ctypes.c_int, [_i32, _i32, _i32, ctypes.POINTER(_sz)]),
+        "uno_psi_spec_build_tree": (ctypes.c_int, [_p, ctypes.c_int, _i32, _i32, _p, _i32, _p, _i64, _i64, _p, _i32,
+                                                   _f32, _i32, _p, _p, _p, _sz]),
         "uno_rms_norm": (ctypes.c_int, [_p, _i64, _i32, _p, _i64, _p, _i64, _p, _i64, _p, _f32, _p, _i64]),
         "uno_rope": (ctypes.c_int, [_p, _i64, _i32, _p, _i64, _p, _f32]),
         "uno_silu_mul": (ctypes.c_int, [_p, _i64, _i32, _p, _i64, _p, _i64, _p, _i64]),
@@ -400,6 +404,50 @@ def psi_spec_verify_tree(parent, tokens, p_logits, q_logits, u_accept, u_sample,
         _ptr(parent), _ptr(tokens), _ptr(p_logits), _ptr(q_logits), _ptr(u_accept), _ptr(u_sample),
         float(temperature), _ptr(outputs["accept_len"]), _ptr(outputs["path"]), _ptr(outputs["token"]),
         _ptr(ws), _nbytes(ws)))
+    return outputs
+
+
+def tree_size(branching):
+    """Node count of the breadth-first tree with the given branching per depth."""
+    n, width = 1, 1
+    for b in branching:
+        width *= int(b)
+        n += width
+    return n
+
+
+def psi_spec_build_tree_workspace(batch, max_depth, vocab):
+    load()
+    out = _sz(0)
+    _check(_lib.uno_psi_spec_build_tree_workspace(batch, max_depth, vocab, ctypes.byref(out)))
+    return out.value
+
+
+def psi_spec_build_tree(q_logits, branching, u_draw, temperature=1.0, without_replacement=False, outputs=None,
+                        workspace=None, stream=None):
+    """Candidate trees from the per-depth draft marginals (uno_psi_spec_build_tree).
+
+    q_logits [B, D, V] (last dim contiguous; any batch and depth strides, e.g.
+    the noisy rows of a step's logits); branching: D ints; u_draw f32 [B, n]
+    with n = tree_size(branching).  Returns dict parent, tokens (int32 [B, n]
+    device tensors; parent[:, 0] = tokens[:, 0] = -1).
+    """
+    import torch
+    load()
+    bsz, dmax, vocab = q_logits.shape
+    if q_logits.stride(2) != 1:
+        raise ValueError("q_logits: the vocabulary dimension must be contiguous")
+    n = tree_size(branching)
+    dev = q_logits.device
+    if outputs is None:
+        outputs = {"parent": torch.empty((bsz, n), dtype=torch.int32, device=dev),
+                   "tokens": torch.empty((bsz, n), dtype=torch.int32, device=dev)}
+    br = (ctypes.c_int32 * max(len(branching), 1))(*[int(b) for b in branching])
+    ws = _workspace(psi_spec_build_tree_workspace(bsz, dmax, vocab), dev, workspace)
+    _check(_lib.uno_psi_spec_build_tree(
+        _stream(stream), _dtype_code(q_logits), bsz, dmax, br, vocab, _ptr(q_logits), q_logits.stride(0),
+        q_logits.stride(1), _ptr(u_draw), n, float(temperature), int(bool(without_replacement)),
+        _ptr(outputs["parent"]), _ptr(outputs["tokens"]), _ptr(ws), _nbytes(ws)))
     return outputs
 
 

@@ -149,6 +149,85 @@ static uno_status check_verify_linear_shape(int32_t batch, int32_t k, int32_t vo
   return UNO_OK;
 }
 
+// ------------------------------------------------------------------ tree construction
+static uno_status check_tree_build(int32_t batch, int32_t max_depth, const int32_t* branching, int32_t vocab,
+                                   int32_t n_tree, int32_t without) {
+  if (batch < 1 || batch > 65535) return fail(UNO_ERR_INVALID_ARGUMENT, "batch must be in [1, 65535]");
+  if (max_depth < 1 || max_depth > 64) return fail(UNO_ERR_INVALID_ARGUMENT, "max_depth must be in [1, 64]");
+  if (vocab < 1) return fail(UNO_ERR_INVALID_ARGUMENT, "vocab must be >= 1");
+  if (vocab > (1 << 20)) return fail(UNO_ERR_UNSUPPORTED, "vocab above 2^20");
+  if (!branching) return fail(UNO_ERR_INVALID_ARGUMENT, "branching is NULL");
+  int64_t n = 1, width = 1;
+  for (int d = 0; d < max_depth; ++d) {
+    const int32_t br = branching[d];
+    if (br < 1 || br > kMaxBranch) return fail(UNO_ERR_INVALID_ARGUMENT, "branching[%d] must be in [1, %d]", d, kMaxBranch);
+    if (without && br > vocab)
+      return fail(UNO_ERR_INVALID_ARGUMENT, "branching[%d] = %d above vocab without replacement", d, br);
+    width *= br;
+    n += width;
+    if (n > 1024) return fail(UNO_ERR_UNSUPPORTED, "tree above 1024 nodes");
+  }
+  if (n_tree != n) return fail(UNO_ERR_INVALID_ARGUMENT, "n_tree %d, the branching gives %lld nodes", n_tree, (long long)n);
+  return UNO_OK;
+}
+
+uno_status uno_psi_spec_build_tree_workspace(int32_t batch, int32_t max_depth, int32_t vocab, size_t* bytes) {
+  UNO_GUARD_BEGIN
+  if (!bytes) return fail(UNO_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (batch < 1 || batch > 65535) return fail(UNO_ERR_INVALID_ARGUMENT, "batch must be in [1, 65535]");
+  if (max_depth < 1 || max_depth > 64) return fail(UNO_ERR_INVALID_ARGUMENT, "max_depth must be in [1, 64]");
+  if (vocab < 1) return fail(UNO_ERR_INVALID_ARGUMENT, "vocab must be >= 1");
+  if (vocab > (1 << 20)) return fail(UNO_ERR_UNSUPPORTED, "vocab above 2^20");
+  *bytes = tree_build_workspace_bytes(batch, max_depth, vocab);
+  return UNO_OK;
+  UNO_GUARD_END
+}
+
+uno_status uno_psi_spec_build_tree(hipStream_t stream, uno_dtype logit_dtype, int32_t batch, int32_t max_depth,
+                                   const int32_t* branching, int32_t vocab, const void* q_logits,
+                                   int64_t q_seq_stride, int64_t q_row_stride, const float* u_draw, int32_t n_tree,
+                                   float temperature, int32_t without_replacement, int32_t* out_parent,
+                                   int32_t* out_tokens, void* workspace, size_t workspace_bytes) {
+  UNO_GUARD_BEGIN
+  if (logit_dtype != UNO_F32 && logit_dtype != UNO_BF16)
+    return fail(UNO_ERR_INVALID_ARGUMENT, "unknown dtype %d", int(logit_dtype));
+  if (without_replacement != 0 && without_replacement != 1)
+    return fail(UNO_ERR_INVALID_ARGUMENT, "without_replacement must be 0 or 1");
+  uno_status s = check_tree_build(batch, max_depth, branching, vocab, n_tree, without_replacement);
+  if (s != UNO_OK) return s;
+  if (!q_logits || !u_draw || !out_parent || !out_tokens)
+    return fail(UNO_ERR_INVALID_ARGUMENT, "required pointer is NULL");
+  if (q_row_stride < vocab || q_seq_stride < 0)
+    return fail(UNO_ERR_INVALID_ARGUMENT, "q_row_stride below vocab or negative q_seq_stride");
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(UNO_ERR_INVALID_ARGUMENT, "temperature must be finite and > 0");
+  const size_t need = tree_build_workspace_bytes(batch, max_depth, vocab);
+  if (workspace_bytes < need || !workspace)
+    return fail(UNO_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  TreeBuildArgs a{};
+  a.dtype = logit_dtype;
+  a.batch = batch;
+  a.max_depth = max_depth;
+  a.vocab = vocab;
+  a.n = n_tree;
+  for (int d = 0; d < max_depth; ++d) a.branching[d] = branching[d];
+  a.q = q_logits;
+  a.q_seq = q_seq_stride;
+  a.q_row = q_row_stride;
+  a.u = u_draw;
+  a.scale_log2 = float(1.4426950408889634 / double(temperature));
+  a.without = without_replacement;
+  a.out_parent = out_parent;
+  a.out_tokens = out_tokens;
+  a.ws = workspace;
+  if (debug_checks()) {
+    const uno_status d = debug_check_unit(stream, u_draw, int64_t(batch) * n_tree, "u_draw");
+    if (d != UNO_OK) return d;
+  }
+  return check_hip(launch_tree_build(a, stream), "uno_psi_spec_build_tree launch");
+  UNO_GUARD_END
+}
+
 }  // extern "C"
 
 namespace uno {

@@ -101,6 +101,24 @@ inline uno_status debug_check_verify_linear(hipStream_t stream, const VerifyLine
   if (s == UNO_OK) s = debug_check_unit(stream, a.u_s, a.batch, "u_sample");
   return s;
 }
+// Candidate trees from the per-depth draft marginals (breadth first, branching[d]
+// children for every node at depth d), tokens drawn with or without replacement.
+constexpr int kMaxBranch = 64;
+struct TreeBuildArgs {
+  uno_dtype dtype;
+  int batch, max_depth, vocab, n;
+  int branching[64];
+  const void* q; int64_t q_seq, q_row;   // q row d of tree b at q + b * q_seq + d * q_row
+  const float* u;                        // [batch][n]
+  float scale_log2;
+  int without;
+  int32_t* out_parent;                   // [batch][n]
+  int32_t* out_tokens;                   // [batch][n]
+  void* ws;
+};
+size_t tree_build_workspace_bytes(int batch, int max_depth, int vocab);
+hipError_t launch_tree_build(const TreeBuildArgs& a, hipStream_t stream);
+
 size_t verify_linear_workspace_bytes(int batch, int k, int vocab);
 hipError_t launch_verify_linear(const VerifyLinearArgs& a, hipStream_t stream);
 // The same verify on rows transformed by top-k (0: off), top-p (1: off) or greedy.

@@ -595,12 +595,230 @@ hipError_t launch_sr(const SampleRowsArgs& a, hipStream_t stream) {
                         "uno_sample_seg", "uno_sample_resolve");
 }
 
+// ---------------------------------------------------------------- tree construction
+// Candidate trees drawn from the per-depth draft marginals: every node at
+// depth d gets branching[d] children, breadth first; the children of a
+// depth-d node draw their tokens from q row d by inverse CDF, each with its
+// own uniform, with replacement (independent draws) or without (sibling j
+// draws from q with the tokens of siblings 1..j-1 removed).  The q rows'
+// statistics and segment masses come from the row sampler's first kernels
+// (one descriptor per q row); then one wave per internal node draws its
+// children in order.
+
+// Level offsets of the breadth-first layout: off[d] = first node id at depth d.
+__device__ __forceinline__ int level_of(const TreeBuildArgs& a, int v, int& off_d, int& off_next) {
+  int off = 0, width = 1;
+  for (int d = 0; d <= a.max_depth; ++d) {
+    if (v < off + width) {
+      off_d = off;
+      off_next = off + width;
+      return d;
+    }
+    off += width;
+    width *= (d < a.max_depth) ? a.branching[d] : 1;
+  }
+  off_d = off_next = off;
+  return a.max_depth;
+}
+
+// One wave per (tree, internal node): the node's children, drawn in order.
+// The q row's segment masses sit in registers (lane l holds segments
+// l + 64 t); a draw takes their prefix, finds the segment holding u times the
+// total and then the token within it.  Without replacement every drawn token
+// is zeroed in the element scan and its segment's mass is recomputed from the
+// row with all drawn tokens zeroed (the same summation order as the segment
+// pass), so the masses the search sees are those of the reduced row.  When no
+// mass is left (every token of positive mass drawn) the draw is the smallest
+// token id not drawn yet.
+template <typename T>
+__global__ __launch_bounds__(kWave) void build_draw_kernel(TreeBuildArgs a, SrWs w) {
+  __shared__ int ex[kMaxBranch];
+  const int b = blockIdx.y, v = blockIdx.x, lane = threadIdx.x;
+  int off_d, off_next;
+  const int d = level_of(a, v, off_d, off_next);
+  const int nb = a.branching[d];
+  const int first = off_next + (v - off_d) * nb;
+  int32_t* par = a.out_parent + int64_t(b) * a.n;
+  int32_t* tok = a.out_tokens + int64_t(b) * a.n;
+  if (v == 0 && lane == 0) {
+    par[0] = -1;
+    tok[0] = -1;
+  }
+  const int row = b * a.max_depth + d;
+  const DrawDesc desc = w.desc[row];
+  const int vocab = a.vocab;
+  const float sl2 = a.scale_log2;
+  const int nchunk = num_chunks(vocab), nseg = nchunk * kSegPerChunk;
+  const float* base = w.seg + int64_t(row) * nchunk * (2 * kSegPerChunk);
+  const bool vp = row_vec_ok(static_cast<const T*>(desc.prow));
+  constexpr int kPerLane = kMaxChunks * kSegPerChunk / kWave;
+  const int ngroup = (nseg + kWave - 1) / kWave;
+  float sv[kPerLane], incl[kPerLane];
+#pragma unroll
+  for (int t = 0; t < kPerLane; ++t) {
+    const int i = t * kWave + lane;
+    sv[t] = (i < nseg) ? base[(i / kSegPerChunk) * (2 * kSegPerChunk) + (i % kSegPerChunk)] : 0.f;
+  }
+  auto drawn = [&](int tkn, int upto) {
+    for (int e = 0; e < upto; ++e)
+      if (ex[e] == tkn) return true;
+    return false;
+  };
+  for (int j = 0; j < nb; ++j) {
+    const int c = first + j;
+    const int ne = a.without ? j : 0;
+    const float u = a.u[int64_t(b) * a.n + c];
+    float carry = 0.f;
+#pragma unroll
+    for (int t = 0; t < kPerLane; ++t) {
+      if (t < ngroup) {
+        incl[t] = wave_inclusive_scan(sv[t]) + carry;
+        carry = __shfl(incl[t], kWave - 1);
+      }
+    }
+    const float S = carry;
+    int y = 0;
+    if (!(S > 0.f)) {
+      while (drawn(y, ne)) ++y;
+    } else {
+      const float target = u * S;
+      int hit_seg = -1, last_pos = -1;
+      float carry_before = 0.f;
+#pragma unroll
+      for (int t = 0; t < kPerLane; ++t) {
+        if (t < ngroup && hit_seg < 0) {
+          const int c0 = t * kWave;
+          const bool valid = c0 + lane < nseg;
+          const uint64_t hit = wave_ballot(valid && incl[t] > target);
+          const uint64_t pos = wave_ballot(valid && sv[t] > 0.f);
+          if (hit) {
+            const int l = int(__builtin_ctzll(hit));
+            hit_seg = c0 + l;
+            carry_before = __shfl(incl[t] - sv[t], l);
+          } else if (pos) {
+            const int l = 63 - int(__builtin_clzll(pos));
+            last_pos = c0 + l;
+            carry_before = __shfl(incl[t] - sv[t], l);
+          }
+        }
+      }
+      const bool by_target = hit_seg >= 0;
+      const int sidx = by_target ? hit_seg : last_pos;
+      const int e0 = (sidx / kSegPerChunk) * kChunk + (sidx % kSegPerChunk) * kSegLen + lane * 8;
+      float wv[8], pw[8];
+      weights8<T>(desc, e0, vocab, sl2, vp, true, wv, pw);
+      float ls = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (ne > 0 && drawn(e0 + k, ne)) wv[k] = 0.f;
+        ls += wv[k];
+      }
+      const float inc = wave_inclusive_scan(ls);
+      const uint64_t hit = wave_ballot(by_target && carry_before + inc > target);
+      const uint64_t pos = wave_ballot(ls > 0.f);
+      int sel;
+      bool tgt;
+      if (hit) {
+        sel = int(__builtin_ctzll(hit));
+        tgt = true;
+      } else {
+        sel = pos ? 63 - int(__builtin_clzll(pos)) : 0;
+        tgt = false;
+      }
+      if (lane == sel) {
+        float cum = carry_before + inc - ls;
+        int pick = -1, lastp = -1;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          cum += wv[k];
+          if (wv[k] > 0.f) lastp = k;
+          if (tgt && pick < 0 && cum > target) pick = k;
+        }
+        if (pick < 0) pick = (lastp >= 0) ? lastp : 0;
+        y = e0 + pick;
+      }
+      y = __shfl(y, sel);
+    }
+    if (lane == 0) {
+      par[c] = v;
+      tok[c] = y;
+      ex[j] = y;
+    }
+    __syncthreads();
+    if (a.without && j + 1 < nb && y < vocab) {
+      // the drawn token's segment, recomputed with every drawn token zeroed
+      const int sy = (y / kChunk) * kSegPerChunk + (y % kChunk) / kSegLen;
+      const int s0 = (sy / kSegPerChunk) * kChunk + (sy % kSegPerChunk) * kSegLen + lane * 8;
+      float wv[8], pw[8];
+      weights8<T>(desc, s0, vocab, sl2, vp, true, wv, pw);
+      float ls = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) ls += drawn(s0 + k, j + 1) ? 0.f : wv[k];
+      const float m = wave_sum(ls);
+#pragma unroll
+      for (int t = 0; t < kPerLane; ++t)
+        if (t * kWave + lane == sy) sv[t] = m;
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_build(const TreeBuildArgs& a, hipStream_t stream) {
+  // the q rows as a row-sampler call: statistics, descriptors, segment masses
+  SampleRowsArgs s{};
+  s.dtype = a.dtype;
+  s.rows = a.batch * a.max_depth;
+  s.vocab = a.vocab;
+  s.logits = a.q;
+  s.row_stride = a.q_row;
+  s.per_seq = a.max_depth;
+  s.seq_stride = a.q_seq;
+  s.scale_log2 = a.scale_log2;
+  SrWs w = sr_ws(a.ws, s.rows, a.vocab);
+  const int ns = stats_splits(s.rows, a.vocab);
+  {
+    ProfileScope ps("uno_build_stats", stream);
+    hipLaunchKernelGGL(sr_stats_kernel<T>, dim3(s.rows, ns), dim3(kChunkThreads), 0, stream, s, w);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    ProfileScope ps("uno_build_desc", stream);
+    hipLaunchKernelGGL(sr_desc_kernel<T>, dim3(s.rows), dim3(kWave), 0, stream, s, w);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    ProfileScope ps("uno_build_seg", stream);
+    hipLaunchKernelGGL((draw_seg_kernel<T, false>), dim3(s.rows, num_chunks(a.vocab)), dim3(kChunkThreads), 0, stream,
+                       w.desc, a.vocab, a.scale_log2, w.seg);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int internal = 0, width = 1;
+  for (int d = 0; d < a.max_depth; ++d) {
+    internal += width;
+    width *= a.branching[d];
+  }
+  ProfileScope ps("uno_build_draw", stream);
+  hipLaunchKernelGGL(build_draw_kernel<T>, dim3(unsigned(internal), unsigned(a.batch)), dim3(kWave), 0, stream, a, w);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t sample_rows_workspace_bytes(int rows, int vocab) {
   const int ns = stats_splits(rows, vocab);
   return align_up(size_t(rows) * ns * sizeof(float2), 256) + align_up(size_t(rows) * sizeof(DrawDesc), 256) +
          draw_seg_bytes(rows, vocab);
+}
+
+size_t tree_build_workspace_bytes(int batch, int max_depth, int vocab) {
+  return sample_rows_workspace_bytes(batch * max_depth, vocab);
+}
+
+hipError_t launch_tree_build(const TreeBuildArgs& a, hipStream_t stream) {
+  return a.dtype == UNO_BF16 ? launch_build<uint16_t>(a, stream) : launch_build<float>(a, stream);
 }
 
 hipError_t launch_sample_rows(const SampleRowsArgs& a, hipStream_t stream) {

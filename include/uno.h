@@ -277,6 +277,45 @@ uno_status uno_psi_spec_verify_tree(hipStream_t stream, uno_dtype logit_dtype,
                                     int32_t* out_accept_len, int32_t* out_path, int32_t* out_token,
                                     void* workspace, size_t workspace_bytes);
 
+/* --------------------------------------------------------------------------
+ * Psi-Spec candidate tree from the per-depth draft marginals.
+ * Source: Uno summary (hyper.ai), section "方法", last paragraph (the tree
+ * sampler draws several candidates from the diffusion path's marginals and
+ * verifies them as a prefix tree).  The pages fix neither the shape nor the
+ * draw; this call builds a breadth-first tree with a budget per depth: every
+ * node at depth d (the root is depth 0) has branching[d] children; node ids
+ * run level by level, the children of one node consecutive.  The children of
+ * a depth-d node draw their tokens from q row d (the draft marginal of depth
+ * d + 1) at temperature T, child c with uniform u_draw[b][c], by the inverse
+ * CDF of every other draw (smallest v with cumsum(q)_v > u * sum(q)):
+ *   without_replacement = 0: siblings are independent draws (duplicates
+ *     possible) -- verify with uno_psi_spec_verify_tree;
+ *   without_replacement = 1: sibling j draws from q with the tokens of the
+ *     earlier siblings removed and the rest renormalised; if no mass is left
+ *     (every token of positive mass drawn) the token is the smallest id not
+ *     drawn yet, so siblings are distinct -- verify with
+ *     uno_psi_spec_verify_tree_wor.
+ *
+ * branching: HOST int32 [max_depth], each in [1, 64] (<= vocab without
+ *   replacement); n_tree must equal 1 + sum_d prod_{i<=d} branching[i] and be
+ *   at most 1024.
+ * q_logits: q row d of tree b at q_logits + b * q_seq_stride + d * q_row_stride
+ *   elements (bf16 or fp32), q_row_stride >= vocab, q_seq_stride >= 0 (the
+ *   noisy rows of a decode step's logits can be passed in place).
+ * u_draw f32 [batch][n_tree] in [0, 1) (entry 0 of each tree unused).
+ * Outputs int32 [batch][n_tree]: out_parent (parent[0] = -1), out_tokens
+ *   (tokens[0] = -1: the root's token is the caller's).
+ * 1 <= batch <= 65535, 1 <= max_depth <= 64, 1 <= vocab <= 2^20, T > 0;
+ * workspace from the query (row statistics, draw descriptors, segment
+ * masses).
+ * ------------------------------------------------------------------------ */
+uno_status uno_psi_spec_build_tree_workspace(int32_t batch, int32_t max_depth, int32_t vocab, size_t* bytes);
+uno_status uno_psi_spec_build_tree(hipStream_t stream, uno_dtype logit_dtype, int32_t batch, int32_t max_depth,
+                                   const int32_t* branching, int32_t vocab, const void* q_logits,
+                                   int64_t q_seq_stride, int64_t q_row_stride, const float* u_draw, int32_t n_tree,
+                                   float temperature, int32_t without_replacement, int32_t* out_parent,
+                                   int32_t* out_tokens, void* workspace, size_t workspace_bytes);
+
 /* ==========================================================================
  * The composed decode step.  Source: Uno summary (hyper.ai), section 方法
  * (one forward over the concatenated clean and noisy rows of a block, the

@@ -19,6 +19,9 @@ are drawn.  Readings:
 * Without replacement: sibling j draws from q with the tokens of siblings
   1..j-1 removed and the rest renormalised (no duplicates); it needs the
   verifier that removes the same tokens (verify_tree(without_replacement=True)).
+  When every token of positive mass has been drawn already (the remaining
+  mass is zero; the pages have no such case), the draw is the smallest token
+  id not drawn yet, so siblings stay distinct.
 """
 
 import numpy as np
@@ -49,6 +52,9 @@ def draw_without(q, removed, u):
     w = np.asarray(q, dtype=np.float64).copy()
     for t in removed:
         w[int(t)] = 0.0
+    if not np.sum(w) > 0.0:
+        taken = {int(t) for t in removed}
+        return next(v for v in range(w.size) if v not in taken)
     return inverse_cdf(w, u)
 
 

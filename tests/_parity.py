@@ -237,3 +237,49 @@ def check_linear_sampled(case_rows, gpu, seqs, k, temperature, top_k, top_p, gre
             assert draw_is_valid(w, us, yg, tie), f"seq {b}: token gpu {yg} oracle {yo} (L={Lo})"
             ties += 1
     return ties
+
+
+def check_tree_build(q_logits, branching, u_draw, parent_gpu, tokens_gpu, temperature, without, tie=TIE):
+    """Compare GPU-built trees with oracle.build_tree.
+
+    q_logits [B, D, V] host values the GPU drew from; u_draw [B, n];
+    parent_gpu, tokens_gpu [B, n] host arrays.  The parent arrays must equal
+    the oracle's layout.  A token must equal the oracle's draw from the same
+    reduced row -- q without the GPU's own earlier siblings when drawing
+    without replacement -- except where u lies within `tie` of a CDF
+    boundary of that row (counted and returned).  Without replacement the
+    siblings must be distinct."""
+    parent_ref, depth = oracle.tree_layout(branching)
+    bsz, n = np.asarray(tokens_gpu).shape
+    assert n == parent_ref.size
+    ties = 0
+    for b in range(bsz):
+        assert list(parent_gpu[b]) == parent_ref.tolist(), f"tree {b}: parent array differs from the layout"
+        assert int(tokens_gpu[b, 0]) == -1
+        q = [oracle.softmax_rows(np.asarray(r, np.float64), temperature) for r in q_logits[b]]
+        _, ref_tok = oracle.build_tree(q_logits[b], branching, u_draw[b], temperature, without)
+        same = True
+        kids = oracle.children_lists(parent_ref)
+        for v in range(n):
+            sib = kids[v]
+            got_before = []
+            for c in sib:
+                d = int(depth[c]) - 1
+                y = int(tokens_gpu[b, c])
+                removed = got_before if without else []
+                ref = oracle.draw_without(q[d], removed, u_draw[b, c]) if without else oracle.inverse_cdf(q[d], u_draw[b, c])
+                if y != ref:
+                    w = q[d].copy()
+                    for t in removed:
+                        w[int(t)] = 0.0
+                    assert w.sum() > 0.0 and draw_is_valid(w, float(u_draw[b, c]), y, tie), \
+                        f"tree {b} node {c}: gpu {y} oracle {ref} (removed {removed})"
+                    ties += 1
+                    same = False
+                got_before.append(y)
+            if without:
+                toks = [int(tokens_gpu[b, c]) for c in sib]
+                assert len(set(toks)) == len(toks), f"tree {b} node {v}: repeated sibling tokens {toks}"
+        if same:
+            assert np.array_equal(np.asarray(tokens_gpu[b]), ref_tok), f"tree {b}: tokens differ from build_tree"
+    return ties

@@ -94,6 +94,19 @@ int main() {
                                             D, (const float*)D, (const float*)D, 1.f, (int32_t*)D, (int32_t*)D,
                                             (int32_t*)D, D, big), false);
 
+  // tree construction (branching is a host array read by the call)
+  const int32_t br[3] = {4, 2, 2};   // 1 + 4 + 8 + 16 = 29 nodes
+  const int32_t br_bad[3] = {4, 0, 2};
+  expect("build ws", uno_psi_spec_build_tree_workspace(2, 3, V, &bytes), true);
+  expect("build", uno_psi_spec_build_tree(s, UNO_BF16, 2, 3, br, V, D, 3 * V, V, (const float*)D, 29, 1.f, 1,
+                                          (int32_t*)D, (int32_t*)D, D, big), true);
+  expect("build n", uno_psi_spec_build_tree(s, UNO_BF16, 2, 3, br, V, D, 3 * V, V, (const float*)D, 30, 1.f, 0,
+                                            (int32_t*)D, (int32_t*)D, D, big), false);
+  expect("build branch", uno_psi_spec_build_tree(s, UNO_BF16, 2, 3, br_bad, V, D, 3 * V, V, (const float*)D, 29,
+                                                 1.f, 0, (int32_t*)D, (int32_t*)D, D, big), false);
+  expect("build null", uno_psi_spec_build_tree(s, UNO_BF16, 2, 3, nullptr, V, D, 3 * V, V, (const float*)D, 29,
+                                               1.f, 0, (int32_t*)D, (int32_t*)D, D, big), false);
+
   // layer ops
   expect("norm", uno_rms_norm(s, 16, 256, D, 256, nullptr, 0, nullptr, 0, D, 1e-6f, D, 256), true);
   expect("norm dim", uno_rms_norm(s, 16, 0, D, 256, nullptr, 0, nullptr, 0, D, 1e-6f, D, 256), false);

@@ -26,6 +26,7 @@ size_t gated_lora_workspace_bytes(uno_dtype, int64_t, int64_t, int64_t, int64_t)
 size_t lora_down_part_bytes(int64_t, int64_t, int64_t) { return 256; }
 size_t sample_rows_workspace_bytes(int, int) { return 256; }
 size_t tree_attention_workspace_bytes(int, int, int, int, int, int) { return 256; }
+size_t tree_build_workspace_bytes(int, int, int) { return 256; }
 size_t tree_verify_workspace_bytes(int, int, int, int, int) { return 256; }
 size_t verify_linear_workspace_bytes(int, int, int) { return 256; }
 size_t verify_linear_sampled_workspace_bytes(int, int, int) { return 256; }
@@ -48,6 +49,7 @@ hipError_t launch_silu_mul(const SiluMulArgs&, hipStream_t) { return launched();
 hipError_t launch_step_finish(const StepFinishArgs&, hipStream_t) { return launched(); }
 hipError_t launch_step_setup(const StepSetupArgs&, hipStream_t) { return launched(); }
 hipError_t launch_tree_attention(const TreeAttnArgs&, hipStream_t) { return launched(); }
+hipError_t launch_tree_build(const TreeBuildArgs&, hipStream_t) { return launched(); }
 hipError_t launch_tree_verify(const TreeVerifyArgs&, hipStream_t) { return launched(); }
 hipError_t launch_verify_linear(const VerifyLinearArgs&, hipStream_t) { return launched(); }
 hipError_t launch_verify_linear_sampled(const VerifyLinearArgs&, int, float, int, hipStream_t) { return launched(); }

@@ -268,6 +268,37 @@ def test_sample_rows_rejects_bad_calls(lib):
     assert call(wsb=4) == WORKSPACE
 
 
+def test_build_tree_rejects_bad_calls(lib):
+    ws = ctypes.c_size_t(0)
+    assert lib.uno_psi_spec_build_tree_workspace(256, 15, 151936, ctypes.byref(ws)) == OK
+    assert ws.value > 0
+    assert lib.uno_psi_spec_build_tree_workspace(0, 3, 100, ctypes.byref(ws)) == INVALID
+    assert lib.uno_psi_spec_build_tree_workspace(1, 65, 100, ctypes.byref(ws)) == INVALID
+
+    def call(br=(4, 2, 2), **kw):
+        a = dict(dtype=BF16, batch=2, D=len(br), V=100, q=FAKE16, qs=300, qr=100, u=FAKE16, n=29, T=1.0, wor=0,
+                 par=FAKE16, tok=FAKE16, ws=FAKE16, wsb=1 << 20)
+        a.update(kw)
+        arr = (ctypes.c_int32 * max(len(br), 1))(*br)
+        return lib.uno_psi_spec_build_tree(None, a["dtype"], a["batch"], a["D"], arr if br is not None else None,
+                                           a["V"], a["q"], a["qs"], a["qr"], a["u"], a["n"], a["T"], a["wor"],
+                                           a["par"], a["tok"], a["ws"], a["wsb"])
+    assert call(dtype=7) == INVALID
+    assert call(batch=0) == INVALID
+    assert call(batch=65536) == INVALID
+    assert call(n=28) == INVALID                         # 1 + 4 + 8 + 16 = 29
+    assert call(br=(4, 0, 2)) == INVALID
+    assert call(br=(65,), n=66) == INVALID               # at most 64 children per node
+    assert call(br=(8, 8, 8, 8), n=1 + 8 + 64 + 512 + 4096) == UNSUPPORTED
+    assert call(br=(5,), n=6, V=4, qr=4, wor=1) == INVALID   # distinct siblings need vocab >= branching
+    assert call(wor=2) == INVALID
+    assert call(qr=99) == INVALID
+    assert call(qs=-1) == INVALID
+    assert call(u=None) == INVALID
+    assert call(T=float("nan")) == INVALID
+    assert call(wsb=16) == WORKSPACE
+
+
 def test_decoder_layer_rejects_bad_calls(lib):
     ws = ctypes.c_size_t(0)
     assert lib.uno_decoder_layer_workspace(128, 16, 8192, 4096, 12288, 32, 8, 128, ctypes.byref(ws)) == OK

@@ -191,3 +191,19 @@ def test_build_then_verify_with_replacement_matches_the_iid_law():
         f = _token_of(ql, [3], node, u0, False)
         cdf = [float(_bisect(lambda us, v=v: f(us) <= v, 1)[0]) for v in range(V)]
         np.testing.assert_allclose(np.diff([0.0] + cdf), q, rtol=0, atol=1e-12)
+
+
+def test_without_replacement_past_the_support_takes_the_smallest_free_id():
+    """A q row with all its mass on two tokens (the rest underflows to exactly
+    0 in float64): without replacement the first two siblings take those two
+    tokens in inverse-CDF order, the next ones the smallest ids not taken yet;
+    with replacement every sibling stays inside the support."""
+    V = 6
+    ql = np.full((1, V), -1.0e4)
+    ql[0, 3] = 0.0
+    ql[0, 5] = 0.0                      # q = 1/2 on tokens 3 and 5
+    u = np.array([0.0, 0.7, 0.9, 0.1, 0.5, 0.2])
+    _, tok = oracle.build_tree(ql, [5], u, without_replacement=True)
+    assert tok.tolist() == [-1, 5, 3, 0, 1, 2]
+    _, tok = oracle.build_tree(ql, [5], u, without_replacement=False)
+    assert tok.tolist() == [-1, 5, 5, 3, 5, 3]

@@ -23,6 +23,7 @@ _T_P, _T_Q, _T_DRAFT, _T_UACC, _T_US = 21, 22, 23, 24, 25
 _T_ATT_Q, _T_ATT_KC, _T_ATT_VC, _T_ATT_KT, _T_ATT_VT = 31, 32, 33, 34, 35
 _T_TREE_SHAPE, _T_TREE_BASE, _T_TREE_P, _T_TREE_Q, _T_TREE_TOK = 41, 42, 43, 44, 45
 _T_TREE_UACC, _T_TREE_US = 46, 47
+_T_BUILD_U = 48
 
 
 def rng_for(seed, *tags):
@@ -305,6 +306,48 @@ def tree_verify_case(parent, vocab, dtype="bf16", seed=0, base_std=2.0, node_std
             "temperature": temperature, "parent": np.tile(parent, (batch, 1)),
             "tokens": tokens, "p": p_st, "q": q_st, "p_f32": p_f, "q_f32": q_f,
             "u_acc": u_acc, "u_s": u_s}
+
+
+def level_depths(branching):
+    """Depth of every node of the breadth-first tree with `branching[d]`
+    children per depth-d node (root depth 0), in node-id order."""
+    depth = [0]
+    width = 1
+    for d, b in enumerate(branching):
+        width *= int(b)
+        depth += [d + 1] * width
+    return np.asarray(depth, dtype=np.int64)
+
+
+def tree_build_case(batch, branching, vocab, dtype="bf16", seed=0, base_std=2.0, node_std=0.5, q_std=0.5):
+    """Inputs of the candidate-tree construction and of the verify of the
+    built tree, with the distributions of tree_verify_case: base_d ~
+    N(0, base_std^2); the draft marginal of depth d (q row d - 1) is base_d +
+    N(0, q_std^2); the AR row of a node at depth d is base_{d+1} +
+    N(0, node_std^2).  u_draw [B, n] (entry 0 unused), u_acc [B, n], u_s [B]
+    float32 in [0, 1)."""
+    depth = level_depths(branching)
+    n = depth.size
+    dmax = len(branching)
+    store_dt = np.uint16 if dtype == "bf16" else np.float32
+    q_st = np.empty((batch, dmax, vocab), dtype=store_dt)
+    q_f = np.empty((batch, dmax, vocab), dtype=np.float32)
+    p_st = np.empty((batch, n, vocab), dtype=store_dt)
+    p_f = np.empty((batch, n, vocab), dtype=np.float32)
+    for b in range(batch):
+        base = [rng_for(seed, _T_TREE_BASE, b, d).standard_normal(vocab, dtype=np.float32)
+                * np.float32(base_std) for d in range(dmax + 2)]
+        for d in range(1, dmax + 1):
+            lq = base[d] + rng_for(seed, _T_TREE_Q, b, d).standard_normal(vocab, dtype=np.float32) * np.float32(q_std)
+            q_st[b, d - 1], q_f[b, d - 1] = _store(lq, dtype)
+        for i in range(n):
+            lp = base[depth[i] + 1] + rng_for(seed, _T_TREE_P, b, i).standard_normal(vocab, dtype=np.float32) * np.float32(node_std)
+            p_st[b, i], p_f[b, i] = _store(lp, dtype)
+    return {"batch": batch, "n": n, "max_depth": dmax, "vocab": vocab, "dtype": dtype, "branching": list(branching),
+            "q": q_st, "q_f32": q_f, "p": p_st, "p_f32": p_f,
+            "u_draw": rng_for(seed, _T_BUILD_U).random((batch, n), dtype=np.float32),
+            "u_acc": rng_for(seed, _T_TREE_UACC).random((batch, n), dtype=np.float32),
+            "u_s": rng_for(seed, _T_TREE_US).random(batch, dtype=np.float32)}
 
 
 # ------------------------------------------------------------ named workloads
