@@ -23,6 +23,7 @@ EXPORTS = (
     "uno_psi_spec_verify_linear_sampled_workspace", "uno_psi_spec_verify_linear_sampled",
     "uno_tree_verify_attention_workspace", "uno_tree_verify_attention",
     "uno_psi_spec_verify_tree_workspace", "uno_psi_spec_verify_tree",
+    "uno_psi_spec_verify_tree_wor_workspace", "uno_psi_spec_verify_tree_wor",
     "uno_psi_spec_build_tree_workspace", "uno_psi_spec_build_tree",
     "uno_rms_norm", "uno_rope", "uno_silu_mul",
     "uno_block_verify_attention_workspace", "uno_block_verify_attention",
@@ -97,6 +98,10 @@ def _declare(lib):
         "uno_psi_spec_verify_tree_workspace": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
         "uno_psi_spec_verify_tree": (ctypes.c_int, [_p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32,
                                                     _p, _p, _p, _p, _p, _p, _f32, _p, _p, _p, _p, _sz]),
+        "uno_psi_spec_verify_tree_wor_workspace": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32,
+                                                                  ctypes.POINTER(_sz)]),
+        "uno_psi_spec_verify_tree_wor": (ctypes.c_int, [_p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32,
+                                                        _p, _p, _p, _p, _p, _p, _f32, _p, _p, _p, _p, _sz]),
         "uno_psi_spec_build_tree_workspace": (ctypes.c_int, [_i32, _i32, _i32, ctypes.POINTER(_sz)]),
         "uno_psi_spec_build_tree": (ctypes.c_int, [_p, ctypes.c_int, _i32, _i32, _p, _i32, _p, _i64, _i64, _p, _i32,
                                                    _f32, _i32, _p, _p, _p, _sz]),
@@ -368,21 +373,22 @@ def tree_verify_attention(q, k_cache, v_cache, k_tree, v_tree, parent, softmax_s
 
 
 # ------------------------------------------------------------------ tree verify
-def psi_spec_verify_tree_workspace(batch, n_tree, max_depth, max_children, vocab):
+def psi_spec_verify_tree_workspace(batch, n_tree, max_depth, max_children, vocab, without_replacement=False):
     load()
     out = _sz(0)
-    _check(_lib.uno_psi_spec_verify_tree_workspace(batch, n_tree, max_depth, max_children, vocab,
-                                                   ctypes.byref(out)))
+    fn = _lib.uno_psi_spec_verify_tree_wor_workspace if without_replacement else _lib.uno_psi_spec_verify_tree_workspace
+    _check(fn(batch, n_tree, max_depth, max_children, vocab, ctypes.byref(out)))
     return out.value
 
 
 def psi_spec_verify_tree(parent, tokens, p_logits, q_logits, u_accept, u_sample, temperature=1.0,
-                         max_children=None, outputs=None, workspace=None, stream=None):
-    """Tree Psi-Spec verify (uno_psi_spec_verify_tree).
+                         max_children=None, outputs=None, workspace=None, stream=None, without_replacement=False):
+    """Tree Psi-Spec verify (uno_psi_spec_verify_tree, or
+    uno_psi_spec_verify_tree_wor for siblings drawn without replacement).
 
     parent, tokens int32 [B, n]; p_logits [B, n, V]; q_logits [B, D, V]
     (contiguous); u_accept f32 [B, n]; u_sample f32 [B].  max_children: bound
-    on the children of any node (None: n - 1).
+    on the children of any node (None: n - 1, at most 64 without replacement).
     Returns dict: accept_len [B], path [B, D], token [B] (int32 device tensors).
     """
     import torch
@@ -392,14 +398,18 @@ def psi_spec_verify_tree(parent, tokens, p_logits, q_logits, u_accept, u_sample,
     dev = p_logits.device
     if max_children is None:
         max_children = max(n - 1, 0)
+        if without_replacement:
+            max_children = min(max_children, 64)
     if outputs is None:
         outputs = {
             "accept_len": torch.empty(bsz, dtype=torch.int32, device=dev),
             "path": torch.empty((bsz, dmax), dtype=torch.int32, device=dev),
             "token": torch.empty(bsz, dtype=torch.int32, device=dev),
         }
-    ws = _workspace(psi_spec_verify_tree_workspace(bsz, n, dmax, max_children, vocab), dev, workspace)
-    _check(_lib.uno_psi_spec_verify_tree(
+    ws = _workspace(psi_spec_verify_tree_workspace(bsz, n, dmax, max_children, vocab, without_replacement), dev,
+                    workspace)
+    fn = _lib.uno_psi_spec_verify_tree_wor if without_replacement else _lib.uno_psi_spec_verify_tree
+    _check(fn(
         _stream(stream), _dtype_code(p_logits), bsz, n, dmax, max_children, vocab,
         _ptr(parent), _ptr(tokens), _ptr(p_logits), _ptr(q_logits), _ptr(u_accept), _ptr(u_sample),
         float(temperature), _ptr(outputs["accept_len"]), _ptr(outputs["path"]), _ptr(outputs["token"]),

@@ -444,34 +444,35 @@ static uno_status check_tree_verify_shape(int32_t batch, int32_t n_tree, int32_t
   return UNO_OK;
 }
 
-uno_status uno_psi_spec_verify_tree_workspace(int32_t batch, int32_t n_tree, int32_t max_depth, int32_t max_children,
-                                              int32_t vocab, size_t* bytes) {
-  UNO_GUARD_BEGIN
+static uno_status tree_workspace(int32_t batch, int32_t n_tree, int32_t max_depth, int32_t max_children,
+                                 int32_t vocab, int wor, size_t* bytes) {
   if (!bytes) return fail(UNO_ERR_INVALID_ARGUMENT, "bytes is NULL");
   uno_status s = check_tree_verify_shape(batch, n_tree, max_depth, max_children, vocab);
   if (s != UNO_OK) return s;
-  *bytes = tree_verify_workspace_bytes(batch, n_tree, max_depth, max_children, vocab);
+  if (wor && max_children > 64)
+    return fail(UNO_ERR_UNSUPPORTED, "without replacement: max_children above 64 (got %d)", max_children);
+  *bytes = tree_verify_workspace_bytes(batch, n_tree, max_depth, max_children, vocab, wor);
   return UNO_OK;
-  UNO_GUARD_END
 }
 
-uno_status uno_psi_spec_verify_tree(hipStream_t stream, uno_dtype logit_dtype, int32_t batch, int32_t n_tree,
-                                    int32_t max_depth, int32_t max_children, int32_t vocab, const int32_t* parent,
-                                    const int32_t* tokens, const void* p_logits, const void* q_logits,
-                                    const float* u_accept, const float* u_sample, float temperature,
-                                    int32_t* out_accept_len, int32_t* out_path, int32_t* out_token, void* workspace,
-                                    size_t workspace_bytes) {
-  UNO_GUARD_BEGIN
+static uno_status verify_tree(hipStream_t stream, uno_dtype logit_dtype, int32_t batch, int32_t n_tree,
+                              int32_t max_depth, int32_t max_children, int32_t vocab, const int32_t* parent,
+                              const int32_t* tokens, const void* p_logits, const void* q_logits,
+                              const float* u_accept, const float* u_sample, float temperature,
+                              int32_t* out_accept_len, int32_t* out_path, int32_t* out_token, void* workspace,
+                              size_t workspace_bytes, int wor, const char* name) {
   if (logit_dtype != UNO_F32 && logit_dtype != UNO_BF16)
     return fail(UNO_ERR_INVALID_ARGUMENT, "unknown dtype %d", int(logit_dtype));
   uno_status s = check_tree_verify_shape(batch, n_tree, max_depth, max_children, vocab);
   if (s != UNO_OK) return s;
+  if (wor && max_children > 64)
+    return fail(UNO_ERR_UNSUPPORTED, "without replacement: max_children above 64 (got %d)", max_children);
   if (!parent || !tokens || !p_logits || !q_logits || !u_accept || !u_sample || !out_accept_len || !out_path ||
       !out_token)
     return fail(UNO_ERR_INVALID_ARGUMENT, "required pointer is NULL");
   if (!(temperature > 0.f) || !std::isfinite(temperature))
     return fail(UNO_ERR_INVALID_ARGUMENT, "temperature must be finite and > 0");
-  const size_t need = tree_verify_workspace_bytes(batch, n_tree, max_depth, max_children, vocab);
+  const size_t need = tree_verify_workspace_bytes(batch, n_tree, max_depth, max_children, vocab, wor);
   if (workspace_bytes < need || !workspace)
     return fail(UNO_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
   TreeVerifyArgs a{};
@@ -493,13 +494,53 @@ uno_status uno_psi_spec_verify_tree(hipStream_t stream, uno_dtype logit_dtype, i
   a.out_tok = out_token;
   a.ws = workspace;
   a.ws_bytes = workspace_bytes;
+  a.wor = wor;
   if (debug_checks()) {   // node tokens (the root's is unused) and the uniforms
     uno_status d = debug_check_ids(stream, tokens, batch, n_tree, n_tree, 1, 0, vocab, "tokens");
     if (d == UNO_OK) d = debug_check_unit(stream, u_accept, int64_t(batch) * n_tree, "u_accept");
     if (d == UNO_OK) d = debug_check_unit(stream, u_sample, batch, "u_sample");
     if (d != UNO_OK) return d;
   }
-  return check_hip(launch_tree_verify(a, stream), "uno_psi_spec_verify_tree launch");
+  return check_hip(launch_tree_verify(a, stream), name);
+}
+
+uno_status uno_psi_spec_verify_tree_workspace(int32_t batch, int32_t n_tree, int32_t max_depth, int32_t max_children,
+                                              int32_t vocab, size_t* bytes) {
+  UNO_GUARD_BEGIN
+  return tree_workspace(batch, n_tree, max_depth, max_children, vocab, 0, bytes);
+  UNO_GUARD_END
+}
+
+uno_status uno_psi_spec_verify_tree(hipStream_t stream, uno_dtype logit_dtype, int32_t batch, int32_t n_tree,
+                                    int32_t max_depth, int32_t max_children, int32_t vocab, const int32_t* parent,
+                                    const int32_t* tokens, const void* p_logits, const void* q_logits,
+                                    const float* u_accept, const float* u_sample, float temperature,
+                                    int32_t* out_accept_len, int32_t* out_path, int32_t* out_token, void* workspace,
+                                    size_t workspace_bytes) {
+  UNO_GUARD_BEGIN
+  return verify_tree(stream, logit_dtype, batch, n_tree, max_depth, max_children, vocab, parent, tokens, p_logits,
+                     q_logits, u_accept, u_sample, temperature, out_accept_len, out_path, out_token, workspace,
+                     workspace_bytes, 0, "uno_psi_spec_verify_tree launch");
+  UNO_GUARD_END
+}
+
+uno_status uno_psi_spec_verify_tree_wor_workspace(int32_t batch, int32_t n_tree, int32_t max_depth,
+                                                  int32_t max_children, int32_t vocab, size_t* bytes) {
+  UNO_GUARD_BEGIN
+  return tree_workspace(batch, n_tree, max_depth, max_children, vocab, 1, bytes);
+  UNO_GUARD_END
+}
+
+uno_status uno_psi_spec_verify_tree_wor(hipStream_t stream, uno_dtype logit_dtype, int32_t batch, int32_t n_tree,
+                                        int32_t max_depth, int32_t max_children, int32_t vocab, const int32_t* parent,
+                                        const int32_t* tokens, const void* p_logits, const void* q_logits,
+                                        const float* u_accept, const float* u_sample, float temperature,
+                                        int32_t* out_accept_len, int32_t* out_path, int32_t* out_token,
+                                        void* workspace, size_t workspace_bytes) {
+  UNO_GUARD_BEGIN
+  return verify_tree(stream, logit_dtype, batch, n_tree, max_depth, max_children, vocab, parent, tokens, p_logits,
+                     q_logits, u_accept, u_sample, temperature, out_accept_len, out_path, out_token, workspace,
+                     workspace_bytes, 1, "uno_psi_spec_verify_tree_wor launch");
   UNO_GUARD_END
 }
 

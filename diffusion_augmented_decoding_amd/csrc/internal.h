@@ -258,8 +258,9 @@ struct TreeVerifyArgs {
   int32_t* out_path;
   int32_t* out_tok;
   void* ws; size_t ws_bytes;
+  int wor;   // siblings drawn without replacement (max_children <= 64)
 };
-size_t tree_verify_workspace_bytes(int batch, int n_tree, int max_depth, int max_children, int vocab);
+size_t tree_verify_workspace_bytes(int batch, int n_tree, int max_depth, int max_children, int vocab, int wor);
 hipError_t launch_tree_verify(const TreeVerifyArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- row sampler

@@ -31,6 +31,24 @@
 //     (a chunk's F, a tree's walk result, a segment mass) are single words,
 //     written and read with device-scope atomic stores and loads, and each is
 //     its own ready flag (a sentinel until written).
+//
+// Siblings drawn without replacement (recursive rejection sampling without
+// replacement, Jeon et al. 2024): sibling j is tested against q_j, q with the
+// tokens of siblings 1..j-1 removed and renormalised by Z_j = 1 - (their q
+// mass), and a rejection subtracts q_j.  With C_0 = 0, D_0 = 1 the residual
+// after j rejections is r_j = rho_j / D_j with
+//     rho_j(v) = max(0, p_v - C_j q_v)          for v not removed,
+//     rho_j(t_k) = max(0, p_{t_k} - C_k q_{t_k}) for the token of sibling k <= j
+//                                                 (first occurrence),
+//     C_j = C_{j-1} + D_{j-1} / Z_j,   D_j = sum_v rho_j(v)
+//         = F(C_j) + sum_{k<j} [max(0, p_{t_k} - C_k q_{t_k}) - max(0, p_{t_k} - C_j q_{t_k})],
+// a zero D_j freezing (C, D) as before and a Z_j without mass (below kZEps)
+// leaving C unchanged.  The tokens of the siblings are inputs, so the (C, D)
+// sequence is again known before the walk: the rounds compute F(C_j) chunk-
+// parallel, and every replay adds the per-sibling corrections, one sibling
+// per lane.  The final draw's weights are rho of the last state: the segment
+// masses and the element scan put max(0, p - C_k q) in place of the common
+// weight at every removed token.
 #include "sampler_common.h"
 
 namespace uno {
@@ -58,14 +76,18 @@ struct TreeWs {
   int* err;          // a wait ran past kSpinMax (never expected)
   int* cnt;          // [batch]: nodes with children (0 for a malformed tree)
   int* list;         // [batch][n]: those nodes in increasing id
+  int* kids;         // without replacement: [batch][n][max_children] children in increasing id
+  float* ck;         // without replacement: [batch][64] C_k of the walk's last node
 };
+constexpr float kZEps = 1e-6f;   // a remaining draft mass below this is taken as none (fp32 resolves no less)
+constexpr int kMaxWorChildren = 64;
 constexpr int kMaxListTrees = 1024;   // trees whose node lists the flow launch indexes
 
 inline __host__ __device__ int tree_stat_splits(int batch, int n, int dmax, int vocab) {
   return stats_splits(batch * (n + dmax), vocab);
 }
 
-TreeWs tree_ws(void* base, int batch, int n, int dmax, int maxc, int vocab) {
+TreeWs tree_ws(void* base, int batch, int n, int dmax, int maxc, int vocab, int wor) {
   const int nc = num_chunks(vocab);
   const int ns = tree_stat_splits(batch, n, dmax, vocab);
   char* p = static_cast<char*>(base);
@@ -88,6 +110,14 @@ TreeWs tree_ws(void* base, int batch, int n, int dmax, int maxc, int vocab) {
   w.cnt = reinterpret_cast<int*>(p);
   p += align_up(size_t(batch) * sizeof(int), 256);
   w.list = reinterpret_cast<int*>(p);
+  p += align_up(size_t(batch) * n * sizeof(int), 256);
+  w.kids = nullptr;
+  w.ck = nullptr;
+  if (wor) {
+    w.kids = reinterpret_cast<int*>(p);
+    p += align_up(size_t(batch) * n * (maxc > 0 ? maxc : 1) * sizeof(int), 256);
+    w.ck = reinterpret_cast<float*>(p);
+  }
   return w;
 }
 
@@ -123,7 +153,17 @@ __device__ __forceinline__ void tree_setup_body(const TreeVerifyArgs& a, const T
         ++d;
       }
       depth = (d <= a.max_depth) ? d : -1;
-      for (int u = v + 1; u < n; ++u) nchild += (par[u] == v);
+      if (a.wor) {   // the children in increasing id (at most max_children stored)
+        int* kl = w.kids + (int64_t(b) * n + v) * a.max_children;
+        for (int u = v + 1; u < n; ++u) {
+          if (par[u] == v) {
+            if (nchild < a.max_children) kl[nchild] = u;
+            ++nchild;
+          }
+        }
+      } else {
+        for (int u = v + 1; u < n; ++u) nchild += (par[u] == v);
+      }
       if (depth < 0 || nchild > a.max_children || (nchild > 0 && depth >= a.max_depth)) sh_bad = 1;
     }
     w.info[int64_t(b) * n + v] = NodeInfo{depth, nchild};
@@ -177,15 +217,18 @@ __global__ __launch_bounds__(kChunkThreads) void tree_stats_kernel(TreeVerifyArg
   const int nc = num_chunks(a.vocab);
   const int64_t nf = int64_t(a.max_children) * a.batch * a.n_tree * nc;
   const int64_t nseg = int64_t(a.batch) * nc * 2 * kSegPerChunk;
+  const int64_t nck = a.wor ? int64_t(a.batch) * kMaxWorChildren : 0;
   const int64_t stride = int64_t(ninit_blocks) * kChunkThreads;
-  for (int64_t t = int64_t(blk - nstat - a.batch) * kChunkThreads + threadIdx.x; t < nf + nseg + a.batch;
+  for (int64_t t = int64_t(blk - nstat - a.batch) * kChunkThreads + threadIdx.x; t < nf + nseg + a.batch + nck;
        t += stride) {
     if (t < nf)
       w.fpart[t] = kUnset;
     else if (t < nf + nseg)
       w.seg[t - nf] = kUnset;
-    else
+    else if (t < nf + nseg + a.batch)
       w.walk[t - nf - nseg] = kWalkUnset;
+    else
+      w.ck[t - nf - nseg - a.batch] = kUnset;
   }
   if (blk == nstat + a.batch && threadIdx.x == 0) {
     w.queue[0] = 0;
@@ -253,6 +296,119 @@ __device__ __forceinline__ float prob_at(const T* row, int t, const RowStat& s, 
   return fast_exp2(fmaf(load_logit<T>(row, t), sl2, -s.m)) / s.s;
 }
 
+// ---------------------------------------------------------------- without replacement
+// Child k (increasing id) of a node in lane k < m, by one whole wave: its id,
+// token, uniform, p and q at the token, and whether it is the first child with
+// that token (fi: the lane of the first one, for a repeated token; -1 else).
+struct Sib {
+  int ch, t, fi;
+  float p, q, u;
+  bool first;
+};
+template <typename T>
+__device__ __forceinline__ Sib load_sib(const TreeVerifyArgs& a, const TreeWs& w, int b, int node, int m,
+                                        const T* prow, const T* qrow, const RowStat& sp, const RowStat& sq) {
+  const int lane = threadIdx.x & (kWave - 1);
+  Sib s{-1, -1, -1, 0.f, 0.f, 1.f, false};
+  const bool in = lane < m;
+  if (in) {
+    s.ch = w.kids[(int64_t(b) * a.n_tree + node) * a.max_children + lane];
+    s.t = a.tokens[int64_t(b) * a.n_tree + s.ch];
+    s.u = a.u_acc[int64_t(b) * a.n_tree + s.ch];
+    if (s.t >= 0 && s.t < a.vocab) {
+      s.p = prob_at<T>(prow, s.t, sp, a.scale_log2);
+      s.q = prob_at<T>(qrow, s.t, sq, a.scale_log2);
+    }
+  }
+  const bool valid = in && s.t >= 0 && s.t < a.vocab;
+  for (int k = 0; k + 1 < m; ++k) {
+    const int tk = __shfl(s.t, k);
+    if (valid && k < lane && tk == s.t && s.fi < 0) s.fi = k;
+  }
+  s.first = valid && s.fi < 0;
+  return s;
+}
+
+struct WorState {
+  float C, D, Z;
+  bool frozen;
+};
+
+// The C at which the next rejection subtracts q (C_j from state j - 1).
+__device__ __forceinline__ float wor_next_c(const WorState& st) {
+  return (!st.frozen && st.Z > kZEps) ? st.C + st.D / st.Z : st.C;
+}
+
+// Rejection of sibling j (1-based, lane j - 1) with F = F(C_j) summed over the
+// vocabulary; ak (per lane): max(0, p - C_k q) of that lane's sibling once
+// removed.  Returns C_j, the C at which the sibling's token was removed.
+// Whole wave.
+__device__ __forceinline__ float wor_step(WorState& st, const Sib& s, int j, float F, float& ak) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int l = j - 1;
+  const bool fj = __shfl(s.first ? 1 : 0, l) != 0;
+  const float qj = __shfl(s.q, l);
+  if (!st.frozen) {
+    const float Cn = wor_next_c(st);
+    // tokens removed before: their rho stays at their own C_k (each term >= 0)
+    const float corr = wave_sum((lane < l && s.first) ? ak - fmaxf(fmaf(-Cn, s.q, s.p), 0.f) : 0.f);
+    const float Dn = F + corr;
+    if (Dn > 0.f) {
+      st.C = Cn;
+      st.D = Dn;
+    } else {
+      st.frozen = true;
+    }
+  }
+  if (lane == l && s.first) ak = fmaxf(fmaf(-st.C, s.q, s.p), 0.f);
+  if (fj) st.Z -= qj;
+  return st.C;
+}
+
+// Replacement weights of the removed tokens of a draw: lane k < m holds
+// max(0, p - C_k q) of its sibling's token when it is that token's first
+// occurrence.  Waits for the walk's C_k (published single words).
+template <typename T>
+__device__ __forceinline__ Sib wor_removed(const TreeVerifyArgs& a, const TreeWs& w, int b, int node, int depth,
+                                           float& repl) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int n = a.n_tree, rpb = n + a.max_depth;
+  const int ns = tree_stat_splits(a.batch, n, a.max_depth, a.vocab);
+  const int m = w.info[int64_t(b) * n + node].nchild;
+  Sib s{-1, -1, -1, 0.f, 0.f, 1.f, false};
+  repl = 0.f;
+  if (m == 0) return s;
+  const RowStat sp = wave_merge_chunks(w.part + (int64_t(b) * rpb + node) * ns, ns);
+  const RowStat sq = wave_merge_chunks(w.part + (int64_t(b) * rpb + n + depth) * ns, ns);
+  s = load_sib<T>(a, w, b, node, m, tree_row<T>(a, b, node), tree_row<T>(a, b, n + depth), sp, sq);
+  float ck = 0.f;
+  for (int it = 0;; ++it) {
+    ck = lane < m ? load_pub(w.ck + int64_t(b) * kMaxWorChildren + lane) : 0.f;
+    if (!wave_ballot(ck < 0.f)) break;
+    if (it == kSpinMax) {
+      if (lane == 0) atomicOr(w.err, 1);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  repl = s.first ? fmaxf(fmaf(-ck, s.q, s.p), 0.f) : 0.f;
+  return s;
+}
+
+// Puts the removed tokens' weights into the 8 weights of elements e0..e0+7.
+__device__ __forceinline__ void wor_patch(float (&wv)[8], int e0, const Sib& s, float repl, int m) {
+  for (int k = 0; k < m; ++k) {
+    const bool fk = __shfl(s.first ? 1 : 0, k) != 0;
+    const int tk = __shfl(s.t, k);
+    const float rk = __shfl(repl, k);
+    if (fk) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (tk == e0 + e) wv[e] = rk;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- flow items
 // Round j (1-based) of node node_idx, chunk c: F(c_j) of the chunk, with
 // (c_j, D_j) replayed from the node's earlier rounds.  Whole block.
@@ -281,7 +437,29 @@ __device__ void round_item(const TreeVerifyArgs& a, const TreeWs& w, int j, int 
       sh_st[1] = st[1];
     }
   }
-  if (wave == 0) {
+  if (a.wor) {   // the replay needs the rows' statistics for the siblings' probabilities
+    __syncthreads();
+    if (wave == 0) {
+      const Sib sb = load_sib<T>(a, w, b, i, inf.nchild, tree_row<T>(a, b, i), tree_row<T>(a, b, n + inf.depth),
+                                 sh_st[0], sh_st[1]);
+      WorState st{0.f, 1.f, 1.f, false};
+      float ak = 0.f;
+      const int64_t rs = int64_t(bn_total) * nc;
+      for (int t0 = 1; t0 < j && !st.frozen; t0 += kRoundBatch) {
+        const int cnt = min(kRoundBatch, j - t0);
+        float F[kRoundBatch];
+        wave_sums_published(w.fpart + (int64_t(t0 - 1) * bn_total + node_idx) * nc, rs, cnt, nc, w.err, F);
+#pragma unroll
+        for (int r = 0; r < kRoundBatch; ++r)
+          if (r < cnt && !st.frozen) wor_step(st, sb, t0 + r, F[r], ak);
+      }
+      if (lane == 0) {
+        sh_cd[0] = wor_next_c(st);
+        sh_cd[1] = 0.f;
+        sh_frozen = st.frozen ? 1 : 0;
+      }
+    }
+  } else if (wave == 0) {
     float cc = 0.f, D = 1.f;
     bool frozen = false;
     const int64_t rs = int64_t(bn_total) * nc;   // between rounds of one node
@@ -476,6 +654,86 @@ __device__ void walk_item(const TreeVerifyArgs& a, const TreeWs& w, int b) {
   for (int t = L + lane; t < a.max_depth; t += kWave) path_out[t] = -1;
 }
 
+// The walk of tree b with siblings drawn without replacement (one whole
+// wave): at each node the children sit one per lane; sibling j is accepted iff
+// u * q_j(t) < rho(t) / D, q_j(t) = q(t) / Z_j for a token not removed yet
+// (0 for a repeated one or when no draft mass is left), rho(t) at the
+// current C, or at C_k for a token first removed by sibling k.  The walk
+// publishes C_k of every child of its last node, then the draw.
+template <typename T>
+__device__ void walk_item_wor(const TreeVerifyArgs& a, const TreeWs& w, int b) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int n = a.n_tree, nc = num_chunks(a.vocab), rpb = n + a.max_depth;
+  const int ns = tree_stat_splits(a.batch, n, a.max_depth, a.vocab);
+  const int bn_total = a.batch * n;
+  int32_t* path_out = a.out_path + int64_t(b) * a.max_depth;
+  if (w.bad[b]) {
+    for (int t = lane; t < a.max_depth; t += kWave) path_out[t] = -1;
+    if (lane == 0) {
+      a.out_len[b] = -1;
+      __hip_atomic_store(w.walk + b, pack_walk(0.f, 0, 0, false, false), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
+  int cur = 0, depth = 0, L = 0;
+  while (true) {
+    const bool has_q = depth < a.max_depth;
+    const int m = w.info[int64_t(b) * n + cur].nchild;
+    WorState st{0.f, 1.f, 1.f, false};
+    float ak = 0.f, myck = 0.f;
+    bool accepted = false;
+    if (m > 0) {
+      RowStat sts[2];
+      wave_merge_two(w.part + (int64_t(b) * rpb + cur) * ns, w.part + (int64_t(b) * rpb + n + depth) * ns, ns, sts);
+      const Sib sb = load_sib<T>(a, w, b, cur, m, tree_row<T>(a, b, cur), tree_row<T>(a, b, n + depth), sts[0],
+                                 sts[1]);
+      float Fr[kRoundBatch];
+      wave_sums_published(w.fpart + (int64_t(b) * n + cur) * nc, int64_t(bn_total) * nc, min(m, kRoundBatch), nc,
+                          w.err, Fr);
+      for (int j = 1; j <= m && !accepted; ++j) {
+        const int l = j - 1;
+        const int t = __shfl(sb.t, l), ch = __shfl(sb.ch, l), fi = __shfl(sb.fi, l);
+        const float pt = __shfl(sb.p, l), qt = __shfl(sb.q, l), u = __shfl(sb.u, l);
+        const bool fj = __shfl(sb.first ? 1 : 0, l) != 0;
+        const float ck_first = __shfl(myck, fi >= 0 ? fi : 0);
+        const float qn = (fj && st.Z > kZEps) ? qt / st.Z : 0.f;
+        const float rho = fmaxf(fmaf(-(fj ? st.C : ck_first), qt, pt), 0.f);
+        if (t >= 0 && t < a.vocab && u * qn < rho / st.D) {
+          if (lane == 0) path_out[L] = ch;
+          ++L;
+          cur = ch;
+          ++depth;
+          accepted = true;
+        } else {
+          float F = 0.f;
+          if (!st.frozen) {
+            if (j <= kRoundBatch) {
+#pragma unroll
+              for (int r = 0; r < kRoundBatch; ++r)
+                if (r == l) F = Fr[r];
+            } else {
+              F = wave_sum_published(w.fpart + (int64_t(l) * bn_total + int64_t(b) * n + cur) * nc, nc, w.err);
+            }
+          }
+          const float ck = wor_step(st, sb, j, F, ak);
+          if (lane == l) myck = ck;
+        }
+      }
+    }
+    if (!accepted) {
+      if (lane < m) store_pub(w.ck + int64_t(b) * kMaxWorChildren + lane, myck);
+      if (lane == 0) {
+        a.out_len[b] = L;
+        __hip_atomic_store(w.walk + b, pack_walk(m > 0 ? st.C : 0.f, cur, depth, has_q, true), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+      break;
+    }
+  }
+  for (int t = L + lane; t < a.max_depth; t += kWave) path_out[t] = -1;
+}
+
 // Thread 0 waits for tree b's walk result; the whole block receives it.
 __device__ __forceinline__ uint64_t wait_walk(const TreeWs& w, int b) {
   __shared__ uint64_t sh_word;
@@ -510,12 +768,22 @@ __device__ void seg_item(const TreeVerifyArgs& a, const TreeWs& w, int b, int c)
   const bool vp = row_vec_ok(static_cast<const T*>(d.prow)), vq = row_vec_ok(static_cast<const T*>(d.qrow));
   constexpr int kSegPerWave = kSegPerChunk / (kChunkThreads / kWave);
   float* dst = w.seg + (int64_t(b) * nc + c) * (2 * kSegPerChunk);
+  // without replacement: the removed tokens' weights (every wave its own copy)
+  int wm = 0;
+  float repl = 0.f;
+  Sib sb{-1, -1, -1, 0.f, 0.f, 1.f, false};
+  if (a.wor) {
+    const int node = int((word >> 32) & 2047), depth = int((word >> 43) & 2047);
+    wm = w.info[int64_t(b) * a.n_tree + node].nchild;
+    sb = wor_removed<T>(a, w, b, node, depth, repl);
+  }
 #pragma unroll
   for (int q = 0; q < kSegPerWave; ++q) {
     const int k = wave * kSegPerWave + q;
     const int e0 = c * kChunk + k * kSegLen + lane * 8;
     float wv[8], pw[8];
     weights8<T, false>(d, e0, a.vocab, a.scale_log2, vp, vq, wv, pw);
+    if (wm > 0) wor_patch(wv, e0, sb, repl, wm);
     float sw = 0.f, sp = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -543,6 +811,14 @@ __device__ void resolve_item(const TreeVerifyArgs& a, const TreeWs& w, int b, ui
   DrawDesc d = walk_desc<T>(a, w, b, word);
   const int nc = num_chunks(a.vocab);
   const int nseg = nc * kSegPerChunk;
+  int wm = 0;
+  float repl = 0.f;
+  Sib sb{-1, -1, -1, 0.f, 0.f, 1.f, false};
+  if (a.wor) {
+    const int node = int((word >> 32) & 2047), depth = int((word >> 43) & 2047);
+    wm = w.info[int64_t(b) * a.n_tree + node].nchild;
+    sb = wor_removed<T>(a, w, b, node, depth, repl);
+  }
   const float* base = w.seg + int64_t(b) * nc * (2 * kSegPerChunk);
   auto segaddr = [&](int i, int which) {
     return base + (i / kSegPerChunk) * (2 * kSegPerChunk) + which * kSegPerChunk + (i % kSegPerChunk);
@@ -613,6 +889,7 @@ __device__ void resolve_item(const TreeVerifyArgs& a, const TreeWs& w, int b, ui
     float wv[8], pw[8];
     weights8<T, false>(d, e0, a.vocab, a.scale_log2, row_vec_ok(static_cast<const T*>(d.prow)),
                 row_vec_ok(static_cast<const T*>(d.qrow)), wv, pw);
+    if (wm > 0 && which == 0) wor_patch(wv, e0, sb, repl, wm);
     float ls = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) ls += wv[j];
@@ -696,7 +973,12 @@ __global__ __launch_bounds__(kChunkThreads) void tree_flow_kernel(TreeVerifyArgs
       }
       round_item<T>(a, w, j, node_idx, rem % nc);
     } else if (it < n_walk) {
-      if (threadIdx.x < kWave) walk_item<T>(a, w, it - n_round);
+      if (threadIdx.x < kWave) {
+        if (a.wor)
+          walk_item_wor<T>(a, w, it - n_round);
+        else
+          walk_item<T>(a, w, it - n_round);
+      }
     } else if (it < n_seg) {
       const int r = it - n_walk;
       seg_item<T>(a, w, r / nc, r % nc);
@@ -711,12 +993,12 @@ __global__ __launch_bounds__(kChunkThreads) void tree_flow_kernel(TreeVerifyArgs
 
 template <typename T>
 hipError_t launch_tree(const TreeVerifyArgs& a, hipStream_t stream) {
-  TreeWs w = tree_ws(a.ws, a.batch, a.n_tree, a.max_depth, a.max_children, a.vocab);
+  TreeWs w = tree_ws(a.ws, a.batch, a.n_tree, a.max_depth, a.max_children, a.vocab, a.wor);
   const int ns = tree_stat_splits(a.batch, a.n_tree, a.max_depth, a.vocab);
   const int nc = num_chunks(a.vocab);
   const int nstat = a.batch * (a.n_tree + a.max_depth) * ns;
   const int64_t init = int64_t(a.max_children) * a.batch * a.n_tree * nc + int64_t(a.batch) * nc * 2 * kSegPerChunk +
-                       a.batch;
+                       a.batch + (a.wor ? int64_t(a.batch) * kMaxWorChildren : 0);
   const int ninit = int(std::min<int64_t>(64, (init + kChunkThreads - 1) / kChunkThreads));
   {
     ProfileScope ps("uno_tree_stats", stream);
@@ -736,14 +1018,18 @@ hipError_t launch_tree(const TreeVerifyArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-size_t tree_verify_workspace_bytes(int batch, int n, int dmax, int maxc, int vocab) {
+size_t tree_verify_workspace_bytes(int batch, int n, int dmax, int maxc, int vocab, int wor) {
   const int nc = num_chunks(vocab);
   const int ns = tree_stat_splits(batch, n, dmax, vocab);
-  return align_up(size_t(batch) * n * sizeof(NodeInfo), 256) + align_up(size_t(batch) * sizeof(int), 256) +
-         align_up(size_t(batch) * (n + dmax) * ns * sizeof(float2), 256) +
-         align_up(size_t(maxc > 0 ? maxc : 1) * batch * n * nc * sizeof(float), 256) +
-         align_up(size_t(batch) * sizeof(uint64_t), 256) + draw_seg_bytes(batch, vocab) + 256 +
-         align_up(size_t(batch) * sizeof(int), 256) + align_up(size_t(batch) * n * sizeof(int), 256);
+  size_t bytes = align_up(size_t(batch) * n * sizeof(NodeInfo), 256) + align_up(size_t(batch) * sizeof(int), 256) +
+                 align_up(size_t(batch) * (n + dmax) * ns * sizeof(float2), 256) +
+                 align_up(size_t(maxc > 0 ? maxc : 1) * batch * n * nc * sizeof(float), 256) +
+                 align_up(size_t(batch) * sizeof(uint64_t), 256) + draw_seg_bytes(batch, vocab) + 256 +
+                 align_up(size_t(batch) * sizeof(int), 256) + align_up(size_t(batch) * n * sizeof(int), 256);
+  if (wor)
+    bytes += align_up(size_t(batch) * n * (maxc > 0 ? maxc : 1) * sizeof(int), 256) +
+             align_up(size_t(batch) * kMaxWorChildren * sizeof(float), 256);
+  return bytes;
 }
 
 hipError_t launch_tree_verify(const TreeVerifyArgs& a, hipStream_t stream) {

@@ -56,7 +56,7 @@ typedef enum {
 
 typedef enum { UNO_F32 = 0, UNO_BF16 = 1 } uno_dtype;
 
-#define UNO_ABI_VERSION 5
+#define UNO_ABI_VERSION 6
 
 int uno_abi_version(void);
 const char* uno_status_string(uno_status s);
@@ -276,6 +276,35 @@ uno_status uno_psi_spec_verify_tree(hipStream_t stream, uno_dtype logit_dtype,
                                     float temperature,
                                     int32_t* out_accept_len, int32_t* out_path, int32_t* out_token,
                                     void* workspace, size_t workspace_bytes);
+
+/* --------------------------------------------------------------------------
+ * Psi-Spec tree verify for siblings drawn WITHOUT REPLACEMENT ("wor"), e.g. by
+ * uno_psi_spec_build_tree with without_replacement = 1.  Source: Uno summary
+ * (hyper.ai), section "方法", last paragraph (lossless tree verify); read as
+ * recursive rejection sampling without replacement (Jeon et al. 2024):
+ *   cur = root, r = p_root; the children c of cur in ascending node id, with
+ *   R the tokens of the children of cur tried before c:
+ *     q_c = q_d with the tokens in R set to 0, renormalised (left at 0 when no
+ *       mass remains);
+ *     accept iff u_accept[b][c] * q_c[t] < r[t] -> cur = c, r = p_c, repeat;
+ *     reject -> r = max(0, r - q_c) / sum (unchanged, and for the node's later
+ *       children too, once the sum is 0);
+ *   no child accepted (or no child): y = inverse CDF of r at u_sample.
+ * Arguments, layouts, outputs and the checks on the tree as for
+ * uno_psi_spec_verify_tree, with max_children <= 64.  A remaining draft mass
+ * below 1e-6 of the row counts as none (fp32 cannot resolve less).
+ * ------------------------------------------------------------------------ */
+uno_status uno_psi_spec_verify_tree_wor_workspace(int32_t batch, int32_t n_tree, int32_t max_depth,
+                                                  int32_t max_children, int32_t vocab, size_t* bytes);
+uno_status uno_psi_spec_verify_tree_wor(hipStream_t stream, uno_dtype logit_dtype,
+                                        int32_t batch, int32_t n_tree, int32_t max_depth, int32_t max_children,
+                                        int32_t vocab,
+                                        const int32_t* parent, const int32_t* tokens,
+                                        const void* p_logits, const void* q_logits,
+                                        const float* u_accept, const float* u_sample,
+                                        float temperature,
+                                        int32_t* out_accept_len, int32_t* out_path, int32_t* out_token,
+                                        void* workspace, size_t workspace_bytes);
 
 /* --------------------------------------------------------------------------
  * Psi-Spec candidate tree from the per-depth draft marginals.

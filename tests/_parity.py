@@ -98,12 +98,13 @@ def check_linear(case_rows, gpu, seqs, k, temperature=1.0, tie=TIE, prob_rtol=1e
     return ties
 
 
-def tree_outcome_near(parent, tokens, p, q, ua, us, temperature, gpu_out, tie=TIE):
+def tree_outcome_near(parent, tokens, p, q, ua, us, temperature, gpu_out, tie=TIE, without=False):
     """True if perturbing one visited uniform (or u_s) by at most `tie` makes
     the oracle produce the GPU's (L, path, y): the GPU differs only on a
     near-tie decision."""
+    kw = dict(without_replacement=without)
     base = oracle.verify_tree(parent[None], tokens[None], p[None], q[None], ua[None], np.array([us]),
-                              temperature, return_visited=True)
+                              temperature, return_visited=True, **kw)
     L, path, y = gpu_out
 
     def same(r):
@@ -115,12 +116,12 @@ def tree_outcome_near(parent, tokens, p, q, ua, us, temperature, gpu_out, tie=TI
             u2 = ua.copy()
             u2[node] = min(max(u2[node] + delta, 0.0), 1.0 - 1e-12)
             r = oracle.verify_tree(parent[None], tokens[None], p[None], q[None], u2[None], np.array([us]),
-                                   temperature)
+                                   temperature, **kw)
             if same(r):
                 return True
     for delta in (-tie, tie):
         r = oracle.verify_tree(parent[None], tokens[None], p[None], q[None], ua[None],
-                               np.array([min(max(us + delta, 0.0), 1.0 - 1e-12)]), temperature)
+                               np.array([min(max(us + delta, 0.0), 1.0 - 1e-12)]), temperature, **kw)
         if same(r):
             return True
     return False

@@ -94,6 +94,15 @@ int main() {
                                             D, (const float*)D, (const float*)D, 1.f, (int32_t*)D, (int32_t*)D,
                                             (int32_t*)D, D, big), false);
 
+  expect("tree wor ws", uno_psi_spec_verify_tree_wor_workspace(2, 65, 3, 4, V, &bytes), true);
+  expect("tree wor", uno_psi_spec_verify_tree_wor(s, UNO_BF16, 2, 65, 3, 4, V, (const int32_t*)D, (const int32_t*)D,
+                                                  D, D, (const float*)D, (const float*)D, 1.f, (int32_t*)D,
+                                                  (int32_t*)D, (int32_t*)D, D, big), true);
+  expect("tree wor children", uno_psi_spec_verify_tree_wor(s, UNO_BF16, 2, 65, 3, 65, V, (const int32_t*)D,
+                                                           (const int32_t*)D, D, D, (const float*)D, (const float*)D,
+                                                           1.f, (int32_t*)D, (int32_t*)D, (int32_t*)D, D, big),
+         false);
+
   // tree construction (branching is a host array read by the call)
   const int32_t br[3] = {4, 2, 2};   // 1 + 4 + 8 + 16 = 29 nodes
   const int32_t br_bad[3] = {4, 0, 2};

@@ -27,7 +27,7 @@ size_t lora_down_part_bytes(int64_t, int64_t, int64_t) { return 256; }
 size_t sample_rows_workspace_bytes(int, int) { return 256; }
 size_t tree_attention_workspace_bytes(int, int, int, int, int, int) { return 256; }
 size_t tree_build_workspace_bytes(int, int, int) { return 256; }
-size_t tree_verify_workspace_bytes(int, int, int, int, int) { return 256; }
+size_t tree_verify_workspace_bytes(int, int, int, int, int, int) { return 256; }
 size_t verify_linear_workspace_bytes(int, int, int) { return 256; }
 size_t verify_linear_sampled_workspace_bytes(int, int, int) { return 256; }
 int rms_norm_max_dim() { return 1 << 16; }

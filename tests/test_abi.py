@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.uno_abi_version() == 5
+    assert lib.uno_abi_version() == 6
     for s in range(6):
         assert lib.uno_status_string(s)
     assert lib.uno_status_string(99) == b"unknown status"
@@ -266,6 +266,28 @@ def test_sample_rows_rejects_bad_calls(lib):
     assert call(u=None) == INVALID
     assert call(T=0.0) == INVALID
     assert call(wsb=4) == WORKSPACE
+
+
+def test_tree_verify_wor_rejects_bad_calls(lib):
+    ws = ctypes.c_size_t(0)
+    assert lib.uno_psi_spec_verify_tree_wor_workspace(1, 65, 3, 4, 1000, ctypes.byref(ws)) == OK
+    wor = ws.value
+    assert lib.uno_psi_spec_verify_tree_workspace(1, 65, 3, 4, 1000, ctypes.byref(ws)) == OK
+    assert wor > ws.value                                  # the children lists and C_k
+    assert lib.uno_psi_spec_verify_tree_wor_workspace(1, 65, 3, 65, 1000, ctypes.byref(ws)) == UNSUPPORTED
+
+    def call(**kw):
+        a = dict(dtype=BF16, batch=1, n=65, D=3, C=4, V=1000, par=FAKE16, tok=FAKE16, p=FAKE16, q=FAKE16, ua=FAKE16,
+                 us=FAKE16, T=1.0, L=FAKE16, path=FAKE16, y=FAKE16, ws=FAKE16, wsb=1 << 20)
+        a.update(kw)
+        return lib.uno_psi_spec_verify_tree_wor(None, a["dtype"], a["batch"], a["n"], a["D"], a["C"], a["V"],
+                                                a["par"], a["tok"], a["p"], a["q"], a["ua"], a["us"], a["T"],
+                                                a["L"], a["path"], a["y"], a["ws"], a["wsb"])
+    assert call(C=65) == UNSUPPORTED
+    assert call(n=1025) == UNSUPPORTED
+    assert call(tok=None) == INVALID
+    assert call(T=-1.0) == INVALID
+    assert call(wsb=wor - 1) == WORKSPACE
 
 
 def test_build_tree_rejects_bad_calls(lib):
