@@ -21,6 +21,7 @@ themselves live in `tests/test_oracle_*.py`.
 """
 
 from .gated_lora import gated_lora_linear, merged_weight
+from .distill import log_softmax_rows, distill_losses, gated_lora_backward
 from .verify_linear import (
     softmax_rows,
     row_log_stats,
@@ -49,6 +50,9 @@ from .kv_commit import kv_commit
 __all__ = [
     "gated_lora_linear",
     "merged_weight",
+    "log_softmax_rows",
+    "distill_losses",
+    "gated_lora_backward",
     "softmax_rows",
     "row_log_stats",
     "accept_draft",
