@@ -109,6 +109,8 @@ def main():
             out["components"]["tree_batch1"] = comp["components"]["tree"]
             out["components"]["linear_verify_sigma_sweep"] = bench_linear_sigma_sweep(args, dad, torch)
             out["components"]["tree_batch1_graph"] = bench_tree_graph(args, dad, torch)
+            out["components"]["tree_batch16_built"] = bench_tree_batch(args, dad, torch)
+            out["components"]["distill_loss_128x16"] = bench_distill(args, dad, torch)
     else:
         out = bench_hot_path(args, dad, torch, steps=args.steps, warmup=args.warmup,
                              with_cpu=not args.no_cpu_baseline)
@@ -785,6 +787,128 @@ def bench_tree_graph(args, dad, torch, copies=64, distinct=4, replays=5):
     return {"timing": timing, "copies": copies, "replays": replays, "us_per_tree": per_tree_us,
             "gbs": (attn_bytes + verify_bytes) / (per_tree_us * 1e-6) / 1e9, "bytes_per_tree": attn_bytes + verify_bytes,
             "replays_match_eager": bool(checks_ok), "launches_per_tree": launches}
+
+
+def bench_tree_batch(args, dad, torch, batch=16, branching=(4, 4, 3), sigma=0.5, reps=20):
+    """The tree sampler at batch 16 with the trees built on the device: 69-node
+    trees (4, 4, 3 children per level), V = 151,936, bf16, drawn from the
+    per-depth draft rows with and without replacement, then verified by the
+    matching rule.  Rows as in workloads.tree_build_case, generated on the
+    device: base_d ~ N(0, 2^2); the draft row of depth d is base_d +
+    N(0, sigma^2); the AR row of a node at depth d is base_{d+1} + N(0, 0.5^2).
+    Times are HIP events around each call's launches, averaged over `reps`
+    calls; the byte rates count every row the call reads once (build: the
+    draft rows; verify: every AR row and the draft rows)."""
+    import numpy as np
+    import workloads
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed + 3)
+    br = list(branching)
+    D = len(br)
+    depth = workloads.level_depths(br)
+    n = int(depth.size)
+    base = torch.randn((batch, D + 2, VOCAB), device=dev, generator=gen) * 2.0
+    q = (base[:, 1:D + 1] + torch.randn((batch, D, VOCAB), device=dev, generator=gen) * sigma).to(torch.bfloat16)
+    idx = torch.from_numpy(depth + 1).to(dev)
+    p = (base[:, idx] + torch.randn((batch, n, VOCAB), device=dev, generator=gen) * 0.5).to(torch.bfloat16)
+    del base
+    u_draw = torch.rand((batch, n), device=dev, generator=gen)
+    ua = torch.rand((batch, n), device=dev, generator=gen)
+    us = torch.rand((batch,), device=dev, generator=gen)
+    maxc = max(br)
+    ws_b = torch.empty(dad.psi_spec_build_tree_workspace(batch, D, VOCAB), dtype=torch.uint8, device=dev)
+    row = VOCAB * 2.0
+    build_bytes = batch * D * row
+    verify_bytes = batch * (n + D) * row
+    res = {"batch": batch, "branching": br, "n_tree": n, "vocab": VOCAB, "sigma": sigma}
+
+    def timed(fn, names):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        dad.profile_reset()
+        dad.profile_enable(True)
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        ms = sum(dad.profile_query(nm)[0] for nm in names) / reps
+        dad.profile_enable(False)
+        dad.profile_reset()
+        return ms
+
+    for wor in (False, True):
+        key = "without_replacement" if wor else "with_replacement"
+        built = dad.psi_spec_build_tree(q, br, u_draw, 1.0, wor)
+        b_ms = timed(lambda: dad.psi_spec_build_tree(q, br, u_draw, 1.0, wor, outputs=built, workspace=ws_b),
+                     ("uno_build_stats", "uno_build_desc", "uno_build_seg", "uno_build_draw"))
+        tokens = built["tokens"].clone()
+        tokens[:, 0] = 0
+        ws_v = torch.empty(dad.psi_spec_verify_tree_workspace(batch, n, D, maxc, VOCAB, wor), dtype=torch.uint8,
+                           device=dev)
+        res_v = dad.psi_spec_verify_tree(built["parent"], tokens, p, q, ua, us, max_children=maxc, workspace=ws_v,
+                                         without_replacement=wor)
+        v_ms = timed(lambda: dad.psi_spec_verify_tree(built["parent"], tokens, p, q, ua, us, max_children=maxc,
+                                                      outputs=res_v, workspace=ws_v, without_replacement=wor),
+                     ("uno_tree_stats", "uno_tree_flow"))
+        L = res_v["accept_len"].float()
+        res[key] = {"build_us": b_ms * 1e3, "build_gbs": build_bytes / (b_ms * 1e-3) / 1e9,
+                    "verify_us": v_ms * 1e3, "verify_gbs": verify_bytes / (v_ms * 1e-3) / 1e9,
+                    "verify_hbm_frac": verify_bytes / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "mean_accept_len": float(L.mean()),
+                    "distinct_siblings": bool(wor)}
+        log(f"tree batch {batch} {key}: build {b_ms * 1e3:.1f} us, verify {v_ms * 1e3:.1f} us, "
+            f"mean L {float(L.mean()):.2f}")
+        del ws_v
+    del p, q
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_distill(args, dad, torch, batch=128, block=16, sigma=0.5, reps=10):
+    """The distillation losses over the logits of one concatenated forward at
+    the step's shape: 128 sequences x (16 clean + 16 noisy) rows, V = 151,936,
+    bf16; teacher rows ~ N(0, 2^2), student rows = teacher + N(0, sigma^2),
+    generated on the device.  The teacher and student halves are passed in
+    place; the gradient goes into the noisy half of a same-shaped buffer.
+    Algorithmic bytes per pair: both rows read once and the gradient row
+    written once (3 V x 2 bytes); losses only: the two reads."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed + 4)
+    t = torch.randn((batch, block, VOCAB), device=dev, generator=gen) * 2.0
+    s = t + torch.randn((batch, block, VOCAB), device=dev, generator=gen) * sigma
+    logits = torch.cat([t, s], dim=1).to(torch.bfloat16)
+    del t, s
+    gbuf = torch.empty_like(logits)
+    kl = torch.empty((batch, block), dtype=torch.float32, device=dev)
+    tv = torch.empty_like(kl)
+    res = {"batch": batch, "block": block, "vocab": VOCAB, "sigma": sigma}
+    pairs = batch * block
+    for name, want in (("with_grad", True), ("losses_only", False)):
+        outs = {"kl": kl, "tv": tv}
+        if want:
+            outs["grad"] = gbuf[:, block:]
+        for _ in range(2):
+            dad.distill_loss(logits[:, :block], logits[:, block:], grad_scale=1.0 / pairs, outputs=outs)
+        torch.cuda.synchronize()
+        dad.profile_reset()
+        dad.profile_enable(True)
+        for _ in range(reps):
+            dad.distill_loss(logits[:, :block], logits[:, block:], grad_scale=1.0 / pairs, outputs=outs)
+        torch.cuda.synchronize()
+        ms = dad.profile_query("uno_distill")[0] / reps
+        dad.profile_enable(False)
+        dad.profile_reset()
+        nbytes = pairs * VOCAB * 2.0 * (3 if want else 2)
+        res[name] = {"us": ms * 1e3, "bytes": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9,
+                     "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        log(f"distill {name}: {ms * 1e3:.1f} us, {nbytes / (ms * 1e-3) / 1e9:.0f} GB/s")
+    res["mean_kl"] = float(kl.mean())
+    res["mean_tv"] = float(tv.mean())
+    del logits, gbuf
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline_hot_path(args, lin, ta, tv, tokens_per_step):

@@ -25,6 +25,7 @@ EXPORTS = (
     "uno_psi_spec_verify_tree_workspace", "uno_psi_spec_verify_tree",
     "uno_psi_spec_verify_tree_wor_workspace", "uno_psi_spec_verify_tree_wor",
     "uno_psi_spec_build_tree_workspace", "uno_psi_spec_build_tree",
+    "uno_distill_loss",
     "uno_rms_norm", "uno_rope", "uno_silu_mul",
     "uno_block_verify_attention_workspace", "uno_block_verify_attention",
     "uno_sample_rows_workspace", "uno_sample_rows",
@@ -103,6 +104,8 @@ def _declare(lib):
         "uno_psi_spec_verify_tree_wor": (ctypes.c_int, [_p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32,
                                                         _p, _p, _p, _p, _p, _p, _f32, _p, _p, _p, _p, _sz]),
         "uno_psi_spec_build_tree_workspace": (ctypes.c_int, [_i32, _i32, _i32, ctypes.POINTER(_sz)]),
+        "uno_distill_loss": (ctypes.c_int, [_p, ctypes.c_int, _i32, _i32, _i32, _p, _i64, _i64, _p, _i64, _i64,
+                                            _f32, _f32, _f32, _f32, _p, _p, _p, _i64, _i64]),
         "uno_psi_spec_build_tree": (ctypes.c_int, [_p, ctypes.c_int, _i32, _i32, _p, _i32, _p, _i64, _i64, _p, _i32,
                                                    _f32, _i32, _p, _p, _p, _sz]),
         "uno_rms_norm": (ctypes.c_int, [_p, _i64, _i32, _p, _i64, _p, _i64, _p, _i64, _p, _f32, _p, _i64]),
@@ -458,6 +461,35 @@ def psi_spec_build_tree(q_logits, branching, u_draw, temperature=1.0, without_re
         _stream(stream), _dtype_code(q_logits), bsz, dmax, br, vocab, _ptr(q_logits), q_logits.stride(0),
         q_logits.stride(1), _ptr(u_draw), n, float(temperature), int(bool(without_replacement)),
         _ptr(outputs["parent"]), _ptr(outputs["tokens"]), _ptr(ws), _nbytes(ws)))
+    return outputs
+
+
+def distill_loss(teacher, student, temperature=1.0, alpha=1.0, beta=1.0, grad_scale=1.0, want_grad=True,
+                 outputs=None, stream=None):
+    """Distillation losses of row pairs (uno_distill_loss).
+
+    teacher, student [B, R, V] (last dim contiguous; any batch and row strides,
+    e.g. the clean and noisy halves of a step's logits).  Returns dict kl, tv
+    (f32 [B, R]) and grad ([B, R, V], the logits' dtype) when want_grad."""
+    import torch
+    load()
+    bsz, rows, vocab = student.shape
+    if teacher.shape != student.shape or teacher.dtype != student.dtype:
+        raise ValueError("teacher and student must have the same shape and dtype")
+    if teacher.stride(2) != 1 or student.stride(2) != 1:
+        raise ValueError("the vocabulary dimension must be contiguous")
+    dev = student.device
+    if outputs is None:
+        outputs = {"kl": torch.empty((bsz, rows), dtype=torch.float32, device=dev),
+                   "tv": torch.empty((bsz, rows), dtype=torch.float32, device=dev)}
+        if want_grad:
+            outputs["grad"] = torch.empty((bsz, rows, vocab), dtype=student.dtype, device=dev)
+    g = outputs.get("grad")
+    _check(_lib.uno_distill_loss(
+        _stream(stream), _dtype_code(student), bsz, rows, vocab, _ptr(teacher), teacher.stride(0), teacher.stride(1),
+        _ptr(student), student.stride(0), student.stride(1), float(temperature), float(alpha), float(beta),
+        float(grad_scale), _ptr(outputs["kl"]), _ptr(outputs["tv"]), _ptr(g),
+        g.stride(0) if g is not None else 0, g.stride(1) if g is not None else vocab))
     return outputs
 
 

@@ -149,6 +149,52 @@ static uno_status check_verify_linear_shape(int32_t batch, int32_t k, int32_t vo
   return UNO_OK;
 }
 
+// ------------------------------------------------------------------ distillation losses
+uno_status uno_distill_loss(hipStream_t stream, uno_dtype logit_dtype, int32_t batch, int32_t rows, int32_t vocab,
+                            const void* teacher, int64_t t_seq_stride, int64_t t_row_stride, const void* student,
+                            int64_t s_seq_stride, int64_t s_row_stride, float temperature, float alpha, float beta,
+                            float grad_scale, float* out_kl, float* out_tv, void* grad, int64_t g_seq_stride,
+                            int64_t g_row_stride) {
+  UNO_GUARD_BEGIN
+  if (logit_dtype != UNO_F32 && logit_dtype != UNO_BF16)
+    return fail(UNO_ERR_INVALID_ARGUMENT, "unknown dtype %d", int(logit_dtype));
+  if (batch < 1 || rows < 1 || vocab < 1) return fail(UNO_ERR_INVALID_ARGUMENT, "batch, rows and vocab must be >= 1");
+  if (int64_t(batch) * rows > 0x7fffffff) return fail(UNO_ERR_UNSUPPORTED, "more than 2^31 - 1 row pairs");
+  if (vocab > (1 << 20)) return fail(UNO_ERR_UNSUPPORTED, "vocab above 2^20");
+  if (!teacher || !student || !out_kl || !out_tv) return fail(UNO_ERR_INVALID_ARGUMENT, "required pointer is NULL");
+  if (t_row_stride < vocab || s_row_stride < vocab || (grad && g_row_stride < vocab))
+    return fail(UNO_ERR_INVALID_ARGUMENT, "a row stride is below vocab");
+  if (t_seq_stride < 0 || s_seq_stride < 0 || (grad && g_seq_stride < 0))
+    return fail(UNO_ERR_INVALID_ARGUMENT, "negative sequence stride");
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(UNO_ERR_INVALID_ARGUMENT, "temperature must be finite and > 0");
+  if (!std::isfinite(alpha) || !std::isfinite(beta) || !std::isfinite(grad_scale))
+    return fail(UNO_ERR_INVALID_ARGUMENT, "alpha, beta and grad_scale must be finite");
+  DistillArgs a{};
+  a.dtype = logit_dtype;
+  a.batch = batch;
+  a.rows = rows;
+  a.vocab = vocab;
+  a.teacher = teacher;
+  a.t_seq = t_seq_stride;
+  a.t_row = t_row_stride;
+  a.student = student;
+  a.s_seq = s_seq_stride;
+  a.s_row = s_row_stride;
+  a.scale_log2 = float(1.4426950408889634 / double(temperature));
+  a.inv_t = float(1.0 / double(temperature));
+  a.alpha = alpha;
+  a.beta = beta;
+  a.grad_scale = grad_scale;
+  a.out_kl = out_kl;
+  a.out_tv = out_tv;
+  a.grad = grad;
+  a.g_seq = g_seq_stride;
+  a.g_row = g_row_stride;
+  return check_hip(launch_distill(a, stream), "uno_distill_loss launch");
+  UNO_GUARD_END
+}
+
 // ------------------------------------------------------------------ tree construction
 static uno_status check_tree_build(int32_t batch, int32_t max_depth, const int32_t* branching, int32_t vocab,
                                    int32_t n_tree, int32_t without) {

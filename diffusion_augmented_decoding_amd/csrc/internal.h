@@ -101,6 +101,20 @@ inline uno_status debug_check_verify_linear(hipStream_t stream, const VerifyLine
   if (s == UNO_OK) s = debug_check_unit(stream, a.u_s, a.batch, "u_sample");
   return s;
 }
+// Distillation losses of row pairs (student rows against teacher rows).
+struct DistillArgs {
+  uno_dtype dtype;
+  int batch, rows, vocab;                // pair i of sequence b: teacher/student row i
+  const void* teacher; int64_t t_seq, t_row;
+  const void* student; int64_t s_seq, s_row;
+  float scale_log2, inv_t;               // log2(e) / T, 1 / T
+  float alpha, beta, grad_scale;
+  float* out_kl;                         // [batch * rows]
+  float* out_tv;                         // [batch * rows]
+  void* grad; int64_t g_seq, g_row;      // optional, the logits' dtype
+};
+hipError_t launch_distill(const DistillArgs& a, hipStream_t stream);
+
 // Candidate trees from the per-depth draft marginals (breadth first, branching[d]
 // children for every node at depth d), tokens drawn with or without replacement.
 constexpr int kMaxBranch = 64;

@@ -345,6 +345,41 @@ uno_status uno_psi_spec_build_tree(hipStream_t stream, uno_dtype logit_dtype, in
                                    float temperature, int32_t without_replacement, int32_t* out_parent,
                                    int32_t* out_tokens, void* workspace, size_t workspace_bytes);
 
+/* --------------------------------------------------------------------------
+ * Distillation losses of row pairs (the training side of the gated forward).
+ * Source: Uno summary (hyper.ai), section "方法", the paragraphs on diffusion
+ * distillation: the objective alpha * L_DCD + beta * L_TV; one forward over
+ * the concatenated clean and noisy rows with the adapter off on clean rows
+ * (teacher logits, AR weights only) and on on noisy rows (student logits);
+ * the block-level KL between the student and the teacher distribution; the
+ * TV distance between the diffusion and the AR distribution, which lengthens
+ * the accepted draft prefix.  Readings: student row i pairs with teacher row
+ * i; the block KL is the sum of the per-row KL(student || teacher) (product
+ * of per-position marginals against the teacher's per-position
+ * conditionals); the TV loss is the sum of per-row TV.  Per pair, with
+ * p = softmax(teacher / T) and q = softmax(student / T):
+ *   out_kl = sum_v q_v (ln q_v - ln p_v),   out_tv = 1/2 sum_v |q_v - p_v|,
+ *   grad (optional) = d/dz [grad_scale * (alpha KL + beta TV)] in the
+ *     student logits z: grad_scale / T * q_v * (alpha (ln q_v - ln p_v - KL)
+ *     + beta / 2 (sign(q_v - p_v) - sum_u sign(q_u - p_u) q_u)), sign(0) = 0.
+ *
+ * Row i of sequence b: teacher + b * t_seq_stride + i * t_row_stride
+ * elements (likewise student and grad), bf16 or fp32 (grad in the logits'
+ * dtype); strides >= vocab per row, >= 0 per sequence.  With the decode
+ * step's logits [batch][2*block][vocab]: teacher = logits, student = logits +
+ * block * vocab, both strides 2*block*vocab and vocab, rows = block.
+ * out_kl, out_tv: f32 [batch * rows].  grad = NULL: losses only.
+ * batch, rows >= 1, batch * rows < 2^31, 1 <= vocab <= 2^20, T > 0, alpha,
+ * beta, grad_scale finite.  No workspace: one workgroup per pair, three
+ * passes over it, fixed summation order (deterministic).
+ * ------------------------------------------------------------------------ */
+uno_status uno_distill_loss(hipStream_t stream, uno_dtype logit_dtype, int32_t batch, int32_t rows, int32_t vocab,
+                            const void* teacher, int64_t t_seq_stride, int64_t t_row_stride,
+                            const void* student, int64_t s_seq_stride, int64_t s_row_stride,
+                            float temperature, float alpha, float beta, float grad_scale,
+                            float* out_kl, float* out_tv,
+                            void* grad, int64_t g_seq_stride, int64_t g_row_stride);
+
 /* ==========================================================================
  * The composed decode step.  Source: Uno summary (hyper.ai), section 方法
  * (one forward over the concatenated clean and noisy rows of a block, the

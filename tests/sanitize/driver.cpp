@@ -103,6 +103,14 @@ int main() {
                                                            1.f, (int32_t*)D, (int32_t*)D, (int32_t*)D, D, big),
          false);
 
+  // distillation losses
+  expect("distill", uno_distill_loss(s, UNO_BF16, 2, 8, V, D, 16 * V, V, D, 16 * V, V, 1.f, 1.f, 1.f, 1.f, (float*)D,
+                                     (float*)D, D, 16 * V, V), true);
+  expect("distill no grad", uno_distill_loss(s, UNO_F32, 2, 8, V, D, 16 * V, V, D, 16 * V, V, 0.7f, 1.f, 0.f, 1.f,
+                                             (float*)D, (float*)D, nullptr, 0, 0), true);
+  expect("distill stride", uno_distill_loss(s, UNO_BF16, 2, 8, V, D, 16 * V, V - 1, D, 16 * V, V, 1.f, 1.f, 1.f, 1.f,
+                                            (float*)D, (float*)D, D, 16 * V, V), false);
+
   // tree construction (branching is a host array read by the call)
   const int32_t br[3] = {4, 2, 2};   // 1 + 4 + 8 + 16 = 29 nodes
   const int32_t br_bad[3] = {4, 0, 2};

@@ -49,6 +49,7 @@ hipError_t launch_silu_mul(const SiluMulArgs&, hipStream_t) { return launched();
 hipError_t launch_step_finish(const StepFinishArgs&, hipStream_t) { return launched(); }
 hipError_t launch_step_setup(const StepSetupArgs&, hipStream_t) { return launched(); }
 hipError_t launch_tree_attention(const TreeAttnArgs&, hipStream_t) { return launched(); }
+hipError_t launch_distill(const DistillArgs&, hipStream_t) { return launched(); }
 hipError_t launch_tree_build(const TreeBuildArgs&, hipStream_t) { return launched(); }
 hipError_t launch_tree_verify(const TreeVerifyArgs&, hipStream_t) { return launched(); }
 hipError_t launch_verify_linear(const VerifyLinearArgs&, hipStream_t) { return launched(); }

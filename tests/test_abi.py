@@ -290,6 +290,29 @@ def test_tree_verify_wor_rejects_bad_calls(lib):
     assert call(wsb=wor - 1) == WORKSPACE
 
 
+def test_distill_loss_rejects_bad_calls(lib):
+    def call(**kw):
+        a = dict(dtype=BF16, batch=2, rows=3, V=100, t=FAKE16, ts=300, tr=100, s=FAKE16, ss=300, sr=100, T=1.0,
+                 alpha=1.0, beta=1.0, gs=1.0, kl=FAKE16, tv=FAKE16, g=FAKE16, gsq=300, gr=100)
+        a.update(kw)
+        return lib.uno_distill_loss(None, a["dtype"], a["batch"], a["rows"], a["V"], a["t"], a["ts"], a["tr"],
+                                    a["s"], a["ss"], a["sr"], a["T"], a["alpha"], a["beta"], a["gs"], a["kl"],
+                                    a["tv"], a["g"], a["gsq"], a["gr"])
+    assert call(dtype=9) == INVALID
+    assert call(batch=0) == INVALID
+    assert call(rows=0) == INVALID
+    assert call(V=(1 << 20) + 1, tr=1 << 21, sr=1 << 21, gr=1 << 21) == UNSUPPORTED
+    assert call(t=None) == INVALID
+    assert call(tv=None) == INVALID
+    assert call(sr=99) == INVALID
+    assert call(gr=99) == INVALID
+    assert call(ts=-1) == INVALID
+    assert call(T=0.0) == INVALID
+    assert call(alpha=float("inf")) == INVALID
+    assert call(gs=float("nan")) == INVALID
+    assert call(batch=1 << 16, rows=1 << 15) == UNSUPPORTED
+
+
 def test_build_tree_rejects_bad_calls(lib):
     ws = ctypes.c_size_t(0)
     assert lib.uno_psi_spec_build_tree_workspace(256, 15, 151936, ctypes.byref(ws)) == OK
