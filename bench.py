@@ -111,6 +111,7 @@ def main():
             out["components"]["tree_batch1_graph"] = bench_tree_graph(args, dad, torch)
             out["components"]["tree_batch16_built"] = bench_tree_batch(args, dad, torch)
             out["components"]["distill_loss_128x16"] = bench_distill(args, dad, torch)
+            out["components"]["gated_lora_backward_1024_rows"] = bench_lora_backward(args, dad, torch)
     else:
         out = bench_hot_path(args, dad, torch, steps=args.steps, warmup=args.warmup,
                              with_cpu=not args.no_cpu_baseline)
@@ -907,6 +908,60 @@ def bench_distill(args, dad, torch, batch=128, block=16, sigma=0.5, reps=10):
     res["mean_kl"] = float(kl.mean())
     res["mean_tv"] = float(tv.mean())
     del logits, gbuf
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_lora_backward(args, dad, torch, reps=10):
+    """The gated-LoRA backward of the 1024-row layer workload's projections
+    (64 sequences x 8 clean + 8 noisy rows, Qwen3-8B shapes, rank 128, bf16):
+    q (N = K = 4096), gate/up (N = 12288, K = 4096) and down (N = 4096,
+    K = 12288).  Per launch: HIP-event time and MFMA rate against the dense
+    bf16 peak; FLOPs of the five products 2 M r K (U), 2 M r N (dT),
+    2 N r M (dB), 2 r K M (dA) and 2 M K (N + r) (dx)."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed + 5)
+    M, r = 1024, 128
+    gate = torch.tensor(([0] * 8 + [1] * 8) * (M // 16), dtype=torch.uint8, device=dev)
+    # phases of the call with W^T given: per-call transposes of A and B, the LoRA-down
+    # for U and dT, the adapter gradients, the main GEMM for dx
+    phases = {"transpose": ("uno_transpose",), "u_dt": ("uno_lora_down", "uno_lora_gate"),
+              "db": ("uno_lora_bwd_db",), "da": ("uno_lora_bwd_da",), "dx": ("uno_gemm",)}
+    res = {"rows": M, "rank": r}
+    for proj, N, K in (("q", 4096, 4096), ("gate_up", 12288, 4096), ("down", 4096, 12288)):
+        x = (torch.randn((M, K), device=dev, generator=gen)).to(torch.bfloat16)
+        w = (torch.randn((N, K), device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+        a = (torch.randn((r, K), device=dev, generator=gen) * 0.05).to(torch.bfloat16)
+        b = (torch.randn((N, r), device=dev, generator=gen) * 0.05).to(torch.bfloat16)
+        dy = torch.randn((M, N), device=dev, generator=gen).to(torch.bfloat16)
+        wt = dad.transpose_bf16(w)   # the frozen weight, transposed once
+        ws = torch.empty(dad.gated_lora_backward_workspace(M, N, K, r, True), dtype=torch.uint8, device=dev)
+        outs = dad.gated_lora_backward(x, w, a, b, gate, dy, workspace=ws, w_t=wt)
+        for _ in range(2):
+            dad.gated_lora_backward(x, w, a, b, gate, dy, outputs=outs, workspace=ws, w_t=wt)
+        torch.cuda.synchronize()
+        dad.profile_reset()
+        dad.profile_enable(True)
+        for _ in range(reps):
+            dad.gated_lora_backward(x, w, a, b, gate, dy, outputs=outs, workspace=ws, w_t=wt)
+        torch.cuda.synchronize()
+        flops = {"transpose": 0.0, "u_dt": 2.0 * M * r * (K + N), "db": 2.0 * N * r * M, "da": 2.0 * r * K * M,
+                 "dx": 2.0 * M * K * (N + r)}
+        per = {}
+        total_ms = 0.0
+        for ph, nms in phases.items():
+            ms = sum(dad.profile_query(nm)[0] for nm in nms) / reps
+            total_ms += ms
+            per[ph] = {"us": ms * 1e3, "tflops": flops[ph] / (ms * 1e-3) / 1e12,
+                       "mfma_frac": flops[ph] / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+        dad.profile_enable(False)
+        dad.profile_reset()
+        tf = sum(flops.values())
+        res[proj] = {"N": N, "K": K, "w_t": True, "us": total_ms * 1e3, "tflops": tf / (total_ms * 1e-3) / 1e12,
+                     "mfma_frac": tf / (total_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, "launches": per}
+        log(f"lora backward {proj}: {total_ms * 1e3:.1f} us, {tf / (total_ms * 1e-3) / 1e12:.0f} TFLOP/s")
+        del x, w, a, b, dy, ws, outs, wt
     torch.cuda.empty_cache()
     return res
 

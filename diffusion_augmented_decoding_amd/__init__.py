@@ -26,6 +26,7 @@ EXPORTS = (
     "uno_psi_spec_verify_tree_wor_workspace", "uno_psi_spec_verify_tree_wor",
     "uno_psi_spec_build_tree_workspace", "uno_psi_spec_build_tree",
     "uno_distill_loss",
+    "uno_gated_lora_backward_workspace", "uno_gated_lora_backward", "uno_transpose_bf16",
     "uno_rms_norm", "uno_rope", "uno_silu_mul",
     "uno_block_verify_attention_workspace", "uno_block_verify_attention",
     "uno_sample_rows_workspace", "uno_sample_rows",
@@ -104,6 +105,11 @@ def _declare(lib):
         "uno_psi_spec_verify_tree_wor": (ctypes.c_int, [_p, ctypes.c_int, _i32, _i32, _i32, _i32, _i32,
                                                         _p, _p, _p, _p, _p, _p, _f32, _p, _p, _p, _p, _sz]),
         "uno_psi_spec_build_tree_workspace": (ctypes.c_int, [_i32, _i32, _i32, ctypes.POINTER(_sz)]),
+        "uno_gated_lora_backward_workspace": (ctypes.c_int, [_i64, _i64, _i64, _i64, _i32, ctypes.POINTER(_sz)]),
+        "uno_gated_lora_backward": (ctypes.c_int, [_p, _i64, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64,
+                                                   _p, _f32, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p,
+                                                   _sz]),
+        "uno_transpose_bf16": (ctypes.c_int, [_p, _i64, _i64, _p, _i64, _p, _i64]),
         "uno_distill_loss": (ctypes.c_int, [_p, ctypes.c_int, _i32, _i32, _i32, _p, _i64, _i64, _p, _i64, _i64,
                                             _f32, _f32, _f32, _f32, _p, _p, _p, _i64, _i64]),
         "uno_psi_spec_build_tree": (ctypes.c_int, [_p, ctypes.c_int, _i32, _i32, _p, _i32, _p, _i64, _i64, _p, _i32,
@@ -461,6 +467,53 @@ def psi_spec_build_tree(q_logits, branching, u_draw, temperature=1.0, without_re
         _stream(stream), _dtype_code(q_logits), bsz, dmax, br, vocab, _ptr(q_logits), q_logits.stride(0),
         q_logits.stride(1), _ptr(u_draw), n, float(temperature), int(bool(without_replacement)),
         _ptr(outputs["parent"]), _ptr(outputs["tokens"]), _ptr(ws), _nbytes(ws)))
+    return outputs
+
+
+def gated_lora_backward_workspace(M, N, K, r, with_w_t=False):
+    load()
+    out = _sz(0)
+    _check(_lib.uno_gated_lora_backward_workspace(M, N, K, r, int(bool(with_w_t)), ctypes.byref(out)))
+    return out.value
+
+
+def transpose_bf16(src, out=None, stream=None):
+    """out = src^T for a bf16 [rows, cols] matrix (uno_transpose_bf16)."""
+    import torch
+    load()
+    rows, cols = src.shape
+    if out is None:
+        out = torch.empty((cols, rows), dtype=src.dtype, device=src.device)
+    _check(_lib.uno_transpose_bf16(_stream(stream), rows, cols, _ptr(src), src.stride(0), _ptr(out), out.stride(0)))
+    return out
+
+
+def gated_lora_backward(x, w, a, b, gate, dy, lora_scale=1.0, want_dx=True, outputs=None, workspace=None,
+                        stream=None, w_t=None):
+    """Gradients of the gated-LoRA linear layer (uno_gated_lora_backward).
+
+    bf16 x [M, K], w [N, K], a [r, K], b [N, r], dy [M, N] (rows with a
+    contiguous last dim); gate uint8 [M] or None; w_t: optional W^T [K, N]
+    (transpose_bf16(w), made once for a frozen weight).  Returns dict da (f32
+    [r, K]), db (f32 [N, r]) and dx (bf16 [M, K]) when want_dx."""
+    import torch
+    load()
+    M, K = x.shape
+    N = w.shape[0]
+    r = a.shape[0]
+    dev = x.device
+    if outputs is None:
+        outputs = {"da": torch.empty((r, K), dtype=torch.float32, device=dev),
+                   "db": torch.empty((N, r), dtype=torch.float32, device=dev)}
+        if want_dx:
+            outputs["dx"] = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    dx = outputs.get("dx")
+    ws = _workspace(gated_lora_backward_workspace(M, N, K, r, w_t is not None), dev, workspace)
+    _check(_lib.uno_gated_lora_backward(
+        _stream(stream), M, N, K, r, _ptr(x), x.stride(0), _ptr(w), w.stride(0), _ptr(a), a.stride(0), _ptr(b),
+        b.stride(0), _ptr(gate), float(lora_scale), _ptr(dy), dy.stride(0), _ptr(dx),
+        dx.stride(0) if dx is not None else K, _ptr(outputs["da"]), outputs["da"].stride(0), _ptr(outputs["db"]),
+        outputs["db"].stride(0), _ptr(w_t), w_t.stride(0) if w_t is not None else 0, _ptr(ws), _nbytes(ws)))
     return outputs
 
 

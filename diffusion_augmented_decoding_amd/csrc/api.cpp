@@ -149,6 +149,95 @@ static uno_status check_verify_linear_shape(int32_t batch, int32_t k, int32_t vo
   return UNO_OK;
 }
 
+// ------------------------------------------------------------------ gated-LoRA backward
+static uno_status check_lora_backward(int64_t M, int64_t N, int64_t K, int64_t r) {
+  if (M < 1 || N < 1 || K < 1 || r < 1) return fail(UNO_ERR_INVALID_ARGUMENT, "M, N, K and r must be >= 1");
+  if (M > (int64_t(1) << 24) || N > (int64_t(1) << 20) || K > (int64_t(1) << 20) || r > 4096)
+    return fail(UNO_ERR_UNSUPPORTED, "shape above the supported range");
+  if (N % 32 || K % 8 || r % 8)
+    return fail(UNO_ERR_UNSUPPORTED, "N must be a multiple of 32, K and r multiples of 8");
+  return UNO_OK;
+}
+
+uno_status uno_gated_lora_backward_workspace(int64_t M, int64_t N, int64_t K, int64_t r, int32_t with_w_t,
+                                            size_t* bytes) {
+  UNO_GUARD_BEGIN
+  if (!bytes) return fail(UNO_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  uno_status s = check_lora_backward(M, N, K, r);
+  if (s != UNO_OK) return s;
+  *bytes = lora_backward_workspace_bytes(M, N, K, r, with_w_t ? 1 : 0);
+  return UNO_OK;
+  UNO_GUARD_END
+}
+
+uno_status uno_gated_lora_backward(hipStream_t stream, int64_t M, int64_t N, int64_t K, int64_t r, const void* x,
+                                   int64_t ldx, const void* W, int64_t ldw, const void* A, int64_t lda, const void* B,
+                                   int64_t ldb, const uint8_t* gate, float lora_scale, const void* dy, int64_t lddy,
+                                   void* dx, int64_t lddx, float* dA, int64_t ldda, float* dB, int64_t lddb,
+                                   const void* W_t, int64_t ldwt, void* workspace, size_t workspace_bytes) {
+  UNO_GUARD_BEGIN
+  uno_status s = check_lora_backward(M, N, K, r);
+  if (s != UNO_OK) return s;
+  if (!x || !A || !B || !dy || !dA || !dB || (dx && !W))
+    return fail(UNO_ERR_INVALID_ARGUMENT, "required pointer is NULL");
+  if (ldx < K || lda < K || ldb < r || lddy < N || ldda < K || lddb < r || (dx && (ldw < K || lddx < K)))
+    return fail(UNO_ERR_INVALID_ARGUMENT, "leading dimension smaller than the row width");
+  if (ldx % 8 || lda % 8 || ldb % 8 || lddy % 8 || ldda % 8 || lddb % 8 || (dx && (ldw % 8 || lddx % 8)))
+    return fail(UNO_ERR_UNSUPPORTED, "leading dimensions must be multiples of 8");
+  if (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(dy) || !aligned16(dA) || !aligned16(dB) ||
+      (dx && (!aligned16(W) || !aligned16(dx))))
+    return fail(UNO_ERR_UNSUPPORTED, "matrices must be 16-byte aligned");
+  if (!std::isfinite(lora_scale)) return fail(UNO_ERR_INVALID_ARGUMENT, "lora_scale must be finite");
+  if (W_t && (ldwt < N || ldwt % 8 || !aligned16(W_t)))
+    return fail(UNO_ERR_INVALID_ARGUMENT, "W_t needs ldwt >= N, a multiple of 8, and 16-byte alignment");
+  const size_t need = lora_backward_workspace_bytes(M, N, K, r, W_t ? 1 : 0);
+  if (workspace_bytes < need || !workspace)
+    return fail(UNO_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(UNO_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  LoraBackwardArgs a{};
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.r = r;
+  a.x = x;
+  a.ldx = ldx;
+  a.w = W;
+  a.ldw = ldw;
+  a.a = A;
+  a.lda = lda;
+  a.b = B;
+  a.ldb = ldb;
+  a.gate = gate;
+  a.lora_scale = lora_scale;
+  a.dy = dy;
+  a.lddy = lddy;
+  a.dx = dx;
+  a.lddx = lddx;
+  a.da = dA;
+  a.ldda = ldda;
+  a.db = dB;
+  a.lddb = lddb;
+  a.w_t = W_t;
+  a.ldwt = ldwt;
+  a.ws = workspace;
+  return check_hip(launch_lora_backward(a, stream), "uno_gated_lora_backward launch");
+  UNO_GUARD_END
+}
+
+uno_status uno_transpose_bf16(hipStream_t stream, int64_t rows, int64_t cols, const void* src, int64_t ld_src,
+                              void* dst, int64_t ld_dst) {
+  UNO_GUARD_BEGIN
+  if (rows < 1 || cols < 1) return fail(UNO_ERR_INVALID_ARGUMENT, "rows and cols must be >= 1");
+  if (rows > (int64_t(1) << 30) || cols > (int64_t(1) << 30)) return fail(UNO_ERR_UNSUPPORTED, "too large");
+  if ((cols + 63) / 64 > 0x7fffffff || (rows + 63) / 64 > 65535) return fail(UNO_ERR_UNSUPPORTED, "too many rows");
+  if (!src || !dst) return fail(UNO_ERR_INVALID_ARGUMENT, "src and dst must be non-NULL");
+  if (ld_src < cols || ld_dst < rows) return fail(UNO_ERR_INVALID_ARGUMENT, "leading dimension below the row width");
+  if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 1u) != 0)
+    return fail(UNO_ERR_INVALID_ARGUMENT, "src and dst must be 2-byte aligned");
+  return check_hip(launch_transpose_bf16(src, ld_src, dst, ld_dst, rows, cols, stream), "uno_transpose_bf16 launch");
+  UNO_GUARD_END
+}
+
 // ------------------------------------------------------------------ distillation losses
 uno_status uno_distill_loss(hipStream_t stream, uno_dtype logit_dtype, int32_t batch, int32_t rows, int32_t vocab,
                             const void* teacher, int64_t t_seq_stride, int64_t t_row_stride, const void* student,

@@ -101,6 +101,28 @@ inline uno_status debug_check_verify_linear(hipStream_t stream, const VerifyLine
   if (s == UNO_OK) s = debug_check_unit(stream, a.u_s, a.batch, "u_sample");
   return s;
 }
+// Gated-LoRA backward (bf16 operands): dx = dY W + dT A (bf16, optional),
+// dA = dT^T x and dB = s dY^T U (fp32), U = g (x A^T), dT = s g (dY B).
+struct LoraBackwardArgs {
+  int64_t M, N, K, r;
+  const void* x; int64_t ldx;
+  const void* w; int64_t ldw;
+  const void* a; int64_t lda;
+  const void* b; int64_t ldb;
+  const uint8_t* gate;                  // NULL: every row gate 0
+  float lora_scale;
+  const void* dy; int64_t lddy;
+  void* dx; int64_t lddx;               // optional
+  float* da; int64_t ldda;
+  float* db; int64_t lddb;
+  const void* w_t; int64_t ldwt;        // optional: W^T [K][N]; dx and U / dT then run on the forward's kernels
+  void* ws;                             // U and dT (bf16 [M][r] each), transposes, partials
+};
+size_t lora_backward_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r, int with_wt);
+hipError_t launch_transpose_bf16(const void* src, int64_t lds, void* dst, int64_t ldd, int64_t rows, int64_t cols,
+                                 hipStream_t stream);
+hipError_t launch_lora_backward(const LoraBackwardArgs& a, hipStream_t stream);
+
 // Distillation losses of row pairs (student rows against teacher rows).
 struct DistillArgs {
   uno_dtype dtype;

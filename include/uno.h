@@ -346,6 +346,51 @@ uno_status uno_psi_spec_build_tree(hipStream_t stream, uno_dtype logit_dtype, in
                                    int32_t* out_tokens, void* workspace, size_t workspace_bytes);
 
 /* --------------------------------------------------------------------------
+ * dst[c][r] = src[r][c] for a rows x cols bf16 matrix (src ld ld_src >=
+ * cols, dst ld ld_dst >= rows, both 2-byte aligned, not overlapping).  For
+ * callers of uno_gated_lora_backward: the frozen AR weight W [N][K] is
+ * transposed once into W^T [K][N].  rows <= 64 * 65535.
+ * ------------------------------------------------------------------------ */
+uno_status uno_transpose_bf16(hipStream_t stream, int64_t rows, int64_t cols, const void* src, int64_t ld_src,
+                              void* dst, int64_t ld_dst);
+
+/* --------------------------------------------------------------------------
+ * Gated-LoRA backward (the training side of the gated concatenated forward).
+ * Source: Uno summary (hyper.ai), section "方法": the diffusion weights are
+ * low-rank adapters on every AR weight matrix, trained by diffusion
+ * distillation after the AR weights are frozen; one forward runs over the
+ * concatenated clean and noisy rows with the adapter masked off on clean
+ * rows.  For y = x W^T + s diag(g) (x A^T) B^T (uno_gated_lora_linear) and
+ * dY = dL/dy, with U = diag(g) (x A^T) and dT = s diag(g) (dY B):
+ *   dB = s dY^T U            f32 [N][r] (ld lddb)
+ *   dA = dT^T x              f32 [r][K] (ld ldda)
+ *   dx = dY W + dT A         bf16 [M][K] (ld lddx); dx = NULL skips it (and W)
+ * W is frozen (no gradient).  bf16 operands x [M][K], W [N][K], A [r][K],
+ * B [N][r], dY [M][N]; gate u8 [M] (0 = clean row, nonzero = gated row;
+ * NULL = every row clean: dA = dB = 0, dx = dY W).  U and dT are rounded to
+ * bf16 between the products (as the forward's adapter input is).
+ * W_t (optional, bf16 [K][N], ld ldwt): the frozen weight transposed once
+ * (uno_transpose_bf16).  With it (and a gate) dx, U and dT run on the
+ * forward's tuned kernels (every operand with the reduction index
+ * contiguous; A^T and B^T are transposed per call); without it every
+ * product runs on a generic kernel that reads W as stored.  The workspace
+ * query takes with_w_t accordingly.
+ * Requirements: N % 32 == 0, K % 8 == 0, r % 8 == 0, every leading dimension
+ * a multiple of 8 and at least its row width, every matrix and the
+ * workspace 16-byte aligned; workspace from the query (U and dT).
+ * ------------------------------------------------------------------------ */
+uno_status uno_gated_lora_backward_workspace(int64_t M, int64_t N, int64_t K, int64_t r, int32_t with_w_t,
+                                            size_t* bytes);
+uno_status uno_gated_lora_backward(hipStream_t stream, int64_t M, int64_t N, int64_t K, int64_t r,
+                                   const void* x, int64_t ldx, const void* W, int64_t ldw,
+                                   const void* A, int64_t lda, const void* B, int64_t ldb,
+                                   const uint8_t* gate, float lora_scale,
+                                   const void* dy, int64_t lddy,
+                                   void* dx, int64_t lddx, float* dA, int64_t ldda, float* dB, int64_t lddb,
+                                   const void* W_t, int64_t ldwt,
+                                   void* workspace, size_t workspace_bytes);
+
+/* --------------------------------------------------------------------------
  * Distillation losses of row pairs (the training side of the gated forward).
  * Source: Uno summary (hyper.ai), section "方法", the paragraphs on diffusion
  * distillation: the objective alpha * L_DCD + beta * L_TV; one forward over

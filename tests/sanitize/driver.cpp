@@ -103,6 +103,20 @@ int main() {
                                                            1.f, (int32_t*)D, (int32_t*)D, (int32_t*)D, D, big),
          false);
 
+  // gated-LoRA backward
+  expect("lora bwd ws", uno_gated_lora_backward_workspace(1024, 4096, 4096, 128, 1, &bytes), true);
+  expect("lora bwd", uno_gated_lora_backward(s, 64, 256, 128, 16, D, 128, D, 128, D, 128, D, 16, (const uint8_t*)D,
+                                             1.f, D, 256, D, 128, (float*)D, 128, (float*)D, 16, nullptr, 0, D, big),
+         true);
+  expect("lora bwd wt", uno_gated_lora_backward(s, 64, 256, 128, 16, D, 128, D, 128, D, 128, D, 16,
+                                                (const uint8_t*)D, 1.f, D, 256, D, 128, (float*)D, 128, (float*)D, 16,
+                                                D, 256, D, big), true);
+  expect("lora bwd N", uno_gated_lora_backward(s, 64, 250, 128, 16, D, 128, D, 128, D, 128, D, 16,
+                                               (const uint8_t*)D, 1.f, D, 256, D, 128, (float*)D, 128, (float*)D, 16,
+                                               nullptr, 0, D, big), false);
+  expect("transpose", uno_transpose_bf16(s, 100, 60, D, 64, D, 104), true);
+  expect("transpose ld", uno_transpose_bf16(s, 100, 60, D, 50, D, 104), false);
+
   // distillation losses
   expect("distill", uno_distill_loss(s, UNO_BF16, 2, 8, V, D, 16 * V, V, D, 16 * V, V, 1.f, 1.f, 1.f, 1.f, (float*)D,
                                      (float*)D, D, 16 * V, V), true);

@@ -26,6 +26,7 @@ size_t gated_lora_workspace_bytes(uno_dtype, int64_t, int64_t, int64_t, int64_t)
 size_t lora_down_part_bytes(int64_t, int64_t, int64_t) { return 256; }
 size_t sample_rows_workspace_bytes(int, int) { return 256; }
 size_t tree_attention_workspace_bytes(int, int, int, int, int, int) { return 256; }
+size_t lora_backward_workspace_bytes(int64_t, int64_t, int64_t, int64_t, int) { return 256; }
 size_t tree_build_workspace_bytes(int, int, int) { return 256; }
 size_t tree_verify_workspace_bytes(int, int, int, int, int, int) { return 256; }
 size_t verify_linear_workspace_bytes(int, int, int) { return 256; }
@@ -50,6 +51,10 @@ hipError_t launch_step_finish(const StepFinishArgs&, hipStream_t) { return launc
 hipError_t launch_step_setup(const StepSetupArgs&, hipStream_t) { return launched(); }
 hipError_t launch_tree_attention(const TreeAttnArgs&, hipStream_t) { return launched(); }
 hipError_t launch_distill(const DistillArgs&, hipStream_t) { return launched(); }
+hipError_t launch_lora_backward(const LoraBackwardArgs&, hipStream_t) { return launched(); }
+hipError_t launch_transpose_bf16(const void*, int64_t, void*, int64_t, int64_t, int64_t, hipStream_t) {
+  return launched();
+}
 hipError_t launch_tree_build(const TreeBuildArgs&, hipStream_t) { return launched(); }
 hipError_t launch_tree_verify(const TreeVerifyArgs&, hipStream_t) { return launched(); }
 hipError_t launch_verify_linear(const VerifyLinearArgs&, hipStream_t) { return launched(); }

@@ -28,7 +28,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(uno_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(uno_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_and_binding_agree():
@@ -288,6 +288,41 @@ def test_tree_verify_wor_rejects_bad_calls(lib):
     assert call(tok=None) == INVALID
     assert call(T=-1.0) == INVALID
     assert call(wsb=wor - 1) == WORKSPACE
+
+
+def test_gated_lora_backward_rejects_bad_calls(lib):
+    ws = ctypes.c_size_t(0)
+    assert lib.uno_gated_lora_backward_workspace(1024, 4096, 4096, 128, 0, ctypes.byref(ws)) == OK
+    assert ws.value >= 2 * 1024 * 128 * 2
+    plain = ws.value
+    assert lib.uno_gated_lora_backward_workspace(1024, 4096, 4096, 128, 1, ctypes.byref(ws)) == OK
+    assert ws.value > plain                               # the transposes of A and B
+    assert lib.uno_gated_lora_backward_workspace(1024, 4008, 4096, 128, 0, ctypes.byref(ws)) == UNSUPPORTED
+
+    def call(**kw):
+        a = dict(M=64, N=256, K=128, r=16, x=FAKE16, ldx=128, w=FAKE16, ldw=128, a=FAKE16, lda=128, b=FAKE16, ldb=16,
+                 g=FAKE16, s=1.0, dy=FAKE16, lddy=256, dx=FAKE16, lddx=128, da=FAKE16, ldda=128, db=FAKE16, lddb=16,
+                 wt=None, ldwt=0, ws=FAKE16, wsb=16)
+        a.update(kw)
+        return lib.uno_gated_lora_backward(None, a["M"], a["N"], a["K"], a["r"], a["x"], a["ldx"], a["w"], a["ldw"],
+                                           a["a"], a["lda"], a["b"], a["ldb"], a["g"], a["s"], a["dy"], a["lddy"],
+                                           a["dx"], a["lddx"], a["da"], a["ldda"], a["db"], a["lddb"], a["wt"],
+                                           a["ldwt"], a["ws"], a["wsb"])
+    assert call(M=0) == INVALID
+    assert call(N=250, lddy=256) == UNSUPPORTED
+    assert call(K=100, ldx=104, lda=104, ldw=104, lddx=104, ldda=104) == UNSUPPORTED
+    assert call(x=None) == INVALID
+    assert call(w=None) == INVALID                     # W is read for dx
+    assert call(ldb=8) == INVALID
+    assert call(lddy=260) == UNSUPPORTED
+    assert call(dy=ctypes.c_void_p(0x10008)) == UNSUPPORTED
+    assert call(s=float("nan")) == INVALID
+    assert call(wsb=8) == WORKSPACE
+    assert call(wt=FAKE16, ldwt=128) == INVALID           # ldwt below N
+    assert call(wt=FAKE16, ldwt=260) == INVALID           # not a multiple of 8
+    assert lib.uno_transpose_bf16(None, 0, 8, FAKE16, 8, FAKE16, 8) == INVALID
+    assert lib.uno_transpose_bf16(None, 8, 8, FAKE16, 7, FAKE16, 8) == INVALID
+    assert lib.uno_transpose_bf16(None, 8, 8, ctypes.c_void_p(0x10001), 8, FAKE16, 8) == INVALID
 
 
 def test_distill_loss_rejects_bad_calls(lib):

@@ -24,6 +24,7 @@ _T_ATT_Q, _T_ATT_KC, _T_ATT_VC, _T_ATT_KT, _T_ATT_VT = 31, 32, 33, 34, 35
 _T_TREE_SHAPE, _T_TREE_BASE, _T_TREE_P, _T_TREE_Q, _T_TREE_TOK = 41, 42, 43, 44, 45
 _T_TREE_UACC, _T_TREE_US = 46, 47
 _T_BUILD_U = 48
+_T_BWD_DY = 71
 
 
 def rng_for(seed, *tags):
@@ -97,6 +98,21 @@ def gated_lora_case(m, n, k, r, dtype="bf16", seed=0, gate=None, weight_std=0.02
         out[name] = st
         out[name + "_f32"] = val
     return out
+
+
+def lora_backward_case(m, n, k, r, seed=0, gate=None, weight_std=0.02, adapter_std=0.05):
+    """Inputs of the gated-LoRA backward, bf16: the projection of
+    gated_lora_case with A, B ~ N(0, adapter_std^2) (large enough that the
+    adapter's share of dx is well above bf16 rounding) and the upstream
+    gradient dY [m, n] ~ N(0, 1)."""
+    c = gated_lora_case(m, n, k, r, "bf16", seed=seed, gate=gate, weight_std=weight_std)
+    for name, tag in (("a", _T_A), ("b", _T_B)):
+        shape = (r, k) if name == "a" else (n, r)
+        arr = rng_for(seed, tag, 1).standard_normal(shape, dtype=np.float32) * np.float32(adapter_std)
+        c[name], c[name + "_f32"] = _store(arr, "bf16")
+    dy = rng_for(seed, _T_BWD_DY).standard_normal((m, n), dtype=np.float32)
+    c["dy"], c["dy_f32"] = _store(dy, "bf16")
+    return c
 
 
 def default_gate(m, block=8):
