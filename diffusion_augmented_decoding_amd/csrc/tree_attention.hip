@@ -34,6 +34,8 @@
 // Workgroups are numbered so that the tiles sharing one (batch, KV head, key
 // split) land on one XCD (hardware deals workgroups to the 8 XCDs round
 // robin): their common K/V blocks are fetched into that XCD's L2 once.
+#include <stdlib.h>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -49,7 +51,7 @@ constexpr int kMaxNodes = 256;
 static_assert(kMaxNodes <= kThreads, "one thread per tree node in the set-up");
 constexpr int kVtStride = 36;           // bf16 per transposed-V row (32 keys + pad)
 constexpr int kXcd = 8;
-constexpr int kTargetWgs = 512;         // 2 resident workgroups per CU (register-bound)
+constexpr int kTargetWgs = 256;         // 1 resident workgroup per CU (register-bound with the prefetch)
 constexpr int kMrgStride = kHD + 4;     // fp32 row stride of the merge buffer (bank spread)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -74,9 +76,11 @@ AttnPlan make_plan(int batch, int n, int ctx, int H, int Hkv) {
   p.tiles = (n * G + 31) / 32;
   p.nblk = (ctx + n + kKB - 1) / kKB;
   const int64_t base = int64_t(p.tiles) * Hkv * batch;
+  int64_t target = kTargetWgs;
+  if (const char* env = tuning_env("UNO_TREE_ATTN_WGS")) target = atoi(env);   // tuning build only
   int ks = 1;
-  if (base < kTargetWgs) {
-    ks = int(kTargetWgs / base);      // every workgroup resident at once
+  if (base < target) {
+    ks = int(target / base);          // every workgroup resident at once
     const int most = (p.nblk + kWaves - 1) / kWaves;   // at least one block per wave
     if (ks > most) ks = most;
     if (ks < 1) ks = 1;
@@ -222,7 +226,9 @@ __global__ __launch_bounds__(kThreads) void tree_attn_kernel(TreeAttnArgs a, Att
 
   uint16_t* myvt = vt[wave];
   for (int i = 0, j = j0; i < nb; ++i, j += stride) {
-    if (i > 0) load_block(j, kr, vr);
+    // the wave's next key block is loaded while this one is computed
+    u32x4 kn[8], vn[8];
+    if (i + 1 < nb) load_block(j + stride, kn, vn);
     const u32x4(&kcur)[8] = kr;
     const u32x4(&vcur)[8] = vr;
     const int kb = j * kKB;
@@ -303,6 +309,13 @@ __global__ __launch_bounds__(kThreads) void tree_attn_kernel(TreeAttnArgs a, Att
       }
     }
     wave_sync_lds();
+    if (i + 1 < nb) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        kr[t] = kn[t];
+        vr[t] = vn[t];
+      }
+    }
   }
 
   // ---- merge the 4 waves' states: (2,3) -> (0,1), then 1 -> 0; vt reused as fp32 [32 rows][128 d]

@@ -21,10 +21,13 @@
 //     of every node); a few more blocks mark the values the second launch
 //     publishes as not yet written and reset its work counter.
 //  2. tree_flow: blocks take work items in increasing order from a counter:
-//     first the residual rounds (round j, node, 8192-token chunk: F(c_j) of
-//     the chunk), then one walk per tree (one wave walks it with gathered
-//     probabilities and the (c, D) sequences), then the draw's segment masses
-//     per (tree, chunk), then one inverse-CDF search per tree.  An item waits
+//     first one gather per node with children (its children's p and q at
+//     their tokens, published per child), then the residual rounds (round j,
+//     node, 8192-token chunk: F(c_j) of the chunk), then one walk per tree
+//     (one wave walks it with the gathered probabilities and the (c, D)
+//     sequences, waiting for a node's rounds only once a child is rejected),
+//     then the draw's segment masses per (tree, chunk), then one inverse-CDF
+//     search per tree.  An item waits
 //     only for values that items with smaller numbers publish, so the item
 //     with the smallest number in progress always has its inputs and the
 //     launch finishes for any number of resident blocks.  Published values
@@ -78,6 +81,7 @@ struct TreeWs {
   int* list;         // [batch][n]: those nodes in increasing id
   int* kids;         // without replacement: [batch][n][max_children] children in increasing id
   float* ck;         // without replacement: [batch][64] C_k of the walk's last node
+  uint64_t* kidpq;   // [batch][n]: (p, q) at a node's token under its parent's AR row and its depth's draft row
 };
 constexpr float kZEps = 1e-6f;   // a remaining draft mass below this is taken as none (fp32 resolves no less)
 constexpr int kMaxWorChildren = 64;
@@ -111,6 +115,8 @@ TreeWs tree_ws(void* base, int batch, int n, int dmax, int maxc, int vocab, int 
   p += align_up(size_t(batch) * sizeof(int), 256);
   w.list = reinterpret_cast<int*>(p);
   p += align_up(size_t(batch) * n * sizeof(int), 256);
+  w.kidpq = reinterpret_cast<uint64_t*>(p);
+  p += align_up(size_t(batch) * n * sizeof(uint64_t), 256);
   w.kids = nullptr;
   w.ck = nullptr;
   if (wor) {
@@ -218,17 +224,20 @@ __global__ __launch_bounds__(kChunkThreads) void tree_stats_kernel(TreeVerifyArg
   const int64_t nf = int64_t(a.max_children) * a.batch * a.n_tree * nc;
   const int64_t nseg = int64_t(a.batch) * nc * 2 * kSegPerChunk;
   const int64_t nck = a.wor ? int64_t(a.batch) * kMaxWorChildren : 0;
+  const int64_t nkp = int64_t(a.batch) * a.n_tree;
   const int64_t stride = int64_t(ninit_blocks) * kChunkThreads;
-  for (int64_t t = int64_t(blk - nstat - a.batch) * kChunkThreads + threadIdx.x; t < nf + nseg + a.batch + nck;
-       t += stride) {
+  for (int64_t t = int64_t(blk - nstat - a.batch) * kChunkThreads + threadIdx.x;
+       t < nf + nseg + a.batch + nck + nkp; t += stride) {
     if (t < nf)
       w.fpart[t] = kUnset;
     else if (t < nf + nseg)
       w.seg[t - nf] = kUnset;
     else if (t < nf + nseg + a.batch)
       w.walk[t - nf - nseg] = kWalkUnset;
-    else
+    else if (t < nf + nseg + a.batch + nck)
       w.ck[t - nf - nseg - a.batch] = kUnset;
+    else
+      w.kidpq[t - nf - nseg - a.batch - nck] = kWalkUnset;
   }
   if (blk == nstat + a.batch && threadIdx.x == 0) {
     w.queue[0] = 0;
@@ -410,6 +419,40 @@ __device__ __forceinline__ void wor_patch(float (&wv)[8], int e0, const Sib& s, 
 }
 
 // ---------------------------------------------------------------- flow items
+// Gather of node i of tree b (one whole wave): for every child v of the node,
+// p and q at v's token (p from the node's AR row, q from the draft row of the
+// children's depth), published as one word per child (all ones until written;
+// an out-of-range token gives (0, 0)).
+template <typename T>
+__device__ void gather_item(const TreeVerifyArgs& a, const TreeWs& w, int node_idx) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int n = a.n_tree, rpb = n + a.max_depth;
+  const int b = node_idx / n, i = node_idx - b * n;
+  if (w.bad[b]) return;   // the walk publishes the malformed result without reading these
+  const NodeInfo inf = w.info[node_idx];
+  if (inf.nchild == 0) return;
+  const int ns = tree_stat_splits(a.batch, n, a.max_depth, a.vocab);
+  RowStat st[2];
+  wave_merge_two(w.part + (int64_t(b) * rpb + i) * ns, w.part + (int64_t(b) * rpb + n + inf.depth) * ns, ns, st);
+  const T* prow = tree_row<T>(a, b, i);
+  const T* qrow = tree_row<T>(a, b, n + inf.depth);
+  const int32_t* par = a.parent + int64_t(b) * n;
+  for (int base = i + 1; base < n; base += kWave) {
+    const int v = base + lane;
+    if (v < n && par[v] == i) {
+      const int t = a.tokens[int64_t(b) * n + v];
+      float pt = 0.f, qt = 0.f;
+      if (t >= 0 && t < a.vocab) {
+        pt = prob_at<T>(prow, t, st[0], a.scale_log2);
+        qt = prob_at<T>(qrow, t, st[1], a.scale_log2);
+      }
+      __hip_atomic_store(w.kidpq + int64_t(b) * n + v,
+                         uint64_t(__float_as_uint(pt)) | (uint64_t(__float_as_uint(qt)) << 32), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 // Round j (1-based) of node node_idx, chunk c: F(c_j) of the chunk, with
 // (c_j, D_j) replayed from the node's earlier rounds.  Whole block.
 template <typename T>
@@ -579,35 +622,39 @@ __device__ void walk_item(const TreeVerifyArgs& a, const TreeWs& w, int b) {
   const int32_t* par = a.parent + int64_t(b) * n;
   int cur = 0, depth = 0, L = 0;
   while (true) {
-    const RowStat sp = wave_merge_chunks(w.part + (int64_t(b) * rpb + cur) * ns, ns);
-    RowStat sq{};
     const bool has_q = depth < a.max_depth;
-    if (has_q) sq = wave_merge_chunks(w.part + (int64_t(b) * rpb + n + depth) * ns, ns);
-    const T* prow = tree_row<T>(a, b, cur);
-    const T* qrow = has_q ? tree_row<T>(a, b, n + depth) : prow;
     float c = 0.f, D = 1.f;
     bool frozen = false, haskids = false, accepted = false;
     int rank = 0;
-    // the residual masses after the first kRoundBatch rejections, waited for together
+    // the residual masses after the first kRoundBatch rejections, waited for
+    // together at the node's first rejection
     const int nkids = w.info[int64_t(b) * n + cur].nchild;
     float Fr[kRoundBatch];
-    if (nkids > 0)
-      wave_sums_published(w.fpart + (int64_t(b) * n + cur) * nc, int64_t(bn_total) * nc, min(nkids, kRoundBatch),
-                          nc, w.err, Fr);
+    bool have_fr = false;
     for (int base = cur + 1; base < n && !accepted; base += kWave) {
       const int v = base + lane;
       const bool kid = v < n && par[v] == cur;
       uint64_t mask = wave_ballot(kid);
-      // every child's token, probabilities and uniform, loaded by its own lane
+      // every child's token, gathered probabilities and uniform, loaded by its own lane
       int tl = -1;
       float ptl = 0.f, qtl = 0.f, ul = 1.f;
       if (kid) {
         tl = a.tokens[int64_t(b) * n + v];
         ul = a.u_acc[int64_t(b) * n + v];
-        if (tl >= 0 && tl < a.vocab) {
-          ptl = prob_at<T>(prow, tl, sp, sl2);
-          qtl = prob_at<T>(qrow, tl, sq, sl2);
+      }
+      uint64_t word = 0;
+      for (int it = 0;; ++it) {
+        word = kid ? __hip_atomic_load(w.kidpq + int64_t(b) * n + v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+        if (!wave_ballot(word == kWalkUnset)) break;
+        if (it == kSpinMax) {
+          if (lane == 0) atomicOr(w.err, 1);
+          break;
         }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      if (kid) {
+        ptl = __uint_as_float(uint32_t(word));
+        qtl = __uint_as_float(uint32_t(word >> 32));
       }
       while (mask && !accepted) {
         const int l = int(__builtin_ctzll(mask));
@@ -627,6 +674,11 @@ __device__ void walk_item(const TreeVerifyArgs& a, const TreeWs& w, int b) {
         } else if (!frozen) {   // residual after this rejection
           float F = 0.f;
           if (rank <= kRoundBatch) {
+            if (!have_fr) {
+              wave_sums_published(w.fpart + (int64_t(b) * n + cur) * nc, int64_t(bn_total) * nc,
+                                  min(nkids, kRoundBatch), nc, w.err, Fr);
+              have_fr = true;
+            }
 #pragma unroll
             for (int r = 0; r < kRoundBatch; ++r)
               if (r == rank - 1) F = Fr[r];
@@ -948,7 +1000,8 @@ __global__ __launch_bounds__(kChunkThreads) void tree_flow_kernel(TreeVerifyArgs
   } else {
     per_round = a.batch * n * nc;
   }
-  const int n_round = a.max_children * per_round;
+  const int n_gather = per_round / nc;   // one per (listed) node
+  const int n_round = n_gather + a.max_children * per_round;
   const int n_walk = n_round + a.batch;
   const int n_seg = n_walk + a.batch * nc;
   const int total = n_seg + a.batch;
@@ -960,7 +1013,9 @@ __global__ __launch_bounds__(kChunkThreads) void tree_flow_kernel(TreeVerifyArgs
     __syncthreads();
     if (it >= total) break;
     if (it < n_round) {
-      const int j = it / per_round + 1, rem = it % per_round;
+      const bool gather = it < n_gather;
+      const int r_it = it - n_gather;
+      const int j = gather ? 0 : r_it / per_round + 1, rem = gather ? it * nc : r_it % per_round;
       const int slot = rem / nc;
       int node_idx = slot;
       if (listed) {   // slot -> (tree, position in its list): the last tree with sh_pre[b] <= slot
@@ -971,7 +1026,11 @@ __global__ __launch_bounds__(kChunkThreads) void tree_flow_kernel(TreeVerifyArgs
         }
         node_idx = lo * n + w.list[int64_t(lo) * n + (slot - sh_pre[lo])];
       }
-      round_item<T>(a, w, j, node_idx, rem % nc);
+      if (gather) {
+        if (threadIdx.x < kWave) gather_item<T>(a, w, node_idx);
+      } else {
+        round_item<T>(a, w, j, node_idx, rem % nc);
+      }
     } else if (it < n_walk) {
       if (threadIdx.x < kWave) {
         if (a.wor)
@@ -998,7 +1057,7 @@ hipError_t launch_tree(const TreeVerifyArgs& a, hipStream_t stream) {
   const int nc = num_chunks(a.vocab);
   const int nstat = a.batch * (a.n_tree + a.max_depth) * ns;
   const int64_t init = int64_t(a.max_children) * a.batch * a.n_tree * nc + int64_t(a.batch) * nc * 2 * kSegPerChunk +
-                       a.batch + (a.wor ? int64_t(a.batch) * kMaxWorChildren : 0);
+                       a.batch + (a.wor ? int64_t(a.batch) * kMaxWorChildren : 0) + int64_t(a.batch) * a.n_tree;
   const int ninit = int(std::min<int64_t>(64, (init + kChunkThreads - 1) / kChunkThreads));
   {
     ProfileScope ps("uno_tree_stats", stream);
@@ -1025,7 +1084,8 @@ size_t tree_verify_workspace_bytes(int batch, int n, int dmax, int maxc, int voc
                  align_up(size_t(batch) * (n + dmax) * ns * sizeof(float2), 256) +
                  align_up(size_t(maxc > 0 ? maxc : 1) * batch * n * nc * sizeof(float), 256) +
                  align_up(size_t(batch) * sizeof(uint64_t), 256) + draw_seg_bytes(batch, vocab) + 256 +
-                 align_up(size_t(batch) * sizeof(int), 256) + align_up(size_t(batch) * n * sizeof(int), 256);
+                 align_up(size_t(batch) * sizeof(int), 256) + align_up(size_t(batch) * n * sizeof(int), 256) +
+                 align_up(size_t(batch) * n * sizeof(uint64_t), 256);
   if (wor)
     bytes += align_up(size_t(batch) * n * (maxc > 0 ? maxc : 1) * sizeof(int), 256) +
              align_up(size_t(batch) * kMaxWorChildren * sizeof(float), 256);
