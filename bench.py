@@ -927,7 +927,7 @@ def bench_lora_backward(args, dad, torch, reps=10):
     # phases of the call with W^T given: per-call transposes of A and B, the LoRA-down
     # for U and dT, the adapter gradients, the main GEMM for dx
     phases = {"transpose": ("uno_transpose",), "u_dt": ("uno_lora_down", "uno_lora_gate"),
-              "db": ("uno_lora_bwd_db",), "da": ("uno_lora_bwd_da",), "dx": ("uno_gemm",)}
+              "da_db": ("uno_lora_bwd_dadb",), "dx": ("uno_gemm",)}
     res = {"rows": M, "rank": r}
     for proj, N, K in (("q", 4096, 4096), ("gate_up", 12288, 4096), ("down", 4096, 12288)):
         x = (torch.randn((M, K), device=dev, generator=gen)).to(torch.bfloat16)
@@ -946,7 +946,7 @@ def bench_lora_backward(args, dad, torch, reps=10):
         for _ in range(reps):
             dad.gated_lora_backward(x, w, a, b, gate, dy, outputs=outs, workspace=ws, w_t=wt)
         torch.cuda.synchronize()
-        flops = {"transpose": 0.0, "u_dt": 2.0 * M * r * (K + N), "db": 2.0 * N * r * M, "da": 2.0 * r * K * M,
+        flops = {"transpose": 0.0, "u_dt": 2.0 * M * r * (K + N), "da_db": 2.0 * r * M * (N + K),
                  "dx": 2.0 * M * K * (N + r)}
         per = {}
         total_ms = 0.0

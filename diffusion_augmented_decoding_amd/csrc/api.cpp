@@ -229,7 +229,7 @@ uno_status uno_transpose_bf16(hipStream_t stream, int64_t rows, int64_t cols, co
   UNO_GUARD_BEGIN
   if (rows < 1 || cols < 1) return fail(UNO_ERR_INVALID_ARGUMENT, "rows and cols must be >= 1");
   if (rows > (int64_t(1) << 30) || cols > (int64_t(1) << 30)) return fail(UNO_ERR_UNSUPPORTED, "too large");
-  if ((cols + 63) / 64 > 0x7fffffff || (rows + 63) / 64 > 65535) return fail(UNO_ERR_UNSUPPORTED, "too many rows");
+  if (((cols + 63) / 64) * ((rows + 63) / 64) > 0x7fffffff) return fail(UNO_ERR_UNSUPPORTED, "too many tiles");
   if (!src || !dst) return fail(UNO_ERR_INVALID_ARGUMENT, "src and dst must be non-NULL");
   if (ld_src < cols || ld_dst < rows) return fail(UNO_ERR_INVALID_ARGUMENT, "leading dimension below the row width");
   if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 1u) != 0)

@@ -61,8 +61,9 @@ struct BwdGemm {
   void* c; int64_t ldc;
   float alpha;
   const uint8_t* gate;              // optional: rows with gate 0 are written as 0
-  int kt_per_split;                 // K tiles per blockIdx.z (split-K: raw fp32 partials to part)
-  float* part;                      // [splits][M][N] when gridDim.z > 1
+  int kt_per_split;                 // K tiles per split
+  int nsplit;                       // > 1: raw fp32 partials to part, summed by split_reduce_kernel
+  float* part;                      // [nsplit][M][N]
 };
 
 // One operand's K tile, global -> registers (two 16-byte vectors per thread).
@@ -151,15 +152,23 @@ __device__ __forceinline__ void frags(bf16x8 (&f)[2], const unsigned char* tile,
   }
 }
 
+// Two products in one launch (same operand layouts): blockIdx.z < z0 runs
+// split blockIdx.z of p0, the rest split blockIdx.z - z0 of p1; blockIdx.x
+// numbers the output tiles of either (row-major over the tile grid).
 template <bool AKX, bool BKX, bool OUTF32>
-__global__ __launch_bounds__(kThr) void bwd_gemm_kernel(BwdGemm p) {
+__global__ __launch_bounds__(kThr) void bwd_gemm_kernel(BwdGemm p0, BwdGemm p1, int z0) {
   __shared__ __align__(16) unsigned char smem[2 * kStageBytes];
   uint32_t lds_base = uint32_t(reinterpret_cast<uintptr_t>(smem));
   asm volatile("" : "+s"(lds_base));
-  const int n0 = blockIdx.x * kBT, m0 = blockIdx.y * kBT;
+  const bool first = int(blockIdx.z) < z0;
+  const BwdGemm& p = first ? p0 : p1;
+  const int zi = first ? int(blockIdx.z) : int(blockIdx.z) - z0;
+  const int tiles_n = (p.N + kBT - 1) / kBT;
+  if (int(blockIdx.x) >= tiles_n * ((p.M + kBT - 1) / kBT)) return;
+  const int n0 = (int(blockIdx.x) % tiles_n) * kBT, m0 = (int(blockIdx.x) / tiles_n) * kBT;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int wm = wave >> 1, wn = wave & 1;
-  const int kt0 = blockIdx.z * p.kt_per_split;
+  const int kt0 = zi * p.kt_per_split;
   const int nkt = min((p.K + kBK - 1) / kBK - kt0, p.kt_per_split);
 
   auto load_tile = [&](int kt, u32x4 (&va)[2], u32x4 (&vb)[2]) {
@@ -215,8 +224,8 @@ __global__ __launch_bounds__(kThr) void bwd_gemm_kernel(BwdGemm p) {
 
   // lane l holds C[m = .. + 32 j + l % 32][n = .. + 32 i + 8 g + 4 (l / 32) + e] in acc[i][j][4 g + e]
   const int lh = lane >> 5;
-  if (gridDim.z > 1) {   // raw partial sums of this split
-    float* part = p.part + int64_t(blockIdx.z) * p.M * p.N;
+  if (p.nsplit > 1) {   // raw partial sums of this split
+    float* part = p.part + int64_t(zi) * p.M * p.N;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int m = m0 + wm * 64 + 32 * j + (lane & 31);
@@ -258,15 +267,18 @@ __global__ __launch_bounds__(kThr) void bwd_gemm_kernel(BwdGemm p) {
   }
 }
 
-// out[m][n] = alpha * g(m) * sum_s part[s][m][n] (splits summed in order); 4 columns per thread.
+// out[m][n] = alpha * g(m) * sum_s part[s][m][n] (splits summed in order); 4
+// columns per thread; quads [0, nq0) belong to p0, the rest to p1.
 template <bool OUTF32>
-__global__ __launch_bounds__(256) void split_reduce_kernel(BwdGemm p, int splits) {
-  const int64_t q = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t nq = int64_t(p.M) * (p.N / 4);
+__global__ __launch_bounds__(256) void split_reduce_kernel(BwdGemm p0, BwdGemm p1, int64_t nq0, int64_t nq) {
+  int64_t q = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (q >= nq) return;
+  const bool first = q < nq0;
+  const BwdGemm& p = first ? p0 : p1;
+  if (!first) q -= nq0;
   const int m = int(q / (p.N / 4)), n = int(q % (p.N / 4)) * 4;
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  for (int z = 0; z < splits; ++z) s += *reinterpret_cast<const f32x4*>(p.part + (int64_t(z) * p.M + m) * p.N + n);
+  for (int z = 0; z < p.nsplit; ++z) s += *reinterpret_cast<const f32x4*>(p.part + (int64_t(z) * p.M + m) * p.N + n);
   const float sc = (p.gate && p.gate[m] == 0) ? 0.f : p.alpha;
   s *= sc;
   if constexpr (OUTF32) {
@@ -292,22 +304,51 @@ size_t split_bytes(int M, int N, int K) {
   return s > 1 ? align_up(size_t(s) * M * N * sizeof(float), 256) : 0;
 }
 
+// Fixes a product's splits (its partials at part).
+void plan_splits(BwdGemm& p, float* part) {
+  const int nkt = (p.K + kBK - 1) / kBK;
+  const int splits = choose_splits(p.M, p.N, p.K);
+  p.kt_per_split = std::max(1, (nkt + splits - 1) / splits);
+  p.nsplit = std::max(1, (nkt + p.kt_per_split - 1) / p.kt_per_split);   // no empty split
+  p.part = part;
+}
+
+// One product, or two with the same operand layouts in one launch (p1 with
+// its partials after p0's), each followed by the split sums where split.
+template <bool AKX, bool BKX, bool OUTF32>
+hipError_t run2(BwdGemm p0, const BwdGemm* p1in, float* part, hipStream_t stream, const char* name) {
+  plan_splits(p0, part);
+  BwdGemm p1 = p0;
+  int z1 = 0;
+  if (p1in) {
+    p1 = *p1in;
+    plan_splits(p1, part + (p0.nsplit > 1 ? size_t(p0.nsplit) * p0.M * p0.N : 0));
+    z1 = p1.nsplit;
+  }
+  auto tiles = [](const BwdGemm& p) { return ((p.N + kBT - 1) / kBT) * ((p.M + kBT - 1) / kBT); };
+  const int gx = std::max(tiles(p0), p1in ? tiles(p1) : 0);
+  ProfileScope ps(name, stream);
+  hipLaunchKernelGGL((bwd_gemm_kernel<AKX, BKX, OUTF32>), dim3(gx, 1, p0.nsplit + z1), dim3(kThr), 0, stream, p0, p1,
+                     p0.nsplit);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t nq0 = p0.nsplit > 1 ? int64_t(p0.M) * (p0.N / 4) : 0;
+  const int64_t nq1 = (p1in && p1.nsplit > 1) ? int64_t(p1.M) * (p1.N / 4) : 0;
+  if (nq0 + nq1 == 0) return hipSuccess;
+  if (nq0 == 0) {   // only p1 is split
+    hipLaunchKernelGGL(split_reduce_kernel<OUTF32>, dim3(unsigned((nq1 + 255) / 256)), dim3(256), 0, stream, p1, p1,
+                       nq1, nq1);
+  } else {
+    hipLaunchKernelGGL(split_reduce_kernel<OUTF32>, dim3(unsigned((nq0 + nq1 + 255) / 256)), dim3(256), 0, stream,
+                       p0, p1, nq0, nq0 + nq1);
+  }
+  return hipGetLastError();
+}
+
 template <bool AKX, bool BKX, bool OUTF32>
 hipError_t run(BwdGemm p, float* part, hipStream_t stream, const char* name) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
-  const int nkt = (p.K + kBK - 1) / kBK;
-  const int splits = choose_splits(p.M, p.N, p.K);
-  p.kt_per_split = (nkt + splits - 1) / splits;
-  const int z = (nkt + p.kt_per_split - 1) / p.kt_per_split;   // no empty split
-  p.part = part;
-  ProfileScope ps(name, stream);
-  hipLaunchKernelGGL((bwd_gemm_kernel<AKX, BKX, OUTF32>),
-                     dim3((p.N + kBT - 1) / kBT, (p.M + kBT - 1) / kBT, z > 1 ? z : 1), dim3(kThr), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || z <= 1) return e;
-  const int64_t nq = int64_t(p.M) * (p.N / 4);
-  hipLaunchKernelGGL(split_reduce_kernel<OUTF32>, dim3(unsigned((nq + 255) / 256)), dim3(256), 0, stream, p, z);
-  return hipGetLastError();
+  return run2<AKX, BKX, OUTF32>(p, nullptr, part, stream, name);
 }
 
 BwdGemm gemm(int M, int N, int K, const void* a, int64_t lda, const void* b, int64_t ldb, void* c, int64_t ldc,
@@ -328,23 +369,79 @@ BwdGemm gemm(int M, int N, int K, const void* a, int64_t lda, const void* b, int
   return p;
 }
 
-// dst[c][r] = src[r][c] for a rows x cols bf16 matrix: 64 x 64 tiles through
-// LDS (one padding element per row), 256 threads, 2-byte accesses.
-__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ src, int64_t lds,
-                                                        uint16_t* __restrict__ dst, int64_t ldd, int rows,
-                                                        int cols) {
-  __shared__ uint16_t tile[64][65];
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int r = r0 + i, c = c0 + tx;
-    if (r < rows && c < cols) tile[i][tx] = src[int64_t(r) * lds + c];
+// dst[c][r] = src[r][c] for rows x cols bf16 matrices, one or two per launch
+// (blockIdx.z): 64 x 64 tiles through LDS; 16-byte loads along src rows and
+// 16-byte stores along dst rows where aligned and whole, single elements
+// otherwise.
+struct TransposeJob {
+  const uint16_t* src;
+  int64_t lds;
+  uint16_t* dst;
+  int64_t ldd;
+  int rows, cols;
+};
+
+constexpr int kTPitch = 64 + 8;   // LDS row pitch (elements)
+
+__global__ __launch_bounds__(256) void transpose_kernel(TransposeJob j0, TransposeJob j1) {
+  __shared__ __align__(16) uint16_t tile[64 * kTPitch];
+  const TransposeJob& j = blockIdx.z == 0 ? j0 : j1;
+  const int tc = (j.cols + 63) / 64;
+  if (int(blockIdx.x) >= tc * ((j.rows + 63) / 64)) return;
+  const int r0 = (int(blockIdx.x) / tc) * 64, c0 = (int(blockIdx.x) % tc) * 64;
+  const bool vsrc = (j.lds % 8 == 0) && ((reinterpret_cast<uintptr_t>(j.src) & 15u) == 0);
+  const bool vdst = (j.ldd % 8 == 0) && ((reinterpret_cast<uintptr_t>(j.dst) & 15u) == 0);
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int q = threadIdx.x + 256 * rr;
+    const int row = q >> 3, cc = (q & 7) * 8;
+    const int r = r0 + row, c = c0 + cc;
+    uint16_t v[8];
+    if (r < j.rows && vsrc && c + 8 <= j.cols) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(j.src + int64_t(r) * j.lds + c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = uint16_t(x[e] & 0xffffu);
+        v[2 * e + 1] = uint16_t(x[e] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (r < j.rows && c + e < j.cols) ? j.src[int64_t(r) * j.lds + c + e] : 0;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[row * kTPitch + cc + e] = v[e];
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int c = c0 + i, r = r0 + tx;
-    if (c < cols && r < rows) dst[int64_t(c) * ldd + r] = tile[tx][i];
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int q = threadIdx.x + 256 * rr;
+    const int orow = q >> 3, rc = (q & 7) * 8;   // dst row = src column c0 + orow
+    const int c = c0 + orow, r = r0 + rc;
+    if (c >= j.cols) continue;
+    uint16_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = tile[(rc + e) * kTPitch + orow];
+    uint16_t* d = j.dst + int64_t(c) * j.ldd + r;
+    if (vdst && r + 8 <= j.rows) {
+      u32x4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = uint32_t(v[2 * e]) | (uint32_t(v[2 * e + 1]) << 16);
+      *reinterpret_cast<u32x4*>(d) = x;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (r + e < j.rows) d[e] = v[e];
+    }
   }
+}
+
+hipError_t launch_transpose2(const TransposeJob& j0, const TransposeJob* j1, hipStream_t stream) {
+  const TransposeJob& k1 = j1 ? *j1 : j0;
+  auto tiles = [](const TransposeJob& j) { return int64_t((j.cols + 63) / 64) * ((j.rows + 63) / 64); };
+  const int64_t gx = std::max(tiles(j0), tiles(k1));
+  ProfileScope ps("uno_transpose", stream);
+  hipLaunchKernelGGL(transpose_kernel, dim3(unsigned(gx), 1, j1 ? 2 : 1), dim3(256), 0, stream, j0, k1);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -352,11 +449,9 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restri
 hipError_t launch_transpose_bf16(const void* src, int64_t lds, void* dst, int64_t ldd, int64_t rows, int64_t cols,
                                  hipStream_t stream) {
   if (rows <= 0 || cols <= 0) return hipSuccess;
-  ProfileScope ps("uno_transpose", stream);
-  hipLaunchKernelGGL(transpose_kernel, dim3(unsigned((cols + 63) / 64), unsigned((rows + 63) / 64)), dim3(256), 0,
-                     stream, static_cast<const uint16_t*>(src), lds, static_cast<uint16_t*>(dst), ldd, int(rows),
-                     int(cols));
-  return hipGetLastError();
+  const TransposeJob j{static_cast<const uint16_t*>(src), lds, static_cast<uint16_t*>(dst), ldd, int(rows),
+                       int(cols)};
+  return launch_transpose2(j, nullptr, stream);
 }
 
 namespace {
@@ -371,8 +466,9 @@ hipError_t launch_with_wt(const LoraBackwardArgs& a, uint16_t* u, uint16_t* dt, 
   uint16_t* bt = reinterpret_cast<uint16_t*>(ws);                        // B^T [r][N]
   ws += align_up(size_t(N) * r * 2, 256);
   float* part = reinterpret_cast<float*>(ws);
-  hipError_t e = launch_transpose_bf16(a.a, a.lda, at, r, r, K, stream);
-  if (e == hipSuccess) e = launch_transpose_bf16(a.b, a.ldb, bt, N, N, r, stream);
+  const TransposeJob ja{static_cast<const uint16_t*>(a.a), a.lda, at, r, int(r), int(K)};
+  const TransposeJob jb{static_cast<const uint16_t*>(a.b), a.ldb, bt, N, int(N), int(r)};
+  hipError_t e = launch_transpose2(ja, &jb, stream);
   if (e != hipSuccess) return e;
   LoraDownArgs ld{};
   ld.M = M;
@@ -397,11 +493,11 @@ hipError_t launch_with_wt(const LoraBackwardArgs& a, uint16_t* u, uint16_t* dt, 
   ld.t = dt;
   e = launch_lora_down(ld, stream);                                      // dT = s g (dY B)
   if (e != hipSuccess) return e;
-  e = run<true, true, true>(gemm(int(N), int(r), int(M), a.dy, a.lddy, u, r, a.db, a.lddb, a.lora_scale, nullptr),
-                            part, stream, "uno_lora_bwd_db");
-  if (e != hipSuccess) return e;
-  e = run<true, true, true>(gemm(int(r), int(K), int(M), dt, r, a.x, a.ldx, a.da, a.ldda, 1.f, nullptr), part, stream,
-                            "uno_lora_bwd_da");
+  {   // dB and dA in one launch (same layouts)
+    const BwdGemm gda = gemm(int(r), int(K), int(M), dt, r, a.x, a.ldx, a.da, a.ldda, 1.f, nullptr);
+    e = run2<true, true, true>(gemm(int(N), int(r), int(M), a.dy, a.lddy, u, r, a.db, a.lddb, a.lora_scale, nullptr),
+                               &gda, part, stream, "uno_lora_bwd_dadb");
+  }
   if (e != hipSuccess || !a.dx) return e;
   GatedLoraArgs g{};                                                     // dx = dY W + dT A
   g.dtype = UNO_BF16;
@@ -429,8 +525,8 @@ hipError_t launch_with_wt(const LoraBackwardArgs& a, uint16_t* u, uint16_t* dt, 
 
 size_t lora_backward_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t r, int with_wt) {
   const int m = int(M), n = int(N), k = int(K), rr = int(r);
-  size_t part = std::max({split_bytes(m, rr, k), split_bytes(m, rr, n), split_bytes(n, rr, m),
-                          split_bytes(rr, k, m), split_bytes(m, k, n + rr)});
+  size_t part = std::max({split_bytes(m, rr, k), split_bytes(m, rr, n), split_bytes(n, rr, m) + split_bytes(rr, k, m),
+                          split_bytes(m, k, n + rr)});
   size_t extra = 0;
   if (with_wt) {   // A^T, B^T, the LoRA-down's and the main GEMM's partials
     extra = align_up(size_t(K) * r * 2, 256) + align_up(size_t(N) * r * 2, 256);
@@ -458,12 +554,12 @@ hipError_t launch_lora_backward(const LoraBackwardArgs& a, hipStream_t stream) {
                               stream, "uno_lora_bwd_dt");
   if (e != hipSuccess) return e;
   // dB = s dY^T U: A(n, m) = dY[m][n] ("kx"), B(m, j) = U[m][j] ("kx")
-  e = run<true, true, true>(gemm(N, r, M, a.dy, a.lddy, u, r, a.db, a.lddb, a.lora_scale, nullptr), part, stream,
-                            "uno_lora_bwd_db");
-  if (e != hipSuccess) return e;
-  // dA = dT^T x: A(j, m) = dT[m][j] ("kx"), B(m, k) = x[m][k] ("kx")
-  e = run<true, true, true>(gemm(r, K, M, dt, r, a.x, a.ldx, a.da, a.ldda, 1.f, nullptr), part, stream,
-                            "uno_lora_bwd_da");
+  // dA = dT^T x: A(j, m) = dT[m][j] ("kx"), B(m, k) = x[m][k] ("kx"); one launch with dB
+  {
+    const BwdGemm gda = gemm(r, K, M, dt, r, a.x, a.ldx, a.da, a.ldda, 1.f, nullptr);
+    e = run2<true, true, true>(gemm(N, r, M, a.dy, a.lddy, u, r, a.db, a.lddb, a.lora_scale, nullptr), &gda, part,
+                               stream, "uno_lora_bwd_dadb");
+  }
   if (e != hipSuccess) return e;
   if (!a.dx) return hipSuccess;
   // dx = [dY | dT] [W ; A]: A side "xk" in both segments, W(n, k) and A(j, k) "kx"

@@ -349,7 +349,7 @@ uno_status uno_psi_spec_build_tree(hipStream_t stream, uno_dtype logit_dtype, in
  * dst[c][r] = src[r][c] for a rows x cols bf16 matrix (src ld ld_src >=
  * cols, dst ld ld_dst >= rows, both 2-byte aligned, not overlapping).  For
  * callers of uno_gated_lora_backward: the frozen AR weight W [N][K] is
- * transposed once into W^T [K][N].  rows <= 64 * 65535.
+ * transposed once into W^T [K][N].  At most 2^31 - 1 tiles of 64 x 64.
  * ------------------------------------------------------------------------ */
 uno_status uno_transpose_bf16(hipStream_t stream, int64_t rows, int64_t cols, const void* src, int64_t ld_src,
                               void* dst, int64_t ld_dst);
