@@ -10,7 +10,11 @@ give no layer internals.  Readings taken here:
 
 * Qwen3-8B shapes: hidden 4096, MLP 12288, 32 query / 8 KV heads of 128;
   pre-norm RMSNorm (eps 1e-6) before attention and before the MLP, SwiGLU MLP
-  (silu(gate) * up), residual adds, no biases, no per-head q/k norm;
+  (silu(gate) * up), residual adds, no biases;
+* Qwen3's per-head RMSNorm of q and k (weights q_norm, k_norm of 128, the
+  same eps) over each 128-wide head, after the projection and before the
+  rotation; optional (a layer without the two weights skips it).  The normed
+  values are not stored: the one bf16 rounding comes after the rotation;
 * rotary position embedding on q and k, base 1e6, "rotate half" pairing
   (element i with element i + 64 of a 128-wide head);
 * rows of one sequence: `block` clean rows (adapter off) then `block` noisy
@@ -131,8 +135,9 @@ def decoder_layer(h, w, gate, positions, k_cache, v_cache, block, n_heads, n_kv_
     ctx_lens: per-sequence valid cache rows, as in `block_attention`.
 
     w: dict with attn_norm, mlp_norm [hidden] and, for p in q k v o g u d,
-    w{p} [out, in], a{p} [r, in], b{p} [out, r].  Every stored intermediate
-    is rounded to bf16; returns (h_out, dict of the stored intermediates).
+    w{p} [out, in], a{p} [r, in], b{p} [out, r]; optionally q_norm and k_norm
+    [128] (both or neither).  Every stored intermediate is rounded to bf16;
+    returns (h_out, dict of the stored intermediates).
     """
     bf = round_bf16
     h = np.asarray(h, dtype=np.float64)
@@ -147,6 +152,10 @@ def decoder_layer(h, w, gate, positions, k_cache, v_cache, block, n_heads, n_kv_
     q = proj(a, "q").reshape(rows, n_heads, hd)
     k = proj(a, "k").reshape(rows, n_kv_heads, hd)
     v = proj(a, "v").reshape(rows, n_kv_heads, hd)
+    assert ("q_norm" in w) == ("k_norm" in w), "q_norm and k_norm come together"
+    if "q_norm" in w:
+        q = rms_norm(q, w["q_norm"], eps)          # over each head's 128 values
+        k = rms_norm(k, w["k_norm"], eps)
     q = bf(rope(q, positions, theta))
     k = bf(rope(k, positions, theta))
     n = 2 * block

@@ -39,13 +39,14 @@ POWER = 3.0          # each planted mistake must move the output by POWER * BAR
 
 
 def case(name, batch, block, ctx, hidden, inter, nh, nkv, r, packed=False, lens=None, seqs=None, gate=True,
-         seed=None):
+         seed=None, qk_norm=True):
     """One GPU layer case.  lens: per-sequence valid cache rows (ctx is then
     the capacity, the decode loop's form); seqs: the sequences the oracle
-    recomputes (None: all); gate False: no adapter anywhere."""
+    recomputes (None: all); gate False: no adapter anywhere; qk_norm False:
+    a layer without the per-head q/k RMSNorm."""
     return {"name": name, "batch": batch, "block": block, "ctx": ctx, "hidden": hidden, "inter": inter,
             "nh": nh, "nkv": nkv, "r": r, "packed": packed, "lens": lens, "seqs": seqs, "gate": gate,
-            "seed": batch + ctx if seed is None else seed}
+            "seed": batch + ctx if seed is None else seed, "qk_norm": qk_norm}
 
 
 LAYER_CASES = [
@@ -63,6 +64,7 @@ LAYER_CASES = [
     # 2048 rows: k and v as one two-segment GEMM, gate/up/SwiGLU as one GEMM
     case("rows2048_sampled", 64, 16, 40, 512, 1024, 8, 2, 64, packed=True, seqs=[3, 60], seed=21),
     case("no_adapters", 2, 8, 136, 512, 1088, 8, 2, 64, gate=False, seed=11),
+    case("no_qk_norm", 2, 4, 40, 256, 512, 4, 2, 16, qk_norm=False, seed=12),
 ]
 
 # decode-loop form: per-sequence cache lengths, the clean rows appended
@@ -94,7 +96,8 @@ def positions(lens, block):
 def make(c):
     """Seeded inputs of a case (workloads.decoder_layer_case at the scales above)."""
     d = workloads.decoder_layer_case(c["batch"], c["block"], c["ctx"], c["hidden"], c["inter"], c["nh"], c["nkv"],
-                                     c["r"], seed=c["seed"], weight_std=WEIGHT_STD, x_std=X_STD)
+                                     c["r"], seed=c["seed"], weight_std=WEIGHT_STD, x_std=X_STD,
+                                     qk_norm=c["qk_norm"])
     if not c["gate"]:
         d["gate"] = np.zeros_like(d["gate"])
     if c["lens"] is not None:
@@ -117,7 +120,7 @@ def make_seqs(c):
             "k_cache": np.stack([k for k, _ in kv]), "v_cache": np.stack([v for _, v in kv]),
             "lens": None if c["lens"] is None else np.asarray(c["lens"])[seqs],
             "weights": workloads.layer_weights_case(c["hidden"], c["inter"], c["nh"], c["nkv"], c["r"], c["seed"],
-                                                    0, WEIGHT_STD)}
+                                                    0, WEIGHT_STD, qk_norm=c["qk_norm"])}
 
 
 def seq_rows(c):

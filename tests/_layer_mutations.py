@@ -18,6 +18,7 @@ The mistakes are the ones a GPU wiring bug would make:
   drop_down_adapter      no adapter on down
   no_attention           the attention output replaced by zeros
   mlp_norm_of_input      the MLP norm reads the layer input h instead of h + o
+  drop_qk_norm           no per-head RMSNorm of q and k (layers that have it)
 
 Test infrastructure only.
 """
@@ -28,7 +29,7 @@ import oracle
 
 MUTATIONS = ("mask_leak", "positions_at_ctx", "positions_shift", "swiglu_swap", "drop_qkv_adapters",
              "drop_o_adapter", "drop_gate_up_adapters", "drop_down_adapter", "no_attention",
-             "mlp_norm_of_input")
+             "mlp_norm_of_input", "drop_qk_norm")
 ADAPTER_MUTATIONS = ("drop_qkv_adapters", "drop_o_adapter", "drop_gate_up_adapters", "drop_down_adapter")
 
 
@@ -84,8 +85,13 @@ def mutated_layer(h, w, gate, positions, k_cache, v_cache, block, n_heads, n_kv_
     elif mutation == "positions_shift":
         pos = pos + 1
     a = bf(oracle.rms_norm(h, w["attn_norm"], eps))
-    q = bf(oracle.rope(proj(a, "q").reshape(rows, n_heads, hd), pos, theta))
-    k = bf(oracle.rope(proj(a, "k").reshape(rows, n_kv_heads, hd), pos, theta))
+    q = proj(a, "q").reshape(rows, n_heads, hd)
+    k = proj(a, "k").reshape(rows, n_kv_heads, hd)
+    if "q_norm" in w and mutation != "drop_qk_norm":
+        q = oracle.rms_norm(q, w["q_norm"], eps)
+        k = oracle.rms_norm(k, w["k_norm"], eps)
+    q = bf(oracle.rope(q, pos, theta))
+    k = bf(oracle.rope(k, pos, theta))
     v = proj(a, "v").reshape(rows, n_kv_heads, hd)
     att = _attention(q.reshape(bsz, n, n_heads, hd), kc, vc, k.reshape(bsz, n, n_kv_heads, hd),
                      v.reshape(bsz, n, n_kv_heads, hd), block, 1.0 / np.sqrt(hd), lens, mutation == "mask_leak")

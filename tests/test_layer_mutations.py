@@ -7,7 +7,8 @@ ten bf16 storage points; 9e-2, above 3x the single-operation bar of 2e-2 as
 well), so that a GPU path making that mistake fails its parity test instead
 of passing inside the tolerance.  The mistakes: a clean row seeing the noisy rows, wrong rotary
 positions, SwiGLU operands swapped, each adapter group dropped, attention
-dropped, the MLP norm reading the wrong residual.
+dropped, the MLP norm reading the wrong residual, the per-head q/k norm
+dropped.
 
 Source of what the layer computes: Uno summary (hyper.ai, arXiv 2609.04010),
 section 方法 (one forward over concatenated clean and noisy rows, the adapter
@@ -60,6 +61,8 @@ def test_every_planted_mistake_exceeds_the_bar(c):
             continue          # no adapter anywhere: nothing to drop
         if m == "positions_shift" and c["ctx"] == 0:
             continue          # no cache: a global shift is an exact symmetry of RoPE attention
+        if m == "drop_qk_norm" and not c["qk_norm"]:
+            continue          # the layer has no per-head norm to drop
         err = row_relerr(mutated_layer(*args, mutation=m, ctx_lens=lens), ref)
         if err < POWER * BAR:
             weak[m] = err

@@ -112,7 +112,7 @@ def test_silu_mul_matches_torch():
     np.testing.assert_allclose(oracle.silu_mul(g, u), ref, rtol=1e-12, atol=1e-15)
 
 
-def _layer_weights(hidden, inter, nh, nkv, r, scale=0.05, seed=0):
+def _layer_weights(hidden, inter, nh, nkv, r, scale=0.05, seed=0, qk_norm=False):
     g = np.random.default_rng(seed)
     shapes = {"q": (nh * 128, hidden), "k": (nkv * 128, hidden), "v": (nkv * 128, hidden),
               "o": (hidden, nh * 128), "g": (inter, hidden), "u": (inter, hidden), "d": (hidden, inter)}
@@ -122,6 +122,9 @@ def _layer_weights(hidden, inter, nh, nkv, r, scale=0.05, seed=0):
         w["w" + p] = oracle.round_bf16(g.standard_normal((n_out, n_in)) * scale)
         w["a" + p] = oracle.round_bf16(g.standard_normal((r, n_in)) * scale)
         w["b" + p] = oracle.round_bf16(g.standard_normal((n_out, r)) * scale)
+    if qk_norm:
+        w["q_norm"] = oracle.round_bf16(1.0 + 0.3 * g.standard_normal(128))
+        w["k_norm"] = oracle.round_bf16(1.0 + 0.3 * g.standard_normal(128))
     return w
 
 
@@ -179,9 +182,10 @@ def test_lm_head_matches_torch_pipeline():
 
 def _torch_layer(h, w, gate, pos, kc, vc, block, nh, nkv, ctx_lens=None, eps=1e-6, theta=1.0e6):
     """The layer written independently of the oracle, from torch CPU float64
-    primitives: F.rms_norm, F.linear for W x and the gated B(A x), RoPE as a
-    complex rotation (torch.polar), F.scaled_dot_product_attention under an
-    explicit boolean block mask, F.silu(gate) * up, residual adds; storage
+    primitives: F.rms_norm, F.linear for W x and the gated B(A x), F.rms_norm
+    over each 128-wide q and k head when the layer has q_norm / k_norm, RoPE
+    as a complex rotation (torch.polar), F.scaled_dot_product_attention under
+    an explicit boolean block mask, F.silu(gate) * up, residual adds; storage
     rounding fp32 -> bf16 at the same points as the GPU kernels."""
     F = torch.nn.functional
     T = torch.float64
@@ -208,9 +212,12 @@ def _torch_layer(h, w, gate, pos, kc, vc, block, nh, nkv, ctx_lens=None, eps=1e-
         z = z * torch.polar(torch.ones_like(ang), ang)[:, None, :]
         return torch.cat([z.real, z.imag], dim=-1)
 
+    def head_norm(x, name):
+        return F.rms_norm(x, (128,), t(w[name]), eps) if name in w else x
+
     a = bf(F.rms_norm(H, (hidden,), t(w["attn_norm"]), eps))
-    q = bf(rot(lin(a, "q").view(rows, nh, 128)))
-    k = bf(rot(lin(a, "k").view(rows, nkv, 128)))
+    q = bf(rot(head_norm(lin(a, "q").view(rows, nh, 128), "q_norm")))
+    k = bf(rot(head_norm(lin(a, "k").view(rows, nkv, 128), "k_norm")))
     v = lin(a, "v").view(rows, nkv, 128)
     blk = torch.zeros(n, n, dtype=torch.bool)
     blk[:block, :block] = torch.ones(block, block, dtype=torch.bool).tril()   # clean: causal over clean rows
@@ -231,15 +238,17 @@ def _torch_layer(h, w, gate, pos, kc, vc, block, nh, nkv, ctx_lens=None, eps=1e-
     return bf(h1 + lin(m, "d")).numpy()
 
 
+@pytest.mark.parametrize("qk_norm", [False, True])
 @pytest.mark.parametrize("lens", [None, [9, 0, 4]])
-def test_decoder_layer_matches_torch_composition(lens):
+def test_decoder_layer_matches_torch_composition(lens, qk_norm):
     """oracle.decoder_layer against the torch composition above, with the
-    whole cache valid and with per-sequence lengths (one empty).  Both sides
+    whole cache valid and with per-sequence lengths (one empty), without and
+    with the per-head q/k norm.  Both sides
     compute in float64 and round to bf16 at the same points; summation order
     differs, so a value sitting on a bf16 rounding boundary may land one bf16
     ulp apart, which can then move later values by a few ulps."""
     hidden, inter, nh, nkv, r, block, ctx, bsz = 256, 384, 4, 2, 16, 3, 9, 3
-    w = _layer_weights(hidden, inter, nh, nkv, r, scale=0.05, seed=7)
+    w = _layer_weights(hidden, inter, nh, nkv, r, scale=0.05, seed=7, qk_norm=qk_norm)
     g = np.random.default_rng(8)
     h = oracle.round_bf16(0.1 * g.standard_normal((bsz * 2 * block, hidden)))
     gate = np.tile(np.concatenate([np.zeros(block), np.ones(block)]).astype(np.uint8), bsz)
@@ -257,3 +266,8 @@ def test_decoder_layer_matches_torch_composition(lens):
     np.testing.assert_allclose(got, ref, rtol=4 * 2.0 ** -8, atol=1e-3)
     # the layer moved the stream: the comparison is not of the identity
     assert np.max(np.abs(got - h)) > 0.1 * np.max(np.abs(h))
+    if qk_norm:
+        # and the per-head norm matters at this scale: without it the result moves
+        w0 = {k: v for k, v in w.items() if k not in ("q_norm", "k_norm")}
+        plain, _ = oracle.decoder_layer(h, w0, gate, pos, kc, vc, block, nh, nkv, ctx_lens=lens)
+        assert np.max(np.abs(plain - got)) > 10 * 4 * 2.0 ** -8 * np.max(np.abs(got))

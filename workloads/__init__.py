@@ -393,10 +393,11 @@ def layer_shapes(hidden, inter, n_heads, n_kv_heads, head_dim=128):
 
 
 def layer_weights_case(hidden, inter, n_heads, n_kv_heads, r, seed=0, layer=0, weight_std=0.02,
-                       norm_std=0.1, lora_std=None):
+                       norm_std=0.1, lora_std=None, qk_norm=True):
     """bf16 weights of one layer: w{p} [out, in] ~ N(0, weight_std^2), a{p}
     [r, in] and b{p} [out, r] ~ N(0, lora_std^2) (default weight_std);
-    attn_norm, mlp_norm = 1 + N(0, norm_std^2).
+    attn_norm, mlp_norm = 1 + N(0, norm_std^2); with qk_norm also the
+    per-head q_norm, k_norm [128] = 1 + N(0, norm_std^2).
 
     Returns {name: uint16 bits} and {name + "_f32": exact values}."""
     out = {}
@@ -410,6 +411,10 @@ def layer_weights_case(hidden, inter, n_heads, n_kv_heads, r, seed=0, layer=0, w
     for j, name in enumerate(("attn_norm", "mlp_norm")):
         x = 1.0 + rng_for(seed, _T_LAYER_NORM, layer, j).standard_normal(hidden, dtype=np.float32) * np.float32(norm_std)
         out[name], out[name + "_f32"] = _store(x, "bf16")
+    if qk_norm:
+        for j, name in ((2, "q_norm"), (3, "k_norm")):
+            x = 1.0 + rng_for(seed, _T_LAYER_NORM, layer, j).standard_normal(128, dtype=np.float32) * np.float32(norm_std)
+            out[name], out[name + "_f32"] = _store(x, "bf16")
     return out
 
 
@@ -458,7 +463,8 @@ def block_positions(batch, block, ctx):
 
 
 def decoder_layer_case(batch, block, ctx, hidden, inter, n_heads, n_kv_heads, r, seed=0, layer=0,
-                       weight_std=0.02, norm_std=0.1, kv_std=1.0, workers=None, x_std=1.0, lora_std=None):
+                       weight_std=0.02, norm_std=0.1, kv_std=1.0, workers=None, x_std=1.0, lora_std=None,
+                       qk_norm=True):
     """Inputs of one decoder layer over `batch` sequences of `block` clean +
     `block` noisy rows: residual stream h [rows, hidden] ~ N(0, x_std^2), gate
     (0 clean, 1 noisy), positions, KV cache [batch, ctx, Hkv, 128] ~
@@ -472,7 +478,7 @@ def decoder_layer_case(batch, block, ctx, hidden, inter, n_heads, n_kv_heads, r,
             "h": h, "gate": default_gate(rows, block), "positions": block_positions(batch, block, ctx),
             "k_cache": kc, "v_cache": vc,
             "weights": layer_weights_case(hidden, inter, n_heads, n_kv_heads, r, seed, layer, weight_std,
-                                          norm_std, lora_std)}
+                                          norm_std, lora_std, qk_norm)}
 
 
 def rows_case(rows, vocab, dtype="bf16", seed=0, std=2.0):
