@@ -185,7 +185,8 @@ def bench_full_step(args, dad, torch):
     cap = ctx + blk * (n_total + 1)
     layers, keep = [], []
     for li in range(nl):
-        w = {"attn_norm": 1.0 + randn((hid,), 0.1), "mlp_norm": 1.0 + randn((hid,), 0.1)}
+        w = {"attn_norm": 1.0 + randn((hid,), 0.1), "mlp_norm": 1.0 + randn((hid,), 0.1),
+             "q_norm": 1.0 + randn((128,), 0.1), "k_norm": 1.0 + randn((128,), 0.1)}
         # the adapters of q/k/v and of gate/up are stored back to back, so each
         # group's LoRA-down runs as one launch
         a_qkv = randn((3 * r, hid), 0.02)
@@ -352,7 +353,7 @@ def bench_full_step(args, dad, torch):
                 "uniform token ids)",
         "config": {"workload": "psi_spec_full_step",
                    "model": "36-layer Qwen3-8B-shaped stack, hidden 4096, MLP 12288, GQA 32/8, head_dim 128, "
-                            "rank-128 gated LoRA on q/k/v/o/gate/up/down, vocab 151936",
+                            "per-head q/k RMSNorm, rank-128 gated LoRA on q/k/v/o/gate/up/down, vocab 151936",
                    "batch": B, "block": blk, "rows": rows, "ctx_len": ctx, "drafts_per_seq": k,
                    "kv_cache": "decode loop: ctx_len valid rows per sequence at the first step; each layer "
                                "appends the block's clean k/v and the step commits the kept rows, so the cache "

@@ -47,7 +47,7 @@ class LayerWeights(ctypes.Structure):
     _fields_ = [("attn_norm", ctypes.c_void_p), ("mlp_norm", ctypes.c_void_p),
                 ("w", ctypes.c_void_p * NUM_PROJ), ("a", ctypes.c_void_p * NUM_PROJ),
                 ("b", ctypes.c_void_p * NUM_PROJ), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
-                ("w_merged", ctypes.c_void_p * NUM_PROJ)]
+                ("w_merged", ctypes.c_void_p * NUM_PROJ), ("q_norm", ctypes.c_void_p), ("k_norm", ctypes.c_void_p)]
 
 
 class StepConfig(ctypes.Structure):
@@ -115,7 +115,7 @@ def _declare(lib):
         "uno_psi_spec_build_tree": (ctypes.c_int, [_p, ctypes.c_int, _i32, _i32, _p, _i32, _p, _i64, _i64, _p, _i32,
                                                    _f32, _i32, _p, _p, _p, _sz]),
         "uno_rms_norm": (ctypes.c_int, [_p, _i64, _i32, _p, _i64, _p, _i64, _p, _i64, _p, _f32, _p, _i64]),
-        "uno_rope": (ctypes.c_int, [_p, _i64, _i32, _p, _i64, _p, _f32]),
+        "uno_rope": (ctypes.c_int, [_p, _i64, _i32, _p, _i64, _p, _f32, _p, _f32]),
         "uno_silu_mul": (ctypes.c_int, [_p, _i64, _i32, _p, _i64, _p, _i64, _p, _i64]),
         "uno_block_verify_attention_workspace": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _i32,
                                                                 ctypes.POINTER(_sz)]),
@@ -564,11 +564,13 @@ def rms_norm(x, weight, eps=1e-6, res=None, sum_out=None, out=None, want_out=Tru
     return out
 
 
-def rope(x, positions, theta=1.0e6, stream=None):
-    """Rotary embedding in place on x [rows, n_heads * 128] (uno_rope)."""
+def rope(x, positions, theta=1.0e6, norm_weight=None, norm_eps=1e-6, stream=None):
+    """Rotary embedding in place on x [rows, n_heads * 128] (uno_rope), each
+    head first normed with norm_weight [128] when given."""
     load()
     rows, width = x.shape
-    _check(_lib.uno_rope(_stream(stream), rows, width // 128, _ptr(x), x.stride(0), _ptr(positions), float(theta)))
+    _check(_lib.uno_rope(_stream(stream), rows, width // 128, _ptr(x), x.stride(0), _ptr(positions), float(theta),
+                         _ptr(norm_weight) if norm_weight is not None else None, float(norm_eps)))
     return x
 
 
@@ -671,11 +673,14 @@ def merge_layer(w, lora_scale=1.0, stream=None):
 
 def layer_weights(w, k_cache=None, v_cache=None):
     """uno_layer_weights from a dict of device tensors: attn_norm, mlp_norm and
-    w/a/b + one of q k v o g u d (gate, up, down), e.g. "wq", "aq", "bq", and
-    optionally the gate-merged "mq", ... (all seven; see merge_layer)."""
+    w/a/b + one of q k v o g u d (gate, up, down), e.g. "wq", "aq", "bq",
+    optionally the per-head "q_norm", "k_norm" (both or neither) and the
+    gate-merged "mq", ... (all seven; see merge_layer)."""
     lw = LayerWeights()
     lw.attn_norm = w["attn_norm"].data_ptr()
     lw.mlp_norm = w["mlp_norm"].data_ptr()
+    lw.q_norm = w["q_norm"].data_ptr() if "q_norm" in w else None
+    lw.k_norm = w["k_norm"].data_ptr() if "k_norm" in w else None
     for i, p in enumerate(PROJ):
         lw.w[i] = w["w" + p].data_ptr()
         lw.a[i] = w["a" + p].data_ptr() if ("a" + p) in w else None

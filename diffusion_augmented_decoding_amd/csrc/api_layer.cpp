@@ -156,6 +156,9 @@ hipError_t launch_decoder_layer(const DecoderLayerArgs& d, hipStream_t stream) {
     ra.n_heads2 = d.n_kv;
     ra.x2 = k;
     ra.ldx2 = int64_t(d.n_kv) * kHeadDim;
+    ra.norm_w = d.w->q_norm;    // per-head q/k norm (both or neither)
+    ra.norm_w2 = d.w->k_norm;
+    ra.norm_eps = d.rms_eps;
     if (d.cache_len) {   // the clean rows' keys (rotated) and values join the cache's free slots
       ra.cache_len = d.cache_len;
       ra.block = d.block;
@@ -329,13 +332,16 @@ uno_status uno_rms_norm(hipStream_t stream, int64_t rows, int32_t dim, const voi
 
 // ------------------------------------------------------------------ rope
 uno_status uno_rope(hipStream_t stream, int64_t rows, int32_t n_heads, void* x, int64_t ldx,
-                    const int32_t* positions, float theta) {
+                    const int32_t* positions, float theta, const void* norm_weight, float norm_eps) {
   UNO_GUARD_BEGIN
   if (rows < 1 || n_heads < 1) return fail(UNO_ERR_INVALID_ARGUMENT, "rows and n_heads must be >= 1");
   if (rows > 0x7fffffff) return fail(UNO_ERR_UNSUPPORTED, "rows above 2^31 - 1");
   if (!x || !positions) return fail(UNO_ERR_INVALID_ARGUMENT, "x and positions are required");
   if (ldx < int64_t(n_heads) * kHeadDim) return fail(UNO_ERR_INVALID_ARGUMENT, "ldx below n_heads * 128");
   if (!(theta > 1.f) || !std::isfinite(theta)) return fail(UNO_ERR_INVALID_ARGUMENT, "theta must be finite and > 1");
+  if (norm_weight && (!(norm_eps >= 0.f) || !std::isfinite(norm_eps)))
+    return fail(UNO_ERR_INVALID_ARGUMENT, "norm_eps must be finite and >= 0");
+  if (reinterpret_cast<uintptr_t>(norm_weight) & 1u) return fail(UNO_ERR_UNSUPPORTED, "norm_weight must be 2-byte aligned");
   RopeArgs a{};
   a.rows = rows;
   a.n_heads = n_heads;
@@ -343,6 +349,8 @@ uno_status uno_rope(hipStream_t stream, int64_t rows, int32_t n_heads, void* x, 
   a.ldx = ldx;
   a.positions = positions;
   a.theta = theta;
+  a.norm_w = norm_weight;
+  a.norm_eps = norm_eps;
   return check_hip(launch_rope(a, stream), "uno_rope launch");
   UNO_GUARD_END
 }
@@ -513,6 +521,9 @@ uno_status uno_decoder_layer(hipStream_t stream, int32_t batch, int32_t block, i
   }
   if (ctx_len > 0 && (!wt->k_cache || !wt->v_cache || !aligned16(wt->k_cache) || !aligned16(wt->v_cache)))
     return fail(UNO_ERR_INVALID_ARGUMENT, "KV cache NULL or unaligned");
+  if (!wt->q_norm != !wt->k_norm) return fail(UNO_ERR_INVALID_ARGUMENT, "q_norm and k_norm: both or neither");
+  if ((wt->q_norm && !aligned16(wt->q_norm)) || (wt->k_norm && !aligned16(wt->k_norm)))
+    return fail(UNO_ERR_UNSUPPORTED, "q_norm / k_norm must be 16-byte aligned");
   if (!aligned16(hidden_state) || !aligned16(wt->attn_norm) || !aligned16(wt->mlp_norm))
     return fail(UNO_ERR_UNSUPPORTED, "tensors must be 16-byte aligned");
   if (!(rms_eps >= 0.f) || !std::isfinite(rms_eps) || !(rope_theta > 1.f) || !std::isfinite(rope_theta) ||

@@ -119,6 +119,9 @@ uno_status uno_psi_spec_step(hipStream_t stream, const uno_step_config* config, 
     }
     if (c.ctx_len > 0 && (!w.k_cache || !w.v_cache || !aligned16(w.k_cache) || !aligned16(w.v_cache)))
       return fail(UNO_ERR_INVALID_ARGUMENT, "layer %d: KV cache NULL or unaligned", l);
+    if (!w.q_norm != !w.k_norm) return fail(UNO_ERR_INVALID_ARGUMENT, "layer %d: q_norm and k_norm: both or neither", l);
+    if ((w.q_norm && !aligned16(w.q_norm)) || (w.k_norm && !aligned16(w.k_norm)))
+      return fail(UNO_ERR_UNSUPPORTED, "layer %d: q_norm / k_norm must be 16-byte aligned", l);
   }
   const StepWs W = step_ws(c);
   if (workspace_bytes < W.total || !workspace)

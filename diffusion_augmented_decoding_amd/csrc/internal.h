@@ -343,6 +343,12 @@ struct RopeArgs {
   int block, cap;
   void* k_cache; void* v_cache;
   const void* v; int64_t ldv;
+  // Optional per-head RMSNorm before the rotation (bf16 weights of 128):
+  // head <- head / sqrt(mean(head^2) + norm_eps) * weight, for x with norm_w
+  // and for x2 with norm_w2 (nullptr: no norm on that tensor)
+  const void* norm_w;
+  const void* norm_w2;
+  float norm_eps;
 };
 hipError_t launch_rope(const RopeArgs& a, hipStream_t stream);
 

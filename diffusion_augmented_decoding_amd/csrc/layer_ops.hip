@@ -117,6 +117,9 @@ __device__ __forceinline__ bool append_slot(const RopeArgs& a, int64_t row, uint
 // precision (positions far into a long context keep their phase), then
 // rotates the pair (x_i, x_{i+64}) of every 4th head from t / 64 on, in x
 // and then in the optional second tensor at the same positions (q and k).
+// With a norm weight a head is first scaled by 1 / sqrt(mean(head^2) + eps)
+// and the weight (one wave holds the whole head: a wave-wide sum), in fp32,
+// rounded to bf16 once, after the rotation.
 __global__ __launch_bounds__(256) void rope_kernel(RopeArgs a) {
   const int64_t row = blockIdx.x;
   const int i = threadIdx.x & 63, h0 = threadIdx.x >> 6;
@@ -124,16 +127,23 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeArgs a) {
   double s, c;
   sincos(double(a.positions[row]) * inv_freq, &s, &c);
   const float cs = float(c), sn = float(s);
-  auto rotate = [&](uint16_t* p) {
-    const float x1 = bf16_to_f32(p[i]), x2 = bf16_to_f32(p[i + 64]);
+  auto rotate = [&](uint16_t* p, const uint16_t* nw) {
+    float x1 = bf16_to_f32(p[i]), x2 = bf16_to_f32(p[i + 64]);
+    if (nw) {
+      const float rs = 1.f / sqrtf(wave_sum(fmaf(x2, x2, x1 * x1)) / 128.f + a.norm_eps);
+      x1 = x1 * rs * bf16_to_f32(nw[i]);
+      x2 = x2 * rs * bf16_to_f32(nw[i + 64]);
+    }
     p[i] = f32_to_bf16(x1 * cs - x2 * sn);
     p[i + 64] = f32_to_bf16(x2 * cs + x1 * sn);
   };
+  const uint16_t* nw1 = static_cast<const uint16_t*>(a.norm_w);
+  const uint16_t* nw2 = static_cast<const uint16_t*>(a.norm_w2);
   uint16_t* xr = static_cast<uint16_t*>(a.x) + row * a.ldx;
-  for (int h = h0; h < a.n_heads; h += 4) rotate(xr + h * 128);
+  for (int h = h0; h < a.n_heads; h += 4) rotate(xr + h * 128, nw1);
   if (a.x2) {
     uint16_t* xr2 = static_cast<uint16_t*>(a.x2) + row * a.ldx2;
-    for (int h = h0; h < a.n_heads2; h += 4) rotate(xr2 + h * 128);
+    for (int h = h0; h < a.n_heads2; h += 4) rotate(xr2 + h * 128, nw2);
     uint16_t *kd, *vd;
     if (append_slot(a, row, kd, vd)) {
       __syncthreads();   // the rotated row, written by this workgroup, is complete
@@ -150,7 +160,8 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeArgs a) {
 // multiples of 4), one workgroup per row: the 64 angles of the row are formed
 // once, in double precision, by the first 64 threads and shared through LDS;
 // then thread t rotates pairs 4 (t % 16) .. + 3 of heads t / 16, t / 16 + 16,
-// ... with 8-byte loads and stores of x_i and x_{i+64}.
+// ... with 8-byte loads and stores of x_i and x_{i+64}.  The optional
+// per-head norm sums the head's squares over the 16 lanes that hold it.
 __global__ __launch_bounds__(256) void rope_vec_kernel(RopeArgs a) {
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
@@ -170,11 +181,31 @@ __global__ __launch_bounds__(256) void rope_vec_kernel(RopeArgs a) {
     cs[j] = cs_s[i0 + j];
     sn[j] = sn_s[i0 + j];
   }
-  // rotates the head at p in place; dup (optional) receives a copy of the result
-  auto rotate = [&](uint16_t* p, uint16_t* dup) {
+  // rotates the head at p in place (normed first with weight nw when given);
+  // dup (optional) receives a copy of the result
+  auto rotate = [&](uint16_t* p, uint16_t* dup, const uint16_t* nw) {
     const uint2 lo = *reinterpret_cast<const uint2*>(p + i0), hi = *reinterpret_cast<const uint2*>(p + 64 + i0);
-    const float x1[4] = {bf16_lo(lo.x), bf16_hi(lo.x), bf16_lo(lo.y), bf16_hi(lo.y)};
-    const float x2[4] = {bf16_lo(hi.x), bf16_hi(hi.x), bf16_lo(hi.y), bf16_hi(hi.y)};
+    float x1[4] = {bf16_lo(lo.x), bf16_hi(lo.x), bf16_lo(lo.y), bf16_hi(lo.y)};
+    float x2[4] = {bf16_lo(hi.x), bf16_hi(hi.x), bf16_lo(hi.y), bf16_hi(hi.y)};
+    if (nw) {
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ss = fmaf(x2[j], x2[j], fmaf(x1[j], x1[j], ss));
+      // the 16 lanes of one head: xor distances 1..8 stay inside the group
+      ss += swizzle_xor<1>(ss);
+      ss += swizzle_xor<2>(ss);
+      ss += swizzle_xor<4>(ss);
+      ss += swizzle_xor<8>(ss);
+      const float rs = 1.f / sqrtf(ss / 128.f + a.norm_eps);
+      const uint2 wl = *reinterpret_cast<const uint2*>(nw + i0), wh = *reinterpret_cast<const uint2*>(nw + 64 + i0);
+      const float w1[4] = {bf16_lo(wl.x), bf16_hi(wl.x), bf16_lo(wl.y), bf16_hi(wl.y)};
+      const float w2[4] = {bf16_lo(wh.x), bf16_hi(wh.x), bf16_lo(wh.y), bf16_hi(wh.y)};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x1[j] = x1[j] * rs * w1[j];
+        x2[j] = x2[j] * rs * w2[j];
+      }
+    }
     float o1[4], o2[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -190,13 +221,15 @@ __global__ __launch_bounds__(256) void rope_vec_kernel(RopeArgs a) {
       *reinterpret_cast<uint2*>(dup + 64 + i0) = r2;
     }
   };
+  const uint16_t* nw1 = static_cast<const uint16_t*>(a.norm_w);
+  const uint16_t* nw2 = static_cast<const uint16_t*>(a.norm_w2);
   uint16_t* xr = static_cast<uint16_t*>(a.x) + row * a.ldx;
-  for (int h = h0; h < a.n_heads; h += 16) rotate(xr + h * 128, nullptr);
+  for (int h = h0; h < a.n_heads; h += 16) rotate(xr + h * 128, nullptr, nw1);
   if (a.x2) {
     uint16_t* xr2 = static_cast<uint16_t*>(a.x2) + row * a.ldx2;
     uint16_t *kd = nullptr, *vd = nullptr;
     const bool app = append_slot(a, row, kd, vd);
-    for (int h = h0; h < a.n_heads2; h += 16) rotate(xr2 + h * 128, app ? kd + h * 128 : nullptr);
+    for (int h = h0; h < a.n_heads2; h += 16) rotate(xr2 + h * 128, app ? kd + h * 128 : nullptr, nw2);
     if (app) {
       // the value row goes to the cache unchanged, in 8-byte pieces
       const uint2* vr = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.v) + row * a.ldv);
@@ -248,7 +281,8 @@ hipError_t launch_rope(const RopeArgs& a, hipStream_t stream) {
   ProfileScope ps("uno_rope", stream);
   auto vec_ok = [](const void* p, int64_t ld) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0 && ld % 4 == 0; };
   const bool vec = vec_ok(a.x, a.ldx) && (!a.x2 || vec_ok(a.x2, a.ldx2)) &&
-                   (!a.cache_len || (vec_ok(a.v, a.ldv) && vec_ok(a.k_cache, 0) && vec_ok(a.v_cache, 0)));
+                   (!a.cache_len || (vec_ok(a.v, a.ldv) && vec_ok(a.k_cache, 0) && vec_ok(a.v_cache, 0))) &&
+                   (!a.norm_w || vec_ok(a.norm_w, 0)) && (!a.norm_w2 || vec_ok(a.norm_w2, 0));
   if (vec)
     hipLaunchKernelGGL(rope_vec_kernel, dim3(unsigned(a.rows)), dim3(256), 0, stream, a);
   else

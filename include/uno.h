@@ -56,7 +56,7 @@ typedef enum {
 
 typedef enum { UNO_F32 = 0, UNO_BF16 = 1 } uno_dtype;
 
-#define UNO_ABI_VERSION 6
+#define UNO_ABI_VERSION 7
 
 int uno_abi_version(void);
 const char* uno_status_string(uno_status s);
@@ -452,9 +452,14 @@ uno_status uno_rms_norm(hipStream_t stream, int64_t rows, int32_t dim,
 
 /* Rotary position embedding, in place, on x [rows][n_heads][128]: element
  * pair (i, i + 64) of every head is rotated by positions[row] * theta^(-i/64)
- * (angle formed in double precision).  positions int32 [rows], >= 0. */
+ * (angle formed in double precision).  positions int32 [rows], >= 0.
+ * norm_weight (optional, bf16 [128], 2-byte aligned; NULL: none): every head
+ * is first scaled to head / sqrt(mean(head^2) + norm_eps) * norm_weight
+ * (Qwen3's per-head q/k norm), in fp32, with one bf16 rounding after the
+ * rotation; norm_eps finite and >= 0.  Source: Uno summary (hyper.ai),
+ * section 实验 (a Qwen3-8B base). */
 uno_status uno_rope(hipStream_t stream, int64_t rows, int32_t n_heads, void* x, int64_t ldx,
-                    const int32_t* positions, float theta);
+                    const int32_t* positions, float theta, const void* norm_weight, float norm_eps);
 
 /* SwiGLU product out = bf16(silu(g) * u), silu(g) = g / (1 + e^-g);
  * [rows][dim], dim % 8 == 0; out may be g or u. */
@@ -500,7 +505,7 @@ uno_status uno_sample_rows(hipStream_t stream, uno_dtype logit_dtype, int32_t ro
  * [r][in], b[p] [out][r] with (out, in) = (n_heads*128, hidden),
  * (n_kv_heads*128, hidden) twice, (hidden, n_heads*128), (inter, hidden)
  * twice, (hidden, inter).  k_cache/v_cache [batch][ctx][n_kv_heads][128].
- *   a = rmsnorm(h); q, k, v = gated_lora(a); rope(q), rope(k);
+ *   a = rmsnorm(h); q, k, v = gated_lora(a); rope(qnorm(q)), rope(knorm(k));
  *   att = block_attention(q, cache + (k, v)); h += gated_lora(att, o);
  *   a = rmsnorm(h); h += gated_lora(silu(gated_lora(a, gate)) * gated_lora(a, up), down)
  * with every gated_lora as uno_gated_lora_linear under `gate` [rows] and
@@ -516,6 +521,10 @@ uno_status uno_sample_rows(hipStream_t stream, uno_dtype logit_dtype, int32_t ro
  * when that slot is below ctx_len; cache_len itself is not changed (see
  * uno_kv_commit).  The caches are then written: k_cache/v_cache must not be
  * read by concurrent work.
+ * qnorm / knorm: Qwen3's per-head RMSNorm (rms_eps) of every 128-wide q and
+ * k head with the bf16 weights q_norm / k_norm [128], before the rotation,
+ * in fp32 with one bf16 rounding after it (the identity when both weights
+ * are NULL).
  * hidden and inter multiples of 8, r a multiple of 8, n_heads / n_kv_heads
  * <= 8, 1 <= block <= 128. */
 enum { UNO_PROJ_Q = 0, UNO_PROJ_K, UNO_PROJ_V, UNO_PROJ_O, UNO_PROJ_GATE, UNO_PROJ_UP, UNO_PROJ_DOWN,
@@ -535,6 +544,12 @@ typedef struct {
    * w_merged and the clean rows w, and no LoRA-down runs.  Ignored by
    * uno_decoder_layer (its gate is arbitrary). */
   const void* w_merged[UNO_NUM_PROJ];
+  /* Optional per-head q/k RMSNorm weights, bf16 [128] each, 16-byte
+   * aligned, both or neither (NULL: the layer has no per-head norm).
+   * Source: Uno summary (hyper.ai), section 实验 (a Qwen3-8B base, whose
+   * attention normalises every q and k head before the rotary embedding). */
+  const void* q_norm;
+  const void* k_norm;
 } uno_layer_weights;
 
 /* Gate-merged weights for uno_layer_weights.w_merged.  Source: Uno summary

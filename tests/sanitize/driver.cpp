@@ -141,8 +141,10 @@ int main() {
   // layer ops
   expect("norm", uno_rms_norm(s, 16, 256, D, 256, nullptr, 0, nullptr, 0, D, 1e-6f, D, 256), true);
   expect("norm dim", uno_rms_norm(s, 16, 0, D, 256, nullptr, 0, nullptr, 0, D, 1e-6f, D, 256), false);
-  expect("rope", uno_rope(s, 16, 4, D, 512, (const int32_t*)D, 1e6f), true);
-  expect("rope theta", uno_rope(s, 16, 4, D, 512, (const int32_t*)D, 0.5f), false);
+  expect("rope", uno_rope(s, 16, 4, D, 512, (const int32_t*)D, 1e6f, nullptr, 1e-6f), true);
+  expect("rope norm", uno_rope(s, 16, 4, D, 512, (const int32_t*)D, 1e6f, D, 1e-6f), true);
+  expect("rope theta", uno_rope(s, 16, 4, D, 512, (const int32_t*)D, 0.5f, nullptr, 1e-6f), false);
+  expect("rope norm eps", uno_rope(s, 16, 4, D, 512, (const int32_t*)D, 1e6f, D, -1.f), false);
   expect("silu", uno_silu_mul(s, 16, 256, D, 256, D, 256, D, 256), true);
   expect("silu null", uno_silu_mul(s, 16, 256, nullptr, 256, D, 256, D, 256), false);
   expect("block attn ws", uno_block_verify_attention_workspace(4, 16, 128, 32, 8, 128, &bytes), true);
@@ -170,6 +172,14 @@ int main() {
   expect("layer ws", uno_decoder_layer_workspace(2, 4, 40, 256, 512, 4, 2, 16, &bytes), true);
   expect("layer", uno_decoder_layer(s, 2, 4, 40, 256, 512, 4, 2, 16, &w, (const uint8_t*)D, (const int32_t*)D, nullptr,
                                     1e-6f, 1e6f, 1.f, D, D, big), true);
+  w.q_norm = D;
+  w.k_norm = D;
+  expect("layer qk norm", uno_decoder_layer(s, 2, 4, 40, 256, 512, 4, 2, 16, &w, (const uint8_t*)D, (const int32_t*)D,
+                                            nullptr, 1e-6f, 1e6f, 1.f, D, D, big), true);
+  w.k_norm = nullptr;
+  expect("layer q norm alone", uno_decoder_layer(s, 2, 4, 40, 256, 512, 4, 2, 16, &w, (const uint8_t*)D,
+                                                 (const int32_t*)D, nullptr, 1e-6f, 1e6f, 1.f, D, D, big), false);
+  w.q_norm = nullptr;
   expect("layer weights", uno_decoder_layer(s, 2, 4, 40, 256, 512, 4, 2, 16, nullptr, (const uint8_t*)D,
                                             (const int32_t*)D, nullptr, 1e-6f, 1e6f, 1.f, D, D, big), false);
   expect("commit", uno_kv_commit(s, 4, 100, (int32_t*)D, (int32_t*)D), true);

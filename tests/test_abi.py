@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.uno_abi_version() == 6
+    assert lib.uno_abi_version() == 7
     for s in range(6):
         assert lib.uno_status_string(s)
     assert lib.uno_status_string(99) == b"unknown status"
@@ -212,11 +212,13 @@ def test_layer_ops_reject_bad_calls(lib):
     assert lib.uno_rms_norm(None, 4, 64, ctypes.c_void_p(0x10002), 64, None, 64, None, 64, FAKE16, 1e-6,
                             FAKE16, 64) == UNSUPPORTED
     assert lib.uno_rms_norm(None, 4, 64, FAKE16, 64, None, 64, None, 64, FAKE16, -1.0, FAKE16, 64) == INVALID
-    # uno_rope(stream, rows, n_heads, x, ldx, positions, theta)
-    assert lib.uno_rope(None, 0, 8, FAKE16, 1024, FAKE16, 1e6) == INVALID
-    assert lib.uno_rope(None, 4, 8, FAKE16, 1000, FAKE16, 1e6) == INVALID
-    assert lib.uno_rope(None, 4, 8, FAKE16, 1024, None, 1e6) == INVALID
-    assert lib.uno_rope(None, 4, 8, FAKE16, 1024, FAKE16, 1.0) == INVALID
+    # uno_rope(stream, rows, n_heads, x, ldx, positions, theta, norm_weight, norm_eps)
+    assert lib.uno_rope(None, 0, 8, FAKE16, 1024, FAKE16, 1e6, None, 1e-6) == INVALID
+    assert lib.uno_rope(None, 4, 8, FAKE16, 1000, FAKE16, 1e6, None, 1e-6) == INVALID
+    assert lib.uno_rope(None, 4, 8, FAKE16, 1024, None, 1e6, None, 1e-6) == INVALID
+    assert lib.uno_rope(None, 4, 8, FAKE16, 1024, FAKE16, 1.0, None, 1e-6) == INVALID
+    assert lib.uno_rope(None, 4, 8, FAKE16, 1024, FAKE16, 1e6, FAKE16, -1.0) == INVALID       # norm eps
+    assert lib.uno_rope(None, 4, 8, FAKE16, 1024, FAKE16, 1e6, ctypes.c_void_p(0x10001), 1e-6) == UNSUPPORTED
     # uno_silu_mul(stream, rows, dim, g, ldg, u, ldu, out, ldo)
     assert lib.uno_silu_mul(None, 4, 12, FAKE16, 12, FAKE16, 12, FAKE16, 12) == INVALID
     assert lib.uno_silu_mul(None, 4, 16, FAKE16, 16, None, 16, FAKE16, 16) == INVALID
@@ -397,6 +399,13 @@ def test_decoder_layer_rejects_bad_calls(lib):
                                  1.0, FAKE16, FAKE16, 16) == WORKSPACE
     assert lib.uno_decoder_layer(None, 2, 4, 8, 256, 512, 4, 2, 8, ctypes.byref(lw), FAKE16, FAKE16, None, 1e-6, 0.5,
                                  1.0, FAKE16, FAKE16, 1 << 30) == INVALID      # rope theta
+    lw.q_norm = FAKE16.value                                                   # q_norm without k_norm
+    assert lib.uno_decoder_layer(None, 2, 4, 8, 256, 512, 4, 2, 8, ctypes.byref(lw), FAKE16, FAKE16, None, 1e-6, 1e6,
+                                 1.0, FAKE16, FAKE16, 1 << 30) == INVALID
+    lw.k_norm = 0x10008                                                        # unaligned
+    assert lib.uno_decoder_layer(None, 2, 4, 8, 256, 512, 4, 2, 8, ctypes.byref(lw), FAKE16, FAKE16, None, 1e-6, 1e6,
+                                 1.0, FAKE16, FAKE16, 1 << 30) == UNSUPPORTED
+    lw.q_norm = lw.k_norm = None
     lw.w[3] = None
     assert lib.uno_decoder_layer(None, 2, 4, 8, 256, 512, 4, 2, 8, ctypes.byref(lw), FAKE16, FAKE16, None, 1e-6, 1e6,
                                  1.0, FAKE16, FAKE16, 1 << 30) == INVALID
@@ -437,6 +446,9 @@ def test_step_rejects_bad_calls(lib):
         for i in range(7):
             layers[l].w[i] = layers[l].a[i] = layers[l].b[i] = FAKE16.value
     assert call(small, embed=None) == INVALID
+    layers[1].k_norm = FAKE16.value                        # k_norm without q_norm
+    assert call(small) == INVALID
+    layers[1].k_norm = None
     assert call(small, ud=None) == INVALID
     assert call(small, ua=None) == INVALID                 # a carried q needs the accept uniforms
     assert call(small, pq_row=999) == INVALID              # row stride below the vocabulary

@@ -279,7 +279,7 @@ def test_decoder_layer_full_size_sampled_sequences(gpu_lib, lc):
     assert err <= LAYER_BAR
 
 
-@pytest.mark.parametrize("name", ["small", "block16", "no_cache"])
+@pytest.mark.parametrize("name", ["small", "block16", "no_cache", "no_qk_norm"])
 def test_decoder_layer_stages_within_single_op_bar(gpu_lib, name):
     """Each stage of the layer, run through its own entry point on the GPU's
     output of the stage before, against the oracle's stage on the same input:
@@ -321,11 +321,17 @@ def test_decoder_layer_stages_within_single_op_bar(gpu_lib, name):
         qkv[p], ref = proj(a, p)
         err[p] = row_relerr(qkv[p], ref)
     qd, kd = dev(qkv["q"]), dev(qkv["k"])
-    gpu_lib.rope(qd, to_dev(pos), 1e6)
-    gpu_lib.rope(kd, to_dev(pos), 1e6)
+    gpu_lib.rope(qd, to_dev(pos), 1e6, norm_weight=Wd.get("q_norm"))
+    gpu_lib.rope(kd, to_dev(pos), 1e6, norm_weight=Wd.get("k_norm"))
     qr, kr = back(qd), back(kd)
-    err["rope_q"] = row_relerr(qr, bf(oracle.rope(qkv["q"].reshape(rows, nh, 128), pos)).reshape(rows, -1))
-    err["rope_k"] = row_relerr(kr, bf(oracle.rope(qkv["k"].reshape(rows, nkv, 128), pos)).reshape(rows, -1))
+
+    def headnorm(x, name):
+        return oracle.rms_norm(x, w64[name], 1e-6) if name in w64 else x
+
+    err["rope_q"] = row_relerr(qr, bf(oracle.rope(headnorm(qkv["q"].reshape(rows, nh, 128), "q_norm"),
+                                                  pos)).reshape(rows, -1))
+    err["rope_k"] = row_relerr(kr, bf(oracle.rope(headnorm(qkv["k"].reshape(rows, nkv, 128), "k_norm"),
+                                                  pos)).reshape(rows, -1))
     att_d, _ = gpu_lib.block_verify_attention(dev(qr).view(B, n, nh, 128), _bits_dev(c["k_cache"]),
                                               _bits_dev(c["v_cache"]), dev(kr).view(B, n, nkv, 128),
                                               dev(qkv["v"]).view(B, n, nkv, 128), block, 1 / np.sqrt(128))
