@@ -237,64 +237,130 @@ __device__ __forceinline__ void cut_pass(const T* row, int vocab, F f) {
   }
 }
 
-// Radix descent: the first bin, from the top, at which the running total
-// (starting from `before`) reaches `target`; returns the bin, and in
-// `before` the total of the bins above it.  Wave 0 runs it (256 bins, 4 per
-// lane, lane l holding bins 255 - 4l .. 252 - 4l); every lane gets the result.
-template <typename U>
-__device__ __forceinline__ int find_from_top(const U* hist, double target, double& before) {
-  const int lane = threadIdx.x & (kWave - 1);
-  double c[4], mine = 0.0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    c[q] = double(hist[255 - (4 * lane + q)]);
-    mine += c[q];
-  }
-  // inclusive scan of the lanes' sums (exact: integers below 2^53)
-  double incl = mine;
+// Radix levels over a logit key, from the top: 12 key bits, then the rest.
+// bf16 keys vary in their top 16 bits only (12 + 4); fp32 keys take
+// 12 + 12 + 8.  A 4096-bin first level spreads a row's elements over many
+// bins (an 8-bit first level holds little more than sign and exponent, so
+// most of a row lands in a few bins and the histogram atomics serialise).
+constexpr int kCutBins = 4096;
+constexpr int kMaxCand = 512;   // top-k candidates resolved in LDS (pairwise counts: C^2 / 1024 steps per thread)
+__host__ __device__ constexpr int cut_levels(bool half) { return half ? 2 : 3; }
+__device__ __forceinline__ int cut_shift(bool half, int lev) { return lev == 0 ? 20 : (half ? 16 : (lev == 1 ? 8 : 0)); }
+__device__ __forceinline__ int cut_width(bool half, int lev) { return lev == 0 ? 12 : (half ? 4 : (lev == 1 ? 12 : 8)); }
+
+__device__ __forceinline__ unsigned long long shfl_up_u64(unsigned long long v, int off) {
+  const unsigned lo = __shfl_up(unsigned(v), off), hi = __shfl_up(unsigned(v >> 32), off);
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int off) {
+  const unsigned lo = __shfl_xor(unsigned(v), off), hi = __shfl_xor(unsigned(v >> 32), off);
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
+// Block-wide maximum of a 32-bit value (red: kCutWaves words of LDS); every
+// thread gets the result.
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
-    const double o = __shfl_up(incl, off);
+    const uint32_t o = __shfl_xor(v, off);
+    v = o > v ? o : v;
+  }
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  uint32_t r = red[0];
+  for (int q = 1; q < kCutWaves; ++q) r = red[q] > r ? red[q] : r;
+  __syncthreads();
+  return r;
+}
+
+// Block-wide sum of 64-bit integers (exact; red: kCutWaves words); every
+// thread gets the result.
+__device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v, unsigned long long* red) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) v += shfl_xor_u64(v, off);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  unsigned long long r = 0;
+  for (int q = 0; q < kCutWaves; ++q) r += red[q];
+  __syncthreads();
+  return r;
+}
+
+// Radix step over `nb` <= 4 * kCutThreads bins: the first bin, from the top,
+// at which the running total (starting from `before`) reaches `target`;
+// returns the bin, and in `before` the total of the bins above it.  Thread t
+// holds bins nb - 1 - 4t .. nb - 4 - 4t; the sums are exact integers (counts,
+// or fixed-point masses), scanned over the block; every thread gets the
+// result.  A target above the total (never reached) keeps everything: bin 0.
+template <typename U>
+__device__ int find_from_top(const U* hist, int nb, double target, unsigned long long& before,
+                             unsigned long long* sh_w, int* sh_i) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  unsigned long long c[4], mine = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int idx = nb - 1 - (4 * tid + q);
+    c[q] = idx >= 0 ? static_cast<unsigned long long>(hist[idx]) : 0ull;
+    mine += c[q];
+  }
+  unsigned long long incl = mine;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const unsigned long long o = shfl_up_u64(incl, off);
     if (lane >= off) incl += o;
   }
-  const double excl = incl - mine;
-  const uint64_t hit = wave_ballot(before + incl >= target);
-  int bin = 0;
-  double bef = 0.0;
-  if (hit) {
-    const int l = int(__builtin_ctzll(hit));
-    double run = before + __shfl(excl, l);
+  if (lane == kWave - 1) sh_w[wave] = incl;
+  if (tid == 0) sh_i[0] = kCutThreads;
+  __syncthreads();
+  unsigned long long above = before;
+  for (int q = 0; q < wave; ++q) above += sh_w[q];
+  above += incl - mine;   // every bin above this thread's four
+  const uint64_t hit = wave_ballot(double(above + mine) >= target);
+  if (hit && lane == int(__builtin_ctzll(hit))) atomicMin(&sh_i[0], tid);
+  __syncthreads();
+  const int first = sh_i[0];
+  if (tid == first) {
+    unsigned long long run = above;
     int found = 3;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const double cq = __shfl(c[q], l);
-      if (found == 3 && q < 3 && run + cq >= target) {
+      if (found == 3 && q < 3 && double(run + c[q]) >= target) {
         found = q;
       } else if (found == 3 && q < 3) {
-        run += cq;
+        run += c[q];
       }
     }
-    bin = 255 - (4 * l + found);
-    bef = run;
-  } else {   // never reached (target within the total): keep everything
-    bin = 0;
-    bef = before + __shfl(incl, kWave - 1);
+    sh_i[1] = nb - 1 - (4 * tid + found);
+    sh_w[kCutWaves] = run;
+  } else if (first == kCutThreads && tid == kCutThreads - 1) {
+    sh_i[1] = 0;
+    sh_w[kCutWaves] = above + mine;   // the block total
   }
-  before = bef;
+  __syncthreads();
+  const int bin = sh_i[1];
+  before = sh_w[kCutWaves];
+  __syncthreads();   // sh_w / sh_i free for the next step
   return bin;
 }
 
-template <typename T>
-__global__ __launch_bounds__(kCutThreads) void lin_cut_kernel(VerifyLinearArgs a, CutWs w, CutParams cp) {
-  __shared__ uint32_t hcnt[256];
-  __shared__ unsigned long long hmass[256];
+// GREEDY: the instantiation for greedy rows (the maximum only, no histograms
+// in LDS); the other serves top-k and top-p.  Held to 64 VGPRs (8 waves per
+// SIMD): two workgroups per compute unit, so one streams while the other
+// reduces (at 72 VGPRs only one fits and the passes run at half speed).
+template <typename T, bool GREEDY>
+__global__ __launch_bounds__(kCutThreads, 8) void lin_cut_kernel(VerifyLinearArgs a, CutWs w, CutParams cp) {
+  __shared__ uint32_t hcnt[kCutBins];
+  __shared__ unsigned long long hmass[kCutBins];
   __shared__ uint32_t red_k[kCutWaves];
   __shared__ int red_i[kCutWaves];
   __shared__ float red_f[kCutWaves];
+  __shared__ unsigned long long sh_w[kCutWaves + 1];
+  __shared__ int sh_i[2];
   __shared__ uint32_t sh_key;
   __shared__ int sh_idx;
-  __shared__ double sh_before;
-  __shared__ unsigned long long sh_total;
+  __shared__ int sh_ncand;
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int rps = 2 * a.k + 1;
   const int b = row / rps, j = row - b * rps;
@@ -302,9 +368,17 @@ __global__ __launch_bounds__(kCutThreads) void lin_cut_kernel(VerifyLinearArgs a
   const T* base = lin_row<T>(a, b, j, &draft);
   const int V = a.vocab;
   const float sl2 = a.scale_log2;
-  // key bits that vary: 16 for bf16 rows (the low half of a bf16 key is set by its sign)
-  constexpr int kLevels = sizeof(T) == 2 ? 2 : 4;
-
+  constexpr bool kHalf = sizeof(T) == 2;   // bf16 rows: the low 16 key bits follow from the sign
+  constexpr int kLevels = cut_levels(kHalf);
+  const bool topk = !GREEDY && cp.top_k > 0 && cp.top_k < V;
+  const bool topp = !GREEDY && cp.top_p < 1.f;
+  if constexpr (!GREEDY) {
+    for (int i = tid; i < kCutBins; i += kCutThreads) {   // only the histograms this call uses
+      if (topk) hcnt[i] = 0;
+      if (topk || topp) hmass[i] = 0ull;
+    }
+    __syncthreads();
+  }
   // pass A: the largest key and its first index
   uint32_t bk = 0;
   int bi = 0x7fffffff;
@@ -315,6 +389,7 @@ __global__ __launch_bounds__(kCutThreads) void lin_cut_kernel(VerifyLinearArgs a
       bi = v;
     }
   });
+  const uint32_t own_max = bk;   // this thread's largest key (0: no element)
   // block argmax: largest key, then smallest index
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
@@ -328,10 +403,6 @@ __global__ __launch_bounds__(kCutThreads) void lin_cut_kernel(VerifyLinearArgs a
   if (lane == 0) {
     red_k[wave] = bk;
     red_i[wave] = bi;
-  }
-  for (int i = tid; i < 256; i += kCutThreads) {
-    hcnt[i] = 0;
-    hmass[i] = 0ull;
   }
   __syncthreads();
   if (tid == 0) {
@@ -351,88 +422,192 @@ __global__ __launch_bounds__(kCutThreads) void lin_cut_kernel(VerifyLinearArgs a
   const float m = key_logit(maxkey) * sl2;
   if (tid == 0 && j != a.k)   // rows that score a draft: its logit (-inf for an id outside [0, V))
     w.xd[row] = (draft >= 0 && draft < V) ? load_logit<T>(base, draft) : -INFINITY;
-  if (cp.greedy) {
+  if constexpr (GREEDY) {
     if (tid == 0) w.cut[row] = RowCut{m, 1.f, maxkey, amax};
     return;
-  }
+  } else {
   // the key prefix fixed so far and its width; below it every element counts
   uint32_t prefix = 0;
   int fixed_bits = 0;
   auto in_prefix = [&](uint32_t kk) { return fixed_bits == 0 || (kk >> (32 - fixed_bits)) == (prefix >> (32 - fixed_bits)); };
+  // a fixed prefix of a bf16 key: the low 16 bits follow from the sign
+  auto full_key = [&](uint32_t pre) { return kHalf ? (pre | ((pre & 0x80000000u) ? 0u : 0xffffu)) : pre; };
   uint32_t tau = 0;   // keep all
-  // ---- top-k: the k-th largest key, by counts
-  if (cp.top_k > 0 && cp.top_k < V) {
-    double before = 0.0;
-    for (int lev = 0; lev < kLevels; ++lev) {
-      const int shift = 24 - 8 * lev;
-      cut_pass<T>(base, V, [&](int, float x) {
-        const uint32_t kk = logit_key(x);
-        if (in_prefix(kk)) atomicAdd(&hcnt[(kk >> shift) & 255u], 1u);
-      });
-      __syncthreads();
-      if (wave == 0) {
-        double bef = before;
-        const int bin = find_from_top(hcnt, double(cp.top_k), bef);
-        if (lane == 0) {
-          sh_key = uint32_t(bin);
-          sh_before = bef;
-        }
+  auto mass_fx = [&](float x) {   // 2^(y - m) in fixed point (2^-40), truncated
+    return (unsigned long long)(double(fast_exp2(fmaf(x, sl2, -m))) * kMassScale);
+  };
+  // Kept mass in fixed point, taken from the last level of the transform that
+  // sets tau (exact integer sums, so independent of the order of additions);
+  // without top-k and top-p a pass sums it in fp32 below.
+  unsigned long long kept_fx = 0;
+  bool have_kept = false;
+  // ---- top-k: the k-th largest key.  Fast path (k <= one key per thread):
+  // the k-th largest of the threads' own maxima, t0, has at least k keys at
+  // or above it (k distinct elements), so the k-th largest key is >= t0; one
+  // pass gathers the keys >= t0 into LDS, and when they fit (kMaxCand) the
+  // cut (and with top-p the top-p cut too) is resolved among them with exact
+  // integer counts and fixed-point masses.  Otherwise (a row with many equal
+  // keys at the top) the radix passes over the whole row take over.
+  bool topp_done = false;
+  if (topk) {
+    bool fast = cp.top_k <= kCutThreads;
+    if (fast) {
+      unsigned long long before = 0;
+      for (int lev = 0; lev < kLevels; ++lev) {   // radix select over the threads' maxima
+        const int shift = cut_shift(kHalf, lev), width = cut_width(kHalf, lev);
+        if (in_prefix(own_max)) atomicAdd(&hcnt[(own_max >> shift) & ((1u << width) - 1u)], 1u);
+        __syncthreads();
+        const int bin = find_from_top(hcnt, 1 << width, double(cp.top_k), before, sh_w, sh_i);
+        prefix |= uint32_t(bin) << shift;
+        fixed_bits += width;
+        for (int i = tid; i < (1 << width); i += kCutThreads) hcnt[i] = 0;
+        __syncthreads();
       }
+      const uint32_t t0 = full_key(prefix);
+      prefix = 0;
+      fixed_bits = 0;
+      if (tid == 0) sh_ncand = 0;
       __syncthreads();
-      prefix |= sh_key << shift;
-      fixed_bits += 8;
-      before = sh_before;
-      for (int i = tid; i < 256; i += kCutThreads) hcnt[i] = 0;
-      __syncthreads();
-    }
-    if (kLevels == 2) prefix |= (prefix & 0x80000000u) ? 0u : 0xffffu;
-    tau = prefix;
-    prefix = 0;
-    fixed_bits = 0;
-  }
-  // ---- top-p on the kept distribution: the smallest key group whose mass
-  // above is below top_p of the kept mass, by fixed-point masses
-  if (cp.top_p < 1.f) {
-    const uint32_t base_tau = tau;
-    auto mass_fx = [&](float x) {
-      return (unsigned long long)(double(fast_exp2(fmaf(x, sl2, -m))) * kMassScale);
-    };
-    double before = 0.0, target = 0.0;
-    for (int lev = 0; lev < kLevels; ++lev) {
-      const int shift = 24 - 8 * lev;
+      uint32_t* ckey = hcnt;               // candidates: keys >= t0 (first kMaxCand kept)
+      unsigned long long* cmass = hmass;   // and their fixed-point masses
       cut_pass<T>(base, V, [&](int, float x) {
         const uint32_t kk = logit_key(x);
-        if (kk >= base_tau && in_prefix(kk)) atomicAdd(&hmass[(kk >> shift) & 255u], mass_fx(x));
+        // past kMaxCand + 1 the count no longer matters (the row falls back)
+        if (kk >= t0 && *reinterpret_cast<volatile int*>(&sh_ncand) <= kMaxCand) {
+          const int slot = atomicAdd(&sh_ncand, 1);
+          if (slot < kMaxCand) ckey[slot] = kk;
+        }
       });
       __syncthreads();
-      if (lev == 0) {
-        if (tid == 0) {
-          unsigned long long t = 0;
-          for (int i = 0; i < 256; ++i) t += hmass[i];
-          sh_total = t;
+      const int C = sh_ncand;
+      fast = C <= kMaxCand;
+      if (fast) {
+        for (int i = tid; i < C; i += kCutThreads) cmass[i] = mass_fx(key_logit(ckey[i]));
+        __syncthreads();
+        // tau: the largest candidate key with at least k candidates at or above it
+        uint32_t best = 0;
+        for (int i = tid; i < C; i += kCutThreads) {
+          const uint32_t ki = ckey[i];
+          int ge = 0;
+          for (int q = 0; q < C; ++q) ge += ckey[q] >= ki ? 1 : 0;
+          if (ge >= cp.top_k && ki > best) best = ki;
+        }
+        tau = block_max_u32(best, red_k);
+        if (topp) {   // top-p among the kept candidates, by the same rule as the radix path
+          unsigned long long tot = 0;
+          for (int i = tid; i < C; i += kCutThreads)
+            if (ckey[i] >= tau) tot += cmass[i];
+          const double target = double(cp.top_p) * double(block_sum_u64(tot, sh_w));
+          uint32_t low = 0xffffffffu;   // smallest key whose mass strictly above is below target
+          for (int i = tid; i < C; i += kCutThreads) {
+            const uint32_t ki = ckey[i];
+            if (ki < tau) continue;
+            unsigned long long above = 0;
+            for (int q = 0; q < C; ++q) above += ckey[q] > ki ? cmass[q] : 0ull;
+            if (double(above) < target && ki < low) low = ki;
+          }
+          tau = ~block_max_u32(~low, red_k);
+          topp_done = true;
+        }
+        unsigned long long kept = 0;
+        for (int i = tid; i < C; i += kCutThreads)
+          if (ckey[i] >= tau) kept += cmass[i];
+        kept_fx = block_sum_u64(kept, sh_w);
+        have_kept = true;
+      } else {   // back to the radix passes: clear the candidate storage
+        for (int i = tid; i < kCutBins; i += kCutThreads) {
+          hcnt[i] = 0;
+          hmass[i] = 0ull;
         }
         __syncthreads();
-        target = double(cp.top_p) * double(sh_total);
       }
-      if (wave == 0) {
-        double bef = before;
-        const int bin = find_from_top(hmass, target, bef);
-        if (lane == 0) {
-          sh_key = uint32_t(bin);
-          sh_before = bef;
+    }
+    if (!fast) {
+      // radix over the row; without top-p the last level also gathers the
+      // masses: every key above the prefix range fixed so far is kept, and of
+      // the keys inside it those from the chosen bin up
+      const bool masses = !topp;
+      unsigned long long before = 0;
+      for (int lev = 0; lev < kLevels; ++lev) {
+        const int shift = cut_shift(kHalf, lev), width = cut_width(kHalf, lev);
+        const bool last = lev == kLevels - 1;
+        const uint32_t mask = (1u << width) - 1u;
+        const uint32_t hi = fixed_bits == 0 ? 0xffffffffu : (prefix | ((1u << (32 - fixed_bits)) - 1u));
+        unsigned long long above = 0;
+        cut_pass<T>(base, V, [&](int, float x) {
+          const uint32_t kk = logit_key(x);
+          if (in_prefix(kk)) {
+            atomicAdd(&hcnt[(kk >> shift) & mask], 1u);
+            if (last && masses) atomicAdd(&hmass[(kk >> shift) & mask], mass_fx(x));
+          } else if (last && masses && kk > hi) {
+            above += mass_fx(x);
+          }
+        });
+        __syncthreads();
+        if (last && masses) kept_fx = block_sum_u64(above, sh_w);
+        const int bin = find_from_top(hcnt, 1 << width, double(cp.top_k), before, sh_w, sh_i);
+        if (last && masses) {
+          unsigned long long t = 0;
+          for (int i = bin + tid; i < (1 << width); i += kCutThreads) t += hmass[i];
+          kept_fx += block_sum_u64(t, sh_w);
+          have_kept = true;
         }
+        prefix |= uint32_t(bin) << shift;
+        fixed_bits += width;
+        for (int i = tid; i < (1 << width); i += kCutThreads) hcnt[i] = 0;
+        __syncthreads();
       }
+      tau = full_key(prefix);
+      prefix = 0;
+      fixed_bits = 0;
+    }
+  }
+  // ---- top-p on the kept distribution: the smallest key group whose mass
+  // above is below top_p of the kept mass, by fixed-point masses; the kept
+  // mass is then the mass above the last level's bin plus the bin's own
+  if (topp && !topp_done) {
+    const uint32_t base_tau = tau;
+    unsigned long long before = 0;
+    double target = 0.0;
+    for (int lev = 0; lev < kLevels; ++lev) {
+      const int shift = cut_shift(kHalf, lev), width = cut_width(kHalf, lev);
+      const uint32_t mask = (1u << width) - 1u;
+      cut_pass<T>(base, V, [&](int, float x) {
+        const uint32_t kk = logit_key(x);
+        if (kk >= base_tau && in_prefix(kk)) atomicAdd(&hmass[(kk >> shift) & mask], mass_fx(x));
+      });
       __syncthreads();
-      prefix |= sh_key << shift;
-      fixed_bits += 8;
-      before = sh_before;
-      for (int i = tid; i < 256; i += kCutThreads) hmass[i] = 0ull;
+      if (lev == 0) {   // the kept mass in fixed point: the sum of the first level's bins (exact)
+        if (wave == 0) {
+          unsigned long long t = 0;
+          for (int i = lane; i < kCutBins; i += kWave) t += hmass[i];
+#pragma unroll
+          for (int off = 1; off < kWave; off <<= 1) t += shfl_xor_u64(t, off);
+          if (lane == 0) sh_w[kCutWaves] = t;
+        }
+        __syncthreads();
+        target = double(cp.top_p) * double(sh_w[kCutWaves]);
+        __syncthreads();
+      }
+      const int bin = find_from_top(hmass, 1 << width, target, before, sh_w, sh_i);
+      if (lev == kLevels - 1) {
+        kept_fx = before + hmass[bin];
+        have_kept = true;
+      }
+      prefix |= uint32_t(bin) << shift;
+      fixed_bits += width;
+      __syncthreads();   // hmass[bin] read by every thread before the clear
+      for (int i = tid; i < (1 << width); i += kCutThreads) hmass[i] = 0ull;
       __syncthreads();
     }
-    if (kLevels == 2) prefix |= (prefix & 0x80000000u) ? 0u : 0xffffu;
-    tau = prefix > base_tau ? prefix : base_tau;
+    tau = full_key(prefix);
+    tau = tau > base_tau ? tau : base_tau;
   }
-  // kept mass, each thread in index order, then waves in order
+  if (have_kept) {
+    if (tid == 0) w.cut[row] = RowCut{m, float(double(kept_fx) / kMassScale), tau, -1};
+    return;
+  }
+  // kept mass (every key >= tau), each thread in index order, then waves in order
   float acc = 0.f;
   cut_pass<T>(base, V, [&](int, float x) {
     if (logit_key(x) >= tau) acc += fast_exp2(fmaf(x, sl2, -m));
@@ -444,6 +619,7 @@ __global__ __launch_bounds__(kCutThreads) void lin_cut_kernel(VerifyLinearArgs a
     float t = 0.f;
     for (int q = 0; q < kCutWaves; ++q) t += red_f[q];
     w.cut[row] = RowCut{m, t, tau, -1};
+  }
   }
 }
 
@@ -503,7 +679,10 @@ hipError_t launch_lin_cut(const VerifyLinearArgs& a, const CutParams& cp, hipStr
   CutWs w = cut_ws(a.ws, a.batch, a.k, a.vocab);
   {
     ProfileScope ps("uno_row_cut", stream);
-    hipLaunchKernelGGL(lin_cut_kernel<T>, dim3(rows), dim3(kCutThreads), 0, stream, a, w, cp);
+    if (cp.greedy)
+      hipLaunchKernelGGL((lin_cut_kernel<T, true>), dim3(rows), dim3(kCutThreads), 0, stream, a, w, cp);
+    else
+      hipLaunchKernelGGL((lin_cut_kernel<T, false>), dim3(rows), dim3(kCutThreads), 0, stream, a, w, cp);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
