@@ -19,10 +19,19 @@ from _parity import check_linear_sampled, say, to_dev, to_host
 pytestmark = pytest.mark.gpu
 
 
-def _case(batch, k, vocab, sigma, dtype, seed, T, top_k, top_p, greedy, integer_logits=False):
-    """Logits of the linear-verify workload (or small integers, for many ties);
-    drafts drawn from the transformed draft rows."""
+def _case(batch, k, vocab, sigma, dtype, seed, T, top_k, top_p, greedy, integer_logits=False, eighths=False):
+    """Logits of the linear-verify workload (or small integers, for many ties;
+    or the workload's logits rounded to multiples of 1/8, for a few ties at
+    the top); drafts drawn from the transformed draft rows."""
     c = workloads.verify_linear_case(batch, k, vocab, sigma, dtype=dtype, seed=seed, workers=4)
+    if eighths:
+        pv = (np.round(c["p_f32"] * 8.0) / 8.0).astype(np.float32)     # exact in bf16 below 32
+        qv = (np.round(c["q_f32"] * 8.0) / 8.0).astype(np.float32)
+        if dtype == "bf16":
+            c["p"], c["q"] = workloads.bf16_bits(pv), workloads.bf16_bits(qv)
+        else:
+            c["p"], c["q"] = pv, qv
+        c["p_f32"], c["q_f32"] = pv, qv
     if integer_logits:
         rng = workloads.rng_for(seed, 77)
         pv = rng.integers(-6, 4, (batch, k + 1, vocab)).astype(np.float32)
@@ -89,6 +98,35 @@ def test_sampled_verify_tie_groups(gpu_lib, dtype, top_k, top_p):
         return c["p_f32"][b], c["q_f32"][b], c["drafts"][b], c["u_acc"][b], float(c["u_s"][b])
 
     assert check_linear_sampled(rows, g, range(4), 4, 1.0, top_k, top_p, False) <= 1
+
+
+@pytest.mark.parametrize("dtype,top_k,top_p,eighths", [("bf16", 50, 1.0, True), ("bf16", 50, 0.9, True),
+                                                       ("f32", 64, 0.8, True), ("f32", 1024, 1.0, False),
+                                                       ("bf16", 1025, 0.95, False)])
+def test_sampled_verify_topk_candidate_edges(gpu_lib, dtype, top_k, top_p, eighths):
+    """Top-k's two roads: the candidate keys gathered above the k-th largest of
+    the threads' maxima (with a few ties at the boundary when the logits are
+    multiples of 1/8; top-p then resolved among the candidates), k = 1024
+    (the largest k that road takes) and k = 1025 (the radix descent)."""
+    import torch
+    say(f"sampled verify, candidate edges {dtype} top_k={top_k} top_p={top_p} eighths={eighths}")
+    c = _case(3, 4, 20000, 0.5, dtype, 31 + top_k, 1.0, top_k, top_p, False, eighths=eighths)
+    out = gpu_lib.psi_spec_verify_linear_sampled(to_dev(c["p"]), to_dev(c["q"]), to_dev(c["drafts"]),
+                                                 to_dev(c["u_acc"]), to_dev(c["u_s"]), 1.0, top_k, top_p, False)
+    torch.cuda.synchronize()
+    g = {kk: to_host(v) for kk, v in out.items()}
+
+    def rows(b):
+        return c["p_f32"][b], c["q_f32"][b], c["drafts"][b], c["u_acc"][b], float(c["u_s"][b])
+
+    assert check_linear_sampled(rows, g, range(3), 4, 1.0, top_k, top_p, False) <= 1
+    if eighths:   # the boundary of some row falls inside a tie group: the cut keeps it whole
+        tied = 0
+        for b in range(3):
+            for r in c["p_f32"][b]:
+                kth = np.sort(r)[::-1][top_k - 1]
+                tied += int(np.sum(r == kth) > 1)
+        assert tied > 0
 
 
 def test_sampled_verify_off_matches_plain_verify(gpu_lib):
