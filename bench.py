@@ -606,7 +606,8 @@ def bench_linear_sigma_sweep(args, dad, torch, sigmas=(0.1, 0.5, 2.0), reps=20):
     over the rows it reads, the mean accepted length, and two lower bounds at
     the 8 TB/s peak: reading every row once (what this design reads), and
     reading only the rows an early exit at the first rejection would need
-    (p and q rows 0..L, plus the residual or bonus rows of the draw)."""
+    (p and q rows 0..L, plus the residual or bonus rows of the draw); then the
+    early-exit verify itself on the same inputs, its rate over those rows."""
     import numpy as np
     dev = torch.device("cuda:0")
     B, k, V = LIN_BATCH, LIN_K, VOCAB
@@ -653,6 +654,31 @@ def bench_linear_sigma_sweep(args, dad, torch, sigmas=(0.1, 0.5, 2.0), reps=20):
                     "full_read_lower_bound_us": full_bytes / (HBM_PEAK_GBS * 1e9) * 1e6,
                     "early_exit_lower_bound_us": early_bytes / (HBM_PEAK_GBS * 1e9) * 1e6})
         log(f"linear verify sigma {sigma}: {ms * 1e3:.1f} us, mean L {L.mean():.2f}")
+        # the early-exit variant on the same inputs: rows after each sequence's
+        # first rejection are not read (uno_psi_spec_verify_linear_early_exit)
+        ws_e = torch.empty(dad.psi_spec_verify_linear_early_exit_workspace(B, k, V), dtype=torch.uint8, device=dev)
+        out_e = {"accept_len": torch.empty(B, dtype=torch.int32, device=dev),
+                 "token": torch.empty(B, dtype=torch.int32, device=dev)}
+        for _ in range(3):
+            dad.psi_spec_verify_linear_early_exit(p, q, drafts, ua, us, outputs=out_e, workspace=ws_e)
+        torch.cuda.synchronize()
+        dad.profile_reset()
+        dad.profile_enable(True)
+        for _ in range(reps):
+            dad.psi_spec_verify_linear_early_exit(p, q, drafts, ua, us, outputs=out_e, workspace=ws_e)
+        torch.cuda.synchronize()
+        ee_ms = sum(dad.profile_query(n)[0] for n in ("uno_ee_init", "uno_ee_flow", "uno_draw_seg",
+                                                     "uno_draw_resolve")) / reps
+        flow_ms = dad.profile_query("uno_ee_flow")[0] / reps
+        dad.profile_enable(False)
+        dad.profile_reset()
+        Le = out_e["accept_len"].cpu().numpy().astype(np.int64)
+        res[-1]["early_exit"] = {"us": ee_ms * 1e3, "flow_us": flow_ms * 1e3,
+                                 "gbs": early_bytes / (ee_ms * 1e-3) / 1e9,
+                                 "hbm_frac": early_bytes / (ee_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                 "bytes": early_bytes,
+                                 "same_accept_len_as_full": int((Le == L).sum())}
+        log(f"  early exit: {ee_ms * 1e3:.1f} us ({early_bytes / 1e9:.2f} GB read)")
         if sigma == 0.5:
             # the same rows under sampling transforms (uno_psi_spec_verify_linear_sampled;
             # the drafts here come from the untransformed rows, which changes no work)

@@ -20,6 +20,7 @@ EXPORTS = (
     "uno_abi_version", "uno_status_string", "uno_last_error",
     "uno_gated_lora_linear_workspace", "uno_gated_lora_linear", "uno_lora_merge",
     "uno_psi_spec_verify_linear_workspace", "uno_psi_spec_verify_linear", "uno_psi_spec_verify_linear_noalloc",
+    "uno_psi_spec_verify_linear_early_exit_workspace", "uno_psi_spec_verify_linear_early_exit",
     "uno_psi_spec_verify_linear_sampled_workspace", "uno_psi_spec_verify_linear_sampled",
     "uno_tree_verify_attention_workspace", "uno_tree_verify_attention",
     "uno_psi_spec_verify_tree_workspace", "uno_psi_spec_verify_tree",
@@ -85,6 +86,10 @@ def _declare(lib):
         "uno_psi_spec_verify_linear": (ctypes.c_int, [_p, ctypes.c_int, _i32, _i32, _i32,
                                                       _p, _i64, _i64, _p, _i64, _i64,
                                                       _p, _p, _p, _f32, _p, _p, _p, _p, _p, _p, _sz]),
+        "uno_psi_spec_verify_linear_early_exit_workspace": (ctypes.c_int, [_i32, _i32, _i32, ctypes.POINTER(_sz)]),
+        "uno_psi_spec_verify_linear_early_exit": (ctypes.c_int, [_p, ctypes.c_int, _i32, _i32, _i32,
+                                                                 _p, _i64, _i64, _p, _i64, _i64,
+                                                                 _p, _p, _p, _f32, _p, _p, _p, _p, _p, _p, _sz]),
         "uno_psi_spec_verify_linear_sampled_workspace": (ctypes.c_int, [_i32, _i32, _i32, ctypes.POINTER(_sz)]),
         "uno_psi_spec_verify_linear_sampled": (ctypes.c_int, [_p, ctypes.c_int, _i32, _i32, _i32,
                                                               _p, _i64, _i64, _p, _i64, _i64,
@@ -265,6 +270,45 @@ def psi_spec_verify_linear(p_logits, q_logits, drafts, u_accept, u_sample, tempe
     ws = _workspace(psi_spec_verify_linear_workspace(bsz, k, vocab), dev, workspace)
     qs = q_logits.stride() if q_logits is not None else (0, 0, 1)
     _check(_lib.uno_psi_spec_verify_linear(
+        _stream(stream), _dtype_code(p_logits), bsz, k, vocab,
+        _ptr(p_logits), p_logits.stride(0), p_logits.stride(1),
+        _ptr(q_logits), qs[0], qs[1],
+        _ptr(drafts), _ptr(u_accept), _ptr(u_sample), float(temperature),
+        _ptr(outputs["accept_len"]), _ptr(outputs["token"]),
+        _ptr(outputs.get("p_draft")), _ptr(outputs.get("q_draft")), _ptr(outputs.get("residual_mass")),
+        _ptr(ws), _nbytes(ws)))
+    return outputs
+
+
+def psi_spec_verify_linear_early_exit_workspace(batch, k, vocab):
+    load()
+    out = _sz(0)
+    _check(_lib.uno_psi_spec_verify_linear_early_exit_workspace(batch, k, vocab, ctypes.byref(out)))
+    return out.value
+
+
+def psi_spec_verify_linear_early_exit(p_logits, q_logits, drafts, u_accept, u_sample, temperature=1.0,
+                                      outputs=None, want_probs=True, workspace=None, stream=None):
+    """Early-exit linear verify (uno_psi_spec_verify_linear_early_exit): the
+    arguments and outputs of psi_spec_verify_linear; p_draft / q_draft are NaN
+    after the first rejection."""
+    import torch
+    load()
+    bsz, k1, vocab = p_logits.shape
+    k = k1 - 1
+    dev = p_logits.device
+    if outputs is None:
+        outputs = {
+            "accept_len": torch.empty(bsz, dtype=torch.int32, device=dev),
+            "token": torch.empty(bsz, dtype=torch.int32, device=dev),
+        }
+        if want_probs:
+            outputs["p_draft"] = torch.empty((bsz, k), dtype=torch.float32, device=dev)
+            outputs["q_draft"] = torch.empty((bsz, k), dtype=torch.float32, device=dev)
+            outputs["residual_mass"] = torch.empty(bsz, dtype=torch.float32, device=dev)
+    ws = _workspace(psi_spec_verify_linear_early_exit_workspace(bsz, k, vocab), dev, workspace)
+    qs = q_logits.stride() if q_logits is not None else (0, 0, 1)
+    _check(_lib.uno_psi_spec_verify_linear_early_exit(
         _stream(stream), _dtype_code(p_logits), bsz, k, vocab,
         _ptr(p_logits), p_logits.stride(0), p_logits.stride(1),
         _ptr(q_logits), qs[0], qs[1],

@@ -453,6 +453,50 @@ uno_status uno_psi_spec_verify_linear(hipStream_t stream, uno_dtype logit_dtype,
   UNO_GUARD_END
 }
 
+// ------------------------------------------------------------------ early-exit linear verify
+static uno_status check_ee_items(int32_t batch, int32_t k, int32_t vocab) {
+  const int64_t nc = (int64_t(vocab) + 8191) / 8192;
+  if (int64_t(batch) * ((2 * k + 1) * nc + k + 1) > (int64_t(1) << 31) - 1)
+    return fail(UNO_ERR_UNSUPPORTED, "too many work items (batch * ((2k+1) * chunks + k + 1) >= 2^31)");
+  return UNO_OK;
+}
+
+uno_status uno_psi_spec_verify_linear_early_exit_workspace(int32_t batch, int32_t k, int32_t vocab, size_t* bytes) {
+  UNO_GUARD_BEGIN
+  if (!bytes) return fail(UNO_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  uno_status s = check_verify_linear_shape(batch, k, vocab);
+  if (s == UNO_OK) s = check_ee_items(batch, k, vocab);
+  if (s != UNO_OK) return s;
+  *bytes = verify_linear_ee_workspace_bytes(batch, k, vocab);
+  return UNO_OK;
+  UNO_GUARD_END
+}
+
+uno_status uno_psi_spec_verify_linear_early_exit(hipStream_t stream, uno_dtype logit_dtype, int32_t batch, int32_t k,
+                                                 int32_t vocab, const void* p_logits, int64_t p_seq_stride,
+                                                 int64_t p_row_stride, const void* q_logits, int64_t q_seq_stride,
+                                                 int64_t q_row_stride, const int32_t* draft_tokens,
+                                                 const float* u_accept, const float* u_sample, float temperature,
+                                                 int32_t* out_accept_len, int32_t* out_token, float* out_p_draft,
+                                                 float* out_q_draft, float* out_residual_mass, void* workspace,
+                                                 size_t workspace_bytes) {
+  UNO_GUARD_BEGIN
+  VerifyLinearArgs a{};
+  uno_status s = verify_linear_args(logit_dtype, batch, k, vocab, p_logits, p_seq_stride, p_row_stride, q_logits,
+                                    q_seq_stride, q_row_stride, draft_tokens, u_accept, u_sample, temperature,
+                                    out_accept_len, out_token, out_p_draft, out_q_draft, out_residual_mass, &a);
+  if (s == UNO_OK) s = check_ee_items(batch, k, vocab);
+  if (s != UNO_OK) return s;
+  const size_t need = verify_linear_ee_workspace_bytes(batch, k, vocab);
+  if (workspace_bytes < need || !workspace)
+    return fail(UNO_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  a.ws = workspace;
+  s = debug_check_verify_linear(stream, a);
+  if (s != UNO_OK) return s;
+  return check_hip(launch_verify_linear_ee(a, stream), "uno_psi_spec_verify_linear_early_exit launch");
+  UNO_GUARD_END
+}
+
 // ------------------------------------------------------------------ sampled linear verify
 static uno_status check_sampling(int32_t vocab, int32_t top_k, float top_p, int32_t greedy) {
   if (top_k < 0) return fail(UNO_ERR_INVALID_ARGUMENT, "top_k must be >= 0 (0: off; got %d)", top_k);

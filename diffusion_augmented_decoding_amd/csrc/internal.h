@@ -157,6 +157,9 @@ hipError_t launch_tree_build(const TreeBuildArgs& a, hipStream_t stream);
 
 size_t verify_linear_workspace_bytes(int batch, int k, int vocab);
 hipError_t launch_verify_linear(const VerifyLinearArgs& a, hipStream_t stream);
+// early exit: the rows after each sequence's first rejection are not read
+size_t verify_linear_ee_workspace_bytes(int batch, int k, int vocab);
+hipError_t launch_verify_linear_ee(const VerifyLinearArgs& a, hipStream_t stream);
 // The same verify on rows transformed by top-k (0: off), top-p (1: off) or greedy.
 size_t verify_linear_sampled_workspace_bytes(int batch, int k, int vocab);
 hipError_t launch_verify_linear_sampled(const VerifyLinearArgs& a, int top_k, float top_p, int greedy,

@@ -177,11 +177,12 @@ hipError_t launch_lin(const VerifyLinearArgs& a, hipStream_t stream) {
 // row is replaced by its transformed distribution, then the same accept,
 // residual and draw rules run on those.  Four launches:
 //  1. lin_cut: one 1024-thread block per row finds, exactly, the smallest
-//     logit key the transform keeps (radix select from the top, 8 key bits
-//     per level: integer counts for top-k, fixed-point masses for top-p, both
-//     through LDS integer atomics, so the result does not depend on the
-//     order of the additions), then the kept mass in a fixed order, the
-//     row's maximum and its first argmax (greedy) and the draft's logit;
+//     logit key the transform keeps (integer counts for top-k, 2^-40
+//     fixed-point masses for top-p, so the result does not depend on the
+//     order of the additions): top-k among the candidate keys gathered above
+//     the k-th largest of the threads' own maxima, top-p by radix levels of
+//     LDS histograms; the kept mass from the same exact sums; the row's
+//     maximum and its first argmax (greedy) and the draft's logit;
 //  2. lin_accept_cut: the accept tests on the transformed probabilities;
 //  3-4. the draw kernels with the transform applied to both rows.
 struct RowCut {

@@ -56,7 +56,7 @@ typedef enum {
 
 typedef enum { UNO_F32 = 0, UNO_BF16 = 1 } uno_dtype;
 
-#define UNO_ABI_VERSION 7
+#define UNO_ABI_VERSION 8
 
 int uno_abi_version(void);
 const char* uno_status_string(uno_status s);
@@ -142,6 +142,31 @@ uno_status uno_psi_spec_verify_linear(hipStream_t stream, uno_dtype logit_dtype,
                                       int32_t* out_accept_len, int32_t* out_token,
                                       float* out_p_draft, float* out_q_draft, float* out_residual_mass,
                                       void* workspace, size_t workspace_bytes);
+
+/* Early-exit variant of uno_psi_spec_verify_linear: the same accept rule,
+ * residual and draw, but the rows of positions after the first rejection are
+ * not read (drafts are tested in order, and the first rejection ends the
+ * block, so those rows cannot change the result).  Source: the same passage
+ * (the longest valid prefix of the block is kept).  Same arguments and
+ * outputs; the row statistics are summed over 8192-element chunks, so
+ * probabilities agree with uno_psi_spec_verify_linear to rounding and the
+ * decisions are the same except where a draft sits within rounding of its
+ * accept threshold.  out_p_draft / out_q_draft entries of positions after the
+ * first rejection are NaN (not evaluated).  The batch's positions are taken
+ * in order, so the time follows the longest accepted prefix in the batch and
+ * the bytes read follow the accepted lengths.  Extra requirement:
+ * batch * ((2k+1) * ceil(vocab / 8192) + k + 1) < 2^31. */
+uno_status uno_psi_spec_verify_linear_early_exit_workspace(int32_t batch, int32_t k, int32_t vocab, size_t* bytes);
+uno_status uno_psi_spec_verify_linear_early_exit(hipStream_t stream, uno_dtype logit_dtype,
+                                                 int32_t batch, int32_t k, int32_t vocab,
+                                                 const void* p_logits, int64_t p_seq_stride, int64_t p_row_stride,
+                                                 const void* q_logits, int64_t q_seq_stride, int64_t q_row_stride,
+                                                 const int32_t* draft_tokens,
+                                                 const float* u_accept, const float* u_sample,
+                                                 float temperature,
+                                                 int32_t* out_accept_len, int32_t* out_token,
+                                                 float* out_p_draft, float* out_q_draft, float* out_residual_mass,
+                                                 void* workspace, size_t workspace_bytes);
 
 /* Allocation-free variant of uno_psi_spec_verify_linear, for callers that
  * cannot allocate device memory or hand over a workspace (code under HIP graph

@@ -53,13 +53,17 @@ int main() {
 
   // linear verify, plain and sampled
   const int B = 3, K = 4, V = 1000;
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = 0; pass < 3; ++pass) {
     auto call = [&](int batch, int k, int vocab, const void* p, int64_t ps, int64_t pr, float t, int top_k,
                     float top_p, void* ws, size_t wsb) {
       if (pass == 0)
         return uno_psi_spec_verify_linear(s, UNO_BF16, batch, k, vocab, p, ps, pr, D, int64_t(K) * V, V,
                                           (const int32_t*)D, (const float*)D, (const float*)D, t, (int32_t*)D,
                                           (int32_t*)D, nullptr, nullptr, nullptr, ws, wsb);
+      if (pass == 2)
+        return uno_psi_spec_verify_linear_early_exit(s, UNO_BF16, batch, k, vocab, p, ps, pr, D, int64_t(K) * V, V,
+                                                     (const int32_t*)D, (const float*)D, (const float*)D, t,
+                                                     (int32_t*)D, (int32_t*)D, nullptr, nullptr, nullptr, ws, wsb);
       return uno_psi_spec_verify_linear_sampled(s, UNO_BF16, batch, k, vocab, p, ps, pr, D, int64_t(K) * V, V,
                                                 (const int32_t*)D, (const float*)D, (const float*)D, t, top_k,
                                                 top_p, 0, (int32_t*)D, (int32_t*)D, nullptr, nullptr, nullptr, ws,
@@ -78,6 +82,7 @@ int main() {
     }
   }
   expect("verify ws q", uno_psi_spec_verify_linear_workspace(256, 15, 151936, &bytes), true);
+  expect("early exit ws q", uno_psi_spec_verify_linear_early_exit_workspace(256, 15, 151936, &bytes), true);
   expect("sampled ws q", uno_psi_spec_verify_linear_sampled_workspace(256, 15, 151936, &bytes), true);
 
   // tree attention and tree verify

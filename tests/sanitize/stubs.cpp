@@ -30,6 +30,7 @@ size_t lora_backward_workspace_bytes(int64_t, int64_t, int64_t, int64_t, int) { 
 size_t tree_build_workspace_bytes(int, int, int) { return 256; }
 size_t tree_verify_workspace_bytes(int, int, int, int, int, int) { return 256; }
 size_t verify_linear_workspace_bytes(int, int, int) { return 256; }
+size_t verify_linear_ee_workspace_bytes(int, int, int) { return 256; }
 size_t verify_linear_sampled_workspace_bytes(int, int, int) { return 256; }
 int rms_norm_max_dim() { return 1 << 16; }
 
@@ -58,6 +59,7 @@ hipError_t launch_transpose_bf16(const void*, int64_t, void*, int64_t, int64_t, 
 hipError_t launch_tree_build(const TreeBuildArgs&, hipStream_t) { return launched(); }
 hipError_t launch_tree_verify(const TreeVerifyArgs&, hipStream_t) { return launched(); }
 hipError_t launch_verify_linear(const VerifyLinearArgs&, hipStream_t) { return launched(); }
+hipError_t launch_verify_linear_ee(const VerifyLinearArgs&, hipStream_t) { return launched(); }
 hipError_t launch_verify_linear_sampled(const VerifyLinearArgs&, int, float, int, hipStream_t) { return launched(); }
 
 }  // namespace uno

@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.uno_abi_version() == 7
+    assert lib.uno_abi_version() == 8
     for s in range(6):
         assert lib.uno_status_string(s)
     assert lib.uno_status_string(99) == b"unknown status"
@@ -92,35 +92,42 @@ def test_gated_lora_rejects_bad_calls(lib):
     assert b"workspace" in lib.uno_last_error() or b"lora_scale" in lib.uno_last_error()
 
 
-def _vl(lib, **kw):
+def _vl(lib, early_exit=False, **kw):
     a = dict(dtype=BF16, batch=2, k=3, vocab=64, p=FAKE16, ps=256, pr=64, q=FAKE16, qs=192, qr=64,
              d=FAKE16, ua=FAKE16, us=FAKE16, T=1.0, L=FAKE16, y=FAKE16, ws=FAKE16, wsb=1 << 20)
     a.update(kw)
-    return lib.uno_psi_spec_verify_linear(None, a["dtype"], a["batch"], a["k"], a["vocab"], a["p"], a["ps"], a["pr"],
-                                          a["q"], a["qs"], a["qr"], a["d"], a["ua"], a["us"], a["T"], a["L"],
-                                          a["y"], None, None, None, a["ws"], a["wsb"])
+    f = lib.uno_psi_spec_verify_linear_early_exit if early_exit else lib.uno_psi_spec_verify_linear
+    return f(None, a["dtype"], a["batch"], a["k"], a["vocab"], a["p"], a["ps"], a["pr"], a["q"], a["qs"], a["qr"],
+             a["d"], a["ua"], a["us"], a["T"], a["L"], a["y"], None, None, None, a["ws"], a["wsb"])
 
 
-def test_verify_linear_rejects_bad_calls(lib):
-    assert _vl(lib, k=65) == INVALID
-    assert _vl(lib, k=-1) == INVALID
-    assert _vl(lib, batch=0) == INVALID
-    assert _vl(lib, vocab=0) == INVALID
-    assert _vl(lib, vocab=(1 << 20) + 1, pr=(1 << 20) + 1, ps=4 * ((1 << 20) + 1),
+@pytest.mark.parametrize("early_exit", [False, True])
+def test_verify_linear_rejects_bad_calls(lib, early_exit):
+    def call(lib, **kw):   # the same checks for both entry points
+        return _vl(lib, early_exit=early_exit, **kw)
+
+    assert call(lib, k=65) == INVALID
+    assert call(lib, k=-1) == INVALID
+    assert call(lib, batch=0) == INVALID
+    assert call(lib, vocab=0) == INVALID
+    assert call(lib, vocab=(1 << 20) + 1, pr=(1 << 20) + 1, ps=4 * ((1 << 20) + 1),
                qr=(1 << 20) + 1, qs=3 * ((1 << 20) + 1)) == UNSUPPORTED
-    assert _vl(lib, p=None) == INVALID
-    assert _vl(lib, q=None) == INVALID
-    assert _vl(lib, T=0.0) == INVALID
-    assert _vl(lib, T=float("inf")) == INVALID
-    assert _vl(lib, pr=63) == INVALID
-    assert _vl(lib, ps=100) == INVALID
-    assert _vl(lib, qs=100) == INVALID
-    assert _vl(lib, wsb=8) == WORKSPACE
-    assert _vl(lib, dtype=5) == INVALID
+    assert call(lib, p=None) == INVALID
+    assert call(lib, q=None) == INVALID
+    assert call(lib, T=0.0) == INVALID
+    assert call(lib, T=float("inf")) == INVALID
+    assert call(lib, pr=63) == INVALID
+    assert call(lib, ps=100) == INVALID
+    assert call(lib, qs=100) == INVALID
+    assert call(lib, wsb=8) == WORKSPACE
+    assert call(lib, dtype=5) == INVALID
     ws = ctypes.c_size_t(0)
-    assert lib.uno_psi_spec_verify_linear_workspace(256, 15, 151936, ctypes.byref(ws)) == OK
+    wsq = lib.uno_psi_spec_verify_linear_early_exit_workspace if early_exit else lib.uno_psi_spec_verify_linear_workspace
+    assert wsq(256, 15, 151936, ctypes.byref(ws)) == OK
     assert ws.value >= 256 * 31 * 16
-    assert lib.uno_psi_spec_verify_linear_workspace(256, 65, 151936, ctypes.byref(ws)) == INVALID
+    assert wsq(256, 65, 151936, ctypes.byref(ws)) == INVALID
+    if early_exit:   # work items beyond 2^31
+        assert wsq(1 << 24, 64, 1 << 20, ctypes.byref(ws)) == UNSUPPORTED
 
 
 def _ta(lib, **kw):
