@@ -667,18 +667,27 @@ def bench_linear_sigma_sweep(args, dad, torch, sigmas=(0.1, 0.5, 2.0), reps=20):
         for _ in range(reps):
             dad.psi_spec_verify_linear_early_exit(p, q, drafts, ua, us, outputs=out_e, workspace=ws_e)
         torch.cuda.synchronize()
-        ee_ms = sum(dad.profile_query(n)[0] for n in ("uno_ee_init", "uno_ee_flow", "uno_draw_seg",
-                                                     "uno_draw_resolve")) / reps
-        flow_ms = dad.profile_query("uno_ee_flow")[0] / reps
+        ee_ms = sum(dad.profile_query(n)[0] for n in ("uno_ee_init", "uno_ee_stats", "uno_ee_accept",
+                                                     "uno_draw_seg", "uno_draw_resolve")) / reps
+        ee_stats_ms = dad.profile_query("uno_ee_stats")[0] / reps
         dad.profile_enable(False)
         dad.profile_reset()
         Le = out_e["accept_len"].cpu().numpy().astype(np.int64)
-        res[-1]["early_exit"] = {"us": ee_ms * 1e3, "flow_us": flow_ms * 1e3,
-                                 "gbs": early_bytes / (ee_ms * 1e-3) / 1e9,
-                                 "hbm_frac": early_bytes / (ee_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                 "bytes": early_bytes,
-                                 "same_accept_len_as_full": int((Le == L).sum())}
-        log(f"  early exit: {ee_ms * 1e3:.1f} us ({early_bytes / 1e9:.2f} GB read)")
+        # rows actually read: every round up to the one holding L (rounds of
+        # 2, 2, 4, then 8 positions), then the draw rows again
+        ends, i0 = [], 0
+        while i0 <= k:
+            i0 = min(i0 + (2 if len(ends) < 2 else 4 if len(ends) == 2 else 8), k + 1)
+            ends.append(i0)
+        upto = np.array([next(e for e in ends if e > x) for x in Le])
+        read_bytes = float((upto + np.minimum(upto, k) + draw_rows).sum()) * row
+        res[-1]["early_exit"] = {"us": ee_ms * 1e3, "stats_us": ee_stats_ms * 1e3,
+                                 "gbs": read_bytes / (ee_ms * 1e-3) / 1e9,
+                                 "hbm_frac": read_bytes / (ee_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                 "bytes_read": read_bytes, "bytes_needed": early_bytes,
+                                 "same_as_full": int(((Le == L) & (out_e["token"].cpu().numpy() ==
+                                                                   out["token"].cpu().numpy())).sum())}
+        log(f"  early exit: {ee_ms * 1e3:.1f} us ({read_bytes / 1e9:.2f} GB read, {early_bytes / 1e9:.2f} needed)")
         if sigma == 0.5:
             # the same rows under sampling transforms (uno_psi_spec_verify_linear_sampled;
             # the drafts here come from the untransformed rows, which changes no work)

@@ -454,18 +454,10 @@ uno_status uno_psi_spec_verify_linear(hipStream_t stream, uno_dtype logit_dtype,
 }
 
 // ------------------------------------------------------------------ early-exit linear verify
-static uno_status check_ee_items(int32_t batch, int32_t k, int32_t vocab) {
-  const int64_t nc = (int64_t(vocab) + 8191) / 8192;
-  if (int64_t(batch) * ((2 * k + 1) * nc + k + 1) > (int64_t(1) << 31) - 1)
-    return fail(UNO_ERR_UNSUPPORTED, "too many work items (batch * ((2k+1) * chunks + k + 1) >= 2^31)");
-  return UNO_OK;
-}
-
 uno_status uno_psi_spec_verify_linear_early_exit_workspace(int32_t batch, int32_t k, int32_t vocab, size_t* bytes) {
   UNO_GUARD_BEGIN
   if (!bytes) return fail(UNO_ERR_INVALID_ARGUMENT, "bytes is NULL");
-  uno_status s = check_verify_linear_shape(batch, k, vocab);
-  if (s == UNO_OK) s = check_ee_items(batch, k, vocab);
+  const uno_status s = check_verify_linear_shape(batch, k, vocab);
   if (s != UNO_OK) return s;
   *bytes = verify_linear_ee_workspace_bytes(batch, k, vocab);
   return UNO_OK;
@@ -485,7 +477,6 @@ uno_status uno_psi_spec_verify_linear_early_exit(hipStream_t stream, uno_dtype l
   uno_status s = verify_linear_args(logit_dtype, batch, k, vocab, p_logits, p_seq_stride, p_row_stride, q_logits,
                                     q_seq_stride, q_row_stride, draft_tokens, u_accept, u_sample, temperature,
                                     out_accept_len, out_token, out_p_draft, out_q_draft, out_residual_mass, &a);
-  if (s == UNO_OK) s = check_ee_items(batch, k, vocab);
   if (s != UNO_OK) return s;
   const size_t need = verify_linear_ee_workspace_bytes(batch, k, vocab);
   if (workspace_bytes < need || !workspace)

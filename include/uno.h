@@ -144,18 +144,17 @@ uno_status uno_psi_spec_verify_linear(hipStream_t stream, uno_dtype logit_dtype,
                                       void* workspace, size_t workspace_bytes);
 
 /* Early-exit variant of uno_psi_spec_verify_linear: the same accept rule,
- * residual and draw, but the rows of positions after the first rejection are
+ * residual and draw, but most rows of positions after the first rejection are
  * not read (drafts are tested in order, and the first rejection ends the
  * block, so those rows cannot change the result).  Source: the same passage
- * (the longest valid prefix of the block is kept).  Same arguments and
- * outputs; the row statistics are summed over 8192-element chunks, so
- * probabilities agree with uno_psi_spec_verify_linear to rounding and the
- * decisions are the same except where a draft sits within rounding of its
- * accept threshold.  out_p_draft / out_q_draft entries of positions after the
- * first rejection are NaN (not evaluated).  The batch's positions are taken
- * in order, so the time follows the longest accepted prefix in the batch and
- * the bytes read follow the accepted lengths.  Extra requirement:
- * batch * ((2k+1) * ceil(vocab / 8192) + k + 1) < 2^31. */
+ * (the longest valid prefix of the block is kept).  Same arguments, same
+ * requirements, same outputs bit for bit (the row statistics are those of
+ * uno_psi_spec_verify_linear, merged in the same order), except that
+ * out_p_draft / out_q_draft entries of positions after the first rejection
+ * are NaN (not evaluated).  Positions are taken in rounds of 2, 2, 4, then 8
+ * positions: a sequence reads the rows of the rounds up to the one holding
+ * its first rejection (at most 7 positions past it), and each round costs two
+ * kernel launches. */
 uno_status uno_psi_spec_verify_linear_early_exit_workspace(int32_t batch, int32_t k, int32_t vocab, size_t* bytes);
 uno_status uno_psi_spec_verify_linear_early_exit(hipStream_t stream, uno_dtype logit_dtype,
                                                  int32_t batch, int32_t k, int32_t vocab,

@@ -126,8 +126,7 @@ def test_verify_linear_rejects_bad_calls(lib, early_exit):
     assert wsq(256, 15, 151936, ctypes.byref(ws)) == OK
     assert ws.value >= 256 * 31 * 16
     assert wsq(256, 65, 151936, ctypes.byref(ws)) == INVALID
-    if early_exit:   # work items beyond 2^31
-        assert wsq(1 << 24, 64, 1 << 20, ctypes.byref(ws)) == UNSUPPORTED
+    assert wsq(1 << 24, 64, 1 << 20, ctypes.byref(ws)) == UNSUPPORTED   # rows beyond 2^31
 
 
 def _ta(lib, **kw):
