@@ -23,6 +23,8 @@
 // Pass 1 streams the pair from HBM; with one pair per compute unit the pair
 // (2 x 297 KB at V = 151,936 in bf16) stays in the memory-side cache for the
 // re-reads of passes 2 and 3.  Sums are taken in a fixed order (deterministic).
+#include <type_traits>
+
 #include "sampler_common.h"
 
 namespace uno {
@@ -122,6 +124,37 @@ __device__ __forceinline__ void store8(T* row, int e0, int vocab, bool vec_ok, c
   }
 }
 
+constexpr int kStep = kDThreads * 8;           // elements per group across the workgroup
+
+// The kUnroll groups of 8 of both rows at base + u * kStep.  FULL: the whole
+// tile lies inside the rows and both are 16-byte aligned (a condition uniform
+// over the workgroup): straight-line vector loads, all issued before the
+// first use.  Otherwise the bounds-checked loads (elements past V read as 0).
+template <typename T, bool NT, bool FULL>
+__device__ __forceinline__ void load_pair_tile(const T* srow, const T* trow, int base, int V, bool vs, bool vt,
+                                               float (&xq)[kUnroll][8], float (&xp)[kUnroll][8]) {
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    if constexpr (FULL) {
+      load8_vec<T, NT>(srow, base + u * kStep, xq[u]);
+      load8_vec<T, NT>(trow, base + u * kStep, xp[u]);
+    } else {
+      load8<T, NT>(srow, base + u * kStep, V, vs, xq[u]);
+      load8<T, NT>(trow, base + u * kStep, V, vt, xp[u]);
+    }
+  }
+}
+
+// Runs body(std::true_type) for a tile wholly inside aligned rows, else
+// body(std::false_type): the in-range path carries no per-element masks.
+template <typename F>
+__device__ __forceinline__ void tile_dispatch(bool full, F&& body) {
+  if (full)
+    body(std::true_type{});
+  else
+    body(std::false_type{});
+}
+
 template <typename T>
 __global__ __launch_bounds__(kDThreads) void distill_kernel(DistillArgs a) {
 #pragma clang fp contract(off)   // y = x * sl2 stays a rounded product in every pass
@@ -132,32 +165,31 @@ __global__ __launch_bounds__(kDThreads) void distill_kernel(DistillArgs a) {
   const T* trow = pair_row<T>(a.teacher, a.t_seq, a.t_row, pair, a.rows);
   const T* srow = pair_row<T>(a.student, a.s_seq, a.s_row, pair, a.rows);
   const bool vt = row_vec_ok(trow), vs = row_vec_ok(srow);
-  constexpr int kStep = kDThreads * 8;
 
   // pass 1: (max, sum) of both rows, log2 domain
   float mq = -INFINITY, sq = 0.f, mp = -INFINITY, sp = 0.f;
-  for (int base = tid * 8; base < V; base += kStep * kUnroll) {
-    float xq[kUnroll][8], xp[kUnroll][8];
+  for (int tile = 0; tile < V; tile += kStep * kUnroll) {
+    tile_dispatch(vs && vt && tile + kStep * kUnroll <= V, [&](auto full_c) {
+      constexpr bool FULL = decltype(full_c)::value;
+      const int base = tile + tid * 8;
+      float xq[kUnroll][8], xp[kUnroll][8];
+      load_pair_tile<T, false, FULL>(srow, trow, base, V, vs, vt, xq, xp);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      load8<T, false>(srow, base + u * kStep, V, vs, xq[u]);
-      load8<T, false>(trow, base + u * kStep, V, vt, xp[u]);
-    }
+      for (int u = 0; u < kUnroll; ++u) {
+        const int e0 = base + u * kStep;
+        if (FULL || e0 < V) {
+          float yq[8], yp[8];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int e0 = base + u * kStep;
-      if (e0 < V) {
-        float yq[8], yp[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const bool in = e0 + j < V;
-          yq[j] = in ? mul_rn(xq[u][j], sl2) : -INFINITY;
-          yp[j] = in ? mul_rn(xp[u][j], sl2) : -INFINITY;
+          for (int j = 0; j < 8; ++j) {
+            const bool in = FULL || e0 + j < V;
+            yq[j] = in ? mul_rn(xq[u][j], sl2) : -INFINITY;
+            yp[j] = in ? mul_rn(xp[u][j], sl2) : -INFINITY;
+          }
+          lse_update8(mq, sq, yq);
+          lse_update8(mp, sp, yp);
         }
-        lse_update8(mq, sq, yq);
-        lse_update8(mp, sp, yp);
       }
-    }
+    });
   }
   {
     const int lane = tid & (kWave - 1), wave = tid / kWave;
@@ -187,27 +219,27 @@ __global__ __launch_bounds__(kDThreads) void distill_kernel(DistillArgs a) {
 
   // pass 2: KL (log2 units), sum |q - p|, sum sign(q - p) q
   float kl = 0.f, tv = 0.f, ss = 0.f;
-  for (int base = tid * 8; base < V; base += kStep * kUnroll) {
-    float xq[kUnroll][8], xp[kUnroll][8];
+  for (int tile = 0; tile < V; tile += kStep * kUnroll) {
+    tile_dispatch(vs && vt && tile + kStep * kUnroll <= V, [&](auto full_c) {
+      constexpr bool FULL = decltype(full_c)::value;
+      const int base = tile + tid * 8;
+      float xq[kUnroll][8], xp[kUnroll][8];
+      load_pair_tile<T, false, FULL>(srow, trow, base, V, vs, vt, xq, xp);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      load8<T, false>(srow, base + u * kStep, V, vs, xq[u]);
-      load8<T, false>(trow, base + u * kStep, V, vt, xp[u]);
-    }
+      for (int u = 0; u < kUnroll; ++u) {
+        const int e0 = base + u * kStep;
+        const int nv = FULL ? 8 : min(8, V - e0);   // valid elements of the group (<= 0: none)
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int e0 = base + u * kStep;
-      const int nv = min(8, V - e0);   // valid elements of the group (<= 0: none)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float uq = mul_rn(xq[u][j], sl2) - Lq, up = mul_rn(xp[u][j], sl2) - Lp;
-        const float q = j < nv ? fast_exp2(uq) : 0.f, p = j < nv ? fast_exp2(up) : 0.f;
-        const float d = uq - up;
-        kl = fmaf(q, d, kl);
-        tv += fabsf(q - p);
-        ss += (d > 0.f) ? q : ((d < 0.f) ? -q : 0.f);
+        for (int j = 0; j < 8; ++j) {
+          const float uq = mul_rn(xq[u][j], sl2) - Lq, up = mul_rn(xp[u][j], sl2) - Lp;
+          const float q = j < nv ? fast_exp2(uq) : 0.f, p = j < nv ? fast_exp2(up) : 0.f;
+          const float d = uq - up;
+          kl = fmaf(q, d, kl);
+          tv += fabsf(q - p);
+          ss += (d > 0.f) ? q : ((d < 0.f) ? -q : 0.f);
+        }
       }
-    }
+    });
   }
   block_sum3(kl, tv, ss, sh);
   const float KL = kLn2 * kl;
@@ -223,29 +255,29 @@ __global__ __launch_bounds__(kDThreads) void distill_kernel(DistillArgs a) {
   const float c0 = a.grad_scale * a.inv_t;
   const float akl = a.alpha * kLn2, hb = 0.5f * a.beta;
   const float off = a.alpha * KL + hb * ss;     // sum_u q_u (alpha (ln q_u - ln p_u) + beta/2 sign_u)
-  for (int base = tid * 8; base < V; base += kStep * kUnroll) {
-    float xq[kUnroll][8], xp[kUnroll][8];
+  for (int tile = 0; tile < V; tile += kStep * kUnroll) {
+    tile_dispatch(vs && vt && tile + kStep * kUnroll <= V, [&](auto full_c) {
+      constexpr bool FULL = decltype(full_c)::value;
+      const int base = tile + tid * 8;
+      float xq[kUnroll][8], xp[kUnroll][8];
+      load_pair_tile<T, true, FULL>(srow, trow, base, V, vs, vt, xq, xp);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      load8<T, true>(srow, base + u * kStep, V, vs, xq[u]);
-      load8<T, true>(trow, base + u * kStep, V, vt, xp[u]);
-    }
+      for (int u = 0; u < kUnroll; ++u) {
+        const int e0 = base + u * kStep;
+        if (FULL || e0 < V) {
+          float g[8];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int e0 = base + u * kStep;
-      if (e0 < V) {
-        float g[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float uq = mul_rn(xq[u][j], sl2) - Lq, up = mul_rn(xp[u][j], sl2) - Lp;
-          const float q = fast_exp2(uq);
-          const float d = uq - up;
-          const float sg = (d > 0.f) ? 1.f : ((d < 0.f) ? -1.f : 0.f);
-          g[j] = c0 * q * (fmaf(akl, d, fmaf(hb, sg, -off)));
+          for (int j = 0; j < 8; ++j) {
+            const float uq = mul_rn(xq[u][j], sl2) - Lq, up = mul_rn(xp[u][j], sl2) - Lp;
+            const float q = fast_exp2(uq);
+            const float d = uq - up;
+            const float sg = (d > 0.f) ? 1.f : ((d < 0.f) ? -1.f : 0.f);
+            g[j] = c0 * q * (fmaf(akl, d, fmaf(hb, sg, -off)));
+          }
+          store8<T>(grow, e0, V, vg, g);
         }
-        store8<T>(grow, e0, V, vg, g);
       }
-    }
+    });
   }
 }
 

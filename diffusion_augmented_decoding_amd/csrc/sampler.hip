@@ -225,11 +225,28 @@ constexpr int kCutWaves = kCutThreads / kWave;
 constexpr double kMassScale = 1099511627776.0;   // 2^40: fixed-point masses (2^20 tokens of mass <= 1 fit)
 
 // One pass over row elements [0, vocab) by the block: f(index, logit) for
-// each, 8 consecutive elements per thread per step (16-byte loads).
+// each, 8 consecutive elements per thread per step (16-byte loads).  Tiles
+// of kCutUnroll steps wholly inside an aligned row load their vectors
+// together (one memory latency per tile); each thread meets its elements in
+// the same order either way.
+constexpr int kCutUnroll = 4;
 template <typename T, typename F>
 __device__ __forceinline__ void cut_pass(const T* row, int vocab, F f) {
+  constexpr int kStepE = kCutThreads * 8;
   const bool vec = row_vec_ok(row);
-  for (int e0 = threadIdx.x * 8; e0 < vocab; e0 += kCutThreads * 8) {
+  int t0 = 0;
+  if (vec) {
+    for (; t0 + kCutUnroll * kStepE <= vocab; t0 += kCutUnroll * kStepE) {
+      float x[kCutUnroll][8];
+#pragma unroll
+      for (int u = 0; u < kCutUnroll; ++u) load8_vec<T, false>(row, t0 + u * kStepE + threadIdx.x * 8, x[u]);
+#pragma unroll
+      for (int u = 0; u < kCutUnroll; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f(t0 + u * kStepE + threadIdx.x * 8 + j, x[u][j]);
+    }
+  }
+  for (int e0 = t0 + threadIdx.x * 8; e0 < vocab; e0 += kStepE) {
     float x[8];
     load8<T, false>(row, e0, vocab, vec, x);
 #pragma unroll

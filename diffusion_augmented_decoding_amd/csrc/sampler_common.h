@@ -30,13 +30,18 @@ template <> __device__ __forceinline__ float load_logit<uint16_t>(const uint16_t
 template <> __device__ __forceinline__ float load_logit<float>(const float* p, int64_t i) { return p[i]; }
 
 // 16-byte row load: non-temporal (a row streamed once) or cached (a row the
-// caller reads again soon, e.g. the tree verify's rounds).
+// caller reads again soon, e.g. the tree verify's rounds).  Rows are device
+// memory: the load goes through the global address space (a flat load would
+// also count against the scalar-load counter, so waiting for a descriptor
+// read would wait for every row load in flight too).
 template <bool NT, typename V>
 __device__ __forceinline__ V row_load(const V* p) {
+  using GV = const __attribute__((address_space(1))) V;
+  GV* g = (GV*)(p);
   if constexpr (NT)
-    return __builtin_nontemporal_load(p);
+    return __builtin_nontemporal_load(g);
   else
-    return *p;
+    return *g;
 }
 
 // Loads 8 consecutive logits starting at e0 (bounds- and alignment-safe;
@@ -285,6 +290,58 @@ __device__ __forceinline__ void weights8(const DrawDesc& d, int e0, int vocab, f
   }
 }
 
+// 8 logits from a 16-byte aligned row, every element in range.
+template <typename T, bool NT>
+__device__ __forceinline__ void load8_vec(const T* row, int e0, float (&x)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    const u32x4 v = row_load<NT>(reinterpret_cast<const u32x4*>(row + e0));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = bf16_lo(v[j]);
+      x[2 * j + 1] = bf16_hi(v[j]);
+    }
+  } else {
+    const f32x4 v0 = row_load<NT>(reinterpret_cast<const f32x4*>(row + e0));
+    const f32x4 v1 = row_load<NT>(reinterpret_cast<const f32x4*>(row + e0 + 4));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = v0[j];
+      x[4 + j] = v1[j];
+    }
+  }
+}
+
+constexpr int kSegPerWave = kSegPerChunk / (kChunkThreads / kWave);   // 4
+
+// Segment sums of a chunk that lies wholly inside the row, rows 16-byte
+// aligned: every load issued before the first use (one memory latency per
+// thread, not one per segment).  The arithmetic is weights8's for elements
+// in range, so the sums have the same bits as on the general path.
+template <typename T, bool CUT, bool HASQ>
+__device__ __forceinline__ void seg_sums_full(const DrawDesc& d, int ebase, float sl2, float (&sw)[kSegPerWave],
+                                              float (&sp)[kSegPerWave]) {
+  float xp[kSegPerWave][8], xq[kSegPerWave][8];
+#pragma unroll
+  for (int q = 0; q < kSegPerWave; ++q) {   // q rows first: the two variants share no leading load to hoist
+    if constexpr (HASQ) load8_vec<T, true>(static_cast<const T*>(d.qrow), ebase + q * kSegLen, xq[q]);
+    load8_vec<T, true>(static_cast<const T*>(d.prow), ebase + q * kSegLen, xp[q]);
+  }
+#pragma unroll
+  for (int q = 0; q < kSegPerWave; ++q) {
+    sw[q] = 0.f;
+    sp[q] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int v = ebase + q * kSegLen + j;
+      const float p = row_prob<CUT>(xp[q][j], v, sl2, d.mp, d.inv_sp, d.tp, d.gp);
+      float w = p;
+      if constexpr (HASQ) w = fmaxf(fmaf(-d.c, row_prob<CUT>(xq[q][j], v, sl2, d.mq, d.inv_sq, d.tq, d.gq), p), 0.f);
+      sw[q] += w;
+      sp[q] += p;
+    }
+  }
+}
+
 // Segment masses of chunk c of draw b: seg[(b * nchunk + c) * 2*kSegPerChunk + k]
 // for the 16 segments of w, then the 16 of p.  A block of kChunkThreads threads.
 template <typename T, bool CUT = false>
@@ -295,20 +352,26 @@ __device__ __forceinline__ void draw_seg_body(const DrawDesc* __restrict__ desc,
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const bool vp = row_vec_ok(static_cast<const T*>(d.prow));
   const bool vq = row_vec_ok(static_cast<const T*>(d.qrow));
-  constexpr int kSegPerWave = kSegPerChunk / (kChunkThreads / kWave);   // 4
   float sw[kSegPerWave], sp[kSegPerWave];
   // wave w owns segments 4w..4w+3; lane l reads elements [8l, 8l+8) of each
+  const int ebase = c * kChunk + wave * kSegPerWave * kSegLen + lane * 8;
+  if (vp && vq && (c + 1) * kChunk <= vocab) {   // uniform over the workgroup
+    if (d.c != 0.f)
+      seg_sums_full<T, CUT, true>(d, ebase, sl2, sw, sp);
+    else
+      seg_sums_full<T, CUT, false>(d, ebase, sl2, sw, sp);
+  } else {
 #pragma unroll
-  for (int q = 0; q < kSegPerWave; ++q) {
-    const int e0 = c * kChunk + (wave * kSegPerWave + q) * kSegLen + lane * 8;
-    float w[8], pw[8];
-    weights8<T, true, CUT>(d, e0, vocab, sl2, vp, vq, w, pw);
-    sw[q] = 0.f;
-    sp[q] = 0.f;
+    for (int q = 0; q < kSegPerWave; ++q) {
+      float w[8], pw[8];
+      weights8<T, true, CUT>(d, ebase + q * kSegLen, vocab, sl2, vp, vq, w, pw);
+      sw[q] = 0.f;
+      sp[q] = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      sw[q] += w[j];
-      sp[q] += pw[j];
+      for (int j = 0; j < 8; ++j) {
+        sw[q] += w[j];
+        sp[q] += pw[j];
+      }
     }
   }
   float* dst = seg + (int64_t(b) * nchunk + c) * (2 * kSegPerChunk);

@@ -818,7 +818,6 @@ __device__ void seg_item(const TreeVerifyArgs& a, const TreeWs& w, int b, int c)
   const int nc = num_chunks(a.vocab);
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const bool vp = row_vec_ok(static_cast<const T*>(d.prow)), vq = row_vec_ok(static_cast<const T*>(d.qrow));
-  constexpr int kSegPerWave = kSegPerChunk / (kChunkThreads / kWave);
   float* dst = w.seg + (int64_t(b) * nc + c) * (2 * kSegPerChunk);
   // without replacement: the removed tokens' weights (every wave its own copy)
   int wm = 0;
