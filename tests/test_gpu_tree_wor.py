@@ -172,8 +172,9 @@ def test_verify_wor_malformed_and_limits(gpu_lib):
 def test_build_then_verify_on_the_gpu(gpu_lib):
     """The decode-side pair: trees built on the GPU without replacement, then
     verified without replacement.  The built tokens are checked against
-    oracle.build_tree first; where they match, the verify is checked
-    against the oracle on the oracle's own trees."""
+    oracle.build_tree first (equal up to counted near-ties of a draw, u
+    within 1e-5 of a CDF boundary); the verify is then checked against the
+    oracle on the GPU's own trees."""
     import torch
     branching = [4, 4, 3]
     c = workloads.tree_build_case(4, branching, 30000, "bf16", seed=9, q_std=1.0)
@@ -181,7 +182,9 @@ def test_build_then_verify_on_the_gpu(gpu_lib):
     built = gpu_lib.psi_spec_build_tree(q, branching, to_dev(c["u_draw"]), 1.0, True)
     torch.cuda.synchronize()
     par, tok = to_host(built["parent"]), to_host(built["tokens"])
-    assert check_tree_build(c["q_f32"], branching, c["u_draw"], par, tok, 1.0, True) == 0
+    ties = check_tree_build(c["q_f32"], branching, c["u_draw"], par, tok, 1.0, True)
+    say(f"build near-ties: {ties} of {tok.shape[0] * (tok.shape[1] - 1)} draws")
+    assert ties <= 2
     toks = tok.copy()
     toks[:, 0] = 0
     g = gpu_lib.psi_spec_verify_tree(built["parent"], torch.from_numpy(toks).to("cuda"), to_dev(c["p"]), q,
@@ -190,8 +193,11 @@ def test_build_then_verify_on_the_gpu(gpu_lib):
     torch.cuda.synchronize()
     g = {k: to_host(v) for k, v in g.items()}
     ref = _built_case(4, branching, 30000, "bf16", seed=9, q_std=1.0)
-    assert np.array_equal(ref["tokens"], toks)
-    assert _check(ref["parent"], ref["tokens"], ref["p_f32"], ref["q_f32"], ref["u_acc"], ref["u_s"], g) <= 1
+    if ties == 0:
+        assert np.array_equal(ref["tokens"], toks)
+    # the verify is checked on the trees the GPU built (they differ from the
+    # oracle's own only at a counted near-tie of a draw)
+    assert _check(par, toks, ref["p_f32"], ref["q_f32"], ref["u_acc"], ref["u_s"], g) <= 1
 
 
 def test_verify_wor_is_deterministic(gpu_lib):
