@@ -139,7 +139,8 @@ __device__ __forceinline__ void split_range(const GemmParams& p, int bk, int kt_
 }
 
 // BM x BN block tile, WM x WN waves, P K-tiles of register prefetch, DBF:
-// double-buffer the MFMA fragments across k-steps, MODE: 0 = bf16 out,
+// 1 = double-buffer the MFMA fragments across k-steps, 2 = defer each
+// K-tile's last k-step across the barrier (below), MODE: 0 = bf16 out,
 // 1 = fp32 split-K partials, 2 = SwiGLU of a gate and an up projection
 // (below).
 // MODE 2 (FAST only, BN = 256 on 8 waves): a block tile covers BN / 2
@@ -397,7 +398,78 @@ __global__ __launch_bounds__(WM * WN * kWave) void gemm_bf16_kernel(GemmParams p
     }
   };
 
-  if (kt_begin < kt_end) {
+  // DBF == 2: the last k-step of a K-tile is deferred across the barrier.
+  // Its fragments are read into (da, db) with the third k-step's, under that
+  // k-step's MFMAs (so the stage may be overwritten once the barrier is
+  // passed), and its MFMAs are issued after the barrier, under the reads of
+  // the next K-tile's first k-step: the matrix pipe stays busy while those
+  // reads are in flight, where the other form waits for them after every
+  // barrier.  The LDS stores of the next K-tile are spread over the first
+  // three k-steps.  The k-steps of every accumulator keep their order, so the
+  // results are the other form's bit for bit.
+  bf16x8 da[FN], db[FM];
+  auto mfma_frags = [&](const bf16x8 (&fa)[FN], const bf16x8 (&fb)[FM]) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+  auto compute_def = [&](auto def_tag, int cur, u32x4 (&set)[LT], int kt_next, int kt_reload) {
+    constexpr bool DEF = decltype(def_tag)::value;
+    constexpr int KS = kBK / 16;
+    const unsigned char* As = smem + cur * STAGE;
+    const unsigned char* Bs = As + BN * kBK * 2;
+    bf16x8 fa[FN], fb[FM];
+#pragma unroll
+    for (int kk = 0; kk + 1 < KS; ++kk) {
+      read_frags(As, Bs, kk, fa, fb);
+      // the deferred k-step's reads go out with the last undeferred
+      // k-step's, under its MFMAs
+      if (kk + 2 == KS) read_frags(As, Bs, KS - 1, da, db);
+      if (DEF && kk == 0) mfma_frags(da, db);
+      mfma_frags(fa, fb);
+#pragma unroll
+      for (int i = kk * LT / (KS - 1); i < (kk + 1) * LT / (KS - 1); ++i) {
+        sstore(set, cur ^ 1, i, kt_next);
+        gload(set, i, kt_reload);
+      }
+      const int nw = (kk + 1) * LT / (KS - 1) - kk * LT / (KS - 1);
+      if (DEF && kk == 0) {
+        // the reads first, then the deferred MFMAs, then this k-step's
+        __builtin_amdgcn_sched_group_barrier(0x100, FN + FM, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, FN * FM, 0);
+      }
+      if (kk + 2 == KS) __builtin_amdgcn_sched_group_barrier(0x100, 2 * (FN + FM), 0);
+#pragma unroll
+      for (int q = 0; q < FN * FM; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (q < nw) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        if (q < nw) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+    }
+  };
+  static_assert(DBF != 2 || P == 1, "the deferred k-step form keeps one K-tile of register prefetch");
+
+  if constexpr (DBF == 2) {
+    if (kt_begin < kt_end) {
+#pragma unroll
+      for (int i = 0; i < LT; ++i) gload(reg[0], i, kt_begin);
+#pragma unroll
+      for (int i = 0; i < LT; ++i) {
+        sstore(reg[0], 0, i, kt_begin);
+        gload(reg[0], i, kt_begin + 1);
+      }
+      __syncthreads();
+      compute_def(std::false_type{}, 0, reg[0], kt_begin + 1, kt_begin + 2);
+      __syncthreads();
+      for (int kt = kt_begin + 1; kt < kt_end; ++kt) {
+        compute_def(std::true_type{}, (kt - kt_begin) & 1, reg[0], kt + 1, kt + 2);
+        __syncthreads();
+      }
+      mfma_frags(da, db);
+    }
+  } else if (kt_begin < kt_end) {
     // prologue: K-tiles kt_begin .. kt_begin+P-1 into sets 0..P-1; tile 0 to LDS
 #pragma unroll
     for (int s = 0; s < P; ++s)
@@ -1010,7 +1082,12 @@ hipError_t launch_cfg(const TileCfg& c, const GemmParams& p, hipStream_t stream,
     case 0: return launch_tile<64, 64, 2, 2, 4, 1, MODE>(p, c.splits, stream, name);
     case 1: return launch_tile<128, 128, 2, 2, 4, 1, MODE>(p, c.splits, stream, name);
     case 5: return launch_tile<256, 192, 4, 2, 2, 0, MODE>(p, c.splits, stream, name);
-    case 9: return launch_tile<256, 256, 4, 2, 1, 0, MODE>(p, c.splits, stream, name);
+    case 9:
+#ifdef UNO_TUNING
+      if (const char* env = tuning_env("UNO_GEMM_DEFER"))   // tuning override: 0 = no deferred k-step
+        if (atoi(env) == 0) return launch_tile<256, 256, 4, 2, 1, 0, MODE>(p, c.splits, stream, name);
+#endif
+      return launch_tile<256, 256, 4, 2, 1, 2, MODE>(p, c.splits, stream, name);
 #ifdef UNO_TUNING
     case 2: return launch_tile<256, 192, 2, 2, 2, 0, MODE>(p, c.splits, stream, name);
     case 3: return launch_tile<256, 192, 4, 2, 2, 1, MODE>(p, c.splits, stream, name);
@@ -1292,7 +1369,11 @@ bool swiglu_fused_ok(const SwigluArgs& a) {
 // bf16(silu(g) * u); the 256 x 256 tile with 8 waves on the buffer-load path
 hipError_t launch_gated_lora_swiglu(const SwigluArgs& a, hipStream_t stream) {
   if (!swiglu_fused_ok(a)) return hipErrorNotSupported;
-  return launch_tile_k<256, 256, 4, 2, 1, 0, 2, 1>(swiglu_params(a), 1, stream, "uno_gemm_bf16");
+#ifdef UNO_TUNING
+  if (const char* env = tuning_env("UNO_GEMM_DEFER"))   // tuning override: 0 = no deferred k-step
+    if (atoi(env) == 0) return launch_tile_k<256, 256, 4, 2, 1, 0, 2, 1>(swiglu_params(a), 1, stream, "uno_gemm_bf16");
+#endif
+  return launch_tile_k<256, 256, 4, 2, 1, 2, 2, 1>(swiglu_params(a), 1, stream, "uno_gemm_bf16");
 }
 
 namespace {
